@@ -1,0 +1,324 @@
+"""CPU oracle for the fused routed-experts MoE layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers); both sides only receive the
+same seeded inputs from ``moe_workloads``.
+
+Everything is plain numpy in float64 unless a step is defined by the method in
+a narrower precision (the fp8 re-quantisation of the SwiGLU output, done in
+float32 exactly as the method prescribes it).  Sources, cited by page title
+and section:
+
+* [OCR2] model card "DeepSeek-OCR-2 MoE experts" (aymous/deepseek-ocr2-moe-experts):
+  the description paragraph (routed experts, plain SiLU SwiGLU, router-weight
+  scale and scatter-add; routing and shared experts stay outside the op) and
+  the "Usage" listing (operand layouts gate_up_proj [E, 2F, H],
+  down_proj [E, H, F], int32 top_k_index [T, k], fp32 top_k_weights [T, k]).
+* [MPK] mirage-project/mirage issue "[Feature Request] - Supporting MegaKernel
+  for DeepSeek Models", "Layer Tensor Details": moe_w13_fp8_layer and
+  moe_w2_fp8_layer (fp8 E4M3 operands with one fp32 scale per 128-wide K
+  block, per row), moe_silu_mul_layer (SwiGLU on [.., 2M] -> [.., M]),
+  moe_local_reduction (output is the routing-weighted sum over the k slots),
+  bf16_to_fp8_quantize (block-wise quantisation with block size 128).
+
+Readings of points the pages leave open (each is listed in the design doc):
+
+1. gate_up rows [0, F) are the gate (SiLU applied), rows [F, 2F) are "up".
+2. SiLU is z * sigmoid(z) with no clamp.
+3. top_k_weights already carry the routed scaling factor; the op only
+   multiplies by them.
+4. No residual term in this op.
+5. A token that names the same expert in two slots gets both contributions.
+6. Expert ids outside [0, E) drop their slot: it contributes nothing and is
+   absent from the routing plan.
+7. The routing plan orders the flat slot ids s = t*k + j by expert, ties in
+   ascending s; perm/inv use -1 for dropped positions.
+9. The fp8 path re-quantises h per (row, 128 block) with an fp32 scale
+   s = amax / 448, codes = RNE_e4m3fn(clamp(h * (448 / amax), +-448)), and an
+   all-zero block gets s = 1 and zero codes.
+10. FP8 is OCP E4M3FN: bias 7, max 448, codes 0x7F/0xFF are NaN, no infinity.
+
+Parity status: every function here is pinned by the CPU tests in
+tests/test_oracle_pins.py (brute force, closed forms, invariants, library
+routines); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "silu",
+    "routing_plan",
+    "moe_experts_reference",
+    "moe_experts_reference_batched",
+    "e4m3fn_decode",
+    "e4m3fn_encode",
+    "quantize_block128_fp32",
+    "dequantize_block128",
+    "moe_experts_fp8_reference",
+]
+
+# --------------------------------------------------------------------------
+# SwiGLU activation ([OCR2] description: "plain SiLU"; [MPK] silu_mul layers)
+# --------------------------------------------------------------------------
+
+
+def silu(z):
+    """SiLU(z) = z / (1 + exp(-z)) in float64 (reading 2: no clamp, no alpha)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+# --------------------------------------------------------------------------
+# Routing plan (grouping implied by the grouped GEMM of [OCR2]; the [E+1]
+# int32 "masks" tensor of [MPK] moe_w13/moe_w2 is the prefix over experts)
+# --------------------------------------------------------------------------
+
+
+def routing_plan(top_k_index, num_experts):
+    """Counting sort of the flat slots s = t*k + j by expert id.
+
+    Returns ``counts[E]``, ``offsets[E+1]`` (exclusive prefix, offsets[E] is
+    the number of valid slots), ``perm[P]`` (slot ids grouped by expert,
+    ascending s inside a group, -1 past offsets[E]) and ``inv[P]`` (position of
+    slot s in perm, -1 for a dropped slot).  Written as two plain passes over
+    the slots so that it is checkable by eye; reading 6 drops ids outside
+    [0, E), reading 7 fixes the tie order.
+    """
+    ids = np.asarray(top_k_index).reshape(-1).astype(np.int64)
+    P = ids.shape[0]
+    E = int(num_experts)
+    counts = np.zeros(E, dtype=np.int64)
+    for s in range(P):
+        e = ids[s]
+        if 0 <= e < E:
+            counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:E].copy()
+    perm = np.full(P, -1, dtype=np.int64)
+    inv = np.full(P, -1, dtype=np.int64)
+    for s in range(P):
+        e = ids[s]
+        if 0 <= e < E:
+            perm[cursor[e]] = s
+            inv[s] = cursor[e]
+            cursor[e] += 1
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm.astype(np.int32), inv.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# bf16 layer ([OCR2] description and "Usage"; combine as [MPK]
+# moe_local_reduction without the residual)
+# --------------------------------------------------------------------------
+
+
+def _as_f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights):
+    """Routed-experts layer, one token and one slot at a time, in float64.
+
+    hidden [T, H], gate_up [E, 2F, H], down [E, H, F] are the operands' values
+    (bf16 inputs upcast exactly); top_k_index int [T, k]; top_k_weights [T, k].
+    For every token t and slot j with a valid expert e:
+        g   = gate_up[e] @ x[t]               (2F values)
+        h   = silu(g[:F]) * g[F:]             (F values)
+        y   = down[e] @ h                     (H values)
+        out[t] += w[t, j] * y
+    """
+    x = _as_f64(hidden)
+    w13 = np.asarray(gate_up)
+    w2 = np.asarray(down)
+    idx = np.asarray(top_k_index)
+    wts = _as_f64(top_k_weights)
+    T, H = x.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    k = idx.shape[1]
+    out = np.zeros((T, H), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if not 0 <= e < E:
+                continue
+            g = _as_f64(w13[e]) @ x[t]
+            h = silu(g[:F]) * g[F:]
+            y = _as_f64(w2[e]) @ h
+            out[t] += wts[t, j] * y
+    return out
+
+
+def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weights):
+    """Same sums as :func:`moe_experts_reference`, grouped by expert.
+
+    Each expert's rows are gathered once and multiplied as one float64 matrix
+    product, so a large layer does not re-read the expert weights per slot.
+    Only the summation order inside the dot products differs from the
+    per-slot form.
+    """
+    x = _as_f64(hidden)
+    w13 = np.asarray(gate_up)
+    w2 = np.asarray(down)
+    idx = np.asarray(top_k_index)
+    wts = _as_f64(top_k_weights)
+    T, H = x.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    out = np.zeros((T, H), dtype=np.float64)
+    for e in range(E):
+        tt, jj = np.nonzero(idx == e)
+        if tt.size == 0:
+            continue
+        g = x[tt] @ _as_f64(w13[e]).T
+        h = silu(g[:, :F]) * g[:, F:]
+        y = h @ _as_f64(w2[e]).T
+        contrib = wts[tt, jj][:, None] * y
+        np.add.at(out, tt, contrib)
+    return out
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3FN codec (reading 10; [MPK] moe_w13_fp8_layer dtypes "FP8 E4M3")
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3fn_decode(codes):
+    """Exact value of each OCP E4M3FN byte as float64.
+
+    sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+    exponent 0: (-1)^s * 2^-6 * m/8; otherwise (-1)^s * 2^(e-7) * (1 + m/8);
+    exponent 15 with mantissa 7 is NaN (no infinities).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    v = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def e4m3fn_encode(v):
+    """Round-to-nearest-even encoding of finite values with |v| <= 448.
+
+    Callers clamp first (reading 9).  Subnormal range |v| < 2^-6 is a multiple
+    of 2^-9; normal range keeps 3 mantissa bits.  A mantissa that rounds up to
+    8 carries into the exponent, which the integer code arithmetic does by
+    itself (code = (exp+7)*8 + m).
+    """
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    if np.any(~np.isfinite(a)) or np.any(a > E4M3_MAX):
+        raise ValueError("e4m3fn_encode expects finite values within +-448")
+    neg = np.signbit(np.asarray(v, dtype=np.float64))
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormals: magnitude in units of 2^-9, rounded half to even
+    code = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), code)
+    # normals: a = 2^E * f with f in [1, 2)
+    safe = np.where(sub, 1.0, a)
+    mant, exp2 = np.frexp(safe)          # safe = mant * 2^exp2, mant in [0.5, 1)
+    E = exp2 - 1                          # so safe = (2*mant) * 2^E
+    q = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)   # 0..8
+    ncode = (E + 7) * 8 + q
+    code = np.where(sub, code, ncode)
+    code = code | np.where(neg, 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_block128_fp32(h):
+    """Block-128 fp8 quantisation of the rows of ``h`` done in float32.
+
+    [MPK] bf16_to_fp8_quantize gives block size 128; the scale dtype follows
+    moe_w2_fp8_layer's fp32 input_scale (reading 9).  For each row and each
+    128-column block, all in float32 arithmetic:
+        a = max |h|,  s = a / 448,  v = clamp(h * (448 / a), -448, 448),
+        code = RNE_e4m3fn(v);  a == 0 gives s = 1 and zero codes.
+    Returns (codes uint8 [.., K], scales float32 [.., K/128]).
+    """
+    hb = np.asarray(h, dtype=np.float32)
+    K = hb.shape[-1]
+    if K % 128:
+        raise ValueError("last dimension must be a multiple of 128")
+    blocks = hb.reshape(hb.shape[:-1] + (K // 128, 128))
+    amax = np.max(np.abs(blocks), axis=-1)                      # float32, exact
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1.0), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    recip = (np.float32(E4M3_MAX) / safe).astype(np.float32)
+    v = (blocks * recip[..., None]).astype(np.float32)          # fp32 multiply
+    v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    v = np.where(zero[..., None], np.float32(0.0), v)
+    codes = e4m3fn_encode(v).reshape(hb.shape)
+    return codes, scale.astype(np.float32)
+
+
+def dequantize_block128(codes, scales):
+    """value = decode(code) * scale[..., col // 128] in float64."""
+    vals = e4m3fn_decode(codes)
+    K = vals.shape[-1]
+    s = np.repeat(np.asarray(scales, dtype=np.float64), 128, axis=-1)[..., :K]
+    return vals * s
+
+
+# --------------------------------------------------------------------------
+# FP8 block-scaled layer ([MPK] moe_w13_fp8_layer, moe_silu_mul_layer,
+# moe_w2_fp8_layer, moe_local_reduction)
+# --------------------------------------------------------------------------
+
+
+def moe_experts_fp8_reference(x_codes, x_scale, w13_codes, w13_scale,
+                              w2_codes, w2_scale, top_k_index, top_k_weights,
+                              tokens=None):
+    """FP8 routed-experts layer in float64 with the method's fp32 re-quantise.
+
+    Operands: x_codes [T, H] + x_scale [T, H/128]; w13_codes [E, 2F, H] +
+    w13_scale [E, 2F, H/128]; w2_codes [E, H, F] + w2_scale [E, H, F/128].
+    Every operand is dequantised exactly (code value times its block scale).
+    Per slot (t, j) with valid expert e:
+        g  = W13[e] @ x[t];  h = silu(g[:F]) * g[F:]                (float64)
+        (q, s) = quantize_block128_fp32(float32(h));  h~ = decode(q) * s
+        y  = W2[e] @ h~;  out[t] += w[t, j] * y
+    The loop runs expert by expert so each expert is dequantised once; within
+    an expert each slot is its own matrix-vector product.  ``tokens``
+    restricts the result to a subset of rows (others stay zero), which is how
+    a sampled check of a large layer is made.
+    Returns out [T, H] float64 (and nothing is rounded to bf16).
+    """
+    xq = np.asarray(x_codes)
+    T, H = xq.shape
+    idx = np.asarray(top_k_index)
+    wts = np.asarray(top_k_weights, dtype=np.float64)
+    E = w13_codes.shape[0]
+    F = w13_codes.shape[1] // 2
+    want = np.zeros(T, dtype=bool)
+    if tokens is None:
+        want[:] = True
+    else:
+        want[np.asarray(tokens)] = True
+    x = dequantize_block128(xq, x_scale)
+    out = np.zeros((T, H), dtype=np.float64)
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & want[:, None])
+        if tt.size == 0:
+            continue
+        W13 = dequantize_block128(np.asarray(w13_codes[e]), np.asarray(w13_scale[e]))
+        W2 = dequantize_block128(np.asarray(w2_codes[e]), np.asarray(w2_scale[e]))
+        for t, j in zip(tt.tolist(), jj.tolist()):
+            g = W13 @ x[t]
+            h = silu(g[:F]) * g[F:]
+            q, s = quantize_block128_fp32(h.astype(np.float32))
+            ht = dequantize_block128(q, s)
+            y = W2 @ ht
+            out[t] += wts[t, j] * y
+    return out

@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a library routine, a brute
+force evaluation written differently, or an invariant of the mathematics, so
+that a plausible slip in the oracle (a swapped gate/up, a dropped term, a
+wrong scale index, a transposed operand, a wrong tie order) fails one of them.
+No GPU is needed.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import moe_workloads as wl
+from oracle import moe_oracle as orc
+
+
+def _problem(T, H, F, E, k, seed, std=0.3, distinct=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H))
+    w13 = rng.standard_normal((E, 2 * F, H)) * std
+    w2 = rng.standard_normal((E, H, F)) * std
+    if distinct:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    else:
+        idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k))
+    return x, w13, w2, idx, w
+
+
+def _dense_bruteforce(x, w13, w2, idx, w):
+    """Every expert on every token (einsum over the full tensors, sigmoid from
+    scipy), then a mask matrix M[t, e] = sum_j w[t, j] [idx[t, j] == e]."""
+    T, H = x.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    G = np.einsum("th,enh->ten", x, w13)                      # [T, E, 2F]
+    gate, up = G[..., :F], G[..., F:]
+    Hh = gate * scipy.special.expit(gate) * up                # [T, E, F]
+    Y = np.einsum("tef,ecf->tec", Hh, w2)                     # [T, E, H]
+    M = np.zeros((T, E))
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            if 0 <= idx[t, j] < E:
+                M[t, idx[t, j]] += w[t, j]
+    return np.einsum("te,tec->tc", M, Y)
+
+
+def _rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ----------------------------------------------------------------- SiLU
+
+
+def test_silu_matches_library_sigmoid():
+    z = np.linspace(-40, 40, 2001)
+    ref = z * scipy.special.expit(z)
+    np.testing.assert_allclose(orc.silu(z), ref, rtol=1e-14, atol=1e-300)
+
+
+def test_silu_closed_values(golden):
+    assert orc.silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert orc.silu(0.0) == 0.0
+    assert orc.silu(-800.0) == 0.0   # no overflow trap at large negative arguments
+
+
+# --------------------------------------------------------- routing plan
+
+
+def _plan_by_library(ids, E):
+    ids = np.asarray(ids).reshape(-1).astype(np.int64)
+    valid = (ids >= 0) & (ids < E)
+    counts = np.bincount(ids[valid], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    key = np.where(valid, ids, E)                     # dropped slots sort last
+    order = np.argsort(key, kind="stable")[: int(valid.sum())]
+    perm = np.full(ids.size, -1)
+    perm[: order.size] = order
+    inv = np.full(ids.size, -1)
+    inv[order] = np.arange(order.size)
+    return counts, offsets, perm, inv
+
+
+@pytest.mark.parametrize("name", ["tiny", "ocr2_decode_t4", "ocr2_prefill"])
+def test_plan_matches_library_sort(name):
+    c = wl.CONFIGS[name]
+    g = wl._gen(c["seed"], "cpu")
+    idx, _ = wl.route_uniform_softmax(c["T"], c["E"], c["k"], g)
+    got = orc.routing_plan(idx.numpy(), c["E"])
+    ref = _plan_by_library(idx.numpy(), c["E"])
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_plan_zipf_with_empty_experts():
+    idx, _ = wl.route_zipf(4096, 128, 8, wl._gen(1005, "cpu"))
+    counts, offsets, perm, inv = orc.routing_plan(idx.numpy(), 128)
+    assert (counts == 0).sum() == 8
+    for a, b in zip((counts, offsets, perm, inv), _plan_by_library(idx.numpy(), 128)):
+        np.testing.assert_array_equal(a, b)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.integers(1, 40), st.integers(1, 9), st.integers(1, 12), st.integers(0, 2**31 - 1))
+def test_plan_properties(T, k, E, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)     # includes dropped ids
+    counts, offsets, perm, inv = orc.routing_plan(ids, E)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    n = int(valid.sum())
+    assert counts.sum() == n and offsets[-1] == n and offsets[0] == 0
+    assert np.all(perm[n:] == -1)
+    assert np.all(inv[~valid] == -1)
+    p = perm[:n]
+    assert np.all(inv[p] == np.arange(n))                 # inv is perm's inverse
+    ex = flat[p]
+    assert np.all(np.diff(ex) >= 0)                        # grouped by expert
+    for e in range(E):
+        seg = p[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)                   # ties by ascending slot id
+    for a, b in zip((counts, offsets, perm, inv), _plan_by_library(ids, E)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_plan_empty_and_all_dropped():
+    counts, offsets, perm, inv = orc.routing_plan(np.zeros((0, 3), np.int32), 4)
+    assert counts.tolist() == [0] * 4 and offsets.tolist() == [0] * 5 and perm.size == 0
+    counts, offsets, perm, inv = orc.routing_plan(np.full((3, 2), -1, np.int32), 4)
+    assert offsets[-1] == 0 and np.all(perm == -1) and np.all(inv == -1)
+
+
+# ------------------------------------------------------------ bf16 layer
+
+
+def test_closed_form_gate_up_order(golden):
+    c = golden["swiglu_h1_f1"]
+    out = orc.moe_experts_reference(np.array([c["x"]]), np.array(c["gate_up"]), np.array(c["down"]),
+                                    np.array(c["top_k_index"]), np.array(c["top_k_weights"]))
+    assert out[0, 0] == pytest.approx(c["out"][0][0], rel=1e-15)
+    assert abs(out[0, 0] - c["out_if_gate_up_swapped"][0][0]) > 0.2
+
+
+def test_closed_form_weighted_slots(golden):
+    c = golden["two_slots_weighted"]
+    for fn in (orc.moe_experts_reference, orc.moe_experts_reference_batched):
+        out = fn(np.array([c["x"]]), np.array(c["gate_up"]), np.array(c["down"]),
+                 np.array(c["top_k_index"]), np.array(c["top_k_weights"]))
+        assert out[0, 0] == pytest.approx(c["out"][0][0], rel=1e-14)
+
+
+def test_single_expert_is_dense_swiglu_mlp():
+    """E=1, k=1, w=1 is the textbook W2 (silu(Wg x) * (Wu x)) for every token."""
+    x, w13, w2, _, _ = _problem(7, 24, 10, 1, 1, seed=3)
+    idx = np.zeros((7, 1), np.int32)
+    w = np.ones((7, 1))
+    Wg, Wu = w13[0, :10], w13[0, 10:]
+    a = x @ Wg.T
+    ref = (a * scipy.special.expit(a) * (x @ Wu.T)) @ w2[0].T
+    out = orc.moe_experts_reference(x, w13, w2, idx, w)
+    assert _rel(out, ref) < 1e-13
+
+
+@pytest.mark.parametrize("shape,seed", [((5, 16, 8, 4, 2), 1), ((9, 12, 6, 7, 3), 2),
+                                        ((6, 8, 4, 5, 5), 3), ((4, 10, 6, 3, 3), 4)])
+def test_oracle_vs_dense_bruteforce(shape, seed):
+    x, w13, w2, idx, w = _problem(*shape, seed=seed, distinct=(seed % 2 == 1))
+    ref = _dense_bruteforce(x, w13, w2, idx, w)
+    assert _rel(orc.moe_experts_reference(x, w13, w2, idx, w), ref) < 1e-12
+    assert _rel(orc.moe_experts_reference_batched(x, w13, w2, idx, w), ref) < 1e-12
+
+
+def test_oracle_vs_bruteforce_on_tiny_config():
+    p = wl.make_config("tiny")
+    x = p["hidden"].float().numpy().astype(np.float64)
+    w13 = p["gate_up"].float().numpy().astype(np.float64)
+    w2 = p["down"].float().numpy().astype(np.float64)
+    idx = p["top_k_index"].numpy()
+    w = p["top_k_weights"].numpy().astype(np.float64)
+    ref = _dense_bruteforce(x, w13, w2, idx, w)
+    assert _rel(orc.moe_experts_reference(x, w13, w2, idx, w), ref) < 1e-12
+    assert _rel(orc.moe_experts_reference_batched(x, w13, w2, idx, w), ref) < 1e-12
+
+
+def test_invariants():
+    x, w13, w2, idx, w = _problem(6, 16, 8, 6, 3, seed=11)
+    f = orc.moe_experts_reference
+    base = f(x, w13, w2, idx, w)
+    # zero routing weights give exactly zero
+    assert np.all(f(x, w13, w2, idx, np.zeros_like(w)) == 0.0)
+    # linear in the routing weights
+    w_b = np.random.default_rng(5).random(w.shape)
+    lin = f(x, w13, w2, idx, 0.7 * w - 1.3 * w_b)
+    assert _rel(lin, 0.7 * base - 1.3 * f(x, w13, w2, idx, w_b)) < 1e-12
+    # permuting the k slots of each token changes nothing
+    for perm in itertools.permutations(range(3)):
+        assert _rel(f(x, w13, w2, idx[:, perm], w[:, perm]), base) < 1e-12
+    # permuting tokens permutes outputs
+    tp = np.random.default_rng(6).permutation(6)
+    assert _rel(f(x[tp], w13, w2, idx[tp], w[tp]), base[tp]) < 1e-12
+    # a duplicated expert in two slots equals one slot with the summed weight
+    idx_d = idx.copy(); idx_d[:, 1] = idx_d[:, 0]
+    w_m = w.copy(); w_m[:, 0] += w_m[:, 1]; w_m[:, 1] = 0.0
+    assert _rel(f(x, w13, w2, idx_d, w), f(x, w13, w2, idx_d, w_m)) < 1e-12
+    # appending an expert nobody routes to changes nothing
+    w13x = np.concatenate([w13, np.ones_like(w13[:1])]); w2x = np.concatenate([w2, np.ones_like(w2[:1])])
+    assert np.array_equal(f(x, w13x, w2x, idx, w), base)
+    # an out-of-range id drops its slot
+    idx_bad = idx.copy(); idx_bad[:, 2] = -1
+    w_z = w.copy(); w_z[:, 2] = 0.0
+    assert _rel(f(x, w13, w2, idx_bad, w), f(x, w13, w2, idx, w_z)) < 1e-12
+
+
+# ------------------------------------------------------------ fp8 codec
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = orc.e4m3fn_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_golden_codes(golden):
+    c = golden["e4m3fn_codes"]
+    got = orc.e4m3fn_decode(np.array(c["codes"], np.uint8))
+    assert got.tolist() == c["values"]
+    assert np.all(np.isnan(orc.e4m3fn_decode(np.array(c["nan_codes"], np.uint8))))
+    assert orc.e4m3fn_encode(np.array(c["values"])).tolist() == c["codes"]
+
+
+def test_e4m3_encode_sweep_vs_torch():
+    rng = np.random.default_rng(0)
+    finite = orc.e4m3fn_decode(np.arange(256, dtype=np.uint8))
+    finite = np.unique(finite[np.isfinite(finite)])
+    mids = (finite[:-1] + finite[1:]) / 2                      # exact ties
+    vals = np.concatenate([
+        finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+        rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 1e-2,
+        rng.standard_normal(20000) * 2.0 ** -8, [2.0 ** -10, -2.0 ** -10, 2.0 ** -11, 0.0, -0.0],
+    ]).astype(np.float32)
+    vals = np.clip(vals, -448, 448)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.e4m3fn_encode(vals)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_roundtrip_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.e4m3fn_decode(codes)
+    ok = np.isfinite(v)
+    assert np.array_equal(orc.e4m3fn_encode(v[ok]), codes[ok])
+
+
+def test_e4m3_encode_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        orc.e4m3fn_encode(np.array([449.0]))
+
+
+def test_block_requant_golden(golden):
+    c = golden["block128_requant"]
+    h = np.zeros(128, np.float32); h[:4] = c["h_first4"]
+    q, s = orc.quantize_block128_fp32(h[None, :])
+    assert q[0, :4].tolist() == c["codes_first4"] and np.all(q[0, 4:] == 0)
+    assert float(s[0, 0]) == c["scale"]
+
+
+def test_block_requant_matches_torch_recipe():
+    """Same fp32 rule as torch's e4m3fn cast after the same fp32 scaling."""
+    rng = np.random.default_rng(1)
+    h = (rng.standard_normal((37, 512)) * np.exp(rng.uniform(-8, 4, (37, 1)))).astype(np.float32)
+    h[3, 128:256] = 0.0                                       # an all-zero block
+    q, s = orc.quantize_block128_fp32(h)
+    tq, ts = wl.quantize_fp8_rows_torch(torch.from_numpy(h))
+    assert np.array_equal(q, tq.numpy()) and np.array_equal(s, ts.numpy())
+    assert s[3, 1] == 1.0 and np.all(q[3, 128:256] == 0)
+
+
+def test_block_requant_error_bound():
+    """|decode(q)*s - h| <= 2^-4 |h| (3 mantissa bits, RNE) or half a
+    subnormal step 2^-10 * s; every block's max maps to +-448."""
+    rng = np.random.default_rng(2)
+    h = (rng.standard_normal((50, 256)) * 3).astype(np.float32)
+    q, s = orc.quantize_block128_fp32(h)
+    back = orc.dequantize_block128(q, s)
+    bound = np.maximum(2.0 ** -4 * np.abs(h), 2.0 ** -10 * np.repeat(s, 128, axis=1)) * (1 + 1e-6)
+    assert np.all(np.abs(back - h) <= bound)
+    blocks = np.abs(orc.e4m3fn_decode(q)).reshape(50, 2, 128)
+    assert np.all(blocks.max(axis=-1) == 448.0)
+
+
+def test_dequantize_matches_torch():
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 256, size=(9, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                        # keep away from NaN codes
+    sc = rng.random((9, 3)).astype(np.float32) + 0.1
+    ref = (torch.from_numpy(codes).view(torch.float8_e4m3fn).double()
+           * torch.from_numpy(sc).double().repeat_interleave(128, dim=1)).numpy()
+    assert np.array_equal(orc.dequantize_block128(codes, sc), ref)
+
+
+# ------------------------------------------------------------ fp8 layer
+
+
+def _fp8_bruteforce(p):
+    """Dense evaluation with torch's fp8 decode and torch's quantiser recipe
+    for the intermediate; shares no function with the oracle's fp8 code."""
+    def deq(c, s):
+        return (c.view(torch.float8_e4m3fn).double() * s.double().repeat_interleave(128, dim=-1))
+    x = deq(p["x"], p["x_scale"])
+    W13 = deq(p["gate_up"], p["gate_up_scale"])
+    W2 = deq(p["down"], p["down_scale"])
+    idx, w = p["top_k_index"].long(), p["top_k_weights"].double()
+    T, H = x.shape
+    E, F2, _ = W13.shape
+    F = F2 // 2
+    out = torch.zeros(T, H, dtype=torch.float64)
+    for t in range(T):
+        for e in range(E):
+            g = W13[e] @ x[t]
+            h = torch.nn.functional.silu(g[:F]) * g[F:]
+            q, s = wl.quantize_fp8_rows_torch(h.float()[None])
+            ht = deq(q, s)[0]
+            y = W2[e] @ ht
+            m = sum(float(w[t, j]) for j in range(idx.shape[1]) if int(idx[t, j]) == e)
+            out[t] += m * y
+    return out.numpy()
+
+
+def test_fp8_oracle_vs_bruteforce():
+    p = wl.make_fp8_problem(6, 256, 128, 5, 3, seed=21, routing="uniform_softmax", routed_scale=1.0)
+    ref = _fp8_bruteforce(p)
+    got = orc.moe_experts_fp8_reference(p["x"].numpy(), p["x_scale"].numpy(), p["gate_up"].numpy(),
+                                        p["gate_up_scale"].numpy(), p["down"].numpy(),
+                                        p["down_scale"].numpy(), p["top_k_index"].numpy(),
+                                        p["top_k_weights"].numpy())
+    assert _rel(got, ref) < 1e-12
+
+
+def test_fp8_oracle_invariants_and_token_subset():
+    p = wl.make_fp8_problem(8, 256, 128, 6, 3, seed=22, routing="uniform_softmax", routed_scale=1.0)
+    args = [p[n].numpy() for n in ("x", "x_scale", "gate_up", "gate_up_scale", "down", "down_scale")]
+    idx, w = p["top_k_index"].numpy(), p["top_k_weights"].numpy().astype(np.float64)
+    f = orc.moe_experts_fp8_reference
+    base = f(*args, idx, w)
+    assert np.all(f(*args, idx, np.zeros_like(w)) == 0.0)
+    assert _rel(f(*args, idx, 2.0 * w), 2.0 * base) < 1e-14
+    assert _rel(f(*args, idx[:, ::-1], w[:, ::-1]), base) < 1e-12
+    sub = f(*args, idx, w, tokens=[1, 5])
+    assert np.array_equal(sub[[1, 5]], base[[1, 5]]) and np.all(sub[[0, 2, 3, 4, 6, 7]] == 0)
