@@ -1,0 +1,184 @@
+/*
+ * moe_experts.h - C ABI of the routed-experts MoE layer for MI355X (gfx950).
+ *
+ * The layer (model card "DeepSeek-OCR-2 MoE experts", description and
+ * "Usage"): given hidden states x [T,H], per-expert gate_up weights
+ * [E,2F,H] and down weights [E,H,F], and the router's top_k_index [T,k]
+ * (int32) and top_k_weights [T,k] (fp32), compute for every token t
+ *
+ *     out[t] = sum_j  w[t,j] * down[e] @ ( silu(g[0:F]) * g[F:2F] ),
+ *              g = gate_up[e] @ x[t],  e = top_k_index[t,j],
+ *
+ * i.e. a per-expert token permutation, a grouped gate_up product, the SwiGLU
+ * activation (rows [0,F) of gate_up are the gate, rows [F,2F) are "up"),
+ * a grouped down product and the router-weighted combine.  Routing and shared
+ * experts are outside the layer; top_k_weights already include any routed
+ * scaling factor.  The fp8 variant follows mirage issue "Supporting
+ * MegaKernel for DeepSeek Models", Layer Tensor Details: moe_w13_fp8_layer,
+ * moe_silu_mul_layer, moe_w2_fp8_layer, moe_local_reduction (without its
+ * residual): E4M3 operands with one fp32 scale per row and 128-wide K block.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, dense row-major, and 16-byte
+ *    aligned.  They are borrowed: the caller owns them and must keep them
+ *    alive until the work enqueued on `stream` has completed.
+ *  - bf16 is passed as uint16_t bit patterns, fp8 as uint8_t OCP E4M3FN codes
+ *    (bias 7, max 448, 0x7F/0xFF are NaN).
+ *  - Expert ids outside [0,E) drop their slot: it contributes nothing.
+ *  - `out` is fully overwritten (never accumulated into).
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *    default stream).  No call allocates memory, synchronises, or copies
+ *    between host and device.  The library keeps no mutable global state;
+ *    concurrent calls are safe when each has its own workspace.
+ *  - Results are deterministic: the combine is a gather-reduce in slot order
+ *    and no floating-point atomics are used anywhere.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Argument errors
+ *    are detected on the host before anything is enqueued.  T == 0 returns
+ *    MOE_OK and enqueues nothing.
+ */
+#ifndef MOE_EXPERTS_H
+#define MOE_EXPERTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,       /* a required pointer is NULL                     */
+    MOE_ERR_SHAPE = -2,      /* a dimension is out of the supported range       */
+    MOE_ERR_ALIGN = -3,      /* a pointer is not 16-byte aligned                */
+    MOE_ERR_WORKSPACE = -4,  /* workspace missing, too small or misaligned      */
+    MOE_ERR_LAUNCH = -5,     /* the HIP runtime rejected a kernel launch        */
+    MOE_ERR_DEVICE = -6,     /* the current device is not a gfx950 GPU          */
+};
+
+enum moe_variant {
+    MOE_VARIANT_PREFILL = 0, /* moe_experts_prefill                            */
+    MOE_VARIANT_DECODE = 1,  /* moe_experts_decode                             */
+    MOE_VARIANT_FP8 = 2,     /* moe_experts_fp8                                */
+    MOE_VARIANT_PLAN = 3,    /* moe_routing_plan                               */
+};
+
+/* Supported ranges (checked on every call; MOE_ERR_SHAPE otherwise):
+ *   1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= E, T >= 0, T*k < 2^31,
+ *   bf16 variants: H and F multiples of 64;  fp8: H and F multiples of 128. */
+#define MOE_MAX_EXPERTS 512
+
+/* Version of this interface (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* moe_strerror(int status);
+
+/*
+ * Bytes of device workspace `variant` needs for these sizes, written to
+ * *bytes.  The workspace is caller-allocated device memory, 256-byte aligned,
+ * that the call uses as scratch (routing plan, intermediate activations and
+ * per-slot expert outputs).  Its contents need no initialisation and are
+ * undefined after the call.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
+ */
+int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_t* bytes);
+
+/*
+ * Byte offsets, inside the workspace of `variant`, of its stages, for tests
+ * and inspection:  offs[0] counts[E] int32, offs[1] offsets[E+1] int32,
+ * offs[2] perm[T*k] int32, offs[3] inv[T*k] int32, offs[4] h (bf16 [T*k,F]
+ * for prefill, fp8 codes [T*k,F] for fp8), offs[5] h scales (fp32
+ * [T*k,F/128], fp8 only), offs[6] y (bf16 [T*k,H], row = flat slot id).
+ * Entries a variant does not use are SIZE_MAX.  The decode fast path
+ * (T <= 4) builds no plan in the workspace.
+ */
+int moe_workspace_layout(int variant, int64_t T, int H, int F, int E, int k, size_t offs[8]);
+
+/*
+ * Routing plan: the deterministic per-expert token permutation that the
+ * grouped products of the model card's prefill op imply (the [E+1] int32
+ * "masks" operand of moe_w13_fp8_layer plays the role of `offsets`).
+ *   top_k_index [T,k] int32 (device)  ->
+ *   counts[E]    number of valid slots per expert,
+ *   offsets[E+1] exclusive prefix of counts; offsets[E] = valid slots,
+ *   perm[T*k]    flat slot ids s = t*k+j grouped by expert, ascending s
+ *                inside a group, -1 after offsets[E],
+ *   inv[T*k]     position of slot s in perm, -1 for a dropped slot.
+ * All outputs are device pointers; ws/ws_bytes as for MOE_VARIANT_PLAN.
+ * The result is bit-exact and independent of launch configuration.
+ */
+int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bf16 routed experts, grouped-GEMM form (the model card's prefill op and
+ * its operand list in "Usage").
+ *   hidden  [T,H]    bf16        gate_up [E,2F,H] bf16     down [E,H,F] bf16
+ *   top_k_index [T,k] int32      top_k_weights [T,k] fp32
+ *   out     [T,H]    bf16 (written)
+ * Accumulation is fp32; the SwiGLU output h and the per-slot expert outputs
+ * are rounded to bf16 in the workspace; the combine sums in fp32 in slot
+ * order and rounds once (round to nearest even).
+ */
+int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+                        const int32_t* top_k_index, const float* top_k_weights,
+                        int64_t T, int H, int F, int E, int k, uint16_t* out,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bf16 routed experts, gather-GEMV form for a handful of tokens (the model
+ * card's decode op: two kernels, no per-expert loop on the host, no
+ * device-to-host synchronisation).  Same operands and results contract as
+ * moe_experts_prefill.  For T <= 4 only the selected experts' weight rows are
+ * streamed, each once, and h stays fp32; larger T runs the grouped-GEMM path.
+ */
+int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+                       const int32_t* top_k_index, const float* top_k_weights,
+                       int64_t T, int H, int F, int E, int k, uint16_t* out,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * FP8 block-scaled routed experts (mirage issue "Supporting MegaKernel for
+ * DeepSeek Models": moe_w13_fp8_layer, moe_silu_mul_layer, moe_w2_fp8_layer,
+ * moe_local_reduction).
+ *   x        [T,H]        fp8   x_scale        [T,H/128]      fp32
+ *   gate_up  [E,2F,H]     fp8   gate_up_scale  [E,2F,H/128]   fp32
+ *   down     [E,H,F]      fp8   down_scale     [E,H,F/128]    fp32
+ *   top_k_index [T,k] int32, top_k_weights [T,k] fp32, out [T,H] bf16.
+ * value(code, block) = e4m3(code) * scale[row][col/128].  Products accumulate
+ * in fp32, one 128-wide K block at a time, then scale by x_scale*w_scale.
+ * The SwiGLU output is re-quantised per (slot row, 128 block) before the down
+ * product: s = amax/448, code = RNE(clamp(h*(448/amax), +-448)); an all-zero
+ * block gets s = 1 and zero codes.
+ */
+int moe_experts_fp8(const uint8_t* x, const float* x_scale,
+                    const uint8_t* gate_up, const float* gate_up_scale,
+                    const uint8_t* down, const float* down_scale,
+                    const int32_t* top_k_index, const float* top_k_weights,
+                    int64_t T, int H, int F, int E, int k, uint16_t* out,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block-128 fp8 quantisation of `rows` rows of K values (mirage issue
+ * "Supporting MegaKernel for DeepSeek Models", bf16_to_fp8_quantize, with the
+ * fp32 scale that moe_w2_fp8_layer's input_scale carries).  `in` is fp32
+ * (in_is_bf16 = 0) or bf16 (in_is_bf16 = 1) [rows,K]; codes [rows,K] fp8;
+ * scales [rows,K/128] fp32.  Per block: s = amax/448,
+ * code = RNE_e4m3(clamp(v*(448/amax), +-448)), all in fp32; an all-zero block
+ * gets s = 1 and zero codes.  This is the same device routine the fp8 layer
+ * uses on h, so it makes the layer's input operands from bf16 activations.
+ * K must be a multiple of 128.
+ */
+int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K,
+                              uint8_t* codes, float* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERTS_H */

@@ -1,0 +1,281 @@
+"""Routed-experts MoE layer for MI355X (gfx950): thin Python binding.
+
+Each function has the name of the C entry point it calls (declared in
+``include/moe_experts.h``) and only marshals arguments: it checks dtypes,
+shapes and devices, allocates the output and a workspace with torch, and
+passes raw device pointers plus torch's current stream.  Every step of the
+layer runs in the HIP kernels of ``libmoe_experts.so``; there is no other
+implementation here, and a missing library is an error.
+
+The operand contract follows the model card "DeepSeek-OCR-2 MoE experts",
+"Usage": ``out = moe_experts_prefill(hidden_states, gate_up_proj, down_proj,
+top_k_index.int(), top_k_weights.float(), top_k)`` with gate_up_proj
+[E, 2F, H] and down_proj [E, H, F]; the decode op has the same arguments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_experts.so")
+
+MOE_VARIANT_PREFILL = 0
+MOE_VARIANT_DECODE = 1
+MOE_VARIANT_FP8 = 2
+MOE_VARIANT_PLAN = 3
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m mixture_experts_routed_amd.build` "
+            "(the layer has no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sigs = {
+        "moe_abi_version": ([], i32),
+        "moe_strerror": ([i32], ctypes.c_char_p),
+        "moe_workspace_size": ([i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
+        "moe_workspace_layout": ([i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
+        "moe_routing_plan": ([vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_experts_prefill": ([vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_decode": ([vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    """Names of the C entry points this binding uses."""
+    return ["moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
+            "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
+            "moe_quantize_fp8_block128"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {moe_strerror(status)} (status {status})")
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise MoeError(rc, where)
+
+
+def moe_abi_version():
+    return _load().moe_abi_version()
+
+
+def moe_strerror(status):
+    return _load().moe_strerror(int(status)).decode()
+
+
+def moe_workspace_size(variant, T, H, F, E, k):
+    n = ctypes.c_size_t(0)
+    _check(_load().moe_workspace_size(variant, T, H, F, E, k, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def moe_workspace_layout(variant, T, H, F, E, k):
+    """Byte offsets of the workspace stages (counts, offsets, perm, inv, h,
+    h scales, y, total); None where a variant has no such stage."""
+    arr = (ctypes.c_size_t * 8)()
+    _check(_load().moe_workspace_layout(variant, T, H, F, E, k, arr), "moe_workspace_layout")
+    none = ctypes.c_size_t(-1).value
+    names = ["counts", "offsets", "perm", "inv", "h", "h_scale", "y", "total"]
+    return {n: (None if v == none else int(v)) for n, v in zip(names, arr)}
+
+
+# ------------------------------------------------------------ workspace cache
+_ws_cache = {}
+
+
+def _workspace(nbytes, device, stream):
+    """Per (device, stream) workspace that only grows; work on one stream is
+    ordered, so consecutive calls on it may share the buffer."""
+    key = (device.index, stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out(out, T, H, dev):
+    if out is None:
+        return torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2, dev)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H]")
+    return out
+
+
+def _bf16_call(entry, variant, hidden_states, gate_up_proj, down_proj, top_k_index,
+               top_k_weights, top_k, workspace=None, out=None):
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(gate_up_proj, "gate_up_proj", torch.bfloat16, 3, dev)
+    _need(down_proj, "down_proj", torch.bfloat16, 3, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = hidden_states.shape
+    E, F2, H2 = gate_up_proj.shape
+    F = F2 // 2
+    k = int(top_k)
+    if H2 != H or F2 != 2 * F or tuple(down_proj.shape) != (E, H, F):
+        raise ValueError("expected gate_up_proj [E,2F,H] and down_proj [E,H,F] matching hidden_states [T,H]")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size(variant, T, H, F, E, k)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        rc = getattr(_load(), entry)(_ptr(hidden_states), _ptr(gate_up_proj), _ptr(down_proj),
+                                     _ptr(top_k_index), _ptr(top_k_weights), T, H, F, E, k,
+                                     _ptr(out), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, entry)
+    return out
+
+
+def moe_experts_prefill(hidden_states, gate_up_proj, down_proj, top_k_index, top_k_weights,
+                        top_k, workspace=None, out=None):
+    """Routed experts, grouped-GEMM form; returns out [T, H] bf16."""
+    return _bf16_call("moe_experts_prefill", MOE_VARIANT_PREFILL, hidden_states, gate_up_proj,
+                      down_proj, top_k_index, top_k_weights, top_k, workspace, out)
+
+
+def moe_experts_decode(hidden_states, gate_up_proj, down_proj, top_k_index, top_k_weights,
+                       top_k, workspace=None, out=None):
+    """Routed experts, gather-GEMV form for T <= 4 (grouped form above);
+    returns out [T, H] bf16."""
+    return _bf16_call("moe_experts_decode", MOE_VARIANT_DECODE, hidden_states, gate_up_proj,
+                      down_proj, top_k_index, top_k_weights, top_k, workspace, out)
+
+
+def moe_experts_fp8(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                    top_k_weights, top_k, workspace=None, out=None):
+    """FP8 block-scaled routed experts.  fp8 operands are uint8 tensors of
+    E4M3FN codes (or torch.float8_e4m3fn tensors); returns out [T, H] bf16."""
+    def codes(t):
+        return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+    x, gate_up, down = codes(x), codes(gate_up), codes(down)
+    dev = x.device
+    _need(x, "x", torch.uint8, 2)
+    _need(x_scale, "x_scale", torch.float32, 2, dev)
+    _need(gate_up, "gate_up", torch.uint8, 3, dev)
+    _need(gate_up_scale, "gate_up_scale", torch.float32, 3, dev)
+    _need(down, "down", torch.uint8, 3, dev)
+    _need(down_scale, "down_scale", torch.float32, 3, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = x.shape
+    E, F2, H2 = gate_up.shape
+    F = F2 // 2
+    k = int(top_k)
+    if (H2 != H or F2 != 2 * F or tuple(down.shape) != (E, H, F)
+            or tuple(x_scale.shape) != (T, H // 128)
+            or tuple(gate_up_scale.shape) != (E, 2 * F, H // 128)
+            or tuple(down_scale.shape) != (E, H, F // 128)):
+        raise ValueError("fp8 operand shapes do not match [T,H], [E,2F,H], [E,H,F] with per-128 scales")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size(MOE_VARIANT_FP8, T, H, F, E, k)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        rc = _load().moe_experts_fp8(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
+                                     _ptr(down), _ptr(down_scale), _ptr(top_k_index),
+                                     _ptr(top_k_weights), T, H, F, E, k, _ptr(out), _ptr(ws),
+                                     ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, "moe_experts_fp8")
+    return out
+
+
+def moe_routing_plan(top_k_index, num_experts):
+    """(counts[E], offsets[E+1], perm[T*k], inv[T*k]) as int32 device tensors."""
+    dev = top_k_index.device
+    _need(top_k_index, "top_k_index", torch.int32, 2)
+    T, k = top_k_index.shape
+    E = int(num_experts)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size(MOE_VARIANT_PLAN, T, 0, 0, E, k)
+        ws = _workspace(need, dev, stream)
+        rc = _load().moe_routing_plan(_ptr(top_k_index), T, k, E, _ptr(counts), _ptr(offsets),
+                                      _ptr(perm), _ptr(inv), _ptr(ws), ws.numel(),
+                                      ctypes.c_void_p(stream))
+    _check(rc, "moe_routing_plan")
+    return counts, offsets, perm, inv
+
+
+def moe_quantize_fp8_block128(t):
+    """fp32 or bf16 [rows, K] -> (codes uint8 [rows, K], scales fp32 [rows, K/128])."""
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("input must be float32 or bfloat16")
+    _need(t, "input", t.dtype, 2)
+    rows, K = t.shape
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=t.device)
+    scales = torch.empty(rows, max(K // 128, 0), dtype=torch.float32, device=t.device)
+    with torch.cuda.device(t.device):
+        rc = _load().moe_quantize_fp8_block128(_ptr(t), int(t.dtype == torch.bfloat16), rows, K,
+                                               _ptr(codes), _ptr(scales),
+                                               ctypes.c_void_p(_stream(t.device)))
+    _check(rc, "moe_quantize_fp8_block128")
+    return codes, scales
+
+
+__all__ = [
+    "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
+    "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
+    "moe_quantize_fp8_block128", "MoeError", "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE",
+    "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "LIB_PATH",
+]

@@ -1,0 +1,296 @@
+// moe_api.hip - C ABI of the routed-experts layer: argument checks, the
+// workspace layout and the launch sequence of each entry point.  Every entry
+// point validates on the host, then only enqueues kernels on the caller's
+// stream (no allocation, no synchronisation, no host<->device copies).
+#include <string.h>
+
+#include <atomic>
+
+#include "moe_internal.h"
+#include "../../include/moe_experts.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- device info
+// Read-only per-device facts, filled once per device on first use.
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu[kMaxDevices];      // 0 = unknown
+std::atomic<int> g_is950[kMaxDevices];   // 0 = unknown, 1 = yes, 2 = no
+
+int query_device(int* dev_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+    if (g_is950[dev].load(std::memory_order_acquire) == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+        g_cu[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_is950[dev].store(ok ? 1 : 2, std::memory_order_release);
+    }
+    *dev_out = dev;
+    return g_is950[dev].load(std::memory_order_acquire) == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    const int n = g_cu[dev].load(std::memory_order_relaxed);
+    return n > 0 ? n : 256;
+}
+
+// ---------------------------------------------------------------- layout
+namespace {
+constexpr size_t kNone = (size_t)-1;
+
+struct Layout {
+    size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
+           ntiles = kNone, h = kNone, hs = kNone, y = kNone, total = 0;
+    bool decode_fast = false;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool decode_fast_path(int64_t T, int F, int k) {
+    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && F <= 2048;
+}
+
+Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
+    Layout L;
+    const int64_t P = T * k;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + (bytes ? bytes : 1));
+        return at;
+    };
+    if (variant == MOE_VARIANT_DECODE && decode_fast_path(T, F, k)) {
+        L.decode_fast = true;
+        L.h = take((size_t)P * F * sizeof(float));
+        L.total = off;
+        return L;
+    }
+    if (variant == MOE_VARIANT_PLAN) {
+        L.tiles = take((size_t)max_m_tiles(P, E) * 2 * sizeof(int32_t));
+        L.ntiles = take(sizeof(int32_t));
+        L.total = off;
+        return L;
+    }
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.perm = take((size_t)P * 4);
+    L.inv = take((size_t)P * 4);
+    L.tiles = take((size_t)max_m_tiles(P, E) * 2 * sizeof(int32_t));
+    L.ntiles = take(sizeof(int32_t));
+    if (variant == MOE_VARIANT_FP8) {
+        L.h = take((size_t)P * F);
+        L.hs = take((size_t)P * (F / 128) * sizeof(float));
+    } else {
+        L.h = take((size_t)P * F * 2);
+    }
+    L.y = take((size_t)P * H * 2);
+    L.total = off;
+    return L;
+}
+
+int check_shape(int variant, int64_t T, int H, int F, int E, int k) {
+    if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_PLAN) return MOE_ERR_SHAPE;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_ERR_SHAPE;
+    if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+    if (variant == MOE_VARIANT_PLAN) return MOE_OK;
+    const int mult = variant == MOE_VARIANT_FP8 ? 128 : 64;
+    if (H < mult || F < mult || H % mult || F % mult) return MOE_ERR_SHAPE;
+    if ((int64_t)E * 2 * F * (int64_t)H >= ((int64_t)1 << 47)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T>
+T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+int check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// Routing plan into the workspace, then the two grouped bf16 products and the combine.
+int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* gate_up,
+                     const uint16_t* down, const int32_t* idx, const float* w, int64_t T, int H,
+                     int F, int E, int k, uint16_t* out, void* ws, hipStream_t s) {
+    const int P = (int)(T * k);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* tiles = at<int32_t>(ws, L.tiles);
+    int32_t* ntiles = at<int32_t>(ws, L.ntiles);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    const int64_t mt = max_m_tiles(P, E);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), offsets, perm,
+                                  at<int32_t>(ws, L.inv), tiles, ntiles, s));
+    if (rc) return rc;
+    rc = launched(launch_gateup_bf16(hidden, gate_up, perm, tiles, ntiles, offsets, mt, H, F, k, h, s));
+    if (rc) return rc;
+    rc = launched(launch_down_bf16(h, down, perm, tiles, ntiles, offsets, mt, H, F, y, s));
+    if (rc) return rc;
+    return launched(launch_combine(y, idx, w, T, k, E, H, out, s));
+}
+
+int check_bf16_args(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+                    const int32_t* idx, const float* w, uint16_t* out) {
+    if (!hidden || !gate_up || !down || !idx || !w || !out) return MOE_ERR_NULL;
+    if (!aligned16(hidden) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
+        ((uintptr_t)idx & 3u) || ((uintptr_t)w & 3u))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer argument is NULL";
+        case MOE_ERR_SHAPE: return "a size argument is outside the supported range";
+        case MOE_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "workspace is NULL, not 256-byte aligned, or too small";
+        case MOE_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case MOE_ERR_DEVICE: return "the current HIP device is not a gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_t* bytes) {
+    if (!bytes) return MOE_ERR_NULL;
+    const int rc = check_shape(variant, T, H, F, E, k);
+    if (rc) return rc;
+    *bytes = make_layout(variant, T, H, F, E, k).total;
+    return MOE_OK;
+}
+
+int moe_workspace_layout(int variant, int64_t T, int H, int F, int E, int k, size_t offs[8]) {
+    if (!offs) return MOE_ERR_NULL;
+    const int rc = check_shape(variant, T, H, F, E, k);
+    if (rc) return rc;
+    const Layout L = make_layout(variant, T, H, F, E, k);
+    offs[0] = L.counts; offs[1] = L.offsets; offs[2] = L.perm; offs[3] = L.inv;
+    offs[4] = L.h; offs[5] = L.hs; offs[6] = L.y; offs[7] = L.total;
+    return MOE_OK;
+}
+
+int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+    if (!top_k_index || !counts || !offsets || !perm || !inv) return MOE_ERR_NULL;
+    int rc = check_shape(MOE_VARIANT_PLAN, T, 0, 0, E, k);
+    if (rc) return rc;
+    if (((uintptr_t)top_k_index | (uintptr_t)counts | (uintptr_t)offsets | (uintptr_t)perm |
+         (uintptr_t)inv) & 3u)
+        return MOE_ERR_ALIGN;
+    const Layout L = make_layout(MOE_VARIANT_PLAN, T, 0, 0, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    return launched(launch_plan(top_k_index, (int)(T * k), E, counts, offsets, perm, inv,
+                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles), stream));
+}
+
+int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+                        const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H,
+                        int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, out);
+    if (rc) return rc;
+    if ((rc = check_shape(MOE_VARIANT_PREFILL, T, H, F, E, k))) return rc;
+    const Layout L = make_layout(MOE_VARIANT_PREFILL, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, T, H, F, E, k,
+                            out, ws, stream);
+}
+
+int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+                       const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H,
+                       int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, out);
+    if (rc) return rc;
+    if ((rc = check_shape(MOE_VARIANT_DECODE, T, H, F, E, k))) return rc;
+    const Layout L = make_layout(MOE_VARIANT_DECODE, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    if (!L.decode_fast)
+        return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, T, H, F, E,
+                                k, out, ws, stream);
+    return launched(launch_decode(hidden, gate_up, down, top_k_index, top_k_weights, (int)T, k, E,
+                                  H, F, at<float>(ws, L.h), out, stream));
+}
+
+int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
+                    const float* gate_up_scale, const uint8_t* down, const float* down_scale,
+                    const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H, int F,
+                    int E, int k, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !x_scale || !gate_up || !gate_up_scale || !down || !down_scale || !top_k_index ||
+        !top_k_weights || !out)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
+        (((uintptr_t)x_scale | (uintptr_t)gate_up_scale | (uintptr_t)down_scale |
+          (uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
+        return MOE_ERR_ALIGN;
+    int rc = check_shape(MOE_VARIANT_FP8, T, H, F, E, k);
+    if (rc) return rc;
+    const Layout L = make_layout(MOE_VARIANT_FP8, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    const int P = (int)(T * k);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* tiles = at<int32_t>(ws, L.tiles);
+    int32_t* ntiles = at<int32_t>(ws, L.ntiles);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    const int64_t mt = max_m_tiles(P, E);
+    uint8_t* hq = at<uint8_t>(ws, L.h);
+    float* hs = at<float>(ws, L.hs);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts), offsets, perm,
+                              at<int32_t>(ws, L.inv), tiles, ntiles, stream));
+    if (rc) return rc;
+    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, perm, tiles, ntiles, offsets,
+                                    mt, H, F, k, hq, hs, stream));
+    if (rc) return rc;
+    rc = launched(launch_down_fp8(hq, hs, down, down_scale, perm, tiles, ntiles, offsets, mt, H, F,
+                                  y, stream));
+    if (rc) return rc;
+    return launched(launch_combine(y, top_k_index, top_k_weights, T, k, E, H, out, stream));
+}
+
+int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
+                              float* scales, hipStream_t stream) {
+    if (!in || !codes || !scales) return MOE_ERR_NULL;
+    if (rows < 0 || K < 128 || K % 128 || rows * (int64_t)(K / 128) * 32 >= ((int64_t)1 << 31))
+        return MOE_ERR_SHAPE;
+    if (((uintptr_t)in | (uintptr_t)scales) & 3u) return MOE_ERR_ALIGN;
+    int dev, rc;
+    if ((rc = query_device(&dev))) return rc;
+    if (rows == 0) return MOE_OK;
+    return launched(launch_quantize_fp8(in, in_is_bf16, rows, K, codes, scales, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// moe_device.h - device-side helpers shared by the gfx950 kernels of the
+// routed-experts layer (internal header, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- vectors
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin over them
+
+// 16-byte load that marks the line as streamed once (weights read a single time).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even; inputs on this path are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Unpack 8 bf16 (one 16-byte chunk) into fp32.
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+// fp32 -> OCP E4M3FN with round to nearest even (gfx950 hardware convert).
+// Callers clamp to +-448 first, so saturation behaviour never matters.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float half_sum32(float v) {  // sum within each 32-lane half
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float half_max32(float v) {  // max within each 32-lane half
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// ------------------------------------------------------------------ MFMA
+// 32x32x16 bf16 -> fp32.  Lane l supplies row/col (l % 32) and K elements
+// [8*(l/32), 8*(l/32)+8); accumulator register r of lane l holds element
+// (row = 8*(r/4) + 4*(l/32) + r%4, col = l % 32).
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const uint4 a, const uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 32x32x64 fp8(e4m3) x fp8(e4m3) -> fp32 with unit E8M0 block scales
+// (127 encodes 2^0): lane l supplies 32 K bytes of row/col (l % 32).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 a, const i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// ------------------------------------------------------- scheduling helpers
+// Persistent grids walk work items i = round * G + slot.  Workgroup b runs on
+// XCD b % 8; giving each XCD a contiguous run of slots keeps work items that
+// share a weight panel (neighbouring M tiles of one expert) inside one L2.
+__device__ __forceinline__ int xcd_slot(int b, int G) {
+    const int per = G / kXcds;  // G is a multiple of 8
+    return (b % kXcds) * per + (b / kXcds);
+}
+
+}  // namespace moe

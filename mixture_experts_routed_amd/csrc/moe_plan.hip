@@ -1,0 +1,142 @@
+// moe_plan.hip - deterministic routing plan (expert histogram, exclusive
+// prefix, stable scatter) for the grouped products of the routed-experts
+// layer.  The model card "DeepSeek-OCR-2 MoE experts" describes its prefill
+// op as a grouped GEMM over experts; the mirage issue "Supporting MegaKernel
+// for DeepSeek Models" passes the per-expert prefix as an [E+1] int32 tensor
+// (moe_w13_fp8_layer "masks").  Slots s = t*k + j are ordered by expert with
+// ties in ascending s; ids outside [0,E) are dropped.
+#include "moe_device.h"
+#include "moe_internal.h"
+#include "../../include/moe_experts.h"
+
+namespace moe {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+
+// One workgroup.  Wave w owns a contiguous, 64-aligned run of slots, so the
+// order (wave, position in run) is the slot order.  Pass 1 counts per
+// (wave, expert) with LDS integer atomics (exact, order-free).  Each expert's
+// per-wave counts then become running bases, and pass 2 walks the slots again
+// in order: lanes with the same expert in one 64-slot step find each other
+// with ballots on the id bits and take consecutive positions by lane rank.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int32_t* __restrict__ idx, int P, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    __shared__ int base[kPlanWaves][MOE_MAX_EXPERTS];
+    __shared__ int tot[MOE_MAX_EXPERTS];
+    __shared__ int off_sh[MOE_MAX_EXPERTS + 1];
+    __shared__ int tile_sh[MOE_MAX_EXPERTS + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kPlanWaves * MOE_MAX_EXPERTS; i += kPlanThreads) (&base[0][0])[i] = 0;
+    __syncthreads();
+
+    const int run = ((P + kPlanWaves * kWave - 1) / (kPlanWaves * kWave)) * kWave;
+    const int s0 = wave * run;
+    const int s1 = min(P, s0 + run);
+
+    for (int s = s0 + lane; s < s1; s += kWave) {
+        const int e = idx[s];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&base[wave][e], 1);
+    }
+    __syncthreads();
+
+    for (int e = tid; e < E; e += kPlanThreads) {
+        int acc = 0;
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const int c = base[w][e];
+            base[w][e] = acc;
+            acc += c;
+        }
+        tot[e] = acc;
+    }
+    __syncthreads();
+
+    if (wave == 0) {  // exclusive prefix of counts and of M tiles over experts
+        const int per = (E + kWave - 1) / kWave;
+        const int e0 = lane * per;
+        int c_sum = 0, t_sum = 0;
+        for (int i = 0; i < per; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                c_sum += tot[e];
+                t_sum += (tot[e] + kTileM - 1) / kTileM;
+            }
+        }
+        int c_inc = c_sum, t_inc = t_sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int cu = __shfl_up(c_inc, o, kWave);
+            const int tu = __shfl_up(t_inc, o, kWave);
+            if (lane >= o) { c_inc += cu; t_inc += tu; }
+        }
+        int c_run = c_inc - c_sum, t_run = t_inc - t_sum;
+        for (int i = 0; i < per; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                off_sh[e] = c_run;
+                tile_sh[e] = t_run;
+                c_run += tot[e];
+                t_run += (tot[e] + kTileM - 1) / kTileM;
+            }
+        }
+        if (lane == kWave - 1) {
+            off_sh[E] = c_inc;
+            tile_sh[E] = t_inc;
+        }
+    }
+    __syncthreads();
+
+    for (int e = tid; e <= E; e += kPlanThreads) {
+        offsets[e] = off_sh[e];
+        if (e < E) {
+            counts[e] = tot[e];
+            const int nt = tile_sh[e + 1] - tile_sh[e];
+            for (int i = 0; i < nt; ++i) {
+                tiles[2 * (tile_sh[e] + i)] = e;
+                tiles[2 * (tile_sh[e] + i) + 1] = off_sh[e] + i * kTileM;
+            }
+        }
+    }
+    if (tid == 0) *ntiles = tile_sh[E];
+
+    // pass 2: stable scatter; each wave only touches its own row of `base`
+    for (int sb = s0; sb < s1; sb += kWave) {
+        const int s = sb + lane;
+        const int e = (s < s1) ? idx[s] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        uint64_t same = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t set = __ballot(bit);
+            same &= bit ? set : ~set;
+        }
+        int rank = 0, pos = -1;
+        if (valid) {
+            rank = __popcll(same & ((1ull << lane) - 1ull));
+            pos = off_sh[e] + base[wave][e] + rank;
+            perm[pos] = s;
+        }
+        if (s < s1) inv[s] = pos;
+        // every lane has read base[wave][*] above before the group leader
+        // bumps it (LDS operations of one wave complete in issue order)
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == 0) base[wave][e] += __popcll(same);
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int i = off_sh[E] + tid; i < P; i += kPlanThreads) perm[i] = -1;
+}
+
+hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
+                       hipStream_t s) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, nbits, counts,
+                       offsets, perm, inv, tiles, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI library (no GPU needed, no kernel launched).
+
+The library must load, export every function declared in
+include/moe_experts.h, size and lay out workspaces, and reject bad arguments
+with the documented status codes before touching the GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mixture_experts_routed_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_experts.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                                reason="libmoe_experts.so not built (run __graft_entry__.build())")
+
+OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV = 0, -1, -2, -3, -4, -5, -6
+P16 = 0x10000          # fake, 16-byte-aligned "device" addresses: only used where
+P16B = 0x20000         # validation must fail before anything is enqueued
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ["moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8", "moe_routing_plan",
+              "moe_workspace_size", "moe_quantize_fp8_block128"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert sorted(moe.exported_symbols()) == declared_functions()
+
+
+def test_version_and_strerror():
+    assert moe.moe_abi_version() == 1
+    for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
+        s = moe.moe_strerror(rc)
+        assert isinstance(s, str) and s
+    assert moe.moe_strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_workspace_sizes_and_layout(variant):
+    T, H, F, E, k = 2048, 1280, 896, 64, 6
+    if variant == 2:
+        T, H, F, E, k = 4096, 7168, 2048, 128, 8
+    n = moe.moe_workspace_size(variant, T, H, F, E, k)
+    lay = moe.moe_workspace_layout(variant, T, H, F, E, k)
+    assert lay["total"] == n
+    offs = [v for key, v in lay.items() if key != "total" and v is not None]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and len(set(offs)) == len(offs) and max(offs) < n
+    P = T * k
+    assert n >= P * H * 2                                   # y [P, H] bf16
+    if variant == 2:
+        assert lay["h_scale"] - lay["h"] >= P * F           # fp8 codes
+        assert n - lay["y"] >= P * H * 2
+
+
+def test_decode_fast_path_workspace_is_small():
+    n1 = moe.moe_workspace_size(1, 1, 1280, 896, 64, 6)
+    lay = moe.moe_workspace_layout(1, 4, 1280, 896, 64, 6)
+    assert n1 >= 6 * 896 * 4 and n1 < 1 << 20
+    assert lay["perm"] is None and lay["h"] == 0
+    # above the fast path the decode entry uses the grouped layout
+    assert moe.moe_workspace_layout(1, 64, 1280, 896, 64, 6)["perm"] is not None
+
+
+@pytest.mark.parametrize("args", [
+    (0, -1, 128, 64, 8, 2),      # T < 0
+    (0, 4, 100, 64, 8, 2),       # H not a multiple of 64
+    (0, 4, 128, 96, 8, 2),       # F not a multiple of 64
+    (0, 4, 128, 64, 8, 9),       # k > E
+    (0, 4, 128, 64, 0, 1),       # E < 1
+    (0, 4, 128, 64, 513, 2),     # E above MOE_MAX_EXPERTS
+    (2, 4, 192, 128, 8, 2),      # fp8 H not a multiple of 128
+    (2, 4, 256, 64, 8, 2),       # fp8 F not a multiple of 128
+    (7, 4, 128, 64, 8, 2),       # unknown variant
+    (0, 1 << 30, 128, 64, 8, 4),  # T*k >= 2^31
+])
+def test_workspace_size_rejects_bad_shapes(args):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(*args)
+    assert ei.value.status == ESHAPE
+
+
+def test_null_out_pointer_status():
+    lib = moe._load()
+    assert lib.moe_workspace_size(0, 4, 128, 64, 8, 2, None) == ENULL
+
+
+def _prefill(lib, fn, *, hidden=P16, gu=P16, dn=P16, idx=P16, w=P16, out=P16, T=4, H=128, F=64,
+             E=8, k=2, ws=P16B, ws_bytes=1 << 30):
+    return getattr(lib, fn)(hidden, gu, dn, idx, w, T, H, F, E, k, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["moe_experts_prefill", "moe_experts_decode"])
+def test_bf16_entry_validation(fn):
+    lib = moe._load()
+    assert _prefill(lib, fn, hidden=None) == ENULL
+    assert _prefill(lib, fn, out=None) == ENULL
+    assert _prefill(lib, fn, gu=P16 + 2) == EALIGN
+    assert _prefill(lib, fn, idx=P16 + 2) == EALIGN
+    assert _prefill(lib, fn, k=9) == ESHAPE
+    assert _prefill(lib, fn, H=96) == ESHAPE
+    assert _prefill(lib, fn, ws=None) == EWS
+    assert _prefill(lib, fn, ws=P16B + 16) == EWS          # not 256-byte aligned
+    assert _prefill(lib, fn, ws_bytes=16) == EWS
+
+
+def test_fp8_and_plan_validation():
+    lib = moe._load()
+    args = [P16] * 8 + [4, 256, 128, 8, 2, P16, P16B, 1 << 30, None]
+    bad = list(args); bad[1] = None
+    assert lib.moe_experts_fp8(*bad) == ENULL
+    bad = list(args); bad[2] = P16 + 8
+    assert lib.moe_experts_fp8(*bad) == EALIGN
+    bad = list(args); bad[9] = 192
+    assert lib.moe_experts_fp8(*bad) == ESHAPE
+    bad = list(args); bad[15] = 0
+    assert lib.moe_experts_fp8(*bad) == EWS
+    assert lib.moe_routing_plan(None, 4, 2, 8, P16, P16, P16, P16, P16B, 1 << 20, None) == ENULL
+    assert lib.moe_routing_plan(P16, 4, 9, 8, P16, P16, P16, P16, P16B, 1 << 20, None) == ESHAPE
+    assert lib.moe_routing_plan(P16, 4, 2, 8, P16, P16, P16, P16, P16B, 1, None) == EWS
+    assert lib.moe_quantize_fp8_block128(P16, 0, 4, 100, P16, P16, None) == ESHAPE
+    assert lib.moe_quantize_fp8_block128(None, 0, 4, 128, P16, P16, None) == ENULL
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")
+def test_valid_arguments_without_gpu_report_device_error():
+    lib = moe._load()
+    assert _prefill(lib, "moe_experts_prefill") == EDEV
+    assert _prefill(lib, "moe_experts_decode") == EDEV
+
+
+def test_python_binding_rejects_cpu_tensors():
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    gu = torch.zeros(8, 128, 128, dtype=torch.bfloat16)
+    dn = torch.zeros(8, 128, 64, dtype=torch.bfloat16)
+    idx = torch.zeros(4, 2, dtype=torch.int32)
+    w = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        moe.moe_experts_prefill(x, gu, dn, idx, w, 2)
+    with pytest.raises(TypeError):
+        moe.moe_experts_prefill(x.float(), gu, dn, idx, w, 2)

@@ -1,0 +1,417 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: the routing plan is bit-exact; bf16 outputs satisfy
+|gpu - ref| <= 1e-2 + 1e-2 |ref| per element, fp8 outputs
+|gpu - ref| <= 3e-2 + 3e-2 |ref|, against the float64 oracle fed the same
+seeded inputs (the fp8 oracle dequantises the same codes and re-quantises h
+in fp32 as the method does).
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = (1e-2, 1e-2)
+FP8_TOL = (3e-2, 3e-2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_routed_amd as moe  # noqa: F401  (fails loudly if the library is missing)
+    moe._load()
+    yield
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _moe():
+    import mixture_experts_routed_amd as moe
+    return moe
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_tol(gpu, ref, tol, what=""):
+    atol, rtol = tol
+    g = f64(gpu)
+    err = np.abs(g - ref)
+    bound = atol + rtol * np.abs(ref)
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    rel_l2 = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    assert worst <= 1.0, f"{what}: worst err/tol {worst:.3f}, rel L2 {rel_l2:.2e}"
+    return worst, rel_l2
+
+
+def bf16_problem(T, H, F, E, k, seed, idx=None, std=0.02):
+    p = wl.make_bf16_problem(T, H, F, E, k, seed, "cpu", weight_std=std)
+    if idx is not None:
+        p["top_k_index"] = torch.as_tensor(idx, dtype=torch.int32).contiguous()
+    return p
+
+
+def bf16_ref(p, batched=True):
+    fn = orc.moe_experts_reference_batched if batched else orc.moe_experts_reference
+    return fn(f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]), p["top_k_index"].numpy(),
+              f64(p["top_k_weights"]))
+
+
+def to_gpu(p):
+    return {n: v.cuda() for n, v in p.items()}
+
+
+def run_bf16(entry, g, out=None):
+    moe = _moe()
+    fn = getattr(moe, entry)
+    return fn(g["hidden"], g["gate_up"], g["down"], g["top_k_index"], g["top_k_weights"],
+              g["top_k_index"].shape[1], out=out)
+
+
+# ------------------------------------------------------------------ plan
+
+
+def _plan_case(idx, E):
+    moe = _moe()
+    idx = torch.as_tensor(idx, dtype=torch.int32)
+    got = [t.cpu().numpy() for t in moe.moe_routing_plan(idx.cuda(), E)]
+    ref = orc.routing_plan(idx.numpy(), E)
+    for name, a, b in zip(("counts", "offsets", "perm", "inv"), got, ref):
+        assert np.array_equal(a, b), f"plan {name} differs"
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_plan_bit_exact_on_workloads(name):
+    c = wl.CONFIGS[name]
+    _say(f"plan {name}")
+    g = wl._gen(c.get("act_seed", c["seed"]), "cpu")
+    if c["routing"] == "zipf":
+        idx, _ = wl.route_zipf(c["T"], c["E"], c["k"], g, "cpu", c["zipf_s"], c["zipf_zero"])
+    elif c["routing"] == "sigmoid_topk":
+        idx, _ = wl.route_sigmoid_topk(c["T"], c["E"], c["k"], g)
+    else:
+        idx, _ = wl.route_uniform_softmax(c["T"], c["E"], c["k"], g)
+    _plan_case(idx, c["E"])
+
+
+def test_plan_edge_cases():
+    rng = np.random.default_rng(7)
+    _say("plan edge cases")
+    _plan_case(np.zeros((1, 1), np.int32), 1)                         # T=1, E=1
+    _plan_case(np.full((700, 1), 3, np.int32), 8)                    # all to one expert
+    _plan_case(rng.integers(-3, 11, (333, 4)).astype(np.int32), 8)   # dropped ids both sides
+    _plan_case(rng.integers(0, 4, (50, 4)).astype(np.int32), 4)      # duplicates inside tokens
+    _plan_case(np.full((5, 3), -1, np.int32), 16)                    # everything dropped
+    _plan_case(np.stack([rng.permutation(512)[:8] for _ in range(600)]).astype(np.int32), 512)
+    _plan_case(np.tile(np.arange(6, dtype=np.int32), (9, 1)), 6)    # k == E
+    _plan_case(rng.integers(0, 128, (40000, 1)).astype(np.int32), 128)  # long run per wave
+
+
+# ------------------------------------------------------------- bf16 layer
+
+
+@pytest.mark.parametrize("entry", ["moe_experts_prefill", "moe_experts_decode"])
+def test_tiny_config(entry):
+    _say(f"tiny {entry}")
+    p = wl.make_config("tiny")
+    ref = bf16_ref(p, batched=False)
+    out = run_bf16(entry, to_gpu(p))
+    check_tol(out, ref, BF16_TOL, f"tiny/{entry}")
+    # outputs of the tiny config are below atol; also require a small relative L2 error
+    rel = np.linalg.norm(f64(out) - ref) / np.linalg.norm(ref)
+    assert rel < 1e-2, rel
+
+
+def test_tiny_scaled_twin():
+    """Tiny shapes with weights ~N(0, 1/sqrt(H)) so that outputs are O(1)."""
+    _say("tiny scaled twin")
+    p = bf16_problem(16, 128, 64, 8, 2, 1001, std=1 / np.sqrt(128))
+    ref = bf16_ref(p, batched=False)
+    for entry in ("moe_experts_prefill", "moe_experts_decode"):
+        check_tol(run_bf16(entry, to_gpu(p)), ref, BF16_TOL, entry)
+
+
+@pytest.mark.parametrize("shape", [
+    (700, 384, 320, 6, 2),     # several M tiles per expert and ragged tails
+    (257, 128, 64, 5, 3),      # one row past a tile
+    (96, 256, 192, 16, 4),     # many small experts, some empty
+    (300, 192, 128, 4, 4),     # k == E; H not a multiple of 128 (64-wide down tiles)
+])
+def test_prefill_medium(shape):
+    T, H, F, E, k = shape
+    _say(f"prefill medium {shape}")
+    p = bf16_problem(T, H, F, E, k, seed=11 + T, std=1 / np.sqrt(H))
+    ref = bf16_ref(p)
+    check_tol(run_bf16("moe_experts_prefill", to_gpu(p)), ref, BF16_TOL, str(shape))
+
+
+def test_prefill_edge_routing():
+    """All tokens to one expert, dropped ids (-1 and E), duplicates in a token, empty experts."""
+    _say("prefill edge routing")
+    T, H, F, E, k = 600, 128, 64, 6, 2
+    rng = np.random.default_rng(3)
+    cases = {
+        "one_expert": np.stack([np.full(T, 2), np.full(T, 2)], 1),
+        "dropped": np.where(rng.random((T, k)) < 0.2, rng.choice([-1, E], (T, k)), rng.integers(0, E, (T, k))),
+        "dups": np.stack([rng.integers(0, 3, T)] * 2, 1),
+    }
+    for name, idx in cases.items():
+        p = bf16_problem(T, H, F, E, k, seed=5, idx=idx.astype(np.int32), std=1 / np.sqrt(H))
+        ref = bf16_ref(p, batched=False)
+        for entry in ("moe_experts_prefill", "moe_experts_decode"):
+            check_tol(run_bf16(entry, to_gpu(p)), ref, BF16_TOL, f"{name}/{entry}")
+
+
+def test_prefill_full_config():
+    """T=2048, H=1280, F=896, E=64, top-6: every output element against the oracle."""
+    _say("prefill full config")
+    p = wl.make_config("ocr2_prefill")
+    g = to_gpu(p)
+    out = run_bf16("moe_experts_prefill", g)
+    torch.cuda.synchronize()
+    ref = bf16_ref(p)
+    worst, rel = check_tol(out, ref, BF16_TOL, "ocr2_prefill")
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("name", ["ocr2_decode_t1", "ocr2_decode_t4"])
+def test_decode_full_config(name):
+    _say(f"decode {name}")
+    p = wl.make_config(name)
+    ref = bf16_ref(p, batched=False)
+    g = to_gpu(p)
+    for entry in ("moe_experts_decode", "moe_experts_prefill"):
+        worst, rel = check_tol(run_bf16(entry, g), ref, BF16_TOL, f"{name}/{entry}")
+        _say(f"  {entry}: worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("shape", [(3, 128, 64, 8, 2), (4, 256, 1536, 6, 5), (2, 512, 2048, 3, 3),
+                                   (4, 128, 128, 40, 8), (7, 128, 64, 8, 2)])
+def test_decode_shapes(shape):
+    """Fast path for T <= 4 (every chunks-per-lane case), grouped path above."""
+    T, H, F, E, k = shape
+    _say(f"decode shape {shape}")
+    p = bf16_problem(T, H, F, E, k, seed=T + F, std=1 / np.sqrt(H))
+    ref = bf16_ref(p, batched=False)
+    check_tol(run_bf16("moe_experts_decode", to_gpu(p)), ref, BF16_TOL, str(shape))
+
+
+def test_stages_prefill():
+    """Layered check: h (bf16, expert order) and y (bf16, slot order) in the workspace."""
+    moe = _moe()
+    _say("prefill stages")
+    T, H, F, E, k = 300, 256, 128, 5, 2
+    p = bf16_problem(T, H, F, E, k, seed=9, std=1 / np.sqrt(H))
+    g = to_gpu(p)
+    lay = moe.moe_workspace_layout(0, T, H, F, E, k)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    moe.moe_experts_prefill(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                            g["top_k_weights"], k, workspace=ws)
+    torch.cuda.synchronize()
+    P = T * k
+    perm = ws[lay["perm"]:lay["perm"] + 4 * P].view(torch.int32).cpu().numpy()
+    h = ws[lay["h"]:lay["h"] + 2 * P * F].view(torch.bfloat16).view(P, F)
+    y = ws[lay["y"]:lay["y"] + 2 * P * H].view(torch.bfloat16).view(P, H)
+    x, w13, w2, idx = f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]), p["top_k_index"].numpy()
+    h_ref = np.zeros((P, F))
+    y_ref = np.zeros((P, H))
+    for m in range(P):
+        s = perm[m]
+        e = idx.reshape(-1)[s]
+        gv = w13[e] @ x[s // k]
+        h_ref[m] = orc.silu(gv[:F]) * gv[F:]
+        y_ref[s] = w2[e] @ h_ref[m]
+    check_tol(h, h_ref, (1e-2, 1e-2), "h stage")
+    check_tol(y, y_ref, (1e-2, 1e-2), "y stage")
+
+
+def test_out_fully_overwritten_and_deterministic():
+    _say("overwrite + determinism")
+    p = wl.make_config("ocr2_decode_t4")
+    g = to_gpu(p)
+    for entry in ("moe_experts_prefill", "moe_experts_decode"):
+        poison = torch.full((4, 1280), float("nan"), dtype=torch.bfloat16, device="cuda")
+        a = run_bf16(entry, g, out=poison).clone()
+        assert torch.isfinite(a.float()).all()
+        b = run_bf16(entry, g)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), entry
+    p = wl.make_config("ocr2_prefill")
+    g = to_gpu(p)
+    a = run_bf16("moe_experts_prefill", g).clone()
+    b = run_bf16("moe_experts_prefill", g)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_tokens_and_zero_weights():
+    _say("T=0 and zero weights")
+    moe = _moe()
+    p = bf16_problem(0, 128, 64, 4, 2, seed=1)
+    g = to_gpu(p)
+    assert run_bf16("moe_experts_prefill", g).shape == (0, 128)
+    p = bf16_problem(64, 128, 64, 4, 2, seed=1)
+    p["top_k_weights"] = torch.zeros_like(p["top_k_weights"])
+    g = to_gpu(p)
+    for entry in ("moe_experts_prefill", "moe_experts_decode"):
+        assert torch.count_nonzero(run_bf16(entry, g).float()) == 0
+    assert moe.moe_experts_decode(g["hidden"][:2], g["gate_up"], g["down"], g["top_k_index"][:2],
+                                  g["top_k_weights"][:2], 2).abs().sum() == 0
+
+
+# -------------------------------------------------------------- fp8 layer
+
+
+def fp8_ref(p, tokens=None):
+    return orc.moe_experts_fp8_reference(
+        p["x"].cpu().numpy(), p["x_scale"].cpu().numpy(), p["gate_up"], p["gate_up_scale"],
+        p["down"], p["down_scale"], p["top_k_index"].cpu().numpy(),
+        p["top_k_weights"].cpu().numpy(), tokens=tokens)
+
+
+def run_fp8(g, out=None):
+    moe = _moe()
+    return moe.moe_experts_fp8(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"],
+                               g["down_scale"], g["top_k_index"], g["top_k_weights"],
+                               g["top_k_index"].shape[1], out=out)
+
+
+class _HostExperts:
+    """Lazy host copies of a few experts of a device weight tensor."""
+
+    def __init__(self, t):
+        self.t, self.cache, self.shape = t, {}, tuple(t.shape)
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = self.t[e].cpu().numpy()
+        return self.cache[e]
+
+
+def _host_fp8(p):
+    q = dict(p)
+    for n in ("gate_up", "gate_up_scale", "down", "down_scale"):
+        q[n] = _HostExperts(p[n])
+    q["gate_up"].shape = tuple(p["gate_up"].shape)
+    return q
+
+
+@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2)])
+def test_fp8_medium(shape):
+    T, H, F, E, k = shape
+    _say(f"fp8 medium {shape}")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=31 + T, routing="uniform_softmax", routed_scale=1.0)
+    ref = fp8_ref({n: v.numpy() if n not in ("x", "x_scale", "top_k_index", "top_k_weights") else v
+                   for n, v in p.items()})
+    worst, rel = check_tol(run_fp8(to_gpu(p)), ref, FP8_TOL, str(shape))
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+def test_fp8_h_stage_codes():
+    """The re-quantised h in the workspace against the oracle's fp32 rule applied
+    to the oracle's h: scales within fp32 rounding, codes equal but for rare
+    one-step flips where the fp32 h of both sides straddles a rounding tie."""
+    moe = _moe()
+    _say("fp8 h stage")
+    T, H, F, E, k = 200, 256, 256, 4, 2
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=41, routing="uniform_softmax", routed_scale=1.0)
+    g = to_gpu(p)
+    lay = moe.moe_workspace_layout(2, T, H, F, E, k)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    moe.moe_experts_fp8(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"],
+                        g["down_scale"], g["top_k_index"], g["top_k_weights"], k, workspace=ws)
+    torch.cuda.synchronize()
+    P = T * k
+    perm = ws[lay["perm"]:lay["perm"] + 4 * P].view(torch.int32).cpu().numpy()
+    hq = ws[lay["h"]:lay["h"] + P * F].cpu().numpy().reshape(P, F)
+    hs = ws[lay["h_scale"]:lay["h_scale"] + 4 * P * (F // 128)].view(torch.float32).cpu().numpy().reshape(P, F // 128)
+    x = orc.dequantize_block128(p["x"].numpy(), p["x_scale"].numpy())
+    idx = p["top_k_index"].numpy().reshape(-1)
+    h_ref = np.zeros((P, F), np.float32)
+    for m in range(P):
+        s = perm[m]
+        e = idx[s]
+        W = orc.dequantize_block128(p["gate_up"][e].numpy(), p["gate_up_scale"][e].numpy())
+        gv = W @ x[s // k]
+        h_ref[m] = (orc.silu(gv[:F]) * gv[F:]).astype(np.float32)
+    q_ref, s_ref = orc.quantize_block128_fp32(h_ref)
+    np.testing.assert_allclose(hs, s_ref, rtol=1e-5)
+    diff = hq != q_ref
+    assert diff.mean() < 2e-3, diff.mean()
+    assert np.all(np.abs(hq[diff].astype(int) - q_ref[diff].astype(int)) <= 1)
+
+
+def test_quantizer_bit_exact():
+    """Stand-alone block-128 quantiser (same device routine as the fp8 epilogue)
+    against the oracle's rule on identical fp32 and bf16 inputs."""
+    moe = _moe()
+    _say("quantizer")
+    rng = np.random.default_rng(5)
+    h = (rng.standard_normal((333, 1024)) * np.exp(rng.uniform(-10, 6, (333, 1)))).astype(np.float32)
+    h[7, 256:384] = 0.0
+    h[8, :128] = -0.0
+    h[9, :128] = 1e-30
+    codes, scales = moe.moe_quantize_fp8_block128(torch.from_numpy(h).cuda())
+    q_ref, s_ref = orc.quantize_block128_fp32(h)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    hb = torch.from_numpy(h).to(torch.bfloat16)
+    codes, scales = moe.moe_quantize_fp8_block128(hb.cuda())
+    q_ref, s_ref = orc.quantize_block128_fp32(hb.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+
+
+def _sample_tokens(T, n, seed):
+    return np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
+
+
+@pytest.mark.parametrize("name,n_sample", [("v3_fp8_decode", 3), ("v3_fp8_prefill", 3)])
+def test_fp8_full_config_sampled(name, n_sample):
+    """Full DeepSeek-V3-shaped expert share; sampled output rows against the oracle."""
+    _say(f"fp8 full {name}")
+    p = wl.make_config(name, device="cuda")
+    out = run_fp8(p)
+    torch.cuda.synchronize()
+    idx = p["top_k_index"].cpu().numpy()
+    counts = np.bincount(idx.reshape(-1), minlength=128)
+    tokens = list(_sample_tokens(p["x"].shape[0], n_sample, 7))
+    hot = int(np.argmax(counts))
+    tokens.append(int(np.nonzero((idx == hot).any(1))[0][0]))       # a token of the hottest expert
+    tokens = sorted(set(tokens))
+    hp = _host_fp8(p)
+    ref = fp8_ref(hp, tokens=tokens)
+    worst, rel = check_tol(out[tokens], ref[tokens], FP8_TOL, name)
+    _say(f"  tokens {tokens}: worst err/tol {worst:.3f} rel L2 {rel:.2e}; "
+         f"max/mean load {counts.max() / counts.mean():.1f}, empty {(counts == 0).sum()}")
+    a = out.clone()
+    b = run_fp8(p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fp8 path not deterministic"
+
+
+def test_fp8_overwrite_and_dropped():
+    _say("fp8 overwrite + dropped")
+    T, H, F, E, k = 100, 256, 128, 4, 3
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=3, routing="uniform_softmax", routed_scale=1.0)
+    idx = p["top_k_index"].clone()
+    idx[::3, 1] = -1
+    idx[1::5, 2] = E
+    p["top_k_index"] = idx.contiguous()
+    ref = fp8_ref({n: v.numpy() if n not in ("x", "x_scale", "top_k_index", "top_k_weights") else v
+                   for n, v in p.items()})
+    g = to_gpu(p)
+    poison = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    check_tol(run_fp8(g, out=poison), ref, FP8_TOL, "fp8 dropped")
