@@ -322,8 +322,11 @@ def test_fp8_medium(shape):
 
 def test_fp8_h_stage_codes():
     """The re-quantised h in the workspace against the oracle's fp32 rule applied
-    to the oracle's h: scales within fp32 rounding, codes equal but for rare
-    one-step flips where the fp32 h of both sides straddles a rounding tie."""
+    to the oracle's h.  The kernel quantises its own fp32-accumulated h, which
+    differs from the oracle's float64 h by fp32 summation error (about 1e-5
+    relative), so scales agree to 1e-3 and codes agree except for rare
+    one-step flips at rounding boundaries.  Bit-exactness of the quantiser on
+    identical inputs is test_quantizer_bit_exact."""
     moe = _moe()
     _say("fp8 h stage")
     T, H, F, E, k = 200, 256, 256, 4, 2
@@ -348,10 +351,12 @@ def test_fp8_h_stage_codes():
         gv = W @ x[s // k]
         h_ref[m] = (orc.silu(gv[:F]) * gv[F:]).astype(np.float32)
     q_ref, s_ref = orc.quantize_block128_fp32(h_ref)
-    np.testing.assert_allclose(hs, s_ref, rtol=1e-5)
+    np.testing.assert_allclose(hs, s_ref, rtol=1e-3)
     diff = hq != q_ref
     assert diff.mean() < 2e-3, diff.mean()
-    assert np.all(np.abs(hq[diff].astype(int) - q_ref[diff].astype(int)) <= 1)
+    a, b = orc.e4m3fn_decode(hq[diff]), orc.e4m3fn_decode(q_ref[diff])
+    # one e4m3 step apart (a sign flip of a value that rounds to zero is no step)
+    assert np.all(np.abs(a - b) <= np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -3 + 2.0 ** -9)
 
 
 def test_quantizer_bit_exact():
