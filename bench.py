@@ -38,7 +38,25 @@ def parse():
     ap.add_argument("--sets", type=int, default=None, help="weight copies rotated over steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (calibrates HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of a known size: under rocprofv3 --pmc its FETCH_SIZE and
+    WRITE_SIZE per dispatch give the counters' scale (expect 262144 KiB each)."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        flush.fill_(0)            # evict src/dst from the 256 MB last-level cache
+        torch.cuda.synchronize()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
 def algorithmic_bytes(kind, T, H, F, k, touched):
@@ -59,6 +77,9 @@ def algorithmic_flops(valid_slots, H, F):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))

@@ -46,14 +46,14 @@ constexpr size_t kNone = (size_t)-1;
 
 struct Layout {
     size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
-           ntiles = kNone, h = kNone, hs = kNone, y = kNone, total = 0;
+           ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, total = 0;
     bool decode_fast = false;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-bool decode_fast_path(int64_t T, int F, int k) {
-    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && F <= 2048;
+bool decode_fast_path(int64_t T, int H, int F, int k) {
+    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && H <= kDecodeMaxDim && F <= kDecodeMaxDim;
 }
 
 Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
@@ -65,7 +65,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
         off = align256(off + (bytes ? bytes : 1));
         return at;
     };
-    if (variant == MOE_VARIANT_DECODE && decode_fast_path(T, F, k)) {
+    if (variant == MOE_VARIANT_DECODE && decode_fast_path(T, H, F, k)) {
         L.decode_fast = true;
         L.h = take((size_t)P * F * sizeof(float));
         L.total = off;
@@ -74,6 +74,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     if (variant == MOE_VARIANT_PLAN) {
         L.tiles = take((size_t)max_m_tiles(P, E) * 2 * sizeof(int32_t));
         L.ntiles = take(sizeof(int32_t));
+        L.tile_off = take((size_t)(E + 1) * sizeof(int32_t));
         L.total = off;
         return L;
     }
@@ -83,6 +84,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     L.inv = take((size_t)P * 4);
     L.tiles = take((size_t)max_m_tiles(P, E) * 2 * sizeof(int32_t));
     L.ntiles = take(sizeof(int32_t));
+    L.tile_off = take((size_t)(E + 1) * sizeof(int32_t));
     if (variant == MOE_VARIANT_FP8) {
         L.h = take((size_t)P * F);
         L.hs = take((size_t)P * (F / 128) * sizeof(float));
@@ -119,24 +121,33 @@ int check_ws(const Layout& L, void* ws, size_t ws_bytes) {
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+GroupedPlan plan_in(const Layout& L, void* ws, int E) {
+    GroupedPlan p;
+    p.perm = at<int32_t>(ws, L.perm);
+    p.tiles = at<int32_t>(ws, L.tiles);
+    p.ntiles = at<int32_t>(ws, L.ntiles);
+    p.tile_off = at<int32_t>(ws, L.tile_off);
+    p.offsets = at<int32_t>(ws, L.offsets);
+    p.E = E;
+    return p;
+}
+
 // Routing plan into the workspace, then the two grouped bf16 products and the combine.
 int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* gate_up,
                      const uint16_t* down, const int32_t* idx, const float* w, int64_t T, int H,
                      int F, int E, int k, uint16_t* out, void* ws, hipStream_t s) {
     const int P = (int)(T * k);
-    int32_t* perm = at<int32_t>(ws, L.perm);
-    int32_t* tiles = at<int32_t>(ws, L.tiles);
-    int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-    int32_t* offsets = at<int32_t>(ws, L.offsets);
-    const int64_t mt = max_m_tiles(P, E);
+    const GroupedPlan pl = plan_in(L, ws, E);
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
-    int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), offsets, perm,
-                                  at<int32_t>(ws, L.inv), tiles, ntiles, s));
+    int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                                  at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
+                                  at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                  at<int32_t>(ws, L.tile_off), bf16_tile_m(), s));
     if (rc) return rc;
-    rc = launched(launch_gateup_bf16(hidden, gate_up, perm, tiles, ntiles, offsets, mt, H, F, k, h, s));
+    rc = launched(launch_gateup_bf16(hidden, gate_up, pl, H, F, k, h, s));
     if (rc) return rc;
-    rc = launched(launch_down_bf16(h, down, perm, tiles, ntiles, offsets, mt, H, F, y, s));
+    rc = launched(launch_down_bf16(h, down, pl, H, F, y, s));
     if (rc) return rc;
     return launched(launch_combine(y, idx, w, T, k, E, H, out, s));
 }
@@ -204,7 +215,8 @@ int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E, int32_
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
     return launched(launch_plan(top_k_index, (int)(T * k), E, counts, offsets, perm, inv,
-                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles), stream));
+                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                at<int32_t>(ws, L.tile_off), kMinTileM, stream));
 }
 
 int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
@@ -261,22 +273,19 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
     const int P = (int)(T * k);
-    int32_t* perm = at<int32_t>(ws, L.perm);
-    int32_t* tiles = at<int32_t>(ws, L.tiles);
-    int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-    int32_t* offsets = at<int32_t>(ws, L.offsets);
-    const int64_t mt = max_m_tiles(P, E);
+    const GroupedPlan pl = plan_in(L, ws, E);
     uint8_t* hq = at<uint8_t>(ws, L.h);
     float* hs = at<float>(ws, L.hs);
     uint16_t* y = at<uint16_t>(ws, L.y);
-    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts), offsets, perm,
-                              at<int32_t>(ws, L.inv), tiles, ntiles, stream));
+    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
+                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
+                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), fp8_tile_m(),
+                              stream));
     if (rc) return rc;
-    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, perm, tiles, ntiles, offsets,
-                                    mt, H, F, k, hq, hs, stream));
+    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
     if (rc) return rc;
-    rc = launched(launch_down_fp8(hq, hs, down, down_scale, perm, tiles, ntiles, offsets, mt, H, F,
-                                  y, stream));
+    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
     if (rc) return rc;
     return launched(launch_combine(y, top_k_index, top_k_weights, T, k, E, H, out, stream));
 }

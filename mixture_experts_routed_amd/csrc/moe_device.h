@@ -84,6 +84,11 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const uint4 a, const uint4 
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const u32x4 a, const u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // 32x32x64 fp8(e4m3) x fp8(e4m3) -> fp32 with unit E8M0 block scales
 // (127 encodes 2^0): lane l supplies 32 K bytes of row/col (l % 32).
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 a, const i32x8 b, f32x16 c) {
@@ -97,8 +102,52 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 // XCD b % 8; giving each XCD a contiguous run of slots keeps work items that
 // share a weight panel (neighbouring M tiles of one expert) inside one L2.
 __device__ __forceinline__ int xcd_slot(int b, int G) {
-    const int per = G / kXcds;  // G is a multiple of 8
+    // G is a multiple of 8 (see resident_grid)
+    const int per = G / kXcds;
     return (b % kXcds) * per + (b / kXcds);
+}
+
+// Work items of a grouped product, numbered expert by expert: expert e owns
+// items [n_tiles_n * tile_off[e], n_tiles_n * tile_off[e+1]), its M tiles
+// varying fastest.  Together with xcd_slot this keeps all tiles of an expert
+// (which share its token rows and its weight panels) inside one XCD's L2.
+// Binary search over the M-tile prefix (E + 1 entries, cached reads).
+struct GroupedItem {
+    int e, mt, nt;
+};
+__device__ __forceinline__ GroupedItem grouped_item(int it, const int32_t* __restrict__ tile_off,
+                                                    int E, int n_tiles_n) {
+    int lo = 0, hi = E;  // find e with tile_off[e]*n <= it < tile_off[e+1]*n
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_off[mid] * n_tiles_n <= it) lo = mid; else hi = mid;
+    }
+    const int t0 = tile_off[lo];
+    const int mtiles = tile_off[lo + 1] - t0;
+    const int local = it - t0 * n_tiles_n;
+    GroupedItem g;
+    g.e = lo;
+    g.nt = local / mtiles;
+    g.mt = t0 + (local - g.nt * mtiles);
+    return g;
+}
+
+// LDS tiles hold rows of eight 16-byte chunks.  MI355X LDS serves a 16-byte
+// read for 16 lanes per cycle (64 banks); the MFMA fragment reads touch 16
+// consecutive rows at one logical chunk, so the physical chunk is the logical
+// one XOR (row / 2) % 8: rows of equal parity then hit 8 distinct chunks.
+__device__ __forceinline__ int lds_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Workgroups of `kernel` that are resident at once on the current device,
+// rounded down to a multiple of 8 XCDs: a persistent grid must never exceed
+// it, or its tail workgroups would start only after the first ones finish.
+inline int resident_grid(const void* kernel, int threads, int cu_count) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int g = per_cu * cu_count;
+    return g >= kXcds ? (g / kXcds) * kXcds : kXcds;
 }
 
 }  // namespace moe

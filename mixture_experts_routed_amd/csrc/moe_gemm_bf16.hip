@@ -13,137 +13,149 @@
 
 namespace moe {
 
-constexpr int kGemmThreads = 512;  // 8 waves; wave w owns tile rows [32w, 32w+32)
+constexpr int kGemmThreads = 512;  // 8 waves
 constexpr int kBK = 64;            // bf16 K elements per stage (128 bytes per row)
 
-// One work item = (M tile of <= 256 rows of one expert) x (BN output columns).
-// SWIGLU: B rows are interleaved in blocks of 32 as gate, up, gate, up, ...
-// so that each wave holds matching gate/up accumulators lane for lane, and
-// the epilogue writes h = silu(gate) * up as bf16 [P, F] in expert order.
+// One work item = (M tile of <= BM = 32*WM rows of one expert) x (BN rows of
+// the expert's weight panel).  Waves form a WM x WN grid; wave (wm, wn) owns
+// rows [32wm, 32wm+32) and 32*NBW panel rows.  Both operands go through a
+// 2-stage LDS ring: every thread moves whole 16-byte chunks with 8 lanes per
+// 128-byte row segment (coalesced global reads), chunks XOR-swizzled for the
+// 64-bank LDS; the MFMA fragments are then read from LDS.  Loads run two
+// k-steps ahead in two register stages (named arrays with constant indices,
+// no branch around any load, so the compiler waits for exactly the stage it
+// consumes).  Rows past an M tile's end load row 0 (valid memory) and their
+// outputs are never stored.
+// SWIGLU: panel rows are interleaved in blocks of 32 as gate, up, gate, up,
+// ... so each wave holds matching gate/up accumulators lane for lane, and the
+// epilogue writes h = silu(gate) * up as bf16 [P, F] in expert order.
 // Otherwise the epilogue writes y[slot, col] bf16 with slot = perm[row].
-template <int BN, bool SWIGLU>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(
+template <int WM, int BN, bool SWIGLU>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ offsets, int K,
-    int n_out, int b_rows, int topk, uint16_t* __restrict__ C) {
-    constexpr int NB = BN / 32;                       // 32-wide accumulator blocks per wave
-    constexpr int A_PER = kTileM * 8 / kGemmThreads;  // 16-byte chunks per thread
+    const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
+    uint16_t* __restrict__ C) {
+    constexpr int WN = 8 / WM;
+    constexpr int BM = 32 * WM;
+    constexpr int NBW = BN / (32 * WN);  // 32-wide accumulator blocks per wave
+    constexpr int A_PER = BM * 8 / kGemmThreads;
     constexpr int B_PER = BN * 8 / kGemmThreads;
-    static_assert(B_PER >= 1, "BN too small");
-    __shared__ uint4 a_lds[2][kTileM][8];
-    __shared__ uint4 b_lds[2][BN][8];
+    static_assert(WM * WN == 8 && NBW >= 1 && A_PER >= 1 && B_PER >= 1, "bad tile shape");
+    static_assert(!SWIGLU || NBW % 2 == 0, "SwiGLU needs gate/up block pairs per wave");
+    __shared__ u32x4 a_lds[2][BM][8];
+    __shared__ u32x4 b_lds[2][BN][8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
     const int chunk = tid & 7, row_t = tid >> 3;
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
     const int items = ntiles * n_tiles_n;
     const int nks = K / kBK;
+    const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32*b + lane%32
 
     for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
-        const int nt = it / ntiles, mt = it - nt * ntiles;
-        const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
-        const int mrows = min(kTileM, offsets[e + 1] - row0);
+        const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        const int nt = gi.nt, mt = gi.mt, e = gi.e;
+        const int row0 = tiles[2 * mt + 1];
+        const int mrows = min(BM, offsets[e + 1] - row0);
+        const bool active = 32 * wm < mrows;
 
         const uint16_t* a_src[A_PER];
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int r = row_t + 64 * i;
-            a_src[i] = nullptr;
-            if (r < mrows) {
-                const int64_t arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
-                a_src[i] = A + arow * K + chunk * 8;
-            }
+            int64_t arow = 0;
+            if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+            a_src[i] = A + arow * K + chunk * 8;
         }
-        const uint16_t* b_src[B_PER];
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int rr = row_t + 64 * i;
-            int brow;
-            if (SWIGLU) {
-                const int blk = rr >> 5;
-                brow = ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
-            } else {
-                brow = nt * BN + rr;
-            }
-            b_src[i] = B + ((int64_t)e * b_rows + brow) * K + chunk * 8;
+        // thread rows row_t + 64 i of the panel: 64 panel rows are 32 weight
+        // rows apart when gate/up interleave in blocks of 32, else 64
+        int brow0;
+        if (SWIGLU) {
+            const int blk = row_t >> 5;
+            brow0 = ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (row_t & 31);
+        } else {
+            brow0 = nt * BN + row_t;
         }
+        const uint16_t* b_src = B + ((int64_t)e * b_rows + brow0) * K + chunk * 8;
+        const int64_t b_step = (int64_t)(SWIGLU ? 32 : 64) * K;
 
-        uint4 a_reg[A_PER], b_reg[B_PER];
-        auto load_stage = [&](int ks) {
+        f32x16 acc[NBW];
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i)
-                a_reg[i] = a_src[i] ? *(const uint4*)(a_src[i] + ks * kBK) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < B_PER; ++i) b_reg[i] = *(const uint4*)(b_src[i] + ks * kBK);
-        };
-        auto store_stage = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < A_PER; ++i) {
-                const int r = row_t + 64 * i;
-                a_lds[buf][r][chunk ^ (r & 7)] = a_reg[i];
-            }
-#pragma unroll
-            for (int i = 0; i < B_PER; ++i) {
-                const int rr = row_t + 64 * i;
-                b_lds[buf][rr][chunk ^ (rr & 7)] = b_reg[i];
-            }
-        };
+        for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x16{};
+        u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
 
-        f32x16 acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-        const bool active = wave * 32 < mrows;
-        const int my_row = wave * 32 + (lane & 31);
-        const int sw = lane & 7;  // == my_row & 7 == (nb*32 + lane%32) & 7
+#define MOE_BF16_LOAD(RA, RB, KS)                                                             \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) RA[i] =                             \
+            *(const u32x4*)(a_src[i] + (KS) * kBK);                                           \
+        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) RB[i] =                             \
+            *(const u32x4*)(b_src + i * b_step + (KS) * kBK);                                 \
+    } while (0)
 
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-        for (int ks = 0; ks < nks; ++ks) {
-            const int buf = ks & 1;
-            if (ks + 1 < nks) load_stage(ks + 1);
-            if (active) {
-#pragma unroll
-                for (int kk = 0; kk < kBK / 16; ++kk) {
-                    const int c = kk * 2 + (lane >> 5);
-                    const uint4 a = a_lds[buf][my_row][c ^ sw];
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const uint4 b = b_lds[buf][nb * 32 + (lane & 31)][c ^ sw];
-                        acc[nb] = mfma_bf16_32x32x16(a, b, acc[nb]);
-                    }
-                }
-            }
-            if (ks + 1 < nks) store_stage(buf ^ 1);
-            __syncthreads();
+#define MOE_BF16_STEP(S, RA, RB, KS)                                                          \
+    do {                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) {                                   \
+            const int rr = row_t + 64 * i;                                                    \
+            a_lds[S][rr][lds_chunk(rr, chunk)] = RA[i];                                       \
+        }                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) {                                   \
+            const int rr = row_t + 64 * i;                                                    \
+            b_lds[S][rr][lds_chunk(rr, chunk)] = RB[i];                                       \
+        }                                                                                     \
+        __syncthreads();                                                                      \
+        if (active && (KS) < nks) {                                                           \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                \
+                const int c = (kk * 2 + (lane >> 5)) ^ fsw;                                   \
+                const u32x4 af = a_lds[S][32 * wm + (lane & 31)][c];                          \
+                u32x4 bf[NBW];                                                                \
+                _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) bf[nb] =                   \
+                    b_lds[S][(wn * NBW + nb) * 32 + (lane & 31)][c];                          \
+                _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) acc[nb] =                  \
+                    mfma_bf16_32x32x16(af, bf[nb], acc[nb]);                                  \
+            }                                                                                 \
+        }                                                                                     \
+        MOE_BF16_LOAD(RA, RB, min((KS) + 2, nks - 1));                                        \
+    } while (0)
+
+        MOE_BF16_LOAD(ra0, rb0, 0);
+        MOE_BF16_LOAD(ra1, rb1, min(1, nks - 1));
+        for (int ks = 0; ks < nks; ks += 2) {
+            MOE_BF16_STEP(0, ra0, rb0, ks);
+            MOE_BF16_STEP(1, ra1, rb1, ks + 1);
         }
+#undef MOE_BF16_STEP
+#undef MOE_BF16_LOAD
+        __syncthreads();  // the next item's first LDS write must not overtake these reads
 
         if (active) {
             if (SWIGLU) {
 #pragma unroll
-                for (int p = 0; p < NB / 2; ++p) {
-                    const int f = nt * (BN / 2) + p * 32 + (lane & 31);
+                for (int p = 0; p < NBW / 2; ++p) {
+                    const int f = nt * (BN / 2) + (wn * NBW / 2 + p) * 32 + (lane & 31);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = wave * 32 + acc_row(r, lane);
+                    for (int q = 0; q < 16; ++q) {
+                        const int row = 32 * wm + acc_row(q, lane);
                         if (row < mrows) {
-                            const float hv = silu(acc[2 * p][r]) * acc[2 * p + 1][r];
+                            const float hv = silu(acc[2 * p][q]) * acc[2 * p + 1][q];
                             C[(int64_t)(row0 + row) * n_out + f] = (uint16_t)f32_to_bf16(hv);
                         }
                     }
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wave * 32 + acc_row(r, lane);
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * wm + acc_row(q, lane);
                     if (row < mrows) {
                         const int64_t slot = perm[row0 + row];
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const int col = nt * BN + nb * 32 + (lane & 31);
-                            C[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][r]);
+                        for (int nb = 0; nb < NBW; ++nb) {
+                            const int col = nt * BN + (wn * NBW + nb) * 32 + (lane & 31);
+                            C[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
                         }
                     }
                 }
@@ -152,28 +164,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(
     }
 }
 
+// Tile shape of the bf16 products: M tile rows (the plan's tile size) and
+// panel rows per work item.
+constexpr int kBf16WM = 4;             // 4 x 2 waves: 128-row M tiles
+constexpr int kBf16TileM = 32 * kBf16WM;
+constexpr int kBf16BN = 128;
+
+int bf16_tile_m() { return kBf16TileM; }
+
+template <int WM, int BN, bool SWIGLU>
 static int gemm_grid() {
-    int g = device_cu_count();
-    return ((g + kXcds - 1) / kXcds) * kXcds;
+    static const int g = resident_grid((const void*)gemm_bf16_kernel<WM, BN, SWIGLU>, kGemmThreads,
+                                       device_cu_count());
+    return g;
 }
 
-hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const int32_t* perm,
-                              const int32_t* tiles, const int32_t* ntiles, const int32_t* offsets,
-                              int64_t, int H, int F, int k, uint16_t* h, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, true>), dim3(gemm_grid()), dim3(kGemmThreads), 0, s,
-                       x, w13, perm, tiles, ntiles, offsets, H, F, 2 * F, k, h);
+hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& pl,
+                              int H, int F, int k, uint16_t* h, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, kBf16BN, true>),
+                       dim3(gemm_grid<kBf16WM, kBf16BN, true>()), dim3(kGemmThreads), 0, s, x, w13,
+                       pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k,
+                       h);
     return hipGetLastError();
 }
 
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const int32_t* perm,
-                            const int32_t* tiles, const int32_t* ntiles, const int32_t* offsets,
-                            int64_t, int H, int F, uint16_t* y, hipStream_t s) {
-    if (H % 128 == 0)
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, false>), dim3(gemm_grid()), dim3(kGemmThreads), 0,
-                           s, h, w2, perm, tiles, ntiles, offsets, F, H, H, 1, y);
+hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& pl, int H,
+                            int F, uint16_t* y, hipStream_t s) {
+    if (H % kBf16BN == 0)
+        hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, kBf16BN, false>),
+                           dim3(gemm_grid<kBf16WM, kBf16BN, false>()), dim3(kGemmThreads), 0, s, h,
+                           w2, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F, H, H,
+                           1, y);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<64, false>), dim3(gemm_grid()), dim3(kGemmThreads), 0,
-                           s, h, w2, perm, tiles, ntiles, offsets, F, H, H, 1, y);
+        hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, 64, false>),
+                           dim3(gemm_grid<kBf16WM, 64, false>()), dim3(kGemmThreads), 0, s, h, w2,
+                           pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F, H, H, 1,
+                           y);
     return hipGetLastError();
 }
 

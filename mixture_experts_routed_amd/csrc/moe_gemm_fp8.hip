@@ -13,7 +13,7 @@
 
 namespace moe {
 
-constexpr int kFp8Threads = 512;  // 8 waves; wave w owns tile rows [32w, 32w+32)
+constexpr int kFp8Threads = 512;  // 8 waves
 constexpr int kFp8BK = 128;       // K bytes per stage == one scale block
 
 // Block-128 quantisation of 128 values spread as 4 per lane over one 32-lane
@@ -35,218 +35,240 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
     return scale;
 }
 
-template <int BN, bool SWIGLU>
-__global__ __launch_bounds__(kFp8Threads, 1) void gemm_fp8_kernel(
+// Same work decomposition and data path as the bf16 products: one work item
+// = (M tile of <= BM = 32*WM rows of one expert) x (BN panel rows); waves
+// form a WM x WN grid, wave (wm, wn) owns rows [32wm, 32wm+32) and 32*NBW
+// panel rows.  A 128-byte K step is one scale block.  The A bytes, the B
+// panel and both operands' per-row scales go through a 2-stage LDS ring fed
+// by branch-free look-ahead loads two k-steps ahead.  Per block, two
+// 32x32x64 MFMAs fill a fresh fp32 temporary that is promoted with
+// scale_a[row] * scale_b[col] into the accumulator.
+// SWIGLU: panel rows interleave gate/up in blocks of 32 (as the bf16 path);
+// one item covers a whole 128-wide h block split over the WN = 2 column
+// waves, which exchange per-row partial maxima through LDS before the
+// block-128 re-quantisation.  Otherwise: y[slot, col] bf16.
+template <int WM, int BN, bool SWIGLU>
+__global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
-    const int32_t* __restrict__ offsets, int K, int n_out, int b_rows, int topk,
-    uint8_t* __restrict__ Cq, float* __restrict__ Cs, uint16_t* __restrict__ Cy) {
-    constexpr int NB = BN / 32;
-    constexpr int A_PER = kTileM * 8 / kFp8Threads;
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, float* __restrict__ Cs,
+    uint16_t* __restrict__ Cy) {
+    constexpr int WN = 8 / WM;
+    constexpr int BM = 32 * WM;
+    constexpr int NBW = BN / (32 * WN);
+    constexpr int A_PER = BM * 8 / kFp8Threads;
     constexpr int B_PER = BN * 8 / kFp8Threads;
-    static_assert(!SWIGLU || BN == 256, "the SwiGLU epilogue needs a full 128-column h block");
-    __shared__ uint4 a_lds[2][kTileM][8];
-    __shared__ uint4 b_lds[2][BN][8];
-    __shared__ __attribute__((aligned(16))) float sa_lds[2][kTileM];
-    __shared__ __attribute__((aligned(16))) float sb_lds[2][BN];
+    static_assert(WM * WN == 8 && NBW >= 1 && A_PER >= 1 && B_PER >= 1, "bad tile shape");
+    static_assert(BM <= kFp8Threads && BN <= kFp8Threads, "one scale per thread");
+    static_assert(!SWIGLU || (BN == 256 && WN == 2), "the SwiGLU epilogue needs a 128-wide h block over 2 waves");
+    __shared__ u32x4 a_lds[2][BM][8];
+    __shared__ u32x4 b_lds[2][BN][8];
+    __shared__ __attribute__((aligned(16))) float sa_lds[2][BM];
+    __shared__ float sb_lds[2][BN];
+    __shared__ float amax_lds[SWIGLU ? WN : 1][SWIGLU ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
     const int chunk = tid & 7, row_t = tid >> 3;
+    const int g = lane >> 5;
+    const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32*b + lane%32
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
     const int items = ntiles * n_tiles_n;
     const int nkb = K / kFp8BK;
 
-    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
-        const int nt = it / ntiles, mt = it - nt * ntiles;
-        const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
-        const int mrows = min(kTileM, offsets[e + 1] - row0);
+    auto panel_row = [&](int rr, int nt) {
+        if (SWIGLU) {
+            const int blk = rr >> 5;
+            return ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
+        }
+        return nt * BN + rr;
+    };
 
+    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+        const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        const int nt = gi.nt, mt = gi.mt, e = gi.e;
+        const int row0 = tiles[2 * mt + 1];
+        const int mrows = min(BM, offsets[e + 1] - row0);
+        const bool active = 32 * wm < mrows;
+
+        // A rows (and A scale rows) past the tile's end read row 0
         const uint8_t* a_src[A_PER];
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int r = row_t + 64 * i;
-            a_src[i] = nullptr;
-            if (r < mrows) {
-                const int64_t arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
-                a_src[i] = A + arow * K + chunk * 16;
-            }
+            int64_t arow = 0;
+            if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+            a_src[i] = A + arow * K + chunk * 16;
         }
-        const uint8_t* b_src[B_PER];
+        const bool sa_ok = tid < BM, sb_ok = tid < BN;
+        int64_t sarow = 0;
+        if (sa_ok && tid < mrows)
+            sarow = SWIGLU ? (int64_t)(perm[row0 + tid] / topk) : (int64_t)(row0 + tid);
+        const float* as_src = As + sarow * nkb;
+        const uint8_t* b_src = B + ((int64_t)e * b_rows + panel_row(row_t, nt)) * K + chunk * 16;
+        const int64_t b_step = (int64_t)(SWIGLU ? 32 : 64) * K;
+        const float* bs_src = Bs + ((int64_t)e * b_rows + panel_row(sb_ok ? tid : 0, nt)) * nkb;
+
+        f32x16 acc[NBW];
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int rr = row_t + 64 * i;
-            int brow;
-            if (SWIGLU) {
-                const int blk = rr >> 5;
-                brow = ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
-            } else {
-                brow = nt * BN + rr;
-            }
-            b_src[i] = B + ((int64_t)e * b_rows + brow) * K + chunk * 16;
+        for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x16{};
+        u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
+        float rsa0, rsa1, rsb0, rsb1;
+
+#define MOE_FP8_LOAD(RA, RB, RSA, RSB, KB)                                                     \
+    do {                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) RA[i] =                              \
+            *(const u32x4*)(a_src[i] + (KB) * kFp8BK);                                         \
+        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) RB[i] =                              \
+            *(const u32x4*)(b_src + i * b_step + (KB) * kFp8BK);                               \
+        RSA = as_src[KB];                                                                      \
+        RSB = bs_src[KB];                                                                      \
+    } while (0)
+
+#define MOE_FP8_STEP(S, RA, RB, RSA, RSB, KB)                                                  \
+    do {                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) {                                    \
+            const int rr = row_t + 64 * i;                                                     \
+            a_lds[S][rr][lds_chunk(rr, chunk)] = RA[i];                                        \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) {                                    \
+            const int rr = row_t + 64 * i;                                                     \
+            b_lds[S][rr][lds_chunk(rr, chunk)] = RB[i];                                        \
+        }                                                                                      \
+        if (sa_ok) sa_lds[S][tid] = RSA;                                                       \
+        if (sb_ok) sb_lds[S][tid] = RSB;                                                       \
+        __syncthreads();                                                                       \
+        if (active && (KB) < nkb) {                                                            \
+            const int ar = 32 * wm + (lane & 31);                                              \
+            const i32x8 a0 = __builtin_bit_cast(i32x8, __builtin_shufflevector(                \
+                a_lds[S][ar][(2 * g) ^ fsw], a_lds[S][ar][(2 * g + 1) ^ fsw],                   \
+                0, 1, 2, 3, 4, 5, 6, 7));                                                      \
+            const i32x8 a1 = __builtin_bit_cast(i32x8, __builtin_shufflevector(                \
+                a_lds[S][ar][(4 + 2 * g) ^ fsw], a_lds[S][ar][(4 + 2 * g + 1) ^ fsw],           \
+                0, 1, 2, 3, 4, 5, 6, 7));                                                      \
+            float sa[16]; /* A scale of each accumulator row of this lane */                   \
+            _Pragma("unroll") for (int qq = 0; qq < 4; ++qq) {                                 \
+                const float4 v = *(const float4*)&sa_lds[S][32 * wm + 8 * qq + 4 * g];          \
+                sa[4 * qq] = v.x; sa[4 * qq + 1] = v.y; sa[4 * qq + 2] = v.z; sa[4 * qq + 3] = v.w; \
+            }                                                                                  \
+            _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) {                               \
+                const int brow = (wn * NBW + nb) * 32 + (lane & 31);                           \
+                const i32x8 b0 = __builtin_bit_cast(i32x8, __builtin_shufflevector(            \
+                    b_lds[S][brow][(2 * g) ^ fsw], b_lds[S][brow][(2 * g + 1) ^ fsw],           \
+                    0, 1, 2, 3, 4, 5, 6, 7));                                                  \
+                const i32x8 b1 = __builtin_bit_cast(i32x8, __builtin_shufflevector(            \
+                    b_lds[S][brow][(4 + 2 * g) ^ fsw], b_lds[S][brow][(4 + 2 * g + 1) ^ fsw],   \
+                    0, 1, 2, 3, 4, 5, 6, 7));                                                  \
+                f32x16 tmp = mfma_fp8_32x32x64(a0, b0, f32x16{});                              \
+                tmp = mfma_fp8_32x32x64(a1, b1, tmp);                                          \
+                const float sbv = sb_lds[S][brow];                                             \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q) acc[nb][q] +=                   \
+                    tmp[q] * (sa[q] * sbv);                                                    \
+            }                                                                                  \
+        }                                                                                      \
+        MOE_FP8_LOAD(RA, RB, RSA, RSB, min((KB) + 2, nkb - 1));                                \
+    } while (0)
+
+        MOE_FP8_LOAD(ra0, rb0, rsa0, rsb0, 0);
+        MOE_FP8_LOAD(ra1, rb1, rsa1, rsb1, min(1, nkb - 1));
+        for (int kb = 0; kb < nkb; kb += 2) {
+            MOE_FP8_STEP(0, ra0, rb0, rsa0, rsb0, kb);
+            MOE_FP8_STEP(1, ra1, rb1, rsa1, rsb1, kb + 1);
         }
-        // scale rows: threads [0,256) -> A rows, [256, 256+BN) -> B rows
-        const float* s_src = nullptr;
-        int s_stride = 0;
-        if (tid < kTileM) {
-            if (tid < mrows) {
-                const int64_t arow = SWIGLU ? (int64_t)(perm[row0 + tid] / topk) : (int64_t)(row0 + tid);
-                s_src = As + arow * nkb;
-                s_stride = 1;
-            }
-        } else if (tid - kTileM < BN) {
-            const int rr = tid - kTileM;
-            int brow;
-            if (SWIGLU) {
-                const int blk = rr >> 5;
-                brow = ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
-            } else {
-                brow = nt * BN + rr;
-            }
-            s_src = Bs + ((int64_t)e * b_rows + brow) * nkb;
-            s_stride = 1;
-        }
+#undef MOE_FP8_STEP
+#undef MOE_FP8_LOAD
 
-        uint4 a_reg[A_PER], b_reg[B_PER];
-        float s_reg = 0.0f;
-        auto load_stage = [&](int kb) {
+        if (SWIGLU) {
+            // h for f = nt*128 + (wn*2 + p)*32 + lane%32, p = 0, 1
+            float hv[2][16];
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i)
-                a_reg[i] = a_src[i] ? *(const uint4*)(a_src[i] + kb * kFp8BK) : make_uint4(0, 0, 0, 0);
+            for (int q = 0; q < 16; ++q) {
+                float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) b_reg[i] = *(const uint4*)(b_src[i] + kb * kFp8BK);
-            s_reg = s_src ? s_src[kb * s_stride] : 0.0f;
-        };
-        auto store_stage = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < A_PER; ++i) {
-                const int r = row_t + 64 * i;
-                a_lds[buf][r][chunk ^ (r & 7)] = a_reg[i];
-            }
-#pragma unroll
-            for (int i = 0; i < B_PER; ++i) {
-                const int rr = row_t + 64 * i;
-                b_lds[buf][rr][chunk ^ (rr & 7)] = b_reg[i];
-            }
-            if (tid < kTileM) sa_lds[buf][tid] = s_reg;
-            else if (tid - kTileM < BN) sb_lds[buf][tid - kTileM] = s_reg;
-        };
-
-        f32x16 acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-        const bool active = wave * 32 < mrows;
-        const int my_row = wave * 32 + (lane & 31);
-        const int sw = lane & 7;
-        const int g = lane >> 5;
-
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-        for (int kb = 0; kb < nkb; ++kb) {
-            const int buf = kb & 1;
-            if (kb + 1 < nkb) load_stage(kb + 1);
-            if (active) {
-                i32x8 a0, a1;
-                {
-                    const uint4 c0 = a_lds[buf][my_row][(2 * g) ^ sw];
-                    const uint4 c1 = a_lds[buf][my_row][(2 * g + 1) ^ sw];
-                    const uint4 c2 = a_lds[buf][my_row][(4 + 2 * g) ^ sw];
-                    const uint4 c3 = a_lds[buf][my_row][(4 + 2 * g + 1) ^ sw];
-                    a0 = i32x8{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-                    a1 = i32x8{(int)c2.x, (int)c2.y, (int)c2.z, (int)c2.w, (int)c3.x, (int)c3.y, (int)c3.z, (int)c3.w};
+                for (int p = 0; p < 2; ++p) {
+                    hv[p][q] = silu(acc[2 * p][q]) * acc[2 * p + 1][q];
+                    m = fmaxf(m, fabsf(hv[p][q]));
                 }
-                float sa[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *(const float4*)&sa_lds[buf][wave * 32 + 8 * q + 4 * g];
-                    sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int brow = nb * 32 + (lane & 31);
-                    const uint4 d0 = b_lds[buf][brow][(2 * g) ^ sw];
-                    const uint4 d1 = b_lds[buf][brow][(2 * g + 1) ^ sw];
-                    const uint4 d2 = b_lds[buf][brow][(4 + 2 * g) ^ sw];
-                    const uint4 d3 = b_lds[buf][brow][(4 + 2 * g + 1) ^ sw];
-                    const i32x8 b0{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w, (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
-                    const i32x8 b1{(int)d2.x, (int)d2.y, (int)d2.z, (int)d2.w, (int)d3.x, (int)d3.y, (int)d3.z, (int)d3.w};
-                    f32x16 tmp = mfma_fp8_32x32x64(a0, b0, f32x16{});
-                    tmp = mfma_fp8_32x32x64(a1, b1, tmp);
-                    const float sbv = sb_lds[buf][brow];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[nb][r] += tmp[r] * (sa[r] * sbv);
-                }
+                m = half_max32(m);
+                if ((lane & 31) == 0) amax_lds[wn][32 * wm + acc_row(q, lane)] = m;
             }
-            if (kb + 1 < nkb) store_stage(buf ^ 1);
             __syncthreads();
-        }
-
-        if (active) {
-            if (SWIGLU) {
-                // h block of 128 columns: f = nt*128 + p*32 + lane%32, p = 0..3
-                const int fblk = nt;
+            if (active) {
                 const int nfb = n_out / 128;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wave * 32 + acc_row(r, lane);
-                    float hv[4];
-                    float amax = 0.0f;
+                for (int q = 0; q < 16; ++q) {
+                    const int row = 32 * wm + acc_row(q, lane);
+                    const float amax = fmaxf(amax_lds[0][row], amax_lds[1][row]);
+                    const bool zero = !(amax > 0.0f);
+                    const float scale = zero ? 1.0f : amax / 448.0f;
+                    const float mul = zero ? 0.0f : 448.0f / amax;
+                    float qv[2];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        hv[p] = silu(acc[2 * p][r]) * acc[2 * p + 1][r];
-                        amax = fmaxf(amax, fabsf(hv[p]));
-                    }
-                    uint32_t codes;
-                    const float scale = quant_block_half(hv, amax, &codes);
+                    for (int p = 0; p < 2; ++p)
+                        qv[p] = zero ? 0.0f : fminf(fmaxf(hv[p][q] * mul, -448.0f), 448.0f);
+                    const uint32_t codes = f32x4_to_e4m3x4(qv[0], qv[1], 0.0f, 0.0f);
                     if (row < mrows) {
-                        uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + fblk * 128 + (lane & 31);
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) dst[p * 32] = (uint8_t)(codes >> (8 * p));
-                        if ((lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + fblk] = scale;
+                        uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + nt * 128 + wn * 64 + (lane & 31);
+                        dst[0] = (uint8_t)codes;
+                        dst[32] = (uint8_t)(codes >> 8);
+                        if (wn == 0 && (lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + nt] = scale;
                     }
                 }
-            } else {
+            }
+        } else if (active) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wave * 32 + acc_row(r, lane);
-                    if (row < mrows) {
-                        const int64_t slot = perm[row0 + row];
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * wm + acc_row(q, lane);
+                if (row < mrows) {
+                    const int64_t slot = perm[row0 + row];
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const int col = nt * BN + nb * 32 + (lane & 31);
-                            Cy[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][r]);
-                        }
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const int col = nt * BN + (wn * NBW + nb) * 32 + (lane & 31);
+                        Cy[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
                     }
                 }
             }
         }
+        __syncthreads();  // LDS (operand rings, amax) is reused by the next item
     }
 }
 
+constexpr int kFp8WM = 4;  // 4 x 2 waves: 128-row M tiles
+constexpr int kFp8TileM = 32 * kFp8WM;
+
+int fp8_tile_m() { return kFp8TileM; }
+
+template <int WM, int BN, bool SWIGLU>
 static int fp8_grid() {
-    int g = device_cu_count();
-    return ((g + kXcds - 1) / kXcds) * kXcds;
+    static const int g = resident_grid((const void*)gemm_fp8_kernel<WM, BN, SWIGLU>, kFp8Threads,
+                                       device_cu_count());
+    return g;
 }
 
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
-                             const float* w13s, const int32_t* perm, const int32_t* tiles,
-                             const int32_t* ntiles, const int32_t* offsets, int64_t, int H, int F,
-                             int k, uint8_t* hq, float* hs, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<256, true>), dim3(fp8_grid()), dim3(kFp8Threads), 0, s, x,
-                       xs, w13, w13s, perm, tiles, ntiles, offsets, H, F, 2 * F, k, hq, hs,
-                       (uint16_t*)nullptr);
+                             const float* w13s, const GroupedPlan& pl, int H, int F, int k,
+                             uint8_t* hq, float* hs, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 256, true>), dim3(fp8_grid<kFp8WM, 256, true>()),
+                       dim3(kFp8Threads), 0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles,
+                       pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
     return hipGetLastError();
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
-                           const int32_t* perm, const int32_t* tiles, const int32_t* ntiles,
-                           const int32_t* offsets, int64_t, int H, int F, uint16_t* y,
-                           hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<128, false>), dim3(fp8_grid()), dim3(kFp8Threads), 0, s,
-                       hq, hs, w2, w2s, perm, tiles, ntiles, offsets, F, H, H, 1,
-                       (uint8_t*)nullptr, (float*)nullptr, y);
+                           const GroupedPlan& pl, int H, int F, uint16_t* y, hipStream_t s) {
+    if (H % 256 == 0)
+        hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 256, false>),
+                           dim3(fp8_grid<kFp8WM, 256, false>()), dim3(kFp8Threads), 0, s, hq, hs,
+                           w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                           H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
+    else
+        hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 128, false>),
+                           dim3(fp8_grid<kFp8WM, 128, false>()), dim3(kFp8Threads), 0, s, hq, hs,
+                           w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                           H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ namespace moe {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kPlanRegs = 32;  // slots per lane loaded together (one round trip per 2048-slot chunk)
 
 // One workgroup.  Wave w owns a contiguous, 64-aligned run of slots, so the
 // order (wave, position in run) is the slot order.  Pass 1 counts per
@@ -23,7 +24,8 @@ constexpr int kPlanWaves = kPlanThreads / kWave;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ idx, int P, int E, int nbits, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles, int32_t* __restrict__ tile_off,
+    int tile_m) {
     __shared__ int base[kPlanWaves][MOE_MAX_EXPERTS];
     __shared__ int tot[MOE_MAX_EXPERTS];
     __shared__ int off_sh[MOE_MAX_EXPERTS + 1];
@@ -37,9 +39,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int s0 = wave * run;
     const int s1 = min(P, s0 + run);
 
-    for (int s = s0 + lane; s < s1; s += kWave) {
-        const int e = idx[s];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&base[wave][e], 1);
+    for (int cb = s0; cb < s1; cb += kWave * kPlanRegs) {
+        int ev[kPlanRegs];
+#pragma unroll
+        for (int i = 0; i < kPlanRegs; ++i) {
+            const int s = cb + kWave * i + lane;
+            ev[i] = s < s1 ? idx[s] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kPlanRegs; ++i)
+            if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&base[wave][ev[i]], 1);
     }
     __syncthreads();
 
@@ -62,7 +71,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int e = e0 + i;
             if (e < E) {
                 c_sum += tot[e];
-                t_sum += (tot[e] + kTileM - 1) / kTileM;
+                t_sum += (tot[e] + tile_m - 1) / tile_m;
             }
         }
         int c_inc = c_sum, t_inc = t_sum;
@@ -79,7 +88,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
                 off_sh[e] = c_run;
                 tile_sh[e] = t_run;
                 c_run += tot[e];
-                t_run += (tot[e] + kTileM - 1) / kTileM;
+                t_run += (tot[e] + tile_m - 1) / tile_m;
             }
         }
         if (lane == kWave - 1) {
@@ -91,51 +100,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 
     for (int e = tid; e <= E; e += kPlanThreads) {
         offsets[e] = off_sh[e];
+        tile_off[e] = tile_sh[e];
         if (e < E) {
             counts[e] = tot[e];
             const int nt = tile_sh[e + 1] - tile_sh[e];
             for (int i = 0; i < nt; ++i) {
                 tiles[2 * (tile_sh[e] + i)] = e;
-                tiles[2 * (tile_sh[e] + i) + 1] = off_sh[e] + i * kTileM;
+                tiles[2 * (tile_sh[e] + i) + 1] = off_sh[e] + i * tile_m;
             }
         }
     }
     if (tid == 0) *ntiles = tile_sh[E];
 
-    // pass 2: stable scatter; each wave only touches its own row of `base`
-    for (int sb = s0; sb < s1; sb += kWave) {
-        const int s = sb + lane;
-        const int e = (s < s1) ? idx[s] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;
-        uint64_t same = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t set = __ballot(bit);
-            same &= bit ? set : ~set;
+    // pass 2: stable scatter in slot order; each wave only touches its own
+    // row of `base`
+    for (int cb = s0; cb < s1; cb += kWave * kPlanRegs) {
+        int ev[kPlanRegs];
+#pragma unroll
+        for (int i = 0; i < kPlanRegs; ++i) {
+            const int s = cb + kWave * i + lane;
+            ev[i] = s < s1 ? idx[s] : -1;
         }
-        int rank = 0, pos = -1;
-        if (valid) {
-            rank = __popcll(same & ((1ull << lane) - 1ull));
-            pos = off_sh[e] + base[wave][e] + rank;
-            perm[pos] = s;
+#pragma unroll
+        for (int i = 0; i < kPlanRegs; ++i) {
+            const int s = cb + kWave * i + lane;
+            const int e = ev[i];
+            const bool valid = (unsigned)e < (unsigned)E;
+            uint64_t same = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t set = __ballot(bit);
+                same &= bit ? set : ~set;
+            }
+            int rank = 0, pos = -1;
+            if (valid) {
+                rank = __popcll(same & ((1ull << lane) - 1ull));
+                pos = off_sh[e] + base[wave][e] + rank;
+                perm[pos] = s;
+            }
+            if (s < s1) inv[s] = pos;
+            // every lane has read base[wave][*] above before the group leader
+            // bumps it (LDS operations of one wave complete in issue order)
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) base[wave][e] += __popcll(same);
+            __builtin_amdgcn_wave_barrier();
         }
-        if (s < s1) inv[s] = pos;
-        // every lane has read base[wave][*] above before the group leader
-        // bumps it (LDS operations of one wave complete in issue order)
-        __builtin_amdgcn_wave_barrier();
-        if (valid && rank == 0) base[wave][e] += __popcll(same);
-        __builtin_amdgcn_wave_barrier();
     }
     for (int i = off_sh[E] + tid; i < P; i += kPlanThreads) perm[i] = -1;
 }
 
 hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
-                       hipStream_t s) {
+                       int32_t* tile_off, int tile_m, hipStream_t s) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, nbits, counts,
-                       offsets, perm, inv, tiles, ntiles);
+                       offsets, perm, inv, tiles, ntiles, tile_off, tile_m);
     return hipGetLastError();
 }
 

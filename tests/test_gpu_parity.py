@@ -355,8 +355,10 @@ def test_fp8_h_stage_codes():
     diff = hq != q_ref
     assert diff.mean() < 2e-3, diff.mean()
     a, b = orc.e4m3fn_decode(hq[diff]), orc.e4m3fn_decode(q_ref[diff])
-    # one e4m3 step apart (a sign flip of a value that rounds to zero is no step)
-    assert np.all(np.abs(a - b) <= np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -3 + 2.0 ** -9)
+    # in code units (h / scale, max 448): one e4m3 step, plus the absolute
+    # fp32 accumulation error of h (<= 1e-4 of the block max) that can push a
+    # near-zero value across zero
+    assert np.all(np.abs(a - b) <= np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -3 + 448e-4)
 
 
 def test_quantizer_bit_exact():
