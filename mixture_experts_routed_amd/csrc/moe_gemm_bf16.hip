@@ -21,18 +21,17 @@ constexpr int kBK = 64;            // bf16 K elements per stage (128 bytes per r
 // rows [32wm, 32wm+32) and 32*NBW panel rows.  Both operands go through a
 // 2-stage LDS ring: every thread moves whole 16-byte chunks with 8 lanes per
 // 128-byte row segment (coalesced global reads), chunks XOR-swizzled for the
-// 64-bank LDS; the MFMA fragments are then read from LDS.  Loads run two
-// k-steps ahead in two register stages (named arrays with constant indices,
-// no branch around any load, so the compiler waits for exactly the stage it
-// consumes).  Rows past an M tile's end load row 0 (valid memory) and their
+// 64-bank LDS; the MFMA fragments are then read from LDS.  Loads run NREG
+// k-steps ahead in NREG register stages (named arrays with constant
+// indices, no branch around any load, so the compiler waits for exactly the
+// stage it consumes).  Rows past an M tile's end load row 0 (valid memory) and their
 // outputs are never stored.
 // SWIGLU: panel rows are interleaved in blocks of 32 as gate, up, gate, up,
 // ... so each wave holds matching gate/up accumulators lane for lane, and the
 // epilogue writes h = silu(gate) * up as bf16 [P, F] in expert order.
 // Otherwise the epilogue writes y[slot, col] bf16 with slot = perm[row].
-template <int WM, int BN, bool SWIGLU>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void gemm_bf16_kernel(
+template <int WM, int BN, bool SWIGLU, int NREG>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
@@ -45,6 +44,7 @@ void gemm_bf16_kernel(
     constexpr int B_PER = BN * 8 / kGemmThreads;
     static_assert(WM * WN == 8 && NBW >= 1 && A_PER >= 1 && B_PER >= 1, "bad tile shape");
     static_assert(!SWIGLU || NBW % 2 == 0, "SwiGLU needs gate/up block pairs per wave");
+    static_assert(NREG == 2 || NREG == 3, "two or three register stages");
     __shared__ u32x4 a_lds[2][BM][8];
     __shared__ u32x4 b_lds[2][BN][8];
 
@@ -87,7 +87,7 @@ void gemm_bf16_kernel(
         f32x16 acc[NBW];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x16{};
-        u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
+        u32x4 ra0[A_PER], ra1[A_PER], ra2[A_PER], rb0[B_PER], rb1[B_PER], rb2[B_PER];
 
 #define MOE_BF16_LOAD(RA, RB, KS)                                                             \
     do {                                                                                      \
@@ -119,14 +119,30 @@ void gemm_bf16_kernel(
                     mfma_bf16_32x32x16(af, bf[nb], acc[nb]);                                  \
             }                                                                                 \
         }                                                                                     \
-        MOE_BF16_LOAD(RA, RB, min((KS) + 2, nks - 1));                                        \
+        MOE_BF16_LOAD(RA, RB, min((KS) + NREG, nks - 1));                                     \
     } while (0)
 
+        // NREG register stages (loads run NREG k-steps ahead) over a two-stage
+        // LDS ring: LDS stage ks % 2, register stage ks % NREG
         MOE_BF16_LOAD(ra0, rb0, 0);
         MOE_BF16_LOAD(ra1, rb1, min(1, nks - 1));
-        for (int ks = 0; ks < nks; ks += 2) {
-            MOE_BF16_STEP(0, ra0, rb0, ks);
-            MOE_BF16_STEP(1, ra1, rb1, ks + 1);
+        if constexpr (NREG == 2) {
+            for (int ks = 0; ks < nks; ks += 2) {
+                MOE_BF16_STEP(0, ra0, rb0, ks);
+                MOE_BF16_STEP(1, ra1, rb1, ks + 1);
+            }
+        } else {
+            MOE_BF16_LOAD(ra2, rb2, min(2, nks - 1));
+            for (int ks = 0; ks < nks; ks += 6) {
+                MOE_BF16_STEP(0, ra0, rb0, ks);
+                MOE_BF16_STEP(1, ra1, rb1, ks + 1);
+                if (ks + 2 >= nks) break;
+                MOE_BF16_STEP(0, ra2, rb2, ks + 2);
+                MOE_BF16_STEP(1, ra0, rb0, ks + 3);
+                if (ks + 4 >= nks) break;
+                MOE_BF16_STEP(0, ra1, rb1, ks + 4);
+                MOE_BF16_STEP(1, ra2, rb2, ks + 5);
+            }
         }
 #undef MOE_BF16_STEP
 #undef MOE_BF16_LOAD
@@ -164,42 +180,43 @@ void gemm_bf16_kernel(
     }
 }
 
-// Tile shape of the bf16 products: M tile rows (the plan's tile size) and
-// panel rows per work item.
-constexpr int kBf16WM = 4;             // 4 x 2 waves: 128-row M tiles
+// Tile shape of the bf16 products: 128-row M tiles (4 x 2 waves), 256 panel
+// rows per item (halves the token-row re-reads per flop compared with 128),
+// three register stages; one workgroup per CU (96 KB of LDS).
+constexpr int kBf16WM = 4;
 constexpr int kBf16TileM = 32 * kBf16WM;
-constexpr int kBf16BN = 128;
+constexpr int kBf16NReg = 3;
 
 int bf16_tile_m() { return kBf16TileM; }
 
-template <int WM, int BN, bool SWIGLU>
+template <int WM, int BN, bool SWIGLU, int NREG>
 static int gemm_grid() {
-    static const int g = resident_grid((const void*)gemm_bf16_kernel<WM, BN, SWIGLU>, kGemmThreads,
-                                       device_cu_count());
+    static const int g = resident_grid((const void*)gemm_bf16_kernel<WM, BN, SWIGLU, NREG>,
+                                       kGemmThreads, device_cu_count());
     return g;
+}
+
+template <int BN, bool SWIGLU>
+static void launch_bf16(const uint16_t* A, const uint16_t* B, const GroupedPlan& pl, int K,
+                        int n_out, int b_rows, int topk, uint16_t* C, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, BN, SWIGLU, kBf16NReg>),
+                       dim3(gemm_grid<kBf16WM, BN, SWIGLU, kBf16NReg>()), dim3(kGemmThreads), 0, s,
+                       A, B, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, K, n_out,
+                       b_rows, topk, C);
 }
 
 hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& pl,
                               int H, int F, int k, uint16_t* h, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, kBf16BN, true>),
-                       dim3(gemm_grid<kBf16WM, kBf16BN, true>()), dim3(kGemmThreads), 0, s, x, w13,
-                       pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k,
-                       h);
+    if (F % 128 == 0) launch_bf16<256, true>(x, w13, pl, H, F, 2 * F, k, h, s);
+    else launch_bf16<128, true>(x, w13, pl, H, F, 2 * F, k, h, s);
     return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& pl, int H,
                             int F, uint16_t* y, hipStream_t s) {
-    if (H % kBf16BN == 0)
-        hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, kBf16BN, false>),
-                           dim3(gemm_grid<kBf16WM, kBf16BN, false>()), dim3(kGemmThreads), 0, s, h,
-                           w2, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F, H, H,
-                           1, y);
-    else
-        hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, 64, false>),
-                           dim3(gemm_grid<kBf16WM, 64, false>()), dim3(kGemmThreads), 0, s, h, w2,
-                           pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F, H, H, 1,
-                           y);
+    if (H % 256 == 0) launch_bf16<256, false>(h, w2, pl, F, H, H, 1, y, s);
+    else if (H % 128 == 0) launch_bf16<128, false>(h, w2, pl, F, H, H, 1, y, s);
+    else launch_bf16<64, false>(h, w2, pl, F, H, H, 1, y, s);
     return hipGetLastError();
 }
 

@@ -47,8 +47,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             ev[i] = s < s1 ? idx[s] : -1;
         }
 #pragma unroll
-        for (int i = 0; i < kPlanRegs; ++i)
+        for (int i = 0; i < kPlanRegs; ++i) {
+            if (cb + kWave * i >= s1) break;  // wave-uniform: past this wave's run
             if ((unsigned)ev[i] < (unsigned)E) atomicAdd(&base[wave][ev[i]], 1);
+        }
     }
     __syncthreads();
 
@@ -111,6 +113,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         }
     }
     if (tid == 0) *ntiles = tile_sh[E];
+    // absolute base of each (wave, expert) run: one LDS read per scatter step
+    for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) base[i / E][i % E] += off_sh[i % E];
+    __syncthreads();
 
     // pass 2: stable scatter in slot order; each wave only touches its own
     // row of `base`
@@ -123,6 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         }
 #pragma unroll
         for (int i = 0; i < kPlanRegs; ++i) {
+            if (cb + kWave * i >= s1) break;  // wave-uniform: past this wave's run
             const int s = cb + kWave * i + lane;
             const int e = ev[i];
             const bool valid = (unsigned)e < (unsigned)E;
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             int rank = 0, pos = -1;
             if (valid) {
                 rank = __popcll(same & ((1ull << lane) - 1ull));
-                pos = off_sh[e] + base[wave][e] + rank;
+                pos = base[wave][e] + rank;
                 perm[pos] = s;
             }
             if (s < s1) inv[s] = pos;
