@@ -92,7 +92,8 @@ int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_
  * and inspection:  offs[0] counts[E] int32, offs[1] offsets[E+1] int32,
  * offs[2] perm[T*k] int32, offs[3] inv[T*k] int32, offs[4] h (bf16 [T*k,F]
  * for prefill, fp8 codes [T*k,F] for fp8), offs[5] h scales (fp32
- * [T*k,F/128], fp8 only), offs[6] y (bf16 [T*k,H], row = flat slot id).
+ * [T*k,F/128], fp8 only), offs[6] y (bf16 [T*k,H], expert order like h:
+ * row m holds slot perm[m]).
  * Entries a variant does not use are SIZE_MAX.  The decode fast path
  * (T <= 4) builds no plan in the workspace.
  */

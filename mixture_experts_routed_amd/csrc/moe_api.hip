@@ -149,7 +149,7 @@ int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* ga
     if (rc) return rc;
     rc = launched(launch_down_bf16(h, down, pl, H, F, y, s));
     if (rc) return rc;
-    return launched(launch_combine(y, idx, w, T, k, E, H, out, s));
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, T, k, H, out, s));
 }
 
 int check_bf16_args(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
@@ -287,7 +287,7 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
     if (rc) return rc;
     rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
     if (rc) return rc;
-    return launched(launch_combine(y, top_k_index, top_k_weights, T, k, E, H, out, stream));
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, T, k, H, out, stream));
 }
 
 int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,

@@ -56,6 +56,27 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Two fp32 -> two bf16 in one word (lo in bits 0-15), round to nearest even
+// by the gfx950 hardware convert.
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    const uint16_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+    const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+// SiLU for the grouped-product epilogues: z * 1 / (1 + 2^(-z log2 e)) with
+// the hardware exp2 and reciprocal (about 1 ulp each, so a relative error
+// near 1e-6, far below the bf16 rounding of the result).  Large negative z
+// gives 2^+inf = inf and a zero reciprocal, i.e. -0; large positive z gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// Value of lane l ^ 1 (swap within lane pairs; a DPP quad permutation).
+__device__ __forceinline__ float pair_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
 // ------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

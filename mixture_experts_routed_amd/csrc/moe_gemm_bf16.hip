@@ -13,196 +13,270 @@
 
 namespace moe {
 
-constexpr int kGemmThreads = 512;  // 8 waves
-constexpr int kBK = 64;            // bf16 K elements per stage (128 bytes per row)
+constexpr int kGemmThreads = 512;  // 8 waves: a 4 (M) x 2 (N) grid of 64 x BN/2 wave tiles
+constexpr int kBM = 256;           // rows of an M tile (about one expert's rows at prefill sizes)
+constexpr int kBK = 64;            // bf16 K elements per stage: one 128-byte line per row
+constexpr int kAStages = 2;        // token-row stages (L2 hits mostly): loads run 1 step ahead
+constexpr int kBStages = 3;        // weight stages (HBM): loads run 2 steps ahead
 
-// One work item = (M tile of <= BM = 32*WM rows of one expert) x (BN rows of
-// the expert's weight panel).  Waves form a WM x WN grid; wave (wm, wn) owns
-// rows [32wm, 32wm+32) and 32*NBW panel rows.  Both operands go through a
-// 2-stage LDS ring: every thread moves whole 16-byte chunks with 8 lanes per
-// 128-byte row segment (coalesced global reads), chunks XOR-swizzled for the
-// 64-bank LDS; the MFMA fragments are then read from LDS.  Loads run NREG
-// k-steps ahead in NREG register stages (named arrays with constant
-// indices, no branch around any load, so the compiler waits for exactly the
-// stage it consumes).  Rows past an M tile's end load row 0 (valid memory) and their
-// outputs are never stored.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: the wave writes
+// 1 KB at `dst` (wave-uniform), lane L's bytes at dst + 16 L.  Counted by
+// vmcnt like a load; no VGPRs are involved.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Workgroup barrier once this wave has at most N vector-memory operations in
+// flight (its older LDS fills have landed) and no LDS operation pending.  The
+// empty asm statements keep the compiler from moving memory operations
+// across it; the explicit wait replaces the vmcnt(0) a __syncthreads() fence
+// would force while later stages are still loading.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier once this wave's LDS reads are done (vector-memory
+// operations may stay in flight): closes an item, so that no wave refills a
+// ring slot another wave is still reading.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
+// expert's weight panel).  Wave (wm, wn) owns tile rows [64wm, 64wm+64) as two
+// 32-row blocks and panel rows [wn*BN/2, (wn+1)*BN/2) as NB 32-row blocks.
+// Operands stream through LDS rings filled by direct global->LDS loads, one
+// whole 128-byte line per row and stage (on MI355X, half-line requests halve
+// what L2 delivers per CU).  Each lane fetches the global chunk that belongs
+// at its fixed LDS position, so the bank swizzle costs nothing.  The token
+// rows have two stages and the weight rows three: weights come from HBM and
+// need the longer lead; together they fill the 160 KB of LDS.  Rows past an
+// M tile's end load row 0 (valid memory) and their outputs are never stored.
 // SWIGLU: panel rows are interleaved in blocks of 32 as gate, up, gate, up,
 // ... so each wave holds matching gate/up accumulators lane for lane, and the
 // epilogue writes h = silu(gate) * up as bf16 [P, F] in expert order.
-// Otherwise the epilogue writes y[slot, col] bf16 with slot = perm[row].
-template <int WM, int BN, bool SWIGLU, int NREG>
+// Otherwise the epilogue writes y bf16 [P, n_out] in expert order too (the
+// combine finds a slot's row through the plan's inverse permutation).
+template <int BN, bool SWIGLU>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
     uint16_t* __restrict__ C) {
-    constexpr int WN = 8 / WM;
-    constexpr int BM = 32 * WM;
-    constexpr int NBW = BN / (32 * WN);  // 32-wide accumulator blocks per wave
-    constexpr int A_PER = BM * 8 / kGemmThreads;
-    constexpr int B_PER = BN * 8 / kGemmThreads;
-    static_assert(WM * WN == 8 && NBW >= 1 && A_PER >= 1 && B_PER >= 1, "bad tile shape");
-    static_assert(!SWIGLU || NBW % 2 == 0, "SwiGLU needs gate/up block pairs per wave");
-    static_assert(NREG == 2 || NREG == 3, "two or three register stages");
-    __shared__ u32x4 a_lds[2][BM][8];
-    __shared__ u32x4 b_lds[2][BN][8];
+    constexpr int MB = 2;                     // 32-row blocks per wave
+    constexpr int NB = BN / 64;               // 32-row panel blocks per wave
+    constexpr int A_INST = kBM / 8 / 8;       // 8 rows per wave load; per wave and stage
+    constexpr int B_INST = BN / 8 / 8;
+    constexpr int A_STAGE = kBM * 8;          // u32x4 per stage
+    constexpr int B_STAGE = BN * 8;
+    constexpr int B_BASE = kAStages * A_STAGE;
+    static_assert(NB >= 1 && B_INST >= 1 && (!SWIGLU || NB % 2 == 0), "bad panel width");
+    // one array for both operands (with fills into two arrays the compiler
+    // adds a wait for all of them before every LDS read)
+    __shared__ u32x4 lds[kAStages * A_STAGE + kBStages * B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WM, wn = wave / WM;
-    const int chunk = tid & 7, row_t = tid >> 3;
+    const int wm = wave & 3, wn = wave >> 2;
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
     const int items = ntiles * n_tiles_n;
     const int nks = K / kBK;
-    const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32*b + lane%32
+    const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32 b + lane % 32
+    const int lrow = lane >> 3, lslot = lane & 7;
 
-    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+    // Per-item state: which tile, and every lane's row pointers for its
+    // share of the LDS fills.
+    struct Item {
+        int e, nt, row0, mrows;
+        const uint16_t* a_src[A_INST];
+        const uint16_t* b_src[B_INST];
+    };
+    auto setup = [&](int it, Item& m) {
         const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
-        const int nt = gi.nt, mt = gi.mt, e = gi.e;
-        const int row0 = tiles[2 * mt + 1];
-        const int mrows = min(BM, offsets[e + 1] - row0);
-        const bool active = 32 * wm < mrows;
-
-        const uint16_t* a_src[A_PER];
+        m.e = gi.e;
+        m.nt = gi.nt;
+        m.row0 = tiles[2 * gi.mt + 1];
+        m.mrows = min(kBM, offsets[m.e + 1] - m.row0);
+        // token rows of the tile (all slot ids requested at once, no branch)
+        int pr[A_INST];
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int r = row_t + 64 * i;
-            int64_t arow = 0;
-            if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
-            a_src[i] = A + arow * K + chunk * 8;
+        for (int i = 0; i < A_INST; ++i) {
+            const int r = 8 * (A_INST * wave + i) + lrow;
+            pr[i] = SWIGLU ? perm[m.row0 + min(r, m.mrows - 1)] : 0;
         }
-        // thread rows row_t + 64 i of the panel: 64 panel rows are 32 weight
-        // rows apart when gate/up interleave in blocks of 32, else 64
-        int brow0;
-        if (SWIGLU) {
-            const int blk = row_t >> 5;
-            brow0 = ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (row_t & 31);
-        } else {
-            brow0 = nt * BN + row_t;
-        }
-        const uint16_t* b_src = B + ((int64_t)e * b_rows + brow0) * K + chunk * 8;
-        const int64_t b_step = (int64_t)(SWIGLU ? 32 : 64) * K;
-
-        f32x16 acc[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x16{};
-        u32x4 ra0[A_PER], ra1[A_PER], ra2[A_PER], rb0[B_PER], rb1[B_PER], rb2[B_PER];
-
-#define MOE_BF16_LOAD(RA, RB, KS)                                                             \
-    do {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) RA[i] =                             \
-            *(const u32x4*)(a_src[i] + (KS) * kBK);                                           \
-        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) RB[i] =                             \
-            *(const u32x4*)(b_src + i * b_step + (KS) * kBK);                                 \
-    } while (0)
-
-#define MOE_BF16_STEP(S, RA, RB, KS)                                                          \
-    do {                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < A_PER; ++i) {                                   \
-            const int rr = row_t + 64 * i;                                                    \
-            a_lds[S][rr][lds_chunk(rr, chunk)] = RA[i];                                       \
-        }                                                                                     \
-        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) {                                   \
-            const int rr = row_t + 64 * i;                                                    \
-            b_lds[S][rr][lds_chunk(rr, chunk)] = RB[i];                                       \
-        }                                                                                     \
-        __syncthreads();                                                                      \
-        if (active && (KS) < nks) {                                                           \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                \
-                const int c = (kk * 2 + (lane >> 5)) ^ fsw;                                   \
-                const u32x4 af = a_lds[S][32 * wm + (lane & 31)][c];                          \
-                u32x4 bf[NBW];                                                                \
-                _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) bf[nb] =                   \
-                    b_lds[S][(wn * NBW + nb) * 32 + (lane & 31)][c];                          \
-                _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) acc[nb] =                  \
-                    mfma_bf16_32x32x16(af, bf[nb], acc[nb]);                                  \
-            }                                                                                 \
-        }                                                                                     \
-        MOE_BF16_LOAD(RA, RB, min((KS) + NREG, nks - 1));                                     \
-    } while (0)
-
-        // NREG register stages (loads run NREG k-steps ahead) over a two-stage
-        // LDS ring: LDS stage ks % 2, register stage ks % NREG
-        MOE_BF16_LOAD(ra0, rb0, 0);
-        MOE_BF16_LOAD(ra1, rb1, min(1, nks - 1));
-        if constexpr (NREG == 2) {
-            for (int ks = 0; ks < nks; ks += 2) {
-                MOE_BF16_STEP(0, ra0, rb0, ks);
-                MOE_BF16_STEP(1, ra1, rb1, ks + 1);
-            }
-        } else {
-            MOE_BF16_LOAD(ra2, rb2, min(2, nks - 1));
-            for (int ks = 0; ks < nks; ks += 6) {
-                MOE_BF16_STEP(0, ra0, rb0, ks);
-                MOE_BF16_STEP(1, ra1, rb1, ks + 1);
-                if (ks + 2 >= nks) break;
-                MOE_BF16_STEP(0, ra2, rb2, ks + 2);
-                MOE_BF16_STEP(1, ra0, rb0, ks + 3);
-                if (ks + 4 >= nks) break;
-                MOE_BF16_STEP(0, ra1, rb1, ks + 4);
-                MOE_BF16_STEP(1, ra2, rb2, ks + 5);
-            }
+        for (int i = 0; i < A_INST; ++i) {
+            const int r = 8 * (A_INST * wave + i) + lrow;
+            const int64_t arow = r < m.mrows ? (SWIGLU ? pr[i] / topk : m.row0 + r) : 0;
+            m.a_src[i] = A + arow * K + lds_chunk(r, lslot) * 8;
         }
-#undef MOE_BF16_STEP
-#undef MOE_BF16_LOAD
-        __syncthreads();  // the next item's first LDS write must not overtake these reads
-
-        if (active) {
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i) {
+            const int r = 8 * (B_INST * wave + i) + lrow;
+            int brow;
             if (SWIGLU) {
-#pragma unroll
-                for (int p = 0; p < NBW / 2; ++p) {
-                    const int f = nt * (BN / 2) + (wn * NBW / 2 + p) * 32 + (lane & 31);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int row = 32 * wm + acc_row(q, lane);
-                        if (row < mrows) {
-                            const float hv = silu(acc[2 * p][q]) * acc[2 * p + 1][q];
-                            C[(int64_t)(row0 + row) * n_out + f] = (uint16_t)f32_to_bf16(hv);
-                        }
-                    }
-                }
+                const int blk = r >> 5;
+                brow = ((blk & 1) ? n_out : 0) + m.nt * (BN / 2) + (blk >> 1) * 32 + (r & 31);
             } else {
+                brow = m.nt * BN + r;
+            }
+            m.b_src[i] = B + ((int64_t)m.e * b_rows + brow) * K + lds_chunk(r, lslot) * 8;
+        }
+    };
+    // every wave issues the same number of loads per step, also when the
+    // step index is clamped past the end (those fill unread slots)
+    auto load_a = [&](const Item& m, int ks) {
+        u32x4* dst = &lds[(ks & 1) * A_STAGE];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = 32 * wm + acc_row(q, lane);
-                    if (row < mrows) {
-                        const int64_t slot = perm[row0 + row];
+        for (int i = 0; i < A_INST; ++i) dma16(m.a_src[i] + ks * kBK, dst + (A_INST * wave + i) * 64);
+    };
+    auto load_b = [&](const Item& m, int ks) {
+        u32x4* dst = &lds[B_BASE + (ks % kBStages) * B_STAGE];
 #pragma unroll
-                        for (int nb = 0; nb < NBW; ++nb) {
-                            const int col = nt * BN + (wn * NBW + nb) * 32 + (lane & 31);
-                            C[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
+        for (int i = 0; i < B_INST; ++i) dma16(m.b_src[i] + ks * kBK, dst + (B_INST * wave + i) * 64);
+    };
+    // the first stages of an item: A(0), B(0), B(1)
+    auto prologue = [&](const Item& m) {
+        load_a(m, 0);
+        load_b(m, 0);
+        load_b(m, min(1, nks - 1));
+    };
+
+    f32x16 acc[MB][NB];
+    // Waves past the tile's last row compute too (on row-0 data, never
+    // stored): a branch here would make the compiler wait for every LDS
+    // fill in flight before the fragment reads.
+    auto compute = [&](int ks) {
+        const u32x4* as = &lds[(ks & 1) * A_STAGE];
+        const u32x4* bs = &lds[B_BASE + (ks % kBStages) * B_STAGE];
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int c = (kk * 2 + (lane >> 5)) ^ fsw;
+            u32x4 af[MB], bf[NB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) af[mb] = as[(64 * wm + 32 * mb + (lane & 31)) * 8 + c];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) bf[nb] = bs[((wn * NB + nb) * 32 + (lane & 31)) * 8 + c];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[mb][nb] = mfma_bf16_32x32x16(af[mb], bf[nb], acc[mb][nb]);
+        }
+    };
+
+    // Stores of the finished tile.  Lanes l and l ^ 1 hold neighbouring
+    // columns of the same rows; after one swap the even lane owns columns
+    // (c, c+1) of row R(q) and the odd lane columns (c-1, c) of row R(q+1),
+    // so every store writes a bf16 pair.
+    auto epilogue = [&](const Item& m) {
+        const bool odd = lane & 1;
+        if (64 * wm >= m.mrows) return;
+        if (SWIGLU) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int p = 0; p < NB / 2; ++p) {
+                    const int f = m.nt * (BN / 2) + (wn * NB / 2 + p) * 32 + (lane & 31);
+#pragma unroll
+                    for (int q = 0; q < 16; q += 2) {
+                        const float h0 = silu_fast(acc[mb][2 * p][q]) * acc[mb][2 * p + 1][q];
+                        const float h1 = silu_fast(acc[mb][2 * p][q + 1]) * acc[mb][2 * p + 1][q + 1];
+                        const float got = pair_swap(odd ? h0 : h1);
+                        const int row = 64 * wm + 32 * mb + acc_row(q, lane) + (odd ? 1 : 0);
+                        if (row < m.mrows) {
+                            const uint32_t v = odd ? pack_bf16x2_hw(got, h1) : pack_bf16x2_hw(h0, got);
+                            *(uint32_t*)(C + (int64_t)(m.row0 + row) * n_out + (f & ~1)) = v;
                         }
                     }
                 }
-            }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 16; q += 2) {
+                    const int row = 64 * wm + 32 * mb + acc_row(q, lane) + (odd ? 1 : 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const float y0 = acc[mb][nb][q], y1 = acc[mb][nb][q + 1];
+                        const float got = pair_swap(odd ? y0 : y1);
+                        const int col = m.nt * BN + (wn * NB + nb) * 32 + (lane & 30);
+                        if (row < m.mrows) {
+                            const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
+                            *(uint32_t*)(C + (int64_t)(m.row0 + row) * n_out + col) = v;
+                        }
+                    }
+                }
         }
+    };
+
+    int it = xcd_slot(blockIdx.x, gridDim.x);
+    if (it >= items) return;
+    Item cur;
+    setup(it, cur);
+    prologue(cur);
+    while (true) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+        // first stage: wait for everything (the previous item's epilogue
+        // stores are vector-memory operations too)
+        stage_barrier<0>();
+        load_a(cur, min(1, nks - 1));
+        load_b(cur, min(2, nks - 1));
+        compute(0);
+        // issue order per step: A(ks+1), then B(ks+2); at step ks the newest
+        // B_INST operations (B(ks+1)) may still be in flight
+        for (int ks = 1; ks < nks; ++ks) {
+            stage_barrier<B_INST>();           // A(ks) and B(ks) have landed for every wave
+            load_a(cur, min(ks + 1, nks - 1)); // refills the A slot read at step ks - 1
+            load_b(cur, min(ks + 2, nks - 1)); // refills the B slot read at step ks - 1
+            compute(ks);
+        }
+        lds_barrier();  // every wave is done with the ring before the next item's fills
+
+        // The next item's first stages load while this tile is stored (on the
+        // last item the same tile is fetched again and never read).
+        const int next = it + gridDim.x;
+        const bool more = next < items;
+        Item nxt;
+        setup(more ? next : it, nxt);
+        prologue(nxt);
+        epilogue(cur);
+        if (!more) break;
+        it = next;
+        cur = nxt;
     }
+    __builtin_amdgcn_s_waitcnt(0);  // no LDS fill may outlive the workgroup
 }
 
-// Tile shape of the bf16 products: 128-row M tiles (4 x 2 waves), 256 panel
-// rows per item (halves the token-row re-reads per flop compared with 128),
-// three register stages; one workgroup per CU (96 KB of LDS).
-constexpr int kBf16WM = 4;
-constexpr int kBf16TileM = 32 * kBf16WM;
-constexpr int kBf16NReg = 3;
+int bf16_tile_m() { return kBM; }
 
-int bf16_tile_m() { return kBf16TileM; }
-
-template <int WM, int BN, bool SWIGLU, int NREG>
+template <int BN, bool SWIGLU>
 static int gemm_grid() {
-    static const int g = resident_grid((const void*)gemm_bf16_kernel<WM, BN, SWIGLU, NREG>,
-                                       kGemmThreads, device_cu_count());
+    static const int g = resident_grid((const void*)gemm_bf16_kernel<BN, SWIGLU>, kGemmThreads,
+                                       device_cu_count());
     return g;
 }
 
 template <int BN, bool SWIGLU>
 static void launch_bf16(const uint16_t* A, const uint16_t* B, const GroupedPlan& pl, int K,
                         int n_out, int b_rows, int topk, uint16_t* C, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<kBf16WM, BN, SWIGLU, kBf16NReg>),
-                       dim3(gemm_grid<kBf16WM, BN, SWIGLU, kBf16NReg>()), dim3(kGemmThreads), 0, s,
-                       A, B, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, K, n_out,
-                       b_rows, topk, C);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BN, SWIGLU>), dim3(gemm_grid<BN, SWIGLU>()),
+                       dim3(kGemmThreads), 0, s, A, B, pl.perm, pl.tiles, pl.ntiles, pl.tile_off,
+                       pl.offsets, pl.E, K, n_out, b_rows, topk, C);
 }
 
 hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& pl,
@@ -221,13 +295,13 @@ hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const Grouped
 }
 
 // ------------------------------------------------------------------ combine
-// One thread per (token, 8 columns): out = sum_j w[t,j] * y[t*k+j] in slot
-// order, fp32, one rounding to bf16.  Dropped slots contribute nothing.
+// One thread per (token, 8 columns): out = sum_j w[t,j] * y[inv[t*k+j]] in
+// slot order, fp32, one rounding to bf16.  y is in expert order; inv (from
+// the plan) is -1 for dropped slots, which contribute nothing.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
-                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int64_t T,
-                                                      int k, int E, int H,
-                                                      uint16_t* __restrict__ out) {
+                                                      int k, int H, uint16_t* __restrict__ out) {
     const int cpr = H / 8;
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= T * cpr) return;
@@ -235,10 +309,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     const int c = (int)(g - t * cpr) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
-        const int e = idx[t * k + j];
-        if ((unsigned)e >= (unsigned)E) continue;
+        const int r = inv[t * k + j];
+        if (r < 0) continue;
         const float wt = w[t * k + j];
-        const uint4 v = *(const uint4*)(y + (t * k + j) * H + c);
+        const uint4 v = *(const uint4*)(y + (int64_t)r * H + c);
         float f[8];
         unpack8(v, f);
 #pragma unroll
@@ -252,11 +326,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     *(uint4*)(out + t * H + c) = o;
 }
 
-hipError_t launch_combine(const uint16_t* y, const int32_t* idx, const float* w, int64_t T, int k,
-                          int E, int H, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int k,
+                          int H, uint16_t* out, hipStream_t s) {
     const int64_t n = T * (H / 8);
     const int blocks = (int)((n + 255) / 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y, idx, w, T, k, E, H, out);
+    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, T, k, H, out);
     return hipGetLastError();
 }
 

@@ -46,7 +46,8 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
 // SWIGLU: panel rows interleave gate/up in blocks of 32 (as the bf16 path);
 // one item covers a whole 128-wide h block split over the WN = 2 column
 // waves, which exchange per-row partial maxima through LDS before the
-// block-128 re-quantisation.  Otherwise: y[slot, col] bf16.
+// block-128 re-quantisation.  Otherwise: y bf16 in expert order (row m of
+// the plan holds slot perm[m]).
 template <int WM, int BN, bool SWIGLU>
 __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
@@ -223,11 +224,10 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
             for (int q = 0; q < 16; ++q) {
                 const int row = 32 * wm + acc_row(q, lane);
                 if (row < mrows) {
-                    const int64_t slot = perm[row0 + row];
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
                         const int col = nt * BN + (wn * NBW + nb) * 32 + (lane & 31);
-                        Cy[slot * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
+                        Cy[(int64_t)(row0 + row) * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
                     }
                 }
             }

@@ -35,13 +35,13 @@ struct GroupedPlan {
 hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& plan,
                               int H, int F, int k, uint16_t* h, hipStream_t s);
 
-// down product -> y bf16 [P, H] indexed by flat slot id.
+// down product -> y bf16 [P, H] in expert order (row = position in perm).
 hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& plan, int H,
                             int F, uint16_t* y, hipStream_t s);
 
-// out[t] = sum_j w[t,j] * y[t*k+j] over valid slots, fp32 in slot order.
-hipError_t launch_combine(const uint16_t* y, const int32_t* idx, const float* w, int64_t T, int k,
-                          int E, int H, uint16_t* out, hipStream_t s);
+// out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots, fp32 in slot order.
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int k,
+                          int H, uint16_t* out, hipStream_t s);
 
 // Decode gather-GEMV (T small): phase 1 writes h fp32 [T*k, F] by slot id,
 // phase 2 does the down rows and the combine.  Limits of this form: T <= 4,

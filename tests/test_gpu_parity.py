@@ -211,7 +211,7 @@ def test_decode_shapes(shape):
 
 
 def test_stages_prefill():
-    """Layered check: h (bf16, expert order) and y (bf16, slot order) in the workspace."""
+    """Layered check: h and y (bf16, both in expert order) in the workspace."""
     moe = _moe()
     _say("prefill stages")
     T, H, F, E, k = 300, 256, 128, 5, 2
@@ -234,7 +234,7 @@ def test_stages_prefill():
         e = idx.reshape(-1)[s]
         gv = w13[e] @ x[s // k]
         h_ref[m] = orc.silu(gv[:F]) * gv[F:]
-        y_ref[s] = w2[e] @ h_ref[m]
+        y_ref[m] = w2[e] @ h_ref[m]
     check_tol(h, h_ref, (1e-2, 1e-2), "h stage")
     check_tol(y, y_ref, (1e-2, 1e-2), "y stage")
 
