@@ -2,17 +2,40 @@
 
 Default workload: DeepSeek-OCR-2-shaped decode, T=1 token, H=1280, F=896,
 64 experts, top-6, bf16 (the gather-GEMV entry point).  A step is one call of
-the whole layer (plan, gate_up + SwiGLU, down, combine) on one batch of
-resident synthetic inputs.  Each step uses a fresh routing and one of several
-copies of the weights, chosen so that the weights a step reads were not read
-by any of the recent steps; the MI355X's 256 MB last-level cache therefore
-cannot serve them, and they stream from HBM as in a real decode loop.
+the whole layer (routing plan or routing lookup, gate_up + SwiGLU, down,
+combine) on one batch of resident synthetic inputs.  Each step uses a fresh
+routing and one of several copies of the weights, chosen so that the weights
+a step reads were not read by any of the recent steps; the MI355X's 256 MB
+last-level cache therefore cannot serve them, and they stream from HBM as in
+a real decode loop.
+
+Two passes over the same steps:
+  A. the timed region: W untimed warm-up steps, then exactly K steps between
+     two synchronisations (value, ms_per_step, per-call percentiles);
+  B. the same K steps with the library's stage-timing recorder on: a HIP
+     event on the kernel's own stream before every kernel and after the
+     last, giving every kernel's mean duration.  The dominant kernel's
+     algorithmic bytes (or flops) per launch over that duration is
+     `roofline.achieved`.
+`roofline.traffic` is the HBM bytes per launch of that kernel from the
+committed rocprofv3 counter summary of this workload
+(profiles/hbm_<workload>.json, FETCH_SIZE and WRITE_SIZE scaled by a plain
+copy kernel), or null when the kernel sources changed since it was taken.
 
 Prints one JSON line.  --config picks another workload (ocr2_decode_t4,
 ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny).
+
+Helper modes (no GPU work of their own):
+  --copy-calibration        a plain 256 MiB device copy, for counter scaling
+  --summarize-stats CSV     markdown table from a rocprofv3 kernel_stats.csv
+  --summarize-pmc ...       HBM bytes per kernel from FETCH_SIZE/WRITE_SIZE runs
 """
 
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +51,39 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 # F=896, 64 experts, top-6, bf16): 0.191 ms per call on an NVIDIA GB10.
 PAGE_DECODE_T1_TOKENS_PER_S = 1.0 / 0.191e-3
 
+# kernel-name prefix -> stage, for matching rocprofv3 rows to recorder stages
+KERNEL_STAGES = [
+    ("moe::plan_kernel", "plan"),
+    ("moe::decode_slice_kernel", "decode_slices"),
+    ("moe::decode_combine_kernel", "combine"),
+    ("moe::combine_kernel", "combine"),
+    ("moe::gemm_bf16_kernel<", "gemm_bf16"),
+    ("moe::gemm_fp8_kernel<", "gemm_fp8"),
+]
+
+
+def kernel_stage(name):
+    name = name.replace("void ", "").split("(")[0]
+    for prefix, stage in KERNEL_STAGES:
+        if name.startswith(prefix):
+            if stage.startswith("gemm"):
+                return "gate_up" if ", true>" in name else "down"
+            return stage
+    return None
+
+
+def source_digest():
+    """sha256 over the kernel sources and the C header: counter figures taken
+    under another digest no longer describe these kernels."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "mixture_experts_routed_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -38,11 +94,17 @@ def parse():
     ap.add_argument("--sets", type=int, default=None, help="weight copies rotated over steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-pass", action="store_true", help="skip pass B (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (calibrates HBM counters)")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("CSV", "TITLE", "COMMAND"))
+    ap.add_argument("--summarize-pmc", nargs=6,
+                    metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV",
+                             "COMMAND"))
     return ap.parse_args()
 
 
+# ------------------------------------------------------------ helper modes
 def copy_calibration():
     """A plain copy of a known size: under rocprofv3 --pmc its FETCH_SIZE and
     WRITE_SIZE per dispatch give the counters' scale (expect 262144 KiB each)."""
@@ -59,24 +121,123 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
+def summarize_stats(path, title, command):
+    rows = list(csv.DictReader(open(path)))
+    print(f"# {title}\n\ncommand: `{command}`\n")
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        if not name.startswith("moe::") and "copyBuffer" not in name:
+            continue
+        print(f"| {name} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+              f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
+
+
+def _per_kernel(path, counter):
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Kernel_Name"].split("(")[0].replace("void ", "")].append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_pmc(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command):
+    """Per-kernel HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB) of
+    each moe:: kernel, scaled by what the same counters read for a plain
+    256 MiB copy.  Writes JSON (with the kernel-source digest) to stdout."""
+    copy_kib = 256 * 1024
+    cf = _per_kernel(copy_fetch_csv, "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    cw = _per_kernel(copy_write_csv, "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    f_scale = copy_kib / max(cf)   # the largest dispatch is the 256 MiB copy
+    w_scale = copy_kib / max(cw)
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    out = {"workload": workload, "command": command, "source_sha256": source_digest(),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "stages": {}}
+    for k in sorted(fetch):
+        st = kernel_stage(k)
+        if st is None:
+            continue
+        f = sum(fetch[k]) / len(fetch[k])
+        w = sum(write.get(k, [0.0])) / max(len(write.get(k, [])), 1)
+        out["stages"][st] = {"kernel": k, "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                             "hbm_bytes": int((f * f_scale + w * w_scale) * 1024)}
+    print(json.dumps(out, indent=1))
+
+
+# ------------------------------------------------------------ algorithmic work
+def stage_work(stage, kind, T, H, F, k, touched, valid):
+    """Algorithmic (bytes, flops) of one launch of `stage`: the weights of the
+    touched experts it reads (with their fp32 block scales for fp8) plus the
+    layer inputs/outputs it reads or writes; intermediates (h, y, partial
+    sums) are implementation overhead and are not counted."""
+    bw = 2 if kind == "bf16" else 1
+    sc = 0 if kind == "bf16" else 4.0 / 128
+    x_bytes = T * H * bw + (0 if kind == "bf16" else T * (H // 128) * 4)
+    out_bytes = T * H * 2
+    route_bytes = T * k * 8
+    gu_w = touched * 2 * F * H * (bw + sc)
+    dn_w = touched * H * F * (bw + sc)
+    if stage == "plan":
+        return T * k * 4, 0
+    if stage == "gate_up":
+        return gu_w + x_bytes, 2 * valid * 2 * F * H
+    if stage == "down":
+        return dn_w, 2 * valid * H * F
+    if stage == "combine":
+        return out_bytes + route_bytes, 2 * valid * H
+    if stage == "decode_slices":
+        return gu_w + dn_w + x_bytes + T * k * 4, 2 * valid * 3 * F * H
+    raise ValueError(stage)
+
+
 def algorithmic_bytes(kind, T, H, F, k, touched):
-    """Bytes the layer must move once: the touched experts' weights (plus
-    their fp32 block scales for fp8), activations in, bf16 out, routing."""
-    if kind == "bf16":
-        w = touched * 3 * F * H * 2
-        act = T * H * 2
-    else:
-        w = touched * (3 * F * H + 3 * F * H // 128 * 4)
-        act = T * H + T * (H // 128) * 4
-    return w + act + T * H * 2 + T * k * 8
+    """Bytes the whole layer must move once (every stage's share)."""
+    stages = ["gate_up", "down", "combine"]   # the plan's id read is in the combine's share
+    return sum(stage_work(s, kind, T, H, F, k, touched, 0)[0] for s in stages)
 
 
 def algorithmic_flops(valid_slots, H, F):
     return 2 * valid_slots * 3 * F * H
 
 
+def roofline_for(stage, kind, dtype, bytes_, flops, ms):
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    secs = ms * 1e-3
+    if flops > 0 and flops / max(bytes_, 1) > ridge:
+        ach = flops / secs / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4)}
+    ach = bytes_ / secs / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
+def committed_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from the committed counter summary, or
+    None if there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_sha256") != source_digest():
+        return None
+    st = d.get("stages", {}).get(stage)
+    return None if st is None else int(st["hbm_bytes"])
+
+
+# ------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -134,53 +295,50 @@ def main():
         dtype = "fp8"
     torch.cuda.synchronize()
 
-    # ---------------------------------------------------------------- timing
+    # ------------------------------------------------------- pass A: timing
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record()
     for i in range(steps):
-        ev[i][0].record()
         step(warmup + i)
-        ev[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     ms_per_step = total_ms / steps
 
     # ------------------------------------------------------ algorithmic work
-    bytes_per_call, flops_per_call = [], []
+    touched_l, valid_l = [], []
     for i in range(steps):
         idx = routes[warmup + i][0].cpu().numpy().reshape(-1)
         valid = idx[(idx >= 0) & (idx < E)]
-        bytes_per_call.append(algorithmic_bytes(kind, T, H, F, k, len(np.unique(valid))))
-        flops_per_call.append(algorithmic_flops(valid.size, H, F))
-    mean_bytes = float(np.mean(bytes_per_call))
-    mean_flops = float(np.mean(flops_per_call))
-    mean_us = float(per_call_us.mean())
+        touched_l.append(len(np.unique(valid)))
+        valid_l.append(valid.size)
+    touched, valid = float(np.mean(touched_l)), float(np.mean(valid_l))
+    mean_bytes = algorithmic_bytes(kind, T, H, F, k, touched)
+    mean_flops = algorithmic_flops(valid, H, F)
+    mean_us = ms_per_step * 1e3
 
-    hbm_gbs = mean_bytes / (mean_us * 1e-6) / 1e9
-    tflops = mean_flops / (mean_us * 1e-6) / 1e12
-    bound = "hbm" if (decode or name == "v3_fp8_decode" or name == "ocr2_prefill") else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        peak = MFMA_PEAK_TFLOPS[dtype]
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": None}
-    roof["kernel"] = "whole layer per call (HIP events around each call)"
+    # ------------------------------------- pass B: per-kernel stage timing
+    stages = {}
+    if not args.no_stage_pass:
+        moe.moe_profile_begin(steps)
+        for i in range(steps):
+            step(warmup + i)
+        torch.cuda.synchronize()
+        calls = moe.moe_profile_end(steps)
+        per = collections.defaultdict(list)
+        for row in calls:
+            for st, ms in row:
+                per[st].append(ms)
+        stages = {st: float(np.mean(v)) for st, v in per.items()}
+        kernel_us = np.array([sum(ms for _, ms in row) * 1e3 for row in calls])
 
-    value = T / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
@@ -188,18 +346,37 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": (round(value / PAGE_DECODE_T1_TOKENS_PER_S, 3) if name == "ocr2_decode_t1" else None),
+        "vs_baseline": None,
         "dtype": dtype,
-        "data": "synthetic",
+        "data": "synthetic (seeded generators; random-init weights of the named shapes)",
         "config": {"workload": name, "T": T, "H": H, "F": F, "E": E, "top_k": k,
                    "weight_copies_rotated": sets},
-        "us_per_call": {"mean": round(mean_us, 2), "p10": round(float(np.percentile(per_call_us, 10)), 2),
-                        "p50": round(float(np.percentile(per_call_us, 50)), 2),
-                        "p90": round(float(np.percentile(per_call_us, 90)), 2)},
-        "algorithmic": {"bytes_per_call": int(mean_bytes), "flops_per_call": int(mean_flops),
-                        "hbm_GBps": round(hbm_gbs, 1), "TFLOPps": round(tflops, 3)},
-        "roofline": roof,
     }
+    value = T / (ms_per_step * 1e-3)
+    out["value"] = round(value, 1)
+    out["vs_baseline"] = round(value / PAGE_DECODE_T1_TOKENS_PER_S, 3) if name == "ocr2_decode_t1" else None
+    out["us_per_call"] = round(mean_us, 2)
+    if stages:   # kernel time per call (pass B), without the gaps between launches
+        out["kernel_us_per_call"] = {"mean": round(float(kernel_us.mean()), 2),
+                                     "p10": round(float(np.percentile(kernel_us, 10)), 2),
+                                     "p50": round(float(np.percentile(kernel_us, 50)), 2),
+                                     "p90": round(float(np.percentile(kernel_us, 90)), 2)}
+    out["layer"] = {"algorithmic_bytes_per_call": int(mean_bytes),
+                    "algorithmic_flops_per_call": int(mean_flops),
+                    "touched_experts": round(touched, 2),
+                    "hbm_GBps": round(mean_bytes / (mean_us * 1e-6) / 1e9, 1),
+                    "TFLOPps": round(mean_flops / (mean_us * 1e-6) / 1e12, 3)}
+    if stages:
+        out["stage_us"] = {st: round(ms * 1e3, 2) for st, ms in stages.items()}
+        dom = max(stages, key=stages.get)
+        b, f = stage_work(dom, kind, T, H, F, k, touched, valid)
+        roof = roofline_for(dom, kind, dtype, b, f, stages[dom])
+        roof["traffic"] = committed_traffic(name, dom)
+        roof["kernel"] = dom
+        roof["kernel_us"] = round(stages[dom] * 1e3, 2)
+        roof["algorithmic_bytes_per_launch"] = int(b)
+        roof["algorithmic_flops_per_launch"] = int(f)
+        out["roofline"] = roof
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:

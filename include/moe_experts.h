@@ -28,8 +28,9 @@
  *  - `out` is fully overwritten (never accumulated into).
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *    default stream).  No call allocates memory, synchronises, or copies
- *    between host and device.  The library keeps no mutable global state;
- *    concurrent calls are safe when each has its own workspace.
+ *    between host and device.  The library keeps no mutable global state
+ *    apart from the optional stage-timing recorder (moe_profile_*, off by
+ *    default); concurrent calls are safe when each has its own workspace.
  *  - Results are deterministic: the combine is a gather-reduce in slot order
  *    and no floating-point atomics are used anywhere.
  *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Argument errors
@@ -95,7 +96,8 @@ int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_
  * [T*k,F/128], fp8 only), offs[6] y (bf16 [T*k,H], expert order like h:
  * row m holds slot perm[m]).
  * Entries a variant does not use are SIZE_MAX.  The decode fast path
- * (T <= 4) builds no plan in the workspace.
+ * (T <= 4) builds no plan and keeps no h: its workspace holds fp32 partial
+ * down products only, and every entry but the total is SIZE_MAX.
  */
 int moe_workspace_layout(int variant, int64_t T, int H, int F, int E, int k, size_t offs[8]);
 
@@ -135,8 +137,11 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
  * bf16 routed experts, gather-GEMV form for a handful of tokens (the model
  * card's decode op: two kernels, no per-expert loop on the host, no
  * device-to-host synchronisation).  Same operands and results contract as
- * moe_experts_prefill.  For T <= 4 only the selected experts' weight rows are
- * streamed, each once, and h stays fp32; larger T runs the grouped-GEMM path.
+ * moe_experts_prefill.  For T <= 4 (T*k <= 32, H and F <= 2048, and
+ * T * ceil(H / 512) <= 12, i.e. H <= 1536 at T = 4) only the
+ * selected experts' weights are streamed, each byte once; h and the partial
+ * down products stay fp32 and are added in a fixed order (deterministic).
+ * Larger calls run the grouped-GEMM path.
  */
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
                        const int32_t* top_k_index, const float* top_k_weights,
@@ -177,6 +182,36 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale,
  */
 int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K,
                               uint8_t* codes, float* scales, hipStream_t stream);
+
+/*
+ * Stage timing, for measurement (not needed for normal use).
+ * moe_profile_begin(max_calls) switches the recorder on: each of the next
+ * max_calls layer calls (moe_experts_prefill / _decode / _fp8, from any host
+ * thread) launches every kernel with a start/stop HIP event pair attached to
+ * that kernel's own dispatch (hipExtLaunchKernelGGL), on the stream it runs
+ * on, so each pair times exactly one kernel's execution.  Creating the
+ * events is the only allocation and happens here.
+ * moe_profile_end(max_calls, &n, ms, ids) waits for those events, switches the
+ * recorder off and writes, for the first n <= max_calls recorded calls,
+ * ms[c * MOE_PROFILE_MAX_STAGES + i] = milliseconds of the call's i-th kernel
+ * and ids[...] = its MOE_STAGE_* (-1 and -1.0 past the call's last kernel).
+ * ms and ids hold max_calls * MOE_PROFILE_MAX_STAGES entries (host memory).
+ * Calls made while begin/end run on another thread race with them.
+ * Errors: MOE_ERR_SHAPE (max_calls outside [1, MOE_PROFILE_MAX_CALLS]),
+ * MOE_ERR_NULL, MOE_ERR_LAUNCH (event creation or query failed),
+ * MOE_ERR_DEVICE.
+ */
+#define MOE_PROFILE_MAX_STAGES 4
+#define MOE_PROFILE_MAX_CALLS 4096
+enum moe_stage {
+    MOE_STAGE_PLAN = 0,          /* routing plan (grouped paths)             */
+    MOE_STAGE_GATE_UP = 1,       /* grouped gate_up product + SwiGLU         */
+    MOE_STAGE_DOWN = 2,          /* grouped down product                     */
+    MOE_STAGE_COMBINE = 3,       /* router-weighted combine                  */
+    MOE_STAGE_DECODE_SLICES = 4, /* decode form: gate_up, SwiGLU and down    */
+};
+int moe_profile_begin(int max_calls);
+int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,9 @@ def _load():
         "moe_experts_decode": ([vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
+        "moe_profile_begin": ([i32], i32),
+        "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
+                             ctypes.POINTER(i32)], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -64,7 +67,7 @@ def exported_symbols():
     """Names of the C entry points this binding uses."""
     return ["moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-            "moe_quantize_fp8_block128"]
+            "moe_quantize_fp8_block128", "moe_profile_begin", "moe_profile_end"]
 
 
 class MoeError(RuntimeError):
@@ -100,6 +103,35 @@ def moe_workspace_layout(variant, T, H, F, E, k):
     none = ctypes.c_size_t(-1).value
     names = ["counts", "offsets", "perm", "inv", "h", "h_scale", "y", "total"]
     return {n: (None if v == none else int(v)) for n, v in zip(names, arr)}
+
+
+# ------------------------------------------------------------ stage timing
+MOE_PROFILE_MAX_STAGES = 4
+STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices"}
+
+
+def moe_profile_begin(max_calls):
+    """Record HIP events around every kernel of the next `max_calls` layer
+    calls (on the stream each kernel runs on)."""
+    _check(_load().moe_profile_begin(int(max_calls)), "moe_profile_begin")
+
+
+def moe_profile_end(max_calls):
+    """Wait for the recorded events; returns one list per call of
+    (stage name, milliseconds) in launch order."""
+    n = ctypes.c_int(0)
+    ms = (ctypes.c_float * (max_calls * MOE_PROFILE_MAX_STAGES))()
+    ids = (ctypes.c_int * (max_calls * MOE_PROFILE_MAX_STAGES))()
+    _check(_load().moe_profile_end(int(max_calls), ctypes.byref(n), ms, ids), "moe_profile_end")
+    out = []
+    for c in range(n.value):
+        row = []
+        for i in range(MOE_PROFILE_MAX_STAGES):
+            sid = ids[c * MOE_PROFILE_MAX_STAGES + i]
+            if sid >= 0:
+                row.append((STAGE_NAMES.get(sid, str(sid)), float(ms[c * MOE_PROFILE_MAX_STAGES + i])))
+        out.append(row)
+    return out
 
 
 # ------------------------------------------------------------ workspace cache
@@ -275,6 +307,7 @@ def moe_quantize_fp8_block128(t):
 
 __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
+    "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
     "moe_quantize_fp8_block128", "MoeError", "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE",
     "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "LIB_PATH",

@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "moe_internal.h"
 #include "../../include/moe_experts.h"
@@ -40,20 +42,75 @@ int device_cu_count() {
     return n > 0 ? n : 256;
 }
 
+// ---------------------------------------------------------------- stage timing
+// Optional instrumentation (moe_profile_begin / moe_profile_end): while on,
+// each layer call takes the next free call slot, and before each of its
+// kernel launches arms a start/stop event pair that the launch carries.
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+
+namespace {
+constexpr int kProfStages = MOE_PROFILE_MAX_STAGES;
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    int cap = 0, used = 0;
+    std::vector<hipEvent_t> ev;  // cap * kProfStages * 2 (start, stop)
+    std::vector<int> ids;        // cap * kProfStages, -1 = no kernel timed
+};
+Profiler g_prof;
+
+class StageClock {
+  public:
+    explicit StageClock(hipStream_t) {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.on && g_prof.used < g_prof.cap) call_ = g_prof.used++;
+    }
+    // right before the launch of the kernel of stage `stage` (MOE_STAGE_*)
+    void mark(int stage) {
+        settle();
+        if (call_ < 0 || n_ >= kProfStages) return;
+        const size_t i = (size_t)call_ * kProfStages + n_;
+        launch_timing() = LaunchTiming{g_prof.ev[2 * i], g_prof.ev[2 * i + 1]};
+        pending_ = stage;
+    }
+    ~StageClock() { settle(); }
+    StageClock(const StageClock&) = delete;
+    StageClock& operator=(const StageClock&) = delete;
+
+  private:
+    // the armed pair was taken by a launch: the stage is timed
+    void settle() {
+        if (pending_ < 0) return;
+        if (!launch_timing().start) g_prof.ids[(size_t)call_ * kProfStages + n_++] = pending_;
+        launch_timing() = LaunchTiming{};
+        pending_ = -1;
+    }
+    int call_ = -1;
+    int n_ = 0;
+    int pending_ = -1;
+};
+}  // namespace
+
 // ---------------------------------------------------------------- layout
 namespace {
 constexpr size_t kNone = (size_t)-1;
 
 struct Layout {
     size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
-           ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, total = 0;
+           ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, part = kNone,
+           total = 0;
     bool decode_fast = false;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool decode_fast_path(int64_t T, int H, int F, int k) {
-    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && H <= kDecodeMaxDim && F <= kDecodeMaxDim;
+    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && H <= kDecodeMaxDim &&
+           F <= kDecodeMaxDim && T * ((H / 8 + 63) / 64) <= kDecodeMaxChunkTokens;
 }
 
 Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
@@ -67,7 +124,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     };
     if (variant == MOE_VARIANT_DECODE && decode_fast_path(T, H, F, k)) {
         L.decode_fast = true;
-        L.h = take((size_t)P * F * sizeof(float));
+        L.part = take(decode_partial_bytes(T, k, E, H, F));
         L.total = off;
         return L;
     }
@@ -140,15 +197,20 @@ int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* ga
     const GroupedPlan pl = plan_in(L, ws, E);
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
+    StageClock clock(s);
+    clock.mark(MOE_STAGE_PLAN);
     int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                                   at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
                                   at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                                   at<int32_t>(ws, L.tile_off), bf16_tile_m(), s));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_GATE_UP);
     rc = launched(launch_gateup_bf16(hidden, gate_up, pl, H, F, k, h, s));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_DOWN);
     rc = launched(launch_down_bf16(h, down, pl, H, F, y, s));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, T, k, H, out, s));
 }
 
@@ -250,8 +312,14 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
     if (!L.decode_fast)
         return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, T, H, F, E,
                                 k, out, ws, stream);
-    return launched(launch_decode(hidden, gate_up, down, top_k_index, top_k_weights, (int)T, k, E,
-                                  H, F, at<float>(ws, L.h), out, stream));
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_DECODE_SLICES);
+    rc = launched(launch_decode_slices(hidden, gate_up, down, top_k_index, (int)T, k, E, H, F,
+                                       at<float>(ws, L.part), stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
+    return launched(launch_decode_combine(at<float>(ws, L.part), top_k_index, top_k_weights,
+                                          (int)T, k, E, H, F, out, stream));
 }
 
 int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
@@ -277,17 +345,65 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
     uint8_t* hq = at<uint8_t>(ws, L.h);
     float* hs = at<float>(ws, L.hs);
     uint16_t* y = at<uint16_t>(ws, L.y);
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_PLAN);
     rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
                               at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
                               at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
                               at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), fp8_tile_m(),
                               stream));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_GATE_UP);
     rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_DOWN);
     rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
     if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, T, k, H, out, stream));
+}
+
+int moe_profile_begin(int max_calls) {
+    if (max_calls < 1 || max_calls > MOE_PROFILE_MAX_CALLS) return MOE_ERR_SHAPE;
+    int dev, rc;
+    if ((rc = query_device(&dev))) return rc;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    const size_t need = (size_t)max_calls * kProfStages * 2;
+    while (g_prof.ev.size() < need) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_LAUNCH;
+        g_prof.ev.push_back(e);
+    }
+    g_prof.ids.assign((size_t)max_calls * kProfStages, -1);
+    g_prof.cap = max_calls;
+    g_prof.used = 0;
+    g_prof.on = true;
+    return MOE_OK;
+}
+
+int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids) {
+    if (!n_calls || !ms || !stage_ids) return MOE_ERR_NULL;
+    if (max_calls < 0) return MOE_ERR_SHAPE;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = false;
+    const int n = g_prof.used < max_calls ? g_prof.used : max_calls;
+    for (int c = 0; c < n; ++c) {
+        for (int i = 0; i < kProfStages; ++i) {
+            const size_t j = (size_t)c * kProfStages + i;
+            ms[j] = -1.0f;
+            stage_ids[j] = -1;
+            if (g_prof.ids[j] < 0) continue;
+            float t = 0.0f;
+            if (hipEventSynchronize(g_prof.ev[2 * j + 1]) != hipSuccess ||
+                hipEventElapsedTime(&t, g_prof.ev[2 * j], g_prof.ev[2 * j + 1]) != hipSuccess)
+                return MOE_ERR_LAUNCH;
+            ms[j] = t;
+            stage_ids[j] = g_prof.ids[j];
+        }
+    }
+    *n_calls = n;
+    g_prof.used = 0;
+    return MOE_OK;
 }
 
 int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,

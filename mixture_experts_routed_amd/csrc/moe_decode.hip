@@ -1,27 +1,46 @@
 // moe_decode.hip - gather-GEMV form of the routed-experts layer for a
 // handful of tokens.  Model card "DeepSeek-OCR-2 MoE experts", description:
-// the decode op handles about 1-4 tokens with two persistent-shape kernels,
-// without a per-expert host loop and without a device-to-host sync.  Here:
-//   phase 1: every (distinct selected expert, f) pair streams gate row f and
-//            up row F+f once and writes h[slot, f] = silu(g) * u in fp32 for
-//            every slot that selected the expert;
-//   phase 2: every output column c streams down row c of each selected
-//            expert and forms out[t, c] = sum_j w[t,j] * (down[e_j][c] . h)
-//            in slot order (the combine, fused, no atomics).
-// Only the selected experts' weights are read from HBM, each row once.
-//
-// The kernel boundary is the only device-wide synchronisation.  On MI355X a
-// launch boundary costs about 1.5 us, while an in-kernel grid barrier costs
-// 7-45 us (same-address atomics serialise at about 15 ns each) and the
-// agent-scope cache write-back/invalidate a flag-based hand-off needs made a
-// single fused launch slower than two.
+// the decode op handles about 1-4 tokens without a per-expert host loop and
+// without a device-to-host sync, streaming only the selected experts'
+// weights.  Here the F dimension is cut into 32-wide slices and one
+// workgroup owns one (selected expert, slice):
+//   - it streams the slice's 32 gate rows and 32 up rows (one read each),
+//     forms h[slot, f] = silu(gate . x) * (up . x) for every slot that chose
+//     the expert, and keeps h in LDS;
+//   - it multiplies h into the slice's columns of the expert's down matrix
+//     (all H rows, 64 bytes each, prefetched into LDS when the workgroup
+//     starts) and writes one fp32 partial sum per (slot, slice, column).
+// A second, small kernel adds the partial sums of every slot in a fixed
+// order and applies the router weights (the combine): deterministic, no
+// float atomics.  Every weight byte of a selected expert is read from HBM
+// once, and the whole weight stream runs in a single launch: on MI355X a
+// short stream pays a fixed start-up cost of several microseconds, so one
+// long stream beats two short ones, and splitting F (not H) lets the down
+// product start without any device-wide synchronisation.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kDecThreads = 256;  // 4 waves
-constexpr int kDecCh = 8;         // 16-byte chunks per lane of a gate/up row: H <= 2048
+constexpr int kDecThreads = 512;  // 8 waves
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Loads below never sit behind a branch: an out-of-range chunk or row loads
+// a valid address (index clamped), so the compiler's waits count exactly the
+// loads a use depends on.  Token chunks past the row end are zeroed.
+__device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
+    return keep ? v : make_uint4(0, 0, 0, 0);
+}
+
+// Workgroup barrier that waits for LDS operations only: weight loads still in
+// flight stay in flight (a __syncthreads() fence would wait for them too).
+__device__ __forceinline__ void lds_only_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // The routing of all P <= 32 slots, held by the lanes of one wave: lane s
 // has slot s's expert (or -1) and weight.  `first` marks the lanes that are
@@ -29,18 +48,15 @@ constexpr int kDecCh = 8;         // 16-byte chunks per lane of a gate/up row: H
 // of first appearance); `u` is the distinct index of the lane's slot.
 struct WaveRouting {
     int e;
-    float w;
     int u;
     uint64_t first;
     int n;
 };
 
-__device__ __forceinline__ WaveRouting wave_routing(const int32_t* __restrict__ idx,
-                                                    const float* __restrict__ wts, int P, int E) {
+__device__ __forceinline__ WaveRouting wave_routing(const int32_t* __restrict__ idx, int P, int E) {
     const int lane = threadIdx.x & 63;
     WaveRouting r;
     int e = lane < P ? idx[lane] : -1;
-    r.w = (wts != nullptr && lane < P) ? wts[lane] : 0.0f;
     const bool valid = (unsigned)e < (unsigned)E;
     if (!valid) e = -1;
     int first = lane;
@@ -56,164 +72,309 @@ __device__ __forceinline__ WaveRouting wave_routing(const int32_t* __restrict__ 
     return r;
 }
 
-// One (expert, f) pair: gate row f in lanes [0,32), up row F+f in lanes
-// [32,64), already loaded; h[s, f] for every slot s of the expert.
-__device__ __forceinline__ void gateup_pair(const uint16_t* __restrict__ x, const uint4 (&wv)[kDecCh],
-                                            uint64_t slots, int k, int H, int F, int f,
-                                            float* __restrict__ h) {
-    const int lane = threadIdx.x & 63, l32 = lane & 31;
-    const int nch = H / 8;
-    while (slots) {
-        const int s = __builtin_ctzll(slots);
-        slots &= slots - 1ull;
-        const uint16_t* xr = x + (int64_t)(s / k) * H;
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kDecCh; ++i) {
-            const int c = l32 + 32 * i;
-            if (c < nch) {
-                const uint4 xv = *(const uint4*)(xr + c * 8);
-                float a[8], b[8];
-                unpack8(wv[i], a);
-                unpack8(xv, b);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) part += a[q] * b[q];
-            }
-        }
-        part = half_sum32(part);
-        const float up = __shfl(part, 32, kWave);
-        if (lane == 0) h[(int64_t)s * F + f] = silu(part) * up;
-    }
-}
-
-// Slots [s0, s0+8) of the down rows: dot each valid slot's row chunk with
-// h[slot] and add w[slot] * dot to its token's accumulator, in slot order.
-template <int CPL>
-__device__ __forceinline__ void down_group(const float* __restrict__ h, const uint4 (&wv)[8][CPL],
-                                           const int (&es)[8], const WaveRouting& R, int s0, int P,
-                                           int k, int F, float (&acc)[kDecodeMaxT]) {
+// Sum over the 64 lanes of each of the N = 2^n values v[0..N): after the
+// call lane l holds the total of value (l >> (6 - n)).  Each halving step
+// trades half of the values with the partner lane, so it takes
+// N - 1 + (6 - n) shuffles instead of 6 N.
+template <int N>
+__device__ __forceinline__ float transpose_sum(float (&v)[N]) {
     const int lane = threadIdx.x & 63;
-    const int nch = F / 8;
+    int bit = 32;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        const int s = s0 + jj;
-        const float ws = __shfl(R.w, s < P ? s : 0, kWave);
-        if (es[jj] < 0) continue;  // dropped slot or past the end (wave-uniform)
-        const float* hr = h + (int64_t)s * F;
-        float part = 0.0f;
+    for (int step = N / 2; step >= 1; step /= 2, bit /= 2) {
+        const bool hi = lane & bit;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int ch = lane + 64 * i;
-            if (ch < nch) {
-                const float4 h0 = *(const float4*)(hr + ch * 8);
-                const float4 h1 = *(const float4*)(hr + ch * 8 + 4);
-                float a[8];
-                unpack8(wv[jj][i], a);
-                part += a[0] * h0.x + a[1] * h0.y + a[2] * h0.z + a[3] * h0.w +
-                        a[4] * h1.x + a[5] * h1.y + a[6] * h1.z + a[7] * h1.w;
-            }
-        }
-        const int t = s / k;
-#pragma unroll
-        for (int tt = 0; tt < kDecodeMaxT; ++tt)
-            if (tt == t) acc[tt] += ws * part;
-    }
-}
-
-template <int CPL>
-__device__ __forceinline__ void down_load(const uint16_t* __restrict__ w2, const WaveRouting& R,
-                                          int s0, int P, int H, int F, int c, uint4 (&wv)[8][CPL],
-                                          int (&es)[8]) {
-    const int lane = threadIdx.x & 63;
-    const int nch = F / 8;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        const int s = s0 + jj;
-        es[jj] = __shfl(R.e, s < P ? s : 0, kWave);
-        if (s >= P || c >= H) es[jj] = -1;
-        const uint16_t* row = w2 + ((int64_t)(es[jj] >= 0 ? es[jj] : 0) * H + (c < H ? c : 0)) * F;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int ch = lane + 64 * i;
-            wv[jj][i] = (es[jj] >= 0 && ch < nch) ? load_nt16(row + ch * 8) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < step; ++i) {
+            // both operands as plain registers: a select between two array
+            // elements would otherwise become an indexed (scratch) access
+            float lo_v = v[i], hi_v = v[i + step];
+            asm("" : "+v"(lo_v), "+v"(hi_v));
+            const float keep = hi ? hi_v : lo_v;
+            const float send = hi ? lo_v : hi_v;
+            v[i] = keep + __shfl_xor(send, bit, kWave);
         }
     }
+    float s = v[0];
+    for (; bit >= 1; bit /= 2) s += __shfl_xor(s, bit, kWave);
+    return s;
 }
 
-// Phase 1: one (distinct expert u, f) pair per wave, pair = 4 * b + wave.
-// Every wave is short-lived and all of a call's row loads are in flight at
-// once: at decode sizes the stream is latency-bound, and on MI355X spreading
-// it over the most waves beats fewer, longer-lived pipelined waves.
-__global__ __launch_bounds__(kDecThreads) void decode_gateup_kernel(
+// One workgroup per (distinct selected expert u, F slice sl), block index
+// u * nslices + sl.  S = slice width (16 or 32), NCH = 16-byte chunks per
+// lane of an H row (H <= 512 NCH), NT = number of tokens.
+template <int S, int NCH, int NT>
+__global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
-    const int32_t* __restrict__ idx, int P, int k, int E, int H, int F,
-    float* __restrict__ h) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const WaveRouting R = wave_routing(idx, nullptr, P, E);
-    const int64_t pair = (int64_t)blockIdx.x * (kDecThreads / kWave) + wave;
-    const int u = (int)(pair / F), f = (int)(pair - (int64_t)u * F);
-    if (u >= R.n) return;  // fewer distinct experts than slots
+    const uint16_t* __restrict__ w2, const int32_t* __restrict__ idx, int k, int E, int H,
+    int F, int nslices, float* __restrict__ part) {
+    constexpr int kSlice = S;
+    constexpr int kRowsPerWave = 2 * S / 8;     // gate/up panel rows per wave
+    constexpr int CPR = S / 8;                  // 16-byte chunks of a down-slice row
+    constexpr int NV = kRowsPerWave * NT;       // dot products per wave
+    // down slice in registers when they allow it (H <= 1536, few tokens):
+    // its rows are then used as they arrive; otherwise it goes through LDS
+    constexpr bool W2REG = NCH <= 3 && NCH * NT <= 8;
+    constexpr int W2ROWS = (3 * 512 + kDecThreads / CPR - 1) / (kDecThreads / CPR);
+    constexpr int NVP = NV <= 8 ? 8 : NV <= 16 ? 16 : 32;  // padded to a power of two
+    static_assert(NV <= 32, "at most 32 dot products per wave");
+    __shared__ u32x4 w2s[W2REG ? 1 : kDecodeMaxDim * CPR];  // down[e][c][f0 .. f0+S): CPR chunks per row
+    __shared__ float dots[2][NT][kSlice];                 // gate / up dot products
+    __shared__ float hs[kDecodeMaxSlots][kSlice];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = NT * k;
+    const int u = blockIdx.x / nslices, sl = blockIdx.x - u * nslices;
+    const int nch = H / 8;
+    // the token rows first: they do not depend on the routing
+    uint4 xv[NT][NCH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = lane + 64 * i;
+            xv[t][i] = zero_unless(c < nch, *(const uint4*)(x + (int64_t)t * H + min(c, nch - 1) * 8));
+        }
+    const WaveRouting R = wave_routing(idx, P, E);
+    if (u >= R.n) return;  // fewer distinct experts than slots (uniform over the workgroup)
     uint64_t fm = R.first;
     for (int i = 0; i < u; ++i) fm &= fm - 1ull;
     const int e = __shfl(R.e, __builtin_ctzll(fm), kWave);
     const uint64_t slots = __ballot(R.u == u);
-    const int half = lane >> 5, l32 = lane & 31;
-    const int nch = H / 8;
-    const uint16_t* row = w13 + ((int64_t)e * 2 * F + (int64_t)half * F + f) * H;
-    uint4 wv[kDecCh];
-#pragma unroll
-    for (int i = 0; i < kDecCh; ++i) {
-        const int c = l32 + 32 * i;
-        wv[i] = c < nch ? load_nt16(row + c * 8) : make_uint4(0, 0, 0, 0);
+    const int f0 = sl * kSlice;
+
+    // 1. (large variants) the slice of the down matrix, straight into LDS:
+    //    row c of w2s holds down[e][c][f0 .. f0+S) as CPR chunks; one wave
+    //    load covers 64/CPR rows
+    if constexpr (!W2REG) {
+        constexpr int RPI = 64 / CPR;
+        const int r = lane / CPR, ch = lane % CPR;
+        const uint16_t* src = w2 + ((int64_t)e * H + r) * F + f0 + ch * 8;
+        for (int j = wave; j < H / RPI; j += kDecThreads / kWave)
+            __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)j * RPI * F),
+                                             (lds_void*)&w2s[j * 64], 16, 0, 0);
     }
-    gateup_pair(x, wv, slots, k, H, F, f, h);
+
+    // 2./3. this wave's gate/up rows (panel row p in [0, 2S) is gate row f0 + p
+    //    for p < S, else up row F + f0 + p - S; lane chunks c = lane + 64 i),
+    //    dotted with every token.
+    constexpr int RB = kRowsPerWave;
+    uint4 w2r[W2REG ? W2ROWS : 1];
+    float v[NVP];
+#pragma unroll
+    for (int i = NV; i < NVP; ++i) v[i] = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < kRowsPerWave; rb += RB) {
+        uint4 wv[RB][NCH];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int p = kRowsPerWave * wave + rb + r;
+            const int row = p < kSlice ? f0 + p : F + f0 + (p - kSlice);
+            const uint16_t* src = w13 + ((int64_t)e * 2 * F + row) * H;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = lane + 64 * i;
+                // a chunk past the row end repeats the last one; it meets a
+                // zeroed token chunk, so it adds nothing
+                wv[r][i] = load_nt16(src + min(c, nch - 1) * 8);
+            }
+        }
+        // (small variants) this thread's rows of the down slice, requested
+        // after the gate/up rows so that the dot products need not wait for
+        // them: rows c = tid / CPR + (512 / CPR) j, chunk tid % CPR
+        if constexpr (W2REG) {
+            const uint16_t* src = w2 + ((int64_t)e * H + tid / CPR) * F + f0 + (tid % CPR) * 8;
+#pragma unroll
+            for (int j = 0; j < W2ROWS; ++j) {
+                const int c = tid / CPR + (kDecThreads / CPR) * j;
+                // a row past H repeats row H - 1 and is never stored
+                w2r[j] = load_nt16(src + (int64_t)(min(c, H - 1) - tid / CPR) * F);
+            }
+        }
+        // every weight load is in flight before the first dot product
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    float a[8], b[8];
+                    unpack8(wv[r][i], a);
+                    unpack8(xv[t][i], b);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc += a[q] * b[q];
+                }
+                v[(rb + r) * NT + t] = acc;
+            }
+    }
+    const float tot = transpose_sum<NVP>(v);
+    {
+        constexpr int n = __builtin_ctz(NVP);
+        const int vi = lane >> (6 - n);
+        if ((lane & ((1 << (6 - n)) - 1)) == 0 && vi < NV) {  // one lane per value
+            const int r = vi / NT, t = vi - r * NT;
+            const int p = kRowsPerWave * wave + r;
+            dots[p < kSlice ? 0 : 1][t][p & (kSlice - 1)] = tot;
+        }
+    }
+    lds_only_barrier();
+
+    // 4. h for every slot of the expert (slot s belongs to token s / k)
+    for (int i = tid; i < kDecodeMaxSlots * kSlice; i += kDecThreads) {
+        const int s = i / kSlice, f = i - s * kSlice;
+        if (s < P && ((slots >> s) & 1ull)) {
+            const int t = s / k;
+            hs[s][f] = silu(dots[0][t][f]) * dots[1][t][f];
+        }
+    }
+    if constexpr (W2REG) {
+        lds_only_barrier();  // h is complete
+    } else {
+        // the down slice has landed (this wave's loads), then every wave's
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // 5. partial down products: CPR lanes per row c, 8 values of the slice each
+    const int q = tid % CPR;
+#pragma unroll
+    for (int j = 0; j < (W2REG ? W2ROWS : (kDecodeMaxDim * CPR + kDecThreads - 1) / kDecThreads); ++j) {
+        const int c = tid / CPR + (kDecThreads / CPR) * j;
+        if (c >= H) break;
+        float wf[8];
+        if constexpr (W2REG) {
+            unpack8(w2r[j], wf);
+        } else {
+            const u32x4 wc = w2s[c * CPR + q];
+            unpack8(make_uint4(wc.x, wc.y, wc.z, wc.w), wf);
+        }
+        uint64_t sm = slots;
+        while (sm) {
+            const int s = __builtin_ctzll(sm);
+            sm &= sm - 1ull;
+            const float* hr = &hs[s][q * 8];
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += wf[j] * hr[j];
+            acc += pair_swap(acc);  // lanes q ^ 1
+            if (CPR == 4)           // lanes q ^ 2
+                acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+            if (q == 0) part[((int64_t)s * nslices + sl) * H + c] = acc;
+        }
+    }
 }
 
-// Phase 2: one wave per output column c = 4 * b + wave.
-template <int CPL>
-__global__ __launch_bounds__(kDecThreads) void decode_down_kernel(
-    const float* __restrict__ h, const uint16_t* __restrict__ w2, const int32_t* __restrict__ idx,
-    const float* __restrict__ wts, int T, int k, int E, int H, int F, uint16_t* __restrict__ out) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// out[t, c] = sum_j w[t, j] * sum_sl part[t*k + j, sl, c] over valid slots.
+// A workgroup owns 16 columns; its 16 column groups split the (slot, slice)
+// pairs (pair = g + 16 i, pair = slot * nslices + slice) and their sums are
+// added in group order, so the result does not depend on timing.  Loads go
+// out in batches of 16 with no dependences between them; dropped slots have
+// weight zero (no branch in the loop).
+constexpr int kCombCols = 16, kCombGroups = 16, kCombBatch = 16;
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
+    int T, int k, int E, int H, int nslices, uint16_t* __restrict__ out) {
+    __shared__ float wsl[kDecodeMaxSlots];
+    __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
+    const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
+    const int c = blockIdx.x * kCombCols + cl;
     const int P = T * k;
-    const WaveRouting R = wave_routing(idx, wts, P, E);
-    const int c = blockIdx.x * (kDecThreads / kWave) + wave;
-    if (c >= H) return;
-    uint4 wv[8][CPL];
-    int es[8];
-    float acc[kDecodeMaxT];
+    const int npairs = P * nslices;
+    // the first batch of partial sums is requested before the slot weights
+    // are read (no dependence between them)
+    float v[kCombBatch];
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxT; ++t) acc[t] = 0.0f;
-    for (int s0 = 0; s0 < P; s0 += 8) {
-        down_load<CPL>(w2, R, s0, P, H, F, c, wv, es);
-        down_group<CPL>(h, wv, es, R, s0, P, k, F, acc);
+    for (int i = 0; i < kCombBatch; ++i) {
+        const int pr = min(g + kCombGroups * i, npairs - 1);
+        v[i] = part[(int64_t)pr * H + c];
+    }
+    if (threadIdx.x < kDecodeMaxSlots) {
+        const int sc = min((int)threadIdx.x, P - 1);  // both loads unconditional
+        const int e = idx[sc];
+        const float wv = wts[sc];
+        wsl[threadIdx.x] = (int)threadIdx.x < P && (unsigned)e < (unsigned)E ? wv : 0.0f;
+    }
+    __syncthreads();
+    float acc[kDecodeMaxT] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int base = g; base < npairs; base += kCombGroups * kCombBatch) {
+        if (base != g) {
+#pragma unroll
+            for (int i = 0; i < kCombBatch; ++i) {
+                const int pr = min(base + kCombGroups * i, npairs - 1);
+                v[i] = part[(int64_t)pr * H + c];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i)
+            if (base + kCombGroups * i >= npairs) v[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kCombBatch; ++i) {
+            const int pr = min(base + kCombGroups * i, npairs - 1);
+            const int s = pr / nslices, t = s / k;
+            const float wv = v[i] * wsl[s];
+#pragma unroll
+            for (int tt = 0; tt < kDecodeMaxT; ++tt)
+                if (tt == t) acc[tt] += wv;
+        }
     }
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxT; ++t) {
-        if (t >= T) break;
-        const float v = wave_sum(acc[t]);
-        if (lane == 0) out[(int64_t)t * H + c] = (uint16_t)f32_to_bf16(v);
+    for (int t = 0; t < kDecodeMaxT; ++t) red[g][t][cl] = acc[t];
+    __syncthreads();
+    if (threadIdx.x < kCombCols * kDecodeMaxT) {
+        const int t = threadIdx.x / kCombCols, cc = threadIdx.x % kCombCols;
+        if (t < T) {
+            float o = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kCombGroups; ++i) o += red[i][t][cc];
+            out[(int64_t)t * H + blockIdx.x * kCombCols + cc] = (uint16_t)f32_to_bf16(o);
+        }
     }
 }
 
-hipError_t launch_decode(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
-                         const int32_t* idx, const float* w, int T, int k, int E, int H, int F,
-                         float* h, uint16_t* out, hipStream_t s) {
-    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    const int64_t pairs = (int64_t)g.umax * F;
-    const int wpb = kDecThreads / kWave;
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((unsigned)((pairs + wpb - 1) / wpb)),
-                       dim3(kDecThreads), 0, s, x, w13, idx, T * k, k, E, H, F, h);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const dim3 grid((unsigned)g.nw2), block(kDecThreads);
-    switch ((F / 8 + 63) / 64) {
-        case 1: hipLaunchKernelGGL(decode_down_kernel<1>, grid, block, 0, s, h, w2, idx, w, T, k, E, H, F, out); break;
-        case 2: hipLaunchKernelGGL(decode_down_kernel<2>, grid, block, 0, s, h, w2, idx, w, T, k, E, H, F, out); break;
-        case 3: hipLaunchKernelGGL(decode_down_kernel<3>, grid, block, 0, s, h, w2, idx, w, T, k, E, H, F, out); break;
-        case 4: hipLaunchKernelGGL(decode_down_kernel<4>, grid, block, 0, s, h, w2, idx, w, T, k, E, H, F, out); break;
-        default: return hipErrorInvalidValue;  // F > 2048 is routed to the grouped path by the caller
+template <int S, int NCH>
+static void launch_slices(dim3 grid, const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                          const int32_t* idx, int T, int k, int E, int H, int F, int ns, float* part,
+                          hipStream_t s) {
+    if (NCH * T > kDecodeMaxChunkTokens) return;  // excluded by decode_fast_path
+    switch (T) {
+        case 1: MOE_LAUNCH((decode_slice_kernel<S, NCH, 1>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
+        case 2: MOE_LAUNCH((decode_slice_kernel<S, NCH, 2>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
+        case 3: MOE_LAUNCH((decode_slice_kernel<S, NCH, 3>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
+        case 4: MOE_LAUNCH((decode_slice_kernel<S, NCH < 4 ? NCH : 3, 4>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
+        default: break;
     }
+}
+
+template <int S>
+static hipError_t launch_width(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                               const int32_t* idx, int T, int k, int E, int H, int F, int umax,
+                               float* part, hipStream_t s) {
+    const int ns = F / S;
+    const dim3 grid((unsigned)(umax * ns));
+    switch ((H / 8 + 63) / 64) {
+        case 1: launch_slices<S, 1>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
+        case 2: launch_slices<S, 2>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
+        case 3: launch_slices<S, 3>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
+        case 4: launch_slices<S, 4>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
+        default: return hipErrorInvalidValue;  // H > 2048 is routed to the grouped path by the caller
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                                const int32_t* idx, int T, int k, int E, int H, int F, float* part,
+                                hipStream_t s) {
+    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
+    return g.slice == 16 ? launch_width<16>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s)
+                         : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s);
+}
+
+hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w, int T,
+                                 int k, int E, int H, int F, uint16_t* out, hipStream_t s) {
+    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
+    MOE_LAUNCH(decode_combine_kernel, dim3((unsigned)(H / kCombCols)), dim3(256), 0, s, part,
+                       idx, w, T, k, E, H, g.nslices, out);
     return hipGetLastError();
 }
 

@@ -274,7 +274,7 @@ static int gemm_grid() {
 template <int BN, bool SWIGLU>
 static void launch_bf16(const uint16_t* A, const uint16_t* B, const GroupedPlan& pl, int K,
                         int n_out, int b_rows, int topk, uint16_t* C, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<BN, SWIGLU>), dim3(gemm_grid<BN, SWIGLU>()),
+    MOE_LAUNCH((gemm_bf16_kernel<BN, SWIGLU>), dim3(gemm_grid<BN, SWIGLU>()),
                        dim3(kGemmThreads), 0, s, A, B, pl.perm, pl.tiles, pl.ntiles, pl.tile_off,
                        pl.offsets, pl.E, K, n_out, b_rows, topk, C);
 }
@@ -330,7 +330,7 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
                           int H, uint16_t* out, hipStream_t s) {
     const int64_t n = T * (H / 8);
     const int blocks = (int)((n + 255) / 256);
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, T, k, H, out);
+    MOE_LAUNCH(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, T, k, H, out);
     return hipGetLastError();
 }
 

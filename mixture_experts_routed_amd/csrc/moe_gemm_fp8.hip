@@ -251,7 +251,7 @@ static int fp8_grid() {
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
                              const float* w13s, const GroupedPlan& pl, int H, int F, int k,
                              uint8_t* hq, float* hs, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 256, true>), dim3(fp8_grid<kFp8WM, 256, true>()),
+    MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, true>), dim3(fp8_grid<kFp8WM, 256, true>()),
                        dim3(kFp8Threads), 0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles,
                        pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
     return hipGetLastError();
@@ -260,12 +260,12 @@ hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
                            const GroupedPlan& pl, int H, int F, uint16_t* y, hipStream_t s) {
     if (H % 256 == 0)
-        hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 256, false>),
+        MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, false>),
                            dim3(fp8_grid<kFp8WM, 256, false>()), dim3(kFp8Threads), 0, s, hq, hs,
                            w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                            H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
     else
-        hipLaunchKernelGGL((gemm_fp8_kernel<kFp8WM, 128, false>),
+        MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 128, false>),
                            dim3(fp8_grid<kFp8WM, 128, false>()), dim3(kFp8Threads), 0, s, hq, hs,
                            w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                            H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
@@ -309,7 +309,7 @@ hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int
     const int64_t nblocks = rows * (K / 128);
     const int64_t threads = nblocks * 32;
     const int blocks = (int)((threads + 255) / 256);
-    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, s, in, in_is_bf16, nblocks, K,
+    MOE_LAUNCH(quantize_kernel, dim3(blocks), dim3(256), 0, s, in, in_is_bf16, nblocks, K,
                        codes, scales);
     return hipGetLastError();
 }

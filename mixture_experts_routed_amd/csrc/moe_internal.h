@@ -1,10 +1,32 @@
 // moe_internal.h - host-side launchers of the gfx950 kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Every kernel launch goes through MOE_LAUNCH.  While the stage-timing
+// recorder has armed an event pair for the calling thread, the launch carries
+// them on its own dispatch (so they time the kernel's execution, not the
+// dispatch queue), and the pair is disarmed; otherwise it is a plain launch.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();  // per host thread
+
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ...)                                     \
+    do {                                                                                        \
+        ::moe::LaunchTiming& lt_ = ::moe::launch_timing();                                      \
+        if (lt_.start) {                                                                        \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, lt_.start, lt_.stop, 0u,  \
+                                  __VA_ARGS__);                                                 \
+            lt_ = ::moe::LaunchTiming{};                                                        \
+        } else {                                                                                \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
+        }                                                                                       \
+    } while (0)
 
 // The plan cuts every expert's rows into M tiles of at most tile_m rows
 // (the grouped products' tile height; never below kMinTileM).
@@ -43,30 +65,44 @@ hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const Grouped
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int k,
                           int H, uint16_t* out, hipStream_t s);
 
-// Decode gather-GEMV (T small): phase 1 writes h fp32 [T*k, F] by slot id,
-// phase 2 does the down rows and the combine.  Limits of this form: T <= 4,
-// T*k <= 32, H <= 2048, F <= 2048 (larger calls take the grouped path).
+// Decode gather-GEMV (T small): one launch streams the selected experts'
+// weights in 32-wide F slices and writes fp32 partial down products
+// part[slot][slice][H]; a second small launch adds them up with the router
+// weights.  Limits of this form: T <= 4, T*k <= 32, H <= 2048, F <= 2048
+// and T * ceil(H / 512) <= 12 (the token rows and weight rows of a wave stay
+// in registers); larger calls take the grouped path.
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxSlots = 32;
 constexpr int kDecodeMaxDim = 2048;
+constexpr int kDecodeMaxChunkTokens = 12;
 
 struct DecodeGeometry {
-    int umax;  // most distinct experts a call can select: min(T*k, E)
-    int nw2;   // phase-2 workgroups (4 output columns each)
+    int umax;     // most distinct experts a call can select: min(T*k, E)
+    int slice;    // F values per workgroup
+    int nslices;  // F / slice
 };
 
 inline DecodeGeometry decode_geometry(int64_t T, int k, int E, int H, int F) {
-    (void)F;
+    (void)H;
     DecodeGeometry g;
     const int P = (int)(T * k);
     g.umax = P < E ? P : E;
-    g.nw2 = (H + 3) / 4;
+    g.slice = 32;  // 16-wide slices (more workgroups) measured slower at T = 1
+    g.nslices = F / g.slice;
     return g;
 }
 
-hipError_t launch_decode(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
-                         const int32_t* idx, const float* w, int T, int k, int E, int H, int F,
-                         float* h, uint16_t* out, hipStream_t s);
+// Bytes of the partial sums of the decode form.
+inline size_t decode_partial_bytes(int64_t T, int k, int E, int H, int F) {
+    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
+    return (size_t)(T * k) * (size_t)g.nslices * (size_t)H * sizeof(float);
+}
+
+hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+                                const int32_t* idx, int T, int k, int E, int H, int F, float* part,
+                                hipStream_t s);
+hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w, int T,
+                                 int k, int E, int H, int F, uint16_t* out, hipStream_t s);
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,

@@ -160,7 +160,7 @@ hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_
                        int32_t* tile_off, int tile_m, hipStream_t s) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, nbits, counts,
+    MOE_LAUNCH(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, nbits, counts,
                        offsets, perm, inv, tiles, ntiles, tile_off, tile_m);
     return hipGetLastError();
 }

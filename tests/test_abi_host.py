@@ -74,8 +74,9 @@ def test_workspace_sizes_and_layout(variant):
 def test_decode_fast_path_workspace_is_small():
     n1 = moe.moe_workspace_size(1, 1, 1280, 896, 64, 6)
     lay = moe.moe_workspace_layout(1, 4, 1280, 896, 64, 6)
-    assert n1 >= 6 * 896 * 4 and n1 < 1 << 20
-    assert lay["perm"] is None and lay["h"] == 0
+    # fp32 partial down products [slots, F / 32, H]
+    assert n1 >= 6 * (896 // 32) * 1280 * 4 and n1 < 1 << 20
+    assert all(v is None for key, v in lay.items() if key != "total")
     # above the fast path the decode entry uses the grouped layout
     assert moe.moe_workspace_layout(1, 64, 1280, 896, 64, 6)["perm"] is not None
 
@@ -157,3 +158,21 @@ def test_python_binding_rejects_cpu_tensors():
         moe.moe_experts_prefill(x, gu, dn, idx, w, 2)
     with pytest.raises(TypeError):
         moe.moe_experts_prefill(x.float(), gu, dn, idx, w, 2)
+
+
+def test_profile_recorder_argument_checks():
+    lib = moe._load()
+    assert lib.moe_profile_begin(0) == ESHAPE
+    assert lib.moe_profile_begin(4097) == ESHAPE
+    n = ctypes.c_int(-1)
+    ms = (ctypes.c_float * 4)()
+    ids = (ctypes.c_int * 4)()
+    assert lib.moe_profile_end(1, None, ms, ids) == ENULL
+    assert lib.moe_profile_end(-1, ctypes.byref(n), ms, ids) == ESHAPE
+    # nothing recorded: zero calls, recorder off
+    assert lib.moe_profile_end(1, ctypes.byref(n), ms, ids) == OK and n.value == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")
+def test_profile_begin_without_gpu_reports_device_error():
+    assert moe._load().moe_profile_begin(8) == EDEV

@@ -200,9 +200,12 @@ def test_decode_full_config(name):
 
 
 @pytest.mark.parametrize("shape", [(3, 128, 64, 8, 2), (4, 256, 1536, 6, 5), (2, 512, 2048, 3, 3),
-                                   (4, 128, 128, 40, 8), (7, 128, 64, 8, 2)])
+                                   (4, 128, 128, 40, 8), (1, 1024, 96 * 2, 8, 4),
+                                   (2, 1536, 64, 5, 2), (3, 2048, 128, 8, 3), (4, 1536, 64, 8, 2),
+                                   (4, 2048, 64, 8, 2), (7, 128, 64, 8, 2)])
 def test_decode_shapes(shape):
-    """Fast path for T <= 4 (every chunks-per-lane case), grouped path above."""
+    """Fast path for T <= 4 (1 to 4 16-byte chunks per lane of an H row, 1 to 4
+    tokens), grouped path above it (T = 7, and T = 4 with H = 2048)."""
     T, H, F, E, k = shape
     _say(f"decode shape {shape}")
     p = bf16_problem(T, H, F, E, k, seed=T + F, std=1 / np.sqrt(H))
@@ -422,3 +425,24 @@ def test_fp8_overwrite_and_dropped():
     g = to_gpu(p)
     poison = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
     check_tol(run_fp8(g, out=poison), ref, FP8_TOL, "fp8 dropped")
+
+
+def test_stage_recorder_times_every_kernel():
+    """The stage-timing recorder sees each kernel of a call, in launch order."""
+    moe = _moe()
+    _say("stage recorder")
+    p = wl.make_config("tiny")
+    k = wl.CONFIGS["tiny"]["k"]
+    g = to_gpu(p)
+    moe.moe_profile_begin(2)
+    moe.moe_experts_prefill(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                            g["top_k_weights"], k)
+    moe.moe_experts_decode(g["hidden"][:1], g["gate_up"], g["down"], g["top_k_index"][:1],
+                           g["top_k_weights"][:1], k)
+    moe.moe_experts_prefill(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                            g["top_k_weights"], k)   # past max_calls: not recorded
+    torch.cuda.synchronize()
+    calls = moe.moe_profile_end(2)
+    assert [s for s, _ in calls[0]] == ["plan", "gate_up", "down", "combine"]
+    assert [s for s, _ in calls[1]] == ["decode_slices", "combine"]
+    assert all(ms > 0 for row in calls for _, ms in row)
