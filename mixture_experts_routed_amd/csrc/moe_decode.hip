@@ -123,7 +123,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = NT * k;
-    const int u = blockIdx.x / nslices, sl = blockIdx.x - u * nslices;
+    // Work w = u * nslices + sl.  Blocks go to XCDs round-robin; mapping
+    // w to XCD-contiguous runs of even length keeps the two 32-wide slices
+    // that share a 128-byte line of the down matrix in one L2.
+    const int per_xcd = gridDim.x / kXcds;
+    const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int u = w / nslices, sl = w - u * nslices;
+    if (u >= kDecodeMaxSlots) return;  // grid padding
     const int nch = H / 8;
     // the token rows first: they do not depend on the routing
     uint4 xv[NT][NCH];
@@ -271,8 +277,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
 // added in group order, so the result does not depend on timing.  Loads go
 // out in batches of 16 with no dependences between them; dropped slots have
 // weight zero (no branch in the loop).
-constexpr int kCombCols = 16, kCombGroups = 16, kCombBatch = 16;
-__global__ __launch_bounds__(256) void decode_combine_kernel(
+constexpr int kCombCols = 16, kCombGroups = 16, kCombBatch = 16;  // many small workgroups: latency-bound
+constexpr int kCombThreads = kCombCols * kCombGroups;
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
     int T, int k, int E, int H, int nslices, uint16_t* __restrict__ out) {
     __shared__ float wsl[kDecodeMaxSlots];
@@ -351,7 +358,9 @@ static hipError_t launch_width(const uint16_t* x, const uint16_t* w13, const uin
                                const int32_t* idx, int T, int k, int E, int H, int F, int umax,
                                float* part, hipStream_t s) {
     const int ns = F / S;
-    const dim3 grid((unsigned)(umax * ns));
+    // padded to a multiple of 16 (even runs per XCD); padding blocks map to
+    // u >= umax, where the routing has no distinct expert
+    const dim3 grid((unsigned)((umax * ns + 15) / 16 * 16));
     switch ((H / 8 + 63) / 64) {
         case 1: launch_slices<S, 1>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
         case 2: launch_slices<S, 2>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
@@ -373,7 +382,7 @@ hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const ui
 hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w, int T,
                                  int k, int E, int H, int F, uint16_t* out, hipStream_t s) {
     const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    MOE_LAUNCH(decode_combine_kernel, dim3((unsigned)(H / kCombCols)), dim3(256), 0, s, part,
+    MOE_LAUNCH(decode_combine_kernel, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0, s, part,
                        idx, w, T, k, E, H, g.nslices, out);
     return hipGetLastError();
 }
