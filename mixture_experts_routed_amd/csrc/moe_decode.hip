@@ -24,22 +24,11 @@ namespace moe {
 
 constexpr int kDecThreads = 512;  // 8 waves
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Loads below never sit behind a branch: an out-of-range chunk or row loads
 // a valid address (index clamped), so the compiler's waits count exactly the
 // loads a use depends on.  Token chunks past the row end are zeroed.
 __device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
     return keep ? v : make_uint4(0, 0, 0, 0);
-}
-
-// Workgroup barrier that waits for LDS operations only: weight loads still in
-// flight stay in flight (a __syncthreads() fence would wait for them too).
-__device__ __forceinline__ void lds_only_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // The routing of all P <= 32 slots, held by the lanes of one wave: lane s
@@ -224,7 +213,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
             dots[p < kSlice ? 0 : 1][t][p & (kSlice - 1)] = tot;
         }
     }
-    lds_only_barrier();
+    lds_barrier();
 
     // 4. h for every slot of the expert (slot s belongs to token s / k)
     for (int i = tid; i < kDecodeMaxSlots * kSlice; i += kDecThreads) {
@@ -235,7 +224,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
         }
     }
     if constexpr (W2REG) {
-        lds_only_barrier();  // h is complete
+        lds_barrier();  // h is complete
     } else {
         // the down slice has landed (this wave's loads), then every wave's
         __builtin_amdgcn_s_waitcnt(0);

@@ -118,6 +118,46 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8 a, const i32x8 b
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// ------------------------------------------------------- direct LDS fills
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: the wave writes
+// 1 KB at `dst` (wave-uniform), lane L's bytes at dst + 16 L.  Counted by
+// vmcnt like a load; no VGPRs are involved.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// 4 bytes per lane from global memory straight into LDS (lane L's word at
+// dst + 4 L), counted by vmcnt like dma16.
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Workgroup barrier once this wave has at most N vector-memory operations in
+// flight (its older LDS fills have landed) and no LDS operation pending.  The
+// empty asm statements keep the compiler from moving memory operations
+// across it; the explicit wait replaces the vmcnt(0) a __syncthreads() fence
+// would force while later stages are still loading.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier once this wave's LDS reads are done (vector-memory
+// operations may stay in flight): closes an item, so that no wave refills a
+// ring slot another wave is still reading.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------- scheduling helpers
 // Persistent grids walk work items i = round * G + slot.  Workgroup b runs on
 // XCD b % 8; giving each XCD a contiguous run of slots keeps work items that

@@ -19,39 +19,6 @@ constexpr int kBK = 64;            // bf16 K elements per stage: one 128-byte li
 constexpr int kAStages = 2;        // token-row stages (L2 hits mostly): loads run 1 step ahead
 constexpr int kBStages = 3;        // weight stages (HBM): loads run 2 steps ahead
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from global memory straight into LDS: the wave writes
-// 1 KB at `dst` (wave-uniform), lane L's bytes at dst + 16 L.  Counted by
-// vmcnt like a load; no VGPRs are involved.
-__device__ __forceinline__ void dma16(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
-
-// Workgroup barrier once this wave has at most N vector-memory operations in
-// flight (its older LDS fills have landed) and no LDS operation pending.  The
-// empty asm statements keep the compiler from moving memory operations
-// across it; the explicit wait replaces the vmcnt(0) a __syncthreads() fence
-// would force while later stages are still loading.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier once this wave's LDS reads are done (vector-memory
-// operations may stay in flight): closes an item, so that no wave refills a
-// ring slot another wave is still reading.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
 // expert's weight panel).  Wave (wm, wn) owns tile rows [64wm, 64wm+64) as two
 // 32-row blocks and panel rows [wn*BN/2, (wn+1)*BN/2) as NB 32-row blocks.
