@@ -29,7 +29,8 @@ Readings of points the pages leave open (each is listed in the design doc):
 2. SiLU is z * sigmoid(z) with no clamp.
 3. top_k_weights already carry the routed scaling factor; the op only
    multiplies by them.
-4. No residual term in this op.
+4. The residual of moe_local_reduction is optional (None: no residual); when
+   given it is added once, after the routing-weighted sum.
 5. A token that names the same expert in two slots gets both contributions.
 6. Expert ids outside [0, E) drop their slot: it contributes nothing and is
    absent from the routing plan.
@@ -115,7 +116,7 @@ def routing_plan(top_k_index, num_experts):
 
 # --------------------------------------------------------------------------
 # bf16 layer ([OCR2] description and "Usage"; combine as [MPK]
-# moe_local_reduction without the residual)
+# moe_local_reduction, its residual optional)
 # --------------------------------------------------------------------------
 
 
@@ -123,7 +124,7 @@ def _as_f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights):
+def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights, residual=None):
     """Routed-experts layer, one token and one slot at a time, in float64.
 
     hidden [T, H], gate_up [E, 2F, H], down [E, H, F] are the operands' values
@@ -133,6 +134,7 @@ def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights):
         h   = silu(g[:F]) * g[F:]             (F values)
         y   = down[e] @ h                     (H values)
         out[t] += w[t, j] * y
+    then out += residual [T, H] when one is given ([MPK] moe_local_reduction).
     """
     x = _as_f64(hidden)
     w13 = np.asarray(gate_up)
@@ -153,10 +155,13 @@ def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights):
             h = silu(g[:F]) * g[F:]
             y = _as_f64(w2[e]) @ h
             out[t] += wts[t, j] * y
+    if residual is not None:
+        out += _as_f64(residual)
     return out
 
 
-def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weights):
+def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weights,
+                                  residual=None):
     """Same sums as :func:`moe_experts_reference`, grouped by expert.
 
     Each expert's rows are gathered once and multiplied as one float64 matrix
@@ -182,6 +187,8 @@ def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weig
         y = h @ _as_f64(w2[e]).T
         contrib = wts[tt, jj][:, None] * y
         np.add.at(out, tt, contrib)
+    if residual is not None:
+        out += _as_f64(residual)
     return out
 
 
@@ -279,7 +286,7 @@ def dequantize_block128(codes, scales):
 
 def moe_experts_fp8_reference(x_codes, x_scale, w13_codes, w13_scale,
                               w2_codes, w2_scale, top_k_index, top_k_weights,
-                              tokens=None):
+                              tokens=None, residual=None):
     """FP8 routed-experts layer in float64 with the method's fp32 re-quantise.
 
     Operands: x_codes [T, H] + x_scale [T, H/128]; w13_codes [E, 2F, H] +
@@ -292,7 +299,8 @@ def moe_experts_fp8_reference(x_codes, x_scale, w13_codes, w13_scale,
     The loop runs expert by expert so each expert is dequantised once; within
     an expert each slot is its own matrix-vector product.  ``tokens``
     restricts the result to a subset of rows (others stay zero), which is how
-    a sampled check of a large layer is made.
+    a sampled check of a large layer is made.  ``residual`` [T, H], when
+    given, is added after the weighted sum (on the selected rows).
     Returns out [T, H] float64 (and nothing is rounded to bf16).
     """
     xq = np.asarray(x_codes)
@@ -321,4 +329,18 @@ def moe_experts_fp8_reference(x_codes, x_scale, w13_codes, w13_scale,
             ht = dequantize_block128(q, s)
             y = W2 @ ht
             out[t] += wts[t, j] * y
+    if residual is not None:
+        out[want] += np.asarray(residual, dtype=np.float64)[want]
     return out
+
+
+def moe_experts_fp8_bf16_reference(hidden, w13_codes, w13_scale, w2_codes, w2_scale,
+                                   top_k_index, top_k_weights, tokens=None, residual=None):
+    """FP8 layer fed with bf16 hidden states ([MPK] bf16_to_fp8_quantize before
+    moe_w13_fp8_layer): the rows of ``hidden`` (values of bf16 numbers) are
+    quantised per 128-wide block by :func:`quantize_block128_fp32` (the same
+    fp32 rule as the re-quantisation of h), then the fp8 layer runs on those
+    codes and scales."""
+    xq, xs = quantize_block128_fp32(np.asarray(hidden, dtype=np.float32))
+    return moe_experts_fp8_reference(xq, xs, w13_codes, w13_scale, w2_codes, w2_scale,
+                                     top_k_index, top_k_weights, tokens=tokens, residual=residual)

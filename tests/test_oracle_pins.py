@@ -358,3 +358,54 @@ def test_fp8_oracle_invariants_and_token_subset():
     assert _rel(f(*args, idx[:, ::-1], w[:, ::-1]), base) < 1e-12
     sub = f(*args, idx, w, tokens=[1, 5])
     assert np.array_equal(sub[[1, 5]], base[[1, 5]]) and np.all(sub[[0, 2, 3, 4, 6, 7]] == 0)
+
+
+# ------------------------------------------------------------ residual, bf16-input fp8
+
+
+def test_residual_closed_form_and_zero_weights(golden):
+    """[MPK] moe_local_reduction: out = sum_j w_j y_j + residual.  On the closed
+    form above (out = silu(2) * 1 = 1.7615941559557646) a residual of 0.25 gives
+    2.0115941559557646; with all routing weights zero the output is the
+    residual itself, exactly."""
+    c = golden["swiglu_h1_f1"]
+    args = [np.array([c["x"]]), np.array(c["gate_up"]), np.array(c["down"]),
+            np.array(c["top_k_index"])]
+    for fn in (orc.moe_experts_reference, orc.moe_experts_reference_batched):
+        out = fn(*args, np.array(c["top_k_weights"]), residual=np.array([[0.25]]))
+        assert out[0, 0] == pytest.approx(2.0115941559557646, rel=1e-15)
+    p = wl.make_bf16_problem(5, 128, 64, 6, 2, seed=31)
+    r = np.random.default_rng(3).standard_normal((5, 128))
+    zero = np.zeros(p["top_k_weights"].shape)
+    for fn in (orc.moe_experts_reference, orc.moe_experts_reference_batched):
+        out = fn(p["hidden"].float().numpy(), p["gate_up"].float().numpy(), p["down"].float().numpy(),
+                 p["top_k_index"].numpy(), zero, residual=r)
+        assert np.array_equal(out, r)
+    q = wl.make_fp8_problem(4, 256, 128, 5, 2, seed=23, routing="uniform_softmax", routed_scale=1.0)
+    fargs = [q[n].numpy() for n in ("x", "x_scale", "gate_up", "gate_up_scale", "down", "down_scale")]
+    r8 = np.random.default_rng(4).standard_normal((4, 256))
+    out = orc.moe_experts_fp8_reference(*fargs, q["top_k_index"].numpy(),
+                                        np.zeros(q["top_k_weights"].shape), residual=r8)
+    assert np.array_equal(out, r8)
+
+
+def test_fp8_bf16_input_reduces_to_the_fp8_layer():
+    """Hidden states that are e4m3 codes times a power-of-two block scale with
+    each block's largest code at 448 quantise without loss (scale = amax/448 is
+    the power of two, code = value * 448/amax exactly), so the bf16-input layer
+    must equal the fp8 layer on those very codes and scales."""
+    rng = np.random.default_rng(5)
+    T, H, F, E, k = 4, 256, 128, 5, 2
+    codes = rng.integers(0, 256, size=(T, H)).astype(np.uint8)
+    codes[(codes & 0x7F) > 0x7E] = 0                 # no NaN, no 448 except where placed
+    codes[(codes & 0x7F) == 0x7E] = 0x7D
+    codes[:, ::128] = 0x7E                           # +448 leads every block
+    scale = np.exp2(-rng.integers(3, 9, size=(T, H // 128))).astype(np.float32)
+    hidden = orc.dequantize_block128(codes, scale)   # exact in float32 (and in bf16)
+    assert np.array_equal(hidden.astype(np.float32).astype(np.float64), hidden)
+    q = wl.make_fp8_problem(T, H, F, E, k, seed=24, routing="uniform_softmax", routed_scale=1.0)
+    w = [q[n].numpy() for n in ("gate_up", "gate_up_scale", "down", "down_scale")]
+    idx, wts = q["top_k_index"].numpy(), q["top_k_weights"].numpy()
+    got = orc.moe_experts_fp8_bf16_reference(hidden, *w, idx, wts)
+    ref = orc.moe_experts_fp8_reference(codes, scale, *w, idx, wts)
+    assert np.array_equal(got, ref)
