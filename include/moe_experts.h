@@ -15,8 +15,8 @@
  * experts are outside the layer; top_k_weights already include any routed
  * scaling factor.  The fp8 variant follows mirage issue "Supporting
  * MegaKernel for DeepSeek Models", Layer Tensor Details: moe_w13_fp8_layer,
- * moe_silu_mul_layer, moe_w2_fp8_layer, moe_local_reduction (without its
- * residual): E4M3 operands with one fp32 scale per row and 128-wide K block.
+ * moe_silu_mul_layer, moe_w2_fp8_layer, moe_local_reduction (its
+ * residual optional): E4M3 operands with one fp32 scale per row and 128-wide K block.
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, dense row-major, and 16-byte
@@ -25,7 +25,12 @@
  *  - bf16 is passed as uint16_t bit patterns, fp8 as uint8_t OCP E4M3FN codes
  *    (bias 7, max 448, 0x7F/0xFF are NaN).
  *  - Expert ids outside [0,E) drop their slot: it contributes nothing.
- *  - `out` is fully overwritten (never accumulated into).
+ *  - `out` is fully overwritten (never accumulated into).  The layer entry
+ *    points take an optional `residual` [T,H] bf16 (NULL: none), added to
+ *    the routing-weighted sum in fp32 before the single rounding of out
+ *    (mirage issue "Supporting MegaKernel for DeepSeek Models",
+ *    moe_local_reduction: out = sum_k in[:,k,:] * w[:,k] + residual);
+ *    `out` may not alias `residual`.
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *    default stream).  No call allocates memory, synchronises, or copies
  *    between host and device.  The library keeps no mutable global state
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
     MOE_OK = 0,
@@ -66,6 +71,7 @@ enum moe_variant {
     MOE_VARIANT_DECODE = 1,  /* moe_experts_decode                             */
     MOE_VARIANT_FP8 = 2,     /* moe_experts_fp8                                */
     MOE_VARIANT_PLAN = 3,    /* moe_routing_plan                               */
+    MOE_VARIANT_FP8_BF16IN = 4, /* moe_experts_fp8_bf16in                      */
 };
 
 /* Supported ranges (checked on every call; MOE_ERR_SHAPE otherwise):
@@ -130,8 +136,8 @@ int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E,
  */
 int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
                         const int32_t* top_k_index, const float* top_k_weights,
-                        int64_t T, int H, int F, int E, int k, uint16_t* out,
-                        void* ws, size_t ws_bytes, hipStream_t stream);
+                        const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * bf16 routed experts, gather-GEMV form for a handful of tokens (the model
@@ -145,8 +151,8 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
  */
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
                        const int32_t* top_k_index, const float* top_k_weights,
-                       int64_t T, int H, int F, int E, int k, uint16_t* out,
-                       void* ws, size_t ws_bytes, hipStream_t stream);
+                       const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * FP8 block-scaled routed experts (mirage issue "Supporting MegaKernel for
@@ -166,8 +172,24 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale,
                     const uint8_t* gate_up, const float* gate_up_scale,
                     const uint8_t* down, const float* down_scale,
                     const int32_t* top_k_index, const float* top_k_weights,
-                    int64_t T, int H, int F, int E, int k, uint16_t* out,
-                    void* ws, size_t ws_bytes, hipStream_t stream);
+                    const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same FP8 layer fed with bf16 hidden states [T,H] (mirage issue
+ * "Supporting MegaKernel for DeepSeek Models": bf16_to_fp8_quantize before
+ * moe_w13_fp8_layer).  Each row is quantised per 128-wide block into the
+ * workspace by the rule of moe_quantize_fp8_block128 (fp32 scale amax/448,
+ * RNE codes; all-zero block: scale 1, codes 0), then moe_experts_fp8 runs on
+ * those codes and scales.  Workspace: moe_workspace_size(MOE_VARIANT_FP8_BF16IN,
+ * ...).  Other operands, results and errors as moe_experts_fp8.
+ */
+int moe_experts_fp8_bf16in(const uint16_t* hidden,
+                           const uint8_t* gate_up, const float* gate_up_scale,
+                           const uint8_t* down, const float* down_scale,
+                           const int32_t* top_k_index, const float* top_k_weights,
+                           const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                           uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Block-128 fp8 quantisation of `rows` rows of K values (mirage issue
@@ -201,7 +223,7 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
  * MOE_ERR_NULL, MOE_ERR_LAUNCH (event creation or query failed),
  * MOE_ERR_DEVICE.
  */
-#define MOE_PROFILE_MAX_STAGES 4
+#define MOE_PROFILE_MAX_STAGES 5
 #define MOE_PROFILE_MAX_CALLS 4096
 enum moe_stage {
     MOE_STAGE_PLAN = 0,          /* routing plan (grouped paths)             */
@@ -209,6 +231,7 @@ enum moe_stage {
     MOE_STAGE_DOWN = 2,          /* grouped down product                     */
     MOE_STAGE_COMBINE = 3,       /* router-weighted combine                  */
     MOE_STAGE_DECODE_SLICES = 4, /* decode form: gate_up, SwiGLU and down    */
+    MOE_STAGE_QUANTIZE = 5,      /* input-side block-128 fp8 quantisation    */
 };
 int moe_profile_begin(int max_calls);
 int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);

@@ -27,6 +27,7 @@ MOE_VARIANT_PREFILL = 0
 MOE_VARIANT_DECODE = 1
 MOE_VARIANT_FP8 = 2
 MOE_VARIANT_PLAN = 3
+MOE_VARIANT_FP8_BF16IN = 4
 
 _lib = None
 
@@ -47,9 +48,12 @@ def _load():
         "moe_workspace_size": ([i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "moe_workspace_layout": ([i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "moe_routing_plan": ([vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
-        "moe_experts_prefill": ([vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
-        "moe_experts_decode": ([vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
-        "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_prefill": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_decode": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp],
+                            i32),
+        "moe_experts_fp8_bf16in": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz,
+                                    vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
@@ -67,7 +71,8 @@ def exported_symbols():
     """Names of the C entry points this binding uses."""
     return ["moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-            "moe_quantize_fp8_block128", "moe_profile_begin", "moe_profile_end"]
+            "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
+            "moe_profile_end"]
 
 
 class MoeError(RuntimeError):
@@ -106,8 +111,8 @@ def moe_workspace_layout(variant, T, H, F, E, k):
 
 
 # ------------------------------------------------------------ stage timing
-MOE_PROFILE_MAX_STAGES = 4
-STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices"}
+MOE_PROFILE_MAX_STAGES = 5
+STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices", 5: "quantize"}
 
 
 def moe_profile_begin(max_calls):
@@ -172,6 +177,16 @@ def _need(t, name, dtype, ndim, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _residual(residual, T, H, dev):
+    """Optional residual [T, H] bf16 (None: no residual); returns a pointer."""
+    if residual is None:
+        return ctypes.c_void_p(None)
+    _need(residual, "residual", torch.bfloat16, 2, dev)
+    if tuple(residual.shape) != (T, H):
+        raise ValueError("residual must be [T, H]")
+    return _ptr(residual)
+
+
 def _out(out, T, H, dev):
     if out is None:
         return torch.empty(T, H, dtype=torch.bfloat16, device=dev)
@@ -182,7 +197,7 @@ def _out(out, T, H, dev):
 
 
 def _bf16_call(entry, variant, hidden_states, gate_up_proj, down_proj, top_k_index,
-               top_k_weights, top_k, workspace=None, out=None):
+               top_k_weights, top_k, residual=None, workspace=None, out=None):
     dev = hidden_states.device
     _need(hidden_states, "hidden_states", torch.bfloat16, 2)
     _need(gate_up_proj, "gate_up_proj", torch.bfloat16, 3, dev)
@@ -197,6 +212,7 @@ def _bf16_call(entry, variant, hidden_states, gate_up_proj, down_proj, top_k_ind
         raise ValueError("expected gate_up_proj [E,2F,H] and down_proj [E,H,F] matching hidden_states [T,H]")
     if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
         raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
     out = _out(out, T, H, dev)
     if T == 0:
         return out
@@ -205,67 +221,90 @@ def _bf16_call(entry, variant, hidden_states, gate_up_proj, down_proj, top_k_ind
         need = moe_workspace_size(variant, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
         rc = getattr(_load(), entry)(_ptr(hidden_states), _ptr(gate_up_proj), _ptr(down_proj),
-                                     _ptr(top_k_index), _ptr(top_k_weights), T, H, F, E, k,
+                                     _ptr(top_k_index), _ptr(top_k_weights), res, T, H, F, E, k,
                                      _ptr(out), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(rc, entry)
     return out
 
 
 def moe_experts_prefill(hidden_states, gate_up_proj, down_proj, top_k_index, top_k_weights,
-                        top_k, workspace=None, out=None):
-    """Routed experts, grouped-GEMM form; returns out [T, H] bf16."""
+                        top_k, residual=None, workspace=None, out=None):
+    """Routed experts, grouped-GEMM form; returns out [T, H] bf16 (plus the
+    optional residual [T, H] bf16)."""
     return _bf16_call("moe_experts_prefill", MOE_VARIANT_PREFILL, hidden_states, gate_up_proj,
-                      down_proj, top_k_index, top_k_weights, top_k, workspace, out)
+                      down_proj, top_k_index, top_k_weights, top_k, residual, workspace, out)
 
 
 def moe_experts_decode(hidden_states, gate_up_proj, down_proj, top_k_index, top_k_weights,
-                       top_k, workspace=None, out=None):
+                       top_k, residual=None, workspace=None, out=None):
     """Routed experts, gather-GEMV form for T <= 4 (grouped form above);
-    returns out [T, H] bf16."""
+    returns out [T, H] bf16 (plus the optional residual)."""
     return _bf16_call("moe_experts_decode", MOE_VARIANT_DECODE, hidden_states, gate_up_proj,
-                      down_proj, top_k_index, top_k_weights, top_k, workspace, out)
+                      down_proj, top_k_index, top_k_weights, top_k, residual, workspace, out)
 
 
-def moe_experts_fp8(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
-                    top_k_weights, top_k, workspace=None, out=None):
-    """FP8 block-scaled routed experts.  fp8 operands are uint8 tensors of
-    E4M3FN codes (or torch.float8_e4m3fn tensors); returns out [T, H] bf16."""
-    def codes(t):
-        return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
-    x, gate_up, down = codes(x), codes(gate_up), codes(down)
-    dev = x.device
-    _need(x, "x", torch.uint8, 2)
-    _need(x_scale, "x_scale", torch.float32, 2, dev)
+def _codes(t):
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _fp8_call(entry, variant, lead, gate_up, gate_up_scale, down, down_scale, top_k_index,
+              top_k_weights, top_k, residual, workspace, out):
+    gate_up, down = _codes(gate_up), _codes(down)
+    dev = lead[0].device
     _need(gate_up, "gate_up", torch.uint8, 3, dev)
     _need(gate_up_scale, "gate_up_scale", torch.float32, 3, dev)
     _need(down, "down", torch.uint8, 3, dev)
     _need(down_scale, "down_scale", torch.float32, 3, dev)
     _need(top_k_index, "top_k_index", torch.int32, 2, dev)
     _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
-    T, H = x.shape
+    T, H = lead[0].shape
     E, F2, H2 = gate_up.shape
     F = F2 // 2
     k = int(top_k)
     if (H2 != H or F2 != 2 * F or tuple(down.shape) != (E, H, F)
-            or tuple(x_scale.shape) != (T, H // 128)
             or tuple(gate_up_scale.shape) != (E, 2 * F, H // 128)
             or tuple(down_scale.shape) != (E, H, F // 128)):
         raise ValueError("fp8 operand shapes do not match [T,H], [E,2F,H], [E,H,F] with per-128 scales")
     if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
         raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
     out = _out(out, T, H, dev)
     if T == 0:
         return out
     with torch.cuda.device(dev):
         stream = _stream(dev)
-        need = moe_workspace_size(MOE_VARIANT_FP8, T, H, F, E, k)
+        need = moe_workspace_size(variant, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
-        rc = _load().moe_experts_fp8(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
+        rc = getattr(_load(), entry)(*[_ptr(t) for t in lead], _ptr(gate_up), _ptr(gate_up_scale),
                                      _ptr(down), _ptr(down_scale), _ptr(top_k_index),
-                                     _ptr(top_k_weights), T, H, F, E, k, _ptr(out), _ptr(ws),
+                                     _ptr(top_k_weights), res, T, H, F, E, k, _ptr(out), _ptr(ws),
                                      ws.numel(), ctypes.c_void_p(stream))
-    _check(rc, "moe_experts_fp8")
+    _check(rc, entry)
     return out
+
+
+def moe_experts_fp8(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                    top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """FP8 block-scaled routed experts.  fp8 operands are uint8 tensors of
+    E4M3FN codes (or torch.float8_e4m3fn tensors); returns out [T, H] bf16
+    (plus the optional residual [T, H] bf16)."""
+    x = _codes(x)
+    _need(x, "x", torch.uint8, 2)
+    _need(x_scale, "x_scale", torch.float32, 2, x.device)
+    if tuple(x_scale.shape) != (x.shape[0], x.shape[1] // 128):
+        raise ValueError("x_scale must be [T, H/128]")
+    return _fp8_call("moe_experts_fp8", MOE_VARIANT_FP8, [x, x_scale], gate_up, gate_up_scale,
+                     down, down_scale, top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_fp8_bf16in(hidden_states, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                           top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """The FP8 layer fed with bf16 hidden states [T, H], quantised per
+    128-wide block inside the call; returns out [T, H] bf16."""
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    return _fp8_call("moe_experts_fp8_bf16in", MOE_VARIANT_FP8_BF16IN, [hidden_states], gate_up,
+                     gate_up_scale, down, down_scale, top_k_index, top_k_weights, top_k, residual,
+                     workspace, out)
 
 
 def moe_routing_plan(top_k_index, num_experts):
@@ -309,6 +348,7 @@ __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
     "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-    "moe_quantize_fp8_block128", "MoeError", "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE",
-    "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "LIB_PATH",
+    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "MoeError", "MOE_VARIANT_PREFILL",
+    "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "MOE_VARIANT_FP8_BF16IN",
+    "LIB_PATH",
 ]

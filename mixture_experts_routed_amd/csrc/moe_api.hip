@@ -102,7 +102,7 @@ constexpr size_t kNone = (size_t)-1;
 struct Layout {
     size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
            ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, part = kNone,
-           total = 0;
+           xq = kNone, xs = kNone, total = 0;
     bool decode_fast = false;
 };
 
@@ -142,23 +142,28 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     L.tiles = take((size_t)max_m_tiles(P, E) * 2 * sizeof(int32_t));
     L.ntiles = take(sizeof(int32_t));
     L.tile_off = take((size_t)(E + 1) * sizeof(int32_t));
-    if (variant == MOE_VARIANT_FP8) {
+    if (variant == MOE_VARIANT_FP8 || variant == MOE_VARIANT_FP8_BF16IN) {
         L.h = take((size_t)P * F);
         L.hs = take((size_t)P * (F / 128) * sizeof(float));
     } else {
         L.h = take((size_t)P * F * 2);
     }
     L.y = take((size_t)P * H * 2);
+    if (variant == MOE_VARIANT_FP8_BF16IN) {  // the quantised hidden states
+        L.xq = take((size_t)T * H);
+        L.xs = take((size_t)T * (H / 128) * sizeof(float));
+    }
     L.total = off;
     return L;
 }
 
 int check_shape(int variant, int64_t T, int H, int F, int E, int k) {
-    if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_PLAN) return MOE_ERR_SHAPE;
+    if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_FP8_BF16IN) return MOE_ERR_SHAPE;
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_ERR_SHAPE;
     if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     if (variant == MOE_VARIANT_PLAN) return MOE_OK;
-    const int mult = variant == MOE_VARIANT_FP8 ? 128 : 64;
+    const bool fp8 = variant == MOE_VARIANT_FP8 || variant == MOE_VARIANT_FP8_BF16IN;
+    const int mult = fp8 ? 128 : 64;
     if (H < mult || F < mult || H % mult || F % mult) return MOE_ERR_SHAPE;
     if ((int64_t)E * 2 * F * (int64_t)H >= ((int64_t)1 << 47)) return MOE_ERR_SHAPE;
     return MOE_OK;
@@ -191,8 +196,9 @@ GroupedPlan plan_in(const Layout& L, void* ws, int E) {
 
 // Routing plan into the workspace, then the two grouped bf16 products and the combine.
 int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* gate_up,
-                     const uint16_t* down, const int32_t* idx, const float* w, int64_t T, int H,
-                     int F, int E, int k, uint16_t* out, void* ws, hipStream_t s) {
+                     const uint16_t* down, const int32_t* idx, const float* w,
+                     const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                     uint16_t* out, void* ws, hipStream_t s) {
     const int P = (int)(T * k);
     const GroupedPlan pl = plan_in(L, ws, E);
     uint16_t* h = at<uint16_t>(ws, L.h);
@@ -211,16 +217,68 @@ int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* ga
     rc = launched(launch_down_bf16(h, down, pl, H, F, y, s));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, T, k, H, out, s));
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, s));
 }
 
 int check_bf16_args(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
-                    const int32_t* idx, const float* w, uint16_t* out) {
+                    const int32_t* idx, const float* w, const uint16_t* residual, uint16_t* out) {
     if (!hidden || !gate_up || !down || !idx || !w || !out) return MOE_ERR_NULL;
     if (!aligned16(hidden) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
-        ((uintptr_t)idx & 3u) || ((uintptr_t)w & 3u))
+        ((uintptr_t)idx & 3u) || ((uintptr_t)w & 3u) || (residual && !aligned16(residual)))
         return MOE_ERR_ALIGN;
     return MOE_OK;
+}
+// FP8 layer: the plan, the two grouped fp8 products and the combine; with
+// `hidden` (bf16) set, its block-128 quantisation into the workspace first.
+int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* x_scale,
+            const uint8_t* gate_up, const float* gate_up_scale, const uint8_t* down,
+            const float* down_scale, const int32_t* top_k_index, const float* top_k_weights,
+            const uint16_t* residual, int64_t T, int H, int F, int E, int k, uint16_t* out,
+            void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!gate_up || !gate_up_scale || !down || !down_scale || !top_k_index || !top_k_weights ||
+        !out)
+        return MOE_ERR_NULL;
+    if (!aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
+        (residual && !aligned16(residual)) ||
+        (((uintptr_t)gate_up_scale | (uintptr_t)down_scale | (uintptr_t)top_k_index |
+          (uintptr_t)top_k_weights) & 3u))
+        return MOE_ERR_ALIGN;
+    int rc = check_shape(variant, T, H, F, E, k);
+    if (rc) return rc;
+    const Layout L = make_layout(variant, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    const int P = (int)(T * k);
+    const GroupedPlan pl = plan_in(L, ws, E);
+    uint8_t* hq = at<uint8_t>(ws, L.h);
+    float* hs = at<float>(ws, L.hs);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    StageClock clock(stream);
+    if (hidden) {
+        x = at<uint8_t>(ws, L.xq);
+        x_scale = at<float>(ws, L.xs);
+        clock.mark(MOE_STAGE_QUANTIZE);
+        rc = launched(launch_quantize_fp8(hidden, 1, T, H, (uint8_t*)x, (float*)x_scale, stream));
+        if (rc) return rc;
+    }
+    clock.mark(MOE_STAGE_PLAN);
+    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
+                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
+                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), fp8_tile_m(),
+                              stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_GATE_UP);
+    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_DOWN);
+    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
+                                   out, stream));
 }
 }  // namespace
 }  // namespace moe
@@ -282,10 +340,10 @@ int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E, int32_
 }
 
 int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
-                        const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H,
-                        int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
-    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, out);
+                        const int32_t* top_k_index, const float* top_k_weights,
+                        const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
     if (rc) return rc;
     if ((rc = check_shape(MOE_VARIANT_PREFILL, T, H, F, E, k))) return rc;
     const Layout L = make_layout(MOE_VARIANT_PREFILL, T, H, F, E, k);
@@ -293,15 +351,15 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
     int dev;
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
-    return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, T, H, F, E, k,
-                            out, ws, stream);
+    return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, residual, T, H,
+                            F, E, k, out, ws, stream);
 }
 
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
-                       const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H,
-                       int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
-    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, out);
+                       const int32_t* top_k_index, const float* top_k_weights,
+                       const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
     if (rc) return rc;
     if ((rc = check_shape(MOE_VARIANT_DECODE, T, H, F, E, k))) return rc;
     const Layout L = make_layout(MOE_VARIANT_DECODE, T, H, F, E, k);
@@ -310,8 +368,8 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
     if (!L.decode_fast)
-        return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, T, H, F, E,
-                                k, out, ws, stream);
+        return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, residual, T,
+                                H, F, E, k, out, ws, stream);
     StageClock clock(stream);
     clock.mark(MOE_STAGE_DECODE_SLICES);
     rc = launched(launch_decode_slices(hidden, gate_up, down, top_k_index, (int)T, k, E, H, F,
@@ -319,48 +377,31 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_decode_combine(at<float>(ws, L.part), top_k_index, top_k_weights,
-                                          (int)T, k, E, H, F, out, stream));
+                                          residual, (int)T, k, E, H, F, out, stream));
 }
 
 int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
                     const float* gate_up_scale, const uint8_t* down, const float* down_scale,
-                    const int32_t* top_k_index, const float* top_k_weights, int64_t T, int H, int F,
-                    int E, int k, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (!x || !x_scale || !gate_up || !gate_up_scale || !down || !down_scale || !top_k_index ||
-        !top_k_weights || !out)
-        return MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
-        (((uintptr_t)x_scale | (uintptr_t)gate_up_scale | (uintptr_t)down_scale |
-          (uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
-        return MOE_ERR_ALIGN;
-    int rc = check_shape(MOE_VARIANT_FP8, T, H, F, E, k);
-    if (rc) return rc;
-    const Layout L = make_layout(MOE_VARIANT_FP8, T, H, F, E, k);
-    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
-    int dev;
-    if ((rc = query_device(&dev))) return rc;
-    if (T == 0) return MOE_OK;
-    const int P = (int)(T * k);
-    const GroupedPlan pl = plan_in(L, ws, E);
-    uint8_t* hq = at<uint8_t>(ws, L.h);
-    float* hs = at<float>(ws, L.hs);
-    uint16_t* y = at<uint16_t>(ws, L.y);
-    StageClock clock(stream);
-    clock.mark(MOE_STAGE_PLAN);
-    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
-                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
-                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
-                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), fp8_tile_m(),
-                              stream));
-    if (rc) return rc;
-    clock.mark(MOE_STAGE_GATE_UP);
-    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
-    if (rc) return rc;
-    clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
-    if (rc) return rc;
-    clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, T, k, H, out, stream));
+                    const int32_t* top_k_index, const float* top_k_weights,
+                    const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                    uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !x_scale) return MOE_ERR_NULL;
+    if (!aligned16(x) || ((uintptr_t)x_scale & 3u)) return MOE_ERR_ALIGN;
+    return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
+                   top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
+}
+
+int moe_experts_fp8_bf16in(const uint16_t* hidden, const uint8_t* gate_up,
+                           const float* gate_up_scale, const uint8_t* down,
+                           const float* down_scale, const int32_t* top_k_index,
+                           const float* top_k_weights, const uint16_t* residual, int64_t T,
+                           int H, int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    if (!hidden) return MOE_ERR_NULL;
+    if (!aligned16(hidden)) return MOE_ERR_ALIGN;
+    return run_fp8(MOE_VARIANT_FP8_BF16IN, hidden, nullptr, nullptr, gate_up, gate_up_scale, down,
+                   down_scale, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
+                   ws_bytes, stream);
 }
 
 int moe_profile_begin(int max_calls) {

@@ -11,8 +11,8 @@
 //     (all H rows, 64 bytes each, prefetched into LDS when the workgroup
 //     starts) and writes one fp32 partial sum per (slot, slice, column).
 // A second, small kernel adds the partial sums of every slot in a fixed
-// order and applies the router weights (the combine): deterministic, no
-// float atomics.  Every weight byte of a selected expert is read from HBM
+// order, applies the router weights and adds the residual if any (the
+// combine): deterministic, no float atomics.  Every weight byte of a selected expert is read from HBM
 // once, and the whole weight stream runs in a single launch: on MI355X a
 // short stream pays a fixed start-up cost of several microseconds, so one
 // long stream beats two short ones, and splitting F (not H) lets the down
@@ -270,7 +270,8 @@ constexpr int kCombCols = 16, kCombGroups = 16, kCombBatch = 16;  // many small 
 constexpr int kCombThreads = kCombCols * kCombGroups;
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
-    int T, int k, int E, int H, int nslices, uint16_t* __restrict__ out) {
+    const uint16_t* __restrict__ residual, int T, int k, int E, int H, int nslices,
+    uint16_t* __restrict__ out) {
     __shared__ float wsl[kDecodeMaxSlots];
     __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
     const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
@@ -323,7 +324,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
             float o = 0.0f;
 #pragma unroll
             for (int i = 0; i < kCombGroups; ++i) o += red[i][t][cc];
-            out[(int64_t)t * H + blockIdx.x * kCombCols + cc] = (uint16_t)f32_to_bf16(o);
+            const int64_t oi = (int64_t)t * H + blockIdx.x * kCombCols + cc;
+            if (residual) o += bf16_to_f32(residual[oi]);
+            out[oi] = (uint16_t)f32_to_bf16(o);
         }
     }
 }
@@ -368,11 +371,12 @@ hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const ui
                          : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s);
 }
 
-hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w, int T,
-                                 int k, int E, int H, int F, uint16_t* out, hipStream_t s) {
+hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
+                                 const uint16_t* residual, int T, int k, int E, int H, int F,
+                                 uint16_t* out, hipStream_t s) {
     const DecodeGeometry g = decode_geometry(T, k, E, H, F);
     MOE_LAUNCH(decode_combine_kernel, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0, s, part,
-                       idx, w, T, k, E, H, g.nslices, out);
+                       idx, w, residual, T, k, E, H, g.nslices, out);
     return hipGetLastError();
 }
 

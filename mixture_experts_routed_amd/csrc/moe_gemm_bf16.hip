@@ -263,12 +263,15 @@ hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const Grouped
 
 // ------------------------------------------------------------------ combine
 // One thread per (token, 8 columns): out = sum_j w[t,j] * y[inv[t*k+j]] in
-// slot order, fp32, one rounding to bf16.  y is in expert order; inv (from
-// the plan) is -1 for dropped slots, which contribute nothing.
+// slot order, plus the residual if any, in fp32, one rounding to bf16.  y is
+// in expert order; inv (from the plan) is -1 for dropped slots, which
+// contribute nothing.
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
-                                                      const float* __restrict__ w, int64_t T,
-                                                      int k, int H, uint16_t* __restrict__ out) {
+                                                      const float* __restrict__ w,
+                                                      const uint16_t* __restrict__ residual,
+                                                      int64_t T, int k, int H,
+                                                      uint16_t* __restrict__ out) {
     const int cpr = H / 8;
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= T * cpr) return;
@@ -285,6 +288,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += wt * f[i];
     }
+    if (residual) {
+        float r[8];
+        unpack8(*(const uint4*)(residual + t * H + c), r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += r[i];
+    }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
     o.y = pack_bf16x2(acc[2], acc[3]);
@@ -293,11 +302,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     *(uint4*)(out + t * H + c) = o;
 }
 
-hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int k,
-                          int H, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
+                          const uint16_t* residual, int64_t T, int k, int H, uint16_t* out,
+                          hipStream_t s) {
     const int64_t n = T * (H / 8);
     const int blocks = (int)((n + 255) / 256);
-    MOE_LAUNCH(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, T, k, H, out);
+    MOE_LAUNCH(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, residual, T, k, H, out);
     return hipGetLastError();
 }
 

@@ -61,9 +61,11 @@ hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const Grou
 hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& plan, int H,
                             int F, uint16_t* y, hipStream_t s);
 
-// out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots, fp32 in slot order.
-hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w, int64_t T, int k,
-                          int H, uint16_t* out, hipStream_t s);
+// out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots (fp32, slot order)
+// + residual[t] when residual is not null.
+hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
+                          const uint16_t* residual, int64_t T, int k, int H, uint16_t* out,
+                          hipStream_t s);
 
 // Decode gather-GEMV (T small): one launch streams the selected experts'
 // weights in 32-wide F slices and writes fp32 partial down products
@@ -101,8 +103,9 @@ inline size_t decode_partial_bytes(int64_t T, int k, int E, int H, int F) {
 hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
                                 const int32_t* idx, int T, int k, int E, int H, int F, float* part,
                                 hipStream_t s);
-hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w, int T,
-                                 int k, int E, int H, int F, uint16_t* out, hipStream_t s);
+hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
+                                 const uint16_t* residual, int T, int k, int E, int H, int F,
+                                 uint16_t* out, hipStream_t s);
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,

@@ -46,17 +46,17 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
     assert moe.moe_strerror(-99) == "unknown status"
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 4])
 def test_workspace_sizes_and_layout(variant):
     T, H, F, E, k = 2048, 1280, 896, 64, 6
-    if variant == 2:
+    if variant in (2, 4):
         T, H, F, E, k = 4096, 7168, 2048, 128, 8
     n = moe.moe_workspace_size(variant, T, H, F, E, k)
     lay = moe.moe_workspace_layout(variant, T, H, F, E, k)
@@ -66,9 +66,11 @@ def test_workspace_sizes_and_layout(variant):
     assert offs == sorted(offs) and len(set(offs)) == len(offs) and max(offs) < n
     P = T * k
     assert n >= P * H * 2                                   # y [P, H] bf16
-    if variant == 2:
+    if variant in (2, 4):
         assert lay["h_scale"] - lay["h"] >= P * F           # fp8 codes
         assert n - lay["y"] >= P * H * 2
+    if variant == 4:                                        # + the quantised hidden states
+        assert n >= moe.moe_workspace_size(2, T, H, F, E, k) + T * H + T * (H // 128) * 4
 
 
 def test_decode_fast_path_workspace_is_small():
@@ -104,9 +106,9 @@ def test_null_out_pointer_status():
     assert lib.moe_workspace_size(0, 4, 128, 64, 8, 2, None) == ENULL
 
 
-def _prefill(lib, fn, *, hidden=P16, gu=P16, dn=P16, idx=P16, w=P16, out=P16, T=4, H=128, F=64,
-             E=8, k=2, ws=P16B, ws_bytes=1 << 30):
-    return getattr(lib, fn)(hidden, gu, dn, idx, w, T, H, F, E, k, out, ws, ws_bytes, None)
+def _prefill(lib, fn, *, hidden=P16, gu=P16, dn=P16, idx=P16, w=P16, res=None, out=P16, T=4,
+             H=128, F=64, E=8, k=2, ws=P16B, ws_bytes=1 << 30):
+    return getattr(lib, fn)(hidden, gu, dn, idx, w, res, T, H, F, E, k, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("fn", ["moe_experts_prefill", "moe_experts_decode"])
@@ -116,6 +118,7 @@ def test_bf16_entry_validation(fn):
     assert _prefill(lib, fn, out=None) == ENULL
     assert _prefill(lib, fn, gu=P16 + 2) == EALIGN
     assert _prefill(lib, fn, idx=P16 + 2) == EALIGN
+    assert _prefill(lib, fn, res=P16 + 2) == EALIGN          # residual not 16-byte aligned
     assert _prefill(lib, fn, k=9) == ESHAPE
     assert _prefill(lib, fn, H=96) == ESHAPE
     assert _prefill(lib, fn, ws=None) == EWS
@@ -125,15 +128,27 @@ def test_bf16_entry_validation(fn):
 
 def test_fp8_and_plan_validation():
     lib = moe._load()
-    args = [P16] * 8 + [4, 256, 128, 8, 2, P16, P16B, 1 << 30, None]
+    args = [P16] * 8 + [None, 4, 256, 128, 8, 2, P16, P16B, 1 << 30, None]
     bad = list(args); bad[1] = None
     assert lib.moe_experts_fp8(*bad) == ENULL
     bad = list(args); bad[2] = P16 + 8
     assert lib.moe_experts_fp8(*bad) == EALIGN
-    bad = list(args); bad[9] = 192
+    bad = list(args); bad[8] = P16 + 8                         # residual
+    assert lib.moe_experts_fp8(*bad) == EALIGN
+    bad = list(args); bad[10] = 192                             # H
     assert lib.moe_experts_fp8(*bad) == ESHAPE
-    bad = list(args); bad[15] = 0
+    bad = list(args); bad[16] = 0                               # ws_bytes
     assert lib.moe_experts_fp8(*bad) == EWS
+    # bf16-input form: hidden replaces (x, x_scale)
+    args = [P16] * 7 + [None, 4, 256, 128, 8, 2, P16, P16B, 1 << 30, None]
+    bad = list(args); bad[0] = None
+    assert lib.moe_experts_fp8_bf16in(*bad) == ENULL
+    bad = list(args); bad[0] = P16 + 2
+    assert lib.moe_experts_fp8_bf16in(*bad) == EALIGN
+    bad = list(args); bad[9] = 192                              # H
+    assert lib.moe_experts_fp8_bf16in(*bad) == ESHAPE
+    bad = list(args); bad[15] = 16                              # ws_bytes
+    assert lib.moe_experts_fp8_bf16in(*bad) == EWS
     assert lib.moe_routing_plan(None, 4, 2, 8, P16, P16, P16, P16, P16B, 1 << 20, None) == ENULL
     assert lib.moe_routing_plan(P16, 4, 9, 8, P16, P16, P16, P16, P16B, 1 << 20, None) == ESHAPE
     assert lib.moe_routing_plan(P16, 4, 2, 8, P16, P16, P16, P16, P16B, 1, None) == EWS

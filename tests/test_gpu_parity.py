@@ -446,3 +446,102 @@ def test_stage_recorder_times_every_kernel():
     assert [s for s, _ in calls[0]] == ["plan", "gate_up", "down", "combine"]
     assert [s for s, _ in calls[1]] == ["decode_slices", "combine"]
     assert all(ms > 0 for row in calls for _, ms in row)
+
+
+# -------------------------------------------------- residual, bf16-input fp8
+
+
+def _residual(T, H, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(T, H, generator=g).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("entry,shape", [("moe_experts_prefill", (300, 256, 128, 6, 2)),
+                                         ("moe_experts_decode", (1, 256, 128, 8, 4)),
+                                         ("moe_experts_decode", (4, 512, 192, 8, 3)),
+                                         ("moe_experts_decode", (7, 128, 64, 8, 2))])
+def test_residual_bf16(entry, shape):
+    """out = weighted sum + residual ([MPK] moe_local_reduction), on the grouped
+    path, the decode form and the decode fallback to the grouped path."""
+    moe = _moe()
+    T, H, F, E, k = shape
+    _say(f"residual {entry} {shape}")
+    p = bf16_problem(T, H, F, E, k, seed=51 + T, std=1 / np.sqrt(H))
+    r = _residual(T, H, 52 + T)
+    ref = orc.moe_experts_reference_batched(f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]),
+                                            p["top_k_index"].numpy(), f64(p["top_k_weights"]),
+                                            residual=f64(r))
+    g = to_gpu(p)
+    out = getattr(moe, entry)(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                              g["top_k_weights"], k, residual=r.cuda())
+    check_tol(out, ref, BF16_TOL, f"{entry} {shape}")
+    # all routing weights zero: the output is the residual, bit for bit
+    z = getattr(moe, entry)(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                            torch.zeros_like(g["top_k_weights"]), k, residual=r.cuda())
+    assert torch.equal(z.cpu().view(torch.int16), r.view(torch.int16))
+
+
+def test_residual_fp8():
+    moe = _moe()
+    T, H, F, E, k = 64, 256, 128, 8, 4
+    _say("residual fp8")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=53, routing="uniform_softmax", routed_scale=1.0)
+    r = _residual(T, H, 54)
+    ref = orc.moe_experts_fp8_reference(
+        p["x"].numpy(), p["x_scale"].numpy(), p["gate_up"].numpy(), p["gate_up_scale"].numpy(),
+        p["down"].numpy(), p["down_scale"].numpy(), p["top_k_index"].numpy(),
+        p["top_k_weights"].numpy(), residual=f64(r))
+    g = to_gpu(p)
+    out = moe.moe_experts_fp8(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"],
+                              g["down_scale"], g["top_k_index"], g["top_k_weights"], k,
+                              residual=r.cuda())
+    check_tol(out, ref, FP8_TOL, "fp8 residual")
+
+
+@pytest.mark.parametrize("shape", [(64, 256, 128, 8, 4), (300, 512, 384, 6, 3), (3, 256, 128, 5, 2)])
+def test_fp8_bf16in_medium(shape):
+    """FP8 layer fed with bf16 hidden states (quantised per 128 block inside the
+    call) against the oracle's bf16_to_fp8_quantize + fp8 layer; and bit-equal
+    to quantising with moe_quantize_fp8_block128 and calling moe_experts_fp8."""
+    moe = _moe()
+    T, H, F, E, k = shape
+    _say(f"fp8 bf16-in {shape}")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=55 + T, routing="uniform_softmax", routed_scale=1.0)
+    hidden = _residual(T, H, 56 + T)
+    r = _residual(T, H, 57 + T) if T % 2 else None
+    ref = orc.moe_experts_fp8_bf16_reference(
+        f64(hidden), p["gate_up"].numpy(), p["gate_up_scale"].numpy(), p["down"].numpy(),
+        p["down_scale"].numpy(), p["top_k_index"].numpy(), p["top_k_weights"].numpy(),
+        residual=None if r is None else f64(r))
+    g = to_gpu(p)
+    rg = None if r is None else r.cuda()
+    out = moe.moe_experts_fp8_bf16in(hidden.cuda(), g["gate_up"], g["gate_up_scale"], g["down"],
+                                     g["down_scale"], g["top_k_index"], g["top_k_weights"], k,
+                                     residual=rg)
+    worst, rel = check_tol(out, ref, FP8_TOL, f"bf16-in {shape}")
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+    xq, xs = moe.moe_quantize_fp8_block128(hidden.cuda())
+    two = moe.moe_experts_fp8(xq, xs, g["gate_up"], g["gate_up_scale"], g["down"], g["down_scale"],
+                              g["top_k_index"], g["top_k_weights"], k, residual=rg)
+    assert torch.equal(out.view(torch.int16), two.view(torch.int16))
+
+
+def test_fp8_bf16in_full_config_sampled():
+    """DeepSeek-V3-shaped decode batch (T=128, H=7168, F=2048, 128 experts,
+    top-8) fed with bf16 N(0,1) hidden states; sampled rows against the oracle."""
+    moe = _moe()
+    _say("fp8 bf16-in full v3_fp8_decode")
+    p = wl.make_config("v3_fp8_decode", device="cuda")
+    T, H = p["x"].shape
+    k = p["top_k_index"].shape[1]
+    hidden = _residual(T, H, 58).cuda()
+    out = moe.moe_experts_fp8_bf16in(hidden, p["gate_up"], p["gate_up_scale"], p["down"],
+                                     p["down_scale"], p["top_k_index"], p["top_k_weights"], k)
+    torch.cuda.synchronize()
+    tokens = sorted(set(_sample_tokens(T, 4, 9)))
+    hp = _host_fp8(p)
+    ref = orc.moe_experts_fp8_bf16_reference(
+        f64(hidden), hp["gate_up"], hp["gate_up_scale"], hp["down"], hp["down_scale"],
+        p["top_k_index"].cpu().numpy(), p["top_k_weights"].cpu().numpy(), tokens=tokens)
+    worst, rel = check_tol(out[tokens], ref[tokens], FP8_TOL, "bf16-in full")
+    _say(f"  tokens {tokens}: worst err/tol {worst:.3f} rel L2 {rel:.2e}")
