@@ -214,7 +214,7 @@ int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* ga
     rc = launched(launch_gateup_bf16(hidden, gate_up, pl, H, F, k, h, s));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_bf16(h, down, pl, H, F, y, s));
+    rc = launched(launch_down_bf16(h, down, pl, P, H, F, y, s));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, s));

@@ -8,6 +8,8 @@
 // K-major, the layout MFMA wants).  The combine follows mirage issue
 // "Supporting MegaKernel for DeepSeek Models", moe_local_reduction, without
 // its residual, done as a gather in slot order (no float atomics).
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -253,9 +255,23 @@ hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const Grou
     return hipGetLastError();
 }
 
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& pl, int H,
-                            int F, uint16_t* y, hipStream_t s) {
-    if (H % 256 == 0) launch_bf16<256, false>(h, w2, pl, F, H, H, 1, y, s);
+// Rounds of a persistent grid of G workgroups over `items` equal items, in
+// units of a 256-wide item (a BN-wide item costs BN/256 of one).
+static double makespan(int64_t items, int G, int BN) {
+    return (double)((items + G - 1) / G) * BN / 256.0;
+}
+
+hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& pl, int P,
+                            int H, int F, uint16_t* y, hipStream_t s) {
+    // The M-tile count is only known on the device; about max(P/256, one
+    // tile per touched expert) tiles: pick the panel width whose rounds of the
+    // persistent grid finish first (256-wide items leave a mostly idle last
+    // round when their count is a little above a multiple of the grid).
+    const int64_t tiles = std::max<int64_t>((P + kBM - 1) / kBM, std::min<int64_t>(pl.E, P));
+    const bool narrow = H % 256 != 0 ||
+                        makespan(tiles * (H / 128), gemm_grid<128, false>(), 128) <
+                            makespan(tiles * (H / 256), gemm_grid<256, false>(), 256);
+    if (!narrow) launch_bf16<256, false>(h, w2, pl, F, H, H, 1, y, s);
     else if (H % 128 == 0) launch_bf16<128, false>(h, w2, pl, F, H, H, 1, y, s);
     else launch_bf16<64, false>(h, w2, pl, F, H, H, 1, y, s);
     return hipGetLastError();

@@ -58,8 +58,8 @@ hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const Grou
                               int H, int F, int k, uint16_t* h, hipStream_t s);
 
 // down product -> y bf16 [P, H] in expert order (row = position in perm).
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& plan, int H,
-                            int F, uint16_t* y, hipStream_t s);
+hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& plan, int P,
+                            int H, int F, uint16_t* y, hipStream_t s);
 
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots (fp32, slot order)
 // + residual[t] when residual is not null.

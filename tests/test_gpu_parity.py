@@ -150,6 +150,7 @@ def test_tiny_scaled_twin():
     (257, 128, 64, 5, 3),      # one row past a tile
     (96, 256, 192, 16, 4),     # many small experts, some empty
     (300, 192, 128, 4, 4),     # k == E; H not a multiple of 128 (64-wide down tiles)
+    (64, 1024, 128, 128, 2),   # many experts: the down product keeps 256-wide panel tiles
 ])
 def test_prefill_medium(shape):
     T, H, F, E, k = shape
