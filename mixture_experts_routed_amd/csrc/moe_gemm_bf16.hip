@@ -9,21 +9,42 @@
 // "Supporting MegaKernel for DeepSeek Models", moe_local_reduction, without
 // its residual, done as a gather in slot order (no float atomics).
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kGemmThreads = 512;  // 8 waves: a 4 (M) x 2 (N) grid of 64 x BN/2 wave tiles
+constexpr int kGemmThreads = 512;  // 8 waves; see WaveGrid for their tiles
 constexpr int kBM = 256;           // rows of an M tile (about one expert's rows at prefill sizes)
 constexpr int kBK = 64;            // bf16 K elements per stage: one 128-byte line per row
 constexpr int kAStages = 2;        // token-row stages (L2 hits mostly): loads run 1 step ahead
 constexpr int kBStages = 3;        // weight stages (HBM): loads run 2 steps ahead
 
+// How the 8 waves split a 256 x BN tile.  Waves w and w + 4 of a workgroup
+// share one SIMD (MI355X places the first four waves on the four SIMDs and
+// the next four in the same order).  For 256-wide panels the grid is 2 (M) x
+// 4 (N), laid out so that the two waves of a SIMD own the same panel columns
+// and the two 128-row halves of the tile: a wave skips its 32-row blocks past
+// the tile's last row, so each SIMD's matrix work follows the rows the tile
+// really has (experts with 160-220 rows fill 256-row tiles only in part).
+// Narrower panels keep a 4 (M) x 2 (N) grid (a SWIGLU wave needs a gate
+// block and its up block).
+template <int BN>
+struct WaveGrid {
+    static constexpr int WN = BN == 256 ? 4 : 2;   // waves along the panel
+    static constexpr int WM = 8 / WN;              // waves along the rows
+    static constexpr int MB = kBM / 32 / WM;       // 32-row blocks per wave
+    static constexpr int NB = BN / 32 / WN;        // 32-row panel blocks per wave
+    __device__ static int wm(int wave) { return WN == 4 ? wave >> 2 : wave & 3; }
+    __device__ static int wn(int wave) { return WN == 4 ? wave & 3 : wave >> 2; }
+};
+
 // One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
-// expert's weight panel).  Wave (wm, wn) owns tile rows [64wm, 64wm+64) as two
-// 32-row blocks and panel rows [wn*BN/2, (wn+1)*BN/2) as NB 32-row blocks.
+// expert's weight panel).  Wave (wm, wn) owns tile rows [32 MB wm, 32 MB
+// (wm+1)) as MB 32-row blocks and panel rows [32 NB wn, 32 NB (wn+1)) as NB
+// 32-row blocks.
 // Operands stream through LDS rings filled by direct global->LDS loads, one
 // whole 128-byte line per row and stage (on MI355X, half-line requests halve
 // what L2 delivers per CU).  Each lane fetches the global chunk that belongs
@@ -43,8 +64,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
     uint16_t* __restrict__ C) {
-    constexpr int MB = 2;                     // 32-row blocks per wave
-    constexpr int NB = BN / 64;               // 32-row panel blocks per wave
+    using WG = WaveGrid<BN>;
+    constexpr int MB = WG::MB;
+    constexpr int NB = WG::NB;
     constexpr int A_INST = kBM / 8 / 8;       // 8 rows per wave load; per wave and stage
     constexpr int B_INST = BN / 8 / 8;
     constexpr int A_STAGE = kBM * 8;          // u32x4 per stage
@@ -56,7 +78,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     __shared__ u32x4 lds[kAStages * A_STAGE + kBStages * B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = WG::wm(wave), wn = WG::wn(wave);
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
     const int items = ntiles * n_tiles_n;
@@ -123,26 +145,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     };
 
     f32x16 acc[MB][NB];
-    // Waves past the tile's last row compute too (on row-0 data, never
-    // stored): a branch here would make the compiler wait for every LDS
-    // fill in flight before the fragment reads.
-    auto compute = [&](int ks) {
+    // The first NV row blocks of the wave, NV a compile-time count: the
+    // fragment reads and products of blocks past the tile's last row are
+    // skipped (their rows hold row-0 data and are never stored).
+    auto compute_nv = [&](auto nv_c, int ks) {
+        constexpr int NV = decltype(nv_c)::value;
         const u32x4* as = &lds[(ks & 1) * A_STAGE];
         const u32x4* bs = &lds[B_BASE + (ks % kBStages) * B_STAGE];
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int c = (kk * 2 + (lane >> 5)) ^ fsw;
-            u32x4 af[MB], bf[NB];
+            u32x4 af[NV], bf[NB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) af[mb] = as[(64 * wm + 32 * mb + (lane & 31)) * 8 + c];
+            for (int mb = 0; mb < NV; ++mb) af[mb] = as[(32 * (MB * wm + mb) + (lane & 31)) * 8 + c];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) bf[nb] = bs[((wn * NB + nb) * 32 + (lane & 31)) * 8 + c];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < NV; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     acc[mb][nb] = mfma_bf16_32x32x16(af[mb], bf[nb], acc[mb][nb]);
         }
+    };
+    // nv (the same in every lane of a wave) = row blocks of this wave that
+    // hold tile rows
+    auto compute = [&](int ks, int nv) {
+        if (nv >= MB) compute_nv(std::integral_constant<int, MB>(), ks);
+        else if (nv == 1) compute_nv(std::integral_constant<int, 1>(), ks);
+        else if (MB > 2 && nv == 2) compute_nv(std::integral_constant<int, (MB > 2 ? 2 : 1)>(), ks);
+        else if (MB > 3 && nv == 3) compute_nv(std::integral_constant<int, (MB > 3 ? 3 : 1)>(), ks);
     };
 
     // Stores of the finished tile.  Lanes l and l ^ 1 hold neighbouring
@@ -151,7 +182,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     // so every store writes a bf16 pair.
     auto epilogue = [&](const Item& m) {
         const bool odd = lane & 1;
-        if (64 * wm >= m.mrows) return;
+        if (32 * MB * wm >= m.mrows) return;
         if (SWIGLU) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
                         const float h0 = silu_fast(acc[mb][2 * p][q]) * acc[mb][2 * p + 1][q];
                         const float h1 = silu_fast(acc[mb][2 * p][q + 1]) * acc[mb][2 * p + 1][q + 1];
                         const float got = pair_swap(odd ? h0 : h1);
-                        const int row = 64 * wm + 32 * mb + acc_row(q, lane) + (odd ? 1 : 0);
+                        const int row = 32 * (MB * wm + mb) + acc_row(q, lane) + (odd ? 1 : 0);
                         if (row < m.mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, h1) : pack_bf16x2_hw(h0, got);
                             *(uint32_t*)(C + (int64_t)(m.row0 + row) * n_out + (f & ~1)) = v;
@@ -175,7 +206,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int q = 0; q < 16; q += 2) {
-                    const int row = 64 * wm + 32 * mb + acc_row(q, lane) + (odd ? 1 : 0);
+                    const int row = 32 * (MB * wm + mb) + acc_row(q, lane) + (odd ? 1 : 0);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const float y0 = acc[mb][nb][q], y1 = acc[mb][nb][q + 1];
@@ -200,19 +231,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
-        // first stage: wait for everything (the previous item's epilogue
-        // stores are vector-memory operations too)
-        stage_barrier<0>();
-        load_a(cur, min(1, nks - 1));
-        load_b(cur, min(2, nks - 1));
-        compute(0);
-        // issue order per step: A(ks+1), then B(ks+2); at step ks the newest
-        // B_INST operations (B(ks+1)) may still be in flight
-        for (int ks = 1; ks < nks; ++ks) {
+        const int nv = min(MB, max(0, (cur.mrows - 32 * MB * wm + 31) >> 5));
+        // Issue order per step: A(ks+1), then B(ks+2); at step ks the newest
+        // B_INST operations (B(ks+1)) may still be in flight.  Loads complete
+        // in issue order, so at most B_INST operations in flight means A(ks)
+        // and B(ks) have landed: at step 0 too, where the prologue's B(1) and
+        // the previous item's epilogue stores are the newer operations.
+        for (int ks = 0; ks < nks; ++ks) {
             stage_barrier<B_INST>();           // A(ks) and B(ks) have landed for every wave
             load_a(cur, min(ks + 1, nks - 1)); // refills the A slot read at step ks - 1
             load_b(cur, min(ks + 2, nks - 1)); // refills the B slot read at step ks - 1
-            compute(ks);
+            compute(ks, nv);
         }
         lds_barrier();  // every wave is done with the ring before the next item's fills
 
