@@ -313,7 +313,10 @@ def _host_fp8(p):
     return q
 
 
-@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2)])
+# (T, H, F, E, k)
+@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2),
+                                   (600, 256, 128, 4, 2),    # 3 M tiles per expert, 1 K step in down
+                                   (700, 512, 256, 3, 2)])   # 467 rows per expert
 def test_fp8_medium(shape):
     T, H, F, E, k = shape
     _say(f"fp8 medium {shape}")
@@ -324,7 +327,8 @@ def test_fp8_medium(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-def test_fp8_h_stage_codes():
+@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 256, 256, 4, 2)])
+def test_fp8_h_stage_codes(shape):
     """The re-quantised h in the workspace against the oracle's fp32 rule applied
     to the oracle's h.  The kernel quantises its own fp32-accumulated h, which
     differs from the oracle's float64 h by fp32 summation error (about 1e-5
@@ -332,8 +336,8 @@ def test_fp8_h_stage_codes():
     one-step flips at rounding boundaries.  Bit-exactness of the quantiser on
     identical inputs is test_quantizer_bit_exact."""
     moe = _moe()
-    _say("fp8 h stage")
-    T, H, F, E, k = 200, 256, 256, 4, 2
+    _say(f"fp8 h stage {shape}")
+    T, H, F, E, k = shape
     p = wl.make_fp8_problem(T, H, F, E, k, seed=41, routing="uniform_softmax", routed_scale=1.0)
     g = to_gpu(p)
     lay = moe.moe_workspace_layout(2, T, H, F, E, k)
@@ -413,9 +417,10 @@ def test_fp8_full_config_sampled(name, n_sample):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fp8 path not deterministic"
 
 
-def test_fp8_overwrite_and_dropped():
-    _say("fp8 overwrite + dropped")
-    T, H, F, E, k = 100, 256, 128, 4, 3
+@pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 256, 128, 4, 3)])
+def test_fp8_overwrite_and_dropped(shape):
+    _say(f"fp8 overwrite + dropped {shape}")
+    T, H, F, E, k = shape
     p = wl.make_fp8_problem(T, H, F, E, k, seed=3, routing="uniform_softmax", routed_scale=1.0)
     idx = p["top_k_index"].clone()
     idx[::3, 1] = -1
