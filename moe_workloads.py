@@ -16,6 +16,9 @@ Models", Layer Tensor Details for moe_w13_fp8_layer / moe_w2_fp8_layer):
 * ``ocr2_prefill``    T=2048, same shapes, bf16
 * ``v3_fp8_decode``   T=128, H=7168, F=2048, E=128, k=8, fp8 block-scaled
 * ``v3_fp8_prefill``  T=4096, same shapes and weights, Zipf(1.2) routing
+* ``ocr2_prefill_shared``, ``ocr2_decode_t1_shared``: the OCR-2 workloads
+  plus the model's two shared experts (same F as a routed expert), which
+  every token passes through with weight 1
 """
 
 from __future__ import annotations
@@ -38,6 +41,11 @@ CONFIGS = {
     "v3_fp8_prefill": dict(T=4096, H=7168, F=2048, E=128, k=8, kind="fp8", seed=1004,
                            act_seed=1005, routing="zipf", zipf_s=1.2, zipf_zero=8,
                            routed_scale=2.5),
+    "ocr2_prefill_shared": dict(T=2048, H=1280, F=896, E=64, k=6, kind="bf16", seed=1003,
+                                routing="uniform_softmax", routed_scale=1.0, S=2, shared_seed=1006),
+    "ocr2_decode_t1_shared": dict(T=1, H=1280, F=896, E=64, k=6, kind="bf16", seed=1002,
+                                  routing="uniform_softmax", routed_scale=1.0, S=2,
+                                  shared_seed=1006),
 }
 
 
@@ -183,12 +191,24 @@ def make_fp8_problem(T, H, F, E, k, seed, device="cpu", act_seed=None, **kw):
     return p
 
 
+def make_shared_experts(S, H, F, seed, device="cpu", weight_std=0.02):
+    """Shared-expert weights, drawn like routed ones: shared_gate_up [S,2F,H]
+    and shared_down [S,H,F], bf16 N(0, std), gate_up first."""
+    g = _gen(seed, "cpu")
+    sg = (torch.randn(S, 2 * F, H, generator=g) * weight_std).to(torch.bfloat16)
+    sd = (torch.randn(S, H, F, generator=g) * weight_std).to(torch.bfloat16)
+    return dict(shared_gate_up=sg.to(device).contiguous(), shared_down=sd.to(device).contiguous())
+
+
 def make_config(name, device="cpu"):
     """Problem tensors for one named workload (see CONFIGS)."""
     c = CONFIGS[name]
     if c["kind"] == "bf16":
-        return make_bf16_problem(c["T"], c["H"], c["F"], c["E"], c["k"], c["seed"], device,
-                                 routing=c["routing"], routed_scale=c["routed_scale"])
+        p = make_bf16_problem(c["T"], c["H"], c["F"], c["E"], c["k"], c["seed"], device,
+                              routing=c["routing"], routed_scale=c["routed_scale"])
+        if c.get("S"):
+            p.update(make_shared_experts(c["S"], c["H"], c["F"], c["shared_seed"], device))
+        return p
     extra = {}
     if c["routing"] == "zipf":
         extra = dict(zipf_s=c["zipf_s"], zipf_zero=c["zipf_zero"])

@@ -22,6 +22,8 @@ and section:
   block, per row), moe_silu_mul_layer (SwiGLU on [.., 2M] -> [.., M]),
   moe_local_reduction (output is the routing-weighted sum over the k slots),
   bf16_to_fp8_quantize (block-wise quantisation with block size 128).
+* [GC] DeepGEMM issue "GC MoE" (its summary paragraph): routed experts with
+  optional fused shared experts.
 
 Readings of points the pages leave open (each is listed in the design doc):
 
@@ -40,6 +42,11 @@ Readings of points the pages leave open (each is listed in the design doc):
    s = amax / 448, codes = RNE_e4m3fn(clamp(h * (448 / amax), +-448)), and an
    all-zero block gets s = 1 and zero codes.
 10. FP8 is OCP E4M3FN: bias 7, max 448, codes 0x7F/0xFF are NaN, no infinity.
+11. Shared experts ([GC] "optional fused shared experts"; [OCR2] keeps two
+    shared experts beside the routed ones): each of the S shared experts is a
+    SwiGLU expert laid out like a routed one (gate_up [S, 2Fs, H],
+    down [S, H, Fs]) that every token passes through with weight 1; their
+    outputs join the routing-weighted sum, before the residual.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (brute force, closed forms, invariants, library
@@ -124,7 +131,16 @@ def _as_f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights, residual=None):
+def _swiglu_expert(w13_e, w2_e, xt):
+    """One expert on one token: down @ (silu(gate @ x) * (up @ x))."""
+    g = _as_f64(w13_e) @ xt
+    F = g.shape[0] // 2
+    h = silu(g[:F]) * g[F:]
+    return _as_f64(w2_e) @ h
+
+
+def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights, residual=None,
+                          shared_gate_up=None, shared_down=None):
     """Routed-experts layer, one token and one slot at a time, in float64.
 
     hidden [T, H], gate_up [E, 2F, H], down [E, H, F] are the operands' values
@@ -134,7 +150,9 @@ def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights, res
         h   = silu(g[:F]) * g[F:]             (F values)
         y   = down[e] @ h                     (H values)
         out[t] += w[t, j] * y
-    then out += residual [T, H] when one is given ([MPK] moe_local_reduction).
+    then, for every shared expert s (reading 11), out[t] += the same SwiGLU
+    expert of shared_gate_up[s], shared_down[s] with weight 1, and finally
+    out += residual [T, H] when one is given ([MPK] moe_local_reduction).
     """
     x = _as_f64(hidden)
     w13 = np.asarray(gate_up)
@@ -155,13 +173,18 @@ def moe_experts_reference(hidden, gate_up, down, top_k_index, top_k_weights, res
             h = silu(g[:F]) * g[F:]
             y = _as_f64(w2[e]) @ h
             out[t] += wts[t, j] * y
+    if shared_gate_up is not None:
+        sg, sd = np.asarray(shared_gate_up), np.asarray(shared_down)
+        for t in range(T):
+            for s_ in range(sg.shape[0]):
+                out[t] += _swiglu_expert(sg[s_], sd[s_], x[t])
     if residual is not None:
         out += _as_f64(residual)
     return out
 
 
 def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weights,
-                                  residual=None):
+                                  residual=None, shared_gate_up=None, shared_down=None):
     """Same sums as :func:`moe_experts_reference`, grouped by expert.
 
     Each expert's rows are gathered once and multiplied as one float64 matrix
@@ -187,6 +210,12 @@ def moe_experts_reference_batched(hidden, gate_up, down, top_k_index, top_k_weig
         y = h @ _as_f64(w2[e]).T
         contrib = wts[tt, jj][:, None] * y
         np.add.at(out, tt, contrib)
+    if shared_gate_up is not None:
+        sg, sd = np.asarray(shared_gate_up), np.asarray(shared_down)
+        for s_ in range(sg.shape[0]):
+            g = x @ _as_f64(sg[s_]).T
+            Fs = g.shape[1] // 2
+            out += (silu(g[:, :Fs]) * g[:, Fs:]) @ _as_f64(sd[s_]).T
     if residual is not None:
         out += _as_f64(residual)
     return out

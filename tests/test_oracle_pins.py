@@ -409,3 +409,58 @@ def test_fp8_bf16_input_reduces_to_the_fp8_layer():
     got = orc.moe_experts_fp8_bf16_reference(hidden, *w, idx, wts)
     ref = orc.moe_experts_fp8_reference(codes, scale, *w, idx, wts)
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------- shared experts
+
+def test_shared_expert_closed_form(golden):
+    """Reading 11 on H = F = 1: routed silu(2) at weight 0.5 plus a shared
+    expert -6 silu(1) at weight 1 (values derived by hand in the fixture)."""
+    c = golden["shared_expert_h1_f1"]
+    args = [np.array([c["x"]]), np.array(c["gate_up"]), np.array(c["down"]), np.array(c["top_k_index"])]
+    sh = dict(shared_gate_up=np.array(c["shared_gate_up"]), shared_down=np.array(c["shared_down"]))
+    for fn in (orc.moe_experts_reference, orc.moe_experts_reference_batched):
+        out = fn(*args, np.array(c["top_k_weights"]), **sh)
+        assert out[0, 0] == pytest.approx(c["out"][0][0], rel=1e-15)
+        out0 = fn(*args, np.zeros((1, 1)), **sh)
+        assert out0[0, 0] == pytest.approx(c["out_routing_weight_zero"][0][0], rel=1e-15)
+
+
+def test_shared_experts_are_weight_one_slots():
+    """A shared expert is a routed expert that every token selects with weight
+    1: the same layer with the shared experts appended to the routed ones and
+    one extra slot per shared expert gives the same output."""
+    T, H, F, E, k, S = 7, 12, 6, 5, 2, 3
+    x, w13, w2, idx, w = _problem(T, H, F, E, k, seed=21)
+    rng = np.random.default_rng(22)
+    sg = rng.standard_normal((S, 2 * F, H)) * 0.3
+    sd = rng.standard_normal((S, H, F)) * 0.3
+    idx_aug = np.concatenate([idx, np.tile(np.arange(E, E + S, dtype=np.int32), (T, 1))], axis=1)
+    w_aug = np.concatenate([w, np.ones((T, S))], axis=1)
+    ref = _dense_bruteforce(x, np.concatenate([w13, sg]), np.concatenate([w2, sd]), idx_aug, w_aug)
+    for fn in (orc.moe_experts_reference, orc.moe_experts_reference_batched):
+        assert _rel(fn(x, w13, w2, idx, w, shared_gate_up=sg, shared_down=sd), ref) < 1e-12
+
+
+def test_shared_experts_equal_one_wide_expert():
+    """S shared experts of width F equal one shared SwiGLU MLP of width S F
+    whose gate rows, up rows and down columns are the experts' concatenated
+    (SwiGLU is elementwise in F and the down product sums over F)."""
+    T, H, F, E, k, S = 5, 10, 4, 3, 2, 2
+    x, w13, w2, idx, w = _problem(T, H, F, E, k, seed=23)
+    rng = np.random.default_rng(24)
+    sg = rng.standard_normal((S, 2 * F, H)) * 0.3
+    sd = rng.standard_normal((S, H, F)) * 0.3
+    wide_g = np.concatenate([sg[s, :F] for s in range(S)])
+    wide_u = np.concatenate([sg[s, F:] for s in range(S)])
+    wide_gu = np.concatenate([wide_g, wide_u])[None]          # [1, 2 S F, H]
+    wide_d = np.concatenate([sd[s] for s in range(S)], axis=1)[None]  # [1, H, S F]
+    a = orc.moe_experts_reference(x, w13, w2, idx, w, shared_gate_up=sg, shared_down=sd)
+    b = orc.moe_experts_reference(x, w13, w2, idx, w, shared_gate_up=wide_gu, shared_down=wide_d)
+    assert _rel(a, b) < 1e-12
+    # and with no routed contribution it is the dense SwiGLU MLP
+    g = x @ wide_g.T
+    dense = (g * scipy.special.expit(g) * (x @ wide_u.T)) @ wide_d[0].T
+    c = orc.moe_experts_reference_batched(x, w13, w2, idx, np.zeros_like(w),
+                                          shared_gate_up=sg, shared_down=sd)
+    assert _rel(c, dense) < 1e-12
