@@ -23,7 +23,8 @@ committed rocprofv3 counter summary of this workload
 copy kernel), or null when the kernel sources changed since it was taken.
 
 Prints one JSON line.  --config picks another workload (ocr2_decode_t4,
-ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny).
+ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny, and ocr2_prefill_shared /
+ocr2_decode_t1_shared with the model's two shared experts).
 
 Helper modes (no GPU work of their own):
   --copy-calibration        a plain 256 MiB device copy, for counter scaling
@@ -59,6 +60,8 @@ KERNEL_STAGES = [
     ("moe::combine_kernel", "combine"),
     ("moe::gemm_bf16_kernel<", "gemm_bf16"),
     ("moe::gemm_fp8_kernel<", "gemm_fp8"),
+    ("moe::quantize_kernel", "quantize"),
+    ("moe::augment_routing_kernel", "shared_route"),
 ]
 
 
@@ -189,6 +192,8 @@ def stage_work(stage, kind, T, H, F, k, touched, valid):
         return out_bytes + route_bytes, 2 * valid * H
     if stage == "decode_slices":
         return gu_w + dn_w + x_bytes + T * k * 4, 2 * valid * 3 * F * H
+    if stage == "shared_route":
+        return route_bytes, 0
     raise ValueError(stage)
 
 
@@ -255,6 +260,7 @@ def main():
     cfg = dict(wl.CONFIGS[args.config])
     name = args.config
     T, H, F, E, k, kind = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["k"], cfg["kind"]
+    S = cfg.get("S", 0)   # shared experts (every token, weight 1)
     decode = name.startswith("ocr2_decode") or name == "tiny"
     steps = args.steps if args.steps is not None else (200 if decode else (20 if kind == "bf16" else 10))
     warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
@@ -267,7 +273,8 @@ def main():
     routes = []
     if kind == "bf16":
         base = wl.make_config(name, device="cpu")
-        weight_bytes = base["gate_up"].numel() * 2 + base["down"].numel() * 2
+        weight_bytes = sum(base[n].numel() * 2 for n in ("gate_up", "down", "shared_gate_up", "shared_down")
+                           if n in base)
         sets = args.sets or (16 if decode else max(1, min(16, int(np.ceil(2.5e9 / weight_bytes)))))
         gu_sets = [base["gate_up"].to(dev) for _ in range(sets)]
         dn_sets = [base["down"].to(dev) for _ in range(sets)]
@@ -276,12 +283,22 @@ def main():
             g = wl._gen(cfg["seed"] * 1000 + i, "cpu")
             idx, w = wl.route_uniform_softmax(T, E, k, g, "cpu", cfg["routed_scale"])
             routes.append((idx.to(dev), w.to(dev)))
-        entry = moe.moe_experts_decode if decode else moe.moe_experts_prefill
+        if S:   # the shared experts' weights rotate with the routed ones
+            sgu_sets = [base["shared_gate_up"].to(dev) for _ in range(sets)]
+            sdn_sets = [base["shared_down"].to(dev) for _ in range(sets)]
+            entry_sh = moe.moe_experts_decode_shared if decode else moe.moe_experts_prefill_shared
 
-        def step(i):
-            s = i % sets
-            idx, w = routes[i]
-            return entry(hidden, gu_sets[s], dn_sets[s], idx, w, k)
+            def step(i):
+                s = i % sets
+                idx, w = routes[i]
+                return entry_sh(hidden, gu_sets[s], dn_sets[s], sgu_sets[s], sdn_sets[s], idx, w, k)
+        else:
+            entry = moe.moe_experts_decode if decode else moe.moe_experts_prefill
+
+            def step(i):
+                s = i % sets
+                idx, w = routes[i]
+                return entry(hidden, gu_sets[s], dn_sets[s], idx, w, k)
         dtype = "bf16"
     else:
         p = wl.make_config(name, device=dev)
@@ -314,8 +331,8 @@ def main():
     for i in range(steps):
         idx = routes[warmup + i][0].cpu().numpy().reshape(-1)
         valid = idx[(idx >= 0) & (idx < E)]
-        touched_l.append(len(np.unique(valid)))
-        valid_l.append(valid.size)
+        touched_l.append(len(np.unique(valid)) + S)     # shared experts: every token
+        valid_l.append(valid.size + T * S)
     touched, valid = float(np.mean(touched_l)), float(np.mean(valid_l))
     mean_bytes = algorithmic_bytes(kind, T, H, F, k, touched)
     mean_flops = algorithmic_flops(valid, H, F)
@@ -350,7 +367,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded generators; random-init weights of the named shapes)",
         "config": {"workload": name, "T": T, "H": H, "F": F, "E": E, "top_k": k,
-                   "weight_copies_rotated": sets},
+                   "shared_experts": S, "weight_copies_rotated": sets},
     }
     value = T / (ms_per_step * 1e-3)
     out["value"] = round(value, 1)
@@ -399,6 +416,10 @@ def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
         x = problem["hidden"].float().numpy().astype(np.float64)
         w13 = problem["gate_up"].float().numpy().astype(np.float64)
         w2 = problem["down"].float().numpy().astype(np.float64)
+        sh = {}
+        if "shared_gate_up" in problem:
+            sh = dict(shared_gate_up=problem["shared_gate_up"].float().numpy().astype(np.float64),
+                      shared_down=problem["shared_down"].float().numpy().astype(np.float64))
         done_tokens, calls = 0, 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
@@ -406,11 +427,11 @@ def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
             idx = idx.cpu().numpy()
             w = w.cpu().numpy().astype(np.float64)
             if T <= 16:
-                orc.moe_experts_reference(x, w13, w2, idx, w)
+                orc.moe_experts_reference(x, w13, w2, idx, w, **sh)
                 done_tokens += T
             else:   # a bounded sample: the first 64 tokens through the per-token loop
                 n = min(64, T)
-                orc.moe_experts_reference(x[:n], w13, w2, idx[:n], w)
+                orc.moe_experts_reference(x[:n], w13, w2, idx[:n], w[:n], **sh)
                 done_tokens += n
             calls += 1
         el = time.perf_counter() - t0

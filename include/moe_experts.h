@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
     MOE_OK = 0,
@@ -155,6 +155,49 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * bf16 routed experts plus S shared experts fused into the same products
+ * (DeepGEMM issue "GC MoE": routed experts with optional fused shared
+ * experts; the model card "DeepSeek-OCR-2 MoE experts" keeps two shared
+ * experts beside the routed ones).  Every token passes through each shared
+ * expert with weight 1:
+ *   out[t] = sum_j w[t,j] * E_idx[t,j](x[t]) + sum_s S_s(x[t]) (+ residual[t])
+ * where each expert is down @ (silu(gate @ x) * (up @ x)).
+ *   shared_gate_up [S,2F,H] bf16, shared_down [S,H,F] bf16: device, 16-byte
+ *   aligned, the same F and layout as the routed experts; 1 <= S and
+ *   E + S <= MOE_MAX_EXPERTS.  Other operands as moe_experts_prefill.
+ * The call appends one weight-1 slot per shared expert to each token's
+ * routing (in the workspace; routed ids outside [0, E) stay dropped) and runs
+ * the prefill (or decode) sequence over E + S experts and k + S slots; the
+ * shared slots come after the routed ones in the fixed summation order.
+ * ws_bytes: moe_workspace_size_shared.  Errors as moe_experts_prefill, plus
+ * MOE_ERR_NULL / MOE_ERR_ALIGN for the shared weights and MOE_ERR_SHAPE for
+ * S out of range.
+ */
+int moe_experts_prefill_shared(const uint16_t* hidden, const uint16_t* gate_up,
+                               const uint16_t* down, const uint16_t* shared_gate_up,
+                               const uint16_t* shared_down, const int32_t* top_k_index,
+                               const float* top_k_weights, const uint16_t* residual, int64_t T,
+                               int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Decode form of moe_experts_prefill_shared (the gather-GEMV kernels when
+ * T*(k+S) <= 32 and the moe_experts_decode size limits hold, else the
+ * grouped path).  Same operands, workspace rule and errors. */
+int moe_experts_decode_shared(const uint16_t* hidden, const uint16_t* gate_up,
+                              const uint16_t* down, const uint16_t* shared_gate_up,
+                              const uint16_t* shared_down, const int32_t* top_k_index,
+                              const float* top_k_weights, const uint16_t* residual, int64_t T,
+                              int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for the shared-expert entry points: variant
+ * MOE_VARIANT_PREFILL (moe_experts_prefill_shared) or MOE_VARIANT_DECODE
+ * (moe_experts_decode_shared); MOE_ERR_SHAPE otherwise or when the shapes
+ * are out of range. */
+int moe_workspace_size_shared(int variant, int64_t T, int H, int F, int E, int k, int S,
+                              size_t* bytes);
+
+/*
  * FP8 block-scaled routed experts (mirage issue "Supporting MegaKernel for
  * DeepSeek Models": moe_w13_fp8_layer, moe_silu_mul_layer, moe_w2_fp8_layer,
  * moe_local_reduction).
@@ -232,6 +275,7 @@ enum moe_stage {
     MOE_STAGE_COMBINE = 3,       /* router-weighted combine                  */
     MOE_STAGE_DECODE_SLICES = 4, /* decode form: gate_up, SwiGLU and down    */
     MOE_STAGE_QUANTIZE = 5,      /* input-side block-128 fp8 quantisation    */
+    MOE_STAGE_SHARED_ROUTE = 6,  /* routing with the shared experts appended */
 };
 int moe_profile_begin(int max_calls);
 int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);

@@ -50,6 +50,9 @@ def _load():
         "moe_routing_plan": ([vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_experts_prefill": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_decode": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_prefill_shared": ([vp] * 8 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_decode_shared": ([vp] * 8 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_workspace_size_shared": ([i32, i64, i32, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp],
                             i32),
         "moe_experts_fp8_bf16in": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz,
@@ -72,7 +75,8 @@ def exported_symbols():
     return ["moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
-            "moe_profile_end"]
+            "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
+            "moe_workspace_size_shared"]
 
 
 class MoeError(RuntimeError):
@@ -100,6 +104,15 @@ def moe_workspace_size(variant, T, H, F, E, k):
     return n.value
 
 
+def moe_workspace_size_shared(variant, T, H, F, E, k, S):
+    """Workspace bytes of moe_experts_prefill_shared (variant 0) or
+    moe_experts_decode_shared (variant 1)."""
+    n = ctypes.c_size_t(0)
+    _check(_load().moe_workspace_size_shared(variant, T, H, F, E, k, S, ctypes.byref(n)),
+           "moe_workspace_size_shared")
+    return n.value
+
+
 def moe_workspace_layout(variant, T, H, F, E, k):
     """Byte offsets of the workspace stages (counts, offsets, perm, inv, h,
     h scales, y, total); None where a variant has no such stage."""
@@ -112,7 +125,8 @@ def moe_workspace_layout(variant, T, H, F, E, k):
 
 # ------------------------------------------------------------ stage timing
 MOE_PROFILE_MAX_STAGES = 5
-STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices", 5: "quantize"}
+STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices", 5: "quantize",
+               6: "shared_route"}
 
 
 def moe_profile_begin(max_calls):
@@ -243,6 +257,63 @@ def moe_experts_decode(hidden_states, gate_up_proj, down_proj, top_k_index, top_
                       down_proj, top_k_index, top_k_weights, top_k, residual, workspace, out)
 
 
+def _shared_call(entry, variant, hidden_states, gate_up_proj, down_proj, shared_gate_up,
+                 shared_down, top_k_index, top_k_weights, top_k, residual=None, workspace=None,
+                 out=None):
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(gate_up_proj, "gate_up_proj", torch.bfloat16, 3, dev)
+    _need(down_proj, "down_proj", torch.bfloat16, 3, dev)
+    _need(shared_gate_up, "shared_gate_up", torch.bfloat16, 3, dev)
+    _need(shared_down, "shared_down", torch.bfloat16, 3, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = hidden_states.shape
+    E, F2, H2 = gate_up_proj.shape
+    F = F2 // 2
+    S = shared_gate_up.shape[0]
+    k = int(top_k)
+    if H2 != H or F2 != 2 * F or tuple(down_proj.shape) != (E, H, F):
+        raise ValueError("expected gate_up_proj [E,2F,H] and down_proj [E,H,F] matching hidden_states [T,H]")
+    if tuple(shared_gate_up.shape) != (S, 2 * F, H) or tuple(shared_down.shape) != (S, H, F):
+        raise ValueError("expected shared_gate_up [S,2F,H] and shared_down [S,H,F] (the routed F)")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size_shared(variant, T, H, F, E, k, S)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        rc = getattr(_load(), entry)(_ptr(hidden_states), _ptr(gate_up_proj), _ptr(down_proj),
+                                     _ptr(shared_gate_up), _ptr(shared_down), _ptr(top_k_index),
+                                     _ptr(top_k_weights), res, T, H, F, E, k, S, _ptr(out),
+                                     _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, entry)
+    return out
+
+
+def moe_experts_prefill_shared(hidden_states, gate_up_proj, down_proj, shared_gate_up,
+                               shared_down, top_k_index, top_k_weights, top_k, residual=None,
+                               workspace=None, out=None):
+    """Routed experts plus S always-on shared experts (weight 1), grouped
+    form; shared_gate_up [S,2F,H], shared_down [S,H,F] bf16."""
+    return _shared_call("moe_experts_prefill_shared", MOE_VARIANT_PREFILL, hidden_states,
+                        gate_up_proj, down_proj, shared_gate_up, shared_down, top_k_index,
+                        top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_decode_shared(hidden_states, gate_up_proj, down_proj, shared_gate_up,
+                              shared_down, top_k_index, top_k_weights, top_k, residual=None,
+                              workspace=None, out=None):
+    """Decode form of moe_experts_prefill_shared."""
+    return _shared_call("moe_experts_decode_shared", MOE_VARIANT_DECODE, hidden_states,
+                        gate_up_proj, down_proj, shared_gate_up, shared_down, top_k_index,
+                        top_k_weights, top_k, residual, workspace, out)
+
+
 def _codes(t):
     return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 
@@ -348,7 +419,8 @@ __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
     "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "MoeError", "MOE_VARIANT_PREFILL",
+    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_experts_prefill_shared",
+    "moe_experts_decode_shared", "moe_workspace_size_shared", "MoeError", "MOE_VARIANT_PREFILL",
     "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "MOE_VARIANT_FP8_BF16IN",
     "LIB_PATH",
 ]

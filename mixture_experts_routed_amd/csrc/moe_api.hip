@@ -102,7 +102,7 @@ constexpr size_t kNone = (size_t)-1;
 struct Layout {
     size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
            ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, part = kNone,
-           xq = kNone, xs = kNone, total = 0;
+           xq = kNone, xs = kNone, aug_idx = kNone, aug_w = kNone, total = 0;
     bool decode_fast = false;
 };
 
@@ -157,6 +157,17 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     return L;
 }
 
+// Shared experts: the layout of the same variant over E + S experts and
+// k + S slots, followed by the augmented routing [T, k+S] (ids, weights).
+Layout make_shared_layout(int variant, int64_t T, int H, int F, int E, int k, int S) {
+    Layout L = make_layout(variant, T, H, F, E + S, k + S);
+    const size_t n = (size_t)(T * (k + S)) * 4;
+    L.aug_idx = L.total;
+    L.aug_w = align256(L.aug_idx + (n ? n : 1));
+    L.total = align256(L.aug_w + (n ? n : 1));
+    return L;
+}
+
 int check_shape(int variant, int64_t T, int H, int F, int E, int k) {
     if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_FP8_BF16IN) return MOE_ERR_SHAPE;
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_ERR_SHAPE;
@@ -195,15 +206,14 @@ GroupedPlan plan_in(const Layout& L, void* ws, int E) {
 }
 
 // Routing plan into the workspace, then the two grouped bf16 products and the combine.
-int run_grouped_bf16(const Layout& L, const uint16_t* hidden, const uint16_t* gate_up,
-                     const uint16_t* down, const int32_t* idx, const float* w,
-                     const uint16_t* residual, int64_t T, int H, int F, int E, int k,
-                     uint16_t* out, void* ws, hipStream_t s) {
+int run_grouped_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
+                     const ExpertWeights& gate_up, const ExpertWeights& down, const int32_t* idx,
+                     const float* w, const uint16_t* residual, int64_t T, int H, int F, int E,
+                     int k, uint16_t* out, void* ws, hipStream_t s) {
     const int P = (int)(T * k);
     const GroupedPlan pl = plan_in(L, ws, E);
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
-    StageClock clock(s);
     clock.mark(MOE_STAGE_PLAN);
     int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                                   at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
@@ -280,6 +290,55 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
                                    out, stream));
 }
+// The decode launch sequence (gather-GEMV for a few tokens, else the grouped
+// path) over E experts (routed, then shared) and k slots per token.
+int run_decode(StageClock& clock, const Layout& L, const uint16_t* hidden,
+               const ExpertWeights& gate_up, const ExpertWeights& down, const int32_t* idx,
+               const float* w, const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+               uint16_t* out, void* ws, hipStream_t stream) {
+    if (!L.decode_fast)
+        return run_grouped_bf16(clock, L, hidden, gate_up, down, idx, w, residual, T, H, F, E, k,
+                                out, ws, stream);
+    clock.mark(MOE_STAGE_DECODE_SLICES);
+    int rc = launched(launch_decode_slices(hidden, gate_up, down, idx, (int)T, k, E, H, F,
+                                           at<float>(ws, L.part), stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
+    return launched(launch_decode_combine(at<float>(ws, L.part), idx, w, residual, (int)T, k, E, H,
+                                          F, out, stream));
+}
+
+// Both shared-expert entry points: the augmented routing into the workspace,
+// then the plain prefill or decode sequence over E + S experts.
+int run_shared(int variant, const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
+               const uint16_t* shared_gate_up, const uint16_t* shared_down,
+               const int32_t* top_k_index, const float* top_k_weights, const uint16_t* residual,
+               int64_t T, int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+               size_t ws_bytes, hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
+    if (rc) return rc;
+    if (!shared_gate_up || !shared_down) return MOE_ERR_NULL;
+    if (!aligned16(shared_gate_up) || !aligned16(shared_down)) return MOE_ERR_ALIGN;
+    if (S < 1 || S > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if ((rc = check_shape(variant, T, H, F, E + S, k + S))) return rc;
+    const Layout L = make_shared_layout(variant, T, H, F, E, k, S);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    int32_t* idx2 = at<int32_t>(ws, L.aug_idx);
+    float* w2 = at<float>(ws, L.aug_w);
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_SHARED_ROUTE);
+    rc = launched(launch_augment_routing(top_k_index, top_k_weights, T, k, E, S, idx2, w2, stream));
+    if (rc) return rc;
+    const ExpertWeights gu{gate_up, shared_gate_up, E}, dn{down, shared_down, E};
+    if (variant == MOE_VARIANT_PREFILL)
+        return run_grouped_bf16(clock, L, hidden, gu, dn, idx2, w2, residual, T, H, F, E + S,
+                                k + S, out, ws, stream);
+    return run_decode(clock, L, hidden, gu, dn, idx2, w2, residual, T, H, F, E + S, k + S, out, ws,
+                      stream);
+}
 }  // namespace
 }  // namespace moe
 
@@ -351,8 +410,9 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
     int dev;
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
-    return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, residual, T, H,
-                            F, E, k, out, ws, stream);
+    StageClock clock(stream);
+    return run_grouped_bf16(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E),
+                            top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, stream);
 }
 
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
@@ -367,17 +427,43 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
     int dev;
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
-    if (!L.decode_fast)
-        return run_grouped_bf16(L, hidden, gate_up, down, top_k_index, top_k_weights, residual, T,
-                                H, F, E, k, out, ws, stream);
     StageClock clock(stream);
-    clock.mark(MOE_STAGE_DECODE_SLICES);
-    rc = launched(launch_decode_slices(hidden, gate_up, down, top_k_index, (int)T, k, E, H, F,
-                                       at<float>(ws, L.part), stream));
+    return run_decode(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E), top_k_index,
+                      top_k_weights, residual, T, H, F, E, k, out, ws, stream);
+}
+
+int moe_workspace_size_shared(int variant, int64_t T, int H, int F, int E, int k, int S,
+                              size_t* bytes) {
+    if (!bytes) return MOE_ERR_NULL;
+    if ((variant != MOE_VARIANT_PREFILL && variant != MOE_VARIANT_DECODE) || S < 1 ||
+        S > MOE_MAX_EXPERTS)
+        return MOE_ERR_SHAPE;
+    const int rc = check_shape(variant, T, H, F, E + S, k + S);
     if (rc) return rc;
-    clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_decode_combine(at<float>(ws, L.part), top_k_index, top_k_weights,
-                                          residual, (int)T, k, E, H, F, out, stream));
+    *bytes = make_shared_layout(variant, T, H, F, E, k, S).total;
+    return MOE_OK;
+}
+
+int moe_experts_prefill_shared(const uint16_t* hidden, const uint16_t* gate_up,
+                               const uint16_t* down, const uint16_t* shared_gate_up,
+                               const uint16_t* shared_down, const int32_t* top_k_index,
+                               const float* top_k_weights, const uint16_t* residual, int64_t T,
+                               int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    return run_shared(MOE_VARIANT_PREFILL, hidden, gate_up, down, shared_gate_up, shared_down,
+                      top_k_index, top_k_weights, residual, T, H, F, E, k, S, out, ws, ws_bytes,
+                      stream);
+}
+
+int moe_experts_decode_shared(const uint16_t* hidden, const uint16_t* gate_up,
+                              const uint16_t* down, const uint16_t* shared_gate_up,
+                              const uint16_t* shared_down, const int32_t* top_k_index,
+                              const float* top_k_weights, const uint16_t* residual, int64_t T,
+                              int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    return run_shared(MOE_VARIANT_DECODE, hidden, gate_up, down, shared_gate_up, shared_down,
+                      top_k_index, top_k_weights, residual, T, H, F, E, k, S, out, ws, ws_bytes,
+                      stream);
 }
 
 int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,

@@ -93,8 +93,8 @@ __device__ __forceinline__ float transpose_sum(float (&v)[N]) {
 // lane of an H row (H <= 512 NCH), NT = number of tokens.
 template <int S, int NCH, int NT>
 __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
-    const uint16_t* __restrict__ w2, const int32_t* __restrict__ idx, int k, int E, int H,
+    const uint16_t* __restrict__ x, const ExpertWeights w13,
+    const ExpertWeights w2, const int32_t* __restrict__ idx, int k, int E, int H,
     int F, int nslices, float* __restrict__ part) {
     constexpr int kSlice = S;
     constexpr int kRowsPerWave = 2 * S / 8;     // gate/up panel rows per wave
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
     if constexpr (!W2REG) {
         constexpr int RPI = 64 / CPR;
         const int r = lane / CPR, ch = lane % CPR;
-        const uint16_t* src = w2 + ((int64_t)e * H + r) * F + f0 + ch * 8;
+        const uint16_t* src = w2.expert(e, (int64_t)H * F) + (int64_t)r * F + f0 + ch * 8;
         for (int j = wave; j < H / RPI; j += kDecThreads / kWave)
             __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)j * RPI * F),
                                              (lds_void*)&w2s[j * 64], 16, 0, 0);
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
         for (int r = 0; r < RB; ++r) {
             const int p = kRowsPerWave * wave + rb + r;
             const int row = p < kSlice ? f0 + p : F + f0 + (p - kSlice);
-            const uint16_t* src = w13 + ((int64_t)e * 2 * F + row) * H;
+            const uint16_t* src = w13.expert(e, (int64_t)2 * F * H) + (int64_t)row * H;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 const int c = lane + 64 * i;
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
         // after the gate/up rows so that the dot products need not wait for
         // them: rows c = tid / CPR + (512 / CPR) j, chunk tid % CPR
         if constexpr (W2REG) {
-            const uint16_t* src = w2 + ((int64_t)e * H + tid / CPR) * F + f0 + (tid % CPR) * 8;
+            const uint16_t* src = w2.expert(e, (int64_t)H * F) + (int64_t)(tid / CPR) * F + f0 + (tid % CPR) * 8;
 #pragma unroll
             for (int j = 0; j < W2ROWS; ++j) {
                 const int c = tid / CPR + (kDecThreads / CPR) * j;
@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const uint16_t* __restrict__ residual, int T, int k, int E, int H, int nslices,
     uint16_t* __restrict__ out) {
     __shared__ float wsl[kDecodeMaxSlots];
+    __shared__ int vsl[kDecodeMaxSlots];  // 1 for a valid slot
     __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
     const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
     const int c = blockIdx.x * kCombCols + cl;
@@ -290,7 +291,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
         const int sc = min((int)threadIdx.x, P - 1);  // both loads unconditional
         const int e = idx[sc];
         const float wv = wts[sc];
-        wsl[threadIdx.x] = (int)threadIdx.x < P && (unsigned)e < (unsigned)E ? wv : 0.0f;
+        const bool valid = (int)threadIdx.x < P && (unsigned)e < (unsigned)E;
+        wsl[threadIdx.x] = valid ? wv : 0.0f;
+        vsl[threadIdx.x] = valid;
     }
     __syncthreads();
     float acc[kDecodeMaxT] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -309,7 +312,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
         for (int i = 0; i < kCombBatch; ++i) {
             const int pr = min(base + kCombGroups * i, npairs - 1);
             const int s = pr / nslices, t = s / k;
-            const float wv = v[i] * wsl[s];
+            // a dropped slot's partial sums are never written: select, do
+            // not multiply (stale memory may hold NaN)
+            const float wv = vsl[s] ? v[i] * wsl[s] : 0.0f;
 #pragma unroll
             for (int tt = 0; tt < kDecodeMaxT; ++tt)
                 if (tt == t) acc[tt] += wv;
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 }
 
 template <int S, int NCH>
-static void launch_slices(dim3 grid, const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+static void launch_slices(dim3 grid, const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                           const int32_t* idx, int T, int k, int E, int H, int F, int ns, float* part,
                           hipStream_t s) {
     if (NCH * T > kDecodeMaxChunkTokens) return;  // excluded by decode_fast_path
@@ -346,7 +351,7 @@ static void launch_slices(dim3 grid, const uint16_t* x, const uint16_t* w13, con
 }
 
 template <int S>
-static hipError_t launch_width(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
+static hipError_t launch_width(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                                const int32_t* idx, int T, int k, int E, int H, int F, int umax,
                                float* part, hipStream_t s) {
     const int ns = F / S;
@@ -363,9 +368,9 @@ static hipError_t launch_width(const uint16_t* x, const uint16_t* w13, const uin
     return hipGetLastError();
 }
 
-hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
-                                const int32_t* idx, int T, int k, int E, int H, int F, float* part,
-                                hipStream_t s) {
+hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
+                                const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
+                                int H, int F, float* part, hipStream_t s) {
     const DecodeGeometry g = decode_geometry(T, k, E, H, F);
     return g.slice == 16 ? launch_width<16>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s)
                          : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s);

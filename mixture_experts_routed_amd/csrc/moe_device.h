@@ -27,11 +27,9 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
 // ------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even; inputs on this path are finite.
+// Round to nearest even by the gfx950 hardware convert (a NaN stays a NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

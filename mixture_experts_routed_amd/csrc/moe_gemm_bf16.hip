@@ -59,7 +59,7 @@ struct WaveGrid {
 // combine finds a slot's row through the plan's inverse permutation).
 template <int BN, bool SWIGLU>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ A, const ExpertWeights B,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
             const int64_t arow = r < m.mrows ? (SWIGLU ? pr[i] / topk : m.row0 + r) : 0;
             m.a_src[i] = A + arow * K + lds_chunk(r, lslot) * 8;
         }
+        const uint16_t* Be = B.expert(m.e, (int64_t)b_rows * K);
 #pragma unroll
         for (int i = 0; i < B_INST; ++i) {
             const int r = 8 * (B_INST * wave + i) + lrow;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
             } else {
                 brow = m.nt * BN + r;
             }
-            m.b_src[i] = B + ((int64_t)m.e * b_rows + brow) * K + lds_chunk(r, lslot) * 8;
+            m.b_src[i] = Be + (int64_t)brow * K + lds_chunk(r, lslot) * 8;
         }
     };
     // every wave issues the same number of loads per step, also when the
@@ -270,14 +271,14 @@ static int gemm_grid() {
 }
 
 template <int BN, bool SWIGLU>
-static void launch_bf16(const uint16_t* A, const uint16_t* B, const GroupedPlan& pl, int K,
+static void launch_bf16(const uint16_t* A, const ExpertWeights& B, const GroupedPlan& pl, int K,
                         int n_out, int b_rows, int topk, uint16_t* C, hipStream_t s) {
     MOE_LAUNCH((gemm_bf16_kernel<BN, SWIGLU>), dim3(gemm_grid<BN, SWIGLU>()),
                        dim3(kGemmThreads), 0, s, A, B, pl.perm, pl.tiles, pl.ntiles, pl.tile_off,
                        pl.offsets, pl.E, K, n_out, b_rows, topk, C);
 }
 
-hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& pl,
+hipError_t launch_gateup_bf16(const uint16_t* x, const ExpertWeights& w13, const GroupedPlan& pl,
                               int H, int F, int k, uint16_t* h, hipStream_t s) {
     if (F % 128 == 0) launch_bf16<256, true>(x, w13, pl, H, F, 2 * F, k, h, s);
     else launch_bf16<128, true>(x, w13, pl, H, F, 2 * F, k, h, s);
@@ -290,8 +291,8 @@ static double makespan(int64_t items, int G, int BN) {
     return (double)((items + G - 1) / G) * BN / 256.0;
 }
 
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& pl, int P,
-                            int H, int F, uint16_t* y, hipStream_t s) {
+hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const GroupedPlan& pl,
+                            int P, int H, int F, uint16_t* y, hipStream_t s) {
     // The M-tile count is only known on the device; about max(P/256, one
     // tile per touched expert) tiles: pick the panel width whose rounds of the
     // persistent grid finish first (256-wide items leave a mostly idle last

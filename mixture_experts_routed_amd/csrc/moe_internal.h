@@ -43,6 +43,26 @@ hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_
                        int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
                        int32_t* tile_off, int tile_m, hipStream_t s);
 
+// Per-expert weight matrices of `stride` elements: the E routed experts in
+// one tensor, optionally followed by S shared experts in a tensor of their
+// own (expert ids E .. E+S-1, see the shared-expert entry points).  Without
+// shared experts `shared` is unused (n_routed covers every id).
+struct ExpertWeights {
+    const uint16_t* base;
+    const uint16_t* shared;
+    int n_routed;
+    __host__ __device__ const uint16_t* expert(int e, int64_t stride) const {
+        return e < n_routed ? base + (int64_t)e * stride : shared + (int64_t)(e - n_routed) * stride;
+    }
+};
+inline ExpertWeights routed_only(const uint16_t* w, int E) { return ExpertWeights{w, w, E}; }
+
+// Augmented routing for S shared experts: idx2/w2 [T, k+S] hold the routed
+// slots (ids outside [0, E) as -1, i.e. dropped) followed by S slots naming
+// experts E .. E+S-1 with weight 1.
+hipError_t launch_augment_routing(const int32_t* idx, const float* w, int64_t T, int k, int E,
+                                  int S, int32_t* idx2, float* w2, hipStream_t s);
+
 // Grouped-GEMM inputs produced by the plan.
 struct GroupedPlan {
     const int32_t* perm;
@@ -54,12 +74,12 @@ struct GroupedPlan {
 };
 
 // gate_up product with SwiGLU epilogue -> h bf16 [P, F] (expert order).
-hipError_t launch_gateup_bf16(const uint16_t* x, const uint16_t* w13, const GroupedPlan& plan,
+hipError_t launch_gateup_bf16(const uint16_t* x, const ExpertWeights& w13, const GroupedPlan& plan,
                               int H, int F, int k, uint16_t* h, hipStream_t s);
 
 // down product -> y bf16 [P, H] in expert order (row = position in perm).
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* w2, const GroupedPlan& plan, int P,
-                            int H, int F, uint16_t* y, hipStream_t s);
+hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const GroupedPlan& plan,
+                            int P, int H, int F, uint16_t* y, hipStream_t s);
 
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots (fp32, slot order)
 // + residual[t] when residual is not null.
@@ -100,9 +120,9 @@ inline size_t decode_partial_bytes(int64_t T, int k, int E, int H, int F) {
     return (size_t)(T * k) * (size_t)g.nslices * (size_t)H * sizeof(float);
 }
 
-hipError_t launch_decode_slices(const uint16_t* x, const uint16_t* w13, const uint16_t* w2,
-                                const int32_t* idx, int T, int k, int E, int H, int F, float* part,
-                                hipStream_t s);
+hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
+                                const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
+                                int H, int F, float* part, hipStream_t s);
 hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
                                  const uint16_t* residual, int T, int k, int E, int H, int F,
                                  uint16_t* out, hipStream_t s);

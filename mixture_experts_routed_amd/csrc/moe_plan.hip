@@ -165,4 +165,37 @@ hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_
     return hipGetLastError();
 }
 
+// ----------------------------------------------------- shared experts
+// Routing with the S shared experts appended as always-on slots: slot j < k
+// keeps the router's choice (an id outside [0, E) becomes -1, dropped, so it
+// can never name a shared expert), slots k .. k+S-1 name experts E .. E+S-1
+// with weight 1.  One thread per augmented slot.
+__global__ __launch_bounds__(256) void augment_routing_kernel(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ w,
+                                                              int64_t T, int k, int E, int S,
+                                                              int32_t* __restrict__ idx2,
+                                                              float* __restrict__ w2) {
+    const int k2 = k + S;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * k2) return;
+    const int64_t t = i / k2;
+    const int j = (int)(i - t * k2);
+    if (j < k) {
+        const int e = idx[t * k + j];
+        idx2[i] = (unsigned)e < (unsigned)E ? e : -1;
+        w2[i] = w[t * k + j];
+    } else {
+        idx2[i] = E + (j - k);
+        w2[i] = 1.0f;
+    }
+}
+
+hipError_t launch_augment_routing(const int32_t* idx, const float* w, int64_t T, int k, int E,
+                                  int S, int32_t* idx2, float* w2, hipStream_t s) {
+    const int64_t n = T * (k + S);
+    MOE_LAUNCH(augment_routing_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, w,
+               T, k, E, S, idx2, w2);
+    return hipGetLastError();
+}
+
 }  // namespace moe

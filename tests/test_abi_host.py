@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
@@ -191,3 +191,37 @@ def test_profile_recorder_argument_checks():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")
 def test_profile_begin_without_gpu_reports_device_error():
     assert moe._load().moe_profile_begin(8) == EDEV
+
+
+def test_shared_workspace_size_rules():
+    T, H, F, E, k, S = 2048, 1280, 896, 64, 6, 2
+    for variant in (0, 1):
+        n = moe.moe_workspace_size_shared(variant, T, H, F, E, k, S)
+        assert n >= moe.moe_workspace_size(variant, T, H, F, E + S, k + S) + 2 * T * (k + S) * 4
+    for bad in [(2, T, H, F, E, k, S), (0, T, H, F, E, k, 0), (0, T, H, F, 511, k, 2),
+                (0, T, 100, F, E, k, S)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_workspace_size_shared(*bad)
+        assert ei.value.status == ESHAPE
+
+
+@pytest.mark.parametrize("fn", ["moe_experts_prefill_shared", "moe_experts_decode_shared"])
+def test_shared_entry_validation(fn):
+    lib = moe._load()
+
+    def call(**kw):
+        a = dict(hidden=P16, gu=P16, dn=P16, sgu=P16, sdn=P16, idx=P16, w=P16, res=None, T=4,
+                 H=128, F=64, E=8, k=2, S=2, out=P16, ws=P16B, ws_bytes=1 << 30)
+        a.update(kw)
+        return getattr(lib, fn)(a["hidden"], a["gu"], a["dn"], a["sgu"], a["sdn"], a["idx"], a["w"],
+                                a["res"], a["T"], a["H"], a["F"], a["E"], a["k"], a["S"], a["out"],
+                                a["ws"], a["ws_bytes"], None)
+    assert call(sgu=None) == ENULL
+    assert call(sdn=None) == ENULL
+    assert call(hidden=None) == ENULL
+    assert call(sgu=P16 + 2) == EALIGN
+    assert call(sdn=P16 + 8) == EALIGN
+    assert call(S=0) == ESHAPE
+    assert call(E=511) == ESHAPE          # E + S above MOE_MAX_EXPERTS
+    assert call(H=96) == ESHAPE
+    assert call(ws_bytes=16) == EWS

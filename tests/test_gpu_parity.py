@@ -214,6 +214,28 @@ def test_decode_shapes(shape):
     check_tol(run_bf16("moe_experts_decode", to_gpu(p)), ref, BF16_TOL, str(shape))
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_dropped_slots_with_stale_workspace(T):
+    """Dropped slots (-1 and E) on the gather-GEMV path with a workspace whose
+    stale contents are NaN: a dropped slot's partial sums are never written and
+    must not reach the output (no 0 * NaN)."""
+    moe = _moe()
+    H, F, E, k = 256, 128, 8, 3
+    _say(f"decode dropped slots, stale NaN workspace, T={T}")
+    p = bf16_problem(T, H, F, E, k, seed=71, std=1 / np.sqrt(H))
+    idx = p["top_k_index"].clone()
+    idx[:, 0] = -1
+    idx[::2, 1] = E
+    p["top_k_index"] = idx.contiguous()
+    ref = bf16_ref(p, batched=False)
+    g = to_gpu(p)
+    n = moe.moe_workspace_size(1, T, H, F, E, k)
+    ws = torch.full((n // 4,), float("nan"), device="cuda").view(torch.uint8)
+    out = moe.moe_experts_decode(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                                 g["top_k_weights"], k, workspace=ws)
+    check_tol(out, ref, BF16_TOL, f"dropped slots T={T}")
+
+
 def test_stages_prefill():
     """Layered check: h and y (bf16, both in expert order) in the workspace."""
     moe = _moe()
@@ -551,3 +573,78 @@ def test_fp8_bf16in_full_config_sampled():
         p["top_k_index"].cpu().numpy(), p["top_k_weights"].cpu().numpy(), tokens=tokens)
     worst, rel = check_tol(out[tokens], ref[tokens], FP8_TOL, "bf16-in full")
     _say(f"  tokens {tokens}: worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+# ------------------------------------------------------- shared experts
+
+def _shared_problem(T, H, F, E, k, S, seed, std=0.02):
+    p = bf16_problem(T, H, F, E, k, seed, std=std)
+    p.update(wl.make_shared_experts(S, H, F, seed + 500, weight_std=std))
+    return p
+
+
+def _shared_ref(p, w=None, residual=None, batched=True):
+    fn = orc.moe_experts_reference_batched if batched else orc.moe_experts_reference
+    return fn(f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]), p["top_k_index"].numpy(),
+              f64(p["top_k_weights"]) if w is None else w, residual=residual,
+              shared_gate_up=f64(p["shared_gate_up"]), shared_down=f64(p["shared_down"]))
+
+
+def _run_shared(entry, g, w=None, residual=None):
+    return getattr(_moe(), entry)(g["hidden"], g["gate_up"], g["down"], g["shared_gate_up"],
+                                  g["shared_down"], g["top_k_index"],
+                                  g["top_k_weights"] if w is None else w,
+                                  g["top_k_index"].shape[1], residual=residual)
+
+
+@pytest.mark.parametrize("entry,shape", [
+    ("moe_experts_prefill_shared", (300, 256, 128, 6, 2, 2)),
+    ("moe_experts_prefill_shared", (520, 384, 192, 8, 3, 1)),   # 3 M tiles for each shared expert
+    ("moe_experts_decode_shared", (1, 256, 128, 8, 2, 2)),
+    ("moe_experts_decode_shared", (4, 384, 256, 16, 4, 3)),
+    ("moe_experts_decode_shared", (40, 256, 128, 6, 2, 2)),      # grouped path under decode
+])
+def test_shared_experts(entry, shape):
+    """Routed + always-on shared experts (weight 1) against the oracle."""
+    T, H, F, E, k, S = shape
+    _say(f"shared {entry} {shape}")
+    p = _shared_problem(T, H, F, E, k, S, seed=61 + T, std=1 / np.sqrt(H))
+    g = to_gpu(p)
+    worst, rel = check_tol(_run_shared(entry, g), _shared_ref(p), BF16_TOL, f"{entry} {shape}")
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("entry", ["moe_experts_prefill_shared", "moe_experts_decode_shared"])
+def test_shared_experts_dropped_ids_zero_weights_residual(entry):
+    """Routed ids E (one past the last routed expert) and -1 are dropped, never
+    a shared expert; with zero routing weights only the shared experts and the
+    residual remain."""
+    T, H, F, E, k, S = (3, 256, 128, 8, 3, 2) if "decode" in entry else (200, 256, 128, 8, 3, 2)
+    _say(f"shared dropped/zero/residual {entry}")
+    p = _shared_problem(T, H, F, E, k, S, seed=71, std=1 / np.sqrt(H))
+    idx = p["top_k_index"].clone()
+    idx[:, 0] = E
+    idx[::2, 1] = -1
+    p["top_k_index"] = idx.contiguous()
+    g = to_gpu(p)
+    r = torch.randn(T, H, generator=torch.Generator().manual_seed(72)).to(torch.bfloat16)
+    check_tol(_run_shared(entry, g, residual=r.cuda()), _shared_ref(p, residual=f64(r)), BF16_TOL,
+              "dropped + residual")
+    zw = torch.zeros_like(g["top_k_weights"])
+    check_tol(_run_shared(entry, g, w=zw), _shared_ref(p, w=np.zeros((T, k))), BF16_TOL,
+              "zero routing weights")
+
+
+@pytest.mark.parametrize("name", ["ocr2_decode_t1_shared", "ocr2_prefill_shared"])
+def test_shared_full_config(name):
+    """The OCR-2 workloads with their two shared experts; sampled tokens for
+    the prefill, every token for the decode."""
+    _say(f"shared full {name}")
+    p = wl.make_config(name)
+    g = to_gpu(p)
+    entry = "moe_experts_decode_shared" if "decode" in name else "moe_experts_prefill_shared"
+    out = _run_shared(entry, g)
+    T = p["hidden"].shape[0]
+    tokens = list(range(T)) if T <= 4 else sorted(set(_sample_tokens(T, 6, 9)))
+    sub = {n: (v[tokens] if n in ("hidden", "top_k_index", "top_k_weights") else v) for n, v in p.items()}
+    check_tol(out[tokens], _shared_ref(sub, batched=False), BF16_TOL, name)
