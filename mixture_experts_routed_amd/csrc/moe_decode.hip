@@ -266,14 +266,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
 // added in group order, so the result does not depend on timing.  Loads go
 // out in batches of 16 with no dependences between them; dropped slots have
 // weight zero (no branch in the loop).
-constexpr int kCombCols = 16, kCombGroups = 16, kCombBatch = 16;  // many small workgroups: latency-bound
+// The batch B of loads a thread has in flight is 16, or 64 when there are
+// more than 16 x 16 pairs, so that up to 1024 pairs take one round trip.
+constexpr int kCombCols = 16, kCombGroups = 16;  // many small workgroups: latency-bound
 constexpr int kCombThreads = kCombCols * kCombGroups;
+template <int kCombBatch>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
     const uint16_t* __restrict__ residual, int T, int k, int E, int H, int nslices,
     uint16_t* __restrict__ out) {
-    __shared__ float wsl[kDecodeMaxSlots];
-    __shared__ int vsl[kDecodeMaxSlots];  // 1 for a valid slot
+    // per slot: the routing weight's bits (0 for a dropped slot) and a mask
+    // that is all ones for a valid slot, zero for a dropped one
+    __shared__ int2 wsl[kDecodeMaxSlots];
     __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
     const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
     const int c = blockIdx.x * kCombCols + cl;
@@ -292,8 +296,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
         const int e = idx[sc];
         const float wv = wts[sc];
         const bool valid = (int)threadIdx.x < P && (unsigned)e < (unsigned)E;
-        wsl[threadIdx.x] = valid ? wv : 0.0f;
-        vsl[threadIdx.x] = valid;
+        wsl[threadIdx.x] = make_int2(valid ? __float_as_int(wv) : 0, valid ? -1 : 0);
     }
     __syncthreads();
     float acc[kDecodeMaxT] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -312,9 +315,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
         for (int i = 0; i < kCombBatch; ++i) {
             const int pr = min(base + kCombGroups * i, npairs - 1);
             const int s = pr / nslices, t = s / k;
-            // a dropped slot's partial sums are never written: select, do
-            // not multiply (stale memory may hold NaN)
-            const float wv = vsl[s] ? v[i] * wsl[s] : 0.0f;
+            // a dropped slot's partial sums are never written: masked out,
+            // not multiplied by zero (stale memory may hold NaN)
+            const int2 ws = wsl[s];
+            const float wv = __int_as_float(__float_as_int(v[i] * __int_as_float(ws.x)) & ws.y);
 #pragma unroll
             for (int tt = 0; tt < kDecodeMaxT; ++tt)
                 if (tt == t) acc[tt] += wv;
@@ -380,8 +384,12 @@ hipError_t launch_decode_combine(const float* part, const int32_t* idx, const fl
                                  const uint16_t* residual, int T, int k, int E, int H, int F,
                                  uint16_t* out, hipStream_t s) {
     const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    MOE_LAUNCH(decode_combine_kernel, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0, s, part,
-                       idx, w, residual, T, k, E, H, g.nslices, out);
+    if (T * k * g.nslices > kCombGroups * 16)
+        MOE_LAUNCH(decode_combine_kernel<64>, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0,
+                   s, part, idx, w, residual, T, k, E, H, g.nslices, out);
+    else
+        MOE_LAUNCH(decode_combine_kernel<16>, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0,
+                   s, part, idx, w, residual, T, k, E, H, g.nslices, out);
     return hipGetLastError();
 }
 
