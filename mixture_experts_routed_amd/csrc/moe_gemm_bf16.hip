@@ -224,10 +224,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 
     int it = xcd_slot(blockIdx.x, gridDim.x);
     if (it >= items) return;
-    Item cur;
+    Item cur, nxt;
     setup(it, cur);
     prologue(cur);
     while (true) {
+        // The next item's row pointers are worked out while this item's first
+        // stages load (their slot-id loads then cost no wait of their own).
+        const int next = it + gridDim.x;
+        const bool more = next < items;
+        setup(more ? next : it, nxt);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -248,10 +253,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 
         // The next item's first stages load while this tile is stored (on the
         // last item the same tile is fetched again and never read).
-        const int next = it + gridDim.x;
-        const bool more = next < items;
-        Item nxt;
-        setup(more ? next : it, nxt);
         prologue(nxt);
         epilogue(cur);
         if (!more) break;
