@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         }                                                                                      \
         if (sa_ok) sa_lds[S][tid] = RSA;                                                       \
         if (sb_ok) sb_lds[S][tid] = RSB;                                                       \
-        __syncthreads();                                                                       \
+        lds_barrier(); /* LDS only: the next steps' loads stay in flight */                    \
         if (active && (KB) < nkb) {                                                            \
             const int ar = 32 * wm + (lane & 31);                                              \
             const i32x8 a0 = __builtin_bit_cast(i32x8, __builtin_shufflevector(                \
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                 m = half_max32(m);
                 if ((lane & 31) == 0) amax_lds[wn][32 * wm + acc_row(q, lane)] = m;
             }
-            __syncthreads();
+            lds_barrier();
             if (active) {
                 const int nfb = n_out / 128;
 #pragma unroll
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                 }
             }
         }
-        __syncthreads();  // LDS (operand rings, amax) is reused by the next item
+        lds_barrier();  // LDS (operand rings, amax) is reused by the next item
     }
 }
 
