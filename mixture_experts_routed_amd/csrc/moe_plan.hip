@@ -19,20 +19,27 @@ constexpr int kPlanRegs = 32;  // slots per lane loaded together (one round trip
 // order (wave, position in run) is the slot order.  Pass 1 counts per
 // (wave, expert) with LDS integer atomics (exact, order-free).  Each expert's
 // per-wave counts then become running bases, and pass 2 walks the slots again
-// in order: lanes with the same expert in one 64-slot step find each other
-// with ballots on the id bits and take consecutive positions by lane rank.
+// in order: lanes with the same expert in one 64-slot step find each other by
+// OR-ing their lane bits into a per-(wave, expert) LDS mask (order-free, so
+// deterministic) and take consecutive positions by lane rank.  (A ballot per
+// id bit costs about 7 vector instructions per bit and step, which on one CU
+// shared by 16 waves made this pass the kernel's main cost.)
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t* __restrict__ idx, int P, int E, int nbits, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int P, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles, int32_t* __restrict__ tile_off,
     int tile_m) {
     __shared__ int base[kPlanWaves][MOE_MAX_EXPERTS];
+    __shared__ unsigned long long lanes_of[kPlanWaves][MOE_MAX_EXPERTS];  // pass 2, zero between steps
     __shared__ int tot[MOE_MAX_EXPERTS];
     __shared__ int off_sh[MOE_MAX_EXPERTS + 1];
     __shared__ int tile_sh[MOE_MAX_EXPERTS + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < kPlanWaves * MOE_MAX_EXPERTS; i += kPlanThreads) (&base[0][0])[i] = 0;
+    for (int i = tid; i < kPlanWaves * MOE_MAX_EXPERTS; i += kPlanThreads) {
+        (&base[0][0])[i] = 0;
+        (&lanes_of[0][0])[i] = 0ull;
+    }
     __syncthreads();
 
     const int run = ((P + kPlanWaves * kWave - 1) / (kPlanWaves * kWave)) * kWave;
@@ -132,12 +139,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             const int s = cb + kWave * i + lane;
             const int e = ev[i];
             const bool valid = (unsigned)e < (unsigned)E;
-            uint64_t same = __ballot(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = (e >> b) & 1;
-                const uint64_t set = __ballot(bit);
-                same &= bit ? set : ~set;
-            }
+            // the lanes of this step that hold expert e (LDS operations of
+            // one wave complete in issue order: the ORs land before the read,
+            // the read before the clear)
+            if (valid) atomicOr(&lanes_of[wave][e], 1ull << lane);
+            __builtin_amdgcn_wave_barrier();
+            const uint64_t same = valid ? lanes_of[wave][e] : 0ull;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) lanes_of[wave][e] = 0ull;
             int rank = 0, pos = -1;
             if (valid) {
                 rank = __popcll(same & ((1ull << lane) - 1ull));
@@ -158,9 +167,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
                        int32_t* tile_off, int tile_m, hipStream_t s) {
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    MOE_LAUNCH(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, nbits, counts,
+    MOE_LAUNCH(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, idx, P, E, counts,
                        offsets, perm, inv, tiles, ntiles, tile_off, tile_m);
     return hipGetLastError();
 }
