@@ -19,6 +19,9 @@ Models", Layer Tensor Details for moe_w13_fp8_layer / moe_w2_fp8_layer):
 * ``ocr2_prefill_shared``, ``ocr2_decode_t1_shared``: the OCR-2 workloads
   plus the model's two shared experts (same F as a routed expert), which
   every token passes through with weight 1
+* ``v3_mxfp4_decode`` / ``v3_mxfp4_prefill``: the V3 expert-share shapes with
+  MXFP4 routed weights (E2M1 + E8M0 per 32) and MXFP8 activations (E4M3 +
+  E8M0 per 32), decode-batch (T=128) and Zipf prefill (T=4096) routing
 """
 
 from __future__ import annotations
@@ -46,6 +49,11 @@ CONFIGS = {
     "ocr2_decode_t1_shared": dict(T=1, H=1280, F=896, E=64, k=6, kind="bf16", seed=1002,
                                   routing="uniform_softmax", routed_scale=1.0, S=2,
                                   shared_seed=1006),
+    "v3_mxfp4_decode": dict(T=128, H=7168, F=2048, E=128, k=8, kind="mxfp4", seed=1007,
+                            routing="sigmoid_topk", routed_scale=2.5),
+    "v3_mxfp4_prefill": dict(T=4096, H=7168, F=2048, E=128, k=8, kind="mxfp4", seed=1007,
+                             act_seed=1005, routing="zipf", zipf_s=1.2, zipf_zero=8,
+                             routed_scale=2.5),
 }
 
 
@@ -191,6 +199,109 @@ def make_fp8_problem(T, H, F, E, k, seed, device="cpu", act_seed=None, **kw):
     return p
 
 
+# -------------------------------------------- microscaling (MX) operands
+
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _mx_exponents(b, emax):
+    """Shared exponent per block of the last dim: floor(log2(amax)) - emax,
+    clamped to [-127, 127]; an all-zero block gets -127."""
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    e = (ex.to(torch.int32) - 1) - emax
+    e = torch.where(amax > 0, e, torch.full_like(e, -127))
+    return e.clamp(-127, 127)
+
+
+def quantize_mxfp8_rows_torch(t):
+    """fp32 [.., K] -> (E4M3 codes uint8 [.., K], E8M0 scale bytes uint8 [.., K/32]).
+
+    Input recipe (OCP Microscaling MXFP8): per 32-wide block, e =
+    floor(log2(amax)) - 8, codes = torch's e4m3fn cast of t / 2^e clamped to
+    +-448, scale byte e + 127.
+    """
+    K = t.shape[-1]
+    assert K % 32 == 0
+    b = t.float().reshape(*t.shape[:-1], K // 32, 32)
+    e = _mx_exponents(b, 8)
+    v = torch.ldexp(b, (-e).to(torch.float32)[..., None]).clamp(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(t.shape)
+    return codes.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
+def quantize_mxfp4_rows_torch(t):
+    """fp32 [.., K] -> (E2M1 codes packed two per byte uint8 [.., K/2], element
+    2i in the low nibble; E8M0 scale bytes uint8 [.., K/32]).
+
+    Input recipe (OCP Microscaling MXFP4): per 32-wide block, e =
+    floor(log2(amax)) - 2, values t / 2^e clamped to +-6 and rounded to the
+    nearest E2M1 value, ties to the even code (mantissa bit 0).
+    """
+    K = t.shape[-1]
+    assert K % 32 == 0
+    b = t.float().reshape(*t.shape[:-1], K // 32, 32)
+    e = _mx_exponents(b, 2)
+    v = torch.ldexp(b, (-e).to(torch.float32)[..., None]).clamp(-6.0, 6.0)
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float32, device=t.device)
+    d = (v.abs()[..., None] - grid).abs()                       # [.., 8]
+    is_min = d == d.amin(dim=-1, keepdim=True)
+    even = (torch.arange(8, device=t.device) % 2) == 0
+    even_min = is_min & even
+    pick = torch.where(even_min.any(dim=-1), even_min.to(torch.uint8).argmax(dim=-1),
+                       is_min.to(torch.uint8).argmax(dim=-1))
+    codes = (pick | (torch.signbit(v).to(torch.int64) << 3)).to(torch.uint8).reshape(t.shape)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
+def make_mxfp4_weights(H, F, E, seed, device="cpu", weight_std=0.02):
+    """MXFP4 weights: per expert N(0, std) draws quantised per (row, 32 K block).
+
+    gate_up [E,2F,H/2] packed + scales [E,2F,H/32]; down [E,H,F/2] + [E,H,F/32].
+    """
+    g = _gen(seed, device)
+    w13 = torch.empty(E, 2 * F, H // 2, dtype=torch.uint8, device=device)
+    w13s = torch.empty(E, 2 * F, H // 32, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, F // 2, dtype=torch.uint8, device=device)
+    w2s = torch.empty(E, H, F // 32, dtype=torch.uint8, device=device)
+    for e in range(E):
+        c, s_ = quantize_mxfp4_rows_torch(torch.randn(2 * F, H, generator=g, device=device) * weight_std)
+        w13[e].copy_(c)
+        w13s[e].copy_(s_)
+    for e in range(E):
+        c, s_ = quantize_mxfp4_rows_torch(torch.randn(H, F, generator=g, device=device) * weight_std)
+        w2[e].copy_(c)
+        w2s[e].copy_(s_)
+    return dict(gate_up=w13, gate_up_scale=w13s, down=w2, down_scale=w2s)
+
+
+def make_mxfp8_activations(T, H, E, k, seed, device="cpu", routing="sigmoid_topk",
+                           routed_scale=2.5, zipf_s=1.2, zipf_zero=8):
+    """MXFP8 hidden states (N(0,1) quantised per token and 32 block) + routing."""
+    g = _gen(seed, device)
+    x = torch.randn(T, H, generator=g, device=device)
+    xq, xs = quantize_mxfp8_rows_torch(x)
+    if routing == "sigmoid_topk":
+        idx, w = route_sigmoid_topk(T, E, k, g, device, routed_scale)
+    elif routing == "zipf":
+        idx, w = route_zipf(T, E, k, g, device, zipf_s, zipf_zero, routed_scale)
+    elif routing == "uniform_softmax":
+        idx, w = route_uniform_softmax(T, E, k, g, device, routed_scale)
+    else:
+        raise ValueError(routing)
+    return dict(x=xq, x_scale=xs, top_k_index=idx, top_k_weights=w)
+
+
+def make_mxfp4_problem(T, H, F, E, k, seed, device="cpu", act_seed=None, **kw):
+    """MXFP4 weights from ``seed``, MXFP8 activations and routing from
+    ``act_seed`` (or the seed + 1)."""
+    p = make_mxfp4_weights(H, F, E, seed, device)
+    p.update(make_mxfp8_activations(T, H, E, k, act_seed if act_seed is not None else seed + 1,
+                                    device, **kw))
+    return p
+
+
 def make_shared_experts(S, H, F, seed, device="cpu", weight_std=0.02):
     """Shared-expert weights, drawn like routed ones: shared_gate_up [S,2F,H]
     and shared_down [S,H,F], bf16 N(0, std), gate_up first."""
@@ -212,6 +323,10 @@ def make_config(name, device="cpu"):
     extra = {}
     if c["routing"] == "zipf":
         extra = dict(zipf_s=c["zipf_s"], zipf_zero=c["zipf_zero"])
+    if c["kind"] == "mxfp4":
+        return make_mxfp4_problem(c["T"], c["H"], c["F"], c["E"], c["k"], c["seed"], device,
+                                  act_seed=c.get("act_seed"), routing=c["routing"],
+                                  routed_scale=c["routed_scale"], **extra)
     return make_fp8_problem(c["T"], c["H"], c["F"], c["E"], c["k"], c["seed"], device,
                             act_seed=c.get("act_seed"), routing=c["routing"],
                             routed_scale=c["routed_scale"], **extra)

@@ -23,7 +23,8 @@ and section:
   moe_local_reduction (output is the routing-weighted sum over the k slots),
   bf16_to_fp8_quantize (block-wise quantisation with block size 128).
 * [GC] DeepGEMM issue "GC MoE" (its summary paragraph): routed experts with
-  optional fused shared experts.
+  optional fused shared experts; FP8 activations with packed FP4 routed
+  weights.
 
 Readings of points the pages leave open (each is listed in the design doc):
 
@@ -47,6 +48,19 @@ Readings of points the pages leave open (each is listed in the design doc):
     SwiGLU expert laid out like a routed one (gate_up [S, 2Fs, H],
     down [S, H, Fs]) that every token passes through with weight 1; their
     outputs join the routing-weighted sum, before the residual.
+12. MXFP4 routed weights ([GC] "packed FP4 routed weights" with FP8
+    activations; DeepGEMM's FP8 x FP4 and "MXF4" kind; [MPK] ue8m0 scales per
+    32 elements for FP8 GEMM inputs), read as the OCP Microscaling formats:
+    E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit; values
+    0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with element 2i in the low
+    nibble, and one E8M0 scale 2^(s-127) (s = 255 NaN) per 32 consecutive K
+    elements of a row.
+13. FP8 activations of that layer, and its re-quantised SwiGLU output, are
+    MXFP8: E4M3 elements with one E8M0 scale per 32 elements, the shared
+    exponent floor(log2(amax)) - 8 (8 = the largest E4M3 exponent), elements
+    x / 2^e clamped to +-448 and rounded to nearest even; an all-zero block
+    gets s = 0 (2^-127) and zero codes.  The same rule with emax 2 and the
+    E2M1 maximum 6 quantises weights to MXFP4.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (brute force, closed forms, invariants, library
@@ -67,6 +81,13 @@ __all__ = [
     "quantize_block128_fp32",
     "dequantize_block128",
     "moe_experts_fp8_reference",
+    "e2m1_decode",
+    "e2m1_encode",
+    "unpack_e2m1",
+    "e8m0_decode",
+    "quantize_mxfp8_fp32",
+    "dequantize_mx",
+    "moe_experts_mxfp4_reference",
 ]
 
 # --------------------------------------------------------------------------
@@ -373,3 +394,145 @@ def moe_experts_fp8_bf16_reference(hidden, w13_codes, w13_scale, w2_codes, w2_sc
     xq, xs = quantize_block128_fp32(np.asarray(hidden, dtype=np.float32))
     return moe_experts_fp8_reference(xq, xs, w13_codes, w13_scale, w2_codes, w2_scale,
                                      top_k_index, top_k_weights, tokens=tokens, residual=residual)
+
+
+# --------------------------------------------------------------------------
+# Microscaling formats (readings 12-13): E2M1 and E4M3 elements, E8M0 scales
+# per 32 elements
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes):
+    """Value of each 4-bit E2M1 code (0..15) as float64: sign bit 3, exponent
+    bits 2..1 (bias 1), mantissa bit 0; exponent 0 is 0.5 * m (subnormal),
+    otherwise 2^(e-1) * (1 + m/2).  No NaN or infinity."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 1).astype(np.float64)
+    v = np.where(e == 0, 0.5 * m, np.exp2(e.astype(np.float64) - 1.0) * (1.0 + 0.5 * m))
+    return sign * v
+
+
+def e2m1_encode(v):
+    """Round-to-nearest-even E2M1 codes of finite values with |v| <= 6.
+
+    The representable magnitudes are the multiples of 0.5 up to 2 (exponents
+    0 and 1), of 1 up to 4 (exponent 2) and of 2 up to 6 (exponent 3); a tie
+    goes to the neighbour whose mantissa bit is 0.
+    """
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    if np.any(~np.isfinite(a)) or np.any(a > E2M1_MAX):
+        raise ValueError("e2m1_encode expects finite values within +-6")
+    neg = np.signbit(np.asarray(v, dtype=np.float64))
+    # step of the binade the value falls in: 0.5 below 2, 1 below 4, 2 above
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    q = np.rint(a / step) * step                     # half-to-even on the step grid
+    # rint's "even" is even in units of the step, i.e. mantissa bit 0, except
+    # at the binade tops 2 and 4 (reached from below), which are exact codes
+    mag = np.minimum(q, E2M1_MAX)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    code = np.searchsorted(grid, mag)
+    if not np.all(grid[code] == mag):
+        raise AssertionError("E2M1 rounding left the grid")
+    return (code | np.where(neg, 8, 0)).astype(np.uint8)
+
+
+def unpack_e2m1(packed):
+    """Bytes [..., K/2] -> 4-bit codes [..., K]; element 2i is the low nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def e8m0_decode(s):
+    """2^(s - 127) as float64; s = 255 is NaN."""
+    s = np.asarray(s).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2(s.astype(np.float64) - 127.0))
+
+
+def _mx_shared_exponent(amax, emax_elem):
+    """floor(log2(amax)) - emax_elem, clamped to [-127, 127]; amax 0 gives -127.
+    amax is a float32 array; frexp gives amax = m * 2^E with m in [0.5, 1), so
+    floor(log2(amax)) = E - 1 exactly."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, E = np.frexp(np.where(a > 0, a, 1.0))
+    e = (E - 1) - emax_elem
+    e = np.where(a > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_mxfp8_fp32(h):
+    """MXFP8 quantisation of the rows of ``h`` (reading 13), in float32:
+    per 32-column block, e = floor(log2(max|h|)) - 8, codes =
+    RNE_e4m3(clamp(h / 2^e, +-448)), scale byte e + 127; a zero block gets
+    byte 0 and zero codes.  Returns (codes uint8 [.., K], scales uint8 [.., K/32])."""
+    hb = np.asarray(h, dtype=np.float32)
+    K = hb.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("last dimension must be a multiple of 32")
+    blocks = hb.reshape(hb.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blocks), axis=-1)
+    e = _mx_shared_exponent(amax, 8)
+    # division by a power of two: exact in float64, then held in float32
+    v = (blocks.astype(np.float64) / np.exp2(e.astype(np.float64))[..., None]).astype(np.float32)
+    v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    codes = e4m3fn_encode(v).reshape(hb.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def dequantize_mx(values, scales):
+    """Element values times 2^(s-127) of their 32-element block, float64."""
+    vals = np.asarray(values, dtype=np.float64)
+    K = vals.shape[-1]
+    s = np.repeat(e8m0_decode(scales), MX_BLOCK, axis=-1)[..., :K]
+    return vals * s
+
+
+def moe_experts_mxfp4_reference(x_codes, x_scale, w13_packed, w13_scale, w2_packed, w2_scale,
+                                top_k_index, top_k_weights, tokens=None, residual=None):
+    """Routed-experts layer with MXFP4 weights and MXFP8 activations, float64,
+    with the method's fp32 MXFP8 re-quantisation of h (readings 12-13).
+
+    Operands: x_codes [T, H] E4M3 + x_scale [T, H/32] E8M0; w13_packed
+    [E, 2F, H/2] E2M1 pairs + w13_scale [E, 2F, H/32]; w2_packed [E, H, F/2] +
+    w2_scale [E, H, F/32].  Per slot (t, j) with valid expert e:
+        g = W13[e] @ x[t];  h = silu(g[:F]) * g[F:]
+        (q, s) = quantize_mxfp8_fp32(float32(h));  h~ = e4m3(q) * 2^(s-127)
+        y = W2[e] @ h~;  out[t] += w[t, j] * y
+    then + residual.  ``tokens`` restricts the rows computed (others zero).
+    """
+    xq = np.asarray(x_codes)
+    T, H = xq.shape
+    idx = np.asarray(top_k_index)
+    wts = np.asarray(top_k_weights, dtype=np.float64)
+    E = w13_packed.shape[0]
+    F = w13_packed.shape[1] // 2
+    want = np.zeros(T, dtype=bool)
+    if tokens is None:
+        want[:] = True
+    else:
+        want[np.asarray(tokens)] = True
+    x = dequantize_mx(e4m3fn_decode(xq), x_scale)
+    out = np.zeros((T, H), dtype=np.float64)
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & want[:, None])
+        if tt.size == 0:
+            continue
+        W13 = dequantize_mx(e2m1_decode(unpack_e2m1(w13_packed[e])), np.asarray(w13_scale[e]))
+        W2 = dequantize_mx(e2m1_decode(unpack_e2m1(w2_packed[e])), np.asarray(w2_scale[e]))
+        for t, j in zip(tt.tolist(), jj.tolist()):
+            g = W13 @ x[t]
+            h = silu(g[:F]) * g[F:]
+            q, sc = quantize_mxfp8_fp32(h.astype(np.float32))
+            ht = dequantize_mx(e4m3fn_decode(q), sc)
+            y = W2 @ ht
+            out[t] += wts[t, j] * y
+    if residual is not None:
+        out[want] += np.asarray(residual, dtype=np.float64)[want]
+    return out

@@ -464,3 +464,117 @@ def test_shared_experts_equal_one_wide_expert():
     c = orc.moe_experts_reference_batched(x, w13, w2, idx, np.zeros_like(w),
                                           shared_gate_up=sg, shared_down=sd)
     assert _rel(c, dense) < 1e-12
+
+
+# ------------------------------------------------------- MX formats, MXFP4 layer
+
+def test_e2m1_decode_golden(golden):
+    c = golden["e2m1_codes"]
+    got = orc.e2m1_decode(np.array(c["codes"]))
+    assert np.array_equal(got, np.array(c["values"])) and np.array_equal(np.signbit(got), np.signbit(c["values"]))
+
+
+def test_e2m1_encode_ties_roundtrip_and_recipe(golden):
+    c = golden["e2m1_rne_ties"]
+    assert orc.e2m1_encode(np.array(c["inputs"])).tolist() == c["codes"]
+    codes = np.arange(16, dtype=np.uint8)
+    back = orc.e2m1_encode(orc.e2m1_decode(codes))
+    assert np.array_equal(orc.e2m1_decode(back), orc.e2m1_decode(codes))
+    # against the input recipe's independent torch encoder on a dense sweep
+    v = np.linspace(-6.0, 6.0, 24001).astype(np.float32)[None, :24000 // 32 * 32]
+    v = v.reshape(-1, 32)
+    v[:, 0] = 6.0                                        # unit block scale (amax 6 -> e = 0)
+    packed, sc = wl.quantize_mxfp4_rows_torch(torch.from_numpy(v))
+    assert np.all(sc.numpy() == 127)
+    assert np.array_equal(orc.e2m1_decode(orc.unpack_e2m1(packed.numpy())),
+                          orc.e2m1_decode(orc.e2m1_encode(v)))
+
+
+def test_e8m0_decode_golden(golden):
+    c = golden["e8m0_scales"]
+    assert np.array_equal(orc.e8m0_decode(np.array(c["bytes"])), np.array(c["values"]))
+    assert np.isnan(orc.e8m0_decode(255))
+
+
+def test_mxfp8_block_golden_recipe_and_bound(golden):
+    c = golden["mxfp8_block"]
+    h = np.zeros((1, 32), np.float32)
+    h[0, :4] = c["h_first4"]
+    q, s = orc.quantize_mxfp8_fp32(h)
+    assert q[0, :4].tolist() == c["codes_first4"] and np.all(q[0, 4:] == 0) and s[0, 0] == c["scale_byte"]
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((40, 256)) * np.exp(rng.uniform(-12, 12, (40, 1)))).astype(np.float32)
+    x[3, 32:64] = 0.0                                    # an all-zero block
+    q, s = orc.quantize_mxfp8_fp32(x)
+    qt, st = wl.quantize_mxfp8_rows_torch(torch.from_numpy(x))
+    assert np.array_equal(q, qt.numpy()) and np.array_equal(s, st.numpy())
+    assert s[3, 1] == 0 and np.all(q[3, 32:64] == 0)
+    deq = orc.dequantize_mx(orc.e4m3fn_decode(q), s)
+    scale = np.repeat(orc.e8m0_decode(s), 32, axis=-1)
+    # E4M3 keeps 3 mantissa bits: half an ulp is 2^-4 of the value in the normal
+    # range, 2^-10 of the scale in the subnormal range; values above 448 units saturate
+    unit = np.abs(x) / scale
+    bound = np.where(unit >= 2.0 ** -6, np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10)
+    ok = unit <= 448
+    assert np.all(np.abs(deq - x)[ok] <= bound[ok] * (1 + 1e-12))
+    assert np.all(np.abs(deq[~ok]) == 448 * scale[~ok])
+
+
+def _mxfp4_bruteforce(p):
+    """Dense evaluation from the operands' definitions, written apart from the
+    oracle: an E2M1 value table, torch's e4m3 decode, power-of-two scales, and
+    the input recipe's MXFP8 quantiser for the intermediate."""
+    table = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=torch.float64)
+
+    def fp4(packed, sc):
+        lo, hi = (packed & 0xF).long(), (packed >> 4).long()
+        codes = torch.stack([lo, hi], dim=-1).reshape(*packed.shape[:-1], -1)
+        v = table[codes & 7] * torch.where((codes & 8) > 0, -1.0, 1.0).double()
+        return v * torch.pow(2.0, sc.double() - 127).repeat_interleave(32, dim=-1)
+
+    def fp8(c, sc):
+        return c.view(torch.float8_e4m3fn).double() * torch.pow(2.0, sc.double() - 127).repeat_interleave(32, dim=-1)
+
+    x = fp8(p["x"], p["x_scale"])
+    W13 = fp4(p["gate_up"], p["gate_up_scale"])
+    W2 = fp4(p["down"], p["down_scale"])
+    idx, w = p["top_k_index"].long(), p["top_k_weights"].double()
+    T, H = x.shape
+    E, F2, _ = W13.shape
+    F = F2 // 2
+    out = torch.zeros(T, H, dtype=torch.float64)
+    for t in range(T):
+        for e in range(E):
+            g = W13[e] @ x[t]
+            h = torch.nn.functional.silu(g[:F]) * g[F:]
+            q, s = wl.quantize_mxfp8_rows_torch(h.float()[None])
+            y = W2[e] @ fp8(q, s)[0]
+            m = sum(float(w[t, j]) for j in range(idx.shape[1]) if int(idx[t, j]) == e)
+            out[t] += m * y
+    return out.numpy()
+
+
+def _mx_args(p):
+    return [p[n].numpy() for n in ("x", "x_scale", "gate_up", "gate_up_scale", "down", "down_scale")]
+
+
+def test_mxfp4_oracle_vs_bruteforce():
+    p = wl.make_mxfp4_problem(6, 128, 64, 5, 3, seed=31, routing="uniform_softmax", routed_scale=1.0)
+    ref = _mxfp4_bruteforce(p)
+    got = orc.moe_experts_mxfp4_reference(*_mx_args(p), p["top_k_index"].numpy(), p["top_k_weights"].numpy())
+    assert _rel(got, ref) < 1e-12
+
+
+def test_mxfp4_oracle_invariants_and_token_subset():
+    p = wl.make_mxfp4_problem(8, 128, 64, 6, 3, seed=32, routing="uniform_softmax", routed_scale=1.0)
+    args = _mx_args(p)
+    idx, w = p["top_k_index"].numpy(), p["top_k_weights"].numpy().astype(np.float64)
+    f = orc.moe_experts_mxfp4_reference
+    base = f(*args, idx, w)
+    assert np.all(f(*args, idx, np.zeros_like(w)) == 0.0)
+    assert _rel(f(*args, idx, 2.0 * w), 2.0 * base) < 1e-14
+    assert _rel(f(*args, idx[:, ::-1], w[:, ::-1]), base) < 1e-12
+    sub = f(*args, idx, w, tokens=[2, 6])
+    assert np.array_equal(sub[[2, 6]], base[[2, 6]]) and np.all(sub[[0, 1, 3, 4, 5, 7]] == 0)
+    r = np.random.default_rng(9).standard_normal(base.shape)
+    assert _rel(f(*args, idx, w, residual=r), base + r) < 1e-14
