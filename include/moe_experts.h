@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
     MOE_OK = 0,
@@ -72,11 +72,13 @@ enum moe_variant {
     MOE_VARIANT_FP8 = 2,     /* moe_experts_fp8                                */
     MOE_VARIANT_PLAN = 3,    /* moe_routing_plan                               */
     MOE_VARIANT_FP8_BF16IN = 4, /* moe_experts_fp8_bf16in                      */
+    MOE_VARIANT_MXFP4 = 5,   /* moe_experts_mxfp4                              */
 };
 
 /* Supported ranges (checked on every call; MOE_ERR_SHAPE otherwise):
  *   1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= E, T >= 0, T*k < 2^31,
- *   bf16 variants: H and F multiples of 64;  fp8: H and F multiples of 128. */
+ *   bf16 variants: H and F multiples of 64;  fp8 and mxfp4: H and F
+ *   multiples of 128. */
 #define MOE_MAX_EXPERTS 512
 
 /* Version of this interface (MOE_ABI_VERSION). */
@@ -98,8 +100,9 @@ int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_
  * Byte offsets, inside the workspace of `variant`, of its stages, for tests
  * and inspection:  offs[0] counts[E] int32, offs[1] offsets[E+1] int32,
  * offs[2] perm[T*k] int32, offs[3] inv[T*k] int32, offs[4] h (bf16 [T*k,F]
- * for prefill, fp8 codes [T*k,F] for fp8), offs[5] h scales (fp32
- * [T*k,F/128], fp8 only), offs[6] y (bf16 [T*k,H], expert order like h:
+ * for prefill, fp8 codes [T*k,F] for fp8 and mxfp4), offs[5] h scales (fp32
+ * [T*k,F/128] for fp8, E8M0 bytes [T*k,F/32] for mxfp4), offs[6] y (bf16
+ * [T*k,H], expert order like h:
  * row m holds slot perm[m]).
  * Entries a variant does not use are SIZE_MAX.  The decode fast path
  * (T <= 4) builds no plan and keeps no h: its workspace holds fp32 partial
@@ -235,6 +238,33 @@ int moe_experts_fp8_bf16in(const uint16_t* hidden,
                            uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Routed experts with MXFP4 weights and MXFP8 activations (DeepGEMM issue
+ * "GC MoE": FP8 activations with packed FP4 routed weights; its FP8 x FP4
+ * grouped GEMM kinds; mirage issue "Supporting MegaKernel for DeepSeek
+ * Models": ue8m0 scales per 32 elements), read as the OCP Microscaling
+ * formats.
+ *   x        [T,H]      E4M3 codes         x_scale        [T,H/32]    E8M0
+ *   gate_up  [E,2F,H/2] E2M1 pairs         gate_up_scale  [E,2F,H/32] E8M0
+ *   down     [E,H,F/2]  E2M1 pairs         down_scale     [E,H,F/32]  E8M0
+ *   top_k_index [T,k] int32, top_k_weights [T,k] fp32, residual/out [T,H] bf16.
+ * E2M1 element 2i of a row is the low nibble of byte i; an E8M0 byte s scales
+ * its 32 elements by 2^(s-127) (s = 255 is NaN).  Products accumulate in
+ * fp32 with both scales applied by the matrix cores.  The SwiGLU output is
+ * re-quantised to MXFP8 per (slot row, 32 block): shared exponent
+ * e = floor(log2(amax)) - 8 clamped to [-127, 127], code =
+ * RNE_e4m3(clamp(h / 2^e, +-448)), scale byte e + 127; an all-zero block
+ * gets byte 0 and zero codes.  x, gate_up, down, residual and out 16-byte
+ * aligned, the scale tensors 4-byte aligned.  Workspace:
+ * moe_workspace_size(MOE_VARIANT_MXFP4, ...).  Errors as moe_experts_fp8.
+ */
+int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale,
+                      const uint8_t* gate_up, const uint8_t* gate_up_scale,
+                      const uint8_t* down, const uint8_t* down_scale,
+                      const int32_t* top_k_index, const float* top_k_weights,
+                      const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                      uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Block-128 fp8 quantisation of `rows` rows of K values (mirage issue
  * "Supporting MegaKernel for DeepSeek Models", bf16_to_fp8_quantize, with the
  * fp32 scale that moe_w2_fp8_layer's input_scale carries).  `in` is fp32
@@ -251,7 +281,7 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
 /*
  * Stage timing, for measurement (not needed for normal use).
  * moe_profile_begin(max_calls) switches the recorder on: each of the next
- * max_calls layer calls (moe_experts_prefill / _decode / _fp8, from any host
+ * max_calls layer calls (moe_experts_prefill / _decode / _fp8 / _mxfp4, from any host
  * thread) launches every kernel with a start/stop HIP event pair attached to
  * that kernel's own dispatch (hipExtLaunchKernelGGL), on the stream it runs
  * on, so each pair times exactly one kernel's execution.  Creating the

@@ -28,6 +28,7 @@ MOE_VARIANT_DECODE = 1
 MOE_VARIANT_FP8 = 2
 MOE_VARIANT_PLAN = 3
 MOE_VARIANT_FP8_BF16IN = 4
+MOE_VARIANT_MXFP4 = 5
 
 _lib = None
 
@@ -58,6 +59,7 @@ def _load():
         "moe_experts_fp8_bf16in": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz,
                                     vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
+        "moe_experts_mxfp4": ([vp] * 9 + [i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
@@ -76,7 +78,7 @@ def exported_symbols():
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
-            "moe_workspace_size_shared"]
+            "moe_workspace_size_shared", "moe_experts_mxfp4"]
 
 
 class MoeError(RuntimeError):
@@ -378,6 +380,50 @@ def moe_experts_fp8_bf16in(hidden_states, gate_up, gate_up_scale, down, down_sca
                      workspace, out)
 
 
+def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                      top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """Routed experts with MXFP4 weights and MXFP8 activations.  x uint8 [T, H]
+    E4M3 codes (or torch.float8_e4m3fn) with x_scale uint8 [T, H/32] E8M0;
+    gate_up uint8 [E, 2F, H/2] and down uint8 [E, H, F/2] hold two E2M1 codes
+    per byte (element 2i in the low nibble) with uint8 E8M0 scales
+    [E, 2F, H/32] and [E, H, F/32].  Returns out [T, H] bf16 (plus the
+    optional residual [T, H] bf16)."""
+    x = _codes(x)
+    dev = x.device
+    _need(x, "x", torch.uint8, 2)
+    for t, name, nd in ((x_scale, "x_scale", 2), (gate_up, "gate_up", 3),
+                        (gate_up_scale, "gate_up_scale", 3), (down, "down", 3),
+                        (down_scale, "down_scale", 3)):
+        _need(t, name, torch.uint8, nd, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = x.shape
+    E, F2, Hh = gate_up.shape
+    F = F2 // 2
+    k = int(top_k)
+    if (2 * Hh != H or F2 != 2 * F or tuple(x_scale.shape) != (T, H // 32)
+            or tuple(gate_up_scale.shape) != (E, 2 * F, H // 32)
+            or tuple(down.shape) != (E, H, F // 2) or tuple(down_scale.shape) != (E, H, F // 32)):
+        raise ValueError("mxfp4 operand shapes do not match x [T,H], gate_up [E,2F,H/2], "
+                         "down [E,H,F/2] with per-32 scales")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size(MOE_VARIANT_MXFP4, T, H, F, E, k)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        rc = _load().moe_experts_mxfp4(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
+                                       _ptr(down), _ptr(down_scale), _ptr(top_k_index),
+                                       _ptr(top_k_weights), res, T, H, F, E, k, _ptr(out),
+                                       _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, "moe_experts_mxfp4")
+    return out
+
+
 def moe_routing_plan(top_k_index, num_experts):
     """(counts[E], offsets[E+1], perm[T*k], inv[T*k]) as int32 device tensors."""
     dev = top_k_index.device
@@ -420,7 +466,8 @@ __all__ = [
     "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
     "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_experts_prefill_shared",
-    "moe_experts_decode_shared", "moe_workspace_size_shared", "MoeError", "MOE_VARIANT_PREFILL",
-    "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN", "MOE_VARIANT_FP8_BF16IN",
+    "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
+    "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",
+    "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4",
     "LIB_PATH",
 ]

@@ -145,6 +145,9 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     if (variant == MOE_VARIANT_FP8 || variant == MOE_VARIANT_FP8_BF16IN) {
         L.h = take((size_t)P * F);
         L.hs = take((size_t)P * (F / 128) * sizeof(float));
+    } else if (variant == MOE_VARIANT_MXFP4) {
+        L.h = take((size_t)P * F);
+        L.hs = take((size_t)P * (F / 32));
     } else {
         L.h = take((size_t)P * F * 2);
     }
@@ -169,11 +172,12 @@ Layout make_shared_layout(int variant, int64_t T, int H, int F, int E, int k, in
 }
 
 int check_shape(int variant, int64_t T, int H, int F, int E, int k) {
-    if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_FP8_BF16IN) return MOE_ERR_SHAPE;
+    if (variant < MOE_VARIANT_PREFILL || variant > MOE_VARIANT_MXFP4) return MOE_ERR_SHAPE;
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E) return MOE_ERR_SHAPE;
     if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     if (variant == MOE_VARIANT_PLAN) return MOE_OK;
-    const bool fp8 = variant == MOE_VARIANT_FP8 || variant == MOE_VARIANT_FP8_BF16IN;
+    const bool fp8 = variant == MOE_VARIANT_FP8 || variant == MOE_VARIANT_FP8_BF16IN ||
+                     variant == MOE_VARIANT_MXFP4;
     const int mult = fp8 ? 128 : 64;
     if (H < mult || F < mult || H % mult || F % mult) return MOE_ERR_SHAPE;
     if ((int64_t)E * 2 * F * (int64_t)H >= ((int64_t)1 << 47)) return MOE_ERR_SHAPE;
@@ -285,6 +289,50 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
     rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
+                                   out, stream));
+}
+// MXFP4 layer: the plan, the two grouped MX products and the combine.
+int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+              const uint8_t* gate_up_scale, const uint8_t* down, const uint8_t* down_scale,
+              const int32_t* top_k_index, const float* top_k_weights, const uint16_t* residual,
+              int64_t T, int H, int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+    if (!x || !x_scale || !gate_up || !gate_up_scale || !down || !down_scale || !top_k_index ||
+        !top_k_weights || !out)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
+        (residual && !aligned16(residual)) ||
+        (((uintptr_t)x_scale | (uintptr_t)gate_up_scale | (uintptr_t)down_scale |
+          (uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
+        return MOE_ERR_ALIGN;
+    int rc = check_shape(MOE_VARIANT_MXFP4, T, H, F, E, k);
+    if (rc) return rc;
+    const Layout L = make_layout(MOE_VARIANT_MXFP4, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    const int P = (int)(T * k);
+    const GroupedPlan pl = plan_in(L, ws, E);
+    uint8_t* hq = at<uint8_t>(ws, L.h);
+    uint8_t* hs = at<uint8_t>(ws, L.hs);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_PLAN);
+    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
+                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
+                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), mx_tile_m(),
+                              stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_GATE_UP);
+    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_DOWN);
+    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
@@ -488,6 +536,15 @@ int moe_experts_fp8_bf16in(const uint16_t* hidden, const uint8_t* gate_up,
     return run_fp8(MOE_VARIANT_FP8_BF16IN, hidden, nullptr, nullptr, gate_up, gate_up_scale, down,
                    down_scale, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
                    ws_bytes, stream);
+}
+
+int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+                      const uint8_t* gate_up_scale, const uint8_t* down, const uint8_t* down_scale,
+                      const int32_t* top_k_index, const float* top_k_weights,
+                      const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                      uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                     top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
 }
 
 int moe_profile_begin(int max_calls) {

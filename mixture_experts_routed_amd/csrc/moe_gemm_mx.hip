@@ -1,0 +1,251 @@
+// moe_gemm_mx.hip - grouped products with MXFP4 routed weights and MXFP8
+// activations on gfx950's scaled f8f6f4 MFMA.
+//
+// Formats (DeepGEMM issue "GC MoE": FP8 activations with packed FP4 routed
+// weights; the MegaKernel issue's ue8m0 scales per 32 elements for FP8 GEMM
+// inputs; read as the OCP Microscaling formats): weights are E2M1, two per
+// byte with element 2i in the low nibble, one E8M0 scale byte per 32 K
+// elements of a row; activations and the re-quantised SwiGLU output are E4M3
+// with one E8M0 byte per 32 elements.  The MFMA applies both scales itself,
+// so the products accumulate in fp32 registers with no promotion step.
+//
+// Operand placement of v_mfma_scale_f32_32x32x64_f8f6f4 on gfx950 (measured
+// with single-wave probes): lane (r, h) of an fp8 operand holds K [16h, 16h+16)
+// in bytes 0-15 and K [32+16h, 48+16h) in bytes 16-31; of an fp4 operand K
+// [32h, 32h+32) in 16 bytes, low nibble first; its scale byte applies to K
+// block h (K [32h, 32h+32)) of row r.
+#include <algorithm>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kMxThreads = 512;   // 8 waves, a 4 (M) x 2 (N) grid of 32 x 128 wave tiles
+constexpr int kMxBM = 128;        // rows of an M tile
+constexpr int kMxBK = 128;        // K elements per stage: 128 fp8 bytes, 64 fp4 bytes per row
+
+// LDS chunk (16 bytes) of a 64-byte fp4 row: 16 consecutive rows read at one
+// logical chunk land on 16 distinct 4-bank groups.
+__device__ __forceinline__ int lds_chunk4(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+// One work item = (M tile of <= 128 rows of one expert) x (256 panel rows).
+// Per 128-K stage a thread stages 2 A chunks (token rows, fp8), 2 B chunks
+// (panel rows, fp4) and one scale word (4 E8M0 bytes: A scales for threads
+// 0-127, B scales for threads 128-383) in registers, two stages ahead, and
+// writes them into a 2-stage LDS ring.  Wave (wm, wn) owns tile rows
+// [32 wm, 32 wm + 32) and panel rows [128 wn, 128 wn + 128) as 4 blocks of 32.
+// SWIGLU: panel rows interleave gate/up in blocks of 32 (as the bf16 path), so
+// blocks (0, 1) and (2, 3) of a wave are (gate, up) pairs; each pair gives 32
+// h columns of one 32-wide MXFP8 block, whose row maximum is a reduction over
+// the 32 lanes that hold the columns.  Otherwise y bf16 [P, n_out] in expert
+// order.
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
+    uint16_t* __restrict__ Cy) {
+    constexpr int NB = BN / 64;                       // 32-row panel blocks per wave (WN = 2)
+    constexpr int A_PER = kMxBM * 8 / kMxThreads;     // 16-byte A chunks per thread and stage
+    constexpr int B_PER = BN * 4 / kMxThreads;        // 16-byte B chunks per thread and stage
+    static_assert(A_PER == 2 && B_PER >= 1 && (!SWIGLU || NB == 4), "tile shape");
+    __shared__ u32x4 a_lds[2][kMxBM][8];
+    __shared__ u32x4 b_lds[2][BN][4];
+    __shared__ uint32_t sa_lds[2][kMxBM];
+    __shared__ uint32_t sb_lds[2][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int h = lane >> 5;
+    const int ntiles = *ntiles_p;
+    const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
+    const int items = ntiles * n_tiles_n;
+    const int nks = K / kMxBK;
+    const int kb_row = K / 32;                        // scale bytes per row
+
+    auto panel_row = [&](int rr, int nt) {
+        if (SWIGLU) {
+            const int blk = rr >> 5;
+            return ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
+        }
+        return nt * BN + rr;
+    };
+
+    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+        const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        const int nt = gi.nt, e = gi.e;
+        const int row0 = tiles[2 * gi.mt + 1];
+        const int mrows = min(kMxBM, offsets[e + 1] - row0);
+        const bool active = 32 * wm < mrows;
+
+        // sources (rows past the tile's end read row 0, never stored)
+        const uint8_t* a_src[A_PER];
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int q = tid + kMxThreads * i;       // chunk id: row q / 8, chunk q % 8
+            const int r = q >> 3;
+            int64_t arow = 0;
+            if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+            a_src[i] = A + arow * K + (q & 7) * 16;
+        }
+        const uint8_t* b_src[B_PER];
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int q = tid + kMxThreads * i;       // row q / 4, chunk q % 4
+            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q >> 2, nt)) * (K / 2) + (q & 3) * 16;
+        }
+        // scale words: thread t < 128 -> A row t; 128 <= t < 128 + BN -> B row t - 128
+        const bool sa_t = tid < kMxBM, sb_t = tid >= kMxBM && tid < kMxBM + BN;
+        const uint8_t* s_src;
+        {
+            const int r = sa_t ? tid : 0;
+            int64_t arow = 0;
+            if (sa_t && r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+            const uint8_t* sa = As + arow * kb_row;
+            const uint8_t* sb = Bs + ((int64_t)e * b_rows + panel_row(sb_t ? tid - kMxBM : 0, nt)) * kb_row;
+            s_src = sb_t ? sb : sa;
+        }
+
+        f32x16 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+        u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
+        uint32_t rs0, rs1;
+
+        auto load = [&](u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER], uint32_t& rs, int ks) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) ra[i] = *(const u32x4*)(a_src[i] + ks * kMxBK);
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) rb[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
+            rs = *(const uint32_t*)(s_src + ks * 4);   // 4 scale bytes (blocks 4ks .. 4ks+3)
+        };
+        auto step = [&](int S, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER], uint32_t rs, int ks) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) {
+                const int q = tid + kMxThreads * i, r = q >> 3;
+                a_lds[S][r][lds_chunk(r, q & 7)] = ra[i];
+            }
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + kMxThreads * i, r = q >> 2;
+                b_lds[S][r][lds_chunk4(r, q & 3)] = rb[i];
+            }
+            if (sa_t) sa_lds[S][tid] = rs;
+            if (sb_t) sb_lds[S][tid - kMxBM] = rs;
+            lds_barrier();
+            if (active && ks < nks) {
+                const int ar = 32 * wm + (lane & 31);
+                const int asw = (ar >> 1) & 7;
+                const uint32_t sa = sa_lds[S][ar];
+                uint32_t sb[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) sb[nb] = sb_lds[S][(wn * NB + nb) * 32 + (lane & 31)];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {   // two 64-K MFMA chunks per stage
+                    const u32x4 lo = a_lds[S][ar][(4 * c + h) ^ asw];
+                    const u32x4 hi = a_lds[S][ar][(4 * c + 2 + h) ^ asw];
+                    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const int shift = 8 * (2 * c + h);   // this lane's 32-K block
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int br = (wn * NB + nb) * 32 + (lane & 31);
+                        const u32x4 bq = b_lds[S][br][lds_chunk4(br, 2 * c + h)];
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7));
+                        acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a, b, acc[nb], 0 /* A fp8 */, 4 /* B fp4 */, 0, (int)(sa >> shift), 0,
+                            (int)(sb[nb] >> shift));
+                    }
+                }
+            }
+        };
+
+        load(ra0, rb0, rs0, 0);
+        load(ra1, rb1, rs1, min(1, nks - 1));
+        for (int ks = 0; ks < nks; ks += 2) {
+            step(0, ra0, rb0, rs0, ks);
+            load(ra0, rb0, rs0, min(ks + 2, nks - 1));
+            step(1, ra1, rb1, rs1, ks + 1);
+            load(ra1, rb1, rs1, min(ks + 3, nks - 1));
+        }
+
+        if (SWIGLU) {
+            // h for f = nt*128 + (wn*2 + p)*32 + lane%32; one MXFP8 block per p
+            const int nfb = n_out / 32;
+            if (active) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const float hv = silu_fast(acc[2 * p][q]) * acc[2 * p + 1][q];
+                        const float amax = half_max32(fabsf(hv));
+                        // shared exponent floor(log2(amax)) - 8 (a subnormal
+                        // or zero amax ends below -127 and is clamped there)
+                        const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+                        const int se = max(-127, min(127, ex - 8));
+                        const float v = fminf(fmaxf(__builtin_ldexpf(hv, -se), -448.0f), 448.0f);
+                        const uint32_t code = f32x4_to_e4m3x4(v, 0.0f, 0.0f, 0.0f);
+                        const int row = 32 * wm + acc_row(q, lane);
+                        if (row < mrows) {
+                            const int blk = nt * 4 + wn * 2 + p;
+                            Cq[(int64_t)(row0 + row) * n_out + blk * 32 + (lane & 31)] = (uint8_t)code;
+                            if ((lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + blk] = (uint8_t)(se + 127);
+                        }
+                    }
+            }
+        } else if (active) {
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int q = 0; q < 16; q += 2) {
+                const int row = 32 * wm + acc_row(q, lane) + (odd ? 1 : 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float y0 = acc[nb][q], y1 = acc[nb][q + 1];
+                    const float got = pair_swap(odd ? y0 : y1);
+                    const int col = nt * BN + (wn * NB + nb) * 32 + (lane & 30);
+                    if (row < mrows) {
+                        const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
+                        *(uint32_t*)(Cy + (int64_t)(row0 + row) * n_out + col) = v;
+                    }
+                }
+            }
+        }
+        lds_barrier();  // the LDS ring is reused by the next item
+    }
+}
+
+int mx_tile_m() { return kMxBM; }
+
+template <int BN, bool SWIGLU>
+static int mx_grid() {
+    static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU>, kMxThreads,
+                                       device_cu_count());
+    return g;
+}
+
+hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
+                            const uint8_t* w13s, const GroupedPlan& pl, int H, int F, int k,
+                            uint8_t* hq, uint8_t* hs, hipStream_t s) {
+    MOE_LAUNCH((gemm_mx_kernel<256, true>), dim3(mx_grid<256, true>()), dim3(kMxThreads), 0, s, x, xs,
+               w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F, 2 * F,
+               k, hq, hs, (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2, const uint8_t* w2s,
+                          const GroupedPlan& pl, int H, int F, uint16_t* y, hipStream_t s) {
+    if (H % 256 == 0)
+        MOE_LAUNCH((gemm_mx_kernel<256, false>), dim3(mx_grid<256, false>()), dim3(kMxThreads), 0, s,
+                   hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                   H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
+    else
+        MOE_LAUNCH((gemm_mx_kernel<128, false>), dim3(mx_grid<128, false>()), dim3(kMxThreads), 0, s,
+                   hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                   H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -138,6 +138,18 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
                                float* scales, hipStream_t s);
 
+// MXFP4 x MXFP8 products (E2M1 weights two per byte, E4M3 activations, E8M0
+// scales per 32 K elements): gate_up with SwiGLU + MXFP8 re-quantisation
+// (hq [P, F] E4M3, hs [P, F/32] E8M0, expert order), and down -> y bf16
+// [P, H] in expert order.  H, F multiples of 128 (F also of 128 per h tile).
+int mx_tile_m();
+hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
+                            const uint8_t* w13s, const GroupedPlan& plan, int H, int F, int k,
+                            uint8_t* hq, uint8_t* hs, hipStream_t s);
+hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2,
+                          const uint8_t* w2s, const GroupedPlan& plan, int H, int F, uint16_t* y,
+                          hipStream_t s);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -293,10 +293,10 @@ def make_mxfp8_activations(T, H, E, k, seed, device="cpu", routing="sigmoid_topk
     return dict(x=xq, x_scale=xs, top_k_index=idx, top_k_weights=w)
 
 
-def make_mxfp4_problem(T, H, F, E, k, seed, device="cpu", act_seed=None, **kw):
+def make_mxfp4_problem(T, H, F, E, k, seed, device="cpu", act_seed=None, weight_std=0.02, **kw):
     """MXFP4 weights from ``seed``, MXFP8 activations and routing from
     ``act_seed`` (or the seed + 1)."""
-    p = make_mxfp4_weights(H, F, E, seed, device)
+    p = make_mxfp4_weights(H, F, E, seed, device, weight_std=weight_std)
     p.update(make_mxfp8_activations(T, H, E, k, act_seed if act_seed is not None else seed + 1,
                                     device, **kw))
     return p

@@ -46,17 +46,17 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
     assert moe.moe_strerror(-99) == "unknown status"
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 4, 5])
 def test_workspace_sizes_and_layout(variant):
     T, H, F, E, k = 2048, 1280, 896, 64, 6
-    if variant in (2, 4):
+    if variant in (2, 4, 5):
         T, H, F, E, k = 4096, 7168, 2048, 128, 8
     n = moe.moe_workspace_size(variant, T, H, F, E, k)
     lay = moe.moe_workspace_layout(variant, T, H, F, E, k)
@@ -66,9 +66,11 @@ def test_workspace_sizes_and_layout(variant):
     assert offs == sorted(offs) and len(set(offs)) == len(offs) and max(offs) < n
     P = T * k
     assert n >= P * H * 2                                   # y [P, H] bf16
-    if variant in (2, 4):
+    if variant in (2, 4, 5):
         assert lay["h_scale"] - lay["h"] >= P * F           # fp8 codes
         assert n - lay["y"] >= P * H * 2
+    if variant == 5:                                        # E8M0 bytes per 32 of F
+        assert lay["y"] - lay["h_scale"] >= P * (F // 32)
     if variant == 4:                                        # + the quantised hidden states
         assert n >= moe.moe_workspace_size(2, T, H, F, E, k) + T * H + T * (H // 128) * 4
 
@@ -92,6 +94,8 @@ def test_decode_fast_path_workspace_is_small():
     (0, 4, 128, 64, 513, 2),     # E above MOE_MAX_EXPERTS
     (2, 4, 192, 128, 8, 2),      # fp8 H not a multiple of 128
     (2, 4, 256, 64, 8, 2),       # fp8 F not a multiple of 128
+    (5, 4, 192, 128, 8, 2),      # mxfp4 H not a multiple of 128
+    (5, 4, 256, 96, 8, 2),       # mxfp4 F not a multiple of 128
     (7, 4, 128, 64, 8, 2),       # unknown variant
     (0, 1 << 30, 128, 64, 8, 4),  # T*k >= 2^31
 ])
@@ -154,6 +158,30 @@ def test_fp8_and_plan_validation():
     assert lib.moe_routing_plan(P16, 4, 2, 8, P16, P16, P16, P16, P16B, 1, None) == EWS
     assert lib.moe_quantize_fp8_block128(P16, 0, 4, 100, P16, P16, None) == ESHAPE
     assert lib.moe_quantize_fp8_block128(None, 0, 4, 128, P16, P16, None) == ENULL
+
+
+def test_mxfp4_validation():
+    lib = moe._load()
+    # x, x_scale, gate_up, gate_up_scale, down, down_scale, idx, w, residual, T, H, F, E, k,
+    # out, ws, ws_bytes, stream
+    args = [P16] * 8 + [None, 4, 256, 128, 8, 2, P16, P16B, 1 << 30, None]
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 14):
+        bad = list(args); bad[i] = None
+        assert lib.moe_experts_mxfp4(*bad) == ENULL, i
+    for i, off in ((0, 8), (2, 8), (4, 8), (14, 8), (8, 8), (1, 2), (3, 2), (5, 2), (6, 2)):
+        bad = list(args); bad[i] = (bad[i] or P16) + off
+        assert lib.moe_experts_mxfp4(*bad) == EALIGN, i
+    bad = list(args); bad[10] = 192                             # H
+    assert lib.moe_experts_mxfp4(*bad) == ESHAPE
+    bad = list(args); bad[11] = 96                              # F
+    assert lib.moe_experts_mxfp4(*bad) == ESHAPE
+    bad = list(args); bad[13] = 9                               # k > E
+    assert lib.moe_experts_mxfp4(*bad) == ESHAPE
+    need = moe.moe_workspace_size(moe.MOE_VARIANT_MXFP4, 4, 256, 128, 8, 2)
+    bad = list(args); bad[16] = need - 1                        # ws_bytes
+    assert lib.moe_experts_mxfp4(*bad) == EWS
+    bad = list(args); bad[15] = P16B + 16                       # ws not 256-byte aligned
+    assert lib.moe_experts_mxfp4(*bad) == EWS
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")
