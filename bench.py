@@ -23,8 +23,9 @@ committed rocprofv3 counter summary of this workload
 copy kernel), or null when the kernel sources changed since it was taken.
 
 Prints one JSON line.  --config picks another workload (ocr2_decode_t4,
-ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny, and ocr2_prefill_shared /
-ocr2_decode_t1_shared with the model's two shared experts).
+ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny, ocr2_prefill_shared /
+ocr2_decode_t1_shared with the model's two shared experts, and
+v3_mxfp4_decode / v3_mxfp4_prefill with MXFP4 weights).
 
 Helper modes (no GPU work of their own):
   --copy-calibration        a plain 256 MiB device copy, for counter scaling
@@ -47,7 +48,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-experts µs/call + tokens/s; % HBM peak (decode), % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+# Dense MFMA peaks.  The MXFP4 layer multiplies E4M3 activations by E2M1
+# weights; a scaled MFMA with an fp8 operand issues at the fp8 rate, so its
+# peak is fp8's (the fp4 figure holds for fp4 x fp4 only).
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0}
 # The model card's own decode figure for exactly this workload (T=1, H=1280,
 # F=896, 64 experts, top-6, bf16): 0.191 ms per call on an NVIDIA GB10.
 PAGE_DECODE_T1_TOKENS_PER_S = 1.0 / 0.191e-3
@@ -60,6 +64,7 @@ KERNEL_STAGES = [
     ("moe::combine_kernel", "combine"),
     ("moe::gemm_bf16_kernel<", "gemm_bf16"),
     ("moe::gemm_fp8_kernel<", "gemm_fp8"),
+    ("moe::gemm_mx_kernel<", "gemm_mx"),
     ("moe::quantize_kernel", "quantize"),
     ("moe::augment_routing_kernel", "shared_route"),
 ]
@@ -172,12 +177,17 @@ def summarize_pmc(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
 # ------------------------------------------------------------ algorithmic work
 def stage_work(stage, kind, T, H, F, k, touched, valid):
     """Algorithmic (bytes, flops) of one launch of `stage`: the weights of the
-    touched experts it reads (with their fp32 block scales for fp8) plus the
-    layer inputs/outputs it reads or writes; intermediates (h, y, partial
-    sums) are implementation overhead and are not counted."""
-    bw = 2 if kind == "bf16" else 1
-    sc = 0 if kind == "bf16" else 4.0 / 128
-    x_bytes = T * H * bw + (0 if kind == "bf16" else T * (H // 128) * 4)
+    touched experts it reads (with their block scales: fp32 per 128 for fp8,
+    one E8M0 byte per 32 for mxfp4) plus the layer inputs/outputs it reads or
+    writes; intermediates (h, y, partial sums) are implementation overhead and
+    are not counted."""
+    if kind == "mxfp4":
+        bw, sc = 0.5, 1.0 / 32                       # E2M1 pairs + E8M0 per 32
+        x_bytes = T * H * (1 + 1.0 / 32)             # E4M3 + E8M0 per 32
+    else:
+        bw = 2 if kind == "bf16" else 1
+        sc = 0 if kind == "bf16" else 4.0 / 128
+        x_bytes = T * H * bw + (0 if kind == "bf16" else T * (H // 128) * 4)
     out_bytes = T * H * 2
     route_bytes = T * k * 8
     gu_w = touched * 2 * F * H * (bw + sc)
@@ -305,11 +315,12 @@ def main():
         sets = 1
         routes = [(p["top_k_index"], p["top_k_weights"])] * n_route
 
+        entry = moe.moe_experts_mxfp4 if kind == "mxfp4" else moe.moe_experts_fp8
+
         def step(i):
-            return moe.moe_experts_fp8(p["x"], p["x_scale"], p["gate_up"], p["gate_up_scale"],
-                                       p["down"], p["down_scale"], p["top_k_index"],
-                                       p["top_k_weights"], k)
-        dtype = "fp8"
+            return entry(p["x"], p["x_scale"], p["gate_up"], p["gate_up_scale"], p["down"],
+                         p["down_scale"], p["top_k_index"], p["top_k_weights"], k)
+        dtype = kind
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- pass A: timing
@@ -449,12 +460,12 @@ def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
 
             def __getitem__(self, e):
                 return self.t[int(e)].cpu().numpy()
+        ref = (orc.moe_experts_mxfp4_reference if cfg["kind"] == "mxfp4"
+               else orc.moe_experts_fp8_reference)
         t0 = time.perf_counter()
-        orc.moe_experts_fp8_reference(hp["x"].cpu().numpy(), hp["x_scale"].cpu().numpy(),
-                                      Lazy(p["gate_up"]), Lazy(p["gate_up_scale"]),
-                                      Lazy(p["down"]), Lazy(p["down_scale"]),
-                                      hp["top_k_index"].cpu().numpy(),
-                                      hp["top_k_weights"].cpu().numpy(), tokens=tokens)
+        ref(hp["x"].cpu().numpy(), hp["x_scale"].cpu().numpy(), Lazy(p["gate_up"]),
+            Lazy(p["gate_up_scale"]), Lazy(p["down"]), Lazy(p["down_scale"]),
+            hp["top_k_index"].cpu().numpy(), hp["top_k_weights"].cpu().numpy(), tokens=tokens)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         done_tokens = len(tokens)

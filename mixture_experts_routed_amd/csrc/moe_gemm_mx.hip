@@ -24,6 +24,7 @@ namespace moe {
 constexpr int kMxThreads = 512;   // 8 waves, a 4 (M) x 2 (N) grid of 32 x 128 wave tiles
 constexpr int kMxBM = 128;        // rows of an M tile
 constexpr int kMxBK = 128;        // K elements per stage: 128 fp8 bytes, 64 fp4 bytes per row
+constexpr int kMxRegStages = 2;   // stages of operands loading ahead in registers
 
 // LDS chunk (16 bytes) of a 64-byte fp4 row: 16 consecutive rows read at one
 // logical chunk land on 16 distinct 4-bank groups.
@@ -57,8 +58,11 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     __shared__ uint32_t sa_lds[2][kMxBM];
     __shared__ uint32_t sb_lds[2][BN];
 
+    // waves w and w + 4 share a SIMD: (wm, wn) = (w / 2, w % 2) puts the
+    // waves of the first rows on four different SIMDs, so a tile of a few
+    // rows (decode batches) still spreads its products over the CU
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5;
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
@@ -112,30 +116,37 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         f32x16 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-        u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
-        uint32_t rs0, rs1;
+        // kMxRegStages stages of operands in registers: stage ks is written to
+        // the LDS ring, and its registers are refilled with stage
+        // ks + kMxRegStages right after the barrier, before the wave computes
+        // stage ks, so that kMxRegStages stages stay in flight through every
+        // product
+        u32x4 ra[kMxRegStages][A_PER], rb[kMxRegStages][B_PER];
+        uint32_t rs[kMxRegStages];
 
-        auto load = [&](u32x4 (&ra)[A_PER], u32x4 (&rb)[B_PER], uint32_t& rs, int ks) {
+        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rs_, int ks) {
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i) ra[i] = *(const u32x4*)(a_src[i] + ks * kMxBK);
+            for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * kMxBK);
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) rb[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
-            rs = *(const uint32_t*)(s_src + ks * 4);   // 4 scale bytes (blocks 4ks .. 4ks+3)
+            for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
+            rs_ = *(const uint32_t*)(s_src + ks * 4);   // 4 scale bytes (blocks 4ks .. 4ks+3)
         };
-        auto step = [&](int S, const u32x4 (&ra)[A_PER], const u32x4 (&rb)[B_PER], uint32_t rs, int ks) {
+        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rs_, int ks) {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) {
                 const int q = tid + kMxThreads * i, r = q >> 3;
-                a_lds[S][r][lds_chunk(r, q & 7)] = ra[i];
+                a_lds[S][r][lds_chunk(r, q & 7)] = ra_[i];
             }
 #pragma unroll
             for (int i = 0; i < B_PER; ++i) {
                 const int q = tid + kMxThreads * i, r = q >> 2;
-                b_lds[S][r][lds_chunk4(r, q & 3)] = rb[i];
+                b_lds[S][r][lds_chunk4(r, q & 3)] = rb_[i];
             }
-            if (sa_t) sa_lds[S][tid] = rs;
-            if (sb_t) sb_lds[S][tid - kMxBM] = rs;
+            if (sa_t) sa_lds[S][tid] = rs_;
+            if (sb_t) sb_lds[S][tid - kMxBM] = rs_;
             lds_barrier();
+            // refill (past the last stage: re-read the last one, an L2 hit)
+            load(ra_, rb_, rs_, min(ks + kMxRegStages, nks - 1));
             if (active && ks < nks) {
                 const int ar = 32 * wm + (lane & 31);
                 const int asw = (ar >> 1) & 7;
@@ -163,13 +174,14 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
             }
         };
 
-        load(ra0, rb0, rs0, 0);
-        load(ra1, rb1, rs1, min(1, nks - 1));
+        static_assert(kMxRegStages == 2, "one register buffer per LDS stage");
+        load(ra[0], rb[0], rs[0], 0);
+        load(ra[1], rb[1], rs[1], min(1, nks - 1));
         for (int ks = 0; ks < nks; ks += 2) {
-            step(0, ra0, rb0, rs0, ks);
-            load(ra0, rb0, rs0, min(ks + 2, nks - 1));
-            step(1, ra1, rb1, rs1, ks + 1);
-            load(ra1, rb1, rs1, min(ks + 3, nks - 1));
+            // unconditional (an odd last step computes nothing): a path that
+            // skipped it would leave the compiler's wait counts pessimistic
+            step(0, ra[0], rb[0], rs[0], ks);
+            step(1, ra[1], rb[1], rs[1], ks + 1);
         }
 
         if (SWIGLU) {
