@@ -61,6 +61,21 @@ Readings of points the pages leave open (each is listed in the design doc):
     x / 2^e clamped to +-448 and rounded to nearest even; an all-zero block
     gets s = 0 (2^-127) and zero codes.  The same rule with emax 2 and the
     E2M1 maximum 6 quantises weights to MXFP4.
+14. The softmax router ([OCR2]: fp32 softmax over the E router logits, greedy
+    top-k, weights scaled by routed_scaling_factor) keeps the k largest
+    probabilities without renormalising them.  Softmax is increasing in the
+    logit, so the choice is the k largest logits; equal logits go to the lower
+    expert id.  Slots are written in the order chosen (largest first).
+15. The group-aware sigmoid router ([MPK] moe_topk_sigmoid_routing_layer:
+    logits + bias, num_groups, topk_group, routed_scaling_factor) is read as:
+    s = sigmoid(logit); the choice score c = s + bias; the E experts form
+    num_groups consecutive groups; a group's score is the sum of its
+    `group_top` largest c (group_top = 2 is the DeepSeek-V3 rule the page's
+    layer serves, group_top = 1 ranks a group by its best member); the
+    topk_group best groups are kept (ties: lower group id); the k largest c
+    among their experts are chosen (ties: lower expert id), largest first;
+    their weights are the unbiased s renormalised to sum 1, times
+    routed_scaling_factor.  The choice is made on float64 scores.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (brute force, closed forms, invariants, library
@@ -88,6 +103,8 @@ __all__ = [
     "quantize_mxfp8_fp32",
     "dequantize_mx",
     "moe_experts_mxfp4_reference",
+    "route_softmax_topk",
+    "route_sigmoid_group_topk",
 ]
 
 # --------------------------------------------------------------------------
@@ -140,6 +157,82 @@ def routing_plan(top_k_index, num_experts):
             cursor[e] += 1
     return (counts.astype(np.int32), offsets.astype(np.int32),
             perm.astype(np.int32), inv.astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# Routers: logits -> (top_k_index, top_k_weights) ([OCR2] description: fp32
+# softmax + greedy top-k scaled by routed_scaling_factor; [MPK]
+# moe_topk_sigmoid_routing_layer: group-aware sigmoid routing)
+# --------------------------------------------------------------------------
+
+
+def _greedy_topk(score, k, allowed=None):
+    """Indices of the k largest entries of one row, largest first, equal
+    values in ascending index; ``allowed`` masks candidates (plain loop)."""
+    E = score.shape[0]
+    taken = np.zeros(E, dtype=bool)
+    if allowed is not None:
+        taken |= ~allowed
+    out = []
+    for _ in range(k):
+        best = -1
+        for e in range(E):
+            if taken[e]:
+                continue
+            if best < 0 or score[e] > score[best]:
+                best = e
+        out.append(best)
+        taken[best] = True
+    return out
+
+
+def route_softmax_topk(logits, k, routed_scaling_factor=1.0):
+    """Softmax router (reading 14).  logits [T, E] -> idx int32 [T, k] and
+    weights [T, k] float64 = softmax(logits)[idx] * routed_scaling_factor."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    idx = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        z = lg[t] - np.max(lg[t])
+        p = np.exp(z) / np.sum(np.exp(z))
+        ch = _greedy_topk(lg[t], k)
+        idx[t] = ch
+        w[t] = p[ch] * routed_scaling_factor
+    return idx, w
+
+
+def route_sigmoid_group_topk(logits, bias, k, num_groups, topk_group, routed_scaling_factor=1.0,
+                             group_top=2):
+    """Group-aware sigmoid router (reading 15).  logits [T, E], bias [E] ->
+    idx int32 [T, k], weights float64 [T, k]."""
+    lg = np.asarray(logits, dtype=np.float64)
+    b = np.asarray(bias, dtype=np.float64).reshape(-1)
+    T, E = lg.shape
+    if E % num_groups or not 1 <= topk_group <= num_groups:
+        raise ValueError("E must split into num_groups groups, 1 <= topk_group <= num_groups")
+    gsize = E // num_groups
+    if not 1 <= group_top <= gsize or not 1 <= k <= topk_group * gsize:
+        raise ValueError("group_top or k out of range")
+    idx = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        s = 1.0 / (1.0 + np.exp(-lg[t]))
+        c = s + b
+        gscore = np.zeros(num_groups)
+        for g in range(num_groups):
+            members = c[g * gsize:(g + 1) * gsize]
+            gscore[g] = sum(members[j] for j in _greedy_topk(members, group_top))
+        kept = _greedy_topk(gscore, topk_group)
+        allowed = np.zeros(E, dtype=bool)
+        for g in kept:
+            allowed[g * gsize:(g + 1) * gsize] = True
+        ch = _greedy_topk(c, k, allowed)
+        idx[t] = ch
+        w[t] = s[ch] / np.sum(s[ch]) * routed_scaling_factor
+    return idx, w
 
 
 # --------------------------------------------------------------------------

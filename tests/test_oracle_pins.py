@@ -578,3 +578,109 @@ def test_mxfp4_oracle_invariants_and_token_subset():
     assert np.array_equal(sub[[2, 6]], base[[2, 6]]) and np.all(sub[[0, 1, 3, 4, 5, 7]] == 0)
     r = np.random.default_rng(9).standard_normal(base.shape)
     assert _rel(f(*args, idx, w, residual=r), base + r) < 1e-14
+
+
+# ------------------------------------------------------------------ routers
+
+
+def test_softmax_router_golden(golden):
+    c = golden["softmax_router_quarters"]
+    idx, w = orc.route_softmax_topk(np.array(c["logits"]), c["k"], c["routed_scaling_factor"])
+    assert idx.tolist() == c["idx"]
+    np.testing.assert_allclose(w, c["weights"], rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_softmax_router_vs_library(seed):
+    """Distinct random logits: the choice is numpy's descending argsort, the
+    weights scipy's softmax at those ids times the factor."""
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((40, 64)) * 3
+    idx, w = orc.route_softmax_topk(lg, 6, 1.5)
+    ref = np.argsort(-lg, axis=1, kind="stable")[:, :6]
+    assert np.array_equal(idx, ref)
+    p = scipy.special.softmax(lg, axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(p, ref, 1) * 1.5, rtol=1e-12)
+
+
+def _rank_choice(score, allowed, k):
+    """Chosen ids by counting: e is chosen iff it is allowed and fewer than k
+    allowed ids beat it (larger score, or equal score and lower id); ordered
+    by that count."""
+    E = len(score)
+    rank = {}
+    for e in range(E):
+        if not allowed[e]:
+            continue
+        rank[e] = sum(1 for f in range(E) if allowed[f] and
+                      (score[f] > score[e] or (score[f] == score[e] and f < e)))
+    return [e for e, r in sorted(rank.items(), key=lambda kv: kv[1]) if r < k]
+
+
+def test_softmax_router_ties_shift_and_bruteforce():
+    rng = np.random.default_rng(3)
+    lg = rng.integers(-2, 3, (50, 8)).astype(np.float64)       # many exact ties
+    idx, w = orc.route_softmax_topk(lg, 3, 1.0)
+    for t in range(50):
+        assert idx[t].tolist() == _rank_choice(lg[t], [True] * 8, 3)
+    idx2, w2 = orc.route_softmax_topk(lg + 7.25, 3, 1.0)       # softmax is shift-invariant
+    assert np.array_equal(idx, idx2)
+    np.testing.assert_allclose(w, w2, rtol=1e-12)
+    idx, w = orc.route_softmax_topk(np.zeros((2, 8)), 3, 2.0)  # all equal: first k ids, p = 1/E
+    assert idx.tolist() == [[0, 1, 2]] * 2
+    np.testing.assert_allclose(w, 2.0 / 8)
+
+
+def test_sigmoid_router_golden(golden):
+    c = golden["sigmoid_group_router_by_hand"]
+    for gt, key in ((2, "idx_group_top2"), (1, "idx_group_top1")):
+        idx, w = orc.route_sigmoid_group_topk(np.array(c["logits"]), np.array(c["bias"]), c["k"],
+                                              c["num_groups"], c["topk_group"],
+                                              c["routed_scaling_factor"], group_top=gt)
+        assert idx.tolist() == c[key]
+        np.testing.assert_allclose(w, c["weights"], rtol=1e-12)
+
+
+def _sigmoid_router_bruteforce(lg, b, k, G, kg, gt, scale):
+    T, E = lg.shape
+    gs = E // G
+    idx = np.zeros((T, k), np.int64)
+    w = np.zeros((T, k))
+    for t in range(T):
+        s = scipy.special.expit(lg[t])
+        c = s + b
+        gscore = [sum(sorted(c[g * gs:(g + 1) * gs], reverse=True)[:gt]) for g in range(G)]
+        kept = [sum(1 for h in range(G) if gscore[h] > gscore[g] or (gscore[h] == gscore[g] and h < g)) < kg
+                for g in range(G)]
+        ch = _rank_choice(c, [kept[e // gs] for e in range(E)], k)
+        idx[t] = ch
+        w[t] = s[ch] / s[ch].sum() * scale
+    return idx, w
+
+
+@pytest.mark.parametrize("gt", [1, 2])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_sigmoid_router_vs_bruteforce(gt, seed):
+    """Integer logits and a two-valued bias make exact ties in expert and in
+    group scores; the counting formulation must agree id for id."""
+    rng = np.random.default_rng(seed)
+    E, G, kg, k = 16, 4, 2, 3
+    lg = rng.integers(-2, 3, (60, E)).astype(np.float64)
+    b = rng.choice([0.0, 0.25], E)
+    idx, w = orc.route_sigmoid_group_topk(lg, b, k, G, kg, 2.5, group_top=gt)
+    ri, rw = _sigmoid_router_bruteforce(lg, b, k, G, kg, gt, 2.5)
+    assert np.array_equal(idx, ri)
+    np.testing.assert_allclose(w, rw, rtol=1e-12)
+    np.testing.assert_allclose(w.sum(1), 2.5, rtol=1e-12)
+
+
+def test_sigmoid_router_one_group_is_plain_topk():
+    """One group, no bias: the k largest logits (sigmoid is increasing), weights
+    the renormalised sigmoids (torch.topk and scipy's expit as references)."""
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((30, 128))
+    idx, w = orc.route_sigmoid_group_topk(lg, np.zeros(128), 8, 1, 1, 2.5)
+    tv, ti = torch.topk(torch.from_numpy(lg), 8, dim=1)
+    assert np.array_equal(idx, ti.numpy())
+    s = scipy.special.expit(tv.numpy())
+    np.testing.assert_allclose(w, s / s.sum(1, keepdims=True) * 2.5, rtol=1e-12)
