@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
     MOE_OK = 0,
@@ -265,6 +265,55 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale,
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Routers: router logits -> top_k_index [T,k] int32 and top_k_weights [T,k]
+ * fp32 (device), the operands every layer entry point takes.
+ *   MOE_ROUTE_SOFTMAX (model card "DeepSeek-OCR-2 MoE experts", description:
+ *     fp32 softmax, greedy top-k scaled by routed_scaling_factor): the k
+ *     largest logits (softmax is increasing, so the choice is made on the
+ *     logits themselves), weight = softmax probability * routed_scaling_factor,
+ *     not renormalised.  bias must be NULL; the group arguments are ignored.
+ *   MOE_ROUTE_SIGMOID_GROUP (mirage issue "Supporting MegaKernel for DeepSeek
+ *     Models", moe_topk_sigmoid_routing_layer: logits + bias, num_groups,
+ *     topk_group, routed_scaling_factor): s = sigmoid(logit), choice score
+ *     c = s + bias[e] (fp64); the E experts form num_groups consecutive
+ *     groups, ranked by the sum of their group_top (1 or 2) largest c; the
+ *     topk_group best groups are kept and the k largest c among their experts
+ *     chosen; weights = chosen s / sum of chosen s * routed_scaling_factor.
+ *     DeepSeek-V3 uses group_top = 2.
+ * Ties go to the lower expert (group) id; chosen ids are written largest
+ * score first; a NaN score ranks below every number.
+ * logits [T,E] and bias [E] are fp32 (logits_bf16 = 0) or bf16 (1).
+ * Ranges: 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, 32); sigmoid-group:
+ * E % num_groups == 0, 1 <= topk_group <= num_groups <= 64, group_top 1 or 2
+ * (2 needs groups of at least 2), k <= topk_group * E / num_groups.
+ * Pointers 4-byte aligned (logits/bias 2-byte for bf16).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_DEVICE,
+ * MOE_ERR_LAUNCH.
+ */
+#define MOE_ROUTE_SOFTMAX 0
+#define MOE_ROUTE_SIGMOID_GROUP 1
+int moe_route_topk(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T,
+                   int E, int k, int num_groups, int topk_group, int group_top,
+                   float routed_scaling_factor, int32_t* top_k_index, float* top_k_weights,
+                   hipStream_t stream);
+
+/*
+ * Router and routing plan together: the routing of moe_route_topk, then the
+ * plan of moe_routing_plan over the ids it chose (counts[E], offsets[E+1] —
+ * the MegaKernel layer's "masks" — perm[T*k], inv[T*k]).  Batches of up to
+ * MOE_ROUTE_PLAN_FUSED_MAX_T tokens take one launch of one workgroup that
+ * routes and then plans; larger ones take the router launch and the plan
+ * launch.  Workspace: moe_workspace_size(MOE_VARIANT_PLAN, T, 0, 0, E, k).
+ * Arguments and errors as moe_route_topk and moe_routing_plan.
+ */
+#define MOE_ROUTE_PLAN_FUSED_MAX_T 64
+int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T,
+                   int E, int k, int num_groups, int topk_group, int group_top,
+                   float routed_scaling_factor, int32_t* top_k_index, float* top_k_weights,
+                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
  * Block-128 fp8 quantisation of `rows` rows of K values (mirage issue
  * "Supporting MegaKernel for DeepSeek Models", bf16_to_fp8_quantize, with the
  * fp32 scale that moe_w2_fp8_layer's input_scale carries).  `in` is fp32
@@ -281,8 +330,8 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
 /*
  * Stage timing, for measurement (not needed for normal use).
  * moe_profile_begin(max_calls) switches the recorder on: each of the next
- * max_calls layer calls (moe_experts_prefill / _decode / _fp8 / _mxfp4, from any host
- * thread) launches every kernel with a start/stop HIP event pair attached to
+ * max_calls calls (moe_experts_prefill / _decode / _fp8 / _mxfp4 and the
+ * routers, from any host thread) launches every kernel with a start/stop HIP event pair attached to
  * that kernel's own dispatch (hipExtLaunchKernelGGL), on the stream it runs
  * on, so each pair times exactly one kernel's execution.  Creating the
  * events is the only allocation and happens here.
@@ -306,6 +355,8 @@ enum moe_stage {
     MOE_STAGE_DECODE_SLICES = 4, /* decode form: gate_up, SwiGLU and down    */
     MOE_STAGE_QUANTIZE = 5,      /* input-side block-128 fp8 quantisation    */
     MOE_STAGE_SHARED_ROUTE = 6,  /* routing with the shared experts appended */
+    MOE_STAGE_ROUTER = 7,        /* router (logits -> ids, weights)          */
+    MOE_STAGE_ROUTE_PLAN = 8,    /* router and plan in one launch            */
 };
 int moe_profile_begin(int max_calls);
 int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);

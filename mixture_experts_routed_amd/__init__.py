@@ -29,6 +29,8 @@ MOE_VARIANT_FP8 = 2
 MOE_VARIANT_PLAN = 3
 MOE_VARIANT_FP8_BF16IN = 4
 MOE_VARIANT_MXFP4 = 5
+MOE_ROUTE_SOFTMAX = 0
+MOE_ROUTE_SIGMOID_GROUP = 1
 
 _lib = None
 
@@ -60,6 +62,10 @@ def _load():
                                     vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
         "moe_experts_mxfp4": ([vp] * 9 + [i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_route_topk": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
+                            vp], i32),
+        "moe_route_plan": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
+                            vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
@@ -78,7 +84,7 @@ def exported_symbols():
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
-            "moe_workspace_size_shared", "moe_experts_mxfp4"]
+            "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan"]
 
 
 class MoeError(RuntimeError):
@@ -128,7 +134,7 @@ def moe_workspace_layout(variant, T, H, F, E, k):
 # ------------------------------------------------------------ stage timing
 MOE_PROFILE_MAX_STAGES = 5
 STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices", 5: "quantize",
-               6: "shared_route"}
+               6: "shared_route", 7: "router", 8: "route_plan"}
 
 
 def moe_profile_begin(max_calls):
@@ -424,6 +430,64 @@ def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_
     return out
 
 
+def _route_args(logits, k, mode, bias, num_groups, topk_group, group_top):
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be float32 or bfloat16")
+    _need(logits, "logits", logits.dtype, 2)
+    dev = logits.device
+    if mode not in (MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_GROUP):
+        raise ValueError("mode must be MOE_ROUTE_SOFTMAX or MOE_ROUTE_SIGMOID_GROUP")
+    if bias is not None:
+        _need(bias, "bias", logits.dtype, 1, dev)
+        if bias.shape[0] != logits.shape[1]:
+            raise ValueError("bias must be [E]")
+    T, E = logits.shape
+    idx = torch.empty(T, int(k), dtype=torch.int32, device=dev)
+    w = torch.empty(T, int(k), dtype=torch.float32, device=dev)
+    args = [_ptr(logits), ctypes.c_void_p(None) if bias is None else _ptr(bias),
+            int(logits.dtype == torch.bfloat16), int(mode), T, E, int(k), int(num_groups),
+            int(topk_group), int(group_top)]
+    return dev, T, E, idx, w, args
+
+
+def moe_route_topk(logits, k, mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, topk_group=1,
+                   group_top=2, routed_scaling_factor=1.0):
+    """Router: logits [T, E] (fp32 or bf16) -> (top_k_index int32 [T, k],
+    top_k_weights fp32 [T, k]).  MOE_ROUTE_SOFTMAX: softmax top-k times the
+    factor; MOE_ROUTE_SIGMOID_GROUP: group-aware sigmoid routing with bias [E]
+    (same dtype as the logits)."""
+    dev, T, E, idx, w, args = _route_args(logits, k, mode, bias, num_groups, topk_group, group_top)
+    if T == 0:
+        return idx, w
+    with torch.cuda.device(dev):
+        rc = _load().moe_route_topk(*args, float(routed_scaling_factor), _ptr(idx), _ptr(w),
+                                    ctypes.c_void_p(_stream(dev)))
+    _check(rc, "moe_route_topk")
+    return idx, w
+
+
+def moe_route_plan(logits, k, mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, topk_group=1,
+                   group_top=2, routed_scaling_factor=1.0):
+    """Router then routing plan (one launch for small batches):
+    (top_k_index, top_k_weights, counts[E], offsets[E+1], perm[T*k], inv[T*k])."""
+    dev, T, E, idx, w, args = _route_args(logits, k, mode, bias, num_groups, topk_group, group_top)
+    P = T * int(k)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(P, dtype=torch.int32, device=dev)
+    inv = torch.empty(P, dtype=torch.int32, device=dev)
+    if T == 0:   # an empty batch: empty plan
+        return idx, w, counts.zero_(), offsets.zero_(), perm, inv
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        ws = _workspace(moe_workspace_size(MOE_VARIANT_PLAN, T, 0, 0, E, int(k)), dev, stream)
+        rc = _load().moe_route_plan(*args, float(routed_scaling_factor), _ptr(idx), _ptr(w),
+                                    _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws),
+                                    ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, "moe_route_plan")
+    return idx, w, counts, offsets, perm, inv
+
+
 def moe_routing_plan(top_k_index, num_experts):
     """(counts[E], offsets[E+1], perm[T*k], inv[T*k]) as int32 device tensors."""
     dev = top_k_index.device
@@ -468,6 +532,7 @@ __all__ = [
     "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_experts_prefill_shared",
     "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
     "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",
-    "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4",
+    "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4", "moe_route_topk", "moe_route_plan",
+    "MOE_ROUTE_SOFTMAX", "MOE_ROUTE_SIGMOID_GROUP",
     "LIB_PATH",
 ]

@@ -338,6 +338,31 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
                                    out, stream));
 }
+// Router arguments (moe_route_topk / moe_route_plan).
+int check_route(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T, int E,
+                int k, int num_groups, int topk_group, int group_top, const int32_t* idx,
+                const float* w) {
+    if (!logits || !idx || !w) return MOE_ERR_NULL;
+    if (mode == MOE_ROUTE_SIGMOID_GROUP && !bias) return MOE_ERR_NULL;
+    if ((logits_bf16 != 0 && logits_bf16 != 1) || T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 ||
+        k > E || k > 32 || T * (int64_t)k >= ((int64_t)1 << 31) || T * (int64_t)E >= ((int64_t)1 << 40))
+        return MOE_ERR_SHAPE;
+    if (mode == MOE_ROUTE_SOFTMAX) {
+        if (bias) return MOE_ERR_SHAPE;
+    } else if (mode == MOE_ROUTE_SIGMOID_GROUP) {
+        if (num_groups < 1 || num_groups > 64 || E % num_groups || topk_group < 1 ||
+            topk_group > num_groups || (group_top != 1 && group_top != 2) ||
+            (group_top == 2 && E / num_groups < 2) || k > topk_group * (E / num_groups))
+            return MOE_ERR_SHAPE;
+    } else {
+        return MOE_ERR_SHAPE;
+    }
+    const uintptr_t a = logits_bf16 ? 1u : 3u;
+    if (((uintptr_t)logits & a) || ((uintptr_t)bias & a) || (((uintptr_t)idx | (uintptr_t)w) & 3u))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 // The decode launch sequence (gather-GEMV for a few tokens, else the grouped
 // path) over E experts (routed, then shared) and k slots per token.
 int run_decode(StageClock& clock, const Layout& L, const uint16_t* hidden,
@@ -545,6 +570,59 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* g
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
                      top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
+}
+
+int moe_route_topk(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T,
+                   int E, int k, int num_groups, int topk_group, int group_top,
+                   float routed_scaling_factor, int32_t* top_k_index, float* top_k_weights,
+                   hipStream_t stream) {
+    int rc = check_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group, group_top,
+                         top_k_index, top_k_weights);
+    if (rc) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_ROUTER);
+    return launched(launch_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group,
+                                 group_top, routed_scaling_factor, top_k_index, top_k_weights,
+                                 stream));
+}
+
+int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T,
+                   int E, int k, int num_groups, int topk_group, int group_top,
+                   float routed_scaling_factor, int32_t* top_k_index, float* top_k_weights,
+                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+    int rc = check_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group, group_top,
+                         top_k_index, top_k_weights);
+    if (rc) return rc;
+    if (!counts || !offsets || !perm || !inv) return MOE_ERR_NULL;
+    if (((uintptr_t)counts | (uintptr_t)offsets | (uintptr_t)perm | (uintptr_t)inv) & 3u)
+        return MOE_ERR_ALIGN;
+    const Layout L = make_layout(MOE_VARIANT_PLAN, T, 0, 0, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    StageClock clock(stream);
+    if (T <= MOE_ROUTE_PLAN_FUSED_MAX_T) {
+        clock.mark(MOE_STAGE_ROUTE_PLAN);
+        return launched(launch_route_plan(logits, bias, logits_bf16, mode, (int)T, E, k, num_groups,
+                                          topk_group, group_top, routed_scaling_factor,
+                                          top_k_index, top_k_weights, counts, offsets, perm, inv,
+                                          at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                          at<int32_t>(ws, L.tile_off), kMinTileM, stream));
+    }
+    clock.mark(MOE_STAGE_ROUTER);
+    rc = launched(launch_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group,
+                               group_top, routed_scaling_factor, top_k_index, top_k_weights,
+                               stream));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_PLAN);
+    return launched(launch_plan(top_k_index, (int)(T * k), E, counts, offsets, perm, inv,
+                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                at<int32_t>(ws, L.tile_off), kMinTileM, stream));
 }
 
 int moe_profile_begin(int max_calls) {

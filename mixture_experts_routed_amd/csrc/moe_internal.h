@@ -150,6 +150,17 @@ hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w
                           const uint8_t* w2s, const GroupedPlan& plan, int H, int F, uint16_t* y,
                           hipStream_t s);
 
+// Routers (logits -> ids, weights), alone or followed by the plan in the
+// same launch (one workgroup; small batches).
+hipError_t launch_route(const void* logits, const void* bias, int bf16, int mode, int64_t T, int E,
+                        int k, int num_groups, int topk_group, int group_top, float scale,
+                        int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_route_plan(const void* logits, const void* bias, int bf16, int mode, int T,
+                             int E, int k, int num_groups, int topk_group, int group_top,
+                             float scale, int32_t* idx, float* w, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
+                             int32_t* ntiles, int32_t* tile_off, int tile_m, hipStream_t s);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
@@ -182,6 +182,40 @@ def test_mxfp4_validation():
     assert lib.moe_experts_mxfp4(*bad) == EWS
     bad = list(args); bad[15] = P16B + 16                       # ws not 256-byte aligned
     assert lib.moe_experts_mxfp4(*bad) == EWS
+
+
+def test_router_validation():
+    lib = moe._load()
+    # logits, bias, bf16, mode, T, E, k, groups, topk_group, group_top, scale, idx, w, stream
+    soft = [P16, None, 0, 0, 4, 64, 6, 1, 1, 2, 1.0, P16, P16, None]
+    sig = [P16, P16B, 1, 1, 4, 256, 8, 8, 4, 2, 2.5, P16, P16, None]
+    for args in (soft, sig):
+        for i in (0, 11, 12):
+            bad = list(args); bad[i] = None
+            assert lib.moe_route_topk(*bad) == ENULL, i
+    bad = list(sig); bad[1] = None                                # sigmoid needs the bias
+    assert lib.moe_route_topk(*bad) == ENULL
+    bad = list(soft); bad[1] = P16B                               # softmax takes no bias
+    assert lib.moe_route_topk(*bad) == ESHAPE
+    for i, v in ((3, 2), (2, 2), (5, 0), (5, 513), (6, 0), (6, 65), (6, 33), (4, -1)):
+        bad = list(soft); bad[i] = v
+        assert lib.moe_route_topk(*bad) == ESHAPE, (i, v)
+    for i, v in ((7, 3), (7, 0), (7, 128), (8, 0), (8, 9), (9, 3), (9, 0), (6, 33)):
+        bad = list(sig); bad[i] = v                               # groups must divide E, etc.
+        assert lib.moe_route_topk(*bad) == ESHAPE, (i, v)
+    bad = list(sig); bad[6], bad[7], bad[8] = 17, 16, 1           # k > topk_group * group size
+    assert lib.moe_route_topk(*bad) == ESHAPE
+    bad = list(sig); bad[5], bad[7], bad[9], bad[6] = 8, 8, 2, 1  # groups of one with group_top 2
+    assert lib.moe_route_topk(*bad) == ESHAPE
+    bad = list(soft); bad[0] = P16 + 2                            # fp32 logits need 4 bytes
+    assert lib.moe_route_topk(*bad) == EALIGN
+    bad = list(sig); bad[0] = P16 + 2                             # bf16 logits: 2 is enough
+    assert lib.moe_route_topk(*bad) in (OK, EDEV)
+    plan = soft[:13] + [P16, P16, P16, P16, P16B, 1 << 20, None]
+    bad = list(plan); bad[15] = None
+    assert lib.moe_route_plan(*bad) == ENULL
+    bad = list(plan); bad[18] = 1
+    assert lib.moe_route_plan(*bad) == EWS
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")

@@ -1,0 +1,151 @@
+"""GPU parity of the routers (moe_route_topk, moe_route_plan) against the
+oracle's route_softmax_topk / route_sigmoid_group_topk and routing_plan.
+
+Bars: chosen ids bit-exact (both sides decide on the same values: softmax on
+the input logits themselves, sigmoid-group on float64 scores); plan
+bit-exact; weights within 1e-5 relative for the fp32 softmax and 1e-6 for the
+sigmoid-group weights (float64 arithmetic rounded to fp32 once).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_routed_amd as moe
+    moe._load()
+    yield
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _moe():
+    import mixture_experts_routed_amd as moe
+    return moe
+
+
+def _logits(T, E, seed, dtype, ints=False, scale=2.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randint(-2, 3, (T, E), generator=g).float() if ints else torch.randn(T, E, generator=g) * scale
+    return x.to(dtype)
+
+
+def _bias(E, seed, dtype, two_valued=False):
+    g = torch.Generator().manual_seed(seed)
+    b = (torch.randint(0, 2, (E,), generator=g).float() * 0.25) if two_valued else torch.randn(E, generator=g) * 0.1
+    return b.to(dtype)
+
+
+def _check_plan(idx, E, counts, offsets, perm, inv):
+    ref = orc.routing_plan(idx, E)
+    for name, a, b in zip(("counts", "offsets", "perm", "inv"), (counts, offsets, perm, inv), ref):
+        assert np.array_equal(a.cpu().numpy(), b), f"plan {name} differs"
+
+
+@pytest.mark.parametrize("T,E,k,dtype", [(300, 64, 6, torch.float32), (300, 64, 6, torch.bfloat16),
+                                         (7, 512, 8, torch.float32), (129, 96, 32, torch.bfloat16),
+                                         (3, 8, 8, torch.float32)])
+def test_softmax_router(T, E, k, dtype):
+    moe = _moe()
+    _say(f"softmax router T={T} E={E} k={k} {dtype}")
+    lg = _logits(T, E, 11 + T, dtype)
+    idx, w = moe.moe_route_topk(lg.cuda(), k, moe.MOE_ROUTE_SOFTMAX, routed_scaling_factor=1.5)
+    ri, rw = orc.route_softmax_topk(lg.double().numpy(), k, 1.5)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=1e-30)
+
+
+def test_softmax_router_ties_and_nan():
+    moe = _moe()
+    lg = _logits(200, 64, 3, torch.float32, ints=True)      # exact ties everywhere
+    lg[5, :] = 0.0
+    lg[6, 10] = float("nan")
+    idx, w = moe.moe_route_topk(lg.cuda(), 6, moe.MOE_ROUTE_SOFTMAX)
+    keep = [t for t in range(200) if t != 6]
+    ri, rw = orc.route_softmax_topk(lg[keep].double().numpy(), 6)
+    assert np.array_equal(idx.cpu().numpy()[keep], ri)
+    np.testing.assert_allclose(w.cpu().numpy()[keep], rw, rtol=1e-5)
+    assert idx[5].tolist() == [0, 1, 2, 3, 4, 5]
+    row = idx[6].cpu().numpy()                                # NaN ranks lowest
+    assert len(set(row.tolist())) == 6 and 10 not in row and row.min() >= 0 and row.max() < 64
+
+
+@pytest.mark.parametrize("T,E,G,tg,k,gt,dtype", [
+    (200, 256, 8, 4, 8, 2, torch.bfloat16),      # the MegaKernel layer's shapes
+    (200, 128, 8, 4, 8, 2, torch.bfloat16),
+    (150, 128, 8, 4, 8, 1, torch.float32),
+    (50, 64, 4, 1, 4, 2, torch.float32),
+    (33, 512, 64, 3, 20, 2, torch.float32),
+    (40, 60, 60, 7, 5, 1, torch.float32),        # groups of one expert
+])
+def test_sigmoid_group_router(T, E, G, tg, k, gt, dtype):
+    moe = _moe()
+    _say(f"sigmoid-group router T={T} E={E} G={G} tg={tg} k={k} gt={gt} {dtype}")
+    lg = _logits(T, E, 21 + E, dtype)
+    b = _bias(E, 5 + E, dtype)
+    idx, w = moe.moe_route_topk(lg.cuda(), k, moe.MOE_ROUTE_SIGMOID_GROUP, bias=b.cuda(),
+                                num_groups=G, topk_group=tg, group_top=gt, routed_scaling_factor=2.5)
+    ri, rw = orc.route_sigmoid_group_topk(lg.double().numpy(), b.double().numpy(), k, G, tg, 2.5,
+                                          group_top=gt)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6)
+
+
+@pytest.mark.parametrize("gt", [1, 2])
+def test_sigmoid_group_router_ties(gt):
+    """Integer logits and a two-valued bias: exact ties in expert and group
+    scores, broken by the lower id on both sides."""
+    moe = _moe()
+    lg = _logits(300, 64, 9, torch.bfloat16, ints=True)
+    b = _bias(64, 4, torch.bfloat16, two_valued=True)
+    idx, w = moe.moe_route_topk(lg.cuda(), 6, moe.MOE_ROUTE_SIGMOID_GROUP, bias=b.cuda(),
+                                num_groups=8, topk_group=3, group_top=gt, routed_scaling_factor=1.0)
+    ri, rw = orc.route_sigmoid_group_topk(lg.double().numpy(), b.double().numpy(), 6, 8, 3, 1.0,
+                                          group_top=gt)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6)
+
+
+@pytest.mark.parametrize("T", [1, 4, 64, 65, 4096])
+@pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
+def test_route_plan(T, mode):
+    """Router + plan: ids and weights equal moe_route_topk's, the plan equals
+    the oracle's plan of those ids, on the fused one-launch form (T <= 64)
+    and the two-launch form."""
+    moe = _moe()
+    _say(f"route_plan {mode} T={T}")
+    if mode == "softmax":
+        E, k = 64, 6
+        lg = _logits(T, E, 31 + T, torch.float32).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SOFTMAX, routed_scaling_factor=1.0)
+    else:
+        E, k = 128, 8
+        lg = _logits(T, E, 41 + T, torch.bfloat16).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SIGMOID_GROUP, bias=_bias(E, 2, torch.bfloat16).cuda(),
+                  num_groups=8, topk_group=4, group_top=2, routed_scaling_factor=2.5)
+    idx, w, counts, offsets, perm, inv = moe.moe_route_plan(lg, k, **kw)
+    i2, w2 = moe.moe_route_topk(lg, k, **kw)
+    assert torch.equal(idx, i2) and torch.equal(w, w2)
+    _check_plan(idx.cpu().numpy(), E, counts, offsets, perm, inv)
+
+
+def test_router_zero_tokens():
+    moe = _moe()
+    idx, w = moe.moe_route_topk(torch.zeros(0, 64, device="cuda"), 6)
+    assert idx.shape == (0, 6)
+    out = moe.moe_route_plan(torch.zeros(0, 64, device="cuda"), 6)
+    assert out[0].shape == (0, 6) and out[2].shape == (64,)
+    assert out[2].abs().sum().item() == 0 and out[3].abs().sum().item() == 0
