@@ -67,6 +67,8 @@ KERNEL_STAGES = [
     ("moe::gemm_mx_kernel<", "gemm_mx"),
     ("moe::quantize_kernel", "quantize"),
     ("moe::augment_routing_kernel", "shared_route"),
+    ("moe::route_kernel", "router"),
+    ("moe::route_plan_kernel", "route_plan"),
 ]
 
 
@@ -406,11 +408,48 @@ def main():
         roof["algorithmic_flops_per_launch"] = int(f)
         out["roofline"] = roof
 
+    # ------------------------------------------- pass C: router (+ plan)
+    if not args.no_stage_pass:
+        out["router"] = router_pass(moe, torch, np, name, kind, T, E, k, cfg, steps, warmup)
+
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(name, cfg, args.cpu_seconds, routes, warmup,
                                            base if kind == "bf16" else p)
     print(json.dumps(out), flush=True)
+
+
+def router_pass(moe, torch, np, name, kind, T, E, k, cfg, steps, warmup):
+    """moe_route_plan on seeded logits of this workload's shape: the model
+    card's softmax router for the OCR-2 shapes, the MegaKernel layer's
+    group-aware sigmoid router (8 groups, 4 kept, bf16 logits and bias) for the
+    V3 shapes.  Reported beside the layer (the layer itself takes ids)."""
+    g = torch.Generator().manual_seed(cfg["seed"] + 77)
+    if kind == "bf16":
+        lg = (torch.randn(T, E, generator=g) * 2).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SOFTMAX, routed_scaling_factor=cfg["routed_scale"])
+        rule = "softmax"
+    else:
+        lg = (torch.randn(T, E, generator=g) * 2).to(torch.bfloat16).cuda()
+        bias = (torch.randn(E, generator=g) * 0.1).to(torch.bfloat16).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SIGMOID_GROUP, bias=bias, num_groups=8, topk_group=4,
+                  group_top=2, routed_scaling_factor=cfg["routed_scale"])
+        rule = "sigmoid_group(8 groups, 4 kept, top-2 group score)"
+    for _ in range(warmup):
+        moe.moe_route_plan(lg, k, **kw)
+    torch.cuda.synchronize()
+    moe.moe_profile_begin(steps)
+    for _ in range(steps):
+        moe.moe_route_plan(lg, k, **kw)
+    torch.cuda.synchronize()
+    calls = moe.moe_profile_end(steps)
+    per = collections.defaultdict(list)
+    for row in calls:
+        for st, ms in row:
+            per[st].append(ms)
+    return {"entry": "moe_route_plan", "rule": rule, "launches": len(calls[0]) if calls else 0,
+            "kernel_us": {st: round(float(np.mean(v)) * 1e3, 2) for st, v in per.items()},
+            "kernel_us_total": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2)}
 
 
 def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
