@@ -88,6 +88,19 @@ __device__ __forceinline__ float transpose_sum(float (&v)[N]) {
     return s;
 }
 
+// acc + the dot product of 8 bf16 pairs (one 16-byte chunk each), by four
+// v_dot2c_f32_bf16: the bf16 products are exact in fp32, so only the
+// accumulation rounds, as with fp32 FMAs on the unpacked values, at a third
+// of the vector instructions.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+    return acc;
+}
+
 // One workgroup per (distinct selected expert u, F slice sl), block index
 // u * nslices + sl.  S = slice width (16 or 32), NCH = 16-byte chunks per
 // lane of an H row (H <= 512 NCH), NT = number of tokens.
@@ -193,13 +206,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
             for (int t = 0; t < NT; ++t) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    float a[8], b[8];
-                    unpack8(wv[r][i], a);
-                    unpack8(xv[t][i], b);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) acc += a[q] * b[q];
-                }
+                for (int i = 0; i < NCH; ++i) acc = dot8_bf16(wv[r][i], xv[t][i], acc);
                 v[(rb + r) * NT + t] = acc;
             }
     }
