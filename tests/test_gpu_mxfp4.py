@@ -125,7 +125,11 @@ def to_gpu(p):
 # 128, down panels of 256 (H % 256 == 0) and 128 (H = 128, 384), one or many
 # 128-K steps, and an odd number of them (H = 384: 3 steps)
 SHAPES = [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2),
-          (600, 256, 128, 4, 2), (700, 512, 256, 3, 2), (257, 384, 640, 5, 2)]
+          (600, 256, 128, 4, 2), (700, 512, 256, 3, 2), (257, 384, 640, 5, 2),
+          # decode-batch shapes (at most 32 slots per expert on average, F % 256
+          # == 0, H % 512 == 0): 32-row tiles and 512-row panels; the second has
+          # experts with more than 32 rows (several tiles) and some with none
+          (40, 512, 256, 8, 2), (100, 1024, 512, 16, 4), (9, 1536, 768, 32, 3)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -151,7 +155,7 @@ def test_mxfp4_block_scales_spread(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 384, 384, 4, 2)])
+@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 384, 384, 4, 2), (60, 512, 256, 8, 2)])
 def test_mxfp4_h_stage_codes(shape):
     """The MXFP8 h in the workspace against the oracle's fp32 rule applied to
     the oracle's h.  The kernel quantises its fp32-accumulated h; the scale
@@ -198,7 +202,7 @@ def test_mxfp4_h_stage_codes(shape):
     assert np.all(np.abs(hv - rv) <= np.abs(rv) * 2.0 ** -3 + blk_max * 1e-3)
 
 
-@pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 384, 256, 4, 3)])
+@pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 384, 256, 4, 3), (50, 512, 256, 8, 3)])
 def test_mxfp4_overwrite_and_dropped(shape):
     """Dropped slots (ids -1 and E) contribute nothing and every output
     element is written (a NaN-filled out buffer)."""
