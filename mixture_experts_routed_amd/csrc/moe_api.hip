@@ -329,10 +329,12 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
                               stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_GATE_UP);
-    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
+    const bool wide = mx_use_wide(P, E, H, F);
+    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, wide, H, F, k, hq, hs,
+                                   stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, H, F, y, stream));
+    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, wide, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,

@@ -229,6 +229,196 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     }
 }
 
+// Wide variant for long M tiles (prefill): 128 rows x 512 panel rows, the 8
+// waves a 2 (M) x 4 (N) grid of 64 x 128 wave tiles ((wm, wn) = (w / 4,
+// w % 4): the two waves of a SIMD own the same panel rows and the two 64-row
+// halves).  Each A fragment read from LDS now feeds 4 products and each B
+// fragment 2, against 4 and 1 in the 32 x 128 tiles above: 16 instead of 24
+// LDS bytes per lane and product, which the 128 x 256 kernel spends about as
+// much time on as on its products.  Scales: every thread stages the word of
+// panel row tid, threads < 128 also the word of tile row tid.
+template <bool SWIGLU>
+__global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
+    uint16_t* __restrict__ Cy) {
+    constexpr int BN = 512;
+    constexpr int NB = 4;                             // 32-row panel blocks per wave
+    constexpr int MB = 2;                             // 32-row tile blocks per wave
+    constexpr int A_PER = kMxBM * 8 / kMxThreads;     // 2
+    constexpr int B_PER = BN * 4 / kMxThreads;        // 4
+    __shared__ u32x4 a_lds[2][kMxBM][8];
+    __shared__ u32x4 b_lds[2][BN][4];
+    __shared__ uint32_t sa_lds[2][kMxBM];
+    __shared__ uint32_t sb_lds[2][BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int h = lane >> 5;
+    const int ntiles = *ntiles_p;
+    const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
+    const int items = ntiles * n_tiles_n;
+    const int nks = K / kMxBK;
+    const int kb_row = K / 32;
+    const bool sa_t = tid < kMxBM;
+
+    auto panel_row = [&](int rr, int nt) {
+        if (SWIGLU) {
+            const int blk = rr >> 5;
+            return ((blk & 1) ? n_out : 0) + nt * (BN / 2) + (blk >> 1) * 32 + (rr & 31);
+        }
+        return nt * BN + rr;
+    };
+
+    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+        const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        const int nt = gi.nt, e = gi.e;
+        const int row0 = tiles[2 * gi.mt + 1];
+        const int mrows = min(kMxBM, offsets[e + 1] - row0);
+        const bool active = 64 * wm < mrows;
+        auto a_row = [&](int r) -> int64_t {   // rows past the tile's end read row 0, never stored
+            if (r >= mrows) return 0;
+            return SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+        };
+
+        const uint8_t* a_src[A_PER];
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int q = tid + kMxThreads * i;
+            a_src[i] = A + a_row(q >> 3) * K + (q & 7) * 16;
+        }
+        const uint8_t* b_src[B_PER];
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int q = tid + kMxThreads * i;
+            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q >> 2, nt)) * (K / 2) + (q & 3) * 16;
+        }
+        const uint8_t* sa_src = As + a_row(tid & (kMxBM - 1)) * kb_row;
+        const uint8_t* sb_src = Bs + ((int64_t)e * b_rows + panel_row(tid, nt)) * kb_row;
+
+        f32x16 acc[MB][NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
+        u32x4 ra[2][A_PER], rb[2][B_PER];
+        uint32_t rsa[2], rsb[2];
+
+        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rsa_, uint32_t& rsb_,
+                        int ks) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * kMxBK);
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
+            rsb_ = *(const uint32_t*)(sb_src + ks * 4);
+            rsa_ = *(const uint32_t*)(sa_src + ks * 4);
+        };
+        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rsa_,
+                        uint32_t& rsb_, int ks) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) {
+                const int q = tid + kMxThreads * i, r = q >> 3;
+                a_lds[S][r][lds_chunk(r, q & 7)] = ra_[i];
+            }
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) {
+                const int q = tid + kMxThreads * i, r = q >> 2;
+                b_lds[S][r][lds_chunk4(r, q & 3)] = rb_[i];
+            }
+            sb_lds[S][tid] = rsb_;
+            if (sa_t) sa_lds[S][tid] = rsa_;
+            lds_barrier();
+            load(ra_, rb_, rsa_, rsb_, min(ks + 2, nks - 1));
+            if (active && ks < nks) {
+                uint32_t sa[MB], sb[NB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) sa[mb] = sa_lds[S][64 * wm + 32 * mb + (lane & 31)];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) sb[nb] = sb_lds[S][(wn * NB + nb) * 32 + (lane & 31)];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    i32x8 a[MB];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const int ar = 64 * wm + 32 * mb + (lane & 31);
+                        const int asw = (ar >> 1) & 7;
+                        const u32x4 lo = a_lds[S][ar][(4 * c + h) ^ asw];
+                        const u32x4 hi = a_lds[S][ar][(4 * c + 2 + h) ^ asw];
+                        a[mb] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                    const int shift = 8 * (2 * c + h);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int br = (wn * NB + nb) * 32 + (lane & 31);
+                        const u32x4 bq = b_lds[S][br][lds_chunk4(br, 2 * c + h)];
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                a[mb], b, acc[mb][nb], 0, 4, 0, (int)(sa[mb] >> shift), 0,
+                                (int)(sb[nb] >> shift));
+                    }
+                }
+            }
+        };
+
+        load(ra[0], rb[0], rsa[0], rsb[0], 0);
+        load(ra[1], rb[1], rsa[1], rsb[1], min(1, nks - 1));
+        for (int ks = 0; ks < nks; ks += 2) {
+            step(0, ra[0], rb[0], rsa[0], rsb[0], ks);
+            step(1, ra[1], rb[1], rsa[1], rsb[1], ks + 1);
+        }
+
+        if (SWIGLU) {
+            const int nfb = n_out / 32;
+            if (active) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int p = 0; p < NB / 2; ++p)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const float hv = silu_fast(acc[mb][2 * p][q]) * acc[mb][2 * p + 1][q];
+                            const float amax = half_max32(fabsf(hv));
+                            const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+                            const int se = max(-127, min(127, ex - 8));
+                            const float v = fminf(fmaxf(__builtin_ldexpf(hv, -se), -448.0f), 448.0f);
+                            const uint32_t code = f32x4_to_e4m3x4(v, 0.0f, 0.0f, 0.0f);
+                            const int row = 64 * wm + 32 * mb + acc_row(q, lane);
+                            if (row < mrows) {
+                                const int blk = nt * (BN / 64) + wn * (NB / 2) + p;
+                                Cq[(int64_t)(row0 + row) * n_out + blk * 32 + (lane & 31)] = (uint8_t)code;
+                                if ((lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + blk] = (uint8_t)(se + 127);
+                            }
+                        }
+            }
+        } else if (active) {
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 16; q += 2) {
+                    const int row = 64 * wm + 32 * mb + acc_row(q, lane) + (odd ? 1 : 0);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const float y0 = acc[mb][nb][q], y1 = acc[mb][nb][q + 1];
+                        const float got = pair_swap(odd ? y0 : y1);
+                        const int col = nt * BN + (wn * NB + nb) * 32 + (lane & 30);
+                        if (row < mrows) {
+                            const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
+                            *(uint32_t*)(Cy + (int64_t)(row0 + row) * n_out + col) = v;
+                        }
+                    }
+                }
+        }
+        lds_barrier();
+    }
+}
+
 int mx_tile_m() { return kMxBM; }
 
 template <int BN, bool SWIGLU>
@@ -238,9 +428,26 @@ static int mx_grid() {
     return g;
 }
 
+template <bool SWIGLU>
+static int mx_wide_grid() {
+    static const int g = resident_grid((const void*)gemm_mx_wide_kernel<SWIGLU>, kMxThreads,
+                                       device_cu_count());
+    return g;
+}
+
+bool mx_use_wide(int64_t P, int E, int H, int F) {
+    return P > 64 * (int64_t)E && F % 256 == 0 && H % 512 == 0;
+}
+
 hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
-                            const uint8_t* w13s, const GroupedPlan& pl, int H, int F, int k,
-                            uint8_t* hq, uint8_t* hs, hipStream_t s) {
+                            const uint8_t* w13s, const GroupedPlan& pl, bool wide, int H, int F,
+                            int k, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+    if (wide) {
+        MOE_LAUNCH((gemm_mx_wide_kernel<true>), dim3(mx_wide_grid<true>()), dim3(kMxThreads), 0, s, x,
+                   xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F,
+                   2 * F, k, hq, hs, (uint16_t*)nullptr);
+        return hipGetLastError();
+    }
     MOE_LAUNCH((gemm_mx_kernel<256, true>), dim3(mx_grid<256, true>()), dim3(kMxThreads), 0, s, x, xs,
                w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F, 2 * F,
                k, hq, hs, (uint16_t*)nullptr);
@@ -248,8 +455,13 @@ hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* 
 }
 
 hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2, const uint8_t* w2s,
-                          const GroupedPlan& pl, int H, int F, uint16_t* y, hipStream_t s) {
-    if (H % 256 == 0)
+                          const GroupedPlan& pl, bool wide, int H, int F, uint16_t* y,
+                          hipStream_t s) {
+    if (wide)
+        MOE_LAUNCH((gemm_mx_wide_kernel<false>), dim3(mx_wide_grid<false>()), dim3(kMxThreads), 0, s,
+                   hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                   H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
+    else if (H % 256 == 0)
         MOE_LAUNCH((gemm_mx_kernel<256, false>), dim3(mx_grid<256, false>()), dim3(kMxThreads), 0, s,
                    hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                    H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
