@@ -129,7 +129,10 @@ SHAPES = [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2),
           # decode-batch shapes (at most 32 slots per expert on average, F % 256
           # == 0, H % 512 == 0): 32-row tiles and 512-row panels; the second has
           # experts with more than 32 rows (several tiles) and some with none
-          (40, 512, 256, 8, 2), (100, 1024, 512, 16, 4), (9, 1536, 768, 32, 3)]
+          (40, 512, 256, 8, 2), (100, 1024, 512, 16, 4), (9, 1536, 768, 32, 3),
+          # more than 64 rows per expert with F % 256 == 0 and H % 512 == 0:
+          # the 128 x 512 tiles (ragged last M tile, three h tiles)
+          (900, 1024, 768, 5, 2)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -142,7 +145,7 @@ def test_mxfp4_medium(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (257, 384, 640, 5, 2)])
+@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (257, 384, 640, 5, 2), (600, 1024, 512, 4, 2)])
 def test_mxfp4_block_scales_spread(shape):
     """Every 32-block of weights and activations scaled by 2^u, u in [-4, 4]
     (neighbouring E8M0 bytes up to 2^8 apart): each scale byte must meet its
@@ -155,7 +158,8 @@ def test_mxfp4_block_scales_spread(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 384, 384, 4, 2), (60, 512, 256, 8, 2)])
+@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 384, 384, 4, 2), (60, 512, 256, 8, 2),
+                                   (520, 512, 256, 2, 2)])
 def test_mxfp4_h_stage_codes(shape):
     """The MXFP8 h in the workspace against the oracle's fp32 rule applied to
     the oracle's h.  The kernel quantises its fp32-accumulated h; the scale
@@ -202,7 +206,8 @@ def test_mxfp4_h_stage_codes(shape):
     assert np.all(np.abs(hv - rv) <= np.abs(rv) * 2.0 ** -3 + blk_max * 1e-3)
 
 
-@pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 384, 256, 4, 3), (50, 512, 256, 8, 3)])
+@pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 384, 256, 4, 3), (50, 512, 256, 8, 3),
+                                   (300, 512, 256, 3, 3)])
 def test_mxfp4_overwrite_and_dropped(shape):
     """Dropped slots (ids -1 and E) contribute nothing and every output
     element is written (a NaN-filled out buffer)."""
