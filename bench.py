@@ -411,6 +411,37 @@ def main():
     # ------------------------------------------- pass C: router (+ plan)
     if not args.no_stage_pass:
         out["router"] = router_pass(moe, torch, np, name, kind, T, E, k, cfg, steps, warmup)
+        if decode and kind == "bf16" and not S:
+            # pass D: the same decode steps from router logits, the routing
+            # fused into the slice kernel (moe_experts_decode_routed)
+            gl = torch.Generator().manual_seed(cfg["seed"] + 78)
+            logit_sets = [(torch.randn(T, E, generator=gl) * 2).to(dev) for _ in range(n_route)]
+
+            def step_routed(i):
+                s_ = i % sets
+                return moe.moe_experts_decode_routed(hidden, logit_sets[i], gu_sets[s_], dn_sets[s_], k,
+                                                     mode=moe.MOE_ROUTE_SOFTMAX,
+                                                     routed_scaling_factor=cfg["routed_scale"])
+            for i in range(warmup):
+                step_routed(i)
+            torch.cuda.synchronize()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for i in range(steps):
+                step_routed(warmup + i)
+            ev1.record()
+            torch.cuda.synchronize()
+            moe.moe_profile_begin(steps)
+            for i in range(steps):
+                step_routed(warmup + i)
+            torch.cuda.synchronize()
+            calls = moe.moe_profile_end(steps)
+            out["router"]["decode_routed"] = {
+                "entry": "moe_experts_decode_routed (softmax router fused into the slice kernel)",
+                "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
+                "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
+                "launches": len(calls[0]) if calls else 0}
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:

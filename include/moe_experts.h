@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
     MOE_OK = 0,
@@ -312,6 +312,25 @@ int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mo
                    float routed_scaling_factor, int32_t* top_k_index, float* top_k_weights,
                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bf16 decode from router logits: the router of moe_route_topk fused into
+ * moe_experts_decode.  On the gather-GEMV form (the limits of
+ * moe_experts_decode) every workgroup of the slice kernel routes the T <= 4
+ * tokens itself, so the call is the same two launches as moe_experts_decode;
+ * larger calls take a router launch first.  The chosen ids and weights are
+ * written to top_k_index [T,k] / top_k_weights [T,k] (device, caller-owned),
+ * bit-identical to moe_route_topk's.  Router arguments as moe_route_topk,
+ * layer arguments and workspace (MOE_VARIANT_DECODE) as moe_experts_decode;
+ * the output equals moe_experts_decode on those ids and weights.
+ */
+int moe_experts_decode_routed(const uint16_t* hidden, const void* logits, const void* bias,
+                              int logits_bf16, int mode, int num_groups, int topk_group,
+                              int group_top, float routed_scaling_factor, const uint16_t* gate_up,
+                              const uint16_t* down, const uint16_t* residual, int64_t T, int H,
+                              int F, int E, int k, uint16_t* out, int32_t* top_k_index,
+                              float* top_k_weights, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * Block-128 fp8 quantisation of `rows` rows of K values (mirage issue

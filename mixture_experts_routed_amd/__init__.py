@@ -66,6 +66,8 @@ def _load():
                             vp], i32),
         "moe_route_plan": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
                             vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_experts_decode_routed": ([vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
+                                       vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
@@ -84,7 +86,8 @@ def exported_symbols():
             "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
-            "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan"]
+            "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
+            "moe_experts_decode_routed"]
 
 
 class MoeError(RuntimeError):
@@ -488,6 +491,44 @@ def moe_route_plan(logits, k, mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, t
     return idx, w, counts, offsets, perm, inv
 
 
+def moe_experts_decode_routed(hidden_states, router_logits, gate_up_proj, down_proj, top_k,
+                              mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, topk_group=1,
+                              group_top=2, routed_scaling_factor=1.0, residual=None,
+                              workspace=None, out=None):
+    """bf16 decode from router logits [T, E] (fp32 or bf16): routing fused
+    into the decode kernels (T <= 4 gather-GEMV form).  Returns (out [T, H]
+    bf16, top_k_index int32 [T, k], top_k_weights fp32 [T, k])."""
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(gate_up_proj, "gate_up_proj", torch.bfloat16, 3, dev)
+    _need(down_proj, "down_proj", torch.bfloat16, 3, dev)
+    T, H = hidden_states.shape
+    E, F2, H2 = gate_up_proj.shape
+    F = F2 // 2
+    k = int(top_k)
+    if H2 != H or F2 != 2 * F or tuple(down_proj.shape) != (E, H, F):
+        raise ValueError("expected gate_up_proj [E,2F,H] and down_proj [E,H,F] matching hidden_states [T,H]")
+    _, Tl, El, idx, w, rargs = _route_args(router_logits, k, mode, bias, num_groups, topk_group,
+                                           group_top)
+    if (Tl, El) != (T, E):
+        raise ValueError("router_logits must be [T, E]")
+    res = _residual(residual, T, H, dev)
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out, idx, w
+    with torch.cuda.device(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size(MOE_VARIANT_DECODE, T, H, F, E, k)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        lg, bp, bf, md = rargs[0], rargs[1], rargs[2], rargs[3]
+        rc = _load().moe_experts_decode_routed(
+            _ptr(hidden_states), lg, bp, bf, md, int(num_groups), int(topk_group), int(group_top),
+            float(routed_scaling_factor), _ptr(gate_up_proj), _ptr(down_proj), res, T, H, F, E, k,
+            _ptr(out), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, "moe_experts_decode_routed")
+    return out, idx, w
+
+
 def moe_routing_plan(top_k_index, num_experts):
     """(counts[E], offsets[E+1], perm[T*k], inv[T*k]) as int32 device tensors."""
     dev = top_k_index.device
@@ -533,6 +574,7 @@ __all__ = [
     "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
     "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",
     "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4", "moe_route_topk", "moe_route_plan",
+    "moe_experts_decode_routed",
     "MOE_ROUTE_SOFTMAX", "MOE_ROUTE_SIGMOID_GROUP",
     "LIB_PATH",
 ]

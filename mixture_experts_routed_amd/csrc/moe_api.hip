@@ -627,6 +627,47 @@ int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mo
                                 at<int32_t>(ws, L.tile_off), kMinTileM, stream));
 }
 
+int moe_experts_decode_routed(const uint16_t* hidden, const void* logits, const void* bias,
+                              int logits_bf16, int mode, int num_groups, int topk_group,
+                              int group_top, float routed_scaling_factor, const uint16_t* gate_up,
+                              const uint16_t* down, const uint16_t* residual, int64_t T, int H,
+                              int F, int E, int k, uint16_t* out, int32_t* top_k_index,
+                              float* top_k_weights, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
+    if (rc) return rc;
+    if ((rc = check_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group,
+                          group_top, top_k_index, top_k_weights)))
+        return rc;
+    if ((rc = check_shape(MOE_VARIANT_DECODE, T, H, F, E, k))) return rc;
+    const Layout L = make_layout(MOE_VARIANT_DECODE, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    StageClock clock(stream);
+    const ExpertWeights gu = routed_only(gate_up, E), dn = routed_only(down, E);
+    if (!L.decode_fast) {   // router launch, then the decode sequence on its ids
+        clock.mark(MOE_STAGE_ROUTER);
+        rc = launched(launch_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group,
+                                   group_top, routed_scaling_factor, top_k_index, top_k_weights,
+                                   stream));
+        if (rc) return rc;
+        return run_decode(clock, L, hidden, gu, dn, top_k_index, top_k_weights, residual, T, H, F,
+                          E, k, out, ws, stream);
+    }
+    const RouteArgs ra{logits, bias, logits_bf16, mode, E, k, num_groups, topk_group, group_top,
+                       routed_scaling_factor};
+    clock.mark(MOE_STAGE_DECODE_SLICES);
+    rc = launched(launch_decode_slices(hidden, gu, dn, nullptr, (int)T, k, E, H, F,
+                                       at<float>(ws, L.part), stream, ra, top_k_index,
+                                       top_k_weights));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_COMBINE);
+    return launched(launch_decode_combine(at<float>(ws, L.part), top_k_index, top_k_weights,
+                                          residual, (int)T, k, E, H, F, out, stream));
+}
+
 int moe_profile_begin(int max_calls) {
     if (max_calls < 1 || max_calls > MOE_PROFILE_MAX_CALLS) return MOE_ERR_SHAPE;
     int dev, rc;

@@ -19,6 +19,7 @@
 // product start without any device-wide synchronisation.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_route.h"
 
 namespace moe {
 
@@ -104,11 +105,16 @@ __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float a
 // One workgroup per (distinct selected expert u, F slice sl), block index
 // u * nslices + sl.  S = slice width (16 or 32), NCH = 16-byte chunks per
 // lane of an H row (H <= 512 NCH), NT = number of tokens.
+// With ra.logits set the workgroup routes the NT tokens itself first (waves
+// 0 .. NT-1, one token each, into LDS; workgroup 0 also stores the ids and
+// weights for the combine), so a decode call from router logits needs no
+// router launch.
 template <int S, int NCH, int NT>
 __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
     const uint16_t* __restrict__ x, const ExpertWeights w13,
     const ExpertWeights w2, const int32_t* __restrict__ idx, int k, int E, int H,
-    int F, int nslices, float* __restrict__ part) {
+    int F, int nslices, float* __restrict__ part, const RouteArgs ra,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
     constexpr int kSlice = S;
     constexpr int kRowsPerWave = 2 * S / 8;     // gate/up panel rows per wave
     constexpr int CPR = S / 8;                  // 16-byte chunks of a down-slice row
@@ -122,6 +128,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
     __shared__ u32x4 w2s[W2REG ? 1 : kDecodeMaxDim * CPR];  // down[e][c][f0 .. f0+S): CPR chunks per row
     __shared__ float dots[2][NT][kSlice];                 // gate / up dot products
     __shared__ float hs[kDecodeMaxSlots][kSlice];
+    __shared__ int32_t idx_sh[kDecodeMaxSlots];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = NT * k;
@@ -142,7 +149,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
             const int c = lane + 64 * i;
             xv[t][i] = zero_unless(c < nch, *(const uint4*)(x + (int64_t)t * H + min(c, nch - 1) * 8));
         }
-    const WaveRouting R = wave_routing(idx, P, E);
+    const int32_t* ids = idx;
+    if (ra.logits) {   // uniform over the grid
+        if (wave < NT) {
+            int id;
+            float wt;
+            if (ra.E <= 64) route_token_lanes<1>(ra, wave, lane, id, wt);
+            else if (ra.E <= 128) route_token_lanes<2>(ra, wave, lane, id, wt);
+            else route_token_lanes<8>(ra, wave, lane, id, wt);
+            if (lane < k) {
+                idx_sh[wave * k + lane] = id;
+                if (blockIdx.x == 0) {
+                    idx_out[wave * k + lane] = id;
+                    w_out[wave * k + lane] = wt;
+                }
+            }
+        }
+        lds_barrier();
+        ids = idx_sh;
+    }
+    const WaveRouting R = wave_routing(ids, P, E);
     if (u >= R.n) return;  // fewer distinct experts than slots (uniform over the workgroup)
     uint64_t fm = R.first;
     for (int i = 0; i < u; ++i) fm &= fm - 1ull;
@@ -350,13 +376,13 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 template <int S, int NCH>
 static void launch_slices(dim3 grid, const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                           const int32_t* idx, int T, int k, int E, int H, int F, int ns, float* part,
-                          hipStream_t s) {
+                          hipStream_t s, const RouteArgs& ra, int32_t* io, float* wo) {
     if (NCH * T > kDecodeMaxChunkTokens) return;  // excluded by decode_fast_path
     switch (T) {
-        case 1: MOE_LAUNCH((decode_slice_kernel<S, NCH, 1>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
-        case 2: MOE_LAUNCH((decode_slice_kernel<S, NCH, 2>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
-        case 3: MOE_LAUNCH((decode_slice_kernel<S, NCH, 3>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
-        case 4: MOE_LAUNCH((decode_slice_kernel<S, NCH < 4 ? NCH : 3, 4>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part); break;
+        case 1: MOE_LAUNCH((decode_slice_kernel<S, NCH, 1>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
+        case 2: MOE_LAUNCH((decode_slice_kernel<S, NCH, 2>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
+        case 3: MOE_LAUNCH((decode_slice_kernel<S, NCH, 3>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
+        case 4: MOE_LAUNCH((decode_slice_kernel<S, NCH < 4 ? NCH : 3, 4>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
         default: break;
     }
 }
@@ -364,16 +390,17 @@ static void launch_slices(dim3 grid, const uint16_t* x, const ExpertWeights& w13
 template <int S>
 static hipError_t launch_width(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                                const int32_t* idx, int T, int k, int E, int H, int F, int umax,
-                               float* part, hipStream_t s) {
+                               float* part, hipStream_t s, const RouteArgs& ra, int32_t* io,
+                               float* wo) {
     const int ns = F / S;
     // padded to a multiple of 16 (even runs per XCD); padding blocks map to
     // u >= umax, where the routing has no distinct expert
     const dim3 grid((unsigned)((umax * ns + 15) / 16 * 16));
     switch ((H / 8 + 63) / 64) {
-        case 1: launch_slices<S, 1>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
-        case 2: launch_slices<S, 2>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
-        case 3: launch_slices<S, 3>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
-        case 4: launch_slices<S, 4>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s); break;
+        case 1: launch_slices<S, 1>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
+        case 2: launch_slices<S, 2>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
+        case 3: launch_slices<S, 3>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
+        case 4: launch_slices<S, 4>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
         default: return hipErrorInvalidValue;  // H > 2048 is routed to the grouped path by the caller
     }
     return hipGetLastError();
@@ -381,10 +408,12 @@ static hipError_t launch_width(const uint16_t* x, const ExpertWeights& w13, cons
 
 hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
                                 const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
-                                int H, int F, float* part, hipStream_t s) {
+                                int H, int F, float* part, hipStream_t s, const RouteArgs& ra,
+                                int32_t* idx_out, float* w_out) {
     const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    return g.slice == 16 ? launch_width<16>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s)
-                         : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s);
+    return g.slice == 16
+               ? launch_width<16>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s, ra, idx_out, w_out)
+               : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s, ra, idx_out, w_out);
 }
 
 hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,

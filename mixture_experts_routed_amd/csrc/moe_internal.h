@@ -63,6 +63,16 @@ inline ExpertWeights routed_only(const uint16_t* w, int E) { return ExpertWeight
 hipError_t launch_augment_routing(const int32_t* idx, const float* w, int64_t T, int k, int E,
                                   int S, int32_t* idx2, float* w2, hipStream_t s);
 
+// Router arguments as the kernels take them (logits NULL: no routing).
+struct RouteArgs {
+    const void* logits;
+    const void* bias;
+    int bf16;          // logits and bias are bf16 (else fp32)
+    int mode;          // MOE_ROUTE_*
+    int E, k, num_groups, topk_group, group_top;
+    float scale;
+};
+
 // Grouped-GEMM inputs produced by the plan.
 struct GroupedPlan {
     const int32_t* perm;
@@ -120,9 +130,14 @@ inline size_t decode_partial_bytes(int64_t T, int k, int E, int H, int F) {
     return (size_t)(T * k) * (size_t)g.nslices * (size_t)H * sizeof(float);
 }
 
+// With ra.logits set, the kernel routes the T tokens itself (every
+// workgroup, redundantly; workgroup 0 also writes idx_out / w_out for the
+// combine and the caller) and `idx` is unused.
 hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
                                 const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
-                                int H, int F, float* part, hipStream_t s);
+                                int H, int F, float* part, hipStream_t s,
+                                const RouteArgs& ra = RouteArgs{}, int32_t* idx_out = nullptr,
+                                float* w_out = nullptr);
 hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
                                  const uint16_t* residual, int T, int k, int E, int H, int F,
                                  uint16_t* out, hipStream_t s);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s

@@ -149,3 +149,44 @@ def test_router_zero_tokens():
     out = moe.moe_route_plan(torch.zeros(0, 64, device="cuda"), 6)
     assert out[0].shape == (0, 6) and out[2].shape == (64,)
     assert out[2].abs().sum().item() == 0 and out[3].abs().sum().item() == 0
+
+
+@pytest.mark.parametrize("T", [1, 4, 9])
+@pytest.mark.parametrize("mode", ["softmax", "sigmoid"])
+def test_decode_routed(T, mode):
+    """Decode from router logits (routing fused into the slice kernel for
+    T <= 4, a router launch first above): ids and weights equal
+    moe_route_topk's, the output equals moe_experts_decode on those ids and
+    weights bit for bit, and the oracle (router + layer) within the bf16 bar."""
+    import moe_workloads as wl
+    moe = _moe()
+    _say(f"decode_routed {mode} T={T}")
+    H, F, E, k = 1280, 896, 64, 6
+    p = wl.make_bf16_problem(T, H, F, E, k, 1002, "cpu")
+    g = {n: v.cuda() for n, v in p.items()}
+    if mode == "softmax":
+        lg = _logits(T, E, 50 + T, torch.float32).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SOFTMAX, routed_scaling_factor=1.0)
+    else:
+        lg = _logits(T, E, 60 + T, torch.bfloat16).cuda()
+        kw = dict(mode=moe.MOE_ROUTE_SIGMOID_GROUP, bias=_bias(E, 7, torch.bfloat16).cuda(),
+                  num_groups=8, topk_group=4, group_top=2, routed_scaling_factor=2.5)
+    res = (torch.randn(T, H, generator=torch.Generator().manual_seed(T)) * 0.5).to(torch.bfloat16).cuda()
+    out, idx, w = moe.moe_experts_decode_routed(g["hidden"], lg, g["gate_up"], g["down"], k,
+                                                residual=res, **kw)
+    i2, w2 = moe.moe_route_topk(lg, k, **kw)
+    assert torch.equal(idx, i2)
+    torch.testing.assert_close(w, w2, rtol=1e-6, atol=0)
+    ref_out = moe.moe_experts_decode(g["hidden"], g["gate_up"], g["down"], idx, w, k, residual=res)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    if mode == "softmax":
+        ri, rw = orc.route_softmax_topk(lg.double().cpu().numpy(), k, 1.0)
+    else:
+        ri, rw = orc.route_sigmoid_group_topk(lg.double().cpu().numpy(), kw["bias"].double().cpu().numpy(),
+                                              k, 8, 4, 2.5, group_top=2)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    ref = orc.moe_experts_reference(f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]), ri, rw,
+                                    residual=f64(res))
+    err = np.abs(f64(out) - ref) / (1e-2 + 1e-2 * np.abs(ref))
+    assert err.max() <= 1.0, err.max()
