@@ -218,6 +218,25 @@ def test_router_validation():
     assert lib.moe_route_plan(*bad) == EWS
 
 
+def test_decode_routed_validation():
+    lib = moe._load()
+    # hidden, logits, bias, bf16, mode, groups, topk_group, group_top, scale, gate_up, down,
+    # residual, T, H, F, E, k, out, idx, w, ws, ws_bytes, stream
+    args = [P16, P16, None, 0, 0, 1, 1, 2, 1.0, P16, P16, None, 1, 128, 64, 8, 2, P16, P16, P16,
+            P16B, 1 << 30, None]
+    for i in (0, 1, 9, 10, 17, 18, 19):
+        bad = list(args); bad[i] = None
+        assert lib.moe_experts_decode_routed(*bad) == ENULL, i
+    bad = list(args); bad[2] = P16B                           # softmax takes no bias
+    assert lib.moe_experts_decode_routed(*bad) == ESHAPE
+    bad = list(args); bad[13] = 96                            # H not a multiple of 64
+    assert lib.moe_experts_decode_routed(*bad) == ESHAPE
+    bad = list(args); bad[21] = 1                             # workspace too small
+    assert lib.moe_experts_decode_routed(*bad) == EWS
+    bad = list(args); bad[9] = P16 + 2
+    assert lib.moe_experts_decode_routed(*bad) == EALIGN
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful on a host without a GPU")
 def test_valid_arguments_without_gpu_report_device_error():
     lib = moe._load()
