@@ -65,6 +65,7 @@ KERNEL_STAGES = [
     ("moe::gemm_bf16_kernel<", "gemm_bf16"),
     ("moe::gemm_fp8_kernel<", "gemm_fp8"),
     ("moe::gemm_mx_kernel<", "gemm_mx"),
+    ("moe::gemm_mx_wide_kernel<", "gemm_mx"),
     ("moe::quantize_kernel", "quantize"),
     ("moe::augment_routing_kernel", "shared_route"),
     ("moe::route_kernel", "router"),
@@ -76,8 +77,8 @@ def kernel_stage(name):
     name = name.replace("void ", "").split("(")[0]
     for prefix, stage in KERNEL_STAGES:
         if name.startswith(prefix):
-            if stage.startswith("gemm"):
-                return "gate_up" if ", true>" in name else "down"
+            if stage.startswith("gemm"):   # the last template argument is SWIGLU
+                return "gate_up" if name.rstrip().endswith("true>") else "down"
             return stage
     return None
 
