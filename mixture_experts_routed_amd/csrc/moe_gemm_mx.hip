@@ -41,7 +41,10 @@ __device__ __forceinline__ int lds_chunk4(int row, int chunk) { return chunk ^ (
 // h columns of one 32-wide MXFP8 block, whose row maximum is a reduction over
 // the 32 lanes that hold the columns.  Otherwise y bf16 [P, n_out] in expert
 // order.
-template <int BN, bool SWIGLU>
+// KS = 128-K sub-blocks per stage: with KS = 2 every weight row delivers a
+// whole 128-byte line of E2M1 codes per stage (and every token row 256 bytes)
+// instead of half a line.
+template <int BN, bool SWIGLU, int KS>
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
@@ -50,13 +53,19 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
     uint16_t* __restrict__ Cy) {
     constexpr int NB = BN / 64;                       // 32-row panel blocks per wave (WN = 2)
-    constexpr int A_PER = kMxBM * 8 / kMxThreads;     // 16-byte A chunks per thread and stage
-    constexpr int B_PER = BN * 4 / kMxThreads;        // 16-byte B chunks per thread and stage
-    static_assert(A_PER == 2 && B_PER >= 1 && (!SWIGLU || NB == 4), "tile shape");
-    __shared__ u32x4 a_lds[2][kMxBM][8];
-    __shared__ u32x4 b_lds[2][BN][4];
-    __shared__ uint32_t sa_lds[2][kMxBM];
-    __shared__ uint32_t sb_lds[2][BN];
+    constexpr int ACH = 8 * KS, BCH = 4 * KS;         // 16-byte chunks per A / B row and stage
+    constexpr int A_PER = kMxBM * ACH / kMxThreads;   // 16-byte A chunks per thread and stage
+    constexpr int B_PER = BN * BCH / kMxThreads;      // 16-byte B chunks per thread and stage
+    static_assert((KS == 1 || KS == 2) && B_PER >= 1 && (!SWIGLU || NB == 4), "tile shape");
+    __shared__ u32x4 a_lds[2][kMxBM][ACH];
+    __shared__ u32x4 b_lds[2][BN][BCH];
+    __shared__ uint32_t sa_lds[2][KS][kMxBM];
+    __shared__ uint32_t sb_lds[2][KS][BN];
+    // physical LDS chunk of logical chunk c of a row: KS = 1 as lds_chunk /
+    // lds_chunk4; KS = 2 rows are 256 (A) and 128 (B) bytes, so 16 and 8
+    // consecutive rows spread over the positions of a full-row XOR
+    auto a_phys = [](int r, int c) { return KS == 1 ? lds_chunk(r, c) : c ^ (r & 15); };
+    auto b_phys = [](int r, int c) { return KS == 1 ? lds_chunk4(r, c) : c ^ ((r >> 1) & 7); };
 
     // waves w and w + 4 share a SIMD: (wm, wn) = (w / 2, w % 2) puts the
     // waves of the first rows on four different SIMDs, so a tile of a few
@@ -67,7 +76,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
     const int items = ntiles * n_tiles_n;
-    const int nks = K / kMxBK;
+    const int nks = K / (kMxBK * KS);
     const int kb_row = K / 32;                        // scale bytes per row
 
     auto panel_row = [&](int rr, int nt) {
@@ -89,17 +98,17 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         const uint8_t* a_src[A_PER];
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
-            const int q = tid + kMxThreads * i;       // chunk id: row q / 8, chunk q % 8
-            const int r = q >> 3;
+            const int q = tid + kMxThreads * i;       // chunk id: row q / ACH, chunk q % ACH
+            const int r = q / ACH;
             int64_t arow = 0;
             if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
-            a_src[i] = A + arow * K + (q & 7) * 16;
+            a_src[i] = A + arow * K + (q % ACH) * 16;
         }
         const uint8_t* b_src[B_PER];
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
-            const int q = tid + kMxThreads * i;       // row q / 4, chunk q % 4
-            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q >> 2, nt)) * (K / 2) + (q & 3) * 16;
+            const int q = tid + kMxThreads * i;       // row q / BCH, chunk q % BCH
+            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q / BCH, nt)) * (K / 2) + (q % BCH) * 16;
         }
         // scale words: thread t < 128 -> A row t; 128 <= t < 128 + BN -> B row t - 128
         const bool sa_t = tid < kMxBM, sb_t = tid >= kMxBM && tid < kMxBM + BN;
@@ -122,53 +131,64 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         // stage ks, so that kMxRegStages stages stay in flight through every
         // product
         u32x4 ra[kMxRegStages][A_PER], rb[kMxRegStages][B_PER];
-        uint32_t rs[kMxRegStages];
+        uint32_t rs[kMxRegStages][KS];
 
-        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rs_, int ks) {
+        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS], int ks) {
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * kMxBK);
+            for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * (kMxBK * KS));
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
-            rs_ = *(const uint32_t*)(s_src + ks * 4);   // 4 scale bytes (blocks 4ks .. 4ks+3)
+            for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2 * KS));
+            // 4 scale bytes per 128-K sub-block (blocks 4 (KS ks + j) .. + 3)
+            if constexpr (KS == 1) {
+                rs_[0] = *(const uint32_t*)(s_src + ks * 4);
+            } else {   // two words (the scale tensors need only 4-byte alignment)
+                rs_[0] = *(const uint32_t*)(s_src + ks * 8);
+                rs_[1] = *(const uint32_t*)(s_src + ks * 8 + 4);
+            }
         };
-        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rs_, int ks) {
+        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS], int ks) {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) {
-                const int q = tid + kMxThreads * i, r = q >> 3;
-                a_lds[S][r][lds_chunk(r, q & 7)] = ra_[i];
+                const int q = tid + kMxThreads * i, r = q / ACH;
+                a_lds[S][r][a_phys(r, q % ACH)] = ra_[i];
             }
 #pragma unroll
             for (int i = 0; i < B_PER; ++i) {
-                const int q = tid + kMxThreads * i, r = q >> 2;
-                b_lds[S][r][lds_chunk4(r, q & 3)] = rb_[i];
+                const int q = tid + kMxThreads * i, r = q / BCH;
+                b_lds[S][r][b_phys(r, q % BCH)] = rb_[i];
             }
-            if (sa_t) sa_lds[S][tid] = rs_;
-            if (sb_t) sb_lds[S][tid - kMxBM] = rs_;
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                if (sa_t) sa_lds[S][j][tid] = rs_[j];
+                if (sb_t) sb_lds[S][j][tid - kMxBM] = rs_[j];
+            }
             lds_barrier();
             // refill (past the last stage: re-read the last one, an L2 hit)
             load(ra_, rb_, rs_, min(ks + kMxRegStages, nks - 1));
             if (active && ks < nks) {
                 const int ar = 32 * wm + (lane & 31);
-                const int asw = (ar >> 1) & 7;
-                const uint32_t sa = sa_lds[S][ar];
-                uint32_t sb[NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) sb[nb] = sb_lds[S][(wn * NB + nb) * 32 + (lane & 31)];
+                for (int j = 0; j < KS; ++j) {
+                    const uint32_t sa = sa_lds[S][j][ar];
+                    uint32_t sb[NB];
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {   // two 64-K MFMA chunks per stage
-                    const u32x4 lo = a_lds[S][ar][(4 * c + h) ^ asw];
-                    const u32x4 hi = a_lds[S][ar][(4 * c + 2 + h) ^ asw];
-                    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    const int shift = 8 * (2 * c + h);   // this lane's 32-K block
+                    for (int nb = 0; nb < NB; ++nb) sb[nb] = sb_lds[S][j][(wn * NB + nb) * 32 + (lane & 31)];
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const int br = (wn * NB + nb) * 32 + (lane & 31);
-                        const u32x4 bq = b_lds[S][br][lds_chunk4(br, 2 * c + h)];
-                        const u32x4 z = {0u, 0u, 0u, 0u};
-                        const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7));
-                        acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a, b, acc[nb], 0 /* A fp8 */, 4 /* B fp4 */, 0, (int)(sa >> shift), 0,
-                            (int)(sb[nb] >> shift));
+                    for (int c = 0; c < 2; ++c) {   // two 64-K MFMA chunks per 128-K sub-block
+                        const u32x4 lo = a_lds[S][ar][a_phys(ar, 8 * j + 4 * c + h)];
+                        const u32x4 hi = a_lds[S][ar][a_phys(ar, 8 * j + 4 * c + 2 + h)];
+                        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        const int shift = 8 * (2 * c + h);   // this lane's 32-K block
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const int br = (wn * NB + nb) * 32 + (lane & 31);
+                            const u32x4 bq = b_lds[S][br][b_phys(br, 4 * j + 2 * c + h)];
+                            const u32x4 z = {0u, 0u, 0u, 0u};
+                            const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7));
+                            acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                a, b, acc[nb], 0 /* A fp8 */, 4 /* B fp4 */, 0, (int)(sa >> shift), 0,
+                                (int)(sb[nb] >> shift));
+                        }
                     }
                 }
             }
@@ -421,9 +441,9 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
 
 int mx_tile_m() { return kMxBM; }
 
-template <int BN, bool SWIGLU>
+template <int BN, bool SWIGLU, int KS>
 static int mx_grid() {
-    static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU>, kMxThreads,
+    static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU, KS>, kMxThreads,
                                        device_cu_count());
     return g;
 }
@@ -448,9 +468,14 @@ hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* 
                    2 * F, k, hq, hs, (uint16_t*)nullptr);
         return hipGetLastError();
     }
-    MOE_LAUNCH((gemm_mx_kernel<256, true>), dim3(mx_grid<256, true>()), dim3(kMxThreads), 0, s, x, xs,
-               w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F, 2 * F,
-               k, hq, hs, (uint16_t*)nullptr);
+    if (H % 256 == 0)
+        MOE_LAUNCH((gemm_mx_kernel<256, true, 2>), dim3(mx_grid<256, true, 2>()), dim3(kMxThreads), 0,
+                   s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E,
+                   H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
+    else
+        MOE_LAUNCH((gemm_mx_kernel<256, true, 1>), dim3(mx_grid<256, true, 1>()), dim3(kMxThreads), 0,
+                   s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E,
+                   H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
     return hipGetLastError();
 }
 
@@ -461,13 +486,17 @@ hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w
         MOE_LAUNCH((gemm_mx_wide_kernel<false>), dim3(mx_wide_grid<false>()), dim3(kMxThreads), 0, s,
                    hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                    H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
+    else if (H % 256 == 0 && F % 256 == 0)
+        MOE_LAUNCH((gemm_mx_kernel<256, false, 2>), dim3(mx_grid<256, false, 2>()), dim3(kMxThreads), 0,
+                   s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+                   H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
     else if (H % 256 == 0)
-        MOE_LAUNCH((gemm_mx_kernel<256, false>), dim3(mx_grid<256, false>()), dim3(kMxThreads), 0, s,
-                   hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+        MOE_LAUNCH((gemm_mx_kernel<256, false, 1>), dim3(mx_grid<256, false, 1>()), dim3(kMxThreads), 0,
+                   s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                    H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
     else
-        MOE_LAUNCH((gemm_mx_kernel<128, false>), dim3(mx_grid<128, false>()), dim3(kMxThreads), 0, s,
-                   hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
+        MOE_LAUNCH((gemm_mx_kernel<128, false, 1>), dim3(mx_grid<128, false, 1>()), dim3(kMxThreads), 0,
+                   s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                    H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
     return hipGetLastError();
 }
