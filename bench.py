@@ -77,8 +77,9 @@ def kernel_stage(name):
     name = name.replace("void ", "").split("(")[0]
     for prefix, stage in KERNEL_STAGES:
         if name.startswith(prefix):
-            if stage.startswith("gemm"):   # the last template argument is SWIGLU
-                return "gate_up" if name.rstrip().endswith("true>") else "down"
+            if stage.startswith("gemm"):   # the bool template argument is SWIGLU
+                targs = name[name.find("<") + 1:name.rfind(">")].replace(" ", "").split(",")
+                return "gate_up" if "true" in targs else "down"
             return stage
     return None
 
