@@ -21,21 +21,23 @@
 
 namespace moe {
 
-constexpr int kMxThreads = 512;   // 8 waves, a 4 (M) x 2 (N) grid of 32 x 128 wave tiles
+constexpr int kMxThreads = 512;   // 8 waves
 constexpr int kMxBM = 128;        // rows of an M tile
-constexpr int kMxBK = 128;        // K elements per stage: 128 fp8 bytes, 64 fp4 bytes per row
+constexpr int kMxBK = 128;        // K elements of a sub-block: 128 fp8 bytes, 64 fp4 bytes per row
 constexpr int kMxRegStages = 2;   // stages of operands loading ahead in registers
 
 // LDS chunk (16 bytes) of a 64-byte fp4 row: 16 consecutive rows read at one
 // logical chunk land on 16 distinct 4-bank groups.
 __device__ __forceinline__ int lds_chunk4(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// One work item = (M tile of <= 128 rows of one expert) x (256 panel rows).
-// Per 128-K stage a thread stages 2 A chunks (token rows, fp8), 2 B chunks
-// (panel rows, fp4) and one scale word (4 E8M0 bytes: A scales for threads
-// 0-127, B scales for threads 128-383) in registers, two stages ahead, and
-// writes them into a 2-stage LDS ring.  Wave (wm, wn) owns tile rows
-// [32 wm, 32 wm + 32) and panel rows [128 wn, 128 wn + 128) as 4 blocks of 32.
+// One work item = (M tile of <= 128 rows of one expert) x (BN panel rows),
+// the 8 waves a 4 (M) x 2 (N) grid of 32 x BN/2 wave tiles.  Per stage of KS
+// 128-K sub-blocks a thread stages 2 KS A chunks (token rows, fp8), BN KS / 128
+// B chunks (panel rows, fp4) and KS scale words (4 E8M0 bytes each: A scales
+// for threads 0-127, B scales for threads 128-383) in registers, two stages
+// ahead, and writes them into a 2-stage LDS ring.  Wave (wm, wn) owns tile
+// rows [32 wm, 32 wm + 32) and panel rows [BN/2 wn, BN/2 (wn + 1)) as blocks
+// of 32.
 // SWIGLU: panel rows interleave gate/up in blocks of 32 (as the bf16 path), so
 // blocks (0, 1) and (2, 3) of a wave are (gate, up) pairs; each pair gives 32
 // h columns of one 32-wide MXFP8 block, whose row maximum is a reduction over
