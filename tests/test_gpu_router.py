@@ -190,3 +190,40 @@ def test_decode_routed(T, mode):
                                     residual=f64(res))
     err = np.abs(f64(out) - ref) / (1e-2 + 1e-2 * np.abs(ref))
     assert err.max() <= 1.0, err.max()
+
+
+@pytest.mark.parametrize("T", [33, 100])
+def test_route_plan_512_experts(T):
+    """E = 512 (eight scores per lane) on both the fused one-workgroup form
+    (T <= 64) and the two-launch form, 64 groups of 8, group_top 2."""
+    moe = _moe()
+    E, k = 512, 8
+    lg = _logits(T, E, 70 + T, torch.float32).cuda()
+    b = _bias(E, 71, torch.float32).cuda()
+    kw = dict(mode=moe.MOE_ROUTE_SIGMOID_GROUP, bias=b, num_groups=64, topk_group=6, group_top=2,
+              routed_scaling_factor=2.5)
+    idx, w, counts, offsets, perm, inv = moe.moe_route_plan(lg, k, **kw)
+    ri, rw = orc.route_sigmoid_group_topk(lg.double().cpu().numpy(), b.double().cpu().numpy(), k, 64, 6,
+                                          2.5, group_top=2)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6)
+    _check_plan(idx.cpu().numpy(), E, counts, offsets, perm, inv)
+
+
+def test_decode_routed_256_experts():
+    """Routing inside the decode kernel with 256 experts (four scores per
+    lane), T = 4, k = 8, group-aware sigmoid with 8 groups."""
+    import moe_workloads as wl
+    moe = _moe()
+    T, H, F, E, k = 4, 512, 256, 256, 8
+    p = wl.make_bf16_problem(T, H, F, E, k, 77, "cpu", weight_std=1 / 16)
+    g = {n: v.cuda() for n, v in p.items()}
+    lg = _logits(T, E, 78, torch.bfloat16).cuda()
+    b = _bias(E, 79, torch.bfloat16).cuda()
+    kw = dict(mode=moe.MOE_ROUTE_SIGMOID_GROUP, bias=b, num_groups=8, topk_group=4, group_top=2,
+              routed_scaling_factor=2.5)
+    out, idx, w = moe.moe_experts_decode_routed(g["hidden"], lg, g["gate_up"], g["down"], k, **kw)
+    i2, w2 = moe.moe_route_topk(lg, k, **kw)
+    assert torch.equal(idx, i2)
+    ref_out = moe.moe_experts_decode(g["hidden"], g["gate_up"], g["down"], idx, w, k)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
