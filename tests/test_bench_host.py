@@ -17,6 +17,12 @@ def test_kernel_stage_mapping():
     assert bench.kernel_stage("void moe::decode_slice_kernel<32, 3, 1>(x)") == "decode_slices"
     assert bench.kernel_stage("moe::decode_combine_kernel(x)") == "combine"
     assert bench.kernel_stage("moe::combine_kernel(x)") == "combine"
+    assert bench.kernel_stage("void moe::gemm_mx_kernel<256, true, 2>(unsigned char const*)") == "gate_up"
+    assert bench.kernel_stage("void moe::gemm_mx_kernel<256, false, 2>(x)") == "down"
+    assert bench.kernel_stage("void moe::gemm_mx_wide_kernel<true>(x)") == "gate_up"
+    assert bench.kernel_stage("void moe::gemm_mx_wide_kernel<false>(x)") == "down"
+    assert bench.kernel_stage("void moe::route_kernel<2>(moe::RouteArgs)") == "router"
+    assert bench.kernel_stage("void moe::route_plan_kernel<1>(moe::RouteArgs)") == "route_plan"
     assert bench.kernel_stage("__amd_rocclr_copyBuffer") is None
 
 
@@ -34,6 +40,10 @@ def test_stage_work_matches_the_layer_formula():
     # fp8: one byte per weight plus an fp32 scale per 128-wide block
     b8, _ = bench.stage_work("down", "fp8", 128, 7168, 2048, 8, touched=128, valid=1024)
     assert b8 == pytest.approx(128 * 7168 * 2048 * (1 + 4 / 128))
+    # mxfp4: half a byte per weight plus one E8M0 byte per 32
+    b4, f4 = bench.stage_work("gate_up", "mxfp4", 128, 7168, 2048, 8, touched=128, valid=1024)
+    assert b4 == pytest.approx(128 * 2 * 2048 * 7168 * (0.5 + 1 / 32) + 128 * 7168 * (1 + 1 / 32))
+    assert f4 == 2 * 1024 * 2 * 2048 * 7168
 
 
 def test_roofline_bound_follows_arithmetic_intensity():
