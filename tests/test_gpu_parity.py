@@ -236,6 +236,29 @@ def test_decode_dropped_slots_with_stale_workspace(T):
     check_tol(out, ref, BF16_TOL, f"dropped slots T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_decode_repeated_expert_in_token(T):
+    """Gather-GEMV path with a token that lists one expert in several slots
+    (each slot adds its own weighted copy of that expert's output), mixed with
+    a dropped slot, against the per-slot oracle."""
+    moe = _moe()
+    H, F, E, k = 256, 128, 8, 4
+    _say(f"decode repeated expert in a token, T={T}")
+    p = bf16_problem(T, H, F, E, k, seed=90 + T, std=1 / np.sqrt(H))
+    idx = p["top_k_index"].clone()
+    idx[0] = torch.tensor([3, 3, 5, 3], dtype=torch.int32)
+    if T > 1:
+        idx[T - 1] = torch.tensor([6, -1, 6, 2], dtype=torch.int32)
+    p["top_k_index"] = idx.contiguous()
+    ref = bf16_ref(p, batched=False)
+    g = to_gpu(p)
+    n = moe.moe_workspace_size(1, T, H, F, E, k)
+    ws = torch.full((n // 4,), float("nan"), device="cuda").view(torch.uint8)
+    out = moe.moe_experts_decode(g["hidden"], g["gate_up"], g["down"], g["top_k_index"],
+                                 g["top_k_weights"], k, workspace=ws)
+    check_tol(out, ref, BF16_TOL, f"repeated expert T={T}")
+
+
 def test_stages_prefill():
     """Layered check: h and y (bf16, both in expert order) in the workspace."""
     moe = _moe()
