@@ -308,9 +308,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
     const uint16_t* __restrict__ residual, int T, int k, int E, int H, int nslices,
     uint16_t* __restrict__ out) {
-    // per slot: the routing weight's bits (0 for a dropped slot) and a mask
-    // that is all ones for a valid slot, zero for a dropped one
-    __shared__ int2 wsl[kDecodeMaxSlots];
+    // per slot: the routing weight's bits (0 for a dropped slot), a mask
+    // that is all ones for a valid slot, zero for a dropped one, and the token
+    __shared__ int4 wsl[kDecodeMaxSlots];
     __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
     const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
     const int c = blockIdx.x * kCombCols + cl;
@@ -329,10 +329,14 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
         const int e = idx[sc];
         const float wv = wts[sc];
         const bool valid = (int)threadIdx.x < P && (unsigned)e < (unsigned)E;
-        wsl[threadIdx.x] = make_int2(valid ? __float_as_int(wv) : 0, valid ? -1 : 0);
+        wsl[threadIdx.x] = make_int4(valid ? __float_as_int(wv) : 0, valid ? -1 : 0, sc / k, 0);
     }
     __syncthreads();
     float acc[kDecodeMaxT] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // slot s and slice sl of pair g + kCombGroups j, stepped without
+    // divisions: each step adds dq slots and dr slices
+    const int dq = kCombGroups / nslices, dr = kCombGroups - dq * nslices;
+    int s = g / nslices, sl = g - s * nslices;
     for (int base = g; base < npairs; base += kCombGroups * kCombBatch) {
         if (base != g) {
 #pragma unroll
@@ -346,15 +350,20 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
             if (base + kCombGroups * i >= npairs) v[i] = 0.0f;
 #pragma unroll
         for (int i = 0; i < kCombBatch; ++i) {
-            const int pr = min(base + kCombGroups * i, npairs - 1);
-            const int s = pr / nslices, t = s / k;
             // a dropped slot's partial sums are never written: masked out,
-            // not multiplied by zero (stale memory may hold NaN)
-            const int2 ws = wsl[s];
+            // not multiplied by zero (stale memory may hold NaN); pairs past
+            // the end hold 0 and read the last slot's entry
+            const int4 ws = wsl[min(s, P - 1)];
             const float wv = __int_as_float(__float_as_int(v[i] * __int_as_float(ws.x)) & ws.y);
 #pragma unroll
             for (int tt = 0; tt < kDecodeMaxT; ++tt)
-                if (tt == t) acc[tt] += wv;
+                if (tt == ws.z) acc[tt] += wv;
+            sl += dr;
+            s += dq;
+            if (sl >= nslices) {
+                sl -= nslices;
+                ++s;
+            }
         }
     }
 #pragma unroll
