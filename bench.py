@@ -52,6 +52,10 @@ HBM_PEAK_GBS = 8000.0
 # weights; a scaled MFMA with an fp8 operand issues at the fp8 rate, so its
 # peak is fp8's (the fp4 figure holds for fp4 x fp4 only).
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0}
+# default warm-up: at least this much work before the timed steps (a GPU
+# under sustained load settles on its steady clocks after tens of ms)
+kWarmupSeconds = 0.1
+kWarmupMaxSteps = 1000
 # The model card's own decode figure for exactly this workload (T=1, H=1280,
 # F=896, 64 experts, top-6, bf16): 0.191 ms per call on an NVIDIA GB10.
 PAGE_DECODE_T1_TOKENS_PER_S = 1.0 / 0.191e-3
@@ -277,7 +281,9 @@ def main():
     S = cfg.get("S", 0)   # shared experts (every token, weight 1)
     decode = name.startswith("ocr2_decode") or name == "tiny"
     steps = args.steps if args.steps is not None else (200 if decode else (20 if kind == "bf16" else 10))
-    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    # warm-up: --warmup W steps exactly, else at least 20 steps and about
+    # kWarmupSeconds of work (pass A below)
+    warmup = args.warmup if args.warmup is not None else 20
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe._load()
@@ -304,14 +310,14 @@ def main():
 
             def step(i):
                 s = i % sets
-                idx, w = routes[i]
+                idx, w = routes[i % len(routes)]
                 return entry_sh(hidden, gu_sets[s], dn_sets[s], sgu_sets[s], sdn_sets[s], idx, w, k)
         else:
             entry = moe.moe_experts_decode if decode else moe.moe_experts_prefill
 
             def step(i):
                 s = i % sets
-                idx, w = routes[i]
+                idx, w = routes[i % len(routes)]
                 return entry(hidden, gu_sets[s], dn_sets[s], idx, w, k)
         dtype = "bf16"
     else:
@@ -328,9 +334,21 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- pass A: timing
+    # The GPU reaches its steady clocks only after tens of milliseconds of
+    # sustained load (a T=2048 bf16 prefill call runs about 20% faster then),
+    # so the default warm-up runs at least kWarmupSeconds of steps (at most
+    # kWarmupMaxSteps); the steps run are reported as "warmup".
+    t0 = time.perf_counter()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.warmup is None:
+        per_step = (time.perf_counter() - t0) / warmup
+        extra = min(kWarmupMaxSteps, max(warmup, int(kWarmupSeconds / per_step) + 1)) - warmup
+        for i in range(warmup, warmup + extra):
+            step(i)
+        warmup += extra
+        torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
@@ -344,7 +362,7 @@ def main():
     # ------------------------------------------------------ algorithmic work
     touched_l, valid_l = [], []
     for i in range(steps):
-        idx = routes[warmup + i][0].cpu().numpy().reshape(-1)
+        idx = routes[(warmup + i) % len(routes)][0].cpu().numpy().reshape(-1)
         valid = idx[(idx >= 0) & (idx < E)]
         touched_l.append(len(np.unique(valid)) + S)     # shared experts: every token
         valid_l.append(valid.size + T * S)
@@ -421,7 +439,8 @@ def main():
 
             def step_routed(i):
                 s_ = i % sets
-                return moe.moe_experts_decode_routed(hidden, logit_sets[i], gu_sets[s_], dn_sets[s_], k,
+                return moe.moe_experts_decode_routed(hidden, logit_sets[i % len(logit_sets)], gu_sets[s_],
+                                                     dn_sets[s_], k,
                                                      mode=moe.MOE_ROUTE_SOFTMAX,
                                                      routed_scaling_factor=cfg["routed_scale"])
             for i in range(warmup):
