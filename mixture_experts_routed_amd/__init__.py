@@ -15,7 +15,9 @@ top_k_index.int(), top_k_weights.float(), top_k)`` with gate_up_proj
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -109,12 +111,14 @@ def moe_strerror(status):
     return _load().moe_strerror(int(status)).decode()
 
 
+@functools.lru_cache(maxsize=4096)   # a pure function of its arguments; errors are not cached
 def moe_workspace_size(variant, T, H, F, E, k):
     n = ctypes.c_size_t(0)
     _check(_load().moe_workspace_size(variant, T, H, F, E, k, ctypes.byref(n)), "moe_workspace_size")
     return n.value
 
 
+@functools.lru_cache(maxsize=4096)
 def moe_workspace_size_shared(variant, T, H, F, E, k, S):
     """Workspace bytes of moe_experts_prefill_shared (variant 0) or
     moe_experts_decode_shared (variant 1)."""
@@ -179,12 +183,29 @@ def _workspace(nbytes, device, stream):
     return buf
 
 
+# Per-call host work is kept small (a decode call's GPU time is ~15-20 us):
+# pointers go to ctypes as plain integers, the stream handle is read without
+# building a stream object, and the device context is entered only when the
+# tensors are not on the current device.
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device):
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(device):
+    """Context making `device` current (a no-op when it already is)."""
+    return _SAME_DEVICE if device.index == torch.cuda.current_device() else torch.cuda.device(device)
 
 
 def _need(t, name, dtype, ndim, device=None):
@@ -241,7 +262,7 @@ def _bf16_call(entry, variant, hidden_states, gate_up_proj, down_proj, top_k_ind
     out = _out(out, T, H, dev)
     if T == 0:
         return out
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size(variant, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
@@ -294,7 +315,7 @@ def _shared_call(entry, variant, hidden_states, gate_up_proj, down_proj, shared_
     out = _out(out, T, H, dev)
     if T == 0:
         return out
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size_shared(variant, T, H, F, E, k, S)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
@@ -353,7 +374,7 @@ def _fp8_call(entry, variant, lead, gate_up, gate_up_scale, down, down_scale, to
     out = _out(out, T, H, dev)
     if T == 0:
         return out
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size(variant, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
@@ -421,7 +442,7 @@ def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_
     out = _out(out, T, H, dev)
     if T == 0:
         return out
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size(MOE_VARIANT_MXFP4, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
@@ -462,7 +483,7 @@ def moe_route_topk(logits, k, mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, t
     dev, T, E, idx, w, args = _route_args(logits, k, mode, bias, num_groups, topk_group, group_top)
     if T == 0:
         return idx, w
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = _load().moe_route_topk(*args, float(routed_scaling_factor), _ptr(idx), _ptr(w),
                                     ctypes.c_void_p(_stream(dev)))
     _check(rc, "moe_route_topk")
@@ -481,7 +502,7 @@ def moe_route_plan(logits, k, mode=MOE_ROUTE_SOFTMAX, bias=None, num_groups=1, t
     inv = torch.empty(P, dtype=torch.int32, device=dev)
     if T == 0:   # an empty batch: empty plan
         return idx, w, counts.zero_(), offsets.zero_(), perm, inv
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         ws = _workspace(moe_workspace_size(MOE_VARIANT_PLAN, T, 0, 0, E, int(k)), dev, stream)
         rc = _load().moe_route_plan(*args, float(routed_scaling_factor), _ptr(idx), _ptr(w),
@@ -516,7 +537,7 @@ def moe_experts_decode_routed(hidden_states, router_logits, gate_up_proj, down_p
     out = _out(out, T, H, dev)
     if T == 0:
         return out, idx, w
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size(MOE_VARIANT_DECODE, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
@@ -539,7 +560,7 @@ def moe_routing_plan(top_k_index, num_experts):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         stream = _stream(dev)
         need = moe_workspace_size(MOE_VARIANT_PLAN, T, 0, 0, E, k)
         ws = _workspace(need, dev, stream)
@@ -558,7 +579,7 @@ def moe_quantize_fp8_block128(t):
     rows, K = t.shape
     codes = torch.empty(rows, K, dtype=torch.uint8, device=t.device)
     scales = torch.empty(rows, max(K // 128, 0), dtype=torch.float32, device=t.device)
-    with torch.cuda.device(t.device):
+    with _on(t.device):
         rc = _load().moe_quantize_fp8_block128(_ptr(t), int(t.dtype == torch.bfloat16), rows, K,
                                                _ptr(codes), _ptr(scales),
                                                ctypes.c_void_p(_stream(t.device)))
