@@ -278,17 +278,19 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
         if (rc) return rc;
     }
     clock.mark(MOE_STAGE_PLAN);
+    const bool narrow = fp8_use_narrow(P, E, H, F);
     rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
                               at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
                               at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
-                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), fp8_tile_m(),
-                              stream));
+                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off),
+                              fp8_tile_m(narrow), stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_GATE_UP);
-    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, H, F, k, hq, hs, stream));
+    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, narrow, H, F, k, hq, hs,
+                                    stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, H, F, y, stream));
+    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, narrow, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
@@ -470,7 +472,7 @@ int moe_routing_plan(const int32_t* top_k_index, int64_t T, int k, int E, int32_
     if (T == 0) return MOE_OK;
     return launched(launch_plan(top_k_index, (int)(T * k), E, counts, offsets, perm, inv,
                                 at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                at<int32_t>(ws, L.tile_off), kMinTileM, stream));
+                                at<int32_t>(ws, L.tile_off), kPlanTileM, stream));
 }
 
 int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
@@ -614,7 +616,7 @@ int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mo
                                           topk_group, group_top, routed_scaling_factor,
                                           top_k_index, top_k_weights, counts, offsets, perm, inv,
                                           at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                          at<int32_t>(ws, L.tile_off), kMinTileM, stream));
+                                          at<int32_t>(ws, L.tile_off), kPlanTileM, stream));
     }
     clock.mark(MOE_STAGE_ROUTER);
     rc = launched(launch_route(logits, bias, logits_bf16, mode, T, E, k, num_groups, topk_group,
@@ -624,7 +626,7 @@ int moe_route_plan(const void* logits, const void* bias, int logits_bf16, int mo
     clock.mark(MOE_STAGE_PLAN);
     return launched(launch_plan(top_k_index, (int)(T * k), E, counts, offsets, perm, inv,
                                 at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                at<int32_t>(ws, L.tile_off), kMinTileM, stream));
+                                at<int32_t>(ws, L.tile_off), kPlanTileM, stream));
 }
 
 int moe_experts_decode_routed(const uint16_t* hidden, const void* logits, const void* bias,

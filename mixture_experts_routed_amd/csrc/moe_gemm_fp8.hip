@@ -59,11 +59,19 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     constexpr int WN = 8 / WM;
     constexpr int BM = 32 * WM;
     constexpr int NBW = BN / (32 * WN);
-    constexpr int A_PER = BM * 8 / kFp8Threads;
+    // 16-byte A chunks per thread and stage; a 32-row tile has 256 chunks for
+    // 512 threads, so threads 256..511 repeat those of threads 0..255 (same
+    // source, same LDS slot, same value)
+    constexpr int A_PER = BM * 8 >= kFp8Threads ? BM * 8 / kFp8Threads : 1;
     constexpr int B_PER = BN * 8 / kFp8Threads;
-    static_assert(WM * WN == 8 && NBW >= 1 && A_PER >= 1 && B_PER >= 1, "bad tile shape");
+    // SwiGLU: each wave holds PP (gate, up) block pairs = 32 PP h columns; a
+    // 128-wide h block (one E4M3 scale) spans WB = 4 / PP waves
+    constexpr int PP = NBW / 2;
+    constexpr int WB = PP > 0 ? 4 / PP : 1;
+    static_assert(WM * WN == 8 && NBW >= 1 && B_PER >= 1 && (BM * 8) % 256 == 0, "bad tile shape");
     static_assert(BM <= kFp8Threads && BN <= kFp8Threads, "one scale per thread");
-    static_assert(!SWIGLU || (BN == 256 && WN == 2), "the SwiGLU epilogue needs a 128-wide h block over 2 waves");
+    static_assert(!SWIGLU || (NBW % 2 == 0 && 4 % PP == 0 && WN % WB == 0),
+                  "the SwiGLU epilogue needs whole gate/up pairs and whole 128-wide h blocks");
     __shared__ u32x4 a_lds[2][BM][8];
     __shared__ u32x4 b_lds[2][BN][8];
     __shared__ __attribute__((aligned(16))) float sa_lds[2][BM];
@@ -73,6 +81,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
     const int chunk = tid & 7, row_t = tid >> 3;
+    const int a_row_t = row_t & (BM - 1);   // BM = 32: rows 32..63 repeat rows 0..31
     const int g = lane >> 5;
     const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32*b + lane%32
     const int ntiles = *ntiles_p;
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         const uint8_t* a_src[A_PER];
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
-            const int r = row_t + 64 * i;
+            const int r = a_row_t + 64 * i;
             int64_t arow = 0;
             if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
             a_src[i] = A + arow * K + chunk * 16;
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 #define MOE_FP8_STEP(S, RA, RB, RSA, RSB, KB)                                                  \
     do {                                                                                       \
         _Pragma("unroll") for (int i = 0; i < A_PER; ++i) {                                    \
-            const int rr = row_t + 64 * i;                                                     \
+            const int rr = a_row_t + 64 * i;                                                   \
             a_lds[S][rr][lds_chunk(rr, chunk)] = RA[i];                                        \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < B_PER; ++i) {                                    \
@@ -183,13 +192,14 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 #undef MOE_FP8_LOAD
 
         if (SWIGLU) {
-            // h for f = nt*128 + (wn*2 + p)*32 + lane%32, p = 0, 1
-            float hv[2][16];
+            // h for f = nt*(BN/2) + (wn*PP + p)*32 + lane%32, p < PP; wave wn's
+            // 128-wide h block is shared with the waves wb0 .. wb0 + WB - 1
+            float hv[PP > 0 ? PP : 1][16];
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 float m = 0.0f;
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
+                for (int p = 0; p < PP; ++p) {
                     hv[p][q] = silu(acc[2 * p][q]) * acc[2 * p + 1][q];
                     m = fmaxf(m, fabsf(hv[p][q]));
                 }
@@ -199,23 +209,27 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
             lds_barrier();
             if (active) {
                 const int nfb = n_out / 128;
+                const int wb0 = wn - wn % WB;
+                const int hblk = nt * (BN / 256) + wn / WB;
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int row = 32 * wm + acc_row(q, lane);
-                    const float amax = fmaxf(amax_lds[0][row], amax_lds[1][row]);
+                    float amax = amax_lds[wb0][row];
+#pragma unroll
+                    for (int j = 1; j < WB; ++j) amax = fmaxf(amax, amax_lds[wb0 + j][row]);
                     const bool zero = !(amax > 0.0f);
                     const float scale = zero ? 1.0f : amax / 448.0f;
                     const float mul = zero ? 0.0f : 448.0f / amax;
-                    float qv[2];
+                    float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int p = 0; p < 2; ++p)
+                    for (int p = 0; p < PP; ++p)
                         qv[p] = zero ? 0.0f : fminf(fmaxf(hv[p][q] * mul, -448.0f), 448.0f);
-                    const uint32_t codes = f32x4_to_e4m3x4(qv[0], qv[1], 0.0f, 0.0f);
+                    const uint32_t codes = f32x4_to_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
                     if (row < mrows) {
-                        uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + nt * 128 + wn * 64 + (lane & 31);
-                        dst[0] = (uint8_t)codes;
-                        dst[32] = (uint8_t)(codes >> 8);
-                        if (wn == 0 && (lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + nt] = scale;
+                        uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + nt * (BN / 2) + wn * PP * 32 + (lane & 31);
+#pragma unroll
+                        for (int p = 0; p < PP; ++p) dst[32 * p] = (uint8_t)(codes >> (8 * p));
+                        if (wn % WB == 0 && (lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + hblk] = scale;
                     }
                 }
             }
@@ -238,8 +252,18 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 
 constexpr int kFp8WM = 4;  // 4 x 2 waves: 128-row M tiles
 constexpr int kFp8TileM = 32 * kFp8WM;
+// Decode batches (at most 16 rows per expert on average): 32-row M tiles and
+// 512-row panels on 1 x 8 waves (32 x 64 each, one gate/up pair).  A 128-row
+// tile would be mostly padding, and its accumulators would hold the registers
+// that here stage twice the weight bytes per stage (two stages of 64 KB in
+// flight per CU instead of 32 KB), which the weight stream is bound by.
+constexpr int kFp8NarrowTileM = 32;
 
-int fp8_tile_m() { return kFp8TileM; }
+bool fp8_use_narrow(int64_t P, int E, int H, int F) {
+    return P <= 16 * (int64_t)E && F % 256 == 0 && H % 512 == 0;
+}
+
+int fp8_tile_m(bool narrow) { return narrow ? kFp8NarrowTileM : kFp8TileM; }
 
 template <int WM, int BN, bool SWIGLU>
 static int fp8_grid() {
@@ -249,8 +273,14 @@ static int fp8_grid() {
 }
 
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
-                             const float* w13s, const GroupedPlan& pl, int H, int F, int k,
-                             uint8_t* hq, float* hs, hipStream_t s) {
+                             const float* w13s, const GroupedPlan& pl, bool narrow, int H, int F,
+                             int k, uint8_t* hq, float* hs, hipStream_t s) {
+    if (narrow) {
+        MOE_LAUNCH((gemm_fp8_kernel<1, 512, true>), dim3(fp8_grid<1, 512, true>()), dim3(kFp8Threads),
+                   0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets,
+                   pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
+        return hipGetLastError();
+    }
     MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, true>), dim3(fp8_grid<kFp8WM, 256, true>()),
                        dim3(kFp8Threads), 0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles,
                        pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
@@ -258,8 +288,13 @@ hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
-                           const GroupedPlan& pl, int H, int F, uint16_t* y, hipStream_t s) {
-    if (H % 256 == 0)
+                           const GroupedPlan& pl, bool narrow, int H, int F, uint16_t* y,
+                           hipStream_t s) {
+    if (narrow)
+        MOE_LAUNCH((gemm_fp8_kernel<1, 512, false>), dim3(fp8_grid<1, 512, false>()),
+                   dim3(kFp8Threads), 0, s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles,
+                   pl.tile_off, pl.offsets, pl.E, F, H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
+    else if (H % 256 == 0)
         MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, false>),
                            dim3(fp8_grid<kFp8WM, 256, false>()), dim3(kFp8Threads), 0, s, hq, hs,
                            w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,

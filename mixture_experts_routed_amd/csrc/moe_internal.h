@@ -30,9 +30,14 @@ LaunchTiming& launch_timing();  // per host thread
 
 // The plan cuts every expert's rows into M tiles of at most tile_m rows
 // (the grouped products' tile height; never below kMinTileM).
-constexpr int kMinTileM = 128;
+constexpr int kMinTileM = 32;
+// Tile height of the stand-alone plan entry points (their tile list is not
+// read by any product).
+constexpr int kPlanTileM = 128;
 int bf16_tile_m();
-int fp8_tile_m();
+// fp8 decode batches take 32-row tiles (fp8_use_narrow), others 128.
+bool fp8_use_narrow(int64_t P, int E, int H, int F);
+int fp8_tile_m(bool narrow);
 
 // Largest number of M tiles a plan over P slots and E experts can produce.
 inline int64_t max_m_tiles(int64_t P, int E) { return (P + kMinTileM - 1) / kMinTileM + E; }
@@ -144,11 +149,12 @@ hipError_t launch_decode_combine(const float* part, const int32_t* idx, const fl
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
-                             const float* w13s, const GroupedPlan& plan, int H, int F, int k,
-                             uint8_t* hq, float* hs, hipStream_t s);
+                             const float* w13s, const GroupedPlan& plan, bool narrow, int H, int F,
+                             int k, uint8_t* hq, float* hs, hipStream_t s);
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
-                           const GroupedPlan& plan, int H, int F, uint16_t* y, hipStream_t s);
+                           const GroupedPlan& plan, bool narrow, int H, int F, uint16_t* y,
+                           hipStream_t s);
 
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
                                float* scales, hipStream_t s);

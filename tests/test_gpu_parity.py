@@ -372,7 +372,31 @@ def test_fp8_medium(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 256, 256, 4, 2)])
+# (T, H, F, E, k, hot): decode batches (at most 16 rows per expert on average,
+# F % 256 == 0, H % 512 == 0) take 32-row tiles and 512-row panels; `hot`
+# tokens all choose expert 0 first, so that it spans several 32-row tiles
+@pytest.mark.parametrize("shape", [(48, 512, 256, 16, 4, 0), (64, 1024, 512, 8, 2, 40),
+                                   (16, 512, 768, 32, 8, 0)])
+def test_fp8_decode_batch_tiles(shape):
+    T, H, F, E, k, hot = shape
+    _say(f"fp8 decode batch {shape}")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=57 + T, routing="uniform_softmax", routed_scale=1.0)
+    if hot:
+        idx = p["top_k_index"].clone()
+        for t in range(hot):
+            row = idx[t]
+            row[row == 0] = row[0].clone()   # keep the k ids distinct
+            row[0] = 0
+        p["top_k_index"] = idx.contiguous()
+        assert int((p["top_k_index"] == 0).sum()) >= hot
+    ref = fp8_ref({n: v.numpy() if n not in ("x", "x_scale", "top_k_index", "top_k_weights") else v
+                   for n, v in p.items()})
+    worst, rel = check_tol(run_fp8(to_gpu(p)), ref, FP8_TOL, str(shape))
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("shape", [(200, 256, 256, 4, 2), (512, 256, 256, 4, 2),
+                                   (40, 512, 512, 8, 2)])   # decode-batch tiles: 4 waves per h block
 def test_fp8_h_stage_codes(shape):
     """The re-quantised h in the workspace against the oracle's fp32 rule applied
     to the oracle's h.  The kernel quantises its own fp32-accumulated h, which
