@@ -324,19 +324,20 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
     uint16_t* y = at<uint16_t>(ws, L.y);
     StageClock clock(stream);
     clock.mark(MOE_STAGE_PLAN);
+    const bool narrow = mx_use_narrow(P, E, H, F);
     rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
                               at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
                               at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
-                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off), mx_tile_m(),
-                              stream));
+                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off),
+                              mx_tile_m(narrow), stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_GATE_UP);
-    const bool wide = mx_use_wide(P, E, H, F);
-    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, wide, H, F, k, hq, hs,
-                                   stream));
+    const bool wide = !narrow && mx_use_wide(P, E, H, F);
+    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, wide, narrow, H, F, k,
+                                   hq, hs, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, wide, H, F, y, stream));
+    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, wide, narrow, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,

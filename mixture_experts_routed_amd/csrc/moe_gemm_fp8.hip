@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 
 constexpr int kFp8WM = 4;  // 4 x 2 waves: 128-row M tiles
 constexpr int kFp8TileM = 32 * kFp8WM;
-// Decode batches (at most 16 rows per expert on average): 32-row M tiles and
+// Decode batches (at most 32 rows per expert on average): 32-row M tiles and
 // 512-row panels on 1 x 8 waves (32 x 64 each, one gate/up pair).  A 128-row
 // tile would be mostly padding, and its accumulators would hold the registers
 // that here stage twice the weight bytes per stage (two stages of 64 KB in
@@ -260,7 +260,7 @@ constexpr int kFp8TileM = 32 * kFp8WM;
 constexpr int kFp8NarrowTileM = 32;
 
 bool fp8_use_narrow(int64_t P, int E, int H, int F) {
-    return P <= 16 * (int64_t)E && F % 256 == 0 && H % 512 == 0;
+    return P <= 32 * (int64_t)E && F % 256 == 0 && H % 512 == 0;
 }
 
 int fp8_tile_m(bool narrow) { return narrow ? kFp8NarrowTileM : kFp8TileM; }

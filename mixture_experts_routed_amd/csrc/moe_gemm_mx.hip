@@ -46,7 +46,10 @@ __device__ __forceinline__ int lds_chunk4(int row, int chunk) { return chunk ^ (
 // KS = 128-K sub-blocks per stage: with KS = 2 every weight row delivers a
 // whole 128-byte line of E2M1 codes per stage (and every token row 256 bytes)
 // instead of half a line.
-template <int BN, bool SWIGLU, int KS>
+// WM = 1 (decode batches): one 32-row block, the 8 waves side by side over a
+// 512-row panel (32 x 64 each, one gate/up pair); every thread then stages the
+// scale words of panel row t and of tile row t % 32.
+template <int BN, bool SWIGLU, int KS, int WM = 4>
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
@@ -54,14 +57,17 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
     int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
     uint16_t* __restrict__ Cy) {
-    constexpr int NB = BN / 64;                       // 32-row panel blocks per wave (WN = 2)
+    constexpr int BM = 32 * WM, WN = 8 / WM;
+    constexpr int NB = BN / (32 * WN);                // 32-row panel blocks per wave
     constexpr int ACH = 8 * KS, BCH = 4 * KS;         // 16-byte chunks per A / B row and stage
-    constexpr int A_PER = kMxBM * ACH / kMxThreads;   // 16-byte A chunks per thread and stage
+    constexpr int A_PER = BM * ACH / kMxThreads;      // 16-byte A chunks per thread and stage
     constexpr int B_PER = BN * BCH / kMxThreads;      // 16-byte B chunks per thread and stage
-    static_assert((KS == 1 || KS == 2) && B_PER >= 1 && (!SWIGLU || NB == 4), "tile shape");
-    __shared__ u32x4 a_lds[2][kMxBM][ACH];
+    static_assert((KS == 1 || KS == 2) && (WM == 4 || WM == 1) && A_PER >= 1 && B_PER >= 1 &&
+                  (!SWIGLU || NB % 2 == 0) && (WM == 4 ? BM + BN <= kMxThreads : BN == kMxThreads),
+                  "tile shape");
+    __shared__ u32x4 a_lds[2][BM][ACH];
     __shared__ u32x4 b_lds[2][BN][BCH];
-    __shared__ uint32_t sa_lds[2][KS][kMxBM];
+    __shared__ uint32_t sa_lds[2][KS][BM];
     __shared__ uint32_t sb_lds[2][KS][BN];
     // physical LDS chunk of logical chunk c of a row: KS = 1 as lds_chunk /
     // lds_chunk4; KS = 2 rows are 256 (A) and 128 (B) bytes, so 16 and 8
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     // waves of the first rows on four different SIMDs, so a tile of a few
     // rows (decode batches) still spreads its products over the CU
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = WM == 4 ? wave >> 1 : 0, wn = WM == 4 ? wave & 1 : wave;
     const int h = lane >> 5;
     const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
         const int nt = gi.nt, e = gi.e;
         const int row0 = tiles[2 * gi.mt + 1];
-        const int mrows = min(kMxBM, offsets[e + 1] - row0);
+        const int mrows = min(BM, offsets[e + 1] - row0);
         const bool active = 32 * wm < mrows;
 
         // sources (rows past the tile's end read row 0, never stored)
@@ -112,16 +118,20 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
             const int q = tid + kMxThreads * i;       // row q / BCH, chunk q % BCH
             b_src[i] = B + ((int64_t)e * b_rows + panel_row(q / BCH, nt)) * (K / 2) + (q % BCH) * 16;
         }
-        // scale words: thread t < 128 -> A row t; 128 <= t < 128 + BN -> B row t - 128
-        const bool sa_t = tid < kMxBM, sb_t = tid >= kMxBM && tid < kMxBM + BN;
+        // scale words: WM = 4: thread t < 128 -> A row t, 128 <= t < 128 + BN
+        // -> B row t - 128; WM = 1: B row t (s_src) and A row t % 32 (sa_src)
+        const bool sa_t = tid < BM, sb_t = WM == 4 ? tid >= BM && tid < BM + BN : true;
         const uint8_t* s_src;
+        const uint8_t* sa_src;
         {
-            const int r = sa_t ? tid : 0;
+            const int r = WM == 4 ? (sa_t ? tid : 0) : (tid & (BM - 1));
             int64_t arow = 0;
-            if (sa_t && r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
+            if ((WM == 1 || sa_t) && r < mrows)
+                arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
             const uint8_t* sa = As + arow * kb_row;
-            const uint8_t* sb = Bs + ((int64_t)e * b_rows + panel_row(sb_t ? tid - kMxBM : 0, nt)) * kb_row;
-            s_src = sb_t ? sb : sa;
+            const uint8_t* sb = Bs + ((int64_t)e * b_rows + panel_row(sb_t ? (WM == 4 ? tid - BM : tid) : 0, nt)) * kb_row;
+            s_src = WM == 4 ? (sb_t ? sb : sa) : sb;
+            sa_src = sa;
         }
 
         f32x16 acc[NB];
@@ -134,8 +144,10 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         // product
         u32x4 ra[kMxRegStages][A_PER], rb[kMxRegStages][B_PER];
         uint32_t rs[kMxRegStages][KS];
+        uint32_t rsa[kMxRegStages][KS];   // WM = 1 only: the A word
 
-        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS], int ks) {
+        auto load = [&](u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS],
+                        uint32_t (&rsa_)[KS], int ks) {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * (kMxBK * KS));
 #pragma unroll
@@ -143,12 +155,18 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
             // 4 scale bytes per 128-K sub-block (blocks 4 (KS ks + j) .. + 3)
             if constexpr (KS == 1) {
                 rs_[0] = *(const uint32_t*)(s_src + ks * 4);
+                if constexpr (WM == 1) rsa_[0] = *(const uint32_t*)(sa_src + ks * 4);
             } else {   // two words (the scale tensors need only 4-byte alignment)
                 rs_[0] = *(const uint32_t*)(s_src + ks * 8);
                 rs_[1] = *(const uint32_t*)(s_src + ks * 8 + 4);
+                if constexpr (WM == 1) {
+                    rsa_[0] = *(const uint32_t*)(sa_src + ks * 8);
+                    rsa_[1] = *(const uint32_t*)(sa_src + ks * 8 + 4);
+                }
             }
         };
-        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS], int ks) {
+        auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t (&rs_)[KS],
+                        uint32_t (&rsa_)[KS], int ks) {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) {
                 const int q = tid + kMxThreads * i, r = q / ACH;
@@ -161,12 +179,17 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
             }
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                if (sa_t) sa_lds[S][j][tid] = rs_[j];
-                if (sb_t) sb_lds[S][j][tid - kMxBM] = rs_[j];
+                if constexpr (WM == 4) {
+                    if (sa_t) sa_lds[S][j][tid] = rs_[j];
+                    if (sb_t) sb_lds[S][j][tid - BM] = rs_[j];
+                } else {
+                    sb_lds[S][j][tid] = rs_[j];
+                    if (sa_t) sa_lds[S][j][tid] = rsa_[j];
+                }
             }
             lds_barrier();
             // refill (past the last stage: re-read the last one, an L2 hit)
-            load(ra_, rb_, rs_, min(ks + kMxRegStages, nks - 1));
+            load(ra_, rb_, rs_, rsa_, min(ks + kMxRegStages, nks - 1));
             if (active && ks < nks) {
                 const int ar = 32 * wm + (lane & 31);
 #pragma unroll
@@ -197,21 +220,21 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
         };
 
         static_assert(kMxRegStages == 2, "one register buffer per LDS stage");
-        load(ra[0], rb[0], rs[0], 0);
-        load(ra[1], rb[1], rs[1], min(1, nks - 1));
+        load(ra[0], rb[0], rs[0], rsa[0], 0);
+        load(ra[1], rb[1], rs[1], rsa[1], min(1, nks - 1));
         for (int ks = 0; ks < nks; ks += 2) {
             // unconditional (an odd last step computes nothing): a path that
             // skipped it would leave the compiler's wait counts pessimistic
-            step(0, ra[0], rb[0], rs[0], ks);
-            step(1, ra[1], rb[1], rs[1], ks + 1);
+            step(0, ra[0], rb[0], rs[0], rsa[0], ks);
+            step(1, ra[1], rb[1], rs[1], rsa[1], ks + 1);
         }
 
         if (SWIGLU) {
-            // h for f = nt*128 + (wn*2 + p)*32 + lane%32; one MXFP8 block per p
+            // h for f = nt*(BN/2) + (wn*NB/2 + p)*32 + lane%32; one MXFP8 block per p
             const int nfb = n_out / 32;
             if (active) {
 #pragma unroll
-                for (int p = 0; p < 2; ++p)
+                for (int p = 0; p < NB / 2; ++p)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const float hv = silu_fast(acc[2 * p][q]) * acc[2 * p + 1][q];
@@ -224,7 +247,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
                         const uint32_t code = f32x4_to_e4m3x4(v, 0.0f, 0.0f, 0.0f);
                         const int row = 32 * wm + acc_row(q, lane);
                         if (row < mrows) {
-                            const int blk = nt * 4 + wn * 2 + p;
+                            const int blk = nt * (BN / 64) + wn * (NB / 2) + p;
                             Cq[(int64_t)(row0 + row) * n_out + blk * 32 + (lane & 31)] = (uint8_t)code;
                             if ((lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + blk] = (uint8_t)(se + 127);
                         }
@@ -441,11 +464,19 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
     }
 }
 
-int mx_tile_m() { return kMxBM; }
+// Decode batches (at most 32 rows per expert on average, K a multiple of 256
+// for both products): 32-row tiles over 512-row panels, gemm_mx_kernel with
+// WM = 1.  A 128-row tile would be mostly padding rows whose staging
+// registers here hold twice the weight bytes in flight.
+bool mx_use_narrow(int64_t P, int E, int H, int F) {
+    return P <= 32 * (int64_t)E && H % 512 == 0 && F % 256 == 0;
+}
 
-template <int BN, bool SWIGLU, int KS>
+int mx_tile_m(bool narrow) { return narrow ? 32 : kMxBM; }
+
+template <int BN, bool SWIGLU, int KS, int WM = 4>
 static int mx_grid() {
-    static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU, KS>, kMxThreads,
+    static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU, KS, WM>, kMxThreads,
                                        device_cu_count());
     return g;
 }
@@ -462,8 +493,14 @@ bool mx_use_wide(int64_t P, int E, int H, int F) {
 }
 
 hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
-                            const uint8_t* w13s, const GroupedPlan& pl, bool wide, int H, int F,
-                            int k, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+                            const uint8_t* w13s, const GroupedPlan& pl, bool wide, bool narrow, int H,
+                            int F, int k, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+    if (narrow) {
+        MOE_LAUNCH((gemm_mx_kernel<512, true, 2, 1>), dim3(mx_grid<512, true, 2, 1>()), dim3(kMxThreads),
+                   0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E,
+                   H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
+        return hipGetLastError();
+    }
     if (wide) {
         MOE_LAUNCH((gemm_mx_wide_kernel<true>), dim3(mx_wide_grid<true>()), dim3(kMxThreads), 0, s, x,
                    xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, H, F,
@@ -482,9 +519,13 @@ hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* 
 }
 
 hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2, const uint8_t* w2s,
-                          const GroupedPlan& pl, bool wide, int H, int F, uint16_t* y,
+                          const GroupedPlan& pl, bool wide, bool narrow, int H, int F, uint16_t* y,
                           hipStream_t s) {
-    if (wide)
+    if (narrow)
+        MOE_LAUNCH((gemm_mx_kernel<512, false, 2, 1>), dim3(mx_grid<512, false, 2, 1>()),
+                   dim3(kMxThreads), 0, s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off,
+                   pl.offsets, pl.E, F, H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);
+    else if (wide)
         MOE_LAUNCH((gemm_mx_wide_kernel<false>), dim3(mx_wide_grid<false>()), dim3(kMxThreads), 0, s,
                    hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
                    H, H, 1, (uint8_t*)nullptr, (uint8_t*)nullptr, y);

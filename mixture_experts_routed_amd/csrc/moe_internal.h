@@ -35,7 +35,8 @@ constexpr int kMinTileM = 32;
 // read by any product).
 constexpr int kPlanTileM = 128;
 int bf16_tile_m();
-// fp8 decode batches take 32-row tiles (fp8_use_narrow), others 128.
+// fp8 decode batches (at most 32 rows per expert on average) take 32-row
+// tiles (fp8_use_narrow), others 128.
 bool fp8_use_narrow(int64_t P, int E, int H, int F);
 int fp8_tile_m(bool narrow);
 
@@ -164,15 +165,18 @@ hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int
 // (hq [P, F] E4M3, hs [P, F/32] E8M0, expert order), and down -> y bf16
 // [P, H] in expert order.  H, F multiples of 128 (F also of 128 per h tile).
 // `wide` (mx_use_wide: many rows per expert, F % 256 == 0, H % 512 == 0)
-// selects 128 x 512 tiles of 64 x 128 wave tiles instead of 128 x 256 tiles.
-int mx_tile_m();
+// selects 128 x 512 tiles of 64 x 128 wave tiles instead of 128 x 256 tiles;
+// `narrow` (mx_use_narrow: decode batches, H % 512 == 0, F % 256 == 0) 32-row
+// tiles over 512-row panels.  The plan's tile height is mx_tile_m(narrow).
+bool mx_use_narrow(int64_t P, int E, int H, int F);
+int mx_tile_m(bool narrow);
 bool mx_use_wide(int64_t P, int E, int H, int F);
 hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
-                            const uint8_t* w13s, const GroupedPlan& plan, bool wide, int H, int F,
-                            int k, uint8_t* hq, uint8_t* hs, hipStream_t s);
+                            const uint8_t* w13s, const GroupedPlan& plan, bool wide, bool narrow,
+                            int H, int F, int k, uint8_t* hq, uint8_t* hs, hipStream_t s);
 hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2,
-                          const uint8_t* w2s, const GroupedPlan& plan, bool wide, int H, int F,
-                          uint16_t* y, hipStream_t s);
+                          const uint8_t* w2s, const GroupedPlan& plan, bool wide, bool narrow, int H,
+                          int F, uint16_t* y, hipStream_t s);
 
 // Routers (logits -> ids, weights), alone or followed by the plan in the
 // same launch (one workgroup; small batches).

@@ -372,7 +372,7 @@ def test_fp8_medium(shape):
     _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-# (T, H, F, E, k, hot): decode batches (at most 16 rows per expert on average,
+# (T, H, F, E, k, hot): decode batches (at most 32 rows per expert on average,
 # F % 256 == 0, H % 512 == 0) take 32-row tiles and 512-row panels; `hot`
 # tokens all choose expert 0 first, so that it spans several 32-row tiles
 @pytest.mark.parametrize("shape", [(48, 512, 256, 16, 4, 0), (64, 1024, 512, 8, 2, 40),
