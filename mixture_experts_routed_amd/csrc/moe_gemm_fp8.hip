@@ -132,8 +132,13 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     do {                                                                                       \
         _Pragma("unroll") for (int i = 0; i < A_PER; ++i) RA[i] =                              \
             *(const u32x4*)(a_src[i] + (KB) * kFp8BK);                                         \
-        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) RB[i] =                              \
-            *(const u32x4*)(b_src + i * b_step + (KB) * kFp8BK);                               \
+        /* decode batches (WM == 1) read each weight panel once: non-temporal, */         \
+        /* so that the stream does not push the scale rows out of L2 */                   \
+        _Pragma("unroll") for (int i = 0; i < B_PER; ++i) {                                    \
+            const u32x4* src_ = (const u32x4*)(b_src + i * b_step + (KB) * kFp8BK);            \
+            if constexpr (WM == 1) RB[i] = __builtin_nontemporal_load(src_);                   \
+            else RB[i] = *src_;                                                                \
+        }                                                                                      \
         RSA = as_src[KB];                                                                      \
         RSB = bs_src[KB];                                                                      \
     } while (0)

@@ -151,7 +151,13 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) ra_[i] = *(const u32x4*)(a_src[i] + ks * (kMxBK * KS));
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2 * KS));
+            for (int i = 0; i < B_PER; ++i) {
+                // decode batches read each weight panel once: non-temporal,
+                // so that the stream does not push the E8M0 rows out of L2
+                const uint8_t* src = b_src[i] + ks * (kMxBK / 2 * KS);
+                if constexpr (WM == 1) rb_[i] = __builtin_nontemporal_load((const u32x4*)src);
+                else rb_[i] = *(const u32x4*)src;
+            }
             // 4 scale bytes per 128-K sub-block (blocks 4 (KS ks + j) .. + 3)
             if constexpr (KS == 1) {
                 rs_[0] = *(const uint32_t*)(s_src + ks * 4);
