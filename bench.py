@@ -81,9 +81,10 @@ def kernel_stage(name):
     name = name.replace("void ", "").split("(")[0]
     for prefix, stage in KERNEL_STAGES:
         if name.startswith(prefix):
-            if stage.startswith("gemm"):   # the bool template argument is SWIGLU
+            if stage.startswith("gemm"):   # the first bool template argument is SWIGLU
                 targs = name[name.find("<") + 1:name.rfind(">")].replace(" ", "").split(",")
-                return "gate_up" if "true" in targs else "down"
+                flags = [t for t in targs if t in ("true", "false")]
+                return "gate_up" if flags and flags[0] == "true" else "down"
             return stage
     return None
 

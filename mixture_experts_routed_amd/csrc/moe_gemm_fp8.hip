@@ -39,8 +39,9 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
 // = (M tile of <= BM = 32*WM rows of one expert) x (BN panel rows); waves
 // form a WM x WN grid, wave (wm, wn) owns rows [32wm, 32wm+32) and 32*NBW
 // panel rows.  A 128-byte K step is one scale block.  The A bytes, the B
-// panel and both operands' per-row scales go through a 2-stage LDS ring fed
-// by branch-free look-ahead loads two k-steps ahead.  Per block, two
+// panel and both operands' per-row scales go through an LDS ring (2 stages;
+// 8 scale slots under SQ) fed by branch-free look-ahead loads two k-steps
+// ahead.  Per block, two
 // 32x32x64 MFMAs fill a fresh fp32 temporary that is promoted with
 // scale_a[row] * scale_b[col] into the accumulator.
 // SWIGLU: panel rows interleave gate/up in blocks of 32 (as the bf16 path);
@@ -48,7 +49,12 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
 // waves, which exchange per-row partial maxima through LDS before the
 // block-128 re-quantisation.  Otherwise: y bf16 in expert order (row m of
 // the plan holds slot perm[m]).
-template <int WM, int BN, bool SWIGLU>
+// SQ (K a multiple of 512): each thread reads its row's scales for four
+// K blocks with one 16-byte load every fourth step into an 8-slot LDS ring.
+// A scale read touches one cache line per row, against one line per eight
+// lanes for the operand bytes, so one 4-byte read per step doubled the
+// cache-line requests of a stage; SQ cuts that to a quarter.
+template <int WM, int BN, bool SWIGLU, bool SQ>
 __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, const int32_t* __restrict__ perm,
@@ -74,8 +80,9 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                   "the SwiGLU epilogue needs whole gate/up pairs and whole 128-wide h blocks");
     __shared__ u32x4 a_lds[2][BM][8];
     __shared__ u32x4 b_lds[2][BN][8];
-    __shared__ __attribute__((aligned(16))) float sa_lds[2][BM];
-    __shared__ float sb_lds[2][BN];
+    constexpr int SR = SQ ? 8 : 2;  // scale ring slots
+    __shared__ __attribute__((aligned(16))) float sa_lds[SR][BM];
+    __shared__ float sb_lds[SR][BN];
     __shared__ float amax_lds[SWIGLU ? WN : 1][SWIGLU ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -126,9 +133,10 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x16{};
         u32x4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
-        float rsa0, rsa1, rsb0, rsb1;
+        float rsa0, rsa1, rsb0, rsb1;  // !SQ: the scales of one step
+        float4 qa, qb;                 // SQ: the scales of four steps
 
-#define MOE_FP8_LOAD(RA, RB, RSA, RSB, KB)                                                     \
+#define MOE_FP8_LOAD(RA, RB, KB)                                                               \
     do {                                                                                       \
         _Pragma("unroll") for (int i = 0; i < A_PER; ++i) RA[i] =                              \
             *(const u32x4*)(a_src[i] + (KB) * kFp8BK);                                         \
@@ -139,11 +147,10 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
             if constexpr (WM == 1) RB[i] = __builtin_nontemporal_load(src_);                   \
             else RB[i] = *src_;                                                                \
         }                                                                                      \
-        RSA = as_src[KB];                                                                      \
-        RSB = bs_src[KB];                                                                      \
     } while (0)
 
-#define MOE_FP8_STEP(S, RA, RB, RSA, RSB, KB)                                                  \
+    /* J = KB % 4 (SQ); the scales of step KB sit in ring slot SS */                          \
+#define MOE_FP8_STEP(S, J, RA, RB, RSA, RSB, KB)                                               \
     do {                                                                                       \
         _Pragma("unroll") for (int i = 0; i < A_PER; ++i) {                                    \
             const int rr = a_row_t + 64 * i;                                                   \
@@ -153,8 +160,20 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
             const int rr = row_t + 64 * i;                                                     \
             b_lds[S][rr][lds_chunk(rr, chunk)] = RB[i];                                        \
         }                                                                                      \
-        if (sa_ok) sa_lds[S][tid] = RSA;                                                       \
-        if (sb_ok) sb_lds[S][tid] = RSB;                                                       \
+        const int SS = SQ ? ((KB) & 7) : S;                                                    \
+        if constexpr (!SQ) {                                                                   \
+            if (sa_ok) sa_lds[S][tid] = RSA;                                                   \
+            if (sb_ok) sb_lds[S][tid] = RSB;                                                   \
+        } else if constexpr (J == 0) {                                                         \
+            if (sa_ok) {                                                                       \
+                sa_lds[SS][tid] = qa.x; sa_lds[SS + 1][tid] = qa.y;                            \
+                sa_lds[SS + 2][tid] = qa.z; sa_lds[SS + 3][tid] = qa.w;                        \
+            }                                                                                  \
+            if (sb_ok) {                                                                       \
+                sb_lds[SS][tid] = qb.x; sb_lds[SS + 1][tid] = qb.y;                            \
+                sb_lds[SS + 2][tid] = qb.z; sb_lds[SS + 3][tid] = qb.w;                        \
+            }                                                                                  \
+        }                                                                                      \
         lds_barrier(); /* LDS only: the next steps' loads stay in flight */                    \
         if (active && (KB) < nkb) {                                                            \
             const int ar = 32 * wm + (lane & 31);                                              \
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                 0, 1, 2, 3, 4, 5, 6, 7));                                                      \
             float sa[16]; /* A scale of each accumulator row of this lane */                   \
             _Pragma("unroll") for (int qq = 0; qq < 4; ++qq) {                                 \
-                const float4 v = *(const float4*)&sa_lds[S][32 * wm + 8 * qq + 4 * g];          \
+                const float4 v = *(const float4*)&sa_lds[SS][32 * wm + 8 * qq + 4 * g];         \
                 sa[4 * qq] = v.x; sa[4 * qq + 1] = v.y; sa[4 * qq + 2] = v.z; sa[4 * qq + 3] = v.w; \
             }                                                                                  \
             _Pragma("unroll") for (int nb = 0; nb < NBW; ++nb) {                               \
@@ -179,19 +198,45 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                     0, 1, 2, 3, 4, 5, 6, 7));                                                  \
                 f32x16 tmp = mfma_fp8_32x32x64(a0, b0, f32x16{});                              \
                 tmp = mfma_fp8_32x32x64(a1, b1, tmp);                                          \
-                const float sbv = sb_lds[S][brow];                                             \
+                const float sbv = sb_lds[SS][brow];                                            \
                 _Pragma("unroll") for (int q = 0; q < 16; ++q) acc[nb][q] +=                   \
                     tmp[q] * (sa[q] * sbv);                                                    \
             }                                                                                  \
         }                                                                                      \
-        MOE_FP8_LOAD(RA, RB, RSA, RSB, min((KB) + 2, nkb - 1));                                \
+        MOE_FP8_LOAD(RA, RB, min((KB) + 2, nkb - 1));                                          \
+        if constexpr (!SQ) {                                                                   \
+            RSA = as_src[min((KB) + 2, nkb - 1)];                                              \
+            RSB = bs_src[min((KB) + 2, nkb - 1)];                                              \
+        } else if constexpr (J == 0) {                                                         \
+            qa = *(const float4*)(as_src + min((KB) + 4, nkb - 4));                            \
+            qb = *(const float4*)(bs_src + min((KB) + 4, nkb - 4));                            \
+        }                                                                                      \
     } while (0)
 
-        MOE_FP8_LOAD(ra0, rb0, rsa0, rsb0, 0);
-        MOE_FP8_LOAD(ra1, rb1, rsa1, rsb1, min(1, nkb - 1));
-        for (int kb = 0; kb < nkb; kb += 2) {
-            MOE_FP8_STEP(0, ra0, rb0, rsa0, rsb0, kb);
-            MOE_FP8_STEP(1, ra1, rb1, rsa1, rsb1, kb + 1);
+        // prologue loads in the loop's own issue order, so that the waits the
+        // compiler derives at the loop head hold the look-ahead loads in flight
+        if constexpr (SQ) {
+            qa = *(const float4*)as_src;
+            qb = *(const float4*)bs_src;
+            MOE_FP8_LOAD(ra0, rb0, 0);
+            MOE_FP8_LOAD(ra1, rb1, min(1, nkb - 1));
+            for (int kb = 0; kb < nkb; kb += 4) {
+                MOE_FP8_STEP(0, 0, ra0, rb0, rsa0, rsb0, kb);
+                MOE_FP8_STEP(1, 1, ra1, rb1, rsa1, rsb1, kb + 1);
+                MOE_FP8_STEP(0, 2, ra0, rb0, rsa0, rsb0, kb + 2);
+                MOE_FP8_STEP(1, 3, ra1, rb1, rsa1, rsb1, kb + 3);
+            }
+        } else {
+            MOE_FP8_LOAD(ra0, rb0, 0);
+            rsa0 = as_src[0];
+            rsb0 = bs_src[0];
+            MOE_FP8_LOAD(ra1, rb1, min(1, nkb - 1));
+            rsa1 = as_src[min(1, nkb - 1)];
+            rsb1 = bs_src[min(1, nkb - 1)];
+            for (int kb = 0; kb < nkb; kb += 2) {
+                MOE_FP8_STEP(0, 0, ra0, rb0, rsa0, rsb0, kb);
+                MOE_FP8_STEP(1, 0, ra1, rb1, rsa1, rsb1, kb + 1);
+            }
         }
 #undef MOE_FP8_STEP
 #undef MOE_FP8_LOAD
@@ -270,25 +315,35 @@ bool fp8_use_narrow(int64_t P, int E, int H, int F) {
 
 int fp8_tile_m(bool narrow) { return narrow ? kFp8NarrowTileM : kFp8TileM; }
 
-template <int WM, int BN, bool SWIGLU>
+template <int WM, int BN, bool SWIGLU, bool SQ>
 static int fp8_grid() {
-    static const int g = resident_grid((const void*)gemm_fp8_kernel<WM, BN, SWIGLU>, kFp8Threads,
-                                       device_cu_count());
+    static const int g = resident_grid((const void*)gemm_fp8_kernel<WM, BN, SWIGLU, SQ>,
+                                       kFp8Threads, device_cu_count());
     return g;
+}
+
+// SQ (16-byte scale loads) needs K / 128 to be a multiple of 4
+template <int WM, int BN, bool SWIGLU>
+static void launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+                       const GroupedPlan& pl, int K, int n_out, int b_rows, int topk, uint8_t* Cq,
+                       float* Cs, uint16_t* Cy, hipStream_t s) {
+    if ((K / kFp8BK) % 4 == 0)
+        MOE_LAUNCH((gemm_fp8_kernel<WM, BN, SWIGLU, true>), dim3(fp8_grid<WM, BN, SWIGLU, true>()),
+                   dim3(kFp8Threads), 0, s, A, As, B, Bs, pl.perm, pl.tiles, pl.ntiles,
+                   pl.tile_off, pl.offsets, pl.E, K, n_out, b_rows, topk, Cq, Cs, Cy);
+    else
+        MOE_LAUNCH((gemm_fp8_kernel<WM, BN, SWIGLU, false>), dim3(fp8_grid<WM, BN, SWIGLU, false>()),
+                   dim3(kFp8Threads), 0, s, A, As, B, Bs, pl.perm, pl.tiles, pl.ntiles,
+                   pl.tile_off, pl.offsets, pl.E, K, n_out, b_rows, topk, Cq, Cs, Cy);
 }
 
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
                              const float* w13s, const GroupedPlan& pl, bool narrow, int H, int F,
                              int k, uint8_t* hq, float* hs, hipStream_t s) {
-    if (narrow) {
-        MOE_LAUNCH((gemm_fp8_kernel<1, 512, true>), dim3(fp8_grid<1, 512, true>()), dim3(kFp8Threads),
-                   0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets,
-                   pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
-        return hipGetLastError();
-    }
-    MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, true>), dim3(fp8_grid<kFp8WM, 256, true>()),
-                       dim3(kFp8Threads), 0, s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles,
-                       pl.tile_off, pl.offsets, pl.E, H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
+    if (narrow)
+        launch_fp8<1, 512, true>(x, xs, w13, w13s, pl, H, F, 2 * F, k, hq, hs, nullptr, s);
+    else
+        launch_fp8<kFp8WM, 256, true>(x, xs, w13, w13s, pl, H, F, 2 * F, k, hq, hs, nullptr, s);
     return hipGetLastError();
 }
 
@@ -296,19 +351,11 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2
                            const GroupedPlan& pl, bool narrow, int H, int F, uint16_t* y,
                            hipStream_t s) {
     if (narrow)
-        MOE_LAUNCH((gemm_fp8_kernel<1, 512, false>), dim3(fp8_grid<1, 512, false>()),
-                   dim3(kFp8Threads), 0, s, hq, hs, w2, w2s, pl.perm, pl.tiles, pl.ntiles,
-                   pl.tile_off, pl.offsets, pl.E, F, H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
+        launch_fp8<1, 512, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
     else if (H % 256 == 0)
-        MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 256, false>),
-                           dim3(fp8_grid<kFp8WM, 256, false>()), dim3(kFp8Threads), 0, s, hq, hs,
-                           w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
-                           H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
+        launch_fp8<kFp8WM, 256, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
     else
-        MOE_LAUNCH((gemm_fp8_kernel<kFp8WM, 128, false>),
-                           dim3(fp8_grid<kFp8WM, 128, false>()), dim3(kFp8Threads), 0, s, hq, hs,
-                           w2, w2s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E, F,
-                           H, H, 1, (uint8_t*)nullptr, (float*)nullptr, y);
+        launch_fp8<kFp8WM, 128, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
     return hipGetLastError();
 }
 

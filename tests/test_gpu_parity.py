@@ -361,7 +361,11 @@ def _host_fp8(p):
 # (T, H, F, E, k)
 @pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2),
                                    (600, 256, 128, 4, 2),    # 3 M tiles per expert, 1 K step in down
-                                   (700, 512, 256, 3, 2)])   # 467 rows per expert
+                                   (700, 512, 256, 3, 2),    # 467 rows per expert
+                                   # K / 128 a multiple of 4 (16-byte scale loads) in both
+                                   # products, two scale loads per row; then in the
+                                   # 128-wide down panels (H % 256 != 0)
+                                   (600, 1024, 512, 4, 2), (300, 384, 1024, 4, 2)])
 def test_fp8_medium(shape):
     T, H, F, E, k = shape
     _say(f"fp8 medium {shape}")
