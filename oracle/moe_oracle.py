@@ -76,6 +76,10 @@ Readings of points the pages leave open (each is listed in the design doc):
     among their experts are chosen (ties: lower expert id), largest first;
     their weights are the unbiased s renormalised to sum 1, times
     routed_scaling_factor.  The choice is made on float64 scores.
+16. The ue8m0 variant of the block-128 quantiser ([MPK] bf16_to_fp8_quantize
+    names a ue8m0 output scale without its rule) uses the smallest power of
+    two 2^e with max|h| <= 448 * 2^e (e clamped to [-127, 127]), codes
+    RNE_e4m3(h / 2^e), scale byte e + 127; an all-zero block gets byte 127.
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (brute force, closed forms, invariants, library
@@ -96,6 +100,9 @@ __all__ = [
     "quantize_block128_fp32",
     "dequantize_block128",
     "moe_experts_fp8_reference",
+    "moe_experts_fp8_reference_batched",
+    "dequantize_block128_table",
+    "quantize_block128_ue8m0",
     "e2m1_decode",
     "e2m1_encode",
     "unpack_e2m1",
@@ -103,6 +110,8 @@ __all__ = [
     "quantize_mxfp8_fp32",
     "dequantize_mx",
     "moe_experts_mxfp4_reference",
+    "moe_experts_mxfp4_reference_batched",
+    "dequantize_mxfp4_table",
     "route_softmax_topk",
     "route_sigmoid_group_topk",
 ]
@@ -413,6 +422,43 @@ def quantize_block128_fp32(h):
     return codes, scale.astype(np.float32)
 
 
+def quantize_block128_ue8m0(h):
+    """Block-128 fp8 quantisation with a power-of-two (ue8m0) scale per block
+    ([MPK] bf16_to_fp8_quantize: "FP8 E4M3 + scale ue8m0", block size 128,
+    output_scale [..., K/128]).  The page gives no rule; reading 16: for each
+    row and 128-column block of the float32 values, e is the smallest integer
+    with max|h| <= 448 * 2^e (clamped to [-127, 127]), codes =
+    RNE_e4m3fn(clamp(h / 2^e, +-448)) and the scale byte is e + 127 (its
+    value 2^e).  An all-zero block gets byte 127 (scale 1, as the fp32 rule
+    gives a zero block s = 1) and zero codes.  h / 2^e is exact, so the only
+    rounding is the e4m3 one.
+    Returns (codes uint8 [.., K], scale bytes uint8 [.., K/128])."""
+    hb = np.asarray(h, dtype=np.float32)
+    K = hb.shape[-1]
+    if K % 128:
+        raise ValueError("last dimension must be a multiple of 128")
+    blocks = hb.reshape(hb.shape[:-1] + (K // 128, 128)).astype(np.float64)
+    amax = np.max(np.abs(blocks), axis=-1)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    flat_a, flat_e = amax.reshape(-1), e.reshape(-1)
+    for i in range(flat_a.size):
+        a = flat_a[i]
+        if a == 0.0:
+            flat_e[i] = 0
+            continue
+        ei = int(np.ceil(np.log2(a / E4M3_MAX)))       # estimate, then made exact:
+        while E4M3_MAX * 2.0 ** ei < a:
+            ei += 1
+        while E4M3_MAX * 2.0 ** (ei - 1) >= a:
+            ei -= 1
+        flat_e[i] = min(max(ei, -127), 127)
+    e = flat_e.reshape(amax.shape)
+    v = blocks / np.exp2(e.astype(np.float64))[..., None]
+    v = np.clip(v, -E4M3_MAX, E4M3_MAX)
+    codes = e4m3fn_encode(v).reshape(hb.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
 def dequantize_block128(codes, scales):
     """value = decode(code) * scale[..., col // 128] in float64."""
     vals = e4m3fn_decode(codes)
@@ -472,6 +518,79 @@ def moe_experts_fp8_reference(x_codes, x_scale, w13_codes, w13_scale,
             ht = dequantize_block128(q, s)
             y = W2 @ ht
             out[t] += wts[t, j] * y
+    if residual is not None:
+        out[want] += np.asarray(residual, dtype=np.float64)[want]
+    return out
+
+
+def dequantize_block128_table(codes, scales):
+    """Same values as :func:`dequantize_block128`, computed faster for whole
+    expert matrices: each of the 256 codes is decoded once by
+    :func:`e4m3fn_decode` and looked up, and every 128-wide block is scaled
+    through a reshape instead of a repeated scale array."""
+    table = e4m3fn_decode(np.arange(256, dtype=np.uint8))
+    c = np.asarray(codes, dtype=np.uint8)
+    K = c.shape[-1]
+    vals = table[c].reshape(c.shape[:-1] + (K // 128, 128))
+    return (vals * np.asarray(scales, dtype=np.float64)[..., None]).reshape(c.shape)
+
+
+def _fp8_expert_rows(xrows, W13, W2, F):
+    """The fp8 layer's expert on a batch of rows: one float64 product per
+    matrix, h re-quantised row by row in float32 (reading 9).  Returns
+    (y, h in float32, codes, scales)."""
+    g = xrows @ W13.T
+    h = silu(g[:, :F]) * g[:, F:]
+    h32 = h.astype(np.float32)
+    q, s = quantize_block128_fp32(h32)
+    return dequantize_block128(q, s) @ W2.T, h32, q, s
+
+
+def moe_experts_fp8_reference_batched(x_codes, x_scale, w13_codes, w13_scale,
+                                      w2_codes, w2_scale, top_k_index, top_k_weights,
+                                      tokens=None, residual=None, h_report=None):
+    """Same sums as :func:`moe_experts_fp8_reference`, grouped by expert.
+
+    Per expert the weights are dequantised once and the rows of every slot
+    that chose it are multiplied as one float64 matrix product; h is
+    re-quantised per (row, 128 block) in float32 exactly as in the per-slot
+    form.  Only the summation order inside the dot products differs (about
+    1e-16 relative), which lets the full DeepSeek-V3-shaped layers be checked
+    on every output row.  ``tokens`` and ``residual`` as in the per-slot form.
+    ``h_report``, a dict, receives the intermediate of every computed slot
+    s = t*k + j (rows of dropped or unselected slots stay zero): "h" the
+    float32 SwiGLU output [P, F], "codes" its block-128 codes [P, F] and
+    "scales" [P, F/128].
+    """
+    xq = np.asarray(x_codes)
+    T, H = xq.shape
+    idx = np.asarray(top_k_index)
+    wts = np.asarray(top_k_weights, dtype=np.float64)
+    E = w13_codes.shape[0]
+    F = w13_codes.shape[1] // 2
+    want = np.zeros(T, dtype=bool)
+    if tokens is None:
+        want[:] = True
+    else:
+        want[np.asarray(tokens)] = True
+    x = dequantize_block128_table(xq, x_scale)
+    out = np.zeros((T, H), dtype=np.float64)
+    k = idx.shape[1]
+    if h_report is not None:
+        h_report["h"] = np.zeros((T * k, F), np.float32)
+        h_report["codes"] = np.zeros((T * k, F), np.uint8)
+        h_report["scales"] = np.zeros((T * k, F // 128), np.float32)
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & want[:, None])
+        if tt.size == 0:
+            continue
+        W13 = dequantize_block128_table(np.asarray(w13_codes[e]), np.asarray(w13_scale[e]))
+        W2 = dequantize_block128_table(np.asarray(w2_codes[e]), np.asarray(w2_scale[e]))
+        y, h32, q, sc = _fp8_expert_rows(x[tt], W13, W2, F)
+        np.add.at(out, tt, wts[tt, jj][:, None] * y)
+        if h_report is not None:
+            rows = tt * k + jj
+            h_report["h"][rows], h_report["codes"][rows], h_report["scales"][rows] = h32, q, sc
     if residual is not None:
         out[want] += np.asarray(residual, dtype=np.float64)[want]
     return out
@@ -626,6 +745,68 @@ def moe_experts_mxfp4_reference(x_codes, x_scale, w13_packed, w13_scale, w2_pack
             ht = dequantize_mx(e4m3fn_decode(q), sc)
             y = W2 @ ht
             out[t] += wts[t, j] * y
+    if residual is not None:
+        out[want] += np.asarray(residual, dtype=np.float64)[want]
+    return out
+
+
+def dequantize_mxfp4_table(packed, scales):
+    """MXFP4 weights as float64: the value of both nibbles of each of the 256
+    byte values is taken once from :func:`e2m1_decode` (element 2i in the low
+    nibble, as :func:`unpack_e2m1`), and each 32-element block is scaled by
+    :func:`e8m0_decode` of its scale byte.  Same values as
+    ``dequantize_mx(e2m1_decode(unpack_e2m1(packed)), scales)``."""
+    b = np.arange(256, dtype=np.uint8)
+    pair = np.stack([e2m1_decode(b & 0xF), e2m1_decode(b >> 4)], axis=-1)   # [256, 2]
+    p = np.asarray(packed, dtype=np.uint8)
+    K = 2 * p.shape[-1]
+    vals = pair[p].reshape(p.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return (vals * e8m0_decode(scales)[..., None]).reshape(p.shape[:-1] + (K,))
+
+
+def moe_experts_mxfp4_reference_batched(x_codes, x_scale, w13_packed, w13_scale, w2_packed,
+                                        w2_scale, top_k_index, top_k_weights, tokens=None,
+                                        residual=None, h_report=None):
+    """Same sums as :func:`moe_experts_mxfp4_reference`, grouped by expert:
+    per expert the weights are dequantised once, the rows of its slots go
+    through one float64 product per matrix, and h is re-quantised to MXFP8
+    row by row in float32 (reading 13).  Only the summation order inside the
+    dot products differs from the per-slot form.  ``h_report`` as in
+    :func:`moe_experts_fp8_reference_batched` ("scales" are the E8M0 bytes
+    [P, F/32])."""
+    xq = np.asarray(x_codes)
+    T, H = xq.shape
+    idx = np.asarray(top_k_index)
+    wts = np.asarray(top_k_weights, dtype=np.float64)
+    E = w13_packed.shape[0]
+    F = w13_packed.shape[1] // 2
+    want = np.zeros(T, dtype=bool)
+    if tokens is None:
+        want[:] = True
+    else:
+        want[np.asarray(tokens)] = True
+    x = dequantize_mx(e4m3fn_decode(xq), x_scale)
+    out = np.zeros((T, H), dtype=np.float64)
+    k = idx.shape[1]
+    if h_report is not None:
+        h_report["h"] = np.zeros((T * k, F), np.float32)
+        h_report["codes"] = np.zeros((T * k, F), np.uint8)
+        h_report["scales"] = np.zeros((T * k, F // MX_BLOCK), np.uint8)
+    for e in range(E):
+        tt, jj = np.nonzero((idx == e) & want[:, None])
+        if tt.size == 0:
+            continue
+        W13 = dequantize_mxfp4_table(np.asarray(w13_packed[e]), np.asarray(w13_scale[e]))
+        W2 = dequantize_mxfp4_table(np.asarray(w2_packed[e]), np.asarray(w2_scale[e]))
+        g = x[tt] @ W13.T
+        h = silu(g[:, :F]) * g[:, F:]
+        h32 = h.astype(np.float32)
+        q, sc = quantize_mxfp8_fp32(h32)
+        y = dequantize_mx(e4m3fn_decode(q), sc) @ W2.T
+        np.add.at(out, tt, wts[tt, jj][:, None] * y)
+        if h_report is not None:
+            rows = tt * k + jj
+            h_report["h"][rows], h_report["codes"][rows], h_report["scales"][rows] = h32, q, sc
     if residual is not None:
         out[want] += np.asarray(residual, dtype=np.float64)[want]
     return out

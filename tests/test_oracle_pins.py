@@ -684,3 +684,104 @@ def test_sigmoid_router_one_group_is_plain_topk():
     assert np.array_equal(idx, ti.numpy())
     s = scipy.special.expit(tv.numpy())
     np.testing.assert_allclose(w, s / s.sum(1, keepdims=True) * 2.5, rtol=1e-12)
+
+
+# ------------------------------------------------ expert-batched fp8 and MXFP4 forms
+
+
+def test_table_dequantisers_equal_the_element_decoders():
+    """The table-driven dequantisers used by the batched forms give exactly the
+    values of the per-element decoders."""
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 256, size=(7, 384), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 1                         # NaN codes compare unequal
+    sc = (rng.random((7, 3)) + 0.01).astype(np.float32)
+    assert np.array_equal(orc.dequantize_block128_table(codes, sc), orc.dequantize_block128(codes, sc))
+    packed = rng.integers(0, 256, size=(5, 3, 64), dtype=np.uint8)
+    e8 = rng.integers(100, 150, size=(5, 3, 4), dtype=np.uint8)
+    ref = orc.dequantize_mx(orc.e2m1_decode(orc.unpack_e2m1(packed)), e8)
+    assert np.array_equal(orc.dequantize_mxfp4_table(packed, e8), ref)
+
+
+@pytest.mark.parametrize("shape,seed", [((9, 256, 128, 5, 3), 51), ((24, 384, 256, 8, 2), 52),
+                                        ((40, 128, 128, 3, 3), 53)])
+def test_fp8_batched_equals_per_slot(shape, seed):
+    """Expert-batched fp8 form against the per-slot form (same sums, another
+    summation order): dropped ids, a token subset and a residual included."""
+    T, H, F, E, k = shape
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=seed, routing="uniform_softmax", routed_scale=1.0)
+    args = [p[n].numpy() for n in ("x", "x_scale", "gate_up", "gate_up_scale", "down", "down_scale")]
+    idx, w = p["top_k_index"].numpy().copy(), p["top_k_weights"].numpy().astype(np.float64)
+    idx[::4, 0] = -1
+    idx[1::5, -1] = E
+    r = np.random.default_rng(seed).standard_normal((T, H))
+    a = orc.moe_experts_fp8_reference(*args, idx, w, residual=r)
+    b = orc.moe_experts_fp8_reference_batched(*args, idx, w, residual=r)
+    assert _rel(b, a) < 1e-12
+    sub = [1, T - 1]
+    assert _rel(orc.moe_experts_fp8_reference_batched(*args, idx, w, tokens=sub)[sub],
+                orc.moe_experts_fp8_reference(*args, idx, w, tokens=sub)[sub]) < 1e-12
+
+
+@pytest.mark.parametrize("shape,seed", [((9, 128, 64, 5, 3), 61), ((24, 256, 128, 8, 2), 62)])
+def test_mxfp4_batched_equals_per_slot(shape, seed):
+    T, H, F, E, k = shape
+    p = wl.make_mxfp4_problem(T, H, F, E, k, seed=seed, routing="uniform_softmax", routed_scale=1.0)
+    args = _mx_args(p)
+    idx, w = p["top_k_index"].numpy().copy(), p["top_k_weights"].numpy().astype(np.float64)
+    idx[::3, 1] = -1
+    r = np.random.default_rng(seed).standard_normal((T, H))
+    a = orc.moe_experts_mxfp4_reference(*args, idx, w, residual=r)
+    b = orc.moe_experts_mxfp4_reference_batched(*args, idx, w, residual=r)
+    assert _rel(b, a) < 1e-12
+    sub = [0, 5]
+    assert _rel(orc.moe_experts_mxfp4_reference_batched(*args, idx, w, tokens=sub)[sub],
+                orc.moe_experts_mxfp4_reference(*args, idx, w, tokens=sub)[sub]) < 1e-12
+
+
+def test_fp8_batched_vs_bruteforce():
+    """The batched form against the torch-based dense brute force directly."""
+    p = wl.make_fp8_problem(6, 256, 128, 5, 3, seed=23, routing="uniform_softmax", routed_scale=1.0)
+    got = orc.moe_experts_fp8_reference_batched(*(p[n].numpy() for n in (
+        "x", "x_scale", "gate_up", "gate_up_scale", "down", "down_scale", "top_k_index",
+        "top_k_weights")))
+    assert _rel(got, _fp8_bruteforce(p)) < 1e-12
+
+
+# ------------------------------------------------------------ ue8m0 block-128 quantiser
+
+
+def test_ue8m0_block_golden(golden):
+    c = golden["block128_ue8m0"]
+    h = np.zeros((4, 256), np.float32)
+    for i, (row, rest) in enumerate(zip(c["rows_first2"], c["rest_of_row"])):
+        h[i, :2] = row
+        h[i, 2:128] = rest
+    q, b = orc.quantize_block128_ue8m0(h)
+    assert b[:, 0].tolist() == c["scale_bytes"]
+    assert q[:, :2].tolist() == c["codes_first2"]
+    assert np.all(b[:, 1] == 127) and np.all(q[:, 128:] == 0)    # all-zero second blocks
+
+
+def test_ue8m0_matches_torch_recipe_and_bound():
+    """torch recipe: e = ceil(log2(amax / 448)) in float64, then the e4m3fn cast of
+    h / 2^e; plus the defining property amax / 2^e in (224, 448]."""
+    rng = np.random.default_rng(71)
+    h = (rng.standard_normal((29, 512)) * np.exp(rng.uniform(-20, 12, (29, 1)))).astype(np.float32)
+    h[4, :128] = 0.0
+    h[5, 128:256] = 448.0                                      # amax exactly 448 * 2^0
+    h[6, :128] = np.float32(2.0 ** -30) * 448                  # exactly 448 * 2^-30
+    q, b = orc.quantize_block128_ue8m0(h)
+    t = torch.from_numpy(h).double().reshape(29, 4, 128)
+    amax = t.abs().amax(-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 448.0)), torch.zeros_like(amax))
+    v = (t / torch.exp2(e)[..., None]).clamp(-448, 448).float()
+    tq = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(29, 512)
+    assert np.array_equal(q, tq.numpy())
+    assert np.array_equal(b.astype(np.int64), (e + 127).long().numpy())
+    a = amax.numpy()
+    s = np.exp2(b.astype(np.float64) - 127)
+    nz = a > 0
+    assert np.all(a[nz] / s[nz] <= 448.0) and np.all(a[nz] / s[nz] > 224.0)
+    back = orc.e4m3fn_decode(q) * np.repeat(s, 128, axis=1)
+    assert np.all(np.abs(back - h) <= np.maximum(2.0 ** -4 * np.abs(h), 2.0 ** -10 * np.repeat(s, 128, axis=1)))
