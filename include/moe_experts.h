@@ -208,6 +208,8 @@ int moe_workspace_size_shared(int variant, int64_t T, int H, int F, int E, int k
  *   gate_up  [E,2F,H]     fp8   gate_up_scale  [E,2F,H/128]   fp32
  *   down     [E,H,F]      fp8   down_scale     [E,H,F/128]    fp32
  *   top_k_index [T,k] int32, top_k_weights [T,k] fp32, out [T,H] bf16.
+ * The three scale tensors must be 16-byte aligned (the kernels read the
+ * scales of four K blocks per load); other pointers as above.
  * value(code, block) = e4m3(code) * scale[row][col/128].  Products accumulate
  * in fp32, one 128-wide K block at a time, then scale by x_scale*w_scale.
  * The SwiGLU output is re-quantised per (slot row, 128 block) before the down
@@ -364,6 +366,16 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
  * MOE_ERR_NULL, MOE_ERR_LAUNCH (event creation or query failed),
  * MOE_ERR_DEVICE.
  */
+/*
+ * Test hook: caps the persistent grids of the grouped products (and the
+ * persistent decode kernel) at max_workgroups (rounded down to a multiple of
+ * 8, at least 8), so that every workgroup runs many work items; 0 removes
+ * the cap (the default: one resident grid per kernel).  Results do not
+ * depend on the grid.  Process-wide; takes effect at the next launch.
+ * Errors: MOE_ERR_SHAPE for a negative value.
+ */
+int moe_set_grid_cap(int max_workgroups);
+
 #define MOE_PROFILE_MAX_STAGES 5
 #define MOE_PROFILE_MAX_CALLS 4096
 enum moe_stage {

@@ -71,6 +71,7 @@ def _load():
         "moe_experts_decode_routed": ([vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
                                        vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
+        "moe_set_grid_cap": ([i32], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
     }
@@ -89,7 +90,7 @@ def exported_symbols():
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
-            "moe_experts_decode_routed"]
+            "moe_experts_decode_routed", "moe_set_grid_cap"]
 
 
 class MoeError(RuntimeError):
@@ -166,6 +167,11 @@ def moe_profile_end(max_calls):
                 row.append((STAGE_NAMES.get(sid, str(sid)), float(ms[c * MOE_PROFILE_MAX_STAGES + i])))
         out.append(row)
     return out
+
+
+def moe_set_grid_cap(max_workgroups):
+    """Test hook: cap the persistent grids at `max_workgroups` (0 = no cap)."""
+    _check(_load().moe_set_grid_cap(int(max_workgroups)), "moe_set_grid_cap")
 
 
 # ------------------------------------------------------------ workspace cache

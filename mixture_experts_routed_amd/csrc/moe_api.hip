@@ -35,6 +35,9 @@ int query_device(int* dev_out) {
 }
 }  // namespace
 
+std::atomic<int> g_grid_cap{0};
+int grid_cap() { return g_grid_cap.load(std::memory_order_relaxed); }
+
 int device_cu_count() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
@@ -252,10 +255,9 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
     if (!gate_up || !gate_up_scale || !down || !down_scale || !top_k_index || !top_k_weights ||
         !out)
         return MOE_ERR_NULL;
-    if (!aligned16(gate_up) || !aligned16(down) || !aligned16(out) ||
-        (residual && !aligned16(residual)) ||
-        (((uintptr_t)gate_up_scale | (uintptr_t)down_scale | (uintptr_t)top_k_index |
-          (uintptr_t)top_k_weights) & 3u))
+    if (!aligned16(gate_up) || !aligned16(down) || !aligned16(out) || !aligned16(gate_up_scale) ||
+        !aligned16(down_scale) || (residual && !aligned16(residual)) ||
+        (((uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
         return MOE_ERR_ALIGN;
     int rc = check_shape(variant, T, H, F, E, k);
     if (rc) return rc;
@@ -550,7 +552,7 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
                     const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                     uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!x || !x_scale) return MOE_ERR_NULL;
-    if (!aligned16(x) || ((uintptr_t)x_scale & 3u)) return MOE_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(x_scale)) return MOE_ERR_ALIGN;
     return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
                    top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
 }
@@ -711,6 +713,12 @@ int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids) {
     }
     *n_calls = n;
     g_prof.used = 0;
+    return MOE_OK;
+}
+
+int moe_set_grid_cap(int max_workgroups) {
+    if (max_workgroups < 0) return MOE_ERR_SHAPE;
+    g_grid_cap.store(max_workgroups, std::memory_order_relaxed);
     return MOE_OK;
 }
 

@@ -268,7 +268,7 @@ template <int BN, bool SWIGLU>
 static int gemm_grid() {
     static const int g = resident_grid((const void*)gemm_bf16_kernel<BN, SWIGLU>, kGemmThreads,
                                        device_cu_count());
-    return g;
+    return capped_grid(g);
 }
 
 template <int BN, bool SWIGLU>

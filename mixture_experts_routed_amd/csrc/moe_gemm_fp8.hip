@@ -16,11 +16,15 @@ namespace moe {
 constexpr int kFp8Threads = 512;  // 8 waves
 constexpr int kFp8BK = 128;       // K bytes per stage == one scale block
 
-// Block-128 quantisation of 128 values spread as 4 per lane over one 32-lane
-// half (same row): shared by the layer's epilogue and the stand-alone kernel.
-// Returns the scale; writes the four codes packed little-endian in *codes.
-__device__ __forceinline__ float quant_block_half(const float v[4], float amax_local, uint32_t* codes) {
-    const float amax = half_max32(amax_local);
+// Block-128 quantisation (mirage issue "Supporting MegaKernel for DeepSeek
+// Models", bf16_to_fp8_quantize, with moe_w2_fp8_layer's fp32 input scale):
+// given the block's max |v| already reduced over its 128 values, this
+// thread's (up to) four values become codes RNE_e4m3(clamp(v * (448/amax),
+// +-448)) and the block's scale amax/448, all in fp32; an all-zero block
+// gets scale 1 and zero codes.  The one routine behind both the SwiGLU
+// epilogue of the gate_up product and the stand-alone quantiser.  Returns
+// the scale; writes the four codes packed little-endian in *codes.
+__device__ __forceinline__ float quant_block_codes(const float v[4], float amax, uint32_t* codes) {
     const bool zero = !(amax > 0.0f);
     const float scale = zero ? 1.0f : amax / 448.0f;
     const float mul = zero ? 0.0f : 448.0f / amax;
@@ -33,6 +37,11 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
     }
     *codes = f32x4_to_e4m3x4(q[0], q[1], q[2], q[3]);
     return scale;
+}
+
+// 128 values spread as 4 per lane over one 32-lane half (same row).
+__device__ __forceinline__ float quant_block_half(const float v[4], float amax_local, uint32_t* codes) {
+    return quant_block_codes(v, half_max32(amax_local), codes);
 }
 
 // Same work decomposition and data path as the bf16 products: one work item
@@ -267,14 +276,11 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                     float amax = amax_lds[wb0][row];
 #pragma unroll
                     for (int j = 1; j < WB; ++j) amax = fmaxf(amax, amax_lds[wb0 + j][row]);
-                    const bool zero = !(amax > 0.0f);
-                    const float scale = zero ? 1.0f : amax / 448.0f;
-                    const float mul = zero ? 0.0f : 448.0f / amax;
-                    float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int p = 0; p < PP; ++p)
-                        qv[p] = zero ? 0.0f : fminf(fmaxf(hv[p][q] * mul, -448.0f), 448.0f);
-                    const uint32_t codes = f32x4_to_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
+                    for (int p = 0; p < PP; ++p) vv[p] = hv[p][q];
+                    uint32_t codes;
+                    const float scale = quant_block_codes(vv, amax, &codes);
                     if (row < mrows) {
                         uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + nt * (BN / 2) + wn * PP * 32 + (lane & 31);
 #pragma unroll
@@ -319,7 +325,7 @@ template <int WM, int BN, bool SWIGLU, bool SQ>
 static int fp8_grid() {
     static const int g = resident_grid((const void*)gemm_fp8_kernel<WM, BN, SWIGLU, SQ>,
                                        kFp8Threads, device_cu_count());
-    return g;
+    return capped_grid(g);
 }
 
 // SQ (16-byte scale loads) needs K / 128 to be a multiple of 4

@@ -484,14 +484,14 @@ template <int BN, bool SWIGLU, int KS, int WM = 4>
 static int mx_grid() {
     static const int g = resident_grid((const void*)gemm_mx_kernel<BN, SWIGLU, KS, WM>, kMxThreads,
                                        device_cu_count());
-    return g;
+    return capped_grid(g);
 }
 
 template <bool SWIGLU>
 static int mx_wide_grid() {
     static const int g = resident_grid((const void*)gemm_mx_wide_kernel<SWIGLU>, kMxThreads,
                                        device_cu_count());
-    return g;
+    return capped_grid(g);
 }
 
 bool mx_use_wide(int64_t P, int E, int H, int F) {

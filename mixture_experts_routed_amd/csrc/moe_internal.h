@@ -192,4 +192,13 @@ hipError_t launch_route_plan(const void* logits, const void* bias, int bf16, int
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Upper bound on the persistent grids (moe_set_grid_cap; 0 = none), so that
+// tests can make every workgroup run many work items.
+int grid_cap();
+inline int capped_grid(int g) {
+    const int cap = grid_cap();
+    if (cap <= 0 || g <= cap) return g;
+    return cap >= 8 ? cap / 8 * 8 : 8;   // a multiple of the 8 XCDs
+}
+
 }  // namespace moe

@@ -139,6 +139,9 @@ def test_fp8_and_plan_validation():
     assert lib.moe_experts_fp8(*bad) == EALIGN
     bad = list(args); bad[8] = P16 + 8                         # residual
     assert lib.moe_experts_fp8(*bad) == EALIGN
+    for i in (1, 3, 5):                                         # scales: 16-byte aligned
+        bad = list(args); bad[i] = P16 + 4
+        assert lib.moe_experts_fp8(*bad) == EALIGN, i
     bad = list(args); bad[10] = 192                             # H
     assert lib.moe_experts_fp8(*bad) == ESHAPE
     bad = list(args); bad[16] = 0                               # ws_bytes
@@ -149,6 +152,9 @@ def test_fp8_and_plan_validation():
     assert lib.moe_experts_fp8_bf16in(*bad) == ENULL
     bad = list(args); bad[0] = P16 + 2
     assert lib.moe_experts_fp8_bf16in(*bad) == EALIGN
+    for i in (2, 4):                                            # weight scales
+        bad = list(args); bad[i] = P16 + 4
+        assert lib.moe_experts_fp8_bf16in(*bad) == EALIGN, i
     bad = list(args); bad[9] = 192                              # H
     assert lib.moe_experts_fp8_bf16in(*bad) == ESHAPE
     bad = list(args); bad[15] = 16                              # ws_bytes
@@ -306,3 +312,10 @@ def test_shared_entry_validation(fn):
     assert call(E=511) == ESHAPE          # E + S above MOE_MAX_EXPERTS
     assert call(H=96) == ESHAPE
     assert call(ws_bytes=16) == EWS
+
+
+def test_grid_cap_argument():
+    lib = moe._load()
+    assert lib.moe_set_grid_cap(-1) == ESHAPE
+    assert lib.moe_set_grid_cap(16) == OK
+    assert lib.moe_set_grid_cap(0) == OK

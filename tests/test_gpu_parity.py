@@ -16,6 +16,7 @@ import torch
 
 import moe_workloads as wl
 from oracle import moe_oracle as orc
+from oracle_runner import check_quantized_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -337,27 +338,6 @@ def run_fp8(g, out=None):
                                g["top_k_index"].shape[1], out=out)
 
 
-class _HostExperts:
-    """Lazy host copies of a few experts of a device weight tensor."""
-
-    def __init__(self, t):
-        self.t, self.cache, self.shape = t, {}, tuple(t.shape)
-
-    def __getitem__(self, e):
-        e = int(e)
-        if e not in self.cache:
-            self.cache[e] = self.t[e].cpu().numpy()
-        return self.cache[e]
-
-
-def _host_fp8(p):
-    q = dict(p)
-    for n in ("gate_up", "gate_up_scale", "down", "down_scale"):
-        q[n] = _HostExperts(p[n])
-    q["gate_up"].shape = tuple(p["gate_up"].shape)
-    return q
-
-
 # (T, H, F, E, k)
 @pytest.mark.parametrize("shape", [(300, 512, 384, 6, 3), (64, 256, 128, 8, 4), (520, 128, 256, 2, 2),
                                    (600, 256, 128, 4, 2),    # 3 M tiles per expert, 1 K step in down
@@ -405,9 +385,9 @@ def test_fp8_h_stage_codes(shape):
     """The re-quantised h in the workspace against the oracle's fp32 rule applied
     to the oracle's h.  The kernel quantises its own fp32-accumulated h, which
     differs from the oracle's float64 h by fp32 summation error (about 1e-5
-    relative), so scales agree to 1e-3 and codes agree except for rare
+    relative), so scales agree to 1e-4 and codes agree except for rare
     one-step flips at rounding boundaries.  Bit-exactness of the quantiser on
-    identical inputs is test_quantizer_bit_exact."""
+    identical inputs is test_quantizer_bit_exact and test_fp8_h_stage_exact."""
     moe = _moe()
     _say(f"fp8 h stage {shape}")
     T, H, F, E, k = shape
@@ -432,7 +412,7 @@ def test_fp8_h_stage_codes(shape):
         gv = W @ x[s // k]
         h_ref[m] = (orc.silu(gv[:F]) * gv[F:]).astype(np.float32)
     q_ref, s_ref = orc.quantize_block128_fp32(h_ref)
-    np.testing.assert_allclose(hs, s_ref, rtol=1e-3)
+    np.testing.assert_allclose(hs, s_ref, rtol=1e-4)
     diff = hq != q_ref
     assert diff.mean() < 2e-3, diff.mean()
     a, b = orc.e4m3fn_decode(hq[diff]), orc.e4m3fn_decode(q_ref[diff])
@@ -463,31 +443,104 @@ def test_quantizer_bit_exact():
     assert np.array_equal(scales.cpu().numpy(), s_ref)
 
 
-def _sample_tokens(T, n, seed):
-    return np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
+def _run_fp8_ws(moe, g, variant=None):
+    T, H = g["x"].shape
+    E, F2, _ = g["gate_up"].shape
+    k = g["top_k_index"].shape[1]
+    lay = moe.moe_workspace_layout(moe.MOE_VARIANT_FP8 if variant is None else variant, T, H,
+                                   F2 // 2, E, k)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
+    out = moe.moe_experts_fp8(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"],
+                              g["down_scale"], g["top_k_index"], g["top_k_weights"], k, workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws, lay
 
 
-@pytest.mark.parametrize("name,n_sample", [("v3_fp8_decode", 3), ("v3_fp8_prefill", 3)])
-def test_fp8_full_config_sampled(name, n_sample):
-    """Full DeepSeek-V3-shaped expert share; sampled output rows against the oracle."""
+@pytest.mark.parametrize("name", ["v3_fp8_decode", "v3_fp8_prefill"])
+def test_fp8_full_config_every_row(name):
+    """Full DeepSeek-V3-shaped expert share (T=128 decode batch, T=4096 Zipf
+    prefill with empty experts): every output element against the
+    expert-batched oracle (pinned to the per-slot form on the CPU), after
+    checking that each requantised h code the kernel chose is a rounding of
+    the oracle's h; a second call is bit-identical."""
+    moe = _moe()
     _say(f"fp8 full {name}")
     p = wl.make_config(name, device="cuda")
-    out = run_fp8(p)
-    torch.cuda.synchronize()
+    out, ws, lay = _run_fp8_ws(moe, p)
+    st = check_quantized_layer("fp8", out, p, ws, lay, name, orc)
     idx = p["top_k_index"].cpu().numpy()
-    counts = np.bincount(idx.reshape(-1), minlength=128)
-    tokens = list(_sample_tokens(p["x"].shape[0], n_sample, 7))
-    hot = int(np.argmax(counts))
-    tokens.append(int(np.nonzero((idx == hot).any(1))[0][0]))       # a token of the hottest expert
-    tokens = sorted(set(tokens))
-    hp = _host_fp8(p)
-    ref = fp8_ref(hp, tokens=tokens)
-    worst, rel = check_tol(out[tokens], ref[tokens], FP8_TOL, name)
-    _say(f"  tokens {tokens}: worst err/tol {worst:.3f} rel L2 {rel:.2e}; "
-         f"max/mean load {counts.max() / counts.mean():.1f}, empty {(counts == 0).sum()}")
-    a = out.clone()
+    counts = np.bincount(idx.reshape(-1), minlength=p["gate_up"].shape[0])
+    _say(f"  all {out.shape[0]} rows: {st}; max/mean load {counts.max() / counts.mean():.1f}, "
+         f"empty {(counts == 0).sum()}")
     b = run_fp8(p)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fp8 path not deterministic"
+    assert torch.equal(out.view(torch.int16), b.view(torch.int16)), "fp8 path not deterministic"
+
+
+# (T, H, F, E, k): with the persistent grid capped at 8 workgroups every
+# workgroup runs many work items in a row (ring slots, scale rings and the
+# per-item set-up reused across items): 128-row tiles with 16-byte scale loads,
+# 128-wide down panels, and 32-row decode-batch tiles.  The capped call must
+# equal the uncapped one bit for bit, and that one the oracle.
+@pytest.mark.parametrize("shape", [(600, 1024, 512, 4, 2), (700, 512, 256, 3, 2),
+                                   (300, 384, 1024, 4, 2), (128, 1024, 512, 16, 4)])
+def test_fp8_many_items_per_workgroup(shape):
+    moe = _moe()
+    T, H, F, E, k = shape
+    _say(f"fp8 capped grid {shape}")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=83 + T, routing="uniform_softmax", routed_scale=1.0)
+    g = to_gpu(p)
+    out, ws, lay = _run_fp8_ws(moe, g)
+    moe.moe_set_grid_cap(8)
+    try:
+        capped = run_fp8(g)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_set_grid_cap(0)
+    assert torch.equal(out.view(torch.int16), capped.view(torch.int16)), "grid-dependent result"
+    st = check_quantized_layer("fp8", out, g, ws, lay, str(shape), orc)
+    _say(f"  {st}")
+
+
+@pytest.mark.parametrize("shape", [(96, 256, 256, 4, 2), (40, 512, 512, 8, 2)])
+def test_fp8_h_stage_exact(shape):
+    """Small-integer operands with unit scales make every fp32 sum of the
+    gate_up product exact; every gate dot product is at least 20, where
+    silu(g) = g in fp32 (1 + e^-20 rounds to 1), so h = g_gate * g_up is an
+    exact integer and the epilogue's requantised codes and scales must equal
+    the oracle's fp32 block-128 rule bit for bit (128-row tiles, then the
+    32-row decode-batch tiles)."""
+    moe = _moe()
+    T, H, F, E, k = shape
+    _say(f"fp8 exact h stage {shape}")
+    rng = np.random.default_rng(17)
+    x = rng.integers(1, 3, size=(T, H)).astype(np.float64)              # 1 or 2
+    gate = (rng.random((E, F, H)) < 0.3).astype(np.float64)
+    gate[..., :20] = 1.0                                                # >= 20 ones per row
+    up = rng.integers(-2, 3, size=(E, F, H)).astype(np.float64)
+    down = rng.integers(-2, 3, size=(E, H, F)).astype(np.float64)
+    idx, w = wl.route_uniform_softmax(T, E, k, torch.Generator().manual_seed(5), "cpu", 1.0)
+    enc = lambda a: torch.from_numpy(orc.e4m3fn_encode(a))
+    ones = lambda *s: torch.ones(*s, dtype=torch.float32)
+    g = {"x": enc(x), "x_scale": ones(T, H // 128),
+         "gate_up": enc(np.concatenate([gate, up], axis=1)), "gate_up_scale": ones(E, 2 * F, H // 128),
+         "down": enc(down), "down_scale": ones(E, H, F // 128),
+         "top_k_index": idx, "top_k_weights": w}
+    g = to_gpu(g)
+    lay = moe.moe_workspace_layout(moe.MOE_VARIANT_FP8, T, H, F, E, k)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device="cuda")
+    moe.moe_experts_fp8(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"],
+                        g["down_scale"], g["top_k_index"], g["top_k_weights"], k, workspace=ws)
+    torch.cuda.synchronize()
+    P = T * k
+    perm = ws[lay["perm"]:lay["perm"] + 4 * P].view(torch.int32).cpu().numpy()
+    hq = ws[lay["h"]:lay["h"] + P * F].cpu().numpy().reshape(P, F)
+    hs = ws[lay["h_scale"]:lay["h_scale"] + 4 * P * (F // 128)].view(torch.float32).cpu().numpy()
+    ids = idx.numpy().reshape(-1)
+    h = np.stack([(gate[ids[s]] @ x[s // k]) * (up[ids[s]] @ x[s // k]) for s in perm])
+    assert np.all(np.abs(h) < 2.0 ** 24)
+    q_ref, s_ref = orc.quantize_block128_fp32(h.astype(np.float32))
+    assert np.array_equal(hs.reshape(P, F // 128), s_ref), "h scales differ"
+    assert np.array_equal(hq, q_ref), f"{int((hq != q_ref).sum())} h codes differ"
 
 
 @pytest.mark.parametrize("shape", [(100, 256, 128, 4, 3), (400, 256, 128, 4, 3)])
@@ -605,25 +658,29 @@ def test_fp8_bf16in_medium(shape):
     assert torch.equal(out.view(torch.int16), two.view(torch.int16))
 
 
-def test_fp8_bf16in_full_config_sampled():
+def test_fp8_bf16in_full_config_every_row():
     """DeepSeek-V3-shaped decode batch (T=128, H=7168, F=2048, 128 experts,
-    top-8) fed with bf16 N(0,1) hidden states; sampled rows against the oracle."""
+    top-8) fed with bf16 N(0,1) hidden states: the quantised hidden states
+    bit-exact against the oracle's block-128 quantiser, then every row of the
+    layer against the expert-batched fp8 oracle on those codes."""
     moe = _moe()
     _say("fp8 bf16-in full v3_fp8_decode")
     p = wl.make_config("v3_fp8_decode", device="cuda")
     T, H = p["x"].shape
     k = p["top_k_index"].shape[1]
+    E, F2, _ = p["gate_up"].shape
     hidden = _residual(T, H, 58).cuda()
+    lay = moe.moe_workspace_layout(moe.MOE_VARIANT_FP8_BF16IN, T, H, F2 // 2, E, k)
+    ws = torch.empty(lay["total"], dtype=torch.uint8, device="cuda")
     out = moe.moe_experts_fp8_bf16in(hidden, p["gate_up"], p["gate_up_scale"], p["down"],
-                                     p["down_scale"], p["top_k_index"], p["top_k_weights"], k)
+                                     p["down_scale"], p["top_k_index"], p["top_k_weights"], k,
+                                     workspace=ws)
     torch.cuda.synchronize()
-    tokens = sorted(set(_sample_tokens(T, 4, 9)))
-    hp = _host_fp8(p)
-    ref = orc.moe_experts_fp8_bf16_reference(
-        f64(hidden), hp["gate_up"], hp["gate_up_scale"], hp["down"], hp["down_scale"],
-        p["top_k_index"].cpu().numpy(), p["top_k_weights"].cpu().numpy(), tokens=tokens)
-    worst, rel = check_tol(out[tokens], ref[tokens], FP8_TOL, "bf16-in full")
-    _say(f"  tokens {tokens}: worst err/tol {worst:.3f} rel L2 {rel:.2e}")
+    xq, xs = orc.quantize_block128_fp32(f64(hidden).astype(np.float32))
+    q = dict(p)
+    q["x"], q["x_scale"] = torch.from_numpy(xq), torch.from_numpy(xs)
+    st = check_quantized_layer("fp8", out, q, ws, lay, "bf16-in full", orc)
+    _say(f"  all rows: {st}")
 
 
 # ------------------------------------------------------- shared experts
@@ -688,14 +745,10 @@ def test_shared_experts_dropped_ids_zero_weights_residual(entry):
 
 @pytest.mark.parametrize("name", ["ocr2_decode_t1_shared", "ocr2_prefill_shared"])
 def test_shared_full_config(name):
-    """The OCR-2 workloads with their two shared experts; sampled tokens for
-    the prefill, every token for the decode."""
+    """The OCR-2 workloads with their two shared experts, every token."""
     _say(f"shared full {name}")
     p = wl.make_config(name)
     g = to_gpu(p)
     entry = "moe_experts_decode_shared" if "decode" in name else "moe_experts_prefill_shared"
     out = _run_shared(entry, g)
-    T = p["hidden"].shape[0]
-    tokens = list(range(T)) if T <= 4 else sorted(set(_sample_tokens(T, 6, 9)))
-    sub = {n: (v[tokens] if n in ("hidden", "top_k_index", "top_k_weights") else v) for n, v in p.items()}
-    check_tol(out[tokens], _shared_ref(sub, batched=False), BF16_TOL, name)
+    check_tol(out, _shared_ref(p, batched=True), BF16_TOL, name)
