@@ -64,6 +64,7 @@ enum moe_status {
     MOE_ERR_WORKSPACE = -4,  /* workspace missing, too small or misaligned      */
     MOE_ERR_LAUNCH = -5,     /* the HIP runtime rejected a kernel launch        */
     MOE_ERR_DEVICE = -6,     /* the current device is not a gfx950 GPU          */
+    MOE_ERR_SCRATCH = -7,    /* more scratch than MOE_SCRATCH_BYTES needed      */
 };
 
 enum moe_variant {
@@ -156,6 +157,26 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
                        const int32_t* top_k_index, const float* top_k_weights,
                        const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_experts_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call allocates nothing: its
+ * scratch memory is a static device array of MOE_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends.  Every call on one GPU uses that GPU's array, so calls that
+ * overlap in time on one GPU (concurrent streams, or several host threads)
+ * race and must be ordered by the caller; calls on one stream are ordered.
+ * Operands, results and limits are those of moe_experts_decode; a shape
+ * whose moe_workspace_size(MOE_VARIANT_DECODE, ...) exceeds
+ * MOE_SCRATCH_BYTES is rejected with MOE_ERR_SCRATCH before anything is
+ * enqueued (the gather-GEMV form of every T <= 4 shape fits).
+ */
+#define MOE_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_experts_decode_noalloc(const uint16_t* hidden, const uint16_t* gate_up,
+                               const uint16_t* down, const int32_t* top_k_index,
+                               const float* top_k_weights, const uint16_t* residual, int64_t T,
+                               int H, int F, int E, int k, uint16_t* out, hipStream_t stream);
 
 /*
  * bf16 routed experts plus S shared experts fused into the same products

@@ -72,6 +72,7 @@ def _load():
                                        vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_set_grid_cap": ([i32], i32),
+        "moe_experts_decode_noalloc": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
     }
@@ -90,7 +91,7 @@ def exported_symbols():
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
-            "moe_experts_decode_routed", "moe_set_grid_cap"]
+            "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -293,6 +294,35 @@ def moe_experts_decode(hidden_states, gate_up_proj, down_proj, top_k_index, top_
     returns out [T, H] bf16 (plus the optional residual)."""
     return _bf16_call("moe_experts_decode", MOE_VARIANT_DECODE, hidden_states, gate_up_proj,
                       down_proj, top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_decode_noalloc(hidden_states, gate_up_proj, down_proj, top_k_index,
+                               top_k_weights, top_k, residual=None, out=None):
+    """moe_experts_decode with the library's static scratch buffer instead of
+    a workspace (the C call allocates nothing; pass `out` to allocate nothing
+    here either)."""
+    dev = hidden_states.device
+    _need(hidden_states, "hidden_states", torch.bfloat16, 2)
+    _need(gate_up_proj, "gate_up_proj", torch.bfloat16, 3, dev)
+    _need(down_proj, "down_proj", torch.bfloat16, 3, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = hidden_states.shape
+    E, F2, H2 = gate_up_proj.shape
+    F = F2 // 2
+    k = int(top_k)
+    if H2 != H or F2 != 2 * F or tuple(down_proj.shape) != (E, H, F):
+        raise ValueError("expected gate_up_proj [E,2F,H] and down_proj [E,H,F] matching hidden_states [T,H]")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
+    out = _out(out, T, H, dev)
+    with _on(dev):
+        rc = _load().moe_experts_decode_noalloc(
+            _ptr(hidden_states), _ptr(gate_up_proj), _ptr(down_proj), _ptr(top_k_index),
+            _ptr(top_k_weights), res, T, H, F, E, k, _ptr(out), ctypes.c_void_p(_stream(dev)))
+    _check(rc, "moe_experts_decode_noalloc")
+    return out
 
 
 def _shared_call(entry, variant, hidden_states, gate_up_proj, down_proj, shared_gate_up,

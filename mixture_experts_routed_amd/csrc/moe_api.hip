@@ -419,6 +419,26 @@ int run_shared(int variant, const uint16_t* hidden, const uint16_t* gate_up, con
     return run_decode(clock, L, hidden, gu, dn, idx2, w2, residual, T, H, F, E + S, k + S, out, ws,
                       stream);
 }
+// ------------------------------------------------- allocation-free decode
+// The workspace of moe_experts_decode_noalloc: a static device array, one
+// copy per GPU for the life of the process.  In host code `scratch` only
+// names the symbol; its device address (per device) comes from
+// hipGetSymbolAddress and is the only way host code refers to its memory.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch` (looked up once per device, with
+// that device current).
+int scratch_ptr(int dev, void** out) {
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return MOE_OK;
+}
 }  // namespace
 }  // namespace moe
 
@@ -437,6 +457,9 @@ const char* moe_strerror(int status) {
         case MOE_ERR_WORKSPACE: return "workspace is NULL, not 256-byte aligned, or too small";
         case MOE_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
         case MOE_ERR_DEVICE: return "the current HIP device is not a gfx950 GPU";
+        case MOE_ERR_SCRATCH:
+            return "the call needs more scratch memory than the library's static buffer holds "
+                   "(MOE_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -506,6 +529,25 @@ int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const ui
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     int dev;
     if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    StageClock clock(stream);
+    return run_decode(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E), top_k_index,
+                      top_k_weights, residual, T, H, F, E, k, out, ws, stream);
+}
+
+int moe_experts_decode_noalloc(const uint16_t* hidden, const uint16_t* gate_up,
+                               const uint16_t* down, const int32_t* top_k_index,
+                               const float* top_k_weights, const uint16_t* residual, int64_t T,
+                               int H, int F, int E, int k, uint16_t* out, hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
+    if (rc) return rc;
+    if ((rc = check_shape(MOE_VARIANT_DECODE, T, H, F, E, k))) return rc;
+    const Layout L = make_layout(MOE_VARIANT_DECODE, T, H, F, E, k);
+    if (L.total > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_ptr(dev, &ws))) return rc;
     if (T == 0) return MOE_OK;
     StageClock clock(stream);
     return run_decode(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E), top_k_index,
