@@ -27,7 +27,13 @@ ocr2_prefill, v3_fp8_decode, v3_fp8_prefill, tiny, ocr2_prefill_shared /
 ocr2_decode_t1_shared with the model's two shared experts, and
 v3_mxfp4_decode / v3_mxfp4_prefill with MXFP4 weights).
 
-Helper modes (no GPU work of their own):
+By default the line also carries `all_configs`: every other workload measured
+the same way (passes A and B, fewer steps), so that each configuration has a
+number from the same run; --only skips them.
+
+Helper modes:
+  --probe                   ceiling probes: a plain streaming read of the
+                            decode workloads' weight bytes, dense torch GEMMs
   --copy-calibration        a plain 256 MiB device copy, for counter scaling
   --summarize-stats CSV     markdown table from a rocprofv3 kernel_stats.csv
   --summarize-pmc ...       HBM bytes per kernel from FETCH_SIZE/WRITE_SIZE runs
@@ -63,8 +69,7 @@ PAGE_DECODE_T1_TOKENS_PER_S = 1.0 / 0.191e-3
 # kernel-name prefix -> stage, for matching rocprofv3 rows to recorder stages
 KERNEL_STAGES = [
     ("moe::plan_kernel", "plan"),
-    ("moe::decode_slice_kernel", "decode_slices"),
-    ("moe::decode_combine_kernel", "combine"),
+    ("moe::decode_kernel", "decode"),
     ("moe::combine_kernel", "combine"),
     ("moe::gemm_bf16_kernel<", "gemm_bf16"),
     ("moe::gemm_fp8_kernel<", "gemm_fp8"),
@@ -112,6 +117,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-pass", action="store_true", help="skip pass B (profiling runs)")
+    ap.add_argument("--all-configs", dest="all_configs", action="store_true", default=True,
+                    help="also measure every other workload compactly (the default)")
+    ap.add_argument("--only", dest="all_configs", action="store_false",
+                    help="measure the chosen workload only")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the ceiling probes (plain streaming reads, dense GEMMs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (calibrates HBM counters)")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("CSV", "TITLE", "COMMAND"))
@@ -209,8 +220,8 @@ def stage_work(stage, kind, T, H, F, k, touched, valid):
         return dn_w, 2 * valid * H * F
     if stage == "combine":
         return out_bytes + route_bytes, 2 * valid * H
-    if stage == "decode_slices":
-        return gu_w + dn_w + x_bytes + T * k * 4, 2 * valid * 3 * F * H
+    if stage == "decode":   # the whole layer in one launch
+        return gu_w + dn_w + x_bytes + out_bytes + route_bytes, 2 * valid * 3 * F * H
     if stage == "shared_route":
         return route_bytes, 0
     raise ValueError(stage)
@@ -254,49 +265,38 @@ def committed_traffic(workload, stage):
 
 
 # ------------------------------------------------------------ main
-def main():
-    args = parse()
-    if args.summarize_stats:
-        summarize_stats(*args.summarize_stats)
-        return
-    if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+# the workloads the default run also measures (compactly) beside the headline
+ALL_CONFIGS = ["tiny", "ocr2_decode_t1", "ocr2_decode_t4", "ocr2_prefill", "v3_fp8_decode",
+               "v3_fp8_prefill", "ocr2_prefill_shared", "ocr2_decode_t1_shared", "v3_mxfp4_decode",
+               "v3_mxfp4_prefill"]
 
-    import numpy as np
-    import torch
 
-    import mixture_experts_routed_amd as moe
-    import moe_workloads as wl
+def default_steps(name, kind):
+    decode = name.startswith("ocr2_decode") or name == "tiny"
+    return 200 if decode else (20 if kind == "bf16" else 10)
 
-    cfg = dict(wl.CONFIGS[args.config])
-    name = args.config
+
+def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=True, extras=True):
+    """One workload: pass A (timed steps), pass B (per-kernel stage times),
+    and, with `extras`, the router pass and the router-fused decode pass.
+    Returns (bench dict, context for the CPU baseline)."""
+    cfg = dict(wl.CONFIGS[name])
     T, H, F, E, k, kind = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["k"], cfg["kind"]
     S = cfg.get("S", 0)   # shared experts (every token, weight 1)
     decode = name.startswith("ocr2_decode") or name == "tiny"
-    steps = args.steps if args.steps is not None else (200 if decode else (20 if kind == "bf16" else 10))
-    # warm-up: --warmup W steps exactly, else at least 20 steps and about
-    # kWarmupSeconds of work (pass A below)
-    warmup = args.warmup if args.warmup is not None else 20
+    explicit_warmup = warmup is not None
+    warmup = warmup if explicit_warmup else 20
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    moe._load()
 
     # ---------------------------------------------------------------- inputs
     n_route = steps + warmup
     routes = []
+    hidden = gu_sets = dn_sets = None
     if kind == "bf16":
         base = wl.make_config(name, device="cpu")
         weight_bytes = sum(base[n].numel() * 2 for n in ("gate_up", "down", "shared_gate_up", "shared_down")
                            if n in base)
-        sets = args.sets or (16 if decode else max(1, min(16, int(np.ceil(2.5e9 / weight_bytes)))))
+        sets = sets_arg or (16 if decode else max(1, min(16, int(np.ceil(2.5e9 / weight_bytes)))))
         gu_sets = [base["gate_up"].to(dev) for _ in range(sets)]
         dn_sets = [base["down"].to(dev) for _ in range(sets)]
         hidden = base["hidden"].to(dev)
@@ -304,6 +304,9 @@ def main():
             g = wl._gen(cfg["seed"] * 1000 + i, "cpu")
             idx, w = wl.route_uniform_softmax(T, E, k, g, "cpu", cfg["routed_scale"])
             routes.append((idx.to(dev), w.to(dev)))
+        # routing on the host too (the CPU baseline reads it; no copies while timed)
+        host_routes = [(i.cpu().numpy(), w.cpu().numpy().astype(np.float64)) for i, w in routes]
+        out_buf = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         if S:   # the shared experts' weights rotate with the routed ones
             sgu_sets = [base["shared_gate_up"].to(dev) for _ in range(sets)]
             sdn_sets = [base["shared_down"].to(dev) for _ in range(sets)]
@@ -312,26 +315,30 @@ def main():
             def step(i):
                 s = i % sets
                 idx, w = routes[i % len(routes)]
-                return entry_sh(hidden, gu_sets[s], dn_sets[s], sgu_sets[s], sdn_sets[s], idx, w, k)
+                return entry_sh(hidden, gu_sets[s], dn_sets[s], sgu_sets[s], sdn_sets[s], idx, w, k,
+                                out=out_buf)
         else:
             entry = moe.moe_experts_decode if decode else moe.moe_experts_prefill
 
             def step(i):
                 s = i % sets
                 idx, w = routes[i % len(routes)]
-                return entry(hidden, gu_sets[s], dn_sets[s], idx, w, k)
+                return entry(hidden, gu_sets[s], dn_sets[s], idx, w, k, out=out_buf)
         dtype = "bf16"
+        problem = base
     else:
         p = wl.make_config(name, device=dev)
         sets = 1
         routes = [(p["top_k_index"], p["top_k_weights"])] * n_route
-
+        host_routes = [(p["top_k_index"].cpu().numpy(), p["top_k_weights"].cpu().numpy())] * n_route
+        out_buf = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         entry = moe.moe_experts_mxfp4 if kind == "mxfp4" else moe.moe_experts_fp8
 
         def step(i):
             return entry(p["x"], p["x_scale"], p["gate_up"], p["gate_up_scale"], p["down"],
-                         p["down_scale"], p["top_k_index"], p["top_k_weights"], k)
+                         p["down_scale"], p["top_k_index"], p["top_k_weights"], k, out=out_buf)
         dtype = kind
+        problem = p
     torch.cuda.synchronize()
 
     # ------------------------------------------------------- pass A: timing
@@ -343,7 +350,7 @@ def main():
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    if args.warmup is None:
+    if not explicit_warmup:
         per_step = (time.perf_counter() - t0) / warmup
         extra = min(kWarmupMaxSteps, max(warmup, int(kWarmupSeconds / per_step) + 1)) - warmup
         for i in range(warmup, warmup + extra):
@@ -363,7 +370,7 @@ def main():
     # ------------------------------------------------------ algorithmic work
     touched_l, valid_l = [], []
     for i in range(steps):
-        idx = routes[(warmup + i) % len(routes)][0].cpu().numpy().reshape(-1)
+        idx = host_routes[(warmup + i) % len(host_routes)][0].reshape(-1)
         valid = idx[(idx >= 0) & (idx < E)]
         touched_l.append(len(np.unique(valid)) + S)     # shared experts: every token
         valid_l.append(valid.size + T * S)
@@ -374,7 +381,7 @@ def main():
 
     # ------------------------------------- pass B: per-kernel stage timing
     stages = {}
-    if not args.no_stage_pass:
+    if stage_pass:
         moe.moe_profile_begin(steps)
         for i in range(steps):
             step(warmup + i)
@@ -430,11 +437,12 @@ def main():
         out["roofline"] = roof
 
     # ------------------------------------------- pass C: router (+ plan)
-    if not args.no_stage_pass:
+    if extras and stage_pass:
         out["router"] = router_pass(moe, torch, np, name, kind, T, E, k, cfg, steps, warmup)
         if decode and kind == "bf16" and not S:
             # pass D: the same decode steps from router logits, the routing
-            # fused into the slice kernel (moe_experts_decode_routed)
+            # fused into the decode kernel (moe_experts_decode_routed, its own
+            # kernel instantiation)
             gl = torch.Generator().manual_seed(cfg["seed"] + 78)
             logit_sets = [(torch.randn(T, E, generator=gl) * 2).to(dev) for _ in range(n_route)]
 
@@ -460,15 +468,138 @@ def main():
             torch.cuda.synchronize()
             calls = moe.moe_profile_end(steps)
             out["router"]["decode_routed"] = {
-                "entry": "moe_experts_decode_routed (softmax router fused into the slice kernel)",
+                "entry": "moe_experts_decode_routed (softmax router fused into the decode kernel)",
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "launches": len(calls[0]) if calls else 0}
+    ctx = (cfg, host_routes, warmup, problem)
+    return out, ctx
+
+
+def summary_of(out):
+    """The compact per-workload entry of the headline line."""
+    r = out.get("roofline", {})
+    return {"us_per_call": out["us_per_call"], "tokens_per_s": out["value"], "steps": out["steps"],
+            "kernel_us_per_call": out.get("kernel_us_per_call", {}).get("mean"),
+            "layer_hbm_GBps": out["layer"]["hbm_GBps"], "layer_TFLOPps": out["layer"]["TFLOPps"],
+            "dominant_kernel": r.get("kernel"), "dominant_kernel_us": r.get("kernel_us"),
+            "roofline": {kk: r.get(kk) for kk in ("bound", "achieved", "peak", "unit", "frac")} if r else None,
+            "stage_us": out.get("stage_us")}
+
+
+def probe(moe, torch, np):
+    """Ceiling probes, for context (never a denominator): a plain streaming
+    read of 41.3 MB (the T=1 decode's weights) and of 143 MB (T=4), rotating
+    over windows that together exceed the last-level cache, timed per launch;
+    and dense torch GEMMs of the prefill workloads' flops (bf16, fp8)."""
+    dev = torch.device("cuda:0")
+    res = {}
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    for label, nbytes in (("read_41MB", 41290240), ("read_143MB", 143 << 20)):
+        nwin = (1 << 30) // nbytes
+        wins = [buf[i * nbytes:(i + 1) * nbytes] for i in range(nwin)]
+        for grid in (256, 512, 1024):
+            for i in range(10):
+                moe.moe_probe_stream_read(wins[i % nwin], grid, sink)
+            torch.cuda.synchronize()
+            n = 50
+            moe.moe_profile_begin(n)
+            for i in range(n):
+                moe.moe_probe_stream_read(wins[i % nwin], grid, sink)
+            torch.cuda.synchronize()
+            us = np.array([row[0][1] * 1e3 for row in moe.moe_profile_end(n)])
+            res[f"{label}_grid{grid}"] = {"us_mean": round(float(us.mean()), 2),
+                                          "us_min": round(float(us.min()), 2),
+                                          "GBps_mean": round(nbytes / (us.mean() * 1e-6) / 1e9, 1)}
+    del buf, wins
+    # dense GEMMs with the flops of the prefill layers' gate_up products
+    for label, (M, N, K, dt) in {"bf16_12288x1792x1280": (12288, 1792, 1280, torch.bfloat16),
+                                 "bf16_8192x8192x8192": (8192, 8192, 8192, torch.bfloat16),
+                                 "fp8_32768x4096x7168": (32768, 4096, 7168, "fp8")}.items():
+        if dt == "fp8":
+            a = torch.randn(M, K, device=dev).to(torch.float8_e4m3fn)
+            b = torch.randn(N, K, device=dev).to(torch.float8_e4m3fn).t()
+            one = torch.ones((), device=dev)
+
+            def run():
+                return torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        else:
+            a = torch.randn(M, K, device=dev, dtype=dt)
+            b = torch.randn(K, N, device=dev, dtype=dt)
+
+            def run():
+                return a @ b
+        try:
+            for _ in range(5):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            res[f"torch_gemm_{label}"] = {"ms": round(ms, 4), "TFLOPps": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        except Exception as exc:   # a torch build without the fp8 product
+            res[f"torch_gemm_{label}"] = {"error": str(exc)[:120]}
+    return res
+
+
+def main():
+    args = parse()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_amd as moe
+    import moe_workloads as wl
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    moe._load()
+    if args.probe:
+        print(json.dumps({"probe": probe(moe, torch, np)}), flush=True)
+        return
+
+    name = args.config
+    kind = wl.CONFIGS[name]["kind"]
+    steps = args.steps if args.steps is not None else default_steps(name, kind)
+    out, (cfg, host_routes, warmup, problem) = measure(
+        moe, torch, np, wl, name, steps, args.warmup, args.sets, stage_pass=not args.no_stage_pass)
+
+    # every other configuration, compactly (its own default steps, capped by --steps)
+    if args.all_configs and not args.no_stage_pass:
+        allc = {}
+        for other in ALL_CONFIGS:
+            if other == name:
+                allc[other] = summary_of(out)
+                continue
+            o_kind = wl.CONFIGS[other]["kind"]
+            o_steps = min(default_steps(other, o_kind), max(steps, 10))
+            o_out, _ = measure(moe, torch, np, wl, other, o_steps, None, None, stage_pass=True,
+                               extras=False)
+            allc[other] = summary_of(o_out)
+            del o_out
+            torch.cuda.empty_cache()
+        out["all_configs"] = allc
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(name, cfg, args.cpu_seconds, routes, warmup,
-                                           base if kind == "bf16" else p)
+        out["cpu_baseline"] = cpu_baseline(name, cfg, args.cpu_seconds, host_routes, warmup, problem)
     print(json.dumps(out), flush=True)
 
 
@@ -526,9 +657,7 @@ def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
         done_tokens, calls = 0, 0
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
-            idx, w = routes[(warmup + calls) % len(routes)]
-            idx = idx.cpu().numpy()
-            w = w.cpu().numpy().astype(np.float64)
+            idx, w = routes[(warmup + calls) % len(routes)]   # host copies, made before timing
             if T <= 16:
                 orc.moe_experts_reference(x, w13, w2, idx, w, **sh)
                 done_tokens += T
@@ -554,10 +683,10 @@ def cpu_baseline(name, cfg, seconds, routes, warmup, problem):
                 return self.t[int(e)].cpu().numpy()
         ref = (orc.moe_experts_mxfp4_reference if cfg["kind"] == "mxfp4"
                else orc.moe_experts_fp8_reference)
+        host = [hp[n].cpu().numpy() for n in ("x", "x_scale", "top_k_index", "top_k_weights")]
         t0 = time.perf_counter()
-        ref(hp["x"].cpu().numpy(), hp["x_scale"].cpu().numpy(), Lazy(p["gate_up"]),
-            Lazy(p["gate_up_scale"]), Lazy(p["down"]), Lazy(p["down_scale"]),
-            hp["top_k_index"].cpu().numpy(), hp["top_k_weights"].cpu().numpy(), tokens=tokens)
+        ref(host[0], host[1], Lazy(p["gate_up"]), Lazy(p["gate_up_scale"]), Lazy(p["down"]),
+            Lazy(p["down_scale"]), host[2], host[3], tokens=tokens)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         done_tokens = len(tokens)

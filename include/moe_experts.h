@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
     MOE_OK = 0,
@@ -106,8 +106,8 @@ int moe_workspace_size(int variant, int64_t T, int H, int F, int E, int k, size_
  * [T*k,H], expert order like h:
  * row m holds slot perm[m]).
  * Entries a variant does not use are SIZE_MAX.  The decode fast path
- * (T <= 4) builds no plan and keeps no h: its workspace holds fp32 partial
- * down products only, and every entry but the total is SIZE_MAX.
+ * (T <= 4) builds no plan: its workspace holds the hand-off flags and h
+ * (bf16 [T*k, F]), and every entry but the total is SIZE_MAX.
  */
 int moe_workspace_layout(int variant, int64_t T, int H, int F, int E, int k, size_t offs[8]);
 
@@ -145,13 +145,24 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
 
 /*
  * bf16 routed experts, gather-GEMV form for a handful of tokens (the model
- * card's decode op: two kernels, no per-expert loop on the host, no
- * device-to-host synchronisation).  Same operands and results contract as
- * moe_experts_prefill.  For T <= 4 (T*k <= 32, H and F <= 2048, and
- * T * ceil(H / 512) <= 12, i.e. H <= 1536 at T = 4) only the
- * selected experts' weights are streamed, each byte once; h and the partial
- * down products stay fp32 and are added in a fixed order (deterministic).
- * Larger calls run the grouped-GEMM path.
+ * card's decode op: two persistent phases, no per-expert loop on the host,
+ * no device-to-host synchronisation).  Same operands and results contract as
+ * moe_experts_prefill.  For T <= 4 (T*k <= 32, H and F <= 2048, H <= 1536
+ * when T > 1, and T*k*F <= 49152) the whole layer is one launch of one
+ * workgroup per compute unit: gate/up rows of the selected experts produce
+ * h, handed between workgroups through the workspace, then the down rows
+ * produce out directly; every selected weight byte is read once.  h is
+ * stored once per (expert, token) as bf16 of W * silu(gate . x) * (up . x),
+ * W the token's summed routing weight on that expert (fp32 products); each
+ * output element is a fixed-order fp32 sum over the token's experts, rounded
+ * once (deterministic, independent of the grid).  The workgroups wait for
+ * each other at the hand-off, so they must be resident together: the
+ * library sizes the grid from the device's occupancy, and if other work
+ * keeps the compute units busy for more than 100 ms the affected rows come
+ * out NaN rather than wait longer.  The workspace needs no initialisation: a
+ * generation word in it, advanced on the device by every call, stamps the
+ * hand-off flags (calls must be ordered, as on one stream).  Larger calls
+ * run the grouped-GEMM path.
  */
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
                        const int32_t* top_k_index, const float* top_k_weights,
@@ -388,6 +399,20 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
  * MOE_ERR_DEVICE.
  */
 /*
+ * Measurement helper (not part of the layer): one launch of a plain
+ * streaming read of `bytes` bytes at `src` by `grid` workgroups of 512
+ * threads (16-byte non-temporal loads, eight in flight per thread), the HBM
+ * ceiling the layer's weight streams are compared with.  Nothing is written
+ * except, never in practice, to `sink` (4 KB).  src and sink are device
+ * pointers, 16-byte aligned; bytes a positive multiple of 16; 1 <= grid <=
+ * 65535.  Timed by the stage recorder as MOE_STAGE_PROBE.
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_SHAPE, MOE_ERR_DEVICE,
+ * MOE_ERR_LAUNCH.
+ */
+int moe_probe_stream_read(const void* src, size_t bytes, int grid, void* sink,
+                          hipStream_t stream);
+
+/*
  * Test hook: caps the persistent grids of the grouped products (and the
  * persistent decode kernel) at max_workgroups (rounded down to a multiple of
  * 8, at least 8), so that every workgroup runs many work items; 0 removes
@@ -404,11 +429,12 @@ enum moe_stage {
     MOE_STAGE_GATE_UP = 1,       /* grouped gate_up product + SwiGLU         */
     MOE_STAGE_DOWN = 2,          /* grouped down product                     */
     MOE_STAGE_COMBINE = 3,       /* router-weighted combine                  */
-    MOE_STAGE_DECODE_SLICES = 4, /* decode form: gate_up, SwiGLU and down    */
+    MOE_STAGE_DECODE = 4,        /* decode form: the whole layer, one launch  */
     MOE_STAGE_QUANTIZE = 5,      /* input-side block-128 fp8 quantisation    */
     MOE_STAGE_SHARED_ROUTE = 6,  /* routing with the shared experts appended */
     MOE_STAGE_ROUTER = 7,        /* router (logits -> ids, weights)          */
     MOE_STAGE_ROUTE_PLAN = 8,    /* router and plan in one launch            */
+    MOE_STAGE_PROBE = 9,         /* moe_probe_stream_read                    */
 };
 int moe_profile_begin(int max_calls);
 int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);

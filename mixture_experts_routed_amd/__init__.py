@@ -72,6 +72,7 @@ def _load():
                                        vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
         "moe_profile_begin": ([i32], i32),
         "moe_set_grid_cap": ([i32], i32),
+        "moe_probe_stream_read": ([vp, sz, i32, vp, vp], i32),
         "moe_experts_decode_noalloc": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp], i32),
         "moe_profile_end": ([i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float),
                              ctypes.POINTER(i32)], i32),
@@ -91,7 +92,8 @@ def exported_symbols():
             "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_profile_begin",
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
-            "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc"]
+            "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc",
+            "moe_probe_stream_read"]
 
 
 class MoeError(RuntimeError):
@@ -142,8 +144,8 @@ def moe_workspace_layout(variant, T, H, F, E, k):
 
 # ------------------------------------------------------------ stage timing
 MOE_PROFILE_MAX_STAGES = 5
-STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode_slices", 5: "quantize",
-               6: "shared_route", 7: "router", 8: "route_plan"}
+STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode", 5: "quantize",
+               6: "shared_route", 7: "router", 8: "route_plan", 9: "probe"}
 
 
 def moe_profile_begin(max_calls):
@@ -168,6 +170,17 @@ def moe_profile_end(max_calls):
                 row.append((STAGE_NAMES.get(sid, str(sid)), float(ms[c * MOE_PROFILE_MAX_STAGES + i])))
         out.append(row)
     return out
+
+
+def moe_probe_stream_read(src, grid, sink):
+    """Measurement helper: one plain streaming read of the device tensor `src`
+    (its whole storage) by `grid` workgroups; `sink` a device tensor of at
+    least 4 KB."""
+    nbytes = src.numel() * src.element_size()
+    with _on(src.device):
+        rc = _load().moe_probe_stream_read(_ptr(src), nbytes, int(grid), _ptr(sink),
+                                           ctypes.c_void_p(_stream(src.device)))
+    _check(rc, "moe_probe_stream_read")
 
 
 def moe_set_grid_cap(max_workgroups):

@@ -111,10 +111,7 @@ struct Layout {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-bool decode_fast_path(int64_t T, int H, int F, int k) {
-    return T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && H <= kDecodeMaxDim &&
-           F <= kDecodeMaxDim && T * ((H / 8 + 63) / 64) <= kDecodeMaxChunkTokens;
-}
+bool decode_fast_path(int64_t T, int H, int F, int k) { return decode_fits(T, k, H, F); }
 
 Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     Layout L;
@@ -127,7 +124,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     };
     if (variant == MOE_VARIANT_DECODE && decode_fast_path(T, H, F, k)) {
         L.decode_fast = true;
-        L.part = take(decode_partial_bytes(T, k, E, H, F));
+        L.part = take(decode_ws_bytes(T, k, F));
         L.total = off;
         return L;
     }
@@ -379,13 +376,9 @@ int run_decode(StageClock& clock, const Layout& L, const uint16_t* hidden,
     if (!L.decode_fast)
         return run_grouped_bf16(clock, L, hidden, gate_up, down, idx, w, residual, T, H, F, E, k,
                                 out, ws, stream);
-    clock.mark(MOE_STAGE_DECODE_SLICES);
-    int rc = launched(launch_decode_slices(hidden, gate_up, down, idx, (int)T, k, E, H, F,
-                                           at<float>(ws, L.part), stream));
-    if (rc) return rc;
-    clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_decode_combine(at<float>(ws, L.part), idx, w, residual, (int)T, k, E, H,
-                                          F, out, stream));
+    clock.mark(MOE_STAGE_DECODE);
+    return launched(launch_decode(hidden, gate_up, down, idx, w, residual, (int)T, k, E, H, F, out,
+                                  at<void>(ws, L.part), stream));
 }
 
 // Both shared-expert entry points: the augmented routing into the workspace,
@@ -705,14 +698,10 @@ int moe_experts_decode_routed(const uint16_t* hidden, const void* logits, const 
     }
     const RouteArgs ra{logits, bias, logits_bf16, mode, E, k, num_groups, topk_group, group_top,
                        routed_scaling_factor};
-    clock.mark(MOE_STAGE_DECODE_SLICES);
-    rc = launched(launch_decode_slices(hidden, gu, dn, nullptr, (int)T, k, E, H, F,
-                                       at<float>(ws, L.part), stream, ra, top_k_index,
-                                       top_k_weights));
-    if (rc) return rc;
-    clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_decode_combine(at<float>(ws, L.part), top_k_index, top_k_weights,
-                                          residual, (int)T, k, E, H, F, out, stream));
+    clock.mark(MOE_STAGE_DECODE);
+    return launched(launch_decode(hidden, gu, dn, nullptr, nullptr, residual, (int)T, k, E, H, F,
+                                  out, at<void>(ws, L.part), stream, ra, top_k_index,
+                                  top_k_weights));
 }
 
 int moe_profile_begin(int max_calls) {
@@ -756,6 +745,18 @@ int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids) {
     *n_calls = n;
     g_prof.used = 0;
     return MOE_OK;
+}
+
+int moe_probe_stream_read(const void* src, size_t bytes, int grid, void* sink,
+                          hipStream_t stream) {
+    if (!src || !sink) return MOE_ERR_NULL;
+    if (!aligned16(src) || !aligned16(sink)) return MOE_ERR_ALIGN;
+    if (bytes < 16 || bytes % 16 || grid < 1 || grid > 65535) return MOE_ERR_SHAPE;
+    int dev, rc;
+    if ((rc = query_device(&dev))) return rc;
+    StageClock clock(stream);
+    clock.mark(MOE_STAGE_PROBE);
+    return launched(launch_probe_read(src, bytes, grid, sink, stream));
 }
 
 int moe_set_grid_cap(int max_workgroups) {

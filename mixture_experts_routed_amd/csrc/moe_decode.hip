@@ -1,98 +1,166 @@
 // moe_decode.hip - gather-GEMV form of the routed-experts layer for a
-// handful of tokens.  Model card "DeepSeek-OCR-2 MoE experts", description:
-// the decode op handles about 1-4 tokens without a per-expert host loop and
-// without a device-to-host sync, streaming only the selected experts'
-// weights.  Here the F dimension is cut into 32-wide slices and one
-// workgroup owns one (selected expert, slice):
-//   - it streams the slice's 32 gate rows and 32 up rows (one read each),
-//     forms h[slot, f] = silu(gate . x) * (up . x) for every slot that chose
-//     the expert, and keeps h in LDS;
-//   - it multiplies h into the slice's columns of the expert's down matrix
-//     (all H rows, 64 bytes each, prefetched into LDS when the workgroup
-//     starts) and writes one fp32 partial sum per (slot, slice, column).
-// A second, small kernel adds the partial sums of every slot in a fixed
-// order, applies the router weights and adds the residual if any (the
-// combine): deterministic, no float atomics.  Every weight byte of a selected expert is read from HBM
-// once, and the whole weight stream runs in a single launch: on MI355X a
-// short stream pays a fixed start-up cost of several microseconds, so one
-// long stream beats two short ones, and splitting F (not H) lets the down
-// product start without any device-wide synchronisation.
+// handful of tokens, in one persistent launch.  Model card "DeepSeek-OCR-2
+// MoE experts", description: the decode op handles about 1-4 tokens with two
+// persistent-shape phases, without a per-expert host loop and without a
+// device-to-host sync, streaming only the selected experts' weights.
+//
+// One workgroup per compute unit (all resident), 8 waves:
+//  - phase 1 (waves 0-4): the (distinct selected expert u, f) pairs, n_u * F
+//    of them, are split evenly over the grid.  A wave streams the gate row f
+//    and the up row F + f of expert u (each byte read once, two steps of
+//    rows in flight), dots them with every token that chose u and stores
+//    W * silu(gate . x) * (up . x) as bf16 into the workspace row of the
+//    (expert, token)'s representative slot, with device-scope stores (W is
+//    the summed routing weight of the token's slots on u);
+//  - hand-off: once all five waves' stores have completed, wave 4 stores
+//    the workgroup's flag (a 64-bit stamp) and polls the flags of the whole
+//    grid (bounded by a clock limit), then copies all of h into LDS with
+//    device-scope loads and raises an LDS flag.  The stamp comes from a
+//    generation word that workgroup 0 advances once every flag is seen, so
+//    consecutive calls (also replays of a captured graph) never match an old
+//    flag;
+//  - phase 2: the H output rows are split evenly over the grid, and a
+//    workgroup's (row, expert) tasks over waves 0-3 and 5-7.  Waves 5-7
+//    request their down rows at kernel start and hold them in registers;
+//    waves 0-3 request theirs after their gate/up work.  A step dots a
+//    batch of down rows with the h rows of the expert's representatives
+//    (from LDS) and sums all of them across the wave at once (register-swap
+//    and DPP moves); y[row][representative] goes to LDS;
+//  - out[t][c] = sum of y over token t's representatives in slot order
+//    (+ residual), written once.
+// So the layer is one launch: no partial sums, no combine kernel, no float
+// atomics, and the result does not depend on timing or grid size.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_route.h"
 
 namespace moe {
 
-constexpr int kDecThreads = 512;  // 8 waves
+constexpr int kDecThreads = 512;
+constexpr int kDecUpWaves = 5;                    // waves 0-4: gate/up rows and h
+constexpr int kDecDownWaves = 8 - kDecUpWaves;    // waves 5-7: down rows from kernel start
+constexpr int kDecPollWave = kDecUpWaves - 1;     // wave 4: the hand-off
+constexpr int kDecP2Waves = 7;                    // waves with down-phase tasks
+// gate/up row pairs per wave step (two steps in flight): three for one token
+// and H <= 1536, otherwise two (the token rows take more registers)
+template <int NT, int NCH>
+constexpr int pair_batch() { return NT == 1 && NCH <= 3 ? 3 : 2; }
 
-// Loads below never sit behind a branch: an out-of-range chunk or row loads
-// a valid address (index clamped), so the compiler's waits count exactly the
-// loads a use depends on.  Token chunks past the row end are zeroed.
+// Device-scope (sc1) accesses: they bypass the non-coherent per-XCD L2, so
+// data written by one workgroup is seen by any other once the store has
+// completed (s_waitcnt).
+__device__ __forceinline__ void st_dev_f32(float* p, float v) {
+    __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u16(uint16_t* p, uint16_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes per lane from global memory into LDS, device scope (sc1 = 16).
+__device__ __forceinline__ void dma16_dev(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 16);
+}
+// every vector-memory operation of this wave has completed
+__device__ __forceinline__ void wait_vm_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Weight rows are read through buffer resources: a load past the resource's
+// size returns zeros without a memory access.  A resource of size 0 serves
+// the tasks of a step past the end of a wave's work, and an offset beyond
+// the size serves the lanes past the end of a row, so no load sits behind a
+// branch (the waits the compiler derives stay exact) and none costs traffic.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset `off`, marked as streamed once (nt = 2).
+__device__ __forceinline__ uint4 load_nt16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 __device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
     return keep ? v : make_uint4(0, 0, 0, 0);
 }
 
-// The routing of all P <= 32 slots, held by the lanes of one wave: lane s
-// has slot s's expert (or -1) and weight.  `first` marks the lanes that are
-// the first slot of a distinct expert (distinct experts are numbered in order
-// of first appearance); `u` is the distinct index of the lane's slot.
-struct WaveRouting {
-    int e;
-    int u;
-    uint64_t first;
-    int n;
-};
-
-__device__ __forceinline__ WaveRouting wave_routing(const int32_t* __restrict__ idx, int P, int E) {
-    const int lane = threadIdx.x & 63;
-    WaveRouting r;
-    int e = lane < P ? idx[lane] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    if (!valid) e = -1;
-    int first = lane;
-    for (int s = 0; s < P; ++s) {
-        const int es = __shfl(e, s, kWave);
-        if (s < first && es == e) first = s;
+// Sum over the 64 lanes of each of the N = 2^n values v[0..N): afterwards
+// lane l holds the total of value l >> (6 - n).  Each halving step pairs
+// every lane with one whose lane bit b differs and trades half of the values
+// with it: the lanes with bit b clear keep the lower half, the others the
+// upper.  Bits 5 and 4 use the gfx950 row-swap moves (v_permlane32_swap:
+// upper half of one register <-> lower half of the other; v_permlane16_swap:
+// odd rows of one <-> even rows of the other), which need no selects; bits
+// 3 .. 0 use DPP moves within a row (mirror, half-mirror, quad permutes),
+// whose pairings also differ in exactly that bit.  N values take N - 1 moves
+// plus 6 - n for the last one, all without LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_level(float lo, float hi, bool upper) {
+    const float keep = upper ? hi : lo, send = upper ? lo : hi;
+    return keep + dpp_f<CTRL>(send);
+}
+// one halving level at lane bit B (5 .. 0)
+template <int B>
+__device__ __forceinline__ float trade(float lo, float hi, int lane) {
+    if constexpr (B == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (B == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        constexpr int ctrl = B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4E : 0xB1;
+        // both operands as plain registers: a select between two array
+        // elements would otherwise become an indexed access
+        asm("" : "+v"(lo), "+v"(hi));
+        return dpp_level<ctrl>(lo, hi, (lane >> B) & 1);
     }
-    const bool is_first = valid && first == lane;
-    r.first = __ballot(is_first);
-    r.n = __popcll(r.first);
-    r.u = valid ? __popcll(r.first & ((1ull << first) - 1ull)) : -1;
-    r.e = e;
-    return r;
+}
+// t + the t of the partner lane at lane bit B
+template <int B>
+__device__ __forceinline__ float fold(float t) {
+    if constexpr (B == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (B == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        return t + dpp_f<B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4E : 0xB1>(t);
+    }
+}
+// the sum over lane bits B .. 0
+template <int B>
+__device__ __forceinline__ float fold_down(float t) {
+    if constexpr (B < 0) return t;
+    else return fold_down<B - 1>(fold<B>(t));
+}
+template <int N, int B = 5>
+__device__ __forceinline__ float transpose_sum(float (&v)[N], int lane) {
+    if constexpr (N == 1) {
+        return fold_down<B>(v[0]);
+    } else {
+        float w[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) w[i] = trade<B>(v[i], v[i + N / 2], lane);
+        return transpose_sum<N / 2, B - 1>(w, lane);
+    }
 }
 
-// Sum over the 64 lanes of each of the N = 2^n values v[0..N): after the
-// call lane l holds the total of value (l >> (6 - n)).  Each halving step
-// trades half of the values with the partner lane, so it takes
-// N - 1 + (6 - n) shuffles instead of 6 N.
-template <int N>
-__device__ __forceinline__ float transpose_sum(float (&v)[N]) {
-    const int lane = threadIdx.x & 63;
-    int bit = 32;
-#pragma unroll
-    for (int step = N / 2; step >= 1; step /= 2, bit /= 2) {
-        const bool hi = lane & bit;
-#pragma unroll
-        for (int i = 0; i < step; ++i) {
-            // both operands as plain registers: a select between two array
-            // elements would otherwise become an indexed (scratch) access
-            float lo_v = v[i], hi_v = v[i + step];
-            asm("" : "+v"(lo_v), "+v"(hi_v));
-            const float keep = hi ? hi_v : lo_v;
-            const float send = hi ? lo_v : hi_v;
-            v[i] = keep + __shfl_xor(send, bit, kWave);
-        }
-    }
-    float s = v[0];
-    for (; bit >= 1; bit /= 2) s += __shfl_xor(s, bit, kWave);
-    return s;
-}
-
-// acc + the dot product of 8 bf16 pairs (one 16-byte chunk each), by four
-// v_dot2c_f32_bf16: the bf16 products are exact in fp32, so only the
-// accumulation rounds, as with fp32 FMAs on the unpacked values, at a third
-// of the vector instructions.
+// acc + the dot product of 8 bf16 pairs by four v_dot2c_f32_bf16 (the bf16
+// products are exact in fp32; only the accumulation rounds).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
@@ -102,340 +170,498 @@ __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float a
     return acc;
 }
 
-// One workgroup per (distinct selected expert u, F slice sl), block index
-// u * nslices + sl.  S = slice width (16 or 32), NCH = 16-byte chunks per
-// lane of an H row (H <= 512 NCH), NT = number of tokens.
-// With ra.logits set the workgroup routes the NT tokens itself first (waves
-// 0 .. NT-1, one token each, into LDS; workgroup 0 also stores the ids and
-// weights for the combine), so a decode call from router logits needs no
-// router launch.
-template <int S, int NCH, int NT>
-__global__ __launch_bounds__(kDecThreads) void decode_slice_kernel(
-    const uint16_t* __restrict__ x, const ExpertWeights w13,
-    const ExpertWeights w2, const int32_t* __restrict__ idx, int k, int E, int H,
-    int F, int nslices, float* __restrict__ part, const RouteArgs ra,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-    constexpr int kSlice = S;
-    constexpr int kRowsPerWave = 2 * S / 8;     // gate/up panel rows per wave
-    constexpr int CPR = S / 8;                  // 16-byte chunks of a down-slice row
-    constexpr int NV = kRowsPerWave * NT;       // dot products per wave
-    // down slice in registers when they allow it (H <= 1536, few tokens):
-    // its rows are then used as they arrive; otherwise it goes through LDS
-    constexpr bool W2REG = NCH <= 3 && NCH * NT <= 8;
-    constexpr int W2ROWS = (3 * 512 + kDecThreads / CPR - 1) / (kDecThreads / CPR);
-    constexpr int NVP = NV <= 8 ? 8 : NV <= 16 ? 16 : 32;  // padded to a power of two
-    static_assert(NV <= 32, "at most 32 dot products per wave");
-    __shared__ u32x4 w2s[W2REG ? 1 : kDecodeMaxDim * CPR];  // down[e][c][f0 .. f0+S): CPR chunks per row
-    __shared__ float dots[2][NT][kSlice];                 // gate / up dot products
-    __shared__ float hs[kDecodeMaxSlots][kSlice];
-    __shared__ int32_t idx_sh[kDecodeMaxSlots];
+// Workspace of the gather-GEMV form (all offsets fixed, see decode_ws_bytes).
+struct DecodeWs {
+    uint64_t* gen;     // generation word
+    uint64_t* flags;   // one per workgroup
+    uint32_t* err;     // set when a hand-off wait timed out
+    uint16_t* h;       // [P][F] bf16
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int P = NT * k;
-    // Work w = u * nslices + sl.  Blocks go to XCDs round-robin; mapping
-    // w to XCD-contiguous runs of even length keeps the two 32-wide slices
-    // that share a 128-byte line of the down matrix in one L2.
-    const int per_xcd = gridDim.x / kXcds;
-    const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    const int u = w / nslices, sl = w - u * nslices;
-    if (u >= kDecodeMaxSlots) return;  // grid padding
-    const int nch = H / 8;
-    // the token rows first: they do not depend on the routing
-    uint4 xv[NT][NCH];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = lane + 64 * i;
-            xv[t][i] = zero_unless(c < nch, *(const uint4*)(x + (int64_t)t * H + min(c, nch - 1) * 8));
+// Routing of the P <= 32 slots as every wave holds it: lane l describes slot
+// l % 32 (both halves of the wave alike) and, for l < n_u, distinct expert l.
+// The h row of (expert u, token t) is stored once, in the row of the first
+// slot with that expert and token (its representative), already multiplied
+// by W = the sum of the weights of u's slots of token t (a token naming an
+// expert twice gets both weights), so the down phase needs no weights.
+struct DecRouting {
+    int n_u;        // distinct experts, in order of first appearance
+    int u_s;        // this lane's slot: its distinct expert (-1 dropped)
+    int t_s;        // its token
+    bool rep;       // it is the representative of (u_s, t_s)
+    float W;        // the summed weight of (u_s, t_s) (on representatives)
+    int ue;         // lane u < n_u: expert id of u
+    uint32_t repm;  // lane u < n_u: representative slots of u
+};
+
+__device__ __forceinline__ DecRouting dec_routing(const int32_t* slot_e, const float* slot_w, int P,
+                                                  int k) {
+    const int lane = threadIdx.x & 63, ls = lane & 31;
+    DecRouting r;
+    const int e = ls < P ? slot_e[ls] : -1;
+    const float wsl = ls < P ? slot_w[ls] : 0.0f;
+    int first = ls;
+    for (int q = 0; q < P; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        if (q < first && eq == e) first = q;
+    }
+    const uint32_t fm = (uint32_t)__ballot(e >= 0 && first == ls);   // first slots (lanes 0-31)
+    r.n_u = __popc(fm);
+    r.u_s = e >= 0 ? __popc(fm & ((1u << first) - 1u)) : -1;
+    r.t_s = ls / k;
+    int rep = ls;
+    float W = 0.0f;
+    for (int q = 0; q < P; ++q) {   // slot order: a fixed summation order
+        const int uq = __builtin_amdgcn_readlane(r.u_s, q);
+        const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), q));
+        if (uq == r.u_s && q / k == r.t_s) {
+            rep = min(rep, q);
+            W += wq;
         }
-    const int32_t* ids = idx;
-    if (ra.logits) {   // uniform over the grid
-        if (wave < NT) {
+    }
+    r.rep = e >= 0 && rep == ls;
+    r.W = W;
+    r.ue = -1;
+    r.repm = 0u;
+    for (int q = 0; q < r.n_u; ++q) {
+        const uint32_t m = (uint32_t)__ballot(r.rep && r.u_s == q);
+        const int eq = __builtin_amdgcn_readlane(e, __builtin_ctz(m));
+        if (lane == q) {
+            r.repm = m;
+            r.ue = eq;
+        }
+    }
+    return r;
+}
+
+// One workgroup per CU.  NT = 1 (one token) or 4 (2-4 tokens; token rows
+// past T are zero); NCH = 16-byte chunks per lane of an H row (H <= 512 NCH);
+// NCF = chunks per lane of an F row; ROUTED: the workgroup routes the tokens
+// itself from router logits first.
+template <int NT, int NCH, int NCF, bool ROUTED>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    const uint16_t* __restrict__ x, const ExpertWeights w13, const ExpertWeights w2,
+    const int32_t* __restrict__ idx, const float* __restrict__ wts,
+    const uint16_t* __restrict__ residual, int T, int k, int E, int H, int F,
+    uint16_t* __restrict__ out, DecodeWs ws, uint64_t spin_ticks,
+    const RouteArgs ra, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    constexpr int DB = 16 / NCF;                    // down rows per phase-2 step
+    constexpr int kPairBatch = pair_batch<NT, NCH>();
+    __shared__ u32x4 h_lds[kDecodeHBytes / 16];     // h rows [P][F], bf16
+    __shared__ float y_lds[kDecodeMaxRows][kDecodeMaxSlots];   // per (row, representative slot)
+    __shared__ int32_t slot_e[kDecodeMaxSlots];     // expert of each slot (-1 dropped)
+    __shared__ float slot_w[kDecodeMaxSlots];       // routing weight of each slot
+    __shared__ int rep_tab[kDecodeMaxSlots][kDecodeMaxT];   // representative slot of (u, token), -1 none
+    __shared__ int arrive, timed_out, h_ready;
+
+    // the wave index as a scalar: everything derived from it (task ranges,
+    // buffer resources) stays in scalar registers instead of being
+    // re-derived per lane around every load
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x, b = blockIdx.x;
+    const int P = T * k;
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+
+    // ---------------------------------------------------------------- set-up
+    // the token rows (phase-1 waves) do not depend on the routing
+    uint4 xv[NT][NCH];
+    const int nch = H / 8;
+    if (wave < kDecUpWaves) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = lane + 64 * i;
+                const bool ok = t < T && c < nch;
+                xv[t][i] = zero_unless(ok, *(const uint4*)(x + (int64_t)min(t, T - 1) * H + min(c, nch - 1) * 8));
+            }
+    }
+    // this call's generation, read once per workgroup at the start (every
+    // workgroup reads it before its flag goes out, and workgroup 0 advances
+    // it only after seeing every flag)
+    uint64_t gen = 0;
+    if (wave == kDecPollWave) gen = ld_dev_u64(ws.gen);
+    if (ROUTED) {
+        if (wave < T) {
             int id;
             float wt;
             if (ra.E <= 64) route_token_lanes<1>(ra, wave, lane, id, wt);
             else if (ra.E <= 128) route_token_lanes<2>(ra, wave, lane, id, wt);
             else route_token_lanes<8>(ra, wave, lane, id, wt);
             if (lane < k) {
-                idx_sh[wave * k + lane] = id;
-                if (blockIdx.x == 0) {
+                slot_e[wave * k + lane] = (unsigned)id < (unsigned)E ? id : -1;
+                slot_w[wave * k + lane] = wt;
+                if (b == 0) {
                     idx_out[wave * k + lane] = id;
                     w_out[wave * k + lane] = wt;
                 }
             }
         }
-        lds_barrier();
-        ids = idx_sh;
+    } else if (tid < P) {
+        const int e = idx[tid];
+        slot_e[tid] = (unsigned)e < (unsigned)E ? e : -1;
+        slot_w[tid] = wts[tid];
     }
-    const WaveRouting R = wave_routing(ids, P, E);
-    if (u >= R.n) return;  // fewer distinct experts than slots (uniform over the workgroup)
-    uint64_t fm = R.first;
-    for (int i = 0; i < u; ++i) fm &= fm - 1ull;
-    const int e = __shfl(R.e, __builtin_ctzll(fm), kWave);
-    const uint64_t slots = __ballot(R.u == u);
-    const int f0 = sl * kSlice;
-
-    // 1. (large variants) the slice of the down matrix, straight into LDS:
-    //    row c of w2s holds down[e][c][f0 .. f0+S) as CPR chunks; one wave
-    //    load covers 64/CPR rows
-    if constexpr (!W2REG) {
-        constexpr int RPI = 64 / CPR;
-        const int r = lane / CPR, ch = lane % CPR;
-        const uint16_t* src = w2.expert(e, (int64_t)H * F) + (int64_t)r * F + f0 + ch * 8;
-        for (int j = wave; j < H / RPI; j += kDecThreads / kWave)
-            __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)j * RPI * F),
-                                             (lds_void*)&w2s[j * 64], 16, 0, 0);
-    }
-
-    // 2./3. this wave's gate/up rows (panel row p in [0, 2S) is gate row f0 + p
-    //    for p < S, else up row F + f0 + p - S; lane chunks c = lane + 64 i),
-    //    dotted with every token.
-    constexpr int RB = kRowsPerWave;
-    uint4 w2r[W2REG ? W2ROWS : 1];
-    float v[NVP];
-#pragma unroll
-    for (int i = NV; i < NVP; ++i) v[i] = 0.0f;
-#pragma unroll
-    for (int rb = 0; rb < kRowsPerWave; rb += RB) {
-        uint4 wv[RB][NCH];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int p = kRowsPerWave * wave + rb + r;
-            const int row = p < kSlice ? f0 + p : F + f0 + (p - kSlice);
-            const uint16_t* src = w13.expert(e, (int64_t)2 * F * H) + (int64_t)row * H;
-#pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = lane + 64 * i;
-                // a chunk past the row end repeats the last one; it meets a
-                // zeroed token chunk, so it adds nothing
-                wv[r][i] = load_nt16(src + min(c, nch - 1) * 8);
-            }
-        }
-        // (small variants) this thread's rows of the down slice, requested
-        // after the gate/up rows so that the dot products need not wait for
-        // them: rows c = tid / CPR + (512 / CPR) j, chunk tid % CPR
-        if constexpr (W2REG) {
-            const uint16_t* src = w2.expert(e, (int64_t)H * F) + (int64_t)(tid / CPR) * F + f0 + (tid % CPR) * 8;
-#pragma unroll
-            for (int j = 0; j < W2ROWS; ++j) {
-                const int c = tid / CPR + (kDecThreads / CPR) * j;
-                // a row past H repeats row H - 1 and is never stored
-                w2r[j] = load_nt16(src + (int64_t)(min(c, H - 1) - tid / CPR) * F);
-            }
-        }
-        // every weight load is in flight before the first dot product
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) acc = dot8_bf16(wv[r][i], xv[t][i], acc);
-                v[(rb + r) * NT + t] = acc;
-            }
-    }
-    const float tot = transpose_sum<NVP>(v);
-    {
-        constexpr int n = __builtin_ctz(NVP);
-        const int vi = lane >> (6 - n);
-        if ((lane & ((1 << (6 - n)) - 1)) == 0 && vi < NV) {  // one lane per value
-            const int r = vi / NT, t = vi - r * NT;
-            const int p = kRowsPerWave * wave + r;
-            dots[p < kSlice ? 0 : 1][t][p & (kSlice - 1)] = tot;
-        }
+    if (tid == 0) {
+        arrive = 0;
+        timed_out = 0;
+        h_ready = 0;
     }
     lds_barrier();
+    const DecRouting R = dec_routing(slot_e, slot_w, P, k);
+    const int n_u = R.n_u;
+    // lane u < n_u: the representative slot of (u, token t), -1 if none
+    int rep_of[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint32_t tm = t < T ? R.repm & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
+        rep_of[t] = tm ? __builtin_ctz(tm) : -1;
+    }
+    if (tid < kDecodeMaxSlots * kDecodeMaxT) {   // waves 0-1
+        const int u = tid / kDecodeMaxT, t = tid % kDecodeMaxT;
+        const uint32_t m = (uint32_t)__shfl(R.repm, u, kWave);
+        const uint32_t tm = t < T ? m & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
+        rep_tab[u][t] = u < n_u && tm ? __builtin_ctz(tm) : -1;
+    }
 
-    // 4. h for every slot of the expert (slot s belongs to token s / k)
-    for (int i = tid; i < kDecodeMaxSlots * kSlice; i += kDecThreads) {
-        const int s = i / kSlice, f = i - s * kSlice;
-        if (s < P && ((slots >> s) & 1ull)) {
-            const int t = s / k;
-            hs[s][f] = silu(dots[0][t][f]) * dots[1][t][f];
+    // Phase-2 tasks (row r of [c0, c1), expert u), u fastest, in contiguous
+    // ranges.  Waves 5, 6, 7 fetch their rows at kernel start and hold them
+    // in registers; waves 0-3 fetch theirs after their gate/up work; wave 4
+    // polls the flags.  When every wave needs at most one step, the tasks are
+    // spread over all seven (the down products are then short); otherwise
+    // waves 5-7 take two steps each first and waves 0-3 split the rest.
+    const int c0 = (int)((int64_t)b * H / G), c1 = (int)((int64_t)(b + 1) * H / G);
+    const int ntask_wg = (c1 - c0) * n_u;
+    const int npre = min(ntask_wg, kDecDownWaves * 2 * DB);
+    int ta = 0, tb = 0;
+    if (ntask_wg <= kDecP2Waves * DB) {
+        if (wave != kDecPollWave) {
+            const int q = wave < kDecPollWave ? wave : wave - 1;   // 0..6
+            ta = ntask_wg * q / kDecP2Waves;
+            tb = ntask_wg * (q + 1) / kDecP2Waves;
         }
+    } else if (wave >= kDecUpWaves) {
+        const int q = wave - kDecUpWaves;
+        ta = npre * q / kDecDownWaves;
+        tb = npre * (q + 1) / kDecDownWaves;
+    } else if (wave != kDecPollWave) {
+        const int rest = ntask_wg - npre;
+        ta = npre + rest * wave / kDecPollWave;
+        tb = npre + rest * (wave + 1) / kDecPollWave;
     }
-    if constexpr (W2REG) {
-        lds_barrier();  // h is complete
-    } else {
-        // the down slice has landed (this wave's loads), then every wave's
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    // 5. partial down products: CPR lanes per row c, 8 values of the slice each
-    const int q = tid % CPR;
+    const int ntask = tb - ta;
+    const int nchf = F / 8;
+    uint4 da[DB][NCF], db[DB][NCF];
+    auto load_down = [&](uint4 (&buf)[DB][NCF], int step) {
+        const int t0 = ta + step * DB;
+        int rr = t0 / max(n_u, 1), u = t0 - rr * max(n_u, 1);
 #pragma unroll
-    for (int j = 0; j < (W2REG ? W2ROWS : (kDecodeMaxDim * CPR + kDecThreads - 1) / kDecThreads); ++j) {
-        const int c = tid / CPR + (kDecThreads / CPR) * j;
-        if (c >= H) break;
-        float wf[8];
-        if constexpr (W2REG) {
-            unpack8(w2r[j], wf);
-        } else {
-            const u32x4 wc = w2s[c * CPR + q];
-            unpack8(make_uint4(wc.x, wc.y, wc.z, wc.w), wf);
-        }
-        uint64_t sm = slots;
-        while (sm) {
-            const int s = __builtin_ctzll(sm);
-            sm &= sm - 1ull;
-            const float* hr = &hs[s][q * 8];
-            float acc = 0.0f;
+        for (int i = 0; i < DB; ++i) {
+            const bool real = step * DB + i < ntask;
+            // a task past the end reads through an empty resource (zeros)
+            const rsrc_t m = make_rsrc(w2.expert(__builtin_amdgcn_readlane(R.ue, real ? u : 0), (int64_t)H * F),
+                                       real ? (uint32_t)H * F * 2 : 0u);
+            const uint32_t row = (uint32_t)(c0 + rr) * F;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc += wf[j] * hr[j];
-            acc += pair_swap(acc);  // lanes q ^ 1
-            if (CPR == 4)           // lanes q ^ 2
-                acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
-            if (q == 0) part[((int64_t)s * nslices + sl) * H + c] = acc;
-        }
-    }
-}
-
-// out[t, c] = sum_j w[t, j] * sum_sl part[t*k + j, sl, c] over valid slots.
-// A workgroup owns 16 columns; its 16 column groups split the (slot, slice)
-// pairs (pair = g + 16 i, pair = slot * nslices + slice) and their sums are
-// added in group order, so the result does not depend on timing.  Loads go
-// out in batches of 16 with no dependences between them; dropped slots have
-// weight zero (no branch in the loop).
-// The batch B of loads a thread has in flight is 16, or 64 when there are
-// more than 16 x 16 pairs, so that up to 1024 pairs take one round trip.
-constexpr int kCombCols = 16, kCombGroups = 16;  // many small workgroups: latency-bound
-constexpr int kCombThreads = kCombCols * kCombGroups;
-template <int kCombBatch>
-__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ idx, const float* __restrict__ wts,
-    const uint16_t* __restrict__ residual, int T, int k, int E, int H, int nslices,
-    uint16_t* __restrict__ out) {
-    // per slot: the routing weight's bits (0 for a dropped slot), a mask
-    // that is all ones for a valid slot, zero for a dropped one, and the token
-    __shared__ int4 wsl[kDecodeMaxSlots];
-    __shared__ float red[kCombGroups][kDecodeMaxT][kCombCols];
-    const int cl = threadIdx.x % kCombCols, g = threadIdx.x / kCombCols;
-    const int c = blockIdx.x * kCombCols + cl;
-    const int P = T * k;
-    const int npairs = P * nslices;
-    // the first batch of partial sums is requested before the slot weights
-    // are read (no dependence between them)
-    float v[kCombBatch];
-#pragma unroll
-    for (int i = 0; i < kCombBatch; ++i) {
-        const int pr = min(g + kCombGroups * i, npairs - 1);
-        v[i] = part[(int64_t)pr * H + c];
-    }
-    if (threadIdx.x < kDecodeMaxSlots) {
-        const int sc = min((int)threadIdx.x, P - 1);  // both loads unconditional
-        const int e = idx[sc];
-        const float wv = wts[sc];
-        const bool valid = (int)threadIdx.x < P && (unsigned)e < (unsigned)E;
-        wsl[threadIdx.x] = make_int4(valid ? __float_as_int(wv) : 0, valid ? -1 : 0, sc / k, 0);
-    }
-    __syncthreads();
-    float acc[kDecodeMaxT] = {0.0f, 0.0f, 0.0f, 0.0f};
-    // slot s and slice sl of pair g + kCombGroups j, stepped without
-    // divisions: each step adds dq slots and dr slices
-    const int dq = kCombGroups / nslices, dr = kCombGroups - dq * nslices;
-    int s = g / nslices, sl = g - s * nslices;
-    for (int base = g; base < npairs; base += kCombGroups * kCombBatch) {
-        if (base != g) {
-#pragma unroll
-            for (int i = 0; i < kCombBatch; ++i) {
-                const int pr = min(base + kCombGroups * i, npairs - 1);
-                v[i] = part[(int64_t)pr * H + c];
+            for (int j = 0; j < NCF; ++j) {
+                // chunks past the row end read zeros (offset beyond the bound)
+                const int ch = lane + 64 * j;
+                buf[i][j] = load_nt16(m, ch < nchf ? (row + ch * 8) * 2 : 0x80000000u);
+            }
+            if (++u == n_u) {
+                u = 0;
+                ++rr;
             }
         }
-#pragma unroll
-        for (int i = 0; i < kCombBatch; ++i)
-            if (base + kCombGroups * i >= npairs) v[i] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kCombBatch; ++i) {
-            // a dropped slot's partial sums are never written: masked out,
-            // not multiplied by zero (stale memory may hold NaN); pairs past
-            // the end hold 0 and read the last slot's entry
-            const int4 ws = wsl[min(s, P - 1)];
-            const float wv = __int_as_float(__float_as_int(v[i] * __int_as_float(ws.x)) & ws.y);
-#pragma unroll
-            for (int tt = 0; tt < kDecodeMaxT; ++tt)
-                if (tt == ws.z) acc[tt] += wv;
-            sl += dr;
-            s += dq;
-            if (sl >= nslices) {
-                sl -= nslices;
-                ++s;
+    };
+
+    // --------------------------------------------------------------- phase 1
+    // (the prefetch of waves 5-7 is the other branch, so that the two sets
+    // of staging registers are never live together)
+    if (wave < kDecUpWaves) {
+        const int N1 = n_u * F;
+        const int p0 = (int)((int64_t)b * N1 / G), p1 = (int)((int64_t)(b + 1) * N1 / G);
+        const int q0 = p0 + (int)((int64_t)(p1 - p0) * wave / kDecUpWaves);
+        const int q1 = p0 + (int)((int64_t)(p1 - p0) * (wave + 1) / kDecUpWaves);
+        const int nstep = (q1 - q0 + kPairBatch - 1) / kPairBatch;
+        const int u0 = n_u > 0 ? q0 / F : 0, f0 = q0 - u0 * F;
+        // pair q0 + i is (u, f): f0 + i carried into the following experts
+        auto pair_uf = [&](int i, int& u, int& f) {
+            f = f0 + i;
+            u = u0;
+            while (f >= F) {
+                f -= F;
+                ++u;
             }
+        };
+        uint4 wa[kPairBatch][2][NCH], wb[kPairBatch][2][NCH];
+        auto load_pairs = [&](uint4 (&buf)[kPairBatch][2][NCH], int step) {
+#pragma unroll
+            for (int j = 0; j < kPairBatch; ++j) {
+                const int i = step * kPairBatch + j;
+                const bool real = q0 + i < q1;
+                int u, f;
+                pair_uf(real ? i : 0, u, f);
+                // a pair past the end reads through an empty resource (zeros)
+                const rsrc_t m = make_rsrc(w13.expert(__builtin_amdgcn_readlane(R.ue, u), (int64_t)2 * F * H),
+                                           real ? (uint32_t)F * H * 4 : 0u);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const uint32_t row = (uint32_t)(r ? F + f : f) * H;
+#pragma unroll
+                    for (int i2 = 0; i2 < NCH; ++i2) {
+                        // a chunk past the row end repeats the last one and
+                        // meets a zeroed token chunk
+                        const int ch = min(lane + 64 * i2, nch - 1);
+                        buf[j][r][i2] = load_nt16(m, (row + ch * 8) * 2);
+                    }
+                }
+            }
+        };
+        // value (j * 2 + r) * NT + t of a step: row r (gate, up) of pair j
+        // dotted with token t
+        constexpr int NV1 = kPairBatch * 2 * NT;
+        constexpr int NVP1 = NV1 <= 8 ? 8 : NV1 <= 16 ? 16 : NV1 <= 32 ? 32 : 64;
+        constexpr int LB1 = 6 - __builtin_ctz(NVP1);
+        auto compute_pairs = [&](const uint4 (&buf)[kPairBatch][2][NCH], int step) {
+            float v[NVP1];
+#pragma unroll
+            for (int i = NV1; i < NVP1; ++i) v[i] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kPairBatch; ++j)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < NCH; ++i) acc = dot8_bf16(buf[j][r][i], xv[t][i], acc);
+                        v[(j * 2 + r) * NT + t] = acc;
+                    }
+            const float tot = transpose_sum<NVP1>(v, lane);
+            // lane (j, s): pair j of the step, slot s (its representative row)
+            const int sl = lane & 31, ts = min(R.t_s, NT - 1);
+#pragma unroll
+            for (int jb = 0; jb < kPairBatch; jb += 2) {
+                const int j = jb + (lane >> 5);
+                const float g = __shfl(tot, ((j * 2) * NT + ts) << LB1, kWave);
+                const float up = __shfl(tot, ((j * 2 + 1) * NT + ts) << LB1, kWave);
+                const int i = step * kPairBatch + j;
+                if (j < kPairBatch && q0 + i < q1 && R.rep) {
+                    int u, f;
+                    pair_uf(i, u, f);
+                    if (R.u_s == u)
+                        st_dev_u16(ws.h + (int64_t)sl * F + f, (uint16_t)f32_to_bf16(R.W * (silu(g) * up)));
+                }
+            }
+        };
+        // two buffers in turn: a step's rows are requested two steps ahead
+        // (the conditions are wave-uniform)
+        if (nstep > 0) load_pairs(wa, 0);
+        if (nstep > 1) load_pairs(wb, 1);
+        for (int st = 0; st < nstep; st += 2) {
+            compute_pairs(wa, st);
+            if (st + 2 < nstep) load_pairs(wa, st + 2);
+            if (st + 1 < nstep) compute_pairs(wb, st + 1);
+            if (st + 3 < nstep) load_pairs(wb, st + 3);
+        }
+        wait_vm_all();   // this wave's h stores have completed
+        if (lane == 0) atomicAdd(&arrive, 1);
+        if (wave == kDecPollWave) {
+            // once the other four have stored their h: publish this
+            // workgroup's, then wait for every workgroup's
+            while (__hip_atomic_load(&arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kDecUpWaves)
+                __builtin_amdgcn_s_sleep(1);
+            const uint64_t stamp = gen + 1;
+            if (lane == 0) st_dev_u64(ws.flags + b, stamp);
+            bool ok = false;
+            while (true) {
+                bool all = true;
+                for (int q = lane; q < G; q += 64) all &= ld_dev_u64(ws.flags + q) == stamp;
+                if (__all(all)) {
+                    ok = true;
+                    break;
+                }
+                if (__builtin_amdgcn_s_memrealtime() - t_start > spin_ticks) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ok && lane == 0) {
+                timed_out = 1;
+                atomicOr(ws.err, 1u);
+            }
+            // every workgroup has read this call's generation: advance it
+            if (b == 0 && lane == 0) st_dev_u64(ws.gen, stamp);
+            // h of every slot into LDS (device-scope loads), 1 KB per instruction
+            const int nkb = (P * F * 2 + 1023) / 1024;
+            for (int q = 0; q < nkb; ++q)
+                dma16_dev((const char*)ws.h + (int64_t)q * 1024 + lane * 16, (char*)h_lds + q * 1024);
+            wait_vm_all();
+            __hip_atomic_store(&h_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else if (ntask > 0) {
+            load_down(da, 0);
+            if (ntask > DB) load_down(db, 1);
+        }
+    } else if (ntask > 0) {
+        load_down(da, 0);
+        if (ntask > DB) load_down(db, 1);
+    }
+
+    // --------------------------------------------------------------- phase 2
+    if (ntask > 0) {
+        // value i * NT + t of a step: task i's down row dotted with the h row
+        // of its expert's representative slot for token t (zero weights past
+        // the end; a missing representative gives a value that is dropped)
+        constexpr int NV = DB * NT;
+        constexpr int NVP = NV <= 8 ? 8 : NV <= 16 ? 16 : NV <= 32 ? 32 : 64;
+        constexpr int LB = 6 - __builtin_ctz(NVP);   // lanes per value: 1 << LB
+        int hch[NCF];   // this lane's h chunks (tail lanes: the last one, times zero weights)
+#pragma unroll
+        for (int j = 0; j < NCF; ++j) hch[j] = min(lane + 64 * j, nchf - 1);
+        auto compute_down = [&](const uint4 (&buf)[DB][NCF], int step) {
+            const int t0 = ta + step * DB;
+            int rr = t0 / n_u, u = t0 - rr * n_u;
+            float v[NVP];
+#pragma unroll
+            for (int i = NV; i < NVP; ++i) v[i] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    // scalar: the h row of u's representative for token t
+                    const int r = max(__builtin_amdgcn_readlane(rep_of[t], u), 0);
+                    const u32x4* hs = h_lds + r * (F / 8);
+                    float part = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NCF; ++j) {
+                        const u32x4 hv = hs[hch[j]];
+                        part = dot8_bf16(buf[i][j], make_uint4(hv.x, hv.y, hv.z, hv.w), part);
+                    }
+                    v[i * NT + t] = part;
+                }
+                if (++u == n_u) {
+                    u = 0;
+                    ++rr;
+                }
+            }
+            const float tot = transpose_sum<NVP>(v, lane);
+            const int vi = lane >> LB;
+            if ((lane & ((1 << LB) - 1)) == 0 && vi < NV) {
+                const int i = vi / NT, t = vi - (vi / NT) * NT;
+                if (step * DB + i < ntask) {
+                    const int task = t0 + i;
+                    const int rw = task / n_u, uw = task - rw * n_u;
+                    const int r = rep_tab[uw][t];
+                    if (r >= 0) y_lds[rw][r] = tot;
+                }
+            }
+        };
+        const int nsteps = (ntask + DB - 1) / DB;
+        // the poll wave's signal that h is in LDS (it always comes: the
+        // poll is bounded)
+        while (__hip_atomic_load(&h_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+            __builtin_amdgcn_s_sleep(1);
+        for (int st = 0; st < nsteps; st += 2) {
+            compute_down(da, st);
+            if (st + 2 < nsteps) load_down(da, st + 2);
+            if (st + 1 < nsteps) compute_down(db, st + 1);
+            if (st + 3 < nsteps) load_down(db, st + 3);
         }
     }
-#pragma unroll
-    for (int t = 0; t < kDecodeMaxT; ++t) red[g][t][cl] = acc[t];
-    __syncthreads();
-    if (threadIdx.x < kCombCols * kDecodeMaxT) {
-        const int t = threadIdx.x / kCombCols, cc = threadIdx.x % kCombCols;
-        if (t < T) {
-            float o = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kCombGroups; ++i) o += red[i][t][cc];
-            const int64_t oi = (int64_t)t * H + blockIdx.x * kCombCols + cc;
-            if (residual) o += bf16_to_f32(residual[oi]);
-            out[oi] = (uint16_t)f32_to_bf16(o);
+    lds_barrier();   // every row's values are in LDS (and timed_out is final)
+
+    // out[t][c] = sum over token t's representative slots (ascending) of
+    // y[c][slot], + residual; one thread per (token, row)
+    const uint32_t reps = (uint32_t)__ballot(R.rep);   // lanes 0-31: slots 0-31
+    for (int q = tid; q < T * (c1 - c0); q += kDecThreads) {
+        const int t = q / (c1 - c0), rr = q - t * (c1 - c0);
+        uint32_t tm = reps & (((1u << k) - 1u) << (t * k));   // token t's representative slots
+        float o = 0.0f;
+        while (tm) {
+            const int r = __builtin_ctz(tm);
+            tm &= tm - 1u;
+            o += y_lds[rr][r];
         }
+        if (residual) o += bf16_to_f32(residual[(int64_t)t * H + c0 + rr]);
+        out[(int64_t)t * H + c0 + rr] = (uint16_t)f32_to_bf16(timed_out ? __builtin_nanf("") : o);
     }
 }
 
-template <int S, int NCH>
-static void launch_slices(dim3 grid, const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
-                          const int32_t* idx, int T, int k, int E, int H, int F, int ns, float* part,
-                          hipStream_t s, const RouteArgs& ra, int32_t* io, float* wo) {
-    if (NCH * T > kDecodeMaxChunkTokens) return;  // excluded by decode_fast_path
-    switch (T) {
-        case 1: MOE_LAUNCH((decode_slice_kernel<S, NCH, 1>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
-        case 2: MOE_LAUNCH((decode_slice_kernel<S, NCH, 2>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
-        case 3: MOE_LAUNCH((decode_slice_kernel<S, NCH, 3>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
-        case 4: MOE_LAUNCH((decode_slice_kernel<S, NCH < 4 ? NCH : 3, 4>), grid, dim3(kDecThreads), 0, s, x, w13, w2, idx, k, E, H, F, ns, part, ra, io, wo); break;
-        default: break;
-    }
+template <int NT, int NCH, int NCF, bool ROUTED>
+static int decode_grid() {
+    static const int g = std::min(resident_grid((const void*)decode_kernel<NT, NCH, NCF, ROUTED>,
+                                                kDecThreads, device_cu_count()),
+                                  kDecodeMaxGrid);
+    return capped_grid(g);
 }
 
-template <int S>
-static hipError_t launch_width(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
-                               const int32_t* idx, int T, int k, int E, int H, int F, int umax,
-                               float* part, hipStream_t s, const RouteArgs& ra, int32_t* io,
-                               float* wo) {
-    const int ns = F / S;
-    // padded to a multiple of 16 (even runs per XCD); padding blocks map to
-    // u >= umax, where the routing has no distinct expert
-    const dim3 grid((unsigned)((umax * ns + 15) / 16 * 16));
-    switch ((H / 8 + 63) / 64) {
-        case 1: launch_slices<S, 1>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
-        case 2: launch_slices<S, 2>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
-        case 3: launch_slices<S, 3>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
-        case 4: launch_slices<S, 4>(grid, x, w13, w2, idx, T, k, E, H, F, ns, part, s, ra, io, wo); break;
-        default: return hipErrorInvalidValue;  // H > 2048 is routed to the grouped path by the caller
+// The wait for the other workgroups' flags gives up after this many ticks of
+// the 100 MHz constant clock (100 ms): a wait that long means the grid is
+// not resident (other work holds the CUs); the rows then come out NaN and
+// the workspace's error word is set.
+constexpr uint64_t kSpinTicks = 10000000ull;
+
+template <int NT, int NCH, int NCF, bool ROUTED>
+static void launch_one(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
+                       const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
+                       int E, int H, int F, uint16_t* out, const DecodeWs& dws, hipStream_t s,
+                       const RouteArgs& ra, int32_t* io, float* wo) {
+    // at most kDecodeMaxRows output rows per workgroup
+    const int G = std::max(decode_grid<NT, NCH, NCF, ROUTED>(), (H + kDecodeMaxRows - 1) / kDecodeMaxRows);
+    MOE_LAUNCH((decode_kernel<NT, NCH, NCF, ROUTED>), dim3(G), dim3(kDecThreads), 0, s, x, w13, w2, idx, w, residual, T, k, E, H, F, out, dws,
+               kSpinTicks, ra, io, wo);
+}
+
+template <int NT, int NCH, bool ROUTED>
+static hipError_t launch_ncf(int ncf, const uint16_t* x, const ExpertWeights& w13,
+                             const ExpertWeights& w2, const int32_t* idx, const float* w,
+                             const uint16_t* residual, int T, int k, int E, int H, int F,
+                             uint16_t* out, const DecodeWs& d, hipStream_t s, const RouteArgs& ra,
+                             int32_t* io, float* wo) {
+    switch (ncf) {
+        case 1: launch_one<NT, NCH, 1, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
+        case 2: launch_one<NT, NCH, 2, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
+        default: launch_one<NT, NCH, 4, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
-                                const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
-                                int H, int F, float* part, hipStream_t s, const RouteArgs& ra,
-                                int32_t* idx_out, float* w_out) {
-    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    return g.slice == 16
-               ? launch_width<16>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s, ra, idx_out, w_out)
-               : launch_width<32>(x, w13, w2, idx, T, k, E, H, F, g.umax, part, s, ra, idx_out, w_out);
+template <bool ROUTED>
+static hipError_t launch_decode_t(const uint16_t* x, const ExpertWeights& w13,
+                                  const ExpertWeights& w2, const int32_t* idx, const float* w,
+                                  const uint16_t* residual, int T, int k, int E, int H, int F,
+                                  uint16_t* out, void* ws, hipStream_t s, const RouteArgs& ra,
+                                  int32_t* io, float* wo) {
+    char* base = (char*)ws;
+    const DecodeWs d{(uint64_t*)base, (uint64_t*)(base + 256), (uint32_t*)(base + 256 + 8 * kDecodeMaxGrid),
+                     (uint16_t*)(base + kDecodeHOffset)};
+    const int nch = (H / 8 + 63) / 64;
+    const int ncf = (F / 8 + 63) / 64;   // 1, 2, 3 (as 4) or 4
+    if (T == 1) {
+        switch (nch) {
+            case 1: return launch_ncf<1, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+            case 2: return launch_ncf<1, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+            case 3: return launch_ncf<1, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+            case 4: return launch_ncf<1, 4, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (nch) {
+        case 1: return launch_ncf<4, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+        case 2: return launch_ncf<4, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+        case 3: return launch_ncf<4, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+        default: return hipErrorInvalidValue;   // excluded by decode_fast_path
+    }
 }
 
-hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
-                                 const uint16_t* residual, int T, int k, int E, int H, int F,
-                                 uint16_t* out, hipStream_t s) {
-    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    if (T * k * g.nslices > kCombGroups * 16)
-        MOE_LAUNCH(decode_combine_kernel<64>, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0,
-                   s, part, idx, w, residual, T, k, E, H, g.nslices, out);
-    else
-        MOE_LAUNCH(decode_combine_kernel<16>, dim3((unsigned)(H / kCombCols)), dim3(kCombThreads), 0,
-                   s, part, idx, w, residual, T, k, E, H, g.nslices, out);
-    return hipGetLastError();
+hipError_t launch_decode(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
+                         const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
+                         int E, int H, int F, uint16_t* out, void* ws, hipStream_t s,
+                         const RouteArgs& ra, int32_t* idx_out, float* w_out) {
+    if (ra.logits)
+        return launch_decode_t<true>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, ws, s, ra,
+                                     idx_out, w_out);
+    return launch_decode_t<false>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, ws, s, ra,
+                                  idx_out, w_out);
 }
 
 }  // namespace moe

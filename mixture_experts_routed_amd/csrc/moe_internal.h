@@ -103,50 +103,40 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
                           const uint16_t* residual, int64_t T, int k, int H, uint16_t* out,
                           hipStream_t s);
 
-// Decode gather-GEMV (T small): one launch streams the selected experts'
-// weights in 32-wide F slices and writes fp32 partial down products
-// part[slot][slice][H]; a second small launch adds them up with the router
-// weights.  Limits of this form: T <= 4, T*k <= 32, H <= 2048, F <= 2048
-// and T * ceil(H / 512) <= 12 (the token rows and weight rows of a wave stay
-// in registers); larger calls take the grouped path.
+// Decode gather-GEMV (a few tokens): one persistent launch (see
+// moe_decode.hip) streams the selected experts' gate/up rows into h, hands h
+// over between workgroups through the workspace, then streams their down
+// rows and writes out.  Limits of this form: T <= 4, T*k <= 32, H and F <=
+// 2048, H <= 1536 when T > 1 (the token rows stay in registers), and
+// h = T*k*F bf16 values within the LDS budget; larger calls take the
+// grouped path.
 constexpr int kDecodeMaxT = 4;
 constexpr int kDecodeMaxSlots = 32;
 constexpr int kDecodeMaxDim = 2048;
-constexpr int kDecodeMaxChunkTokens = 12;
-
-struct DecodeGeometry {
-    int umax;     // most distinct experts a call can select: min(T*k, E)
-    int slice;    // F values per workgroup
-    int nslices;  // F / slice
-};
-
-inline DecodeGeometry decode_geometry(int64_t T, int k, int E, int H, int F) {
-    (void)H;
-    DecodeGeometry g;
-    const int P = (int)(T * k);
-    g.umax = P < E ? P : E;
-    g.slice = 32;  // 16-wide slices (more workgroups) measured slower at T = 1
-    g.nslices = F / g.slice;
-    return g;
+constexpr int kDecodeMaxGrid = 1024;      // flag slots in the workspace
+constexpr int kDecodeHBytes = 96 << 10;   // LDS budget for h (bf16)
+constexpr int kDecodeMaxRows = 64;        // output rows per workgroup (grid >= H / 64)
+// workspace: generation word, flags [kDecodeMaxGrid] u64, error word, h [T*k][F] bf16
+constexpr size_t kDecodeHOffset = 256 + 8 * (size_t)kDecodeMaxGrid + 256;
+inline size_t decode_h_bytes(int64_t T, int k, int F) {
+    return ((size_t)(T * k) * (size_t)F * 2 + 1023) / 1024 * 1024;   // whole 1 KB copies
 }
-
-// Bytes of the partial sums of the decode form.
-inline size_t decode_partial_bytes(int64_t T, int k, int E, int H, int F) {
-    const DecodeGeometry g = decode_geometry(T, k, E, H, F);
-    return (size_t)(T * k) * (size_t)g.nslices * (size_t)H * sizeof(float);
+inline size_t decode_ws_bytes(int64_t T, int k, int F) { return kDecodeHOffset + decode_h_bytes(T, k, F); }
+inline bool decode_fits(int64_t T, int k, int H, int F) {
+    const int nch = (H / 8 + 63) / 64;
+    return T >= 1 && T <= kDecodeMaxT && T * k <= kDecodeMaxSlots && H <= kDecodeMaxDim &&
+           F <= kDecodeMaxDim && (T == 1 ? nch <= 4 : nch <= 3) &&
+           decode_h_bytes(T, k, F) <= (size_t)kDecodeHBytes;
 }
 
 // With ra.logits set, the kernel routes the T tokens itself (every
-// workgroup, redundantly; workgroup 0 also writes idx_out / w_out for the
-// combine and the caller) and `idx` is unused.
-hipError_t launch_decode_slices(const uint16_t* x, const ExpertWeights& w13,
-                                const ExpertWeights& w2, const int32_t* idx, int T, int k, int E,
-                                int H, int F, float* part, hipStream_t s,
-                                const RouteArgs& ra = RouteArgs{}, int32_t* idx_out = nullptr,
-                                float* w_out = nullptr);
-hipError_t launch_decode_combine(const float* part, const int32_t* idx, const float* w,
-                                 const uint16_t* residual, int T, int k, int E, int H, int F,
-                                 uint16_t* out, hipStream_t s);
+// workgroup, redundantly; workgroup 0 also writes idx_out / w_out) and
+// idx / w are unused.  ws: decode_ws_bytes, 256-byte aligned.
+hipError_t launch_decode(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
+                         const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
+                         int E, int H, int F, uint16_t* out, void* ws, hipStream_t s,
+                         const RouteArgs& ra = RouteArgs{}, int32_t* idx_out = nullptr,
+                         float* w_out = nullptr);
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
@@ -188,6 +178,9 @@ hipError_t launch_route_plan(const void* logits, const void* bias, int bf16, int
                              float scale, int32_t* idx, float* w, int32_t* counts,
                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
                              int32_t* ntiles, int32_t* tile_off, int tile_m, hipStream_t s);
+
+// Measurement helper: a plain streaming read of `bytes` bytes (sink: 4 KB).
+hipError_t launch_probe_read(const void* src, size_t bytes, int grid, void* sink, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

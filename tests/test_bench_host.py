@@ -14,8 +14,7 @@ def test_kernel_stage_mapping():
     assert bench.kernel_stage("void moe::gemm_bf16_kernel<128, false>(x)") == "down"
     assert bench.kernel_stage("void moe::gemm_fp8_kernel<4, 256, true>(x)") == "gate_up"
     assert bench.kernel_stage("void moe::gemm_fp8_kernel<4, 128, false>(x)") == "down"
-    assert bench.kernel_stage("void moe::decode_slice_kernel<32, 3, 1>(x)") == "decode_slices"
-    assert bench.kernel_stage("moe::decode_combine_kernel(x)") == "combine"
+    assert bench.kernel_stage("void moe::decode_kernel<1, 3, 2, false>(x)") == "decode"
     assert bench.kernel_stage("moe::combine_kernel(x)") == "combine"
     assert bench.kernel_stage("void moe::gemm_mx_kernel<256, true, 2>(unsigned char const*)") == "gate_up"
     assert bench.kernel_stage("void moe::gemm_mx_kernel<256, false, 2>(x)") == "down"
@@ -29,8 +28,9 @@ def test_kernel_stage_mapping():
 def test_stage_work_matches_the_layer_formula():
     # DeepSeek-OCR-2 decode, T=1: 6 touched experts x (2FH + HF) bf16 weights
     T, H, F, k = 1, 1280, 896, 6
-    b, f = bench.stage_work("decode_slices", "bf16", T, H, F, k, touched=6, valid=6)
-    assert b == 6 * 3 * F * H * 2 + T * H * 2 + T * k * 4
+    b, f = bench.stage_work("decode", "bf16", T, H, F, k, touched=6, valid=6)
+    # weights, the token row, the output row and the routing (ids + weights)
+    assert b == 6 * 3 * F * H * 2 + T * H * 2 + T * H * 2 + T * k * 8
     assert f == 2 * 6 * 3 * F * H
     gu = bench.stage_work("gate_up", "bf16", 2048, H, F, k, touched=64, valid=2048 * 6)
     dn = bench.stage_work("down", "bf16", 2048, H, F, k, touched=64, valid=2048 * 6)
