@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 enum moe_status {
     MOE_OK = 0,
@@ -226,9 +226,10 @@ int moe_experts_decode_shared(const uint16_t* hidden, const uint16_t* gate_up,
                               size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for the shared-expert entry points: variant
- * MOE_VARIANT_PREFILL (moe_experts_prefill_shared) or MOE_VARIANT_DECODE
- * (moe_experts_decode_shared); MOE_ERR_SHAPE otherwise or when the shapes
- * are out of range. */
+ * MOE_VARIANT_PREFILL (moe_experts_prefill_shared), MOE_VARIANT_DECODE
+ * (moe_experts_decode_shared), MOE_VARIANT_FP8 (moe_experts_fp8_shared) or
+ * MOE_VARIANT_MXFP4 (moe_experts_mxfp4_shared); MOE_ERR_SHAPE otherwise or
+ * when the shapes are out of range. */
 int moe_workspace_size_shared(int variant, int64_t T, int H, int F, int E, int k, int S,
                               size_t* bytes);
 
@@ -254,6 +255,32 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale,
                     const int32_t* top_k_index, const float* top_k_weights,
                     const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                     uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The FP8 layer with S fused shared experts (DeepGEMM issue "GC MoE":
+ * routed experts with optional fused shared experts, FP8 shared weights;
+ * mirage issue "Supporting MegaKernel for DeepSeek Models": the shared
+ * expert is an FP8 block-scaled product of the same kind).  The shared
+ * experts are stored like the routed ones: shared_gate_up [S,2F,H] E4M3 with
+ * fp32 scales [S,2F,H/128], shared_down [S,H,F] E4M3 with fp32 scales
+ * [S,H,F/128] (device; codes 16-byte aligned, scales 16-byte aligned), the
+ * same F as the routed experts.  Every token passes through each with
+ * weight 1, after its routed slots in the fixed summation order:
+ *   out[t] = sum_j w[t,j] * E_idx[t,j](x[t]) + sum_s S_s(x[t]) (+ residual[t]).
+ * The call appends the weight-1 slots to each token's routing in the
+ * workspace and runs the moe_experts_fp8 sequence over E + S experts and
+ * k + S slots.  1 <= S, E + S <= MOE_MAX_EXPERTS.  ws_bytes:
+ * moe_workspace_size_shared(MOE_VARIANT_FP8, ...).  Errors as
+ * moe_experts_fp8.
+ */
+int moe_experts_fp8_shared(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
+                           const float* gate_up_scale, const uint8_t* down,
+                           const float* down_scale, const uint8_t* shared_gate_up,
+                           const float* shared_gate_up_scale, const uint8_t* shared_down,
+                           const float* shared_down_scale, const int32_t* top_k_index,
+                           const float* top_k_weights, const uint16_t* residual, int64_t T, int H,
+                           int F, int E, int k, int S, uint16_t* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /*
  * The same FP8 layer fed with bf16 hidden states [T,H] (mirage issue
@@ -297,6 +324,26 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale,
                       const int32_t* top_k_index, const float* top_k_weights,
                       const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The MXFP4 layer with S fused shared experts, stored like the routed ones:
+ * shared_gate_up [S,2F,H/2] and shared_down [S,H,F/2] E2M1 pairs with E8M0
+ * scales [S,2F,H/32] and [S,H,F/32] (codes 16-byte aligned, scales 4-byte
+ * aligned), the same F; weight 1 for every token, summed after the routed
+ * slots, as moe_experts_fp8_shared.  (The pages' GC MoE pairs FP4 routed
+ * weights with FP8 shared weights; here the shared experts take the routed
+ * experts' format, so that one grouped product serves both.)  ws_bytes:
+ * moe_workspace_size_shared(MOE_VARIANT_MXFP4, ...).  Errors as
+ * moe_experts_mxfp4.
+ */
+int moe_experts_mxfp4_shared(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+                             const uint8_t* gate_up_scale, const uint8_t* down,
+                             const uint8_t* down_scale, const uint8_t* shared_gate_up,
+                             const uint8_t* shared_gate_up_scale, const uint8_t* shared_down,
+                             const uint8_t* shared_down_scale, const int32_t* top_k_index,
+                             const float* top_k_weights, const uint16_t* residual, int64_t T,
+                             int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * Routers: router logits -> top_k_index [T,k] int32 and top_k_weights [T,k]
@@ -379,6 +426,21 @@ int moe_experts_decode_routed(const uint16_t* hidden, const void* logits, const 
  */
 int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int K,
                               uint8_t* codes, float* scales, hipStream_t stream);
+
+/*
+ * The same block-128 fp8 quantisation with power-of-two scales (mirage issue
+ * "Supporting MegaKernel for DeepSeek Models", bf16_to_fp8_quantize: "FP8
+ * E4M3 + scale ue8m0", block size 128).  The page states no rule; this one:
+ * per block, e is the smallest integer with amax <= 448 * 2^e, clamped to
+ * [-127, 127]; codes = RNE_e4m3(clamp(v * 2^-e, +-448)) (the multiplication
+ * by 2^-e is exact, so the e4m3 rounding is the only one); the scale byte is
+ * e + 127, value 2^e.  An all-zero block gets byte 127 and zero codes.
+ * `in` fp32 or bf16 [rows,K] (4-byte aligned); codes [rows,K]; scales
+ * [rows,K/128] bytes.  K must be a multiple of 128.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_DEVICE, MOE_ERR_LAUNCH.
+ */
+int moe_quantize_fp8_block128_ue8m0(const void* in, int in_is_bf16, int64_t rows, int K,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 /*
  * Stage timing, for measurement (not needed for normal use).

@@ -63,7 +63,10 @@ def _load():
         "moe_experts_fp8_bf16in": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz,
                                     vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
+        "moe_quantize_fp8_block128_ue8m0": ([vp, i32, i64, i32, vp, vp, vp], i32),
         "moe_experts_mxfp4": ([vp] * 9 + [i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_fp8_shared": ([vp] * 13 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_mxfp4_shared": ([vp] * 13 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_route_topk": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
                             vp], i32),
         "moe_route_plan": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
@@ -93,7 +96,8 @@ def exported_symbols():
             "moe_profile_end", "moe_experts_prefill_shared", "moe_experts_decode_shared",
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
             "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc",
-            "moe_probe_stream_read"]
+            "moe_probe_stream_read", "moe_quantize_fp8_block128_ue8m0", "moe_experts_fp8_shared",
+            "moe_experts_mxfp4_shared"]
 
 
 class MoeError(RuntimeError):
@@ -459,6 +463,83 @@ def moe_experts_fp8_bf16in(hidden_states, gate_up, gate_up_scale, down, down_sca
                      workspace, out)
 
 
+def _quant_shared_call(entry, variant, x, x_scale, gate_up, gate_up_scale, down, down_scale,
+                       shared, top_k_index, top_k_weights, top_k, residual, workspace, out):
+    """Shared-expert forms of the fp8 / mxfp4 layers: `shared` is (gate_up,
+    gate_up_scale, down, down_scale) of S experts in the routed format."""
+    x = _codes(x)
+    dev = x.device
+    sgu, sgus, sdn, sdns = (_codes(shared[0]), shared[1], _codes(shared[2]), shared[3])
+    gate_up, down = _codes(gate_up), _codes(down)
+    mx = variant == MOE_VARIANT_MXFP4
+    sdt = torch.uint8 if mx else torch.float32
+    for t, name, nd, dt in ((x, "x", 2, torch.uint8), (x_scale, "x_scale", 2, sdt),
+                            (gate_up, "gate_up", 3, torch.uint8), (gate_up_scale, "gate_up_scale", 3, sdt),
+                            (down, "down", 3, torch.uint8), (down_scale, "down_scale", 3, sdt),
+                            (sgu, "shared_gate_up", 3, torch.uint8), (sgus, "shared_gate_up_scale", 3, sdt),
+                            (sdn, "shared_down", 3, torch.uint8), (sdns, "shared_down_scale", 3, sdt)):
+        _need(t, name, dt, nd, dev)
+    _need(top_k_index, "top_k_index", torch.int32, 2, dev)
+    _need(top_k_weights, "top_k_weights", torch.float32, 2, dev)
+    T, H = x.shape
+    E, F2, _ = gate_up.shape
+    F = F2 // 2
+    S = sgu.shape[0]
+    k = int(top_k)
+    pk, sb = (2, 32) if mx else (1, 128)   # codes per byte, values per scale
+    want = {"gate_up": (E, 2 * F, H // pk), "gate_up_scale": (E, 2 * F, H // sb),
+            "down": (E, H, F // pk), "down_scale": (E, H, F // sb),
+            "shared_gate_up": (S, 2 * F, H // pk), "shared_gate_up_scale": (S, 2 * F, H // sb),
+            "shared_down": (S, H, F // pk), "shared_down_scale": (S, H, F // sb),
+            "x_scale": (T, H // sb)}
+    got = {"gate_up": gate_up, "gate_up_scale": gate_up_scale, "down": down, "down_scale": down_scale,
+           "shared_gate_up": sgu, "shared_gate_up_scale": sgus, "shared_down": sdn,
+           "shared_down_scale": sdns, "x_scale": x_scale}
+    for name, shape in want.items():
+        if tuple(got[name].shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}, got {list(got[name].shape)}")
+    if tuple(top_k_index.shape) != (T, k) or tuple(top_k_weights.shape) != (T, k):
+        raise ValueError("top_k_index and top_k_weights must be [T, top_k]")
+    res = _residual(residual, T, H, dev)
+    out = _out(out, T, H, dev)
+    if T == 0:
+        return out
+    with _on(dev):
+        stream = _stream(dev)
+        need = moe_workspace_size_shared(variant, T, H, F, E, k, S)
+        ws = workspace if workspace is not None else _workspace(need, dev, stream)
+        rc = getattr(_load(), entry)(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
+                                     _ptr(down), _ptr(down_scale), _ptr(sgu), _ptr(sgus), _ptr(sdn),
+                                     _ptr(sdns), _ptr(top_k_index), _ptr(top_k_weights), res, T, H,
+                                     F, E, k, S, _ptr(out), _ptr(ws), ws.numel(),
+                                     ctypes.c_void_p(stream))
+    _check(rc, entry)
+    return out
+
+
+def moe_experts_fp8_shared(x, x_scale, gate_up, gate_up_scale, down, down_scale, shared_gate_up,
+                           shared_gate_up_scale, shared_down, shared_down_scale, top_k_index,
+                           top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """moe_experts_fp8 plus S always-on shared experts (weight 1) in the
+    routed experts' FP8 format: shared_gate_up [S,2F,H] + fp32 [S,2F,H/128],
+    shared_down [S,H,F] + fp32 [S,H,F/128]."""
+    return _quant_shared_call("moe_experts_fp8_shared", MOE_VARIANT_FP8, x, x_scale, gate_up,
+                              gate_up_scale, down, down_scale,
+                              (shared_gate_up, shared_gate_up_scale, shared_down, shared_down_scale),
+                              top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_mxfp4_shared(x, x_scale, gate_up, gate_up_scale, down, down_scale, shared_gate_up,
+                             shared_gate_up_scale, shared_down, shared_down_scale, top_k_index,
+                             top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """moe_experts_mxfp4 plus S always-on shared experts (weight 1) in the
+    routed experts' MXFP4 format."""
+    return _quant_shared_call("moe_experts_mxfp4_shared", MOE_VARIANT_MXFP4, x, x_scale, gate_up,
+                              gate_up_scale, down, down_scale,
+                              (shared_gate_up, shared_gate_up_scale, shared_down, shared_down_scale),
+                              top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
 def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
                       top_k_weights, top_k, residual=None, workspace=None, out=None):
     """Routed experts with MXFP4 weights and MXFP8 activations.  x uint8 [T, H]
@@ -636,11 +717,29 @@ def moe_quantize_fp8_block128(t):
     return codes, scales
 
 
+def moe_quantize_fp8_block128_ue8m0(t):
+    """fp32 or bf16 [rows, K] -> (codes uint8 [rows, K], scale bytes uint8
+    [rows, K/128], value 2^(byte - 127))."""
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("input must be float32 or bfloat16")
+    _need(t, "input", t.dtype, 2)
+    rows, K = t.shape
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=t.device)
+    scales = torch.empty(rows, max(K // 128, 0), dtype=torch.uint8, device=t.device)
+    with _on(t.device):
+        rc = _load().moe_quantize_fp8_block128_ue8m0(_ptr(t), int(t.dtype == torch.bfloat16), rows,
+                                                     K, _ptr(codes), _ptr(scales),
+                                                     ctypes.c_void_p(_stream(t.device)))
+    _check(rc, "moe_quantize_fp8_block128_ue8m0")
+    return codes, scales
+
+
 __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
     "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_experts_prefill_shared",
+    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_quantize_fp8_block128_ue8m0",
+    "moe_experts_fp8_shared", "moe_experts_mxfp4_shared", "moe_experts_prefill_shared",
     "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
     "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",
     "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4", "moe_route_topk", "moe_route_plan",

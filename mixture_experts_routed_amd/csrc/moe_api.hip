@@ -242,13 +242,57 @@ int check_bf16_args(const uint16_t* hidden, const uint16_t* gate_up, const uint1
         return MOE_ERR_ALIGN;
     return MOE_OK;
 }
+// Shared experts of the fp8 and mxfp4 layers: S experts stored like the
+// routed ones (weights and block scales), passed by every token with weight
+// 1, as extra experts E .. E+S-1 of the same grouped products.  S == 0: none.
+struct SharedQ {
+    int S;
+    const uint8_t* gate_up;
+    const void* gate_up_scale;
+    const uint8_t* down;
+    const void* down_scale;
+};
+
+// Checks common to the quantised layers with shared experts; fills the
+// workspace layout (routed experts only when S == 0).
+int check_sharedq(const SharedQ& sh, int variant, int64_t T, int H, int F, int E, int k, Layout* L) {
+    if (sh.S < 0 || sh.S > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (sh.S) {
+        if (!sh.gate_up || !sh.gate_up_scale || !sh.down || !sh.down_scale) return MOE_ERR_NULL;
+        const uintptr_t sa = variant == MOE_VARIANT_MXFP4 ? 3u : 15u;   // E8M0 bytes / fp32 scales
+        if (!aligned16(sh.gate_up) || !aligned16(sh.down) ||
+            (((uintptr_t)sh.gate_up_scale | (uintptr_t)sh.down_scale) & sa))
+            return MOE_ERR_ALIGN;
+    }
+    const int rc = check_shape(variant, T, H, F, E + sh.S, k + sh.S);
+    if (rc) return rc;
+    *L = sh.S ? make_shared_layout(variant, T, H, F, E, k, sh.S) : make_layout(variant, T, H, F, E, k);
+    return MOE_OK;
+}
+
+// With shared experts: the augmented routing [T, k+S] into the workspace;
+// idx / w / E / k then describe the augmented problem.
+int augment_if_shared(StageClock& clock, const SharedQ& sh, const Layout& L, void* ws, int64_t T,
+                      const int32_t*& idx, const float*& w, int& E, int& k, hipStream_t stream) {
+    if (!sh.S) return MOE_OK;
+    int32_t* idx2 = at<int32_t>(ws, L.aug_idx);
+    float* w2 = at<float>(ws, L.aug_w);
+    clock.mark(MOE_STAGE_SHARED_ROUTE);
+    const int rc = launched(launch_augment_routing(idx, w, T, k, E, sh.S, idx2, w2, stream));
+    idx = idx2;
+    w = w2;
+    E += sh.S;
+    k += sh.S;
+    return rc;
+}
+
 // FP8 layer: the plan, the two grouped fp8 products and the combine; with
 // `hidden` (bf16) set, its block-128 quantisation into the workspace first.
 int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* x_scale,
             const uint8_t* gate_up, const float* gate_up_scale, const uint8_t* down,
-            const float* down_scale, const int32_t* top_k_index, const float* top_k_weights,
-            const uint16_t* residual, int64_t T, int H, int F, int E, int k, uint16_t* out,
-            void* ws, size_t ws_bytes, hipStream_t stream) {
+            const float* down_scale, const SharedQ& sh, const int32_t* top_k_index,
+            const float* top_k_weights, const uint16_t* residual, int64_t T, int H, int F, int E,
+            int k, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!gate_up || !gate_up_scale || !down || !down_scale || !top_k_index || !top_k_weights ||
         !out)
         return MOE_ERR_NULL;
@@ -256,15 +300,17 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
         !aligned16(down_scale) || (residual && !aligned16(residual)) ||
         (((uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
         return MOE_ERR_ALIGN;
-    int rc = check_shape(variant, T, H, F, E, k);
+    Layout L;
+    int rc = check_sharedq(sh, variant, T, H, F, E, k, &L);
     if (rc) return rc;
-    const Layout L = make_layout(variant, T, H, F, E, k);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     int dev;
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
-    const int P = (int)(T * k);
-    const GroupedPlan pl = plan_in(L, ws, E);
+    const ExpertArray<uint8_t> w13{gate_up, sh.S ? sh.gate_up : gate_up, E};
+    const ExpertArray<float> w13s{gate_up_scale, sh.S ? (const float*)sh.gate_up_scale : gate_up_scale, E};
+    const ExpertArray<uint8_t> w2{down, sh.S ? sh.down : down, E};
+    const ExpertArray<float> w2s{down_scale, sh.S ? (const float*)sh.down_scale : down_scale, E};
     uint8_t* hq = at<uint8_t>(ws, L.h);
     float* hs = at<float>(ws, L.hs);
     uint16_t* y = at<uint16_t>(ws, L.y);
@@ -273,34 +319,36 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
         x = at<uint8_t>(ws, L.xq);
         x_scale = at<float>(ws, L.xs);
         clock.mark(MOE_STAGE_QUANTIZE);
-        rc = launched(launch_quantize_fp8(hidden, 1, T, H, (uint8_t*)x, (float*)x_scale, stream));
+        rc = launched(launch_quantize_fp8(hidden, 1, T, H, (uint8_t*)x, (float*)x_scale, false, stream));
         if (rc) return rc;
     }
+    const int32_t* idx = top_k_index;
+    const float* w = top_k_weights;
+    if ((rc = augment_if_shared(clock, sh, L, ws, T, idx, w, E, k, stream))) return rc;
+    const int P = (int)(T * k);
+    const GroupedPlan pl = plan_in(L, ws, E);
     clock.mark(MOE_STAGE_PLAN);
     const bool narrow = fp8_use_narrow(P, E, H, F);
-    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
-                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
-                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
-                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off),
-                              fp8_tile_m(narrow), stream));
+    rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                              at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
+                              at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                              at<int32_t>(ws, L.tile_off), fp8_tile_m(narrow), stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_GATE_UP);
-    rc = launched(launch_gateup_fp8(x, x_scale, gate_up, gate_up_scale, pl, narrow, H, F, k, hq, hs,
-                                    stream));
+    rc = launched(launch_gateup_fp8(x, x_scale, w13, w13s, pl, narrow, H, F, k, hq, hs, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_fp8(hq, hs, down, down_scale, pl, narrow, H, F, y, stream));
+    rc = launched(launch_down_fp8(hq, hs, w2, w2s, pl, narrow, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
-                                   out, stream));
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, stream));
 }
 // MXFP4 layer: the plan, the two grouped MX products and the combine.
 int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
               const uint8_t* gate_up_scale, const uint8_t* down, const uint8_t* down_scale,
-              const int32_t* top_k_index, const float* top_k_weights, const uint16_t* residual,
-              int64_t T, int H, int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
-              hipStream_t stream) {
+              const SharedQ& sh, const int32_t* top_k_index, const float* top_k_weights,
+              const uint16_t* residual, int64_t T, int H, int F, int E, int k, uint16_t* out,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!x || !x_scale || !gate_up || !gate_up_scale || !down || !down_scale || !top_k_index ||
         !top_k_weights || !out)
         return MOE_ERR_NULL;
@@ -309,38 +357,42 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
         (((uintptr_t)x_scale | (uintptr_t)gate_up_scale | (uintptr_t)down_scale |
           (uintptr_t)top_k_index | (uintptr_t)top_k_weights) & 3u))
         return MOE_ERR_ALIGN;
-    int rc = check_shape(MOE_VARIANT_MXFP4, T, H, F, E, k);
+    Layout L;
+    int rc = check_sharedq(sh, MOE_VARIANT_MXFP4, T, H, F, E, k, &L);
     if (rc) return rc;
-    const Layout L = make_layout(MOE_VARIANT_MXFP4, T, H, F, E, k);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     int dev;
     if ((rc = query_device(&dev))) return rc;
     if (T == 0) return MOE_OK;
-    const int P = (int)(T * k);
-    const GroupedPlan pl = plan_in(L, ws, E);
+    const ExpertArray<uint8_t> w13{gate_up, sh.S ? sh.gate_up : gate_up, E};
+    const ExpertArray<uint8_t> w13s{gate_up_scale, sh.S ? (const uint8_t*)sh.gate_up_scale : gate_up_scale, E};
+    const ExpertArray<uint8_t> w2{down, sh.S ? sh.down : down, E};
+    const ExpertArray<uint8_t> w2s{down_scale, sh.S ? (const uint8_t*)sh.down_scale : down_scale, E};
     uint8_t* hq = at<uint8_t>(ws, L.h);
     uint8_t* hs = at<uint8_t>(ws, L.hs);
     uint16_t* y = at<uint16_t>(ws, L.y);
     StageClock clock(stream);
+    const int32_t* idx = top_k_index;
+    const float* w = top_k_weights;
+    if ((rc = augment_if_shared(clock, sh, L, ws, T, idx, w, E, k, stream))) return rc;
+    const int P = (int)(T * k);
+    const GroupedPlan pl = plan_in(L, ws, E);
     clock.mark(MOE_STAGE_PLAN);
     const bool narrow = mx_use_narrow(P, E, H, F);
-    rc = launched(launch_plan(top_k_index, P, E, at<int32_t>(ws, L.counts),
-                              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
-                              at<int32_t>(ws, L.inv), at<int32_t>(ws, L.tiles),
-                              at<int32_t>(ws, L.ntiles), at<int32_t>(ws, L.tile_off),
-                              mx_tile_m(narrow), stream));
+    rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                              at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
+                              at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                              at<int32_t>(ws, L.tile_off), mx_tile_m(narrow), stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_GATE_UP);
     const bool wide = !narrow && mx_use_wide(P, E, H, F);
-    rc = launched(launch_gateup_mx(x, x_scale, gate_up, gate_up_scale, pl, wide, narrow, H, F, k,
-                                   hq, hs, stream));
+    rc = launched(launch_gateup_mx(x, x_scale, w13, w13s, pl, wide, narrow, H, F, k, hq, hs, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_DOWN);
-    rc = launched(launch_down_mx(hq, hs, down, down_scale, pl, wide, narrow, H, F, y, stream));
+    rc = launched(launch_down_mx(hq, hs, w2, w2s, pl, wide, narrow, H, F, y, stream));
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
-    return launched(launch_combine(y, at<int32_t>(ws, L.inv), top_k_weights, residual, T, k, H,
-                                   out, stream));
+    return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, stream));
 }
 // Router arguments (moe_route_topk / moe_route_plan).
 int check_route(const void* logits, const void* bias, int logits_bf16, int mode, int64_t T, int E,
@@ -550,8 +602,9 @@ int moe_experts_decode_noalloc(const uint16_t* hidden, const uint16_t* gate_up,
 int moe_workspace_size_shared(int variant, int64_t T, int H, int F, int E, int k, int S,
                               size_t* bytes) {
     if (!bytes) return MOE_ERR_NULL;
-    if ((variant != MOE_VARIANT_PREFILL && variant != MOE_VARIANT_DECODE) || S < 1 ||
-        S > MOE_MAX_EXPERTS)
+    if ((variant != MOE_VARIANT_PREFILL && variant != MOE_VARIANT_DECODE &&
+         variant != MOE_VARIANT_FP8 && variant != MOE_VARIANT_MXFP4) ||
+        S < 1 || S > MOE_MAX_EXPERTS)
         return MOE_ERR_SHAPE;
     const int rc = check_shape(variant, T, H, F, E + S, k + S);
     if (rc) return rc;
@@ -589,7 +642,25 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
     if (!x || !x_scale) return MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(x_scale)) return MOE_ERR_ALIGN;
     return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
-                   top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
+                   SharedQ{}, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
+                   ws_bytes, stream);
+}
+
+int moe_experts_fp8_shared(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
+                           const float* gate_up_scale, const uint8_t* down,
+                           const float* down_scale, const uint8_t* shared_gate_up,
+                           const float* shared_gate_up_scale, const uint8_t* shared_down,
+                           const float* shared_down_scale, const int32_t* top_k_index,
+                           const float* top_k_weights, const uint16_t* residual, int64_t T, int H,
+                           int F, int E, int k, int S, uint16_t* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    if (!x || !x_scale) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(x_scale)) return MOE_ERR_ALIGN;
+    if (S < 1) return MOE_ERR_SHAPE;
+    const SharedQ sh{S, shared_gate_up, shared_gate_up_scale, shared_down, shared_down_scale};
+    return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
+                   sh, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes,
+                   stream);
 }
 
 int moe_experts_fp8_bf16in(const uint16_t* hidden, const uint8_t* gate_up,
@@ -601,8 +672,8 @@ int moe_experts_fp8_bf16in(const uint16_t* hidden, const uint8_t* gate_up,
     if (!hidden) return MOE_ERR_NULL;
     if (!aligned16(hidden)) return MOE_ERR_ALIGN;
     return run_fp8(MOE_VARIANT_FP8_BF16IN, hidden, nullptr, nullptr, gate_up, gate_up_scale, down,
-                   down_scale, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
-                   ws_bytes, stream);
+                   down_scale, SharedQ{}, top_k_index, top_k_weights, residual, T, H, F, E, k, out,
+                   ws, ws_bytes, stream);
 }
 
 int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
@@ -610,7 +681,21 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* g
                       const int32_t* top_k_index, const float* top_k_weights,
                       const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-    return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+    return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, SharedQ{}, top_k_index,
+                     top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
+}
+
+int moe_experts_mxfp4_shared(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+                             const uint8_t* gate_up_scale, const uint8_t* down,
+                             const uint8_t* down_scale, const uint8_t* shared_gate_up,
+                             const uint8_t* shared_gate_up_scale, const uint8_t* shared_down,
+                             const uint8_t* shared_down_scale, const int32_t* top_k_index,
+                             const float* top_k_weights, const uint16_t* residual, int64_t T,
+                             int H, int F, int E, int k, int S, uint16_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    if (S < 1) return MOE_ERR_SHAPE;
+    const SharedQ sh{S, shared_gate_up, shared_gate_up_scale, shared_down, shared_down_scale};
+    return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, sh, top_k_index,
                      top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
 }
 
@@ -774,7 +859,19 @@ int moe_quantize_fp8_block128(const void* in, int in_is_bf16, int64_t rows, int 
     int dev, rc;
     if ((rc = query_device(&dev))) return rc;
     if (rows == 0) return MOE_OK;
-    return launched(launch_quantize_fp8(in, in_is_bf16, rows, K, codes, scales, stream));
+    return launched(launch_quantize_fp8(in, in_is_bf16, rows, K, codes, scales, false, stream));
+}
+
+int moe_quantize_fp8_block128_ue8m0(const void* in, int in_is_bf16, int64_t rows, int K,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    if (!in || !codes || !scales) return MOE_ERR_NULL;
+    if (rows < 0 || K < 128 || K % 128 || rows * (int64_t)(K / 128) * 32 >= ((int64_t)1 << 31))
+        return MOE_ERR_SHAPE;
+    if ((uintptr_t)in & 3u) return MOE_ERR_ALIGN;
+    int dev, rc;
+    if ((rc = query_device(&dev))) return rc;
+    if (rows == 0) return MOE_OK;
+    return launched(launch_quantize_fp8(in, in_is_bf16, rows, K, codes, scales, true, stream));
 }
 
 }  // extern "C"

@@ -65,8 +65,8 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
 // cache-line requests of a stage; SQ cuts that to a quarter.
 template <int WM, int BN, bool SWIGLU, bool SQ>
 __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
-    const float* __restrict__ Bs, const int32_t* __restrict__ perm,
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const ExpertArray<uint8_t> B,
+    const ExpertArray<float> Bs, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
     int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, float* __restrict__ Cs,
@@ -134,9 +134,9 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         if (sa_ok && tid < mrows)
             sarow = SWIGLU ? (int64_t)(perm[row0 + tid] / topk) : (int64_t)(row0 + tid);
         const float* as_src = As + sarow * nkb;
-        const uint8_t* b_src = B + ((int64_t)e * b_rows + panel_row(row_t, nt)) * K + chunk * 16;
+        const uint8_t* b_src = B.expert(e, (int64_t)b_rows * K) + (int64_t)panel_row(row_t, nt) * K + chunk * 16;
         const int64_t b_step = (int64_t)(SWIGLU ? 32 : 64) * K;
-        const float* bs_src = Bs + ((int64_t)e * b_rows + panel_row(sb_ok ? tid : 0, nt)) * nkb;
+        const float* bs_src = Bs.expert(e, (int64_t)b_rows * nkb) + (int64_t)panel_row(sb_ok ? tid : 0, nt) * nkb;
 
         f32x16 acc[NBW];
 #pragma unroll
@@ -330,7 +330,8 @@ static int fp8_grid() {
 
 // SQ (16-byte scale loads) needs K / 128 to be a multiple of 4
 template <int WM, int BN, bool SWIGLU>
-static void launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+static void launch_fp8(const uint8_t* A, const float* As, const ExpertArray<uint8_t>& B,
+                       const ExpertArray<float>& Bs,
                        const GroupedPlan& pl, int K, int n_out, int b_rows, int topk, uint8_t* Cq,
                        float* Cs, uint16_t* Cy, hipStream_t s) {
     if ((K / kFp8BK) % 4 == 0)
@@ -343,8 +344,8 @@ static void launch_fp8(const uint8_t* A, const float* As, const uint8_t* B, cons
                    pl.tile_off, pl.offsets, pl.E, K, n_out, b_rows, topk, Cq, Cs, Cy);
 }
 
-hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
-                             const float* w13s, const GroupedPlan& pl, bool narrow, int H, int F,
+hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
+                             const ExpertArray<float>& w13s, const GroupedPlan& pl, bool narrow, int H, int F,
                              int k, uint8_t* hq, float* hs, hipStream_t s) {
     if (narrow)
         launch_fp8<1, 512, true>(x, xs, w13, w13s, pl, H, F, 2 * F, k, hq, hs, nullptr, s);
@@ -353,8 +354,8 @@ hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w
     return hipGetLastError();
 }
 
-hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
-                           const GroupedPlan& pl, bool narrow, int H, int F, uint16_t* y,
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray<uint8_t>& w2,
+                           const ExpertArray<float>& w2s, const GroupedPlan& pl, bool narrow, int H, int F, uint16_t* y,
                            hipStream_t s) {
     if (narrow)
         launch_fp8<1, 512, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
@@ -366,12 +367,37 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2
 }
 
 // ------------------------------------------------------- stand-alone quantiser
+// Block-128 quantisation with a power-of-two scale (mirage issue "Supporting
+// MegaKernel for DeepSeek Models", bf16_to_fp8_quantize: "FP8 E4M3 + scale
+// ue8m0", block 128).  The page gives no rule; the one taken: e is the
+// smallest integer with amax <= 448 * 2^e, clamped to [-127, 127]; codes are
+// RNE_e4m3(clamp(v * 2^-e, +-448)) (v * 2^-e is exact, so the e4m3 rounding
+// is the only one) and the scale byte is e + 127.  An all-zero block gets
+// byte 127 (scale 1) and zero codes.  With amax = m * 2^E, m in [1, 2):
+// 448 = 1.75 * 2^8, so e = E - 8 when m <= 1.75 and E - 7 otherwise.
+__device__ __forceinline__ uint8_t quant_block_ue8m0(const float v[4], float amax, uint32_t* codes) {
+    int e = 0;
+    if (amax > 0.0f) {
+        int x;
+        const float f = frexpf(amax, &x);   // amax = f * 2^x, f in [0.5, 1)
+        e = (x - 1) - 8 + (2.0f * f > 1.75f ? 1 : 0);
+        e = min(max(e, -127), 127);
+    }
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(ldexpf(v[i], -e), -448.0f), 448.0f);
+    *codes = f32x4_to_e4m3x4(q[0], q[1], q[2], q[3]);
+    return (uint8_t)(e + 127);
+}
+
 // One 32-lane half per 128-value block: lane i of the half takes values
 // i, i+32, i+64, i+96 (the same spread as the epilogue's accumulators).
+// UE8M0: power-of-two scale bytes instead of fp32 scales.
+template <bool UE8M0>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ in, int in_is_bf16,
                                                        int64_t nblocks, int K,
                                                        uint8_t* __restrict__ codes,
-                                                       float* __restrict__ scales) {
+                                                       void* __restrict__ scales) {
     const int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
     const int l = threadIdx.x & 31;
     const bool live = blk < nblocks;
@@ -389,21 +415,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         amax = fmaxf(amax, fabsf(v[p]));
     }
     uint32_t c;
-    const float scale = quant_block_half(v, amax, &c);
+    if constexpr (UE8M0) {
+        const uint8_t sb = quant_block_ue8m0(v, half_max32(amax), &c);
+        if (live && l == 0) ((uint8_t*)scales)[b] = sb;
+    } else {
+        const float scale = quant_block_half(v, amax, &c);
+        if (live && l == 0) ((float*)scales)[b] = scale;
+    }
     if (live) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) codes[base + p * 32 + l] = (uint8_t)(c >> (8 * p));
-        if (l == 0) scales[b] = scale;
     }
 }
 
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
-                               float* scales, hipStream_t s) {
+                               void* scales, bool ue8m0, hipStream_t s) {
     const int64_t nblocks = rows * (K / 128);
     const int64_t threads = nblocks * 32;
     const int blocks = (int)((threads + 255) / 256);
-    MOE_LAUNCH(quantize_kernel, dim3(blocks), dim3(256), 0, s, in, in_is_bf16, nblocks, K,
-                       codes, scales);
+    if (ue8m0)
+        MOE_LAUNCH(quantize_kernel<true>, dim3(blocks), dim3(256), 0, s, in, in_is_bf16, nblocks, K,
+                   codes, scales);
+    else
+        MOE_LAUNCH(quantize_kernel<false>, dim3(blocks), dim3(256), 0, s, in, in_is_bf16, nblocks, K,
+                   codes, scales);
     return hipGetLastError();
 }
 

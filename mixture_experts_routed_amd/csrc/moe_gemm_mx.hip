@@ -51,8 +51,8 @@ __device__ __forceinline__ int lds_chunk4(int row, int chunk) { return chunk ^ (
 // scale words of panel row t and of tile row t % 32.
 template <int BN, bool SWIGLU, int KS, int WM = 4>
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const ExpertArray<uint8_t> B,
+    const ExpertArray<uint8_t> Bs, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
     int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
             const int q = tid + kMxThreads * i;       // row q / BCH, chunk q % BCH
-            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q / BCH, nt)) * (K / 2) + (q % BCH) * 16;
+            b_src[i] = B.expert(e, (int64_t)b_rows * (K / 2)) + (int64_t)panel_row(q / BCH, nt) * (K / 2) + (q % BCH) * 16;
         }
         // scale words: WM = 4: thread t < 128 -> A row t, 128 <= t < 128 + BN
         // -> B row t - 128; WM = 1: B row t (s_src) and A row t % 32 (sa_src)
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
             if ((WM == 1 || sa_t) && r < mrows)
                 arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
             const uint8_t* sa = As + arow * kb_row;
-            const uint8_t* sb = Bs + ((int64_t)e * b_rows + panel_row(sb_t ? (WM == 4 ? tid - BM : tid) : 0, nt)) * kb_row;
+            const uint8_t* sb = Bs.expert(e, (int64_t)b_rows * kb_row) + (int64_t)panel_row(sb_t ? (WM == 4 ? tid - BM : tid) : 0, nt) * kb_row;
             s_src = WM == 4 ? (sb_t ? sb : sa) : sb;
             sa_src = sa;
         }
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 // panel row tid, threads < 128 also the word of tile row tid.
 template <bool SWIGLU>
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, const int32_t* __restrict__ perm,
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const ExpertArray<uint8_t> B,
+    const ExpertArray<uint8_t> Bs, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
     int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
@@ -345,10 +345,10 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
             const int q = tid + kMxThreads * i;
-            b_src[i] = B + ((int64_t)e * b_rows + panel_row(q >> 2, nt)) * (K / 2) + (q & 3) * 16;
+            b_src[i] = B.expert(e, (int64_t)b_rows * (K / 2)) + (int64_t)panel_row(q >> 2, nt) * (K / 2) + (q & 3) * 16;
         }
         const uint8_t* sa_src = As + a_row(tid & (kMxBM - 1)) * kb_row;
-        const uint8_t* sb_src = Bs + ((int64_t)e * b_rows + panel_row(tid, nt)) * kb_row;
+        const uint8_t* sb_src = Bs.expert(e, (int64_t)b_rows * kb_row) + (int64_t)panel_row(tid, nt) * kb_row;
 
         f32x16 acc[MB][NB];
 #pragma unroll
@@ -498,8 +498,8 @@ bool mx_use_wide(int64_t P, int E, int H, int F) {
     return P > 64 * (int64_t)E && F % 256 == 0 && H % 512 == 0;
 }
 
-hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
-                            const uint8_t* w13s, const GroupedPlan& pl, bool wide, bool narrow, int H,
+hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const ExpertArray<uint8_t>& w13,
+                            const ExpertArray<uint8_t>& w13s, const GroupedPlan& pl, bool wide, bool narrow, int H,
                             int F, int k, uint8_t* hq, uint8_t* hs, hipStream_t s) {
     if (narrow) {
         MOE_LAUNCH((gemm_mx_kernel<512, true, 2, 1>), dim3(mx_grid<512, true, 2, 1>()), dim3(kMxThreads),
@@ -524,8 +524,8 @@ hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* 
     return hipGetLastError();
 }
 
-hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2, const uint8_t* w2s,
-                          const GroupedPlan& pl, bool wide, bool narrow, int H, int F, uint16_t* y,
+hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const ExpertArray<uint8_t>& w2,
+                          const ExpertArray<uint8_t>& w2s, const GroupedPlan& pl, bool wide, bool narrow, int H, int F, uint16_t* y,
                           hipStream_t s) {
     if (narrow)
         MOE_LAUNCH((gemm_mx_kernel<512, false, 2, 1>), dim3(mx_grid<512, false, 2, 1>()),

@@ -53,15 +53,18 @@ hipError_t launch_plan(const int32_t* idx, int P, int E, int32_t* counts, int32_
 // one tensor, optionally followed by S shared experts in a tensor of their
 // own (expert ids E .. E+S-1, see the shared-expert entry points).  Without
 // shared experts `shared` is unused (n_routed covers every id).
-struct ExpertWeights {
-    const uint16_t* base;
-    const uint16_t* shared;
+template <typename T>
+struct ExpertArray {
+    const T* base;
+    const T* shared;
     int n_routed;
-    __host__ __device__ const uint16_t* expert(int e, int64_t stride) const {
+    __host__ __device__ const T* expert(int e, int64_t stride) const {
         return e < n_routed ? base + (int64_t)e * stride : shared + (int64_t)(e - n_routed) * stride;
     }
 };
-inline ExpertWeights routed_only(const uint16_t* w, int E) { return ExpertWeights{w, w, E}; }
+using ExpertWeights = ExpertArray<uint16_t>;
+template <typename T>
+inline ExpertArray<T> routed_only(const T* w, int E) { return ExpertArray<T>{w, w, E}; }
 
 // Augmented routing for S shared experts: idx2/w2 [T, k+S] hold the routed
 // slots (ids outside [0, E) as -1, i.e. dropped) followed by S slots naming
@@ -139,16 +142,16 @@ hipError_t launch_decode(const uint16_t* x, const ExpertWeights& w13, const Expe
                          float* w_out = nullptr);
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
-hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const uint8_t* w13,
-                             const float* w13s, const GroupedPlan& plan, bool narrow, int H, int F,
+hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
+                             const ExpertArray<float>& w13s, const GroupedPlan& plan, bool narrow, int H, int F,
                              int k, uint8_t* hq, float* hs, hipStream_t s);
 
-hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* w2, const float* w2s,
-                           const GroupedPlan& plan, bool narrow, int H, int F, uint16_t* y,
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray<uint8_t>& w2,
+                           const ExpertArray<float>& w2s, const GroupedPlan& plan, bool narrow, int H, int F, uint16_t* y,
                            hipStream_t s);
 
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
-                               float* scales, hipStream_t s);
+                               void* scales, bool ue8m0, hipStream_t s);
 
 // MXFP4 x MXFP8 products (E2M1 weights two per byte, E4M3 activations, E8M0
 // scales per 32 K elements): gate_up with SwiGLU + MXFP8 re-quantisation
@@ -161,11 +164,11 @@ hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int
 bool mx_use_narrow(int64_t P, int E, int H, int F);
 int mx_tile_m(bool narrow);
 bool mx_use_wide(int64_t P, int E, int H, int F);
-hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* w13,
-                            const uint8_t* w13s, const GroupedPlan& plan, bool wide, bool narrow,
+hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const ExpertArray<uint8_t>& w13,
+                            const ExpertArray<uint8_t>& w13s, const GroupedPlan& plan, bool wide, bool narrow,
                             int H, int F, int k, uint8_t* hq, uint8_t* hs, hipStream_t s);
-hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* w2,
-                          const uint8_t* w2s, const GroupedPlan& plan, bool wide, bool narrow, int H,
+hipError_t launch_down_mx(const uint8_t* hq, const uint8_t* hs, const ExpertArray<uint8_t>& w2,
+                          const ExpertArray<uint8_t>& w2s, const GroupedPlan& plan, bool wide, bool narrow, int H,
                           int F, uint16_t* y, hipStream_t s);
 
 // Routers (logits -> ids, weights), alone or followed by the plan in the

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 7
+    assert moe.moe_abi_version() == 8
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -7, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
@@ -282,11 +282,11 @@ def test_profile_begin_without_gpu_reports_device_error():
 
 def test_shared_workspace_size_rules():
     T, H, F, E, k, S = 2048, 1280, 896, 64, 6, 2
-    for variant in (0, 1):
+    for variant in (0, 1, 2, 5):   # prefill, decode, fp8, mxfp4
         n = moe.moe_workspace_size_shared(variant, T, H, F, E, k, S)
         assert n >= moe.moe_workspace_size(variant, T, H, F, E + S, k + S) + 2 * T * (k + S) * 4
-    for bad in [(2, T, H, F, E, k, S), (0, T, H, F, E, k, 0), (0, T, H, F, 511, k, 2),
-                (0, T, 100, F, E, k, S)]:
+    for bad in [(3, T, H, F, E, k, S), (4, T, H, F, E, k, S), (0, T, H, F, E, k, 0),
+                (0, T, H, F, 511, k, 2), (0, T, 100, F, E, k, S), (2, T, 1344, F, E, k, S)]:
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_workspace_size_shared(*bad)
         assert ei.value.status == ESHAPE
@@ -319,3 +319,28 @@ def test_grid_cap_argument():
     assert lib.moe_set_grid_cap(-1) == ESHAPE
     assert lib.moe_set_grid_cap(16) == OK
     assert lib.moe_set_grid_cap(0) == OK
+
+
+@pytest.mark.parametrize("fn", ["moe_experts_fp8_shared", "moe_experts_mxfp4_shared"])
+def test_quantized_shared_entry_validation(fn):
+    """Argument errors of the fp8 / mxfp4 shared-expert entry points, found on
+    the host before anything is enqueued (no GPU needed)."""
+    lib = moe._load()
+
+    def call(**kw):
+        a = dict(x=P16, xs=P16, gu=P16, gus=P16, dn=P16, dns=P16, sgu=P16, sgus=P16, sdn=P16,
+                 sdns=P16, idx=P16, w=P16, res=None, T=4, H=256, F=128, E=8, k=2, S=2, out=P16,
+                 ws=P16B, ws_bytes=1 << 30)
+        a.update(kw)
+        return getattr(lib, fn)(a["x"], a["xs"], a["gu"], a["gus"], a["dn"], a["dns"], a["sgu"],
+                                a["sgus"], a["sdn"], a["sdns"], a["idx"], a["w"], a["res"], a["T"],
+                                a["H"], a["F"], a["E"], a["k"], a["S"], a["out"], a["ws"],
+                                a["ws_bytes"], None)
+
+    assert call(sgu=None) == ENULL
+    assert call(sdns=None) == ENULL
+    assert call(sgu=P16 + 1) == EALIGN
+    assert call(S=0) == ESHAPE
+    assert call(S=600) == ESHAPE
+    assert call(E=510, S=3) == ESHAPE        # E + S > 512
+    assert call(H=192) == ESHAPE             # not a multiple of 128

@@ -335,3 +335,37 @@ def test_mxfp4_h_stage_exact(shape):
     q_ref, s_ref = orc.quantize_mxfp8_fp32(h.astype(np.float32))
     assert np.array_equal(hs, s_ref), "h scale bytes differ"
     assert np.array_equal(hq, q_ref), f"{int((hq != q_ref).sum())} h codes differ"
+
+
+# (T, H, F, E, k, S): grouped tiles; a decode batch; the 128 x 512 tiles
+@pytest.mark.parametrize("shape", [(300, 512, 256, 6, 2, 2), (40, 512, 256, 8, 2, 1),
+                                   (900, 1024, 768, 5, 2, 1)])
+def test_mxfp4_shared_experts(shape):
+    """MXFP4 layer + shared experts in the routed format, against the oracle
+    of the same layer with the shared experts as weight-1 slots (after the
+    routed ones); with a residual and dropped ids (E, -1: never shared)."""
+    T, H, F, E, k, S = shape
+    _say(f"mxfp4 shared {shape}")
+    p = mx_problem(T, H, F, E + S, k, seed=95 + T)
+    g = torch.Generator().manual_seed(96 + T)
+    idx, w = wl.route_uniform_softmax(T, E, k, g, "cpu", 1.0)
+    idx = idx.clone()
+    idx[::5, 0] = E
+    idx[1::7, k - 1] = -1
+    idx = idx.contiguous()
+    names = ("gate_up", "gate_up_scale", "down", "down_scale")
+    routed = {n: p[n][:-S].contiguous() for n in names}
+    shared = [p[n][-S:].contiguous() for n in names]
+    idx_np = idx.numpy()
+    idx_a = np.concatenate([np.where((idx_np >= 0) & (idx_np < E), idx_np, -1),
+                            np.tile(np.arange(E, E + S), (T, 1))], axis=1)
+    w_a = np.concatenate([w.numpy(), np.ones((T, S))], axis=1)
+    r = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    ref = orc.moe_experts_mxfp4_reference(
+        p["x"].numpy(), p["x_scale"].numpy(), p["gate_up"].numpy(), p["gate_up_scale"].numpy(),
+        p["down"].numpy(), p["down_scale"].numpy(), idx_a, w_a, residual=f64(r))
+    out = _moe().moe_experts_mxfp4_shared(
+        p["x"].cuda(), p["x_scale"].cuda(), *[routed[n].cuda() for n in names],
+        *[t.cuda() for t in shared], idx.cuda(), w.cuda(), k, residual=r.cuda())
+    worst, rel = check_tol(out, ref, MX_TOL, f"mxfp4 shared {shape}")
+    _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")

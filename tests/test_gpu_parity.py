@@ -443,6 +443,32 @@ def test_quantizer_bit_exact():
     assert np.array_equal(scales.cpu().numpy(), s_ref)
 
 
+def test_quantizer_ue8m0_bit_exact():
+    """Power-of-two (ue8m0) block-128 quantiser against the oracle's rule:
+    codes and scale bytes bit for bit, fp32 and bf16 inputs, with zero and
+    negative-zero blocks, tiny and huge blocks, and block maxima exactly at
+    448 * 2^e and just above it (where e steps)."""
+    moe = _moe()
+    _say("quantizer ue8m0")
+    rng = np.random.default_rng(11)
+    h = (rng.standard_normal((257, 1024)) * np.exp(rng.uniform(-30, 30, (257, 1)))).astype(np.float32)
+    h[3, 256:384] = 0.0
+    h[4, :128] = -0.0
+    h[5, :128] = 1e-38                       # amax = 1e-38: e clamps at -127
+    h[6, 128:256] = 448.0                    # amax = 448 * 2^0 exactly: e = 0
+    h[7, 128:256] = -448.0 * 2.0 ** -20      # exactly 448 * 2^-20
+    h[8, :128] = np.nextafter(np.float32(448.0), np.float32(1e9))   # just above: e = 1
+    h[9, 512:640] = 3.0e38                   # near the fp32 maximum
+    t = torch.from_numpy(h).cuda()
+    for inp in (t, t.to(torch.bfloat16)):
+        codes, sb = moe.moe_quantize_fp8_block128_ue8m0(inp)
+        q_ref, s_ref = orc.quantize_block128_ue8m0(inp.float().cpu().numpy())
+        assert np.array_equal(sb.cpu().numpy(), s_ref)
+        assert np.array_equal(codes.cpu().numpy(), q_ref)
+        if inp.dtype == torch.float32:   # the cases at the step of e
+            assert s_ref[6, 1] == 127 and s_ref[8, 0] == 128 and s_ref[5, 0] == 0
+
+
 def _run_fp8_ws(moe, g, variant=None):
     T, H = g["x"].shape
     E, F2, _ = g["gate_up"].shape
@@ -752,3 +778,63 @@ def test_shared_full_config(name):
     entry = "moe_experts_decode_shared" if "decode" in name else "moe_experts_prefill_shared"
     out = _run_shared(entry, g)
     check_tol(out, _shared_ref(p, batched=True), BF16_TOL, name)
+
+
+# ---------------------------------------- shared experts, quantised layers
+
+def _augment(p, S, w=None):
+    """The problem with the S shared experts (the last S of p's experts)
+    written as the definition reads: extra experts E .. E+S-1 that every token
+    passes through with weight 1, after its routed slots."""
+    idx = p["top_k_index"].numpy()
+    T = idx.shape[0]
+    E = p["gate_up"].shape[0] - S
+    wts = p["top_k_weights"].numpy() if w is None else w
+    idx_a = np.concatenate([np.where((idx >= 0) & (idx < E), idx, -1),
+                            np.tile(np.arange(E, E + S), (T, 1))], axis=1)
+    w_a = np.concatenate([wts, np.ones((T, S))], axis=1)
+    return idx_a, w_a
+
+
+def _split_shared(p, S, names):
+    """Routed part (first E experts) and shared part (last S) of p's weights."""
+    routed = {n: p[n][:-S].contiguous() for n in names}
+    shared = tuple(p[n][-S:].contiguous() for n in names)
+    return routed, shared
+
+
+_FP8_W = ("gate_up", "gate_up_scale", "down", "down_scale")
+
+
+# (T, H, F, E, k, S): grouped tiles; a decode batch (32-row tiles, 512-row
+# panels); several M tiles per shared expert
+@pytest.mark.parametrize("shape", [(300, 512, 256, 6, 2, 2), (48, 512, 256, 16, 4, 1),
+                                   (520, 256, 384, 4, 2, 1)])
+def test_fp8_shared_experts(shape):
+    """FP8 layer + shared experts in the routed format, against the oracle of
+    the same layer with the shared experts as weight-1 slots; with a residual,
+    dropped ids (E, -1: never a shared expert) and all-zero routing weights."""
+    T, H, F, E, k, S = shape
+    _say(f"fp8 shared {shape}")
+    p = wl.make_fp8_problem(T, H, F, E + S, k, seed=91 + T, routing="uniform_softmax",
+                            routed_scale=1.0)
+    g = torch.Generator().manual_seed(92 + T)
+    p["top_k_index"], p["top_k_weights"] = wl.route_uniform_softmax(T, E, k, g, "cpu", 1.0)
+    idx = p["top_k_index"].clone()
+    idx[::5, 0] = E
+    idx[1::7, k - 1] = -1
+    p["top_k_index"] = idx.contiguous()
+    routed, shared = _split_shared(p, S, _FP8_W)
+    r = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    moe = _moe()
+    for w in (None, np.zeros((T, k))):
+        idx_a, w_a = _augment(p, S, w)
+        ref = orc.moe_experts_fp8_reference_batched(
+            p["x"].numpy(), p["x_scale"].numpy(), p["gate_up"].numpy(), p["gate_up_scale"].numpy(),
+            p["down"].numpy(), p["down_scale"].numpy(), idx_a, w_a, residual=f64(r))
+        wt = p["top_k_weights"] if w is None else torch.zeros(T, k)
+        out = moe.moe_experts_fp8_shared(
+            p["x"].cuda(), p["x_scale"].cuda(), *[routed[n].cuda() for n in _FP8_W],
+            *[t.cuda() for t in shared], idx.cuda(), wt.float().cuda(), k, residual=r.cuda())
+        worst, rel = check_tol(out, ref, FP8_TOL, f"fp8 shared {shape}")
+        _say(f"  worst err/tol {worst:.3f} rel L2 {rel:.2e}")
