@@ -469,6 +469,34 @@ def test_quantizer_ue8m0_bit_exact():
             assert s_ref[6, 1] == 127 and s_ref[8, 0] == 128 and s_ref[5, 0] == 0
 
 
+# Many rows per expert (prefill-sized, 128-row tiles x 256-row panels):
+# (T, H, F, E, k, skew).  skew > 0 routes most tokens to expert 0 (many M
+# tiles and a ragged last one), gives the last-but-one expert a handful of
+# rows (a tile with idle row blocks) and the last expert none.
+@pytest.mark.parametrize("shape", [(700, 512, 512, 4, 2, 0), (1000, 1024, 512, 3, 2, 0),
+                                   (900, 512, 1024, 5, 2, 1), (64 * 9, 2048, 512, 2, 1, 0)])
+def test_fp8_many_rows_per_expert(shape):
+    T, H, F, E, k, skew = shape
+    _say(f"fp8 many rows {shape}")
+    p = wl.make_fp8_problem(T, H, F, E, k, seed=101 + T, routing="uniform_softmax", routed_scale=1.0)
+    if skew:
+        rng = np.random.default_rng(T)
+        idx = np.zeros((T, k), dtype=np.int32)
+        for t in range(T):
+            first = 0 if t < T - 20 else E - 2
+            rest = rng.choice([e for e in range(E - 1) if e != first], k - 1, replace=False)
+            idx[t] = [first, *rest]
+        p["top_k_index"] = torch.from_numpy(idx)
+    g = to_gpu(p)
+    moe = _moe()
+    out, ws, lay = _run_fp8_ws(moe, g)
+    st = check_quantized_layer("fp8", out, g, ws, lay, str(shape), orc)
+    _say(f"  {st}")
+    again = run_fp8(g)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
 def _run_fp8_ws(moe, g, variant=None):
     T, H = g["x"].shape
     E, F2, _ = g["gate_up"].shape
@@ -508,7 +536,8 @@ def test_fp8_full_config_every_row(name):
 # 128-wide down panels, and 32-row decode-batch tiles.  The capped call must
 # equal the uncapped one bit for bit, and that one the oracle.
 @pytest.mark.parametrize("shape", [(600, 1024, 512, 4, 2), (700, 512, 256, 3, 2),
-                                   (300, 384, 1024, 4, 2), (128, 1024, 512, 16, 4)])
+                                   (300, 384, 1024, 4, 2), (128, 1024, 512, 16, 4),
+                                   (1000, 1024, 512, 3, 2)])
 def test_fp8_many_items_per_workgroup(shape):
     moe = _moe()
     T, H, F, E, k = shape
