@@ -454,10 +454,17 @@ int run_shared(int variant, const uint16_t* hidden, const uint16_t* gate_up, con
     int32_t* idx2 = at<int32_t>(ws, L.aug_idx);
     float* w2 = at<float>(ws, L.aug_w);
     StageClock clock(stream);
+    const ExpertWeights gu{gate_up, shared_gate_up, E}, dn{down, shared_down, E};
+    if (variant == MOE_VARIANT_DECODE && L.decode_fast) {
+        // the gather-GEMV kernel appends the shared slots itself
+        clock.mark(MOE_STAGE_DECODE);
+        return launched(launch_decode(hidden, gu, dn, top_k_index, top_k_weights, residual, (int)T,
+                                      k + S, E + S, H, F, out, at<void>(ws, L.part), stream,
+                                      RouteArgs{}, nullptr, nullptr, S));
+    }
     clock.mark(MOE_STAGE_SHARED_ROUTE);
     rc = launched(launch_augment_routing(top_k_index, top_k_weights, T, k, E, S, idx2, w2, stream));
     if (rc) return rc;
-    const ExpertWeights gu{gate_up, shared_gate_up, E}, dn{down, shared_down, E};
     if (variant == MOE_VARIANT_PREFILL)
         return run_grouped_bf16(clock, L, hidden, gu, dn, idx2, w2, residual, T, H, F, E + S,
                                 k + S, out, ws, stream);

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ wts,
     const uint16_t* __restrict__ residual, int T, int k, int E, int H, int F,
     uint16_t* __restrict__ out, DecodeWs ws, uint64_t spin_ticks,
-    const RouteArgs ra, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    const RouteArgs ra, int32_t* __restrict__ idx_out, float* __restrict__ w_out, int S) {
     constexpr int DB = 16 / NCF;                    // down rows per phase-2 step
     constexpr int kPairBatch = pair_batch<NT, NCH>();
     __shared__ u32x4 h_lds[kDecodeHBytes / 16];     // h rows [P][F], bf16
@@ -298,9 +298,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
         }
     } else if (tid < P) {
-        const int e = idx[tid];
-        slot_e[tid] = (unsigned)e < (unsigned)E ? e : -1;
-        slot_w[tid] = wts[tid];
+        // k counts the S shared slots of each token (experts E-S .. E-1,
+        // weight 1) after its k-S routed ones, read from idx / wts [T, k-S]
+        const int kr = k - S, t = tid / k, j = tid - t * k;
+        int e = E - S + (j - kr);
+        float wv = 1.0f;
+        if (j < kr) {
+            e = idx[t * kr + j];
+            e = (unsigned)e < (unsigned)(E - S) ? e : -1;
+            wv = wts[t * kr + j];
+        }
+        slot_e[tid] = e;
+        slot_w[tid] = wv;
     }
     if (tid == 0) {
         arrive = 0;
@@ -604,11 +613,11 @@ template <int NT, int NCH, int NCF, bool ROUTED>
 static void launch_one(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                        const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
                        int E, int H, int F, uint16_t* out, const DecodeWs& dws, hipStream_t s,
-                       const RouteArgs& ra, int32_t* io, float* wo) {
+                       const RouteArgs& ra, int32_t* io, float* wo, int S) {
     // at most kDecodeMaxRows output rows per workgroup
     const int G = std::max(decode_grid<NT, NCH, NCF, ROUTED>(), (H + kDecodeMaxRows - 1) / kDecodeMaxRows);
     MOE_LAUNCH((decode_kernel<NT, NCH, NCF, ROUTED>), dim3(G), dim3(kDecThreads), 0, s, x, w13, w2, idx, w, residual, T, k, E, H, F, out, dws,
-               kSpinTicks, ra, io, wo);
+               kSpinTicks, ra, io, wo, S);
 }
 
 template <int NT, int NCH, bool ROUTED>
@@ -616,11 +625,11 @@ static hipError_t launch_ncf(int ncf, const uint16_t* x, const ExpertWeights& w1
                              const ExpertWeights& w2, const int32_t* idx, const float* w,
                              const uint16_t* residual, int T, int k, int E, int H, int F,
                              uint16_t* out, const DecodeWs& d, hipStream_t s, const RouteArgs& ra,
-                             int32_t* io, float* wo) {
+                             int32_t* io, float* wo, int S) {
     switch (ncf) {
-        case 1: launch_one<NT, NCH, 1, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
-        case 2: launch_one<NT, NCH, 2, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
-        default: launch_one<NT, NCH, 4, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo); break;
+        case 1: launch_one<NT, NCH, 1, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S); break;
+        case 2: launch_one<NT, NCH, 2, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S); break;
+        default: launch_one<NT, NCH, 4, ROUTED>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S); break;
     }
     return hipGetLastError();
 }
@@ -630,7 +639,7 @@ static hipError_t launch_decode_t(const uint16_t* x, const ExpertWeights& w13,
                                   const ExpertWeights& w2, const int32_t* idx, const float* w,
                                   const uint16_t* residual, int T, int k, int E, int H, int F,
                                   uint16_t* out, void* ws, hipStream_t s, const RouteArgs& ra,
-                                  int32_t* io, float* wo) {
+                                  int32_t* io, float* wo, int S) {
     char* base = (char*)ws;
     const DecodeWs d{(uint64_t*)base, (uint64_t*)(base + 256), (uint32_t*)(base + 256 + 8 * kDecodeMaxGrid),
                      (uint16_t*)(base + kDecodeHOffset)};
@@ -638,17 +647,17 @@ static hipError_t launch_decode_t(const uint16_t* x, const ExpertWeights& w13,
     const int ncf = (F / 8 + 63) / 64;   // 1, 2, 3 (as 4) or 4
     if (T == 1) {
         switch (nch) {
-            case 1: return launch_ncf<1, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
-            case 2: return launch_ncf<1, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
-            case 3: return launch_ncf<1, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
-            case 4: return launch_ncf<1, 4, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+            case 1: return launch_ncf<1, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
+            case 2: return launch_ncf<1, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
+            case 3: return launch_ncf<1, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
+            case 4: return launch_ncf<1, 4, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
             default: return hipErrorInvalidValue;
         }
     }
     switch (nch) {
-        case 1: return launch_ncf<4, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
-        case 2: return launch_ncf<4, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
-        case 3: return launch_ncf<4, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo);
+        case 1: return launch_ncf<4, 1, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
+        case 2: return launch_ncf<4, 2, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
+        case 3: return launch_ncf<4, 3, ROUTED>(ncf, x, w13, w2, idx, w, residual, T, k, E, H, F, out, d, s, ra, io, wo, S);
         default: return hipErrorInvalidValue;   // excluded by decode_fast_path
     }
 }
@@ -656,12 +665,12 @@ static hipError_t launch_decode_t(const uint16_t* x, const ExpertWeights& w13,
 hipError_t launch_decode(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
                          const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
                          int E, int H, int F, uint16_t* out, void* ws, hipStream_t s,
-                         const RouteArgs& ra, int32_t* idx_out, float* w_out) {
+                         const RouteArgs& ra, int32_t* idx_out, float* w_out, int S) {
     if (ra.logits)
         return launch_decode_t<true>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, ws, s, ra,
-                                     idx_out, w_out);
+                                     idx_out, w_out, 0);
     return launch_decode_t<false>(x, w13, w2, idx, w, residual, T, k, E, H, F, out, ws, s, ra,
-                                  idx_out, w_out);
+                                  idx_out, w_out, S);
 }
 
 }  // namespace moe

@@ -132,6 +132,9 @@ inline bool decode_fits(int64_t T, int k, int H, int F) {
            decode_h_bytes(T, k, F) <= (size_t)kDecodeHBytes;
 }
 
+// S > 0: the last S of the E experts are shared experts that every token
+// passes with weight 1; k counts them (k - S routed slots per token, read
+// from idx / w [T, k-S]); no router then.
 // With ra.logits set, the kernel routes the T tokens itself (every
 // workgroup, redundantly; workgroup 0 also writes idx_out / w_out) and
 // idx / w are unused.  ws: decode_ws_bytes, 256-byte aligned.
@@ -139,7 +142,7 @@ hipError_t launch_decode(const uint16_t* x, const ExpertWeights& w13, const Expe
                          const int32_t* idx, const float* w, const uint16_t* residual, int T, int k,
                          int E, int H, int F, uint16_t* out, void* ws, hipStream_t s,
                          const RouteArgs& ra = RouteArgs{}, int32_t* idx_out = nullptr,
-                         float* w_out = nullptr);
+                         float* w_out = nullptr, int S = 0);
 
 // fp8 gate_up product with SwiGLU + block-128 re-quantisation epilogue.
 hipError_t launch_gateup_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
