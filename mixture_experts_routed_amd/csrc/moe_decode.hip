@@ -194,12 +194,11 @@ struct DecRouting {
     uint32_t repm;  // lane u < n_u: representative slots of u
 };
 
-__device__ __forceinline__ DecRouting dec_routing(const int32_t* slot_e, const float* slot_w, int P,
-                                                  int k) {
+// e / wsl: the expert (-1 dropped) and weight of slot lane % 32 (lanes of
+// slots >= P: -1, 0).
+__device__ __forceinline__ DecRouting dec_routing(const int e, const float wsl, int P, int k) {
     const int lane = threadIdx.x & 63, ls = lane & 31;
     DecRouting r;
-    const int e = ls < P ? slot_e[ls] : -1;
-    const float wsl = ls < P ? slot_w[ls] : 0.0f;
     int first = ls;
     for (int q = 0; q < P; ++q) {
         const int eq = __builtin_amdgcn_readlane(e, q);
@@ -297,19 +296,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 }
             }
         }
-    } else if (tid < P) {
-        // k counts the S shared slots of each token (experts E-S .. E-1,
-        // weight 1) after its k-S routed ones, read from idx / wts [T, k-S]
-        const int kr = k - S, t = tid / k, j = tid - t * k;
-        int e = E - S + (j - kr);
-        float wv = 1.0f;
+    }
+    // Given ids: every wave loads slot lane % 32 into its own lanes (no LDS
+    // staging, so the barrier below does not wait for these loads).  k
+    // counts the S shared slots of each token (experts E-S .. E-1, weight 1)
+    // after its k-S routed ones, read from idx / wts [T, k-S].
+    int e_l = -1;
+    float w_l = 0.0f;
+    if (!ROUTED && (lane & 31) < P) {
+        const int ls = lane & 31;
+        const int kr = k - S, t = ls / k, j = ls - t * k;
+        e_l = E - S + (j - kr);
+        w_l = 1.0f;
         if (j < kr) {
-            e = idx[t * kr + j];
-            e = (unsigned)e < (unsigned)(E - S) ? e : -1;
-            wv = wts[t * kr + j];
+            const int e = idx[t * kr + j];
+            e_l = (unsigned)e < (unsigned)(E - S) ? e : -1;
+            w_l = wts[t * kr + j];
         }
-        slot_e[tid] = e;
-        slot_w[tid] = wv;
     }
     if (tid == 0) {
         arrive = 0;
@@ -317,7 +320,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         h_ready = 0;
     }
     lds_barrier();
-    const DecRouting R = dec_routing(slot_e, slot_w, P, k);
+    if (ROUTED && (lane & 31) < P) {
+        e_l = slot_e[lane & 31];
+        w_l = slot_w[lane & 31];
+    }
+    const DecRouting R = dec_routing(e_l, w_l, P, k);
     const int n_u = R.n_u;
     // lane u < n_u: the representative slot of (u, token t), -1 if none
     int rep_of[NT];
