@@ -472,6 +472,39 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "launches": len(calls[0]) if calls else 0}
+        if kind == "bf16" and not decode and not S:
+            # pass E: the same steps through the one-launch form
+            # (moe_experts_prefill_fused: plan, then gate_up, down and the
+            # combine in one persistent launch)
+            def step_fused(i):
+                s_ = i % sets
+                idx, w = routes[i % len(routes)]
+                return moe.moe_experts_prefill_fused(hidden, gu_sets[s_], dn_sets[s_], idx, w, k,
+                                                     out=out_buf)
+            for i in range(warmup):
+                step_fused(i)
+            torch.cuda.synchronize()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for i in range(steps):
+                step_fused(warmup + i)
+            ev1.record()
+            torch.cuda.synchronize()
+            moe.moe_profile_begin(steps)
+            for i in range(steps):
+                step_fused(warmup + i)
+            torch.cuda.synchronize()
+            calls = moe.moe_profile_end(steps)
+            per = collections.defaultdict(list)
+            for row in calls:
+                for st, ms in row:
+                    per[st].append(ms)
+            out["fused_layer"] = {
+                "entry": "moe_experts_prefill_fused (plan, then one persistent launch)",
+                "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
+                "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
+                "stage_us": {st: round(float(np.mean(v)) * 1e3, 2) for st, v in per.items()}}
     ctx = (cfg, host_routes, warmup, problem)
     return out, ctx
 
@@ -484,7 +517,8 @@ def summary_of(out):
             "layer_hbm_GBps": out["layer"]["hbm_GBps"], "layer_TFLOPps": out["layer"]["TFLOPps"],
             "dominant_kernel": r.get("kernel"), "dominant_kernel_us": r.get("kernel_us"),
             "roofline": {kk: r.get(kk) for kk in ("bound", "achieved", "peak", "unit", "frac")} if r else None,
-            "stage_us": out.get("stage_us")}
+            "stage_us": out.get("stage_us"),
+            **({"fused_layer_us_per_call": out["fused_layer"]["us_per_call"]} if "fused_layer" in out else {})}
 
 
 def probe(moe, torch, np):

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 enum moe_status {
     MOE_OK = 0,
@@ -142,6 +142,29 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
                         const int32_t* top_k_index, const float* top_k_weights,
                         const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                         uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same layer as moe_experts_prefill (same operands, workspace
+ * moe_workspace_size(MOE_VARIANT_PREFILL, ...), errors and results: out is
+ * bit-for-bit that of moe_experts_prefill), with the grouped gate_up
+ * product, the grouped down product and the combine in one persistent
+ * launch after the routing plan (the single-kernel MoE idea of the DeepGEMM
+ * "Mega MoE" news item, on one GPU).  Workgroups hand tiles to each other
+ * through flags in the workspace: a down tile starts as soon as its rows of
+ * h are stored, and the combine once every down tile is, so the tails of
+ * the two products overlap.  The workgroups wait for each other, so they
+ * must be resident together (the library sizes the grid from the device's
+ * occupancy); a wait longer than 2 s gives NaN outputs.  The workspace needs
+ * no initialisation: a generation word in it, advanced on the device by
+ * every call, stamps the flags (calls must be ordered, as on one stream).
+ * H and F multiples of 128; other shapes run the moe_experts_prefill
+ * sequence.
+ */
+int moe_experts_prefill_fused(const uint16_t* hidden, const uint16_t* gate_up,
+                              const uint16_t* down, const int32_t* top_k_index,
+                              const float* top_k_weights, const uint16_t* residual, int64_t T,
+                              int H, int F, int E, int k, uint16_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /*
  * bf16 routed experts, gather-GEMV form for a handful of tokens (the model
@@ -497,6 +520,7 @@ enum moe_stage {
     MOE_STAGE_ROUTER = 7,        /* router (logits -> ids, weights)          */
     MOE_STAGE_ROUTE_PLAN = 8,    /* router and plan in one launch            */
     MOE_STAGE_PROBE = 9,         /* moe_probe_stream_read                    */
+    MOE_STAGE_LAYER = 10,        /* gate_up, down and combine in one launch  */
 };
 int moe_profile_begin(int max_calls);
 int moe_profile_end(int max_calls, int* n_calls, float* ms, int* stage_ids);

@@ -54,6 +54,7 @@ def _load():
         "moe_workspace_layout": ([i32, i64, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "moe_routing_plan": ([vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_experts_prefill": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_prefill_fused": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_decode": ([vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_prefill_shared": ([vp] * 8 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_decode_shared": ([vp] * 8 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
@@ -97,7 +98,7 @@ def exported_symbols():
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
             "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc",
             "moe_probe_stream_read", "moe_quantize_fp8_block128_ue8m0", "moe_experts_fp8_shared",
-            "moe_experts_mxfp4_shared"]
+            "moe_experts_mxfp4_shared", "moe_experts_prefill_fused"]
 
 
 class MoeError(RuntimeError):
@@ -149,7 +150,7 @@ def moe_workspace_layout(variant, T, H, F, E, k):
 # ------------------------------------------------------------ stage timing
 MOE_PROFILE_MAX_STAGES = 5
 STAGE_NAMES = {0: "plan", 1: "gate_up", 2: "down", 3: "combine", 4: "decode", 5: "quantize",
-               6: "shared_route", 7: "router", 8: "route_plan", 9: "probe"}
+               6: "shared_route", 7: "router", 8: "route_plan", 9: "probe", 10: "layer"}
 
 
 def moe_profile_begin(max_calls):
@@ -303,6 +304,15 @@ def moe_experts_prefill(hidden_states, gate_up_proj, down_proj, top_k_index, top
     optional residual [T, H] bf16)."""
     return _bf16_call("moe_experts_prefill", MOE_VARIANT_PREFILL, hidden_states, gate_up_proj,
                       down_proj, top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_prefill_fused(hidden_states, gate_up_proj, down_proj, top_k_index,
+                              top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """moe_experts_prefill with gate_up, down and the combine in one
+    persistent launch after the plan (same operands, workspace and result)."""
+    return _bf16_call("moe_experts_prefill_fused", MOE_VARIANT_PREFILL, hidden_states,
+                      gate_up_proj, down_proj, top_k_index, top_k_weights, top_k, residual,
+                      workspace, out)
 
 
 def moe_experts_decode(hidden_states, gate_up_proj, down_proj, top_k_index, top_k_weights,
@@ -737,8 +747,9 @@ def moe_quantize_fp8_block128_ue8m0(t):
 __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
     "moe_profile_begin", "moe_profile_end",
-    "moe_routing_plan", "moe_experts_prefill", "moe_experts_decode", "moe_experts_fp8",
-    "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128", "moe_quantize_fp8_block128_ue8m0",
+    "moe_routing_plan", "moe_experts_prefill", "moe_experts_prefill_fused", "moe_experts_decode",
+    "moe_experts_fp8", "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128",
+    "moe_quantize_fp8_block128_ue8m0",
     "moe_experts_fp8_shared", "moe_experts_mxfp4_shared", "moe_experts_prefill_shared",
     "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
     "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",

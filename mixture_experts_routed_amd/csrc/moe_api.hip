@@ -105,7 +105,7 @@ constexpr size_t kNone = (size_t)-1;
 struct Layout {
     size_t counts = kNone, offsets = kNone, perm = kNone, inv = kNone, tiles = kNone,
            ntiles = kNone, tile_off = kNone, h = kNone, hs = kNone, y = kNone, part = kNone,
-           xq = kNone, xs = kNone, aug_idx = kNone, aug_w = kNone, total = 0;
+           xq = kNone, xs = kNone, aug_idx = kNone, aug_w = kNone, sync = kNone, total = 0;
     bool decode_fast = false;
 };
 
@@ -152,6 +152,8 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
         L.h = take((size_t)P * F * 2);
     }
     L.y = take((size_t)P * H * 2);
+    if (variant == MOE_VARIANT_PREFILL)   // hand-off words of moe_experts_prefill_fused
+        L.sync = take(layer_sync_bytes(P, E, F));
     if (variant == MOE_VARIANT_FP8_BF16IN) {  // the quantised hidden states
         L.xq = take((size_t)T * H);
         L.xs = take((size_t)T * (H / 128) * sizeof(float));
@@ -232,6 +234,30 @@ int run_grouped_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
     if (rc) return rc;
     clock.mark(MOE_STAGE_COMBINE);
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, s));
+}
+
+// The same layer as run_grouped_bf16 with gate_up, down and the combine in
+// one persistent launch after the plan (shapes that fit it; others take the
+// stage-by-stage sequence).
+int run_layer_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
+                   const ExpertWeights& gate_up, const ExpertWeights& down, const int32_t* idx,
+                   const float* w, const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                   uint16_t* out, void* ws, hipStream_t s) {
+    if (!layer_bf16_fits(H, F))
+        return run_grouped_bf16(clock, L, hidden, gate_up, down, idx, w, residual, T, H, F, E, k,
+                                out, ws, s);
+    const int P = (int)(T * k);
+    const GroupedPlan pl = plan_in(L, ws, E);
+    clock.mark(MOE_STAGE_PLAN);
+    int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                                  at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
+                                  at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
+                                  at<int32_t>(ws, L.tile_off), bf16_tile_m(), s));
+    if (rc) return rc;
+    clock.mark(MOE_STAGE_LAYER);
+    return launched(launch_layer_bf16(hidden, gate_up, down, pl, at<int32_t>(ws, L.inv), w,
+                                      residual, T, H, F, k, at<uint16_t>(ws, L.h),
+                                      at<uint16_t>(ws, L.y), out, at<void>(ws, L.sync), s));
 }
 
 int check_bf16_args(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,
@@ -568,6 +594,24 @@ int moe_experts_prefill(const uint16_t* hidden, const uint16_t* gate_up, const u
     StageClock clock(stream);
     return run_grouped_bf16(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E),
                             top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, stream);
+}
+
+int moe_experts_prefill_fused(const uint16_t* hidden, const uint16_t* gate_up,
+                              const uint16_t* down, const int32_t* top_k_index,
+                              const float* top_k_weights, const uint16_t* residual, int64_t T,
+                              int H, int F, int E, int k, uint16_t* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    int rc = check_bf16_args(hidden, gate_up, down, top_k_index, top_k_weights, residual, out);
+    if (rc) return rc;
+    if ((rc = check_shape(MOE_VARIANT_PREFILL, T, H, F, E, k))) return rc;
+    const Layout L = make_layout(MOE_VARIANT_PREFILL, T, H, F, E, k);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    int dev;
+    if ((rc = query_device(&dev))) return rc;
+    if (T == 0) return MOE_OK;
+    StageClock clock(stream);
+    return run_layer_bf16(clock, L, hidden, routed_only(gate_up, E), routed_only(down, E),
+                          top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws, stream);
 }
 
 int moe_experts_decode(const uint16_t* hidden, const uint16_t* gate_up, const uint16_t* down,

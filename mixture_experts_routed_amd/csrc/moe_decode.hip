@@ -48,30 +48,12 @@ constexpr int kDecP2Waves = 7;                    // waves with down-phase tasks
 template <int NT, int NCH>
 constexpr int pair_batch() { return NT == 1 && NCH <= 3 ? 3 : 2; }
 
-// Device-scope (sc1) accesses: they bypass the non-coherent per-XCD L2, so
-// data written by one workgroup is seen by any other once the store has
-// completed (s_waitcnt).
+// More device-scope (sc1) stores, next to those of moe_device.h.
 __device__ __forceinline__ void st_dev_f32(float* p, float v) {
     __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_dev_u16(uint16_t* p, uint16_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16 bytes per lane from global memory into LDS, device scope (sc1 = 16).
-__device__ __forceinline__ void dma16_dev(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 16);
-}
-// every vector-memory operation of this wave has completed
-__device__ __forceinline__ void wait_vm_all() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    asm volatile("" ::: "memory");
 }
 
 // Weight rows are read through buffer resources: a load past the resource's

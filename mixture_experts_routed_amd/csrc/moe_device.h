@@ -156,6 +156,30 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------------- device-scope accesses
+// Relaxed atomics at agent scope (sc1): they bypass the non-coherent per-XCD
+// L2, so data written by one workgroup is seen by any other once the store
+// has completed (s_waitcnt).
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes per lane from global memory into LDS, device scope (sc1 = 16).
+__device__ __forceinline__ void dma16_dev(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 16);
+}
+// every vector-memory operation of this wave has completed
+__device__ __forceinline__ void wait_vm_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------- scheduling helpers
 // Persistent grids walk work items i = round * G + slot.  Workgroup b runs on
 // XCD b % 8; giving each XCD a contiguous run of slots keeps work items that

@@ -41,6 +41,10 @@ struct WaveGrid {
     __device__ static int wn(int wave) { return WN == 4 ? wave & 3 : wave >> 2; }
 };
 
+// The persistent loop of a grouped product, shared by the stand-alone
+// kernels and the one-launch layer, which differ in the Sched hooks: which
+// items a workgroup takes, what it waits for before reading an item's
+// operands, how it stores and what it signals once stores have completed.
 // One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
 // expert's weight panel).  Wave (wm, wn) owns tile rows [32 MB wm, 32 MB
 // (wm+1)) as MB 32-row blocks and panel rows [32 NB wn, 32 NB (wn+1)) as NB
@@ -51,19 +55,19 @@ struct WaveGrid {
 // at its fixed LDS position, so the bank swizzle costs nothing.  The token
 // rows have two stages and the weight rows three: weights come from HBM and
 // need the longer lead; together they fill the 160 KB of LDS.  Rows past an
-// M tile's end load row 0 (valid memory) and their outputs are never stored.
+// M tile's end load a row of the tile (or token row 0) and their outputs are
+// never stored.
 // SWIGLU: panel rows are interleaved in blocks of 32 as gate, up, gate, up,
 // ... so each wave holds matching gate/up accumulators lane for lane, and the
 // epilogue writes h = silu(gate) * up as bf16 [P, F] in expert order.
 // Otherwise the epilogue writes y bf16 [P, n_out] in expert order too (the
 // combine finds a slot's row through the plan's inverse permutation).
-template <int BN, bool SWIGLU>
-__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const ExpertWeights B,
+template <int BN, bool SWIGLU, class Sched>
+__device__ __forceinline__ void grouped_loop(
+    u32x4* __restrict__ lds, const uint16_t* __restrict__ A, const ExpertWeights& B,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
-    uint16_t* __restrict__ C) {
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint16_t* __restrict__ C, Sched& sc) {
     using WG = WaveGrid<BN>;
     constexpr int MB = WG::MB;
     constexpr int NB = WG::NB;
@@ -73,15 +77,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     constexpr int B_STAGE = BN * 8;
     constexpr int B_BASE = kAStages * A_STAGE;
     static_assert(NB >= 1 && B_INST >= 1 && (!SWIGLU || NB % 2 == 0), "bad panel width");
-    // one array for both operands (with fills into two arrays the compiler
-    // adds a wait for all of them before every LDS read)
-    __shared__ u32x4 lds[kAStages * A_STAGE + kBStages * B_STAGE];
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = WG::wm(wave), wn = WG::wn(wave);
-    const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
-    const int items = ntiles * n_tiles_n;
     const int nks = K / kBK;
     const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32 b + lane % 32
     const int lrow = lane >> 3, lslot = lane & 7;
@@ -89,12 +87,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
     // Per-item state: which tile, and every lane's row pointers for its
     // share of the LDS fills.
     struct Item {
+        GroupedItem gi;
         int e, nt, row0, mrows;
         const uint16_t* a_src[A_INST];
         const uint16_t* b_src[B_INST];
     };
     auto setup = [&](int it, Item& m) {
         const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        m.gi = gi;
         m.e = gi.e;
         m.nt = gi.nt;
         m.row0 = tiles[2 * gi.mt + 1];
@@ -109,7 +109,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < A_INST; ++i) {
             const int r = 8 * (A_INST * wave + i) + lrow;
-            const int64_t arow = r < m.mrows ? (SWIGLU ? pr[i] / topk : m.row0 + r) : 0;
+            // rows past the tile's end repeat its first row (never stored)
+            const int64_t arow = SWIGLU ? (r < m.mrows ? pr[i] / topk : 0) : m.row0 + (r < m.mrows ? r : 0);
             m.a_src[i] = A + arow * K + lds_chunk(r, lslot) * 8;
         }
         const uint16_t* Be = B.expert(m.e, (int64_t)b_rows * K);
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
                         const int row = 32 * (MB * wm + mb) + acc_row(q, lane) + (odd ? 1 : 0);
                         if (row < m.mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, h1) : pack_bf16x2_hw(h0, got);
-                            *(uint32_t*)(C + (int64_t)(m.row0 + row) * n_out + (f & ~1)) = v;
+                            sc.store(C + (int64_t)(m.row0 + row) * n_out + (f & ~1), v);
                         }
                     }
                 }
@@ -215,23 +216,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
                         const int col = m.nt * BN + (wn * NB + nb) * 32 + (lane & 30);
                         if (row < m.mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
-                            *(uint32_t*)(C + (int64_t)(m.row0 + row) * n_out + col) = v;
+                            sc.store(C + (int64_t)(m.row0 + row) * n_out + col, v);
                         }
                     }
                 }
         }
     };
 
-    int it = xcd_slot(blockIdx.x, gridDim.x);
-    if (it >= items) return;
+    int it = sc.first();
+    if (it < 0) {
+        sc.drained();
+        return;
+    }
     Item cur, nxt;
     setup(it, cur);
+    sc.wait_inputs(cur.gi);
     prologue(cur);
     while (true) {
         // The next item's row pointers are worked out while this item's first
         // stages load (their slot-id loads then cost no wait of their own).
-        const int next = it + gridDim.x;
-        const bool more = next < items;
+        const int next = sc.next(it);
+        const bool more = next >= 0;
         setup(more ? next : it, nxt);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -253,13 +258,51 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
 
         // The next item's first stages load while this tile is stored (on the
         // last item the same tile is fetched again and never read).
+        if (more) sc.wait_inputs(nxt.gi);
         prologue(nxt);
         epilogue(cur);
+        sc.stored(it);
         if (!more) break;
         it = next;
         cur = nxt;
     }
+    sc.drained();
     __builtin_amdgcn_s_waitcnt(0);  // no LDS fill may outlive the workgroup
+}
+
+// Hooks of the stand-alone kernels: workgroup b takes item xcd_slot(b) and
+// then every G-th (consecutive items run on one XCD), stores are plain and
+// nothing is waited for (the kernel boundaries order the stages).
+struct PlainSched {
+    int items;
+    __device__ int first() const {
+        const int it = xcd_slot(blockIdx.x, gridDim.x);
+        return it < items ? it : -1;
+    }
+    __device__ int next(int it) const {
+        return it + (int)gridDim.x < items ? it + (int)gridDim.x : -1;
+    }
+    __device__ void wait_inputs(const GroupedItem&) const {}
+    __device__ void store(uint16_t* p, uint32_t v) const { *(uint32_t*)p = v; }
+    __device__ void stored(int) const {}
+    __device__ void drained() const {}
+};
+
+// One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
+// expert's weight panel); the grid is persistent (see grouped_loop).
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(kGemmThreads) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const ExpertWeights B,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles_p, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
+    uint16_t* __restrict__ C) {
+    // one array for both operands (with fills into two arrays the compiler
+    // adds a wait for all of them before every LDS read)
+    __shared__ u32x4 lds[kAStages * kBM * 8 + kBStages * BN * 8];
+    PlainSched sc{*ntiles_p * (SWIGLU ? n_out / (BN / 2) : n_out / BN)};
+    grouped_loop<BN, SWIGLU>(lds, A, B, perm, tiles, tile_off, offsets, E, K, n_out, b_rows, topk,
+                             C, sc);
 }
 
 int bf16_tile_m() { return kBM; }
@@ -309,19 +352,17 @@ hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const Gr
 }
 
 // ------------------------------------------------------------------ combine
-// One thread per (token, 8 columns): out = sum_j w[t,j] * y[inv[t*k+j]] in
+// Unit g = (token t, 8 columns c): out = sum_j w[t,j] * y[inv[t*k+j]] in
 // slot order, plus the residual if any, in fp32, one rounding to bf16.  y is
 // in expert order; inv (from the plan) is -1 for dropped slots, which
 // contribute nothing.
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
-                                                      const int32_t* __restrict__ inv,
-                                                      const float* __restrict__ w,
-                                                      const uint16_t* __restrict__ residual,
-                                                      int64_t T, int k, int H,
-                                                      uint16_t* __restrict__ out) {
+__device__ __forceinline__ void combine_unit(const uint16_t* __restrict__ y,
+                                             const int32_t* __restrict__ inv,
+                                             const float* __restrict__ w,
+                                             const uint16_t* __restrict__ residual, int64_t g,
+                                             int k, int H, bool nan_out,
+                                             uint16_t* __restrict__ out) {
     const int cpr = H / 8;
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= T * cpr) return;
     const int64_t t = g / cpr;
     const int c = (int)(g - t * cpr) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -346,7 +387,78 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     o.y = pack_bf16x2(acc[2], acc[3]);
     o.z = pack_bf16x2(acc[4], acc[5]);
     o.w = pack_bf16x2(acc[6], acc[7]);
+    if (nan_out) o = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
     *(uint4*)(out + t * H + c) = o;
+}
+
+// NU units per thread at once with every slot's loads in flight (k <= KM):
+// the same sums as combine_unit, for a grid with few waves per CU.
+template <int KM, int NU>
+__device__ __forceinline__ void combine_units(const uint16_t* __restrict__ y,
+                                              const int32_t* __restrict__ inv,
+                                              const float* __restrict__ w,
+                                              const uint16_t* __restrict__ residual, int64_t g0,
+                                              int64_t gstep, int64_t gend, int k, int H,
+                                              bool nan_out, uint16_t* __restrict__ out) {
+    const int cpr = H / 8;
+    int64_t t[NU];
+    int c[NU], r[NU][KM];
+    float wt[NU][KM];
+    uint4 v[NU][KM];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int64_t g = min(g0 + u * gstep, gend - 1);
+        t[u] = g / cpr;
+        c[u] = (int)(g - t[u] * cpr) * 8;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            r[u][j] = j < k ? inv[t[u] * k + j] : -1;
+            wt[u][j] = j < k ? w[t[u] * k + j] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+            v[u][j] = r[u][j] >= 0 ? *(const uint4*)(y + (int64_t)r[u][j] * H + c[u]) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        if (g0 + u * gstep >= gend) break;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            if (r[u][j] < 0) continue;
+            float f[8];
+            unpack8(v[u][j], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wt[u][j] * f[i];
+        }
+        if (residual) {
+            float rs[8];
+            unpack8(*(const uint4*)(residual + t[u] * H + c[u]), rs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += rs[i];
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        if (nan_out) o = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+        *(uint4*)(out + t[u] * H + c[u]) = o;
+    }
+}
+
+// one thread per unit
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w,
+                                                      const uint16_t* __restrict__ residual,
+                                                      int64_t T, int k, int H,
+                                                      uint16_t* __restrict__ out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= T * (H / 8)) return;
+    combine_unit(y, inv, w, residual, g, k, H, false, out);
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
@@ -355,6 +467,225 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
     const int64_t n = T * (H / 8);
     const int blocks = (int)((n + 255) / 256);
     MOE_LAUNCH(combine_kernel, dim3(blocks), dim3(256), 0, s, y, inv, w, residual, T, k, H, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ one-launch layer
+// The grouped path in one persistent launch after the plan: gate_up items,
+// then down items, then the combine, handed over between workgroups through
+// flags in the workspace instead of kernel boundaries (the single-kernel
+// idea of the DeepGEMM "Mega MoE" news item, on one GPU).  Workgroup b walks
+// the sequence xcd_slot(b) + j G over [gate_up items | down items], so the
+// workgroups with one gate_up item fewer start the down items first, and a
+// workgroup only ever waits for items earlier in the sequence, held by
+// resident workgroups: the waits end.
+//  - a gate_up item stores its h tile with device-scope stores; once they
+//    have completed in every wave (right after the epilogue) it stores its
+//    flag (the call's stamp);
+//  - a down item first waits for the flags of its M tile's gate_up items,
+//    then reads h rows as usual: no copy of them is in any L2 yet, so the
+//    reads fetch the stored values;
+//  - a workgroup past its down items stores its down flag; the combine
+//    waits for every workgroup's down flag, then sums its share of tokens
+//    exactly as combine_kernel does.
+// The stamp is the generation word + 1; workgroup 0 advances the word at
+// the end, once every workgroup has acknowledged reading it, so flags of
+// earlier calls never match.  Waits are bounded by a clock limit: a grid that
+// is not resident together gives NaN outputs and sets the error word.
+// Hand-off words (64-bit) in the workspace, from one base pointer:
+struct LayerSync {
+    uint64_t* base;
+    __device__ uint64_t* gen() const { return base; }        // generation word
+    __device__ uint64_t* err() const { return base + 1; }    // = stamp when a wait timed out
+    __device__ uint64_t* ack() const { return base + 32; }   // [G] workgroup read the generation
+    __device__ uint64_t* dflag() const { return base + 32 + kLayerMaxGrid; }   // [G] down items done
+    __device__ uint64_t* gflag() const { return base + 32 + 2 * kLayerMaxGrid; }  // [gate_up items]
+};
+
+// wave 0 waits until flags[i * stride], i < n, all equal stamp (each wait
+// bounded by kLayerSpinTicks of the 100 MHz clock; past it the error word
+// takes the stamp); then the whole workgroup passes a barrier
+__device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int stride,
+                                           uint64_t stamp, LayerSync sy) {
+    if (threadIdx.x < 64) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (true) {
+            bool all = true;
+            for (int i = threadIdx.x; i < n; i += 64) all &= ld_dev_u64(flags + (int64_t)i * stride) == stamp;
+            if (__all(all)) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kLayerSpinTicks) {
+                if (threadIdx.x == 0) st_dev_u64(sy.err(), stamp);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    lds_barrier();
+}
+
+// gate_up phase (GATE) or down phase of the one-launch layer.
+// Slot s = xcd_slot(b) takes gate_up items s, s + G, ... (q + 1 of them for
+// s < r, q for s >= r, with NG = q G + r), then its down items.  Down items
+// are numbered like gate_up items (expert by expert), and the k-th down item
+// of slot s is the item whose number is:
+//  - for s >= r and k < c ("early" items, started while the last round of
+//    gate_up items still runs): k (G - r) + (s - r), so these come from the
+//    first experts, whose gate_up items finished in the earlier rounds;
+//  - otherwise c (G - r) + the rank of the slot's sequence position
+//    s + (nG(s) + k) G among the positions not taken by early items.
+// c = how many down items fit in one gate_up item's time, bounded so that
+// the early items stay within the tiles of finished rounds.  Any order is
+// deadlock-free: down items wait only for gate_up items, and every
+// workgroup runs all its gate_up items first.
+template <bool GATE>
+struct LayerSched {
+    int items, NG, npg, c;   // npg: gate_up items per M tile
+    uint64_t stamp;
+    LayerSync sy;
+    const int32_t* tile_off;
+    int k;
+    __device__ int down_item(int kk) const {
+        const int G = gridDim.x, s = xcd_slot(blockIdx.x, G);
+        const int q = NG / G, r = NG % G, nf = G - r;
+        if (c > 0 && s >= r && kk < c) return kk * nf + (s - r);
+        const int j = (s < r ? q + 1 : q) + kk;            // the position's round
+        const int jr = q + 1, jf = q + (c > 0 ? c : 0);    // first rounds not early
+        int64_t rank = (int64_t)r * max(0, j - jr) + (int64_t)nf * max(0, j - jf);
+        if (j >= jr) rank += min(s, r);
+        if (j >= jf) rank += max(0, s - r);
+        const int64_t it = (int64_t)c * nf + rank;
+        return it < items ? (int)it : -1;
+    }
+    __device__ int first() {
+        const int G = gridDim.x, seq0 = xcd_slot(blockIdx.x, G);
+        if (GATE) return seq0 < items ? seq0 : -1;
+        k = 0;
+        return down_item(0);
+    }
+    __device__ int next(int it) {
+        if (GATE) return it + (int)gridDim.x < items ? it + (int)gridDim.x : -1;
+        return down_item(++k);
+    }
+    __device__ void wait_inputs(const GroupedItem& gi) const {
+        if (GATE) return;
+        const int t0e = tile_off[gi.e], mtiles = tile_off[gi.e + 1] - t0e;
+        // gate_up items of M tile gi.mt: npg * t0e + panel * mtiles + (mt - t0e)
+        wait_flags(sy.gflag() + (int64_t)npg * t0e + (gi.mt - t0e), npg, mtiles, stamp, sy);
+    }
+    __device__ void store(uint16_t* p, uint32_t v) const { st_dev_u32((uint32_t*)p, v); }
+    // a gate_up item's flag, once its stores have completed in every wave
+    // (the next item's first loads, issued before them, have landed too)
+    __device__ void stored(int it) const {
+        if (!GATE) return;
+        wait_vm_all();
+        lds_barrier();
+        if (threadIdx.x == 0) st_dev_u64(sy.gflag() + it, stamp);
+    }
+    __device__ void drained() const {
+        if (GATE) return;
+        wait_vm_all();
+        lds_barrier();
+        if (threadIdx.x == 0) st_dev_u64(sy.dflag() + blockIdx.x, stamp);
+    }
+};
+
+template <int BNG, int BND>
+__global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
+    const uint16_t* __restrict__ x, const ExpertWeights w13, const ExpertWeights w2,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ inv,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets,
+    const float* __restrict__ wts, const uint16_t* __restrict__ residual, int64_t T, int E, int H,
+    int F, int k, uint16_t* __restrict__ h, uint16_t* __restrict__ y, uint16_t* __restrict__ out,
+    LayerSync sy) {
+    constexpr int BNMAX = BNG > BND ? BNG : BND;
+    __shared__ u32x4 lds[kAStages * kBM * 8 + kBStages * BNMAX * 8];
+    const int b = blockIdx.x, G = gridDim.x;
+    // this call's stamp, known to wave 0 (kept in scalar registers)
+    uint64_t stamp = 0;
+    if (threadIdx.x < 64) {
+        stamp = ld_dev_u64(sy.gen()) + 1;
+        if (threadIdx.x == 0) st_dev_u64(sy.ack() + b, stamp);
+    }
+    stamp = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(stamp >> 32)) << 32) |
+            __builtin_amdgcn_readfirstlane((uint32_t)stamp);
+    const int ntiles = *ntiles_p;
+    const int npg = F / (BNG / 2), npd = H / BND;
+    const int NG = ntiles * npg;
+
+    LayerSched<true> sg{NG, NG, npg, 0, stamp, sy, tile_off, 0};
+    grouped_loop<BNG, true>(lds, x, w13, perm, tiles, tile_off, offsets, E, H, F, 2 * F, k, h, sg);
+    // early down items per slot with one gate_up item fewer: a gate_up item's
+    // time in down items (H x BNG against F x BND products), within the
+    // down items of the tiles finished in the earlier rounds
+    const int ND = ntiles * npd, q = NG / G, nf = G - NG % G;
+    int c = 0;
+    if (NG % G != 0) {
+        c = (H * BNG + F * BND - 1) / (F * BND);
+        c = min(c, min(ND, q * G / npg * npd) / nf);
+    }
+    LayerSched<false> sd{ND, NG, npg, c, stamp, sy, tile_off, 0};
+    grouped_loop<BND, false>(lds, h, w2, perm, tiles, tile_off, offsets, E, F, H, H, 1, y, sd);
+
+    // combine: every workgroup's down items are stored (and the operand
+    // ring is idle: its first word carries the error state to all waves)
+    wait_flags(sy.dflag(), G, 1, stamp, sy);
+    int* failed = (int*)lds;
+    if (threadIdx.x == 0) *failed = ld_dev_u64(sy.err()) == stamp;
+    if (b == 0 && threadIdx.x < 64) {
+        // every workgroup has read the generation word (each stored its
+        // acknowledgement at its start): advance it
+        bool all;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        do {
+            all = true;
+            for (int i = threadIdx.x; i < G; i += 64) all &= ld_dev_u64(sy.ack() + i) == stamp;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kLayerSpinTicks) break;
+        } while (!__all(all));
+        if (threadIdx.x == 0) st_dev_u64(sy.gen(), stamp);
+    }
+    lds_barrier();
+    const bool bad = *failed;
+    const int64_t U = T * (H / 8), u0 = U * b / G, u1 = U * (b + 1) / G;
+    if (k <= 8) {
+        // two units per thread at a time, all their slot loads in flight
+        for (int64_t g = u0 + threadIdx.x; g < u1; g += 2 * kGemmThreads)
+            combine_units<8, 2>(y, inv, wts, residual, g, kGemmThreads, u1, k, H, bad, out);
+    } else {
+        for (int64_t g = u0 + threadIdx.x; g < u1; g += kGemmThreads)
+            combine_unit(y, inv, wts, residual, g, k, H, bad, out);
+    }
+}
+
+// A whole number of 128-column h blocks and down panels (other shapes take
+// the stand-alone kernels).
+bool layer_bf16_fits(int H, int F) { return H % 128 == 0 && F % 128 == 0; }
+
+size_t layer_sync_bytes(int64_t P, int E, int F) {
+    return 8 * (32 + 2 * (size_t)kLayerMaxGrid + (size_t)max_m_tiles(P, E) * (F / 128));
+}
+
+template <int BND>
+static int layer_grid() {
+    static const int g = std::min(
+        resident_grid((const void*)layer_bf16_kernel<256, BND>, kGemmThreads, device_cu_count()),
+        kLayerMaxGrid);
+    return capped_grid(g);
+}
+
+hipError_t launch_layer_bf16(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
+                             const GroupedPlan& pl, const int32_t* inv, const float* w,
+                             const uint16_t* residual, int64_t T, int H, int F, int k,
+                             uint16_t* h, uint16_t* y, uint16_t* out, void* sync, hipStream_t s) {
+    const LayerSync sy{(uint64_t*)sync};
+    if (H % 256 == 0)
+        MOE_LAUNCH((layer_bf16_kernel<256, 256>), dim3(layer_grid<256>()), dim3(kGemmThreads), 0,
+                   s, x, w13, w2, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w,
+                   residual, T, pl.E, H, F, k, h, y, out, sy);
+    else
+        MOE_LAUNCH((layer_bf16_kernel<256, 128>), dim3(layer_grid<128>()), dim3(kGemmThreads), 0,
+                   s, x, w13, w2, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w,
+                   residual, T, pl.E, H, F, k, h, y, out, sy);
     return hipGetLastError();
 }
 

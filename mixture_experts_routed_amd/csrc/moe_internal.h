@@ -100,6 +100,19 @@ hipError_t launch_gateup_bf16(const uint16_t* x, const ExpertWeights& w13, const
 hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const GroupedPlan& plan,
                             int P, int H, int F, uint16_t* y, hipStream_t s);
 
+// The same three stages in one persistent launch after the plan (see
+// moe_gemm_bf16.hip), for H and F multiples of 128: h and y go through the
+// workspace as in the stage-by-stage form and out is bit-for-bit the same.
+// `sync` holds layer_sync_bytes of hand-off words (no initialisation needed).
+constexpr int kLayerMaxGrid = 1024;                  // flag slots per workgroup kind
+constexpr uint64_t kLayerSpinTicks = 200000000ull;   // 2 s of the 100 MHz clock
+bool layer_bf16_fits(int H, int F);
+size_t layer_sync_bytes(int64_t P, int E, int F);
+hipError_t launch_layer_bf16(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
+                             const GroupedPlan& plan, const int32_t* inv, const float* w,
+                             const uint16_t* residual, int64_t T, int H, int F, int k,
+                             uint16_t* h, uint16_t* y, uint16_t* out, void* sync, hipStream_t s);
+
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots (fp32, slot order)
 // + residual[t] when residual is not null.
 hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 8
+    assert moe.moe_abi_version() == 9
     for rc in (OK, ENULL, ESHAPE, EALIGN, EWS, ELAUNCH, EDEV, -7, -99):
         s = moe.moe_strerror(rc)
         assert isinstance(s, str) and s
@@ -115,7 +115,8 @@ def _prefill(lib, fn, *, hidden=P16, gu=P16, dn=P16, idx=P16, w=P16, res=None, o
     return getattr(lib, fn)(hidden, gu, dn, idx, w, res, T, H, F, E, k, out, ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("fn", ["moe_experts_prefill", "moe_experts_decode"])
+@pytest.mark.parametrize("fn", ["moe_experts_prefill", "moe_experts_prefill_fused",
+                                "moe_experts_decode"])
 def test_bf16_entry_validation(fn):
     lib = moe._load()
     assert _prefill(lib, fn, hidden=None) == ENULL
@@ -247,6 +248,7 @@ def test_decode_routed_validation():
 def test_valid_arguments_without_gpu_report_device_error():
     lib = moe._load()
     assert _prefill(lib, "moe_experts_prefill") == EDEV
+    assert _prefill(lib, "moe_experts_prefill_fused") == EDEV
     assert _prefill(lib, "moe_experts_decode") == EDEV
 
 

@@ -1,0 +1,182 @@
+"""GPU parity of moe_experts_prefill_fused: the grouped bf16 layer with
+gate_up, down and the combine in one persistent launch after the plan.
+
+The one-launch form performs the same arithmetic as the stage-by-stage form
+(moe_experts_prefill, itself checked on every element against the oracle in
+test_gpu_parity.py), so its output must equal that form's bit for bit; it is
+also compared with the float64 oracle directly at the bf16 bar
+|gpu - ref| <= 1e-2 + 1e-2 |ref|.  The hand-offs between workgroups are
+exercised with small persistent grids (many items per workgroup, down items
+waiting for gate_up items), repeated calls on one workspace (the generation
+stamps) and a workspace full of stale bytes.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = (1e-2, 1e-2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_routed_amd as moe
+    moe._load()
+    yield
+    moe.moe_set_grid_cap(0)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _moe():
+    import mixture_experts_routed_amd as moe
+    return moe
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_tol(gpu, ref, what):
+    atol, rtol = BF16_TOL
+    g = f64(gpu)
+    err = np.abs(g - ref)
+    worst = float(np.max(err / (atol + rtol * np.abs(ref)))) if err.size else 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite outputs"
+    assert worst <= 1.0, f"{what}: worst err/tol {worst:.3f}"
+
+
+def problem(T, H, F, E, k, seed, device="cuda"):
+    return wl.make_bf16_problem(T, H, F, E, k, seed, device)
+
+
+def oracle(p):
+    return orc.moe_experts_reference_batched(f64(p["hidden"]), f64(p["gate_up"]), f64(p["down"]),
+                                             p["top_k_index"].cpu().numpy(),
+                                             f64(p["top_k_weights"]))
+
+
+def run(entry, p, residual=None, workspace=None, out=None):
+    fn = getattr(_moe(), entry)
+    return fn(p["hidden"], p["gate_up"], p["down"], p["top_k_index"], p["top_k_weights"],
+              p["top_k_index"].shape[1], residual=residual, workspace=workspace, out=out)
+
+
+def same_bits(a, b, what):
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{what}: bits differ"
+
+
+# (T, H, F, E, k): one or a few M tiles per expert; experts with more than
+# 256 rows (several M tiles); H % 256 != 0 (128-wide down panels); more
+# experts than rows; a ragged tail everywhere
+SHAPES = [(16, 128, 128, 8, 2), (300, 256, 384, 12, 3), (200, 384, 256, 8, 2),
+          (1500, 256, 256, 4, 3), (90, 512, 128, 64, 6), (777, 640, 384, 16, 4)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_layer_matches_oracle_and_stage_form(shape):
+    T, H, F, E, k = shape
+    _say(f"one-launch layer {shape}")
+    p = problem(T, H, F, E, k, seed=100 + T)
+    got = run("moe_experts_prefill_fused", p)
+    same_bits(got, run("moe_experts_prefill", p), str(shape))
+    check_tol(got, oracle(p), str(shape))
+
+
+@pytest.mark.parametrize("cap", [8, 16, 40])
+def test_layer_small_grids(cap):
+    """Few workgroups: each runs many gate_up and down items, and down items
+    wait for gate_up items held by other workgroups."""
+    moe = _moe()
+    _say(f"one-launch layer, grid cap {cap}")
+    p = problem(1200, 256, 384, 10, 3, seed=7)
+    ref = run("moe_experts_prefill", p)
+    moe.moe_set_grid_cap(cap)
+    try:
+        got = run("moe_experts_prefill_fused", p)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_set_grid_cap(0)
+    same_bits(got, ref, f"cap {cap}")
+
+
+def test_layer_repeated_calls_and_stale_workspace():
+    """Consecutive calls on one workspace (each stamps its own flags), the
+    first one on a workspace full of stale bytes, inputs changing between
+    calls."""
+    moe = _moe()
+    _say("one-launch layer, repeated calls")
+    T, H, F, E, k = 400, 256, 256, 8, 2
+    n = moe.moe_workspace_size(moe.MOE_VARIANT_PREFILL, T, H, F, E, k)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    for i in range(5):
+        p = problem(T, H, F, E, k, seed=300 + i)
+        got = run("moe_experts_prefill_fused", p, workspace=ws)
+        same_bits(got, run("moe_experts_prefill", p), f"call {i}")
+
+
+def test_layer_residual_dropped_slots_and_poisoned_out():
+    _say("one-launch layer, residual and dropped slots")
+    T, H, F, E, k = 257, 256, 128, 8, 3
+    p = problem(T, H, F, E, k, seed=11)
+    idx = p["top_k_index"].clone()
+    idx[::5, 0] = -1        # dropped
+    idx[::7, 1] = E + 3     # out of range: dropped
+    p["top_k_index"] = idx
+    res = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    poison = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = run("moe_experts_prefill_fused", p, residual=res, out=poison)
+    same_bits(got, run("moe_experts_prefill", p, residual=res), "residual")
+    check_tol(got, oracle(p) + f64(res), "residual")
+
+
+def test_layer_full_ocr2_prefill():
+    """T=2048, H=1280, F=896, 64 experts, top-6: equal to the stage-by-stage
+    form (checked on every element against the oracle elsewhere), and a few
+    rows against the oracle directly."""
+    _say("one-launch layer, full ocr2_prefill")
+    p = wl.make_config("ocr2_prefill", device="cuda")
+    got = run("moe_experts_prefill_fused", p)
+    same_bits(got, run("moe_experts_prefill", p), "ocr2_prefill")
+    rows = [0, 1, 777, 2047]
+    sub = {n: (v[rows] if n in ("hidden", "top_k_index", "top_k_weights") else v)
+           for n, v in p.items()}
+    check_tol(got[rows], oracle(sub), "ocr2_prefill rows")
+
+
+def test_layer_other_shapes_take_the_stage_form():
+    """H not a multiple of 128: the entry point runs the stage-by-stage form."""
+    moe = _moe()
+    _say("one-launch layer, fallback shape")
+    p = problem(64, 192, 128, 4, 2, seed=5)
+    moe.moe_profile_begin(1)
+    got = run("moe_experts_prefill_fused", p)
+    torch.cuda.synchronize()
+    calls = moe.moe_profile_end(1)
+    assert [s for s, _ in calls[0]] == ["plan", "gate_up", "down", "combine"]
+    same_bits(got, run("moe_experts_prefill", p), "fallback")
+
+
+def test_layer_stage_recorder_and_empty_call():
+    moe = _moe()
+    p = problem(64, 256, 128, 4, 2, seed=6)
+    moe.moe_profile_begin(1)
+    run("moe_experts_prefill_fused", p)
+    torch.cuda.synchronize()
+    calls = moe.moe_profile_end(1)
+    assert [s for s, _ in calls[0]] == ["plan", "layer"]
+    empty = {n: v[:0] if n in ("hidden", "top_k_index", "top_k_weights") else v
+             for n, v in p.items()}
+    assert run("moe_experts_prefill_fused", empty).shape == (0, 256)

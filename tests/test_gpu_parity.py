@@ -201,13 +201,15 @@ def test_decode_full_config(name):
         _say(f"  {entry}: worst err/tol {worst:.3f} rel L2 {rel:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(3, 128, 64, 8, 2), (4, 256, 1536, 6, 5), (2, 512, 2048, 3, 3),
+@pytest.mark.parametrize("shape", [(3, 128, 64, 8, 2), (4, 256, 1536, 6, 5), (4, 256, 1536, 8, 8),
+                                   (4, 256, 2048, 8, 7), (2, 512, 2048, 3, 3),
                                    (4, 128, 128, 40, 8), (1, 1024, 96 * 2, 8, 4),
                                    (2, 1536, 64, 5, 2), (3, 2048, 128, 8, 3), (4, 1536, 64, 8, 2),
                                    (4, 2048, 64, 8, 2), (7, 128, 64, 8, 2)])
 def test_decode_shapes(shape):
     """Fast path for T <= 4 (1 to 4 16-byte chunks per lane of an H row, 1 to 4
-    tokens), grouped path above it (T = 7, and T = 4 with H = 2048)."""
+    tokens, h up to its LDS limit T*k*F = 49152 and 32 slots), grouped path
+    above it (T = 7, T = 4 with H = 2048, and T*k*F = 57344)."""
     T, H, F, E, k = shape
     _say(f"decode shape {shape}")
     p = bf16_problem(T, H, F, E, k, seed=T + F, std=1 / np.sqrt(H))
