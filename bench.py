@@ -472,15 +472,25 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "launches": len(calls[0]) if calls else 0}
+        fused_entry = None
         if kind == "bf16" and not decode and not S:
-            # pass E: the same steps through the one-launch form
-            # (moe_experts_prefill_fused: plan, then gate_up, down and the
-            # combine in one persistent launch)
+            fused_entry = "moe_experts_prefill_fused"
+
             def step_fused(i):
                 s_ = i % sets
                 idx, w = routes[i % len(routes)]
                 return moe.moe_experts_prefill_fused(hidden, gu_sets[s_], dn_sets[s_], idx, w, k,
                                                      out=out_buf)
+        elif kind == "fp8" and T * k > 32 * E:
+            fused_entry = "moe_experts_fp8_fused"
+
+            def step_fused(i):
+                return moe.moe_experts_fp8_fused(p["x"], p["x_scale"], p["gate_up"], p["gate_up_scale"],
+                                                 p["down"], p["down_scale"], p["top_k_index"],
+                                                 p["top_k_weights"], k, out=out_buf)
+        if fused_entry:
+            # pass E: the same steps through the one-launch form (the plan,
+            # then gate_up, down and the combine in one persistent launch)
             for i in range(warmup):
                 step_fused(i)
             torch.cuda.synchronize()
@@ -501,7 +511,7 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 for st, ms in row:
                     per[st].append(ms)
             out["fused_layer"] = {
-                "entry": "moe_experts_prefill_fused (plan, then one persistent launch)",
+                "entry": f"{fused_entry} (plan, then one persistent launch)",
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "stage_us": {st: round(float(np.mean(v)) * 1e3, 2) for st, v in per.items()}}

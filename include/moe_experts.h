@@ -280,6 +280,22 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale,
                     uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_experts_fp8 with the two grouped products and the combine in one
+ * persistent launch after the routing plan, as moe_experts_prefill_fused
+ * does for bf16 (same operands, workspace moe_workspace_size(MOE_VARIANT_FP8,
+ * ...), errors and results: out is bit-for-bit that of moe_experts_fp8; the
+ * same residency requirement, 2 s wait limit and generation word).  Used
+ * for prefill shapes (more than 32 slots per expert on average) with H and F
+ * multiples of 512; other calls run the moe_experts_fp8 sequence.
+ */
+int moe_experts_fp8_fused(const uint8_t* x, const float* x_scale,
+                          const uint8_t* gate_up, const float* gate_up_scale,
+                          const uint8_t* down, const float* down_scale,
+                          const int32_t* top_k_index, const float* top_k_weights,
+                          const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                          uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * The FP8 layer with S fused shared experts (DeepGEMM issue "GC MoE":
  * routed experts with optional fused shared experts, FP8 shared weights;
  * mirage issue "Supporting MegaKernel for DeepSeek Models": the shared

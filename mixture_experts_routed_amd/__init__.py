@@ -61,6 +61,8 @@ def _load():
         "moe_workspace_size_shared": ([i32, i64, i32, i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
         "moe_experts_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp],
                             i32),
+        "moe_experts_fp8_fused": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp,
+                                   sz, vp], i32),
         "moe_experts_fp8_bf16in": ([vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz,
                                     vp], i32),
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
@@ -98,7 +100,7 @@ def exported_symbols():
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
             "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc",
             "moe_probe_stream_read", "moe_quantize_fp8_block128_ue8m0", "moe_experts_fp8_shared",
-            "moe_experts_mxfp4_shared", "moe_experts_prefill_fused"]
+            "moe_experts_mxfp4_shared", "moe_experts_prefill_fused", "moe_experts_fp8_fused"]
 
 
 class MoeError(RuntimeError):
@@ -463,6 +465,20 @@ def moe_experts_fp8(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_
                      down, down_scale, top_k_index, top_k_weights, top_k, residual, workspace, out)
 
 
+def moe_experts_fp8_fused(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                          top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """moe_experts_fp8 with the products and the combine in one persistent
+    launch after the plan (same operands, workspace and result)."""
+    x = _codes(x)
+    _need(x, "x", torch.uint8, 2)
+    _need(x_scale, "x_scale", torch.float32, 2, x.device)
+    if tuple(x_scale.shape) != (x.shape[0], x.shape[1] // 128):
+        raise ValueError("x_scale must be [T, H/128]")
+    return _fp8_call("moe_experts_fp8_fused", MOE_VARIANT_FP8, [x, x_scale], gate_up,
+                     gate_up_scale, down, down_scale, top_k_index, top_k_weights, top_k, residual,
+                     workspace, out)
+
+
 def moe_experts_fp8_bf16in(hidden_states, gate_up, gate_up_scale, down, down_scale, top_k_index,
                            top_k_weights, top_k, residual=None, workspace=None, out=None):
     """The FP8 layer fed with bf16 hidden states [T, H], quantised per
@@ -748,7 +764,7 @@ __all__ = [
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_workspace_layout",
     "moe_profile_begin", "moe_profile_end",
     "moe_routing_plan", "moe_experts_prefill", "moe_experts_prefill_fused", "moe_experts_decode",
-    "moe_experts_fp8", "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128",
+    "moe_experts_fp8", "moe_experts_fp8_fused", "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128",
     "moe_quantize_fp8_block128_ue8m0",
     "moe_experts_fp8_shared", "moe_experts_mxfp4_shared", "moe_experts_prefill_shared",
     "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",

@@ -152,7 +152,8 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
         L.h = take((size_t)P * F * 2);
     }
     L.y = take((size_t)P * H * 2);
-    if (variant == MOE_VARIANT_PREFILL)   // hand-off words of moe_experts_prefill_fused
+    if (variant == MOE_VARIANT_PREFILL || variant == MOE_VARIANT_FP8 ||
+        variant == MOE_VARIANT_FP8_BF16IN)   // hand-off words of the one-launch forms
         L.sync = take(layer_sync_bytes(P, E, F));
     if (variant == MOE_VARIANT_FP8_BF16IN) {  // the quantised hidden states
         L.xq = take((size_t)T * H);
@@ -318,7 +319,8 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
             const uint8_t* gate_up, const float* gate_up_scale, const uint8_t* down,
             const float* down_scale, const SharedQ& sh, const int32_t* top_k_index,
             const float* top_k_weights, const uint16_t* residual, int64_t T, int H, int F, int E,
-            int k, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+            int k, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream,
+            bool fused = false) {
     if (!gate_up || !gate_up_scale || !down || !down_scale || !top_k_index || !top_k_weights ||
         !out)
         return MOE_ERR_NULL;
@@ -360,6 +362,12 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
                               at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                               at<int32_t>(ws, L.tile_off), fp8_tile_m(narrow), stream));
     if (rc) return rc;
+    if (fused && layer_fp8_fits(P, E, H, F)) {
+        clock.mark(MOE_STAGE_LAYER);
+        return launched(launch_layer_fp8(x, x_scale, w13, w13s, w2, w2s, pl, at<int32_t>(ws, L.inv),
+                                         w, residual, T, H, F, k, hq, hs, y, out,
+                                         at<void>(ws, L.sync), stream));
+    }
     clock.mark(MOE_STAGE_GATE_UP);
     rc = launched(launch_gateup_fp8(x, x_scale, w13, w13s, pl, narrow, H, F, k, hq, hs, stream));
     if (rc) return rc;
@@ -695,6 +703,18 @@ int moe_experts_fp8(const uint8_t* x, const float* x_scale, const uint8_t* gate_
     return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
                    SharedQ{}, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
                    ws_bytes, stream);
+}
+
+int moe_experts_fp8_fused(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,
+                          const float* gate_up_scale, const uint8_t* down, const float* down_scale,
+                          const int32_t* top_k_index, const float* top_k_weights,
+                          const uint16_t* residual, int64_t T, int H, int F, int E, int k,
+                          uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !x_scale) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(x_scale)) return MOE_ERR_ALIGN;
+    return run_fp8(MOE_VARIANT_FP8, nullptr, x, x_scale, gate_up, gate_up_scale, down, down_scale,
+                   SharedQ{}, top_k_index, top_k_weights, residual, T, H, F, E, k, out, ws,
+                   ws_bytes, stream, true);
 }
 
 int moe_experts_fp8_shared(const uint8_t* x, const float* x_scale, const uint8_t* gate_up,

@@ -13,6 +13,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_layer.h"
 
 namespace moe {
 
@@ -199,7 +200,7 @@ __device__ __forceinline__ void grouped_loop(
                         const int row = 32 * (MB * wm + mb) + acc_row(q, lane) + (odd ? 1 : 0);
                         if (row < m.mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, h1) : pack_bf16x2_hw(h0, got);
-                            sc.store(C + (int64_t)(m.row0 + row) * n_out + (f & ~1), v);
+                            sc.store_u32(C + (int64_t)(m.row0 + row) * n_out + (f & ~1), v);
                         }
                     }
                 }
@@ -216,7 +217,7 @@ __device__ __forceinline__ void grouped_loop(
                         const int col = m.nt * BN + (wn * NB + nb) * 32 + (lane & 30);
                         if (row < m.mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
-                            sc.store(C + (int64_t)(m.row0 + row) * n_out + col, v);
+                            sc.store_u32(C + (int64_t)(m.row0 + row) * n_out + col, v);
                         }
                     }
                 }
@@ -269,24 +270,6 @@ __device__ __forceinline__ void grouped_loop(
     sc.drained();
     __builtin_amdgcn_s_waitcnt(0);  // no LDS fill may outlive the workgroup
 }
-
-// Hooks of the stand-alone kernels: workgroup b takes item xcd_slot(b) and
-// then every G-th (consecutive items run on one XCD), stores are plain and
-// nothing is waited for (the kernel boundaries order the stages).
-struct PlainSched {
-    int items;
-    __device__ int first() const {
-        const int it = xcd_slot(blockIdx.x, gridDim.x);
-        return it < items ? it : -1;
-    }
-    __device__ int next(int it) const {
-        return it + (int)gridDim.x < items ? it + (int)gridDim.x : -1;
-    }
-    __device__ void wait_inputs(const GroupedItem&) const {}
-    __device__ void store(uint16_t* p, uint32_t v) const { *(uint32_t*)p = v; }
-    __device__ void stored(int) const {}
-    __device__ void drained() const {}
-};
 
 // One work item = (M tile of <= 256 rows of one expert) x (BN rows of the
 // expert's weight panel); the grid is persistent (see grouped_loop).
@@ -351,104 +334,6 @@ hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const Gr
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ combine
-// Unit g = (token t, 8 columns c): out = sum_j w[t,j] * y[inv[t*k+j]] in
-// slot order, plus the residual if any, in fp32, one rounding to bf16.  y is
-// in expert order; inv (from the plan) is -1 for dropped slots, which
-// contribute nothing.
-__device__ __forceinline__ void combine_unit(const uint16_t* __restrict__ y,
-                                             const int32_t* __restrict__ inv,
-                                             const float* __restrict__ w,
-                                             const uint16_t* __restrict__ residual, int64_t g,
-                                             int k, int H, bool nan_out,
-                                             uint16_t* __restrict__ out) {
-    const int cpr = H / 8;
-    const int64_t t = g / cpr;
-    const int c = (int)(g - t * cpr) * 8;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-        const int r = inv[t * k + j];
-        if (r < 0) continue;
-        const float wt = w[t * k + j];
-        const uint4 v = *(const uint4*)(y + (int64_t)r * H + c);
-        float f[8];
-        unpack8(v, f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wt * f[i];
-    }
-    if (residual) {
-        float r[8];
-        unpack8(*(const uint4*)(residual + t * H + c), r);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += r[i];
-    }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    if (nan_out) o = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-    *(uint4*)(out + t * H + c) = o;
-}
-
-// NU units per thread at once with every slot's loads in flight (k <= KM):
-// the same sums as combine_unit, for a grid with few waves per CU.
-template <int KM, int NU>
-__device__ __forceinline__ void combine_units(const uint16_t* __restrict__ y,
-                                              const int32_t* __restrict__ inv,
-                                              const float* __restrict__ w,
-                                              const uint16_t* __restrict__ residual, int64_t g0,
-                                              int64_t gstep, int64_t gend, int k, int H,
-                                              bool nan_out, uint16_t* __restrict__ out) {
-    const int cpr = H / 8;
-    int64_t t[NU];
-    int c[NU], r[NU][KM];
-    float wt[NU][KM];
-    uint4 v[NU][KM];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int64_t g = min(g0 + u * gstep, gend - 1);
-        t[u] = g / cpr;
-        c[u] = (int)(g - t[u] * cpr) * 8;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-            r[u][j] = j < k ? inv[t[u] * k + j] : -1;
-            wt[u][j] = j < k ? w[t[u] * k + j] : 0.0f;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int j = 0; j < KM; ++j)
-            v[u][j] = r[u][j] >= 0 ? *(const uint4*)(y + (int64_t)r[u][j] * H + c[u]) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        if (g0 + u * gstep >= gend) break;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-            if (r[u][j] < 0) continue;
-            float f[8];
-            unpack8(v[u][j], f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wt[u][j] * f[i];
-        }
-        if (residual) {
-            float rs[8];
-            unpack8(*(const uint4*)(residual + t[u] * H + c[u]), rs);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += rs[i];
-        }
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        if (nan_out) o = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-        *(uint4*)(out + t[u] * H + c[u]) = o;
-    }
-}
-
 // one thread per unit
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
@@ -470,125 +355,6 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
     return hipGetLastError();
 }
 
-// ------------------------------------------------------ one-launch layer
-// The grouped path in one persistent launch after the plan: gate_up items,
-// then down items, then the combine, handed over between workgroups through
-// flags in the workspace instead of kernel boundaries (the single-kernel
-// idea of the DeepGEMM "Mega MoE" news item, on one GPU).  Workgroup b walks
-// the sequence xcd_slot(b) + j G over [gate_up items | down items], so the
-// workgroups with one gate_up item fewer start the down items first, and a
-// workgroup only ever waits for items earlier in the sequence, held by
-// resident workgroups: the waits end.
-//  - a gate_up item stores its h tile with device-scope stores; once they
-//    have completed in every wave (right after the epilogue) it stores its
-//    flag (the call's stamp);
-//  - a down item first waits for the flags of its M tile's gate_up items,
-//    then reads h rows as usual: no copy of them is in any L2 yet, so the
-//    reads fetch the stored values;
-//  - a workgroup past its down items stores its down flag; the combine
-//    waits for every workgroup's down flag, then sums its share of tokens
-//    exactly as combine_kernel does.
-// The stamp is the generation word + 1; workgroup 0 advances the word at
-// the end, once every workgroup has acknowledged reading it, so flags of
-// earlier calls never match.  Waits are bounded by a clock limit: a grid that
-// is not resident together gives NaN outputs and sets the error word.
-// Hand-off words (64-bit) in the workspace, from one base pointer:
-struct LayerSync {
-    uint64_t* base;
-    __device__ uint64_t* gen() const { return base; }        // generation word
-    __device__ uint64_t* err() const { return base + 1; }    // = stamp when a wait timed out
-    __device__ uint64_t* ack() const { return base + 32; }   // [G] workgroup read the generation
-    __device__ uint64_t* dflag() const { return base + 32 + kLayerMaxGrid; }   // [G] down items done
-    __device__ uint64_t* gflag() const { return base + 32 + 2 * kLayerMaxGrid; }  // [gate_up items]
-};
-
-// wave 0 waits until flags[i * stride], i < n, all equal stamp (each wait
-// bounded by kLayerSpinTicks of the 100 MHz clock; past it the error word
-// takes the stamp); then the whole workgroup passes a barrier
-__device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int stride,
-                                           uint64_t stamp, LayerSync sy) {
-    if (threadIdx.x < 64) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (true) {
-            bool all = true;
-            for (int i = threadIdx.x; i < n; i += 64) all &= ld_dev_u64(flags + (int64_t)i * stride) == stamp;
-            if (__all(all)) break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kLayerSpinTicks) {
-                if (threadIdx.x == 0) st_dev_u64(sy.err(), stamp);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    lds_barrier();
-}
-
-// gate_up phase (GATE) or down phase of the one-launch layer.
-// Slot s = xcd_slot(b) takes gate_up items s, s + G, ... (q + 1 of them for
-// s < r, q for s >= r, with NG = q G + r), then its down items.  Down items
-// are numbered like gate_up items (expert by expert), and the k-th down item
-// of slot s is the item whose number is:
-//  - for s >= r and k < c ("early" items, started while the last round of
-//    gate_up items still runs): k (G - r) + (s - r), so these come from the
-//    first experts, whose gate_up items finished in the earlier rounds;
-//  - otherwise c (G - r) + the rank of the slot's sequence position
-//    s + (nG(s) + k) G among the positions not taken by early items.
-// c = how many down items fit in one gate_up item's time, bounded so that
-// the early items stay within the tiles of finished rounds.  Any order is
-// deadlock-free: down items wait only for gate_up items, and every
-// workgroup runs all its gate_up items first.
-template <bool GATE>
-struct LayerSched {
-    int items, NG, npg, c;   // npg: gate_up items per M tile
-    uint64_t stamp;
-    LayerSync sy;
-    const int32_t* tile_off;
-    int k;
-    __device__ int down_item(int kk) const {
-        const int G = gridDim.x, s = xcd_slot(blockIdx.x, G);
-        const int q = NG / G, r = NG % G, nf = G - r;
-        if (c > 0 && s >= r && kk < c) return kk * nf + (s - r);
-        const int j = (s < r ? q + 1 : q) + kk;            // the position's round
-        const int jr = q + 1, jf = q + (c > 0 ? c : 0);    // first rounds not early
-        int64_t rank = (int64_t)r * max(0, j - jr) + (int64_t)nf * max(0, j - jf);
-        if (j >= jr) rank += min(s, r);
-        if (j >= jf) rank += max(0, s - r);
-        const int64_t it = (int64_t)c * nf + rank;
-        return it < items ? (int)it : -1;
-    }
-    __device__ int first() {
-        const int G = gridDim.x, seq0 = xcd_slot(blockIdx.x, G);
-        if (GATE) return seq0 < items ? seq0 : -1;
-        k = 0;
-        return down_item(0);
-    }
-    __device__ int next(int it) {
-        if (GATE) return it + (int)gridDim.x < items ? it + (int)gridDim.x : -1;
-        return down_item(++k);
-    }
-    __device__ void wait_inputs(const GroupedItem& gi) const {
-        if (GATE) return;
-        const int t0e = tile_off[gi.e], mtiles = tile_off[gi.e + 1] - t0e;
-        // gate_up items of M tile gi.mt: npg * t0e + panel * mtiles + (mt - t0e)
-        wait_flags(sy.gflag() + (int64_t)npg * t0e + (gi.mt - t0e), npg, mtiles, stamp, sy);
-    }
-    __device__ void store(uint16_t* p, uint32_t v) const { st_dev_u32((uint32_t*)p, v); }
-    // a gate_up item's flag, once its stores have completed in every wave
-    // (the next item's first loads, issued before them, have landed too)
-    __device__ void stored(int it) const {
-        if (!GATE) return;
-        wait_vm_all();
-        lds_barrier();
-        if (threadIdx.x == 0) st_dev_u64(sy.gflag() + it, stamp);
-    }
-    __device__ void drained() const {
-        if (GATE) return;
-        wait_vm_all();
-        lds_barrier();
-        if (threadIdx.x == 0) st_dev_u64(sy.dflag() + blockIdx.x, stamp);
-    }
-};
-
 template <int BNG, int BND>
 __global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
     const uint16_t* __restrict__ x, const ExpertWeights w13, const ExpertWeights w2,
@@ -600,61 +366,19 @@ __global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
     LayerSync sy) {
     constexpr int BNMAX = BNG > BND ? BNG : BND;
     __shared__ u32x4 lds[kAStages * kBM * 8 + kBStages * BNMAX * 8];
-    const int b = blockIdx.x, G = gridDim.x;
-    // this call's stamp, known to wave 0 (kept in scalar registers)
-    uint64_t stamp = 0;
-    if (threadIdx.x < 64) {
-        stamp = ld_dev_u64(sy.gen()) + 1;
-        if (threadIdx.x == 0) st_dev_u64(sy.ack() + b, stamp);
-    }
-    stamp = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(stamp >> 32)) << 32) |
-            __builtin_amdgcn_readfirstlane((uint32_t)stamp);
+    const uint64_t stamp = layer_stamp(sy);
     const int ntiles = *ntiles_p;
     const int npg = F / (BNG / 2), npd = H / BND;
     const int NG = ntiles * npg;
 
-    LayerSched<true> sg{NG, NG, npg, 0, stamp, sy, tile_off, 0};
+    LayerSched<true> sg{NG, NG, npg, 0, stamp, sy, tile_off, 0, nullptr, 0};
     grouped_loop<BNG, true>(lds, x, w13, perm, tiles, tile_off, offsets, E, H, F, 2 * F, k, h, sg);
-    // early down items per slot with one gate_up item fewer: a gate_up item's
-    // time in down items (H x BNG against F x BND products), within the
-    // down items of the tiles finished in the earlier rounds
-    const int ND = ntiles * npd, q = NG / G, nf = G - NG % G;
-    int c = 0;
-    if (NG % G != 0) {
-        c = (H * BNG + F * BND - 1) / (F * BND);
-        c = min(c, min(ND, q * G / npg * npd) / nf);
-    }
-    LayerSched<false> sd{ND, NG, npg, c, stamp, sy, tile_off, 0};
+    const int ND = ntiles * npd;
+    const int c = layer_early_down(NG, ND, npg, npd, (int64_t)H * BNG, (int64_t)F * BND);
+    LayerSched<false> sd{ND, NG, npg, c, stamp, sy, tile_off, 0, nullptr, 0};
     grouped_loop<BND, false>(lds, h, w2, perm, tiles, tile_off, offsets, E, F, H, H, 1, y, sd);
 
-    // combine: every workgroup's down items are stored (and the operand
-    // ring is idle: its first word carries the error state to all waves)
-    wait_flags(sy.dflag(), G, 1, stamp, sy);
-    int* failed = (int*)lds;
-    if (threadIdx.x == 0) *failed = ld_dev_u64(sy.err()) == stamp;
-    if (b == 0 && threadIdx.x < 64) {
-        // every workgroup has read the generation word (each stored its
-        // acknowledgement at its start): advance it
-        bool all;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        do {
-            all = true;
-            for (int i = threadIdx.x; i < G; i += 64) all &= ld_dev_u64(sy.ack() + i) == stamp;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kLayerSpinTicks) break;
-        } while (!__all(all));
-        if (threadIdx.x == 0) st_dev_u64(sy.gen(), stamp);
-    }
-    lds_barrier();
-    const bool bad = *failed;
-    const int64_t U = T * (H / 8), u0 = U * b / G, u1 = U * (b + 1) / G;
-    if (k <= 8) {
-        // two units per thread at a time, all their slot loads in flight
-        for (int64_t g = u0 + threadIdx.x; g < u1; g += 2 * kGemmThreads)
-            combine_units<8, 2>(y, inv, wts, residual, g, kGemmThreads, u1, k, H, bad, out);
-    } else {
-        for (int64_t g = u0 + threadIdx.x; g < u1; g += kGemmThreads)
-            combine_unit(y, inv, wts, residual, g, k, H, bad, out);
-    }
+    layer_combine((int*)lds, y, inv, wts, residual, T, k, H, out, stamp, sy);
 }
 
 // A whole number of 128-column h blocks and down panels (other shapes take

@@ -8,8 +8,11 @@
 // weight [E,H,F] + scale [E,H,F/128]) and bf16_to_fp8_quantize (block 128).
 // A 128-wide K block is one MFMA group: two 32x32x64 products into a fresh
 // fp32 temporary, then acc += tmp * scale_a[row] * scale_b[col].
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_layer.h"
 
 namespace moe {
 
@@ -63,14 +66,44 @@ __device__ __forceinline__ float quant_block_half(const float v[4], float amax_l
 // A scale read touches one cache line per row, against one line per eight
 // lanes for the operand bytes, so one 4-byte read per step doubled the
 // cache-line requests of a stage; SQ cuts that to a quarter.
-template <int WM, int BN, bool SWIGLU, bool SQ>
-__global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ As, const ExpertArray<uint8_t> B,
-    const ExpertArray<float> Bs, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
-    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, float* __restrict__ Cs,
-    uint16_t* __restrict__ Cy) {
+// The LDS arrays of one tile shape: separate variables (each with its own
+// base, so fragment reads keep constant offsets), the same ones for the
+// gate_up and the down loop of a one-launch layer, which run one after the
+// other.  SR: scale ring slots.
+template <int WM, int BN, bool SQ>
+struct Fp8Ring {
+    static constexpr int BM = 32 * WM, SR = SQ ? 8 : 2;
+    __device__ static u32x4 (&a())[2][BM][8] {
+        __shared__ u32x4 v[2][BM][8];
+        return v;
+    }
+    __device__ static u32x4 (&b())[2][BN][8] {
+        __shared__ u32x4 v[2][BN][8];
+        return v;
+    }
+    __device__ static float (&sa())[SR][BM] {
+        __shared__ __attribute__((aligned(16))) float v[SR][BM];
+        return v;
+    }
+    __device__ static float (&sb())[SR][BN] {
+        __shared__ float v[SR][BN];
+        return v;
+    }
+    // per-row partial maxima of the SwiGLU epilogue
+    __device__ static float (&amax())[8 / WM][BM] {
+        __shared__ float v[8 / WM][BM];
+        return v;
+    }
+};
+
+// The persistent item loop, with the scheduling hooks of moe_layer.h.
+template <int WM, int BN, bool SWIGLU, bool SQ, class Sched>
+__device__ __forceinline__ void fp8_loop(
+    const uint8_t* __restrict__ A, const float* __restrict__ As,
+    const ExpertArray<uint8_t>& B, const ExpertArray<float>& Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
+    uint8_t* __restrict__ Cq, float* __restrict__ Cs, uint16_t* __restrict__ Cy, Sched& sc) {
     constexpr int WN = 8 / WM;
     constexpr int BM = 32 * WM;
     constexpr int NBW = BN / (32 * WN);
@@ -87,12 +120,11 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     static_assert(BM <= kFp8Threads && BN <= kFp8Threads, "one scale per thread");
     static_assert(!SWIGLU || (NBW % 2 == 0 && 4 % PP == 0 && WN % WB == 0),
                   "the SwiGLU epilogue needs whole gate/up pairs and whole 128-wide h blocks");
-    __shared__ u32x4 a_lds[2][BM][8];
-    __shared__ u32x4 b_lds[2][BN][8];
-    constexpr int SR = SQ ? 8 : 2;  // scale ring slots
-    __shared__ __attribute__((aligned(16))) float sa_lds[SR][BM];
-    __shared__ float sb_lds[SR][BN];
-    __shared__ float amax_lds[SWIGLU ? WN : 1][SWIGLU ? BM : 1];
+    using Ring = Fp8Ring<WM, BN, SQ>;
+    auto& a_lds = Ring::a();
+    auto& b_lds = Ring::b();
+    auto& sa_lds = Ring::sa();
+    auto& sb_lds = Ring::sb();
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
@@ -100,9 +132,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
     const int a_row_t = row_t & (BM - 1);   // BM = 32: rows 32..63 repeat rows 0..31
     const int g = lane >> 5;
     const int fsw = (lane >> 1) & 7;  // lds_chunk swizzle of fragment rows 32*b + lane%32
-    const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
-    const int items = ntiles * n_tiles_n;
     const int nkb = K / kFp8BK;
 
     auto panel_row = [&](int rr, int nt) {
@@ -113,24 +143,26 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         return nt * BN + rr;
     };
 
-    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+    for (int it = sc.first(); it >= 0; it = sc.next(it)) {
         const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        sc.wait_inputs(gi);
         const int nt = gi.nt, mt = gi.mt, e = gi.e;
         const int row0 = tiles[2 * mt + 1];
         const int mrows = min(BM, offsets[e + 1] - row0);
         const bool active = 32 * wm < mrows;
 
-        // A rows (and A scale rows) past the tile's end read row 0
+        // A rows (and A scale rows) past the tile's end read token row 0 or
+        // the tile's first row
         const uint8_t* a_src[A_PER];
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int r = a_row_t + 64 * i;
-            int64_t arow = 0;
+            int64_t arow = SWIGLU ? 0 : row0;
             if (r < mrows) arow = SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
             a_src[i] = A + arow * K + chunk * 16;
         }
         const bool sa_ok = tid < BM, sb_ok = tid < BN;
-        int64_t sarow = 0;
+        int64_t sarow = SWIGLU ? 0 : row0;
         if (sa_ok && tid < mrows)
             sarow = SWIGLU ? (int64_t)(perm[row0 + tid] / topk) : (int64_t)(row0 + tid);
         const float* as_src = As + sarow * nkb;
@@ -214,10 +246,10 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         }                                                                                      \
         MOE_FP8_LOAD(RA, RB, min((KB) + 2, nkb - 1));                                          \
         if constexpr (!SQ) {                                                                   \
-            RSA = as_src[min((KB) + 2, nkb - 1)];                                              \
+            RSA = sc.load_scale(as_src + min((KB) + 2, nkb - 1));                              \
             RSB = bs_src[min((KB) + 2, nkb - 1)];                                              \
         } else if constexpr (J == 0) {                                                         \
-            qa = *(const float4*)(as_src + min((KB) + 4, nkb - 4));                            \
+            qa = sc.load_scale4(as_src + min((KB) + 4, nkb - 4));                              \
             qb = *(const float4*)(bs_src + min((KB) + 4, nkb - 4));                            \
         }                                                                                      \
     } while (0)
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
         // prologue loads in the loop's own issue order, so that the waits the
         // compiler derives at the loop head hold the look-ahead loads in flight
         if constexpr (SQ) {
-            qa = *(const float4*)as_src;
+            qa = sc.load_scale4(as_src);
             qb = *(const float4*)bs_src;
             MOE_FP8_LOAD(ra0, rb0, 0);
             MOE_FP8_LOAD(ra1, rb1, min(1, nkb - 1));
@@ -237,10 +269,10 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
             }
         } else {
             MOE_FP8_LOAD(ra0, rb0, 0);
-            rsa0 = as_src[0];
+            rsa0 = sc.load_scale(as_src);
             rsb0 = bs_src[0];
             MOE_FP8_LOAD(ra1, rb1, min(1, nkb - 1));
-            rsa1 = as_src[min(1, nkb - 1)];
+            rsa1 = sc.load_scale(as_src + min(1, nkb - 1));
             rsb1 = bs_src[min(1, nkb - 1)];
             for (int kb = 0; kb < nkb; kb += 2) {
                 MOE_FP8_STEP(0, 0, ra0, rb0, rsa0, rsb0, kb);
@@ -263,7 +295,7 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                     m = fmaxf(m, fabsf(hv[p][q]));
                 }
                 m = half_max32(m);
-                if ((lane & 31) == 0) amax_lds[wn][32 * wm + acc_row(q, lane)] = m;
+                if ((lane & 31) == 0) Ring::amax()[wn][32 * wm + acc_row(q, lane)] = m;
             }
             lds_barrier();
             if (active) {
@@ -273,9 +305,9 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     const int row = 32 * wm + acc_row(q, lane);
-                    float amax = amax_lds[wb0][row];
+                    float amax = Ring::amax()[wb0][row];
 #pragma unroll
-                    for (int j = 1; j < WB; ++j) amax = fmaxf(amax, amax_lds[wb0 + j][row]);
+                    for (int j = 1; j < WB; ++j) amax = fmaxf(amax, Ring::amax()[wb0 + j][row]);
                     float vv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int p = 0; p < PP; ++p) vv[p] = hv[p][q];
@@ -284,8 +316,8 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
                     if (row < mrows) {
                         uint8_t* dst = Cq + (int64_t)(row0 + row) * n_out + nt * (BN / 2) + wn * PP * 32 + (lane & 31);
 #pragma unroll
-                        for (int p = 0; p < PP; ++p) dst[32 * p] = (uint8_t)(codes >> (8 * p));
-                        if (wn % WB == 0 && (lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + hblk] = scale;
+                        for (int p = 0; p < PP; ++p) sc.store_u8(dst + 32 * p, (uint8_t)(codes >> (8 * p)));
+                        if (wn % WB == 0 && (lane & 31) == 0) sc.store_f32(Cs + (int64_t)(row0 + row) * nfb + hblk, scale);
                     }
                 }
             }
@@ -297,13 +329,28 @@ __global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
                         const int col = nt * BN + (wn * NBW + nb) * 32 + (lane & 31);
-                        Cy[(int64_t)(row0 + row) * n_out + col] = (uint16_t)f32_to_bf16(acc[nb][q]);
+                        sc.store_u16(Cy + (int64_t)(row0 + row) * n_out + col, (uint16_t)f32_to_bf16(acc[nb][q]));
                     }
                 }
             }
         }
         lds_barrier();  // LDS (operand rings, amax) is reused by the next item
+        sc.stored(it);
     }
+    sc.drained();
+}
+
+template <int WM, int BN, bool SWIGLU, bool SQ>
+__global__ __launch_bounds__(kFp8Threads) void gemm_fp8_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const ExpertArray<uint8_t> B,
+    const ExpertArray<float> Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, float* __restrict__ Cs,
+    uint16_t* __restrict__ Cy) {
+    PlainSched sc{*ntiles_p * (SWIGLU ? n_out / (BN / 2) : n_out / BN)};
+    fp8_loop<WM, BN, SWIGLU, SQ>(A, As, B, Bs, perm, tiles, tile_off, offsets, E, K, n_out, b_rows,
+                                 topk, Cq, Cs, Cy, sc);
 }
 
 constexpr int kFp8WM = 4;  // 4 x 2 waves: 128-row M tiles
@@ -363,6 +410,57 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray
         launch_fp8<kFp8WM, 256, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
     else
         launch_fp8<kFp8WM, 128, false>(hq, hs, w2, w2s, pl, F, H, H, 1, nullptr, nullptr, y, s);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ one-launch layer
+// moe_experts_fp8's grouped path in one persistent launch after the plan
+// (the hand-offs of moe_layer.h): 128-row M tiles x 256-row panels for both
+// products, whose 16-byte scale rings share one set of LDS arrays.
+__global__ __launch_bounds__(kFp8Threads) void layer_fp8_kernel(
+    const uint8_t* __restrict__ x, const float* __restrict__ xs, const ExpertArray<uint8_t> w13,
+    const ExpertArray<float> w13s, const ExpertArray<uint8_t> w2, const ExpertArray<float> w2s,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ inv,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets,
+    const float* __restrict__ wts, const uint16_t* __restrict__ residual, int64_t T, int E, int H,
+    int F, int k, uint8_t* __restrict__ hq, float* __restrict__ hs, uint16_t* __restrict__ y,
+    uint16_t* __restrict__ out, LayerSync sy) {
+    __shared__ int claim;
+    const uint64_t stamp = layer_stamp(sy);
+    // this call's queue of down items
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u64(sy.queue(), (uint64_t)(uint32_t)stamp << 32);
+    const int ntiles = *ntiles_p;
+    const int npg = F / 128, npd = H / 256;
+    const int NG = ntiles * npg, ND = ntiles * npd;
+    LayerSched<true> sg{NG, NG, npg, 0, stamp, sy, tile_off, 0, nullptr, 0};
+    fp8_loop<kFp8WM, 256, true, true>(x, xs, w13, w13s, perm, tiles, tile_off, offsets, E, H, F,
+                                       2 * F, k, hq, hs, nullptr, sg);
+    // down items from the queue: many per workgroup, of uneven lengths
+    LayerSched<false, true> sd{ND, NG, npg, 0, stamp, sy, tile_off, 0, &claim, 0};
+    fp8_loop<kFp8WM, 256, false, true>(hq, hs, w2, w2s, perm, tiles, tile_off, offsets, E, F, H,
+                                        H, 1, nullptr, nullptr, y, sd);
+    // the scale ring is idle now: one of its words carries the error state
+    layer_combine((int*)&Fp8Ring<kFp8WM, 256, true>::sb()[0][0], y, inv, wts, residual, T, k, H,
+                  out, stamp, sy);
+}
+
+// Prefill shapes whose K blocks come four per scale load in both products.
+bool layer_fp8_fits(int64_t P, int E, int H, int F) {
+    return !fp8_use_narrow(P, E, H, F) && H % 512 == 0 && F % 512 == 0;
+}
+
+hipError_t launch_layer_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
+                            const ExpertArray<float>& w13s, const ExpertArray<uint8_t>& w2,
+                            const ExpertArray<float>& w2s, const GroupedPlan& pl,
+                            const int32_t* inv, const float* w, const uint16_t* residual,
+                            int64_t T, int H, int F, int k, uint8_t* hq, float* hs, uint16_t* y,
+                            uint16_t* out, void* sync, hipStream_t s) {
+    static const int g = std::min(
+        resident_grid((const void*)layer_fp8_kernel, kFp8Threads, device_cu_count()), kLayerMaxGrid);
+    MOE_LAUNCH(layer_fp8_kernel, dim3(capped_grid(g)), dim3(kFp8Threads), 0, s, x, xs, w13, w13s,
+               w2, w2s, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w, residual, T,
+               pl.E, H, F, k, hq, hs, y, out, LayerSync{(uint64_t*)sync});
     return hipGetLastError();
 }
 

@@ -169,6 +169,16 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
                                void* scales, bool ue8m0, hipStream_t s);
 
+// The fp8 products and the combine in one persistent launch after the plan
+// (as launch_layer_bf16), for prefill shapes with H and F multiples of 512.
+bool layer_fp8_fits(int64_t P, int E, int H, int F);
+hipError_t launch_layer_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
+                            const ExpertArray<float>& w13s, const ExpertArray<uint8_t>& w2,
+                            const ExpertArray<float>& w2s, const GroupedPlan& plan,
+                            const int32_t* inv, const float* w, const uint16_t* residual,
+                            int64_t T, int H, int F, int k, uint8_t* hq, float* hs, uint16_t* y,
+                            uint16_t* out, void* sync, hipStream_t s);
+
 // MXFP4 x MXFP8 products (E2M1 weights two per byte, E4M3 activations, E8M0
 // scales per 32 K elements): gate_up with SwiGLU + MXFP8 re-quantisation
 // (hq [P, F] E4M3, hs [P, F/32] E8M0, expert order), and down -> y bf16
