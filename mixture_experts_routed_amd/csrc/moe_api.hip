@@ -237,8 +237,15 @@ int run_grouped_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
     return launched(launch_combine(y, at<int32_t>(ws, L.inv), w, residual, T, k, H, out, s));
 }
 
-// The same layer as run_grouped_bf16 with gate_up, down and the combine in
-// one persistent launch after the plan (shapes that fit it; others take the
+// The plan arrays of a layout, for the one-launch forms that write them.
+LayerPlan layer_plan_in(const Layout& L, void* ws) {
+    return LayerPlan{at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                     at<int32_t>(ws, L.inv),    at<int32_t>(ws, L.tiles),   at<int32_t>(ws, L.ntiles),
+                     at<int32_t>(ws, L.tile_off)};
+}
+
+// The same layer as run_grouped_bf16 in one persistent launch: the routing
+// plan, gate_up, down and the combine (shapes that fit it; others take the
 // stage-by-stage sequence).
 int run_layer_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
                    const ExpertWeights& gate_up, const ExpertWeights& down, const int32_t* idx,
@@ -247,17 +254,9 @@ int run_layer_bf16(StageClock& clock, const Layout& L, const uint16_t* hidden,
     if (!layer_bf16_fits(H, F))
         return run_grouped_bf16(clock, L, hidden, gate_up, down, idx, w, residual, T, H, F, E, k,
                                 out, ws, s);
-    const int P = (int)(T * k);
-    const GroupedPlan pl = plan_in(L, ws, E);
-    clock.mark(MOE_STAGE_PLAN);
-    int rc = launched(launch_plan(idx, P, E, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
-                                  at<int32_t>(ws, L.perm), at<int32_t>(ws, L.inv),
-                                  at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
-                                  at<int32_t>(ws, L.tile_off), bf16_tile_m(), s));
-    if (rc) return rc;
     clock.mark(MOE_STAGE_LAYER);
-    return launched(launch_layer_bf16(hidden, gate_up, down, pl, at<int32_t>(ws, L.inv), w,
-                                      residual, T, H, F, k, at<uint16_t>(ws, L.h),
+    return launched(launch_layer_bf16(hidden, gate_up, down, idx, layer_plan_in(L, ws), w,
+                                      residual, T, H, F, E, k, at<uint16_t>(ws, L.h),
                                       at<uint16_t>(ws, L.y), out, at<void>(ws, L.sync), s));
 }
 
@@ -354,6 +353,12 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
     const float* w = top_k_weights;
     if ((rc = augment_if_shared(clock, sh, L, ws, T, idx, w, E, k, stream))) return rc;
     const int P = (int)(T * k);
+    if (fused && layer_fp8_fits(P, E, H, F)) {
+        clock.mark(MOE_STAGE_LAYER);
+        return launched(launch_layer_fp8(x, x_scale, w13, w13s, w2, w2s, idx, layer_plan_in(L, ws),
+                                         w, residual, T, H, F, E, k, hq, hs, y, out,
+                                         at<void>(ws, L.sync), stream));
+    }
     const GroupedPlan pl = plan_in(L, ws, E);
     clock.mark(MOE_STAGE_PLAN);
     const bool narrow = fp8_use_narrow(P, E, H, F);
@@ -362,12 +367,6 @@ int run_fp8(int variant, const uint16_t* hidden, const uint8_t* x, const float* 
                               at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.ntiles),
                               at<int32_t>(ws, L.tile_off), fp8_tile_m(narrow), stream));
     if (rc) return rc;
-    if (fused && layer_fp8_fits(P, E, H, F)) {
-        clock.mark(MOE_STAGE_LAYER);
-        return launched(launch_layer_fp8(x, x_scale, w13, w13s, w2, w2s, pl, at<int32_t>(ws, L.inv),
-                                         w, residual, T, H, F, k, hq, hs, y, out,
-                                         at<void>(ws, L.sync), stream));
-    }
     clock.mark(MOE_STAGE_GATE_UP);
     rc = launched(launch_gateup_fp8(x, x_scale, w13, w13s, pl, narrow, H, F, k, hq, hs, stream));
     if (rc) return rc;

@@ -355,18 +355,22 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* inv, const float* w,
     return hipGetLastError();
 }
 
+// The plan arrays (counts .. tile_off) are written by the plan phase and
+// read afterwards, so they are not restrict-qualified here.
 template <int BNG, int BND>
 __global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
     const uint16_t* __restrict__ x, const ExpertWeights w13, const ExpertWeights w2,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ inv,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+    int32_t* inv, int32_t* tiles, int32_t* ntiles_p, int32_t* tile_off,
     const float* __restrict__ wts, const uint16_t* __restrict__ residual, int64_t T, int E, int H,
     int F, int k, uint16_t* __restrict__ h, uint16_t* __restrict__ y, uint16_t* __restrict__ out,
     LayerSync sy) {
     constexpr int BNMAX = BNG > BND ? BNG : BND;
     __shared__ u32x4 lds[kAStages * kBM * 8 + kBStages * BNMAX * 8];
     const uint64_t stamp = layer_stamp(sy);
+    // the routing plan, in the operand ring before its first use
+    layer_plan((int*)lds, idx, (int)(T * k), E, kBM, counts, offsets, perm, inv, tiles, ntiles_p,
+               tile_off, stamp, sy);
     const int ntiles = *ntiles_p;
     const int npg = F / (BNG / 2), npd = H / BND;
     const int NG = ntiles * npg;
@@ -386,7 +390,8 @@ __global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
 bool layer_bf16_fits(int H, int F) { return H % 128 == 0 && F % 128 == 0; }
 
 size_t layer_sync_bytes(int64_t P, int E, int F) {
-    return 8 * (32 + 2 * (size_t)kLayerMaxGrid + (size_t)max_m_tiles(P, E) * (F / 128));
+    return 8 * (32 + 2 * (size_t)kLayerMaxGrid + 2 * (size_t)kLayerPlanChunks +
+                (size_t)kLayerPlanChunks * MOE_MAX_EXPERTS / 2 + (size_t)max_m_tiles(P, E) * (F / 128));
 }
 
 template <int BND>
@@ -398,18 +403,18 @@ static int layer_grid() {
 }
 
 hipError_t launch_layer_bf16(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
-                             const GroupedPlan& pl, const int32_t* inv, const float* w,
-                             const uint16_t* residual, int64_t T, int H, int F, int k,
+                             const int32_t* idx, const LayerPlan& pl, const float* w,
+                             const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                              uint16_t* h, uint16_t* y, uint16_t* out, void* sync, hipStream_t s) {
     const LayerSync sy{(uint64_t*)sync};
     if (H % 256 == 0)
         MOE_LAUNCH((layer_bf16_kernel<256, 256>), dim3(layer_grid<256>()), dim3(kGemmThreads), 0,
-                   s, x, w13, w2, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w,
-                   residual, T, pl.E, H, F, k, h, y, out, sy);
+                   s, x, w13, w2, idx, pl.counts, pl.offsets, pl.perm, pl.inv, pl.tiles,
+                   pl.ntiles, pl.tile_off, w, residual, T, E, H, F, k, h, y, out, sy);
     else
         MOE_LAUNCH((layer_bf16_kernel<256, 128>), dim3(layer_grid<128>()), dim3(kGemmThreads), 0,
-                   s, x, w13, w2, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w,
-                   residual, T, pl.E, H, F, k, h, y, out, sy);
+                   s, x, w13, w2, idx, pl.counts, pl.offsets, pl.perm, pl.inv, pl.tiles,
+                   pl.ntiles, pl.tile_off, w, residual, T, E, H, F, k, h, y, out, sy);
     return hipGetLastError();
 }
 

@@ -420,14 +420,16 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray
 __global__ __launch_bounds__(kFp8Threads) void layer_fp8_kernel(
     const uint8_t* __restrict__ x, const float* __restrict__ xs, const ExpertArray<uint8_t> w13,
     const ExpertArray<float> w13s, const ExpertArray<uint8_t> w2, const ExpertArray<float> w2s,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ inv,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+    int32_t* inv, int32_t* tiles, int32_t* ntiles_p, int32_t* tile_off,
     const float* __restrict__ wts, const uint16_t* __restrict__ residual, int64_t T, int E, int H,
     int F, int k, uint8_t* __restrict__ hq, float* __restrict__ hs, uint16_t* __restrict__ y,
     uint16_t* __restrict__ out, LayerSync sy) {
     __shared__ int claim;
     const uint64_t stamp = layer_stamp(sy);
+    // the routing plan, in the weight ring before its first use
+    layer_plan((int*)&Fp8Ring<kFp8WM, 256, true>::b()[0][0][0], idx, (int)(T * k), E, kFp8TileM,
+               counts, offsets, perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
     // this call's queue of down items
     if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u64(sy.queue(), (uint64_t)(uint32_t)stamp << 32);
     const int ntiles = *ntiles_p;
@@ -452,15 +454,16 @@ bool layer_fp8_fits(int64_t P, int E, int H, int F) {
 
 hipError_t launch_layer_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
                             const ExpertArray<float>& w13s, const ExpertArray<uint8_t>& w2,
-                            const ExpertArray<float>& w2s, const GroupedPlan& pl,
-                            const int32_t* inv, const float* w, const uint16_t* residual,
-                            int64_t T, int H, int F, int k, uint8_t* hq, float* hs, uint16_t* y,
-                            uint16_t* out, void* sync, hipStream_t s) {
+                            const ExpertArray<float>& w2s, const int32_t* idx,
+                            const LayerPlan& pl, const float* w, const uint16_t* residual,
+                            int64_t T, int H, int F, int E, int k, uint8_t* hq, float* hs,
+                            uint16_t* y, uint16_t* out, void* sync, hipStream_t s) {
     static const int g = std::min(
         resident_grid((const void*)layer_fp8_kernel, kFp8Threads, device_cu_count()), kLayerMaxGrid);
     MOE_LAUNCH(layer_fp8_kernel, dim3(capped_grid(g)), dim3(kFp8Threads), 0, s, x, xs, w13, w13s,
-               w2, w2s, pl.perm, inv, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, w, residual, T,
-               pl.E, H, F, k, hq, hs, y, out, LayerSync{(uint64_t*)sync});
+               w2, w2s, idx, pl.counts, pl.offsets, pl.perm, pl.inv, pl.tiles, pl.ntiles,
+               pl.tile_off, w, residual, T, E, H, F, k, hq, hs, y, out,
+               LayerSync{(uint64_t*)sync});
     return hipGetLastError();
 }
 

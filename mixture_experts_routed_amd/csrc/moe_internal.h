@@ -100,17 +100,22 @@ hipError_t launch_gateup_bf16(const uint16_t* x, const ExpertWeights& w13, const
 hipError_t launch_down_bf16(const uint16_t* h, const ExpertWeights& w2, const GroupedPlan& plan,
                             int P, int H, int F, uint16_t* y, hipStream_t s);
 
-// The same three stages in one persistent launch after the plan (see
-// moe_gemm_bf16.hip), for H and F multiples of 128: h and y go through the
-// workspace as in the stage-by-stage form and out is bit-for-bit the same.
-// `sync` holds layer_sync_bytes of hand-off words (no initialisation needed).
+// The whole layer in one persistent launch (see moe_layer.h): the routing
+// plan, gate_up, down and the combine, for H and F multiples of 128; the
+// plan arrays, h and y go through the workspace as in the stage-by-stage
+// form and out is bit-for-bit the same.  `sync` holds layer_sync_bytes of
+// hand-off words (no initialisation needed).
+struct LayerPlan {   // the plan arrays in the workspace (written by the launch)
+    int32_t *counts, *offsets, *perm, *inv, *tiles, *ntiles, *tile_off;
+};
 constexpr int kLayerMaxGrid = 1024;                  // flag slots per workgroup kind
 constexpr uint64_t kLayerSpinTicks = 200000000ull;   // 2 s of the 100 MHz clock
+constexpr int kLayerPlanChunks = 64;                 // workgroups of the in-launch routing plan
 bool layer_bf16_fits(int H, int F);
 size_t layer_sync_bytes(int64_t P, int E, int F);
 hipError_t launch_layer_bf16(const uint16_t* x, const ExpertWeights& w13, const ExpertWeights& w2,
-                             const GroupedPlan& plan, const int32_t* inv, const float* w,
-                             const uint16_t* residual, int64_t T, int H, int F, int k,
+                             const int32_t* idx, const LayerPlan& plan, const float* w,
+                             const uint16_t* residual, int64_t T, int H, int F, int E, int k,
                              uint16_t* h, uint16_t* y, uint16_t* out, void* sync, hipStream_t s);
 
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]] over valid slots (fp32, slot order)
@@ -169,15 +174,15 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
                                void* scales, bool ue8m0, hipStream_t s);
 
-// The fp8 products and the combine in one persistent launch after the plan
-// (as launch_layer_bf16), for prefill shapes with H and F multiples of 512.
+// The fp8 layer in one persistent launch (as launch_layer_bf16), for
+// prefill shapes with H and F multiples of 512.
 bool layer_fp8_fits(int64_t P, int E, int H, int F);
 hipError_t launch_layer_fp8(const uint8_t* x, const float* xs, const ExpertArray<uint8_t>& w13,
                             const ExpertArray<float>& w13s, const ExpertArray<uint8_t>& w2,
-                            const ExpertArray<float>& w2s, const GroupedPlan& plan,
-                            const int32_t* inv, const float* w, const uint16_t* residual,
-                            int64_t T, int H, int F, int k, uint8_t* hq, float* hs, uint16_t* y,
-                            uint16_t* out, void* sync, hipStream_t s);
+                            const ExpertArray<float>& w2s, const int32_t* idx,
+                            const LayerPlan& plan, const float* w, const uint16_t* residual,
+                            int64_t T, int H, int F, int E, int k, uint8_t* hq, float* hs,
+                            uint16_t* y, uint16_t* out, void* sync, hipStream_t s);
 
 // MXFP4 x MXFP8 products (E2M1 weights two per byte, E4M3 activations, E8M0
 // scales per 32 K elements): gate_up with SwiGLU + MXFP8 re-quantisation

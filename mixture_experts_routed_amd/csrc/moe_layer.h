@@ -5,6 +5,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "../../include/moe_experts.h"
 
 namespace moe {
 
@@ -162,7 +163,14 @@ struct LayerSync {
     __device__ uint64_t* queue() const { return base + 2; }
     __device__ uint64_t* ack() const { return base + 32; }   // [G] workgroup read the generation
     __device__ uint64_t* dflag() const { return base + 32 + kLayerMaxGrid; }   // [G] down items done
-    __device__ uint64_t* gflag() const { return base + 32 + 2 * kLayerMaxGrid; }  // [gate_up items]
+    // [kLayerPlanChunks] each: chunk counted / chunk scattered
+    __device__ uint64_t* pcount() const { return base + 32 + 2 * kLayerMaxGrid; }
+    __device__ uint64_t* pdone() const { return pcount() + kLayerPlanChunks; }
+    // [E][kLayerPlanChunks] per-chunk expert counts (expert-major)
+    __device__ int32_t* pcnt() const { return (int32_t*)(pdone() + kLayerPlanChunks); }
+    __device__ uint64_t* gflag() const {   // [gate_up items]
+        return pdone() + kLayerPlanChunks + kLayerPlanChunks * MOE_MAX_EXPERTS / 2;
+    }
 };
 
 // wave 0 waits until flags[i * stride], i < n, all equal stamp (each wait
@@ -321,6 +329,183 @@ struct LayerSched {
         if (threadIdx.x == 0) st_dev_u64(sy.dflag() + blockIdx.x, stamp);
     }
 };
+
+// sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// The routing plan as the layer's first phase, the same arrays as the plan
+// kernel's (the ordering rule fixes every entry): the first Gp = min(G,
+// kLayerPlanChunks) workgroups each take a contiguous chunk of slots,
+//  1. count their slots per (wave, expert) and publish the chunk's counts;
+//  2. once every chunk is counted, each sums the counts of all chunks (the
+//     totals, their exclusive prefix = offsets and the M-tile prefix) and of
+//     the chunks before its own, and scatters its slots in slot order, lanes
+//     of one 64-slot step that share an expert ranked by an OR-ed lane mask
+//     (as the plan kernel);
+//  3. workgroup 0 writes counts, offsets, the tiles and their prefix.
+// Every workgroup then waits until every chunk is scattered.  All plan
+// stores are device-scope; the arrays are first read after that wait.
+// `ldsi`: 56 KB of idle LDS.
+__device__ __forceinline__ void layer_plan(int* ldsi, const int32_t* __restrict__ idx, int P,
+                                           int E, int tile_m, int32_t* __restrict__ counts,
+                                           int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                           int32_t* __restrict__ tiles,
+                                           int32_t* __restrict__ ntiles,
+                                           int32_t* __restrict__ tile_off, uint64_t stamp,
+                                           LayerSync sy) {
+    constexpr int NW = 8;   // waves of a 512-thread workgroup
+    const int G = gridDim.x, b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Gp = min(G, kLayerPlanChunks);
+    if (b < Gp) {
+        int* base = ldsi;                                               // [NW][E]
+        unsigned long long* lanes_of = (unsigned long long*)(ldsi + NW * MOE_MAX_EXPERTS);  // [NW][E]
+        int* tot = ldsi + 3 * NW * MOE_MAX_EXPERTS;                     // [E]
+        int* off = tot + MOE_MAX_EXPERTS;                               // [E + 1]
+        int* tsh = off + MOE_MAX_EXPERTS + 1;                           // [E + 1]
+        for (int i = tid; i < NW * MOE_MAX_EXPERTS; i += blockDim.x) {
+            base[i] = 0;
+            lanes_of[i] = 0ull;
+        }
+        lds_barrier();
+        // the chunk, and each wave's 64-aligned run of it
+        const int c0 = (int)((int64_t)P * b / Gp), c1 = (int)((int64_t)P * (b + 1) / Gp);
+        const int run = ((c1 - c0 + NW * kWave - 1) / (NW * kWave)) * kWave;
+        const int s0 = min(c1, c0 + wave * run), s1 = min(c1, s0 + run);
+        for (int s = s0 + lane; s < s1; s += kWave) {
+            const int e = idx[s];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&base[wave * E + e], 1);
+        }
+        lds_barrier();
+        for (int e = tid; e < E; e += blockDim.x) {
+            int acc = 0;
+            for (int w = 0; w < NW; ++w) acc += base[w * E + e];
+            st_dev_u32((uint32_t*)(sy.pcnt() + e * kLayerPlanChunks + b), (uint32_t)acc);
+        }
+        wait_vm_all();
+        lds_barrier();
+        if (tid == 0) st_dev_u64(sy.pcount() + b, stamp);
+        wait_flags(sy.pcount(), Gp, 1, stamp, sy);
+        // totals, and this chunk's base per expert (chunks before it, then
+        // the waves before each wave's run): lane c of a wave reads chunk c's
+        // count of an expert, and the wave sums them
+        {
+            constexpr int EB = 8;   // experts per batch of loads in flight
+            for (int e0 = wave * EB; e0 < E; e0 += NW * EB) {
+                int v[EB];
+#pragma unroll
+                for (int j = 0; j < EB; ++j)
+                    v[j] = e0 + j < E && lane < Gp
+                               ? (int)__hip_atomic_load((const uint32_t*)(sy.pcnt() + (e0 + j) * kLayerPlanChunks + lane),
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0;
+#pragma unroll
+                for (int j = 0; j < EB; ++j) {
+                    const int e = e0 + j;
+                    const int t = wave_sum_i32(v[j]);
+                    const int pre = wave_sum_i32(lane < b ? v[j] : 0);
+                    if (e < E && lane == 0) {
+                        tot[e] = t;
+                        int run_ = pre;
+                        for (int w = 0; w < NW; ++w) {
+                            const int cw = base[w * E + e];
+                            base[w * E + e] = run_;
+                            run_ += cw;
+                        }
+                    }
+                }
+            }
+        }
+        lds_barrier();
+        if (wave == 0) {   // exclusive prefix of the totals and of the M tiles
+            const int per = (E + kWave - 1) / kWave;
+            const int e0 = lane * per;
+            int c_sum = 0, t_sum = 0;
+            for (int i = 0; i < per; ++i) {
+                const int e = e0 + i;
+                if (e < E) {
+                    c_sum += tot[e];
+                    t_sum += (tot[e] + tile_m - 1) / tile_m;
+                }
+            }
+            int c_inc = c_sum, t_inc = t_sum;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int cu = __shfl_up(c_inc, o, kWave);
+                const int tu = __shfl_up(t_inc, o, kWave);
+                if (lane >= o) {
+                    c_inc += cu;
+                    t_inc += tu;
+                }
+            }
+            int c_run = c_inc - c_sum, t_run = t_inc - t_sum;
+            for (int i = 0; i < per; ++i) {
+                const int e = e0 + i;
+                if (e < E) {
+                    off[e] = c_run;
+                    tsh[e] = t_run;
+                    c_run += tot[e];
+                    t_run += (tot[e] + tile_m - 1) / tile_m;
+                }
+            }
+            if (lane == kWave - 1) {
+                off[E] = c_inc;
+                tsh[E] = t_inc;
+            }
+        }
+        lds_barrier();
+        if (b == 0) {
+            for (int e = tid; e <= E; e += blockDim.x) {
+                st_dev_u32((uint32_t*)(offsets + e), (uint32_t)off[e]);
+                st_dev_u32((uint32_t*)(tile_off + e), (uint32_t)tsh[e]);
+                if (e < E) {
+                    st_dev_u32((uint32_t*)(counts + e), (uint32_t)tot[e]);
+                    for (int i = 0; i < tsh[e + 1] - tsh[e]; ++i) {
+                        st_dev_u32((uint32_t*)(tiles + 2 * (tsh[e] + i)), (uint32_t)e);
+                        st_dev_u32((uint32_t*)(tiles + 2 * (tsh[e] + i) + 1), (uint32_t)(off[e] + i * tile_m));
+                    }
+                }
+            }
+            if (tid == 0) st_dev_u32((uint32_t*)ntiles, (uint32_t)tsh[E]);
+        }
+        for (int i = tid; i < NW * E; i += blockDim.x) base[i] += off[i % E];
+        lds_barrier();
+        // stable scatter of the wave's run, 64 slots per step
+        for (int sb = s0; sb < s1; sb += kWave) {
+            const int s = sb + lane;
+            const int e = s < s1 ? idx[s] : -1;
+            const bool valid = (unsigned)e < (unsigned)E;
+            if (valid) atomicOr(&lanes_of[wave * E + e], 1ull << lane);
+            __builtin_amdgcn_wave_barrier();
+            const unsigned long long same = valid ? lanes_of[wave * E + e] : 0ull;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) lanes_of[wave * E + e] = 0ull;
+            int rank = 0, pos = -1;
+            if (valid) {
+                rank = __popcll(same & ((1ull << lane) - 1ull));
+                pos = base[wave * E + e] + rank;
+                st_dev_u32((uint32_t*)(perm + pos), (uint32_t)s);
+            }
+            if (s < s1) st_dev_u32((uint32_t*)(inv + s), (uint32_t)pos);
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) base[wave * E + e] += __popcll(same);
+            __builtin_amdgcn_wave_barrier();
+        }
+        // this chunk's share of the dropped-slot tail of perm
+        const int d0 = off[E] + (int)((int64_t)(P - off[E]) * b / Gp);
+        const int d1 = off[E] + (int)((int64_t)(P - off[E]) * (b + 1) / Gp);
+        for (int i = d0 + tid; i < d1; i += blockDim.x) st_dev_u32((uint32_t*)(perm + i), 0xffffffffu);
+        wait_vm_all();
+        lds_barrier();
+        if (tid == 0) st_dev_u64(sy.pdone() + b, stamp);
+    }
+    wait_flags(sy.pdone(), Gp, 1, stamp, sy);
+}
 
 // This call's stamp (the generation word + 1), read by wave 0 and kept in
 // scalar registers (the other waves hold 0 and never use it); the

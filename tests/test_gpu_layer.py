@@ -1,5 +1,6 @@
-"""GPU parity of moe_experts_prefill_fused: the grouped bf16 layer with
-gate_up, down and the combine in one persistent launch after the plan.
+"""GPU parity of the one-launch layers (moe_experts_prefill_fused for bf16,
+moe_experts_fp8_fused): the routing plan, gate_up, down and the combine in
+one persistent launch.
 
 The one-launch form performs the same arithmetic as the stage-by-stage form
 (moe_experts_prefill, itself checked on every element against the oracle in
@@ -176,7 +177,7 @@ def test_layer_stage_recorder_and_empty_call():
     run("moe_experts_prefill_fused", p)
     torch.cuda.synchronize()
     calls = moe.moe_profile_end(1)
-    assert [s for s, _ in calls[0]] == ["plan", "layer"]
+    assert [s for s, _ in calls[0]] == ["layer"]
     empty = {n: v[:0] if n in ("hidden", "top_k_index", "top_k_weights") else v
              for n, v in p.items()}
     assert run("moe_experts_prefill_fused", empty).shape == (0, 256)
@@ -258,7 +259,7 @@ def test_fp8_layer_repeated_calls_stale_workspace_and_stages():
         got = run_fp8("moe_experts_fp8_fused", g, workspace=ws)
         torch.cuda.synchronize()
         if i == 3:
-            assert [s for s, _ in moe.moe_profile_end(1)[0]] == ["plan", "layer"]
+            assert [s for s, _ in moe.moe_profile_end(1)[0]] == ["layer"]
         same_bits(got, run_fp8("moe_experts_fp8", g), f"call {i}")
 
 
@@ -282,3 +283,43 @@ def test_fp8_layer_full_v3_prefill():
     _say("one-launch fp8 layer, full v3_fp8_prefill")
     p = wl.make_config("v3_fp8_prefill", device="cuda")
     same_bits(run_fp8("moe_experts_fp8_fused", p), run_fp8("moe_experts_fp8", p), "v3_fp8_prefill")
+
+
+# ------------------------------------------------- the plan inside the launch
+
+
+def _ws_i32(ws, off, n):
+    return ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+
+# (T, k, E, ids): the plan phase's chunks hold a few slots (T*k < 64 chunks
+# too), many slots, every expert id up to 512 experts, and dropped ids
+@pytest.mark.parametrize("case", [(5, 2, 8, "uniform"), (300, 3, 12, "uniform"),
+                                  (2048, 6, 64, "uniform"), (4096, 8, 512, "skewed"),
+                                  (777, 4, 16, "dropped")])
+def test_layer_plan_arrays_match_oracle(case):
+    """The plan arrays the one-launch layer writes into its workspace are the
+    oracle's, bit for bit."""
+    moe = _moe()
+    T, k, E, kind = case
+    _say(f"one-launch layer plan {case}")
+    H, F = 128, 128
+    p = problem(T, H, F, E, k, seed=900 + T)
+    idx = p["top_k_index"].clone()
+    if kind == "skewed":
+        g = torch.Generator().manual_seed(5)
+        idx = (torch.rand(T, k, generator=g) ** 3 * E).to(torch.int32).cuda()
+    elif kind == "dropped":
+        idx[::3, 0] = -1
+        idx[::5, 1] = E + 7
+    p["top_k_index"] = idx.contiguous()
+    lay = moe.moe_workspace_layout(moe.MOE_VARIANT_PREFILL, T, H, F, E, k)
+    ws = torch.full((lay["total"],), 0xEE, dtype=torch.uint8, device="cuda")
+    run("moe_experts_prefill_fused", p, workspace=ws)
+    torch.cuda.synchronize()
+    ref = orc.routing_plan(p["top_k_index"].cpu().numpy(), E)
+    P = T * k
+    got = (_ws_i32(ws, lay["counts"], E), _ws_i32(ws, lay["offsets"], E + 1),
+           _ws_i32(ws, lay["perm"], P), _ws_i32(ws, lay["inv"], P))
+    for name, a, r in zip(("counts", "offsets", "perm", "inv"), got, ref):
+        assert np.array_equal(a, r), f"plan {name} differs"
