@@ -488,6 +488,14 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 return moe.moe_experts_fp8_fused(p["x"], p["x_scale"], p["gate_up"], p["gate_up_scale"],
                                                  p["down"], p["down_scale"], p["top_k_index"],
                                                  p["top_k_weights"], k, out=out_buf)
+        elif kind == "mxfp4" and T * k > 64 * E:
+            fused_entry = "moe_experts_mxfp4_fused"
+
+            def step_fused(i):
+                return moe.moe_experts_mxfp4_fused(p["x"], p["x_scale"], p["gate_up"],
+                                                   p["gate_up_scale"], p["down"], p["down_scale"],
+                                                   p["top_k_index"], p["top_k_weights"], k,
+                                                   out=out_buf)
         if fused_entry:
             # pass E: the same steps through the one-launch form (the plan,
             # then gate_up, down and the combine in one persistent launch)
@@ -511,7 +519,7 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 for st, ms in row:
                     per[st].append(ms)
             out["fused_layer"] = {
-                "entry": f"{fused_entry} (plan, then one persistent launch)",
+                "entry": f"{fused_entry} (one persistent launch: plan, both products, combine)",
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "stage_us": {st: round(float(np.mean(v)) * 1e3, 2) for st, v in per.items()}}

@@ -365,6 +365,23 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale,
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_experts_mxfp4 in one persistent launch (the FP8 x FP4 single-kernel
+ * layer): the routing plan, the two grouped MX products and the combine, as
+ * moe_experts_prefill_fused does for bf16 (same operands, workspace
+ * moe_workspace_size(MOE_VARIANT_MXFP4, ...), errors and results: out is
+ * bit-for-bit that of moe_experts_mxfp4; the same residency requirement,
+ * 2 s wait limit and generation word).  Used for prefill shapes (more than
+ * 64 slots per expert on average, F a multiple of 256, H of 512); other
+ * calls run the moe_experts_mxfp4 sequence.
+ */
+int moe_experts_mxfp4_fused(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+                            const uint8_t* gate_up_scale, const uint8_t* down,
+                            const uint8_t* down_scale, const int32_t* top_k_index,
+                            const float* top_k_weights, const uint16_t* residual, int64_t T, int H,
+                            int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
  * The MXFP4 layer with S fused shared experts, stored like the routed ones:
  * shared_gate_up [S,2F,H/2] and shared_down [S,H,F/2] E2M1 pairs with E8M0
  * scales [S,2F,H/32] and [S,H,F/32] (codes 16-byte aligned, scales 4-byte

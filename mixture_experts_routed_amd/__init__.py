@@ -68,6 +68,7 @@ def _load():
         "moe_quantize_fp8_block128": ([vp, i32, i64, i32, vp, vp, vp], i32),
         "moe_quantize_fp8_block128_ue8m0": ([vp, i32, i64, i32, vp, vp, vp], i32),
         "moe_experts_mxfp4": ([vp] * 9 + [i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+        "moe_experts_mxfp4_fused": ([vp] * 9 + [i64, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_fp8_shared": ([vp] * 13 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_experts_mxfp4_shared": ([vp] * 13 + [i64, i32, i32, i32, i32, i32, vp, vp, sz, vp], i32),
         "moe_route_topk": ([vp, vp, i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
@@ -100,7 +101,8 @@ def exported_symbols():
             "moe_workspace_size_shared", "moe_experts_mxfp4", "moe_route_topk", "moe_route_plan",
             "moe_experts_decode_routed", "moe_set_grid_cap", "moe_experts_decode_noalloc",
             "moe_probe_stream_read", "moe_quantize_fp8_block128_ue8m0", "moe_experts_fp8_shared",
-            "moe_experts_mxfp4_shared", "moe_experts_prefill_fused", "moe_experts_fp8_fused"]
+            "moe_experts_mxfp4_shared", "moe_experts_prefill_fused", "moe_experts_fp8_fused",
+            "moe_experts_mxfp4_fused"]
 
 
 class MoeError(RuntimeError):
@@ -574,6 +576,20 @@ def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_
     per byte (element 2i in the low nibble) with uint8 E8M0 scales
     [E, 2F, H/32] and [E, H, F/32].  Returns out [T, H] bf16 (plus the
     optional residual [T, H] bf16)."""
+    return _mx_call("moe_experts_mxfp4", x, x_scale, gate_up, gate_up_scale, down, down_scale,
+                    top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def moe_experts_mxfp4_fused(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+                            top_k_weights, top_k, residual=None, workspace=None, out=None):
+    """moe_experts_mxfp4 in one persistent launch (plan, both products and the
+    combine; same operands, workspace and result)."""
+    return _mx_call("moe_experts_mxfp4_fused", x, x_scale, gate_up, gate_up_scale, down,
+                    down_scale, top_k_index, top_k_weights, top_k, residual, workspace, out)
+
+
+def _mx_call(entry, x, x_scale, gate_up, gate_up_scale, down, down_scale, top_k_index,
+             top_k_weights, top_k, residual, workspace, out):
     x = _codes(x)
     dev = x.device
     _need(x, "x", torch.uint8, 2)
@@ -602,11 +618,11 @@ def moe_experts_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, top_
         stream = _stream(dev)
         need = moe_workspace_size(MOE_VARIANT_MXFP4, T, H, F, E, k)
         ws = workspace if workspace is not None else _workspace(need, dev, stream)
-        rc = _load().moe_experts_mxfp4(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
-                                       _ptr(down), _ptr(down_scale), _ptr(top_k_index),
-                                       _ptr(top_k_weights), res, T, H, F, E, k, _ptr(out),
-                                       _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
-    _check(rc, "moe_experts_mxfp4")
+        rc = getattr(_load(), entry)(_ptr(x), _ptr(x_scale), _ptr(gate_up), _ptr(gate_up_scale),
+                                     _ptr(down), _ptr(down_scale), _ptr(top_k_index),
+                                     _ptr(top_k_weights), res, T, H, F, E, k, _ptr(out),
+                                     _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    _check(rc, entry)
     return out
 
 
@@ -767,7 +783,8 @@ __all__ = [
     "moe_experts_fp8", "moe_experts_fp8_fused", "moe_experts_fp8_bf16in", "moe_quantize_fp8_block128",
     "moe_quantize_fp8_block128_ue8m0",
     "moe_experts_fp8_shared", "moe_experts_mxfp4_shared", "moe_experts_prefill_shared",
-    "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4", "MoeError",
+    "moe_experts_decode_shared", "moe_workspace_size_shared", "moe_experts_mxfp4",
+    "moe_experts_mxfp4_fused", "MoeError",
     "MOE_VARIANT_PREFILL", "MOE_VARIANT_DECODE", "MOE_VARIANT_FP8", "MOE_VARIANT_PLAN",
     "MOE_VARIANT_FP8_BF16IN", "MOE_VARIANT_MXFP4", "moe_route_topk", "moe_route_plan",
     "moe_experts_decode_routed",

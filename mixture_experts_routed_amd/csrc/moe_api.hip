@@ -153,7 +153,7 @@ Layout make_layout(int variant, int64_t T, int H, int F, int E, int k) {
     }
     L.y = take((size_t)P * H * 2);
     if (variant == MOE_VARIANT_PREFILL || variant == MOE_VARIANT_FP8 ||
-        variant == MOE_VARIANT_FP8_BF16IN)   // hand-off words of the one-launch forms
+        variant == MOE_VARIANT_FP8_BF16IN || variant == MOE_VARIANT_MXFP4)   // one-launch forms
         L.sync = take(layer_sync_bytes(P, E, F));
     if (variant == MOE_VARIANT_FP8_BF16IN) {  // the quantised hidden states
         L.xq = take((size_t)T * H);
@@ -381,7 +381,7 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
               const uint8_t* gate_up_scale, const uint8_t* down, const uint8_t* down_scale,
               const SharedQ& sh, const int32_t* top_k_index, const float* top_k_weights,
               const uint16_t* residual, int64_t T, int H, int F, int E, int k, uint16_t* out,
-              void* ws, size_t ws_bytes, hipStream_t stream) {
+              void* ws, size_t ws_bytes, hipStream_t stream, bool fused = false) {
     if (!x || !x_scale || !gate_up || !gate_up_scale || !down || !down_scale || !top_k_index ||
         !top_k_weights || !out)
         return MOE_ERR_NULL;
@@ -409,6 +409,12 @@ int run_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
     const float* w = top_k_weights;
     if ((rc = augment_if_shared(clock, sh, L, ws, T, idx, w, E, k, stream))) return rc;
     const int P = (int)(T * k);
+    if (fused && layer_mx_fits(P, E, H, F)) {
+        clock.mark(MOE_STAGE_LAYER);
+        return launched(launch_layer_mx(x, x_scale, w13, w13s, w2, w2s, idx, layer_plan_in(L, ws), w,
+                                        residual, T, H, F, E, k, hq, hs, y, out,
+                                        at<void>(ws, L.sync), stream));
+    }
     const GroupedPlan pl = plan_in(L, ws, E);
     clock.mark(MOE_STAGE_PLAN);
     const bool narrow = mx_use_narrow(P, E, H, F);
@@ -753,6 +759,16 @@ int moe_experts_mxfp4(const uint8_t* x, const uint8_t* x_scale, const uint8_t* g
                       uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, SharedQ{}, top_k_index,
                      top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream);
+}
+
+int moe_experts_mxfp4_fused(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,
+                            const uint8_t* gate_up_scale, const uint8_t* down,
+                            const uint8_t* down_scale, const int32_t* top_k_index,
+                            const float* top_k_weights, const uint16_t* residual, int64_t T, int H,
+                            int F, int E, int k, uint16_t* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    return run_mxfp4(x, x_scale, gate_up, gate_up_scale, down, down_scale, SharedQ{}, top_k_index,
+                     top_k_weights, residual, T, H, F, E, k, out, ws, ws_bytes, stream, true);
 }
 
 int moe_experts_mxfp4_shared(const uint8_t* x, const uint8_t* x_scale, const uint8_t* gate_up,

@@ -18,6 +18,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_layer.h"
 
 namespace moe {
 
@@ -288,30 +289,50 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 // LDS bytes per lane and product, which the 128 x 256 kernel spends about as
 // much time on as on its products.  Scales: every thread stages the word of
 // panel row tid, threads < 128 also the word of tile row tid.
-template <bool SWIGLU>
-__global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const ExpertArray<uint8_t> B,
-    const ExpertArray<uint8_t> Bs, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
-    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
-    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
-    uint16_t* __restrict__ Cy) {
+// The wide tiles' LDS arrays: separate variables, the same ones for the
+// gate_up and the down loop of a one-launch layer.
+struct MxWideRing {
+    __device__ static u32x4 (&a())[2][kMxBM][8] {
+        __shared__ u32x4 v[2][kMxBM][8];
+        return v;
+    }
+    __device__ static u32x4 (&b())[2][512][4] {
+        __shared__ u32x4 v[2][512][4];
+        return v;
+    }
+    __device__ static uint32_t (&sa())[2][kMxBM] {
+        __shared__ uint32_t v[2][kMxBM];
+        return v;
+    }
+    __device__ static uint32_t (&sb())[2][512] {
+        __shared__ uint32_t v[2][512];
+        return v;
+    }
+};
+
+// The persistent item loop of the wide tiles, with the scheduling hooks of
+// moe_layer.h.
+template <bool SWIGLU, class Sched>
+__device__ __forceinline__ void mx_wide_loop(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const ExpertArray<uint8_t>& B,
+    const ExpertArray<uint8_t>& Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ offsets, int E, int K, int n_out, int b_rows, int topk,
+    uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs, uint16_t* __restrict__ Cy, Sched& sc) {
     constexpr int BN = 512;
     constexpr int NB = 4;                             // 32-row panel blocks per wave
     constexpr int MB = 2;                             // 32-row tile blocks per wave
     constexpr int A_PER = kMxBM * 8 / kMxThreads;     // 2
     constexpr int B_PER = BN * 4 / kMxThreads;        // 4
-    __shared__ u32x4 a_lds[2][kMxBM][8];
-    __shared__ u32x4 b_lds[2][BN][4];
-    __shared__ uint32_t sa_lds[2][kMxBM];
-    __shared__ uint32_t sb_lds[2][BN];
+    auto& a_lds = MxWideRing::a();
+    auto& b_lds = MxWideRing::b();
+    auto& sa_lds = MxWideRing::sa();
+    auto& sb_lds = MxWideRing::sb();
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5;
-    const int ntiles = *ntiles_p;
     const int n_tiles_n = SWIGLU ? n_out / (BN / 2) : n_out / BN;
-    const int items = ntiles * n_tiles_n;
     const int nks = K / kMxBK;
     const int kb_row = K / 32;
     const bool sa_t = tid < kMxBM;
@@ -324,14 +345,17 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
         return nt * BN + rr;
     };
 
-    for (int it = xcd_slot(blockIdx.x, gridDim.x); it < items; it += gridDim.x) {
+    for (int it = sc.first(); it >= 0; it = sc.next(it)) {
         const GroupedItem gi = grouped_item(it, tile_off, E, n_tiles_n);
+        sc.wait_inputs(gi);
         const int nt = gi.nt, e = gi.e;
         const int row0 = tiles[2 * gi.mt + 1];
         const int mrows = min(kMxBM, offsets[e + 1] - row0);
         const bool active = 64 * wm < mrows;
-        auto a_row = [&](int r) -> int64_t {   // rows past the tile's end read row 0, never stored
-            if (r >= mrows) return 0;
+        // rows past the tile's end read token row 0 or the tile's first row
+        // (never stored)
+        auto a_row = [&](int r) -> int64_t {
+            if (r >= mrows) return SWIGLU ? 0 : row0;
             return SWIGLU ? (int64_t)(perm[row0 + r] / topk) : (int64_t)(row0 + r);
         };
 
@@ -365,7 +389,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
 #pragma unroll
             for (int i = 0; i < B_PER; ++i) rb_[i] = *(const u32x4*)(b_src[i] + ks * (kMxBK / 2));
             rsb_ = *(const uint32_t*)(sb_src + ks * 4);
-            rsa_ = *(const uint32_t*)(sa_src + ks * 4);
+            rsa_ = sc.load_scale_word(sa_src + ks * 4);
         };
         auto step = [&](int S, u32x4 (&ra_)[A_PER], u32x4 (&rb_)[B_PER], uint32_t& rsa_,
                         uint32_t& rsb_, int ks) {
@@ -442,8 +466,8 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
                             const int row = 64 * wm + 32 * mb + acc_row(q, lane);
                             if (row < mrows) {
                                 const int blk = nt * (BN / 64) + wn * (NB / 2) + p;
-                                Cq[(int64_t)(row0 + row) * n_out + blk * 32 + (lane & 31)] = (uint8_t)code;
-                                if ((lane & 31) == 0) Cs[(int64_t)(row0 + row) * nfb + blk] = (uint8_t)(se + 127);
+                                sc.store_u8(Cq + (int64_t)(row0 + row) * n_out + blk * 32 + (lane & 31), (uint8_t)code);
+                                if ((lane & 31) == 0) sc.store_u8(Cs + (int64_t)(row0 + row) * nfb + blk, (uint8_t)(se + 127));
                             }
                         }
             }
@@ -461,13 +485,61 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
                         const int col = nt * BN + (wn * NB + nb) * 32 + (lane & 30);
                         if (row < mrows) {
                             const uint32_t v = odd ? pack_bf16x2_hw(got, y1) : pack_bf16x2_hw(y0, got);
-                            *(uint32_t*)(Cy + (int64_t)(row0 + row) * n_out + col) = v;
+                            sc.store_u32(Cy + (int64_t)(row0 + row) * n_out + col, v);
                         }
                     }
                 }
         }
         lds_barrier();
+        sc.stored(it);
     }
+    sc.drained();
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kMxThreads) void gemm_mx_wide_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const ExpertArray<uint8_t> B,
+    const ExpertArray<uint8_t> Bs, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles_p,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ offsets, int E, int K,
+    int n_out, int b_rows, int topk, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs,
+    uint16_t* __restrict__ Cy) {
+    PlainSched sc{*ntiles_p * (SWIGLU ? n_out / 256 : n_out / 512)};
+    mx_wide_loop<SWIGLU>(A, As, B, Bs, perm, tiles, tile_off, offsets, E, K, n_out, b_rows, topk,
+                         Cq, Cs, Cy, sc);
+}
+
+// ------------------------------------------------------ one-launch layer
+// moe_experts_mxfp4's grouped path for prefill shapes in one persistent
+// launch (the hand-offs of moe_layer.h): the routing plan, then the wide
+// tiles for both products (gate_up items statically, down items from the
+// queue), then the combine.  The FP8 x FP4 precision pair of the DeepGEMM
+// "Mega MoE" news item.
+__global__ __launch_bounds__(kMxThreads) void layer_mx_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs, const ExpertArray<uint8_t> w13,
+    const ExpertArray<uint8_t> w13s, const ExpertArray<uint8_t> w2, const ExpertArray<uint8_t> w2s,
+    const int32_t* __restrict__ idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+    int32_t* inv, int32_t* tiles, int32_t* ntiles_p, int32_t* tile_off,
+    const float* __restrict__ wts, const uint16_t* __restrict__ residual, int64_t T, int E, int H,
+    int F, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ y,
+    uint16_t* __restrict__ out, LayerSync sy) {
+    __shared__ int claim;
+    const uint64_t stamp = layer_stamp(sy);
+    // the routing plan, in the weight ring before its first use
+    layer_plan((int*)&MxWideRing::b()[0][0][0], idx, (int)(T * k), E, kMxBM, counts, offsets,
+               perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u64(sy.queue(), (uint64_t)(uint32_t)stamp << 32);
+    const int ntiles = *ntiles_p;
+    const int npg = F / 256, npd = H / 512;
+    const int NG = ntiles * npg, ND = ntiles * npd;
+    LayerSched<true> sg{NG, NG, npg, 0, stamp, sy, tile_off, 0, nullptr, 0};
+    mx_wide_loop<true>(x, xs, w13, w13s, perm, tiles, tile_off, offsets, E, H, F, 2 * F, k, hq, hs,
+                       nullptr, sg);
+    LayerSched<false, true> sd{ND, NG, npg, 0, stamp, sy, tile_off, 0, &claim, 0};
+    mx_wide_loop<false>(hq, hs, w2, w2s, perm, tiles, tile_off, offsets, E, F, H, H, 1, nullptr,
+                        nullptr, y, sd);
+    // the scale ring is idle now: one of its words carries the error state
+    layer_combine((int*)&MxWideRing::sb()[0][0], y, inv, wts, residual, T, k, H, out, stamp, sy);
 }
 
 // Decode batches (at most 32 rows per expert on average, K a multiple of 256
@@ -521,6 +593,24 @@ hipError_t launch_gateup_mx(const uint8_t* x, const uint8_t* xs, const ExpertArr
         MOE_LAUNCH((gemm_mx_kernel<256, true, 1>), dim3(mx_grid<256, true, 1>()), dim3(kMxThreads), 0,
                    s, x, xs, w13, w13s, pl.perm, pl.tiles, pl.ntiles, pl.tile_off, pl.offsets, pl.E,
                    H, F, 2 * F, k, hq, hs, (uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+bool layer_mx_fits(int64_t P, int E, int H, int F) {
+    return !mx_use_narrow(P, E, H, F) && mx_use_wide(P, E, H, F);
+}
+
+hipError_t launch_layer_mx(const uint8_t* x, const uint8_t* xs, const ExpertArray<uint8_t>& w13,
+                           const ExpertArray<uint8_t>& w13s, const ExpertArray<uint8_t>& w2,
+                           const ExpertArray<uint8_t>& w2s, const int32_t* idx,
+                           const LayerPlan& pl, const float* w, const uint16_t* residual,
+                           int64_t T, int H, int F, int E, int k, uint8_t* hq, uint8_t* hs,
+                           uint16_t* y, uint16_t* out, void* sync, hipStream_t s) {
+    static const int g = std::min(
+        resident_grid((const void*)layer_mx_kernel, kMxThreads, device_cu_count()), kLayerMaxGrid);
+    MOE_LAUNCH(layer_mx_kernel, dim3(capped_grid(g)), dim3(kMxThreads), 0, s, x, xs, w13, w13s, w2,
+               w2s, idx, pl.counts, pl.offsets, pl.perm, pl.inv, pl.tiles, pl.ntiles, pl.tile_off,
+               w, residual, T, E, H, F, k, hq, hs, y, out, LayerSync{(uint64_t*)sync});
     return hipGetLastError();
 }
 

@@ -174,6 +174,16 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const ExpertArray
 hipError_t launch_quantize_fp8(const void* in, int in_is_bf16, int64_t rows, int K, uint8_t* codes,
                                void* scales, bool ue8m0, hipStream_t s);
 
+// The MXFP4 layer in one persistent launch (as launch_layer_bf16), for
+// prefill shapes that take the wide tiles.
+bool layer_mx_fits(int64_t P, int E, int H, int F);
+hipError_t launch_layer_mx(const uint8_t* x, const uint8_t* xs, const ExpertArray<uint8_t>& w13,
+                           const ExpertArray<uint8_t>& w13s, const ExpertArray<uint8_t>& w2,
+                           const ExpertArray<uint8_t>& w2s, const int32_t* idx,
+                           const LayerPlan& plan, const float* w, const uint16_t* residual,
+                           int64_t T, int H, int F, int E, int k, uint8_t* hq, uint8_t* hs,
+                           uint16_t* y, uint16_t* out, void* sync, hipStream_t s);
+
 // The fp8 layer in one persistent launch (as launch_layer_bf16), for
 // prefill shapes with H and F multiples of 512.
 bool layer_fp8_fits(int64_t P, int E, int H, int F);

@@ -29,6 +29,7 @@ struct PlainSched {
     // per-row scales of the A operand (one, or four K blocks at once)
     __device__ float load_scale(const float* p) const { return *p; }
     __device__ float4 load_scale4(const float* p) const { return *(const float4*)p; }
+    __device__ uint32_t load_scale_word(const uint8_t* p) const { return *(const uint32_t*)p; }
     __device__ void stored(int) const {}
     __device__ void drained() const {}
 };
@@ -313,6 +314,11 @@ struct LayerSched {
     __device__ float4 load_scale4(const float* p) const {
         if (GATE) return *(const float4*)p;
         return make_float4(load_scale(p), load_scale(p + 1), load_scale(p + 2), load_scale(p + 3));
+    }
+    // four E8M0 scale bytes of the A operand (same reason)
+    __device__ uint32_t load_scale_word(const uint8_t* p) const {
+        if (GATE) return *(const uint32_t*)p;
+        return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // a gate_up item's flag, once its stores have completed in every wave
     // (the next item's first loads, issued before them, have landed too)

@@ -323,3 +323,65 @@ def test_layer_plan_arrays_match_oracle(case):
            _ws_i32(ws, lay["perm"], P), _ws_i32(ws, lay["inv"], P))
     for name, a, r in zip(("counts", "offsets", "perm", "inv"), got, ref):
         assert np.array_equal(a, r), f"plan {name} differs"
+
+
+# ----------------------------------------------------------- MXFP4 layer
+
+def _mx_helpers():
+    import test_gpu_mxfp4 as tm
+    return tm
+
+
+def run_mx(entry, g, workspace=None):
+    fn = getattr(_moe(), entry)
+    return fn(g["x"], g["x_scale"], g["gate_up"], g["gate_up_scale"], g["down"], g["down_scale"],
+              g["top_k_index"], g["top_k_weights"], g["top_k_index"].shape[1], workspace=workspace)
+
+
+# (T, H, F, E, k): more than 64 slots per expert (the wide tiles), F % 256,
+# H % 512
+MX_SHAPES = [(600, 512, 256, 4, 2), (1000, 1024, 512, 6, 3), (700, 512, 768, 3, 2)]
+
+
+@pytest.mark.parametrize("shape", MX_SHAPES)
+def test_mx_layer_matches_oracle_and_stage_form(shape):
+    tm = _mx_helpers()
+    T, H, F, E, k = shape
+    _say(f"one-launch MXFP4 layer {shape}")
+    p = tm.mx_problem(T, H, F, E, k, seed=60 + T, block_spread=2)
+    g = {n: v.cuda() for n, v in p.items()}
+    got = run_mx("moe_experts_mxfp4_fused", g)
+    same_bits(got, run_mx("moe_experts_mxfp4", g), str(shape))
+    check_fp8_tol(got, tm.mx_ref(g), str(shape))
+
+
+def test_mx_layer_small_grid_repeated_calls_and_stages():
+    moe = _moe()
+    tm = _mx_helpers()
+    _say("one-launch MXFP4 layer, small grid, repeated calls")
+    T, H, F, E, k = 800, 512, 512, 4, 2
+    n = moe.moe_workspace_size(moe.MOE_VARIANT_MXFP4, T, H, F, E, k)
+    ws = torch.full((n,), 0x3C, dtype=torch.uint8, device="cuda")
+    for i, cap in enumerate((16, 0, 0)):
+        p = tm.mx_problem(T, H, F, E, k, seed=70 + i)
+        g = {n_: v.cuda() for n_, v in p.items()}
+        ref = run_mx("moe_experts_mxfp4", g)
+        moe.moe_set_grid_cap(cap)
+        try:
+            if i == 2:
+                moe.moe_profile_begin(1)
+            got = run_mx("moe_experts_mxfp4_fused", g, workspace=ws)
+            torch.cuda.synchronize()
+            if i == 2:
+                assert [s for s, _ in moe.moe_profile_end(1)[0]] == ["layer"]
+        finally:
+            moe.moe_set_grid_cap(0)
+        same_bits(got, ref, f"call {i}")
+
+
+def test_mx_layer_full_v3_prefill():
+    """T=4096 Zipf-routed expert share with MXFP4 weights: equal to the
+    stage-by-stage form."""
+    _say("one-launch MXFP4 layer, full v3_mxfp4_prefill")
+    p = wl.make_config("v3_mxfp4_prefill", device="cuda")
+    same_bits(run_mx("moe_experts_mxfp4_fused", p), run_mx("moe_experts_mxfp4", p), "v3_mxfp4_prefill")
