@@ -79,6 +79,9 @@ KERNEL_STAGES = [
     ("moe::augment_routing_kernel", "shared_route"),
     ("moe::route_kernel", "router"),
     ("moe::route_plan_kernel", "route_plan"),
+    ("moe::layer_bf16_kernel", "layer"),
+    ("moe::layer_fp8_kernel", "layer"),
+    ("moe::layer_mx_kernel", "layer"),
 ]
 
 
@@ -220,7 +223,7 @@ def stage_work(stage, kind, T, H, F, k, touched, valid):
         return dn_w, 2 * valid * H * F
     if stage == "combine":
         return out_bytes + route_bytes, 2 * valid * H
-    if stage == "decode":   # the whole layer in one launch
+    if stage in ("decode", "layer"):   # the whole layer in one launch
         return gu_w + dn_w + x_bytes + out_bytes + route_bytes, 2 * valid * 3 * F * H
     if stage == "shared_route":
         return route_bytes, 0
@@ -523,6 +526,13 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "stage_us": {st: round(float(np.mean(v)) * 1e3, 2) for st, v in per.items()}}
+            if "layer" in per:   # its roofline: the whole layer's work per launch
+                lms = float(np.mean(per["layer"]))
+                lb, lf = stage_work("layer", kind, T, H, F, k, touched, valid)
+                lroof = roofline_for("layer", kind, dtype, lb, lf, lms)
+                lroof["traffic"] = committed_traffic(name, "layer")
+                lroof["kernel_us"] = round(lms * 1e3, 2)
+                out["fused_layer"]["roofline"] = lroof
     ctx = (cfg, host_routes, warmup, problem)
     return out, ctx
 
