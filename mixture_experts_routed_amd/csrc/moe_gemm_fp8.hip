@@ -430,8 +430,8 @@ __global__ __launch_bounds__(kFp8Threads) void layer_fp8_kernel(
     // the routing plan, in the weight ring before its first use
     layer_plan((int*)&Fp8Ring<kFp8WM, 256, true>::b()[0][0][0], idx, (int)(T * k), E, kFp8TileM,
                counts, offsets, perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
-    // this call's queue of down items
-    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u64(sy.queue(), (uint64_t)(uint32_t)stamp << 32);
+    if (blockIdx.x == 0 && threadIdx.x < kXcds)   // this call's queues of down items
+        st_dev_u64(sy.queue(threadIdx.x), (uint64_t)(uint32_t)stamp << 32);
     const int ntiles = *ntiles_p;
     const int npg = F / 128, npd = H / 256;
     const int NG = ntiles * npg, ND = ntiles * npd;

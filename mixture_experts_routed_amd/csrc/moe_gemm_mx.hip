@@ -528,7 +528,8 @@ __global__ __launch_bounds__(kMxThreads) void layer_mx_kernel(
     // the routing plan, in the weight ring before its first use
     layer_plan((int*)&MxWideRing::b()[0][0][0], idx, (int)(T * k), E, kMxBM, counts, offsets,
                perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
-    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u64(sy.queue(), (uint64_t)(uint32_t)stamp << 32);
+    if (blockIdx.x == 0 && threadIdx.x < kXcds)   // this call's queues of down items
+        st_dev_u64(sy.queue(threadIdx.x), (uint64_t)(uint32_t)stamp << 32);
     const int ntiles = *ntiles_p;
     const int npg = F / 256, npd = H / 512;
     const int NG = ntiles * npg, ND = ntiles * npd;

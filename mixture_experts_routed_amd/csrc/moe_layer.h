@@ -160,8 +160,8 @@ struct LayerSync {
     uint64_t* base;
     __device__ uint64_t* gen() const { return base; }        // generation word
     __device__ uint64_t* err() const { return base + 1; }    // = stamp when a wait timed out
-    // dynamic down items: (stamp << 32) | items handed out
-    __device__ uint64_t* queue() const { return base + 2; }
+    // dynamic down items, one queue per XCD: (stamp << 32) | items handed out
+    __device__ uint64_t* queue(int x) const { return base + 2 + x; }
     __device__ uint64_t* ack() const { return base + 32; }   // [G] workgroup read the generation
     __device__ uint64_t* dflag() const { return base + 32 + kLayerMaxGrid; }   // [G] down items done
     // [kLayerPlanChunks] each: chunk counted / chunk scattered
@@ -209,11 +209,14 @@ __device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int str
 // the early items stay within the tiles of finished rounds.  Any order is
 // deadlock-free: down items wait only for gate_up items, and every
 // workgroup runs all its gate_up items first.
-// DYN (down phase): items are handed out in order from the queue word
-// instead, each workgroup claiming one item ahead (its claim for the next
-// item is issued before the current item's first loads, so its latency
-// hides behind theirs); workgroups that finish their gate_up items early
-// take more down items, whatever the items' lengths.
+// DYN (down phase): items are handed out in order from queue words instead,
+// each workgroup claiming one item ahead (its claim for the next item is
+// issued before the current item's first loads, so its latency hides
+// behind theirs); workgroups that finish their gate_up items early take
+// more down items, whatever the items' lengths.  One queue per XCD, over
+// blocks of 32 consecutive items (block c on XCD c mod 8, as the stand-alone
+// kernels map items), so that the items sharing an expert's weight panels
+// and h rows run under one L2.
 template <bool GATE, bool DYN = false>
 struct LayerSched {
     int items, NG, npg, c;   // npg: gate_up items per M tile
@@ -223,8 +226,14 @@ struct LayerSched {
     int k;
     int* claim;       // DYN: LDS word handing thread 0's claim to every wave
     uint32_t ahead;   // DYN: thread 0's claim for the next item
+    // the queue's k-th item
+    __device__ static uint32_t queue_item(uint32_t kq) {
+        const uint32_t x = blockIdx.x % kXcds;
+        return (kq / 32) * (32 * kXcds) + 32 * x + (kq % 32);
+    }
     __device__ uint32_t claim_one() const {
-        return (uint32_t)atomicAdd((unsigned long long*)sy.queue(), 1ull);
+        const uint32_t kq = (uint32_t)atomicAdd((unsigned long long*)sy.queue(blockIdx.x % kXcds), 1ull);
+        return queue_item(kq);
     }
     __device__ int take(uint32_t v) const {
         if (threadIdx.x == 0) *claim = (int)min(v, (uint32_t)items);
@@ -254,7 +263,7 @@ struct LayerSched {
                 // has set it (at its start)
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                 bool ok = true;
-                while ((uint32_t)(ld_dev_u64(sy.queue()) >> 32) != (uint32_t)stamp) {
+                while ((uint32_t)(ld_dev_u64(sy.queue(blockIdx.x % kXcds)) >> 32) != (uint32_t)stamp) {
                     if (__builtin_amdgcn_s_memrealtime() - t0 > kLayerSpinTicks) {
                         st_dev_u64(sy.err(), stamp);
                         ok = false;
