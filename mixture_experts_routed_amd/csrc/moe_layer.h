@@ -345,13 +345,6 @@ struct LayerSched {
     }
 };
 
-// sum over the 64 lanes of a wave
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // The routing plan as the layer's first phase, the same arrays as the plan
 // kernel's (the ordering rule fixes every entry): the first Gp = min(G,
 // kLayerPlanChunks) workgroups each take a contiguous chunk of slots,
@@ -407,33 +400,32 @@ __device__ __forceinline__ void layer_plan(int* ldsi, const int32_t* __restrict_
         if (tid == 0) st_dev_u64(sy.pcount() + b, stamp);
         wait_flags(sy.pcount(), Gp, 1, stamp, sy);
         // totals, and this chunk's base per expert (chunks before it, then
-        // the waves before each wave's run): lane c of a wave reads chunk c's
-        // count of an expert, and the wave sums them
-        {
-            constexpr int EB = 8;   // experts per batch of loads in flight
-            for (int e0 = wave * EB; e0 < E; e0 += NW * EB) {
-                int v[EB];
+        // the waves before each wave's run): a thread per expert reads the
+        // expert's row of chunk counts in 16-byte loads, all in flight
+        // (normal loads: no workgroup reads the counts before every chunk's
+        // flag, so no L2 holds an older copy)
+        for (int e = tid; e < E; e += blockDim.x) {
+            const uint4* row = (const uint4*)(sy.pcnt() + e * kLayerPlanChunks);
+            uint4 q[kLayerPlanChunks / 4];
 #pragma unroll
-                for (int j = 0; j < EB; ++j)
-                    v[j] = e0 + j < E && lane < Gp
-                               ? (int)__hip_atomic_load((const uint32_t*)(sy.pcnt() + (e0 + j) * kLayerPlanChunks + lane),
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : 0;
+            for (int i = 0; i < kLayerPlanChunks / 4; ++i) q[i] = row[i];
+            int t = 0, pre = 0;
 #pragma unroll
-                for (int j = 0; j < EB; ++j) {
-                    const int e = e0 + j;
-                    const int t = wave_sum_i32(v[j]);
-                    const int pre = wave_sum_i32(lane < b ? v[j] : 0);
-                    if (e < E && lane == 0) {
-                        tot[e] = t;
-                        int run_ = pre;
-                        for (int w = 0; w < NW; ++w) {
-                            const int cw = base[w * E + e];
-                            base[w * E + e] = run_;
-                            run_ += cw;
-                        }
-                    }
+            for (int i = 0; i < kLayerPlanChunks / 4; ++i) {
+                const int v4[4] = {(int)q[i].x, (int)q[i].y, (int)q[i].z, (int)q[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 4 * i + j;
+                    const int v = c < Gp ? v4[j] : 0;
+                    t += v;
+                    pre += c < b ? v : 0;
                 }
+            }
+            tot[e] = t;
+            for (int w = 0; w < NW; ++w) {
+                const int cw = base[w * E + e];
+                base[w * E + e] = pre;
+                pre += cw;
             }
         }
         lds_barrier();
