@@ -475,6 +475,8 @@ def measure(moe, torch, np, wl, name, steps, warmup, sets_arg=None, stage_pass=T
                 "us_per_call": round(ev0.elapsed_time(ev1) / steps * 1e3, 2),
                 "kernel_us_per_call": round(float(np.mean([sum(ms for _, ms in row) for row in calls])) * 1e3, 2),
                 "launches": len(calls[0]) if calls else 0}
+    # ------------------------------ pass E: the single-kernel form, if any
+    if stage_pass:
         fused_entry = None
         if kind == "bf16" and not decode and not S:
             fused_entry = "moe_experts_prefill_fused"
@@ -546,7 +548,11 @@ def summary_of(out):
             "dominant_kernel": r.get("kernel"), "dominant_kernel_us": r.get("kernel_us"),
             "roofline": {kk: r.get(kk) for kk in ("bound", "achieved", "peak", "unit", "frac")} if r else None,
             "stage_us": out.get("stage_us"),
-            **({"fused_layer_us_per_call": out["fused_layer"]["us_per_call"]} if "fused_layer" in out else {})}
+            **({"fused_layer": {"us_per_call": out["fused_layer"]["us_per_call"],
+                                "kernel_us": out["fused_layer"].get("roofline", {}).get("kernel_us"),
+                                "roofline_frac": out["fused_layer"].get("roofline", {}).get("frac"),
+                                "traffic": out["fused_layer"].get("roofline", {}).get("traffic")}}
+               if "fused_layer" in out else {})}
 
 
 def probe(moe, torch, np):
