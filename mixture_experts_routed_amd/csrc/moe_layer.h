@@ -216,7 +216,8 @@ __device__ __forceinline__ void wait_flags(const uint64_t* flags, int n, int str
 // more down items, whatever the items' lengths.  One queue per XCD, over
 // blocks of 32 consecutive items (block c on XCD c mod 8, as the stand-alone
 // kernels map items), so that the items sharing an expert's weight panels
-// and h rows run under one L2.
+// and h rows run under one L2; a workgroup whose queue has run dry takes
+// items from the next XCD's queue, so that the XCDs finish together.
 template <bool GATE, bool DYN = false>
 struct LayerSched {
     int items, NG, npg, c;   // npg: gate_up items per M tile
@@ -226,14 +227,44 @@ struct LayerSched {
     int k;
     int* claim;       // DYN: LDS word handing thread 0's claim to every wave
     uint32_t ahead;   // DYN: thread 0's claim for the next item
-    // the queue's k-th item
-    __device__ static uint32_t queue_item(uint32_t kq) {
-        const uint32_t x = blockIdx.x % kXcds;
-        return (kq / 32) * (32 * kXcds) + 32 * x + (kq % 32);
+    int qx = 0;       // DYN: the queue thread 0 takes items from
+    // the next item of queue x (0xffffffff when the queue word does not
+    // carry this call's stamp)
+    __device__ uint32_t claim_from(int x) const {
+        const uint64_t old = atomicAdd((unsigned long long*)sy.queue(x), 1ull);
+        if ((uint32_t)(old >> 32) != (uint32_t)stamp) return 0xffffffffu;
+        const uint32_t kq = (uint32_t)old;
+        return (kq / 32) * (32 * kXcds) + 32 * (uint32_t)x + (kq % 32);
     }
-    __device__ uint32_t claim_one() const {
-        const uint32_t kq = (uint32_t)atomicAdd((unsigned long long*)sy.queue(blockIdx.x % kXcds), 1ull);
-        return queue_item(kq);
+    __device__ uint32_t claim_one() const { return claim_from(qx); }
+    // items in queue x
+    __device__ uint32_t queue_len(int x) const {
+        const uint32_t full = (uint32_t)items / (32 * kXcds), rest = (uint32_t)items % (32 * kXcds);
+        return full * 32 + (uint32_t)min(max((int)rest - 32 * x, 0), 32);
+    }
+    // v, or, if v is past the end (queue qx has run dry), an item of the
+    // queue with the most items left (its words read at once; synchronous,
+    // only at the end of the phase)
+    __device__ uint32_t steal_if_dry(uint32_t v) {
+        while (v >= (uint32_t)items) {
+            uint64_t w[kXcds];
+#pragma unroll
+            for (int x = 0; x < kXcds; ++x) w[x] = ld_dev_u64(sy.queue(x));
+            int best = -1;
+            uint32_t most = 0;
+#pragma unroll
+            for (int x = 0; x < kXcds; ++x) {
+                const uint32_t kq = (uint32_t)w[x], n = queue_len(x);
+                if ((uint32_t)(w[x] >> 32) == (uint32_t)stamp && kq < n && n - kq > most) {
+                    most = n - kq;
+                    best = x;
+                }
+            }
+            if (best < 0) break;   // every queue is dry
+            qx = best;
+            v = claim_from(qx);
+        }
+        return v;
     }
     __device__ int take(uint32_t v) const {
         if (threadIdx.x == 0) *claim = (int)min(v, (uint32_t)items);
@@ -272,8 +303,9 @@ struct LayerSched {
                     __builtin_amdgcn_s_sleep(2);
                 }
                 if (ok) {
-                    v = claim_one();
-                    ahead = claim_one();
+                    qx = blockIdx.x % kXcds;
+                    v = steal_if_dry(claim_one());
+                    ahead = v < (uint32_t)items ? claim_one() : 0xffffffffu;
                 } else {
                     ahead = 0xffffffffu;
                 }
@@ -288,7 +320,7 @@ struct LayerSched {
         if (DYN) {
             uint32_t v = 0;
             if (threadIdx.x == 0) {
-                v = ahead;
+                v = ahead == 0xffffffffu ? ahead : steal_if_dry(ahead);
                 ahead = v < (uint32_t)items ? claim_one() : 0xffffffffu;
             }
             return take(v);
