@@ -70,10 +70,6 @@ __device__ __forceinline__ uint4 load_nt16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
 }
 
-__device__ __forceinline__ uint4 zero_unless(bool keep, uint4 v) {
-    return keep ? v : make_uint4(0, 0, 0, 0);
-}
-
 // Sum over the 64 lanes of each of the N = 2^n values v[0..N): afterwards
 // lane l holds the total of value l >> (6 - n).  Each halving step pairs
 // every lane with one whose lane bit b differs and trades half of the values
@@ -244,17 +240,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
 
     // ---------------------------------------------------------------- set-up
-    // the token rows (phase-1 waves) do not depend on the routing
+    // Request order: the routing (the first weight requests depend on it),
+    // the token rows, then the generation word, and nothing of them is used
+    // before all are requested, so the three round trips overlap.
+    // Given ids: every wave loads slot lane % 32 into its own lanes (no LDS
+    // staging, so the barrier below does not wait for these loads).  k
+    // counts the S shared slots of each token (experts E-S .. E-1, weight 1)
+    // after its k-S routed ones, read from idx / wts [T, k-S].
+    const int ls = lane & 31, kr = k - S, t_ls = ls / k, j_ls = ls - t_ls * k;
+    int e_raw = -1;
+    float w_raw = 0.0f;
+    if (!ROUTED && ls < P && j_ls < kr) {
+        e_raw = idx[t_ls * kr + j_ls];
+        w_raw = wts[t_ls * kr + j_ls];
+    }
+    // the token rows (phase-1 waves), through a buffer resource: chunks past
+    // a row's end and tokens past T read zeros (an offset beyond the bound)
+    // instead of being selected out, which would wait for the loads here
     uint4 xv[NT][NCH];
     const int nch = H / 8;
     if (wave < kDecUpWaves) {
+        const rsrc_t xr = make_rsrc(x, (uint32_t)(T * H * 2));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 const int c = lane + 64 * i;
                 const bool ok = t < T && c < nch;
-                xv[t][i] = zero_unless(ok, *(const uint4*)(x + (int64_t)min(t, T - 1) * H + min(c, nch - 1) * 8));
+                xv[t][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, ok ? (uint32_t)(t * H + c * 8) * 2 : 0x80000000u, 0, 0));
             }
     }
     // this call's generation, read once per workgroup at the start (every
@@ -279,22 +293,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
         }
     }
-    // Given ids: every wave loads slot lane % 32 into its own lanes (no LDS
-    // staging, so the barrier below does not wait for these loads).  k
-    // counts the S shared slots of each token (experts E-S .. E-1, weight 1)
-    // after its k-S routed ones, read from idx / wts [T, k-S].
     int e_l = -1;
     float w_l = 0.0f;
-    if (!ROUTED && (lane & 31) < P) {
-        const int ls = lane & 31;
-        const int kr = k - S, t = ls / k, j = ls - t * k;
-        e_l = E - S + (j - kr);
-        w_l = 1.0f;
-        if (j < kr) {
-            const int e = idx[t * kr + j];
-            e_l = (unsigned)e < (unsigned)(E - S) ? e : -1;
-            w_l = wts[t * kr + j];
-        }
+    if (!ROUTED && ls < P) {
+        e_l = j_ls < kr ? ((unsigned)e_raw < (unsigned)(E - S) ? e_raw : -1) : E - S + (j_ls - kr);
+        w_l = j_ls < kr ? w_raw : 1.0f;
     }
     if (tid == 0) {
         arrive = 0;
@@ -328,7 +331,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // polls the flags.  When every wave needs at most one step, the tasks are
     // spread over all seven (the down products are then short); otherwise
     // waves 5-7 take two steps each first and waves 0-3 split the rest.
-    const int c0 = (int)((int64_t)b * H / G), c1 = (int)((int64_t)(b + 1) * H / G);
+    // (32-bit quotients: b * H < 2^21 and b * N1 < 2^26 at the decode limits)
+    const int c0 = (int)((uint32_t)(b * H) / (uint32_t)G), c1 = (int)((uint32_t)((b + 1) * H) / (uint32_t)G);
     const int ntask_wg = (c1 - c0) * n_u;
     const int npre = min(ntask_wg, kDecDownWaves * 2 * DB);
     int ta = 0, tb = 0;
@@ -378,9 +382,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // of staging registers are never live together)
     if (wave < kDecUpWaves) {
         const int N1 = n_u * F;
-        const int p0 = (int)((int64_t)b * N1 / G), p1 = (int)((int64_t)(b + 1) * N1 / G);
-        const int q0 = p0 + (int)((int64_t)(p1 - p0) * wave / kDecUpWaves);
-        const int q1 = p0 + (int)((int64_t)(p1 - p0) * (wave + 1) / kDecUpWaves);
+        const int p0 = (int)((uint32_t)(b * N1) / (uint32_t)G), p1 = (int)((uint32_t)((b + 1) * N1) / (uint32_t)G);
+        const int q0 = p0 + (int)((uint32_t)((p1 - p0) * wave) / kDecUpWaves);
+        const int q1 = p0 + (int)((uint32_t)((p1 - p0) * (wave + 1)) / kDecUpWaves);
         const int nstep = (q1 - q0 + kPairBatch - 1) / kPairBatch;
         const int u0 = n_u > 0 ? q0 / F : 0, f0 = q0 - u0 * F;
         // pair q0 + i is (u, f): f0 + i carried into the following experts
