@@ -172,19 +172,45 @@ struct DecRouting {
     uint32_t repm;  // lane u < n_u: representative slots of u
 };
 
-// e / wsl: the expert (-1 dropped) and weight of slot lane % 32 (lanes of
-// slots >= P: -1, 0).
-__device__ __forceinline__ DecRouting dec_routing(const int e, const float wsl, int P, int k) {
+// The distinct experts of the routing, which is all the first weight
+// requests need.  e: the expert (-1 dropped) of slot lane % 32 (lanes of
+// slots >= P: -1).
+struct DecExperts {
+    int n_u;      // distinct experts, in order of first appearance
+    int u_s;      // this lane's slot: its distinct expert (-1 dropped)
+    int first;    // the first slot with this lane's expert
+    int ue;       // lane u < n_u: expert id of u (-1 otherwise)
+};
+__device__ __forceinline__ DecExperts dec_experts(const int e, int P) {
     const int lane = threadIdx.x & 63, ls = lane & 31;
-    DecRouting r;
+    DecExperts x;
     int first = ls;
     for (int q = 0; q < P; ++q) {
         const int eq = __builtin_amdgcn_readlane(e, q);
         if (q < first && eq == e) first = q;
     }
-    const uint32_t fm = (uint32_t)__ballot(e >= 0 && first == ls);   // first slots (lanes 0-31)
-    r.n_u = __popc(fm);
-    r.u_s = e >= 0 ? __popc(fm & ((1u << first) - 1u)) : -1;
+    uint32_t fm = (uint32_t)__ballot(e >= 0 && first == ls);   // first slots (lanes 0-31)
+    x.n_u = __popc(fm);
+    x.u_s = e >= 0 ? __popc(fm & ((1u << first) - 1u)) : -1;
+    x.first = first;
+    x.ue = -1;
+    for (int u = 0; fm; ++u) {   // u-th set bit of fm: the first slot of expert u
+        const int eq = __builtin_amdgcn_readlane(e, __builtin_ctz(fm));
+        fm &= fm - 1u;
+        if (lane == u) x.ue = eq;
+    }
+    return x;
+}
+
+// The rest of the routing, derived while the first weight requests are in
+// flight.  wsl: the weight of slot lane % 32 (lanes of slots >= P: 0).
+__device__ __forceinline__ DecRouting dec_routing(const int e, const float wsl, int P, int k,
+                                                  const DecExperts& x) {
+    const int lane = threadIdx.x & 63, ls = lane & 31;
+    DecRouting r;
+    r.n_u = x.n_u;
+    r.u_s = x.u_s;
+    r.ue = x.ue;
     r.t_s = ls / k;
     int rep = ls;
     float W = 0.0f;
@@ -198,15 +224,10 @@ __device__ __forceinline__ DecRouting dec_routing(const int e, const float wsl, 
     }
     r.rep = e >= 0 && rep == ls;
     r.W = W;
-    r.ue = -1;
     r.repm = 0u;
     for (int q = 0; q < r.n_u; ++q) {
         const uint32_t m = (uint32_t)__ballot(r.rep && r.u_s == q);
-        const int eq = __builtin_amdgcn_readlane(e, __builtin_ctz(m));
-        if (lane == q) {
-            r.repm = m;
-            r.ue = eq;
-        }
+        if (lane == q) r.repm = m;
     }
     return r;
 }
@@ -219,9 +240,9 @@ template <int NT, int NCH, int NCF, bool ROUTED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint16_t* __restrict__ x, const ExpertWeights w13, const ExpertWeights w2,
     const int32_t* __restrict__ idx, const float* __restrict__ wts,
-    const uint16_t* __restrict__ residual, int T, int k, int E, int H, int F,
+    const uint16_t* __restrict__ residual, int T, int k, int E, int H, int F, int S,
     uint16_t* __restrict__ out, DecodeWs ws, uint64_t spin_ticks,
-    const RouteArgs ra, int32_t* __restrict__ idx_out, float* __restrict__ w_out, int S) {
+    const RouteArgs ra, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
     constexpr int DB = 16 / NCF;                    // down rows per phase-2 step
     constexpr int kPairBatch = pair_batch<NT, NCH>();
     __shared__ u32x4 h_lds[kDecodeHBytes / 16];     // h rows [P][F], bf16
@@ -241,12 +262,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
     // ---------------------------------------------------------------- set-up
     // Request order: the routing (the first weight requests depend on it),
-    // the token rows, then the generation word, and nothing of them is used
-    // before all are requested, so the three round trips overlap.
+    // then the token rows, and neither is used before both are requested,
+    // so the two round trips overlap.
     // Given ids: every wave loads slot lane % 32 into its own lanes (no LDS
     // staging, so the barrier below does not wait for these loads).  k
     // counts the S shared slots of each token (experts E-S .. E-1, weight 1)
     // after its k-S routed ones, read from idx / wts [T, k-S].
+    // (the pointers these requests need come with the first scalar loads
+    // of the arguments, not one round trip later)
+    asm volatile("" ::"s"(idx), "s"(wts), "s"(x), "s"(S));
     const int ls = lane & 31, kr = k - S, t_ls = ls / k, j_ls = ls - t_ls * k;
     int e_raw = -1;
     float w_raw = 0.0f;
@@ -271,11 +295,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     xr, ok ? (uint32_t)(t * H + c * 8) * 2 : 0x80000000u, 0, 0));
             }
     }
-    // this call's generation, read once per workgroup at the start (every
-    // workgroup reads it before its flag goes out, and workgroup 0 advances
-    // it only after seeing every flag)
+    // this call's generation (read by the poll wave after its first weight
+    // requests; every workgroup reads it before its flag goes out, and
+    // workgroup 0 advances it only after seeing every flag)
     uint64_t gen = 0;
-    if (wave == kDecPollWave) gen = ld_dev_u64(ws.gen);
+    // the weight arguments: loaded now, while the routing is in flight (the
+    // compiler would otherwise load them next to their first use, the first
+    // weight requests, and wait for them there)
+    asm volatile("" ::"s"(w13.base), "s"(w13.shared), "s"(w13.n_routed), "s"(w2.base), "s"(w2.shared),
+                 "s"(w2.n_routed));
     if (ROUTED) {
         if (wave < T) {
             int id;
@@ -309,21 +337,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         e_l = slot_e[lane & 31];
         w_l = slot_w[lane & 31];
     }
-    const DecRouting R = dec_routing(e_l, w_l, P, k);
-    const int n_u = R.n_u;
-    // lane u < n_u: the representative slot of (u, token t), -1 if none
+    const DecExperts X = dec_experts(e_l, P);
+    const int n_u = X.n_u;
+    // The rest of the routing and the tables of the products, once a wave's
+    // first weight requests are out: the representatives, their weights,
+    // lane u < n_u: the representative slot of (u, token t) (-1 if none).
+    DecRouting R;
     int rep_of[NT];
+    auto finish_routing = [&]() {
+        R = dec_routing(e_l, w_l, P, k, X);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const uint32_t tm = t < T ? R.repm & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
-        rep_of[t] = tm ? __builtin_ctz(tm) : -1;
-    }
-    if (tid < kDecodeMaxSlots * kDecodeMaxT) {   // waves 0-1
-        const int u = tid / kDecodeMaxT, t = tid % kDecodeMaxT;
-        const uint32_t m = (uint32_t)__shfl(R.repm, u, kWave);
-        const uint32_t tm = t < T ? m & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
-        rep_tab[u][t] = u < n_u && tm ? __builtin_ctz(tm) : -1;
-    }
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t tm = t < T ? R.repm & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
+            rep_of[t] = tm ? __builtin_ctz(tm) : -1;
+        }
+        if (tid < kDecodeMaxSlots * kDecodeMaxT) {   // waves 0-1
+            const int u = tid / kDecodeMaxT, t = tid % kDecodeMaxT;
+            const uint32_t m = (uint32_t)__shfl(R.repm, u, kWave);
+            const uint32_t tm = t < T ? m & (uint32_t)(((1ull << k) - 1ull) << (t * k)) : 0u;
+            rep_tab[u][t] = u < n_u && tm ? __builtin_ctz(tm) : -1;
+        }
+    };
 
     // Phase-2 tasks (row r of [c0, c1), expert u), u fastest, in contiguous
     // ranges.  Waves 5, 6, 7 fetch their rows at kernel start and hold them
@@ -332,26 +366,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // spread over all seven (the down products are then short); otherwise
     // waves 5-7 take two steps each first and waves 0-3 split the rest.
     // (32-bit quotients: b * H < 2^21 and b * N1 < 2^26 at the decode limits)
-    const int c0 = (int)((uint32_t)(b * H) / (uint32_t)G), c1 = (int)((uint32_t)((b + 1) * H) / (uint32_t)G);
-    const int ntask_wg = (c1 - c0) * n_u;
-    const int npre = min(ntask_wg, kDecDownWaves * 2 * DB);
-    int ta = 0, tb = 0;
-    if (ntask_wg <= kDecP2Waves * DB) {
-        if (wave != kDecPollWave) {
-            const int q = wave < kDecPollWave ? wave : wave - 1;   // 0..6
-            ta = ntask_wg * q / kDecP2Waves;
-            tb = ntask_wg * (q + 1) / kDecP2Waves;
+    // (worked out by each wave where it first needs them: the gate/up
+    // waves after their first weight requests)
+    int c0 = 0, c1 = 0, ta = 0, ntask = 0;
+    auto down_tasks = [&]() {
+        c0 = (int)((uint32_t)(b * H) / (uint32_t)G);
+        c1 = (int)((uint32_t)((b + 1) * H) / (uint32_t)G);
+        const int ntask_wg = (c1 - c0) * n_u;
+        const int npre = min(ntask_wg, kDecDownWaves * 2 * DB);
+        int tb = 0;
+        if (ntask_wg <= kDecP2Waves * DB) {
+            if (wave != kDecPollWave) {
+                const int q = wave < kDecPollWave ? wave : wave - 1;   // 0..6
+                ta = ntask_wg * q / kDecP2Waves;
+                tb = ntask_wg * (q + 1) / kDecP2Waves;
+            }
+        } else if (wave >= kDecUpWaves) {
+            const int q = wave - kDecUpWaves;
+            ta = npre * q / kDecDownWaves;
+            tb = npre * (q + 1) / kDecDownWaves;
+        } else if (wave != kDecPollWave) {
+            const int rest = ntask_wg - npre;
+            ta = npre + rest * wave / kDecPollWave;
+            tb = npre + rest * (wave + 1) / kDecPollWave;
         }
-    } else if (wave >= kDecUpWaves) {
-        const int q = wave - kDecUpWaves;
-        ta = npre * q / kDecDownWaves;
-        tb = npre * (q + 1) / kDecDownWaves;
-    } else if (wave != kDecPollWave) {
-        const int rest = ntask_wg - npre;
-        ta = npre + rest * wave / kDecPollWave;
-        tb = npre + rest * (wave + 1) / kDecPollWave;
-    }
-    const int ntask = tb - ta;
+        ntask = tb - ta;
+    };
     const int nchf = F / 8;
     uint4 da[DB][NCF], db[DB][NCF];
     auto load_down = [&](uint4 (&buf)[DB][NCF], int step) {
@@ -361,7 +401,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         for (int i = 0; i < DB; ++i) {
             const bool real = step * DB + i < ntask;
             // a task past the end reads through an empty resource (zeros)
-            const rsrc_t m = make_rsrc(w2.expert(__builtin_amdgcn_readlane(R.ue, real ? u : 0), (int64_t)H * F),
+            const rsrc_t m = make_rsrc(w2.expert(__builtin_amdgcn_readlane(X.ue, real ? u : 0), (int64_t)H * F),
                                        real ? (uint32_t)H * F * 2 : 0u);
             const uint32_t row = (uint32_t)(c0 + rr) * F;
 #pragma unroll
@@ -405,7 +445,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 int u, f;
                 pair_uf(real ? i : 0, u, f);
                 // a pair past the end reads through an empty resource (zeros)
-                const rsrc_t m = make_rsrc(w13.expert(__builtin_amdgcn_readlane(R.ue, u), (int64_t)2 * F * H),
+                const rsrc_t m = make_rsrc(w13.expert(__builtin_amdgcn_readlane(X.ue, u), (int64_t)2 * F * H),
                                            real ? (uint32_t)F * H * 4 : 0u);
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
@@ -461,6 +501,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         // (the conditions are wave-uniform)
         if (nstep > 0) load_pairs(wa, 0);
         if (nstep > 1) load_pairs(wb, 1);
+        finish_routing();
+        down_tasks();
+        if (wave == kDecPollWave) gen = ld_dev_u64(ws.gen);
         for (int st = 0; st < nstep; st += 2) {
             compute_pairs(wa, st);
             if (st + 2 < nstep) load_pairs(wa, st + 2);
@@ -474,7 +517,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             // workgroup's, then wait for every workgroup's
             while (__hip_atomic_load(&arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kDecUpWaves)
                 __builtin_amdgcn_s_sleep(1);
-            const uint64_t stamp = gen + 1;
+            // (gen enters arithmetic only here: computed where it was loaded,
+            // the wave would wait there for every load before it)
+            uint64_t g = gen;
+            asm volatile("" : "+v"(g));
+            const uint64_t stamp = g + 1;
             if (lane == 0) st_dev_u64(ws.flags + b, stamp);
             bool ok = false;
             while (true) {
@@ -503,9 +550,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             load_down(da, 0);
             if (ntask > DB) load_down(db, 1);
         }
-    } else if (ntask > 0) {
-        load_down(da, 0);
-        if (ntask > DB) load_down(db, 1);
+    } else {
+        down_tasks();
+        if (ntask > 0) {
+            load_down(da, 0);
+            if (ntask > DB) load_down(db, 1);
+        }
+        finish_routing();
     }
 
     // --------------------------------------------------------------- phase 2
@@ -609,8 +660,10 @@ static void launch_one(const uint16_t* x, const ExpertWeights& w13, const Expert
                        const RouteArgs& ra, int32_t* io, float* wo, int S) {
     // at most kDecodeMaxRows output rows per workgroup
     const int G = std::max(decode_grid<NT, NCH, NCF, ROUTED>(), (H + kDecodeMaxRows - 1) / kDecodeMaxRows);
-    MOE_LAUNCH((decode_kernel<NT, NCH, NCF, ROUTED>), dim3(G), dim3(kDecThreads), 0, s, x, w13, w2, idx, w, residual, T, k, E, H, F, out, dws,
-               kSpinTicks, ra, io, wo, S);
+    // (the arguments the first requests need, S included, lie in the first
+    // 128 bytes of the argument block: one scalar round trip fetches them)
+    MOE_LAUNCH((decode_kernel<NT, NCH, NCF, ROUTED>), dim3(G), dim3(kDecThreads), 0, s, x, w13, w2, idx, w, residual, T, k, E, H, F, S,
+               out, dws, kSpinTicks, ra, io, wo);
 }
 
 template <int NT, int NCH, bool ROUTED>
