@@ -13,9 +13,10 @@
 //    (expert, token)'s representative slot, with device-scope stores (W is
 //    the summed routing weight of the token's slots on u);
 //  - hand-off: once all five waves' stores have completed, wave 4 stores
-//    the workgroup's flag (a 64-bit stamp) and polls the flags of the whole
-//    grid (bounded by a clock limit), then copies all of h into LDS with
-//    device-scope loads and raises an LDS flag.  The stamp comes from a
+//    the workgroup's flag (a 64-bit word made from the call's stamp) and
+//    polls the flags of the whole grid (bounded by a clock limit), then
+//    copies all of h into LDS with device-scope loads and raises an LDS
+//    flag.  The stamp comes from a
 //    generation word that workgroup 0 advances once every flag is seen, so
 //    consecutive calls (also replays of a captured graph) never match an old
 //    flag;
@@ -146,6 +147,20 @@ __device__ __forceinline__ float dot8_bf16(const uint4 a, const uint4 b, float a
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
     return acc;
+}
+
+// The flag word of a call's stamp: the splitmix64 finaliser of the stamp.
+// It is a bijection, so consecutive stamps (the generation word counts up by
+// one per call) never share a flag word; and the small integers another
+// entry point leaves in a shared workspace (counts, offsets) cannot pass for
+// one the way the stamp itself could: after a grouped call whose routing
+// gives experts 0, 1, 2 the counts 0, 1, 0, the word at the generation's
+// offset plus one equals the second flag word its offsets left behind.
+__device__ __forceinline__ uint64_t flag_word(uint64_t stamp) {
+    uint64_t z = stamp;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
 }
 
 // Workspace of the gather-GEMV form (all offsets fixed, see decode_ws_bytes).
@@ -522,11 +537,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             uint64_t g = gen;
             asm volatile("" : "+v"(g));
             const uint64_t stamp = g + 1;
-            if (lane == 0) st_dev_u64(ws.flags + b, stamp);
+            const uint64_t flag = flag_word(stamp);
+            if (lane == 0) st_dev_u64(ws.flags + b, flag);
             bool ok = false;
             while (true) {
                 bool all = true;
-                for (int q = lane; q < G; q += 64) all &= ld_dev_u64(ws.flags + q) == stamp;
+                for (int q = lane; q < G; q += 64) all &= ld_dev_u64(ws.flags + q) == flag;
                 if (__all(all)) {
                     ok = true;
                     break;

@@ -239,6 +239,44 @@ def test_decode_dropped_slots_with_stale_workspace(T):
     check_tol(out, ref, BF16_TOL, f"dropped slots T={T}")
 
 
+def test_decode_after_grouped_call_on_one_workspace():
+    """A decode call on a workspace a grouped call has just used, whose
+    routing gives experts 0, 1, 2 the counts 0, 1, 0 (64 experts): the plan
+    then leaves, at the decode's generation word, counts 0 and 1, and at the
+    decode's second flag word the offsets 1 and 1, i.e. the generation word
+    plus one.  The decode's flag words must not take that for a flag of this
+    call; its output equals, bit for bit, the same decode on a fresh
+    workspace, and matches the oracle."""
+    moe = _moe()
+    H, F, E, k, Tg = 1280, 896, 64, 6, 16
+    _say("decode after a grouped call on one workspace (counts 0, 1, 0)")
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(np.arange(3, E), size=k, replace=False) for _ in range(Tg)])
+    idx[0, 0] = 1
+    pg = bf16_problem(Tg, H, F, E, k, seed=73, idx=idx)
+    gg = to_gpu(pg)
+    lay = moe.moe_workspace_layout(0, Tg, H, F, E, k)
+    assert lay["counts"] == 0 and lay["offsets"] == 256, lay   # counts at 0, offsets at 256
+    n = max(moe.moe_workspace_size(0, Tg, H, F, E, k), moe.moe_workspace_size(1, 1, H, F, E, k))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    moe.moe_experts_prefill(gg["hidden"], gg["gate_up"], gg["down"], gg["top_k_index"],
+                            gg["top_k_weights"], k, workspace=ws)
+    torch.cuda.synchronize()
+    head = ws[:512].cpu().view(torch.int32).numpy()
+    assert list(head[:3]) == [0, 1, 0] and list(head[66:68]) == [1, 1], (head[:3], head[64:68])
+    # the decode: one token of the same layer, routed to experts 1 .. 6
+    pd = {"hidden": pg["hidden"][:1].clone(), "gate_up": pg["gate_up"], "down": pg["down"],
+          "top_k_index": torch.arange(1, k + 1, dtype=torch.int32).view(1, k),
+          "top_k_weights": torch.softmax(torch.linspace(-1, 1, k), 0).view(1, k).float()}
+    gd = to_gpu(pd)
+    args = (gd["hidden"], gd["gate_up"], gd["down"], gd["top_k_index"], gd["top_k_weights"], k)
+    out = moe.moe_experts_decode(*args, workspace=ws)
+    fresh = moe.moe_experts_decode(*args, workspace=torch.zeros_like(ws))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fresh.view(torch.int16))
+    check_tol(out, bf16_ref(pd, batched=False), BF16_TOL, "decode after grouped call")
+
+
 @pytest.mark.parametrize("T", [1, 2, 4])
 def test_decode_repeated_expert_in_token(T):
     """Gather-GEMV path with a token that lists one expert in several slots
