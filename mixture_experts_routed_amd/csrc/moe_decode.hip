@@ -540,15 +540,48 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const uint64_t flag = flag_word(stamp);
             if (lane == 0) st_dev_u64(ws.flags + b, flag);
             bool ok = false;
-            while (true) {
-                bool all = true;
-                for (int q = lane; q < G; q += 64) all &= ld_dev_u64(ws.flags + q) == flag;
-                if (__all(all)) {
-                    ok = true;
-                    break;
+            if (G <= 4 * kWave) {
+                // two polls in flight, each read while the other's loads are
+                // out, so the last flag to land is seen about half a round
+                // trip sooner than by polls one after the other
+                uint64_t pa[4], pb[4];
+                auto issue = [&](uint64_t (&f)[4]) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f[i] = ld_dev_u64(ws.flags + min(lane + kWave * i, G - 1));
+                };
+                auto seen = [&](const uint64_t (&f)[4]) {
+                    bool all = true;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) all &= f[i] == flag;
+                    return __all(all);
+                };
+                issue(pa);
+                __builtin_amdgcn_s_sleep(8);
+                issue(pb);
+                while (true) {
+                    if (seen(pa)) {
+                        ok = true;
+                        break;
+                    }
+                    issue(pa);
+                    if (seen(pb)) {
+                        ok = true;
+                        break;
+                    }
+                    issue(pb);
+                    if (__builtin_amdgcn_s_memrealtime() - t_start > spin_ticks) break;
                 }
-                if (__builtin_amdgcn_s_memrealtime() - t_start > spin_ticks) break;
-                __builtin_amdgcn_s_sleep(1);
+            } else {
+                while (true) {
+                    bool all = true;
+                    for (int q = lane; q < G; q += 64) all &= ld_dev_u64(ws.flags + q) == flag;
+                    if (__all(all)) {
+                        ok = true;
+                        break;
+                    }
+                    if (__builtin_amdgcn_s_memrealtime() - t_start > spin_ticks) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
             }
             if (!ok && lane == 0) {
                 timed_out = 1;

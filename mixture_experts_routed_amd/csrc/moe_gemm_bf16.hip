@@ -367,10 +367,9 @@ __global__ __launch_bounds__(kGemmThreads) void layer_bf16_kernel(
     LayerSync sy) {
     constexpr int BNMAX = BNG > BND ? BNG : BND;
     __shared__ u32x4 lds[kAStages * kBM * 8 + kBStages * BNMAX * 8];
-    const uint64_t stamp = layer_stamp(sy);
     // the routing plan, in the operand ring before its first use
-    layer_plan((int*)lds, idx, (int)(T * k), E, kBM, counts, offsets, perm, inv, tiles, ntiles_p,
-               tile_off, stamp, sy);
+    const uint64_t stamp = layer_plan((int*)lds, idx, (int)(T * k), E, kBM, counts, offsets, perm,
+                                      inv, tiles, ntiles_p, tile_off, layer_gen(sy), sy);
     const int ntiles = *ntiles_p;
     const int npg = F / (BNG / 2), npd = H / BND;
     const int NG = ntiles * npg;

@@ -434,10 +434,10 @@ __global__ __launch_bounds__(kFp8Threads) void layer_fp8_kernel(
     int F, int k, uint8_t* __restrict__ hq, float* __restrict__ hs, uint16_t* __restrict__ y,
     uint16_t* __restrict__ out, LayerSync sy) {
     __shared__ int claim;
-    const uint64_t stamp = layer_stamp(sy);
     // the routing plan, in the weight ring before its first use
-    layer_plan((int*)&Fp8Ring<kFp8WM, 256, true>::b()[0][0][0], idx, (int)(T * k), E, kFp8TileM,
-               counts, offsets, perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
+    const uint64_t stamp =
+        layer_plan((int*)&Fp8Ring<kFp8WM, 256, true>::b()[0][0][0], idx, (int)(T * k), E, kFp8TileM,
+                   counts, offsets, perm, inv, tiles, ntiles_p, tile_off, layer_gen(sy), sy);
     if (blockIdx.x == 0 && threadIdx.x < kXcds)   // this call's queues of down items
         st_dev_u64(sy.queue(threadIdx.x), (uint64_t)(uint32_t)stamp << 32);
     const int ntiles = *ntiles_p;

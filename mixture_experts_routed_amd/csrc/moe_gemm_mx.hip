@@ -524,10 +524,10 @@ __global__ __launch_bounds__(kMxThreads) void layer_mx_kernel(
     int F, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, uint16_t* __restrict__ y,
     uint16_t* __restrict__ out, LayerSync sy) {
     __shared__ int claim;
-    const uint64_t stamp = layer_stamp(sy);
     // the routing plan, in the weight ring before its first use
-    layer_plan((int*)&MxWideRing::b()[0][0][0], idx, (int)(T * k), E, kMxBM, counts, offsets,
-               perm, inv, tiles, ntiles_p, tile_off, stamp, sy);
+    const uint64_t stamp = layer_plan((int*)&MxWideRing::b()[0][0][0], idx, (int)(T * k), E, kMxBM,
+                                      counts, offsets, perm, inv, tiles, ntiles_p, tile_off,
+                                      layer_gen(sy), sy);
     if (blockIdx.x == 0 && threadIdx.x < kXcds)   // this call's queues of down items
         st_dev_u64(sy.queue(threadIdx.x), (uint64_t)(uint32_t)stamp << 32);
     const int ntiles = *ntiles_p;

@@ -377,6 +377,26 @@ struct LayerSched {
     }
 };
 
+// This call's generation word, requested by wave 0 and not waited for
+// here: the plan's first loads go out before the wait, so the two round
+// trips overlap.
+__device__ __forceinline__ uint64_t layer_gen(LayerSync sy) {
+    return threadIdx.x < 64 ? ld_dev_u64(sy.gen()) : 0ull;
+}
+// This call's stamp (the generation word + 1) from layer_gen's value, kept
+// in scalar registers (the other waves hold 0 and never use it); the
+// workgroup's acknowledgement that it has read the word.
+__device__ __forceinline__ uint64_t layer_stamp(uint64_t g, LayerSync sy) {
+    uint64_t stamp = 0;
+    if (threadIdx.x < 64) {
+        asm volatile("" : "+v"(g));   // the load is waited for here, not at its issue
+        stamp = g + 1;
+        if (threadIdx.x == 0) st_dev_u64(sy.ack() + blockIdx.x, stamp);
+    }
+    return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(stamp >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((uint32_t)stamp);
+}
+
 // The routing plan as the layer's first phase, the same arrays as the plan
 // kernel's (the ordering rule fixes every entry): the first Gp = min(G,
 // kLayerPlanChunks) workgroups each take a contiguous chunk of slots,
@@ -389,19 +409,21 @@ struct LayerSched {
 //  3. workgroup 0 writes counts, offsets, the tiles and their prefix.
 // Every workgroup then waits until every chunk is scattered.  All plan
 // stores are device-scope; the arrays are first read after that wait.
-// `ldsi`: 56 KB of idle LDS.
-__device__ __forceinline__ void layer_plan(int* ldsi, const int32_t* __restrict__ idx, int P,
+// `ldsi`: 56 KB of idle LDS; `gen`: layer_gen's value.  Returns the call's
+// stamp (layer_stamp).
+__device__ __forceinline__ uint64_t layer_plan(int* ldsi, const int32_t* __restrict__ idx, int P,
                                            int E, int tile_m, int32_t* __restrict__ counts,
                                            int32_t* __restrict__ offsets,
                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                            int32_t* __restrict__ tiles,
                                            int32_t* __restrict__ ntiles,
-                                           int32_t* __restrict__ tile_off, uint64_t stamp,
+                                           int32_t* __restrict__ tile_off, uint64_t gen,
                                            LayerSync sy) {
     constexpr int NW = 8;   // waves of a 512-thread workgroup
     const int G = gridDim.x, b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Gp = min(G, kLayerPlanChunks);
+    uint64_t stamp = 0;
     if (b < Gp) {
         int* base = ldsi;                                               // [NW][E]
         unsigned long long* lanes_of = (unsigned long long*)(ldsi + NW * MOE_MAX_EXPERTS);  // [NW][E]
@@ -427,6 +449,7 @@ __device__ __forceinline__ void layer_plan(int* ldsi, const int32_t* __restrict_
             for (int w = 0; w < NW; ++w) acc += base[w * E + e];
             st_dev_u32((uint32_t*)(sy.pcnt() + e * kLayerPlanChunks + b), (uint32_t)acc);
         }
+        stamp = layer_stamp(gen, sy);
         wait_vm_all();
         lds_barrier();
         if (tid == 0) st_dev_u64(sy.pcount() + b, stamp);
@@ -542,21 +565,11 @@ __device__ __forceinline__ void layer_plan(int* ldsi, const int32_t* __restrict_
         wait_vm_all();
         lds_barrier();
         if (tid == 0) st_dev_u64(sy.pdone() + b, stamp);
+    } else {
+        stamp = layer_stamp(gen, sy);
     }
     wait_flags(sy.pdone(), Gp, 1, stamp, sy);
-}
-
-// This call's stamp (the generation word + 1), read by wave 0 and kept in
-// scalar registers (the other waves hold 0 and never use it); the
-// workgroup's acknowledgement that it has read the word.
-__device__ __forceinline__ uint64_t layer_stamp(LayerSync sy) {
-    uint64_t stamp = 0;
-    if (threadIdx.x < 64) {
-        stamp = ld_dev_u64(sy.gen()) + 1;
-        if (threadIdx.x == 0) st_dev_u64(sy.ack() + blockIdx.x, stamp);
-    }
-    return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(stamp >> 32)) << 32) |
-           __builtin_amdgcn_readfirstlane((uint32_t)stamp);
+    return stamp;
 }
 
 // c of LayerSched: how many down items a slot with one gate_up item fewer
