@@ -6,7 +6,8 @@
 //
 // One workgroup per compute unit (all resident), 8 waves:
 //  - phase 1 (waves 0-4): the (distinct selected expert u, f) pairs, n_u * F
-//    of them, are split evenly over the grid.  A wave streams the gate row f
+//    of them, are split evenly over the workgroups (wave 4, which also
+//    polls, takes a smaller share of its workgroup's).  A wave streams the gate row f
 //    and the up row F + f of expert u (each byte read once, two steps of
 //    rows in flight), dots them with every token that chose u and stores
 //    W * silu(gate . x) * (up . x) as bf16 into the workspace row of the
@@ -44,6 +45,8 @@ constexpr int kDecUpWaves = 5;                    // waves 0-4: gate/up rows and
 constexpr int kDecDownWaves = 8 - kDecUpWaves;    // waves 5-7: down rows from kernel start
 constexpr int kDecPollWave = kDecUpWaves - 1;     // wave 4: the hand-off
 constexpr int kDecP2Waves = 7;                    // waves with down-phase tasks
+constexpr int kDecUpShare = 3;                    // phase-1 share of waves 0-3 ...
+constexpr int kDecUpTotal = 4 * kDecUpShare + 2;  // ... and of wave 4 (2), out of 14
 // gate/up row pairs per wave step (two steps in flight): three for one token
 // and H <= 1536, otherwise two (the token rows take more registers)
 template <int NT, int NCH>
@@ -438,8 +441,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (wave < kDecUpWaves) {
         const int N1 = n_u * F;
         const int p0 = (int)((uint32_t)(b * N1) / (uint32_t)G), p1 = (int)((uint32_t)((b + 1) * N1) / (uint32_t)G);
-        const int q0 = p0 + (int)((uint32_t)((p1 - p0) * wave) / kDecUpWaves);
-        const int q1 = p0 + (int)((uint32_t)((p1 - p0) * (wave + 1)) / kDecUpWaves);
+        // shares 3, 3, 3, 3, 2 (of 14): wave 4 shares a SIMD with wave 0, so
+        // it issues only in wave 0's idle slots and sends its first requests
+        // behind those of the other seven waves; with an even share it ended
+        // phase 1 last in every workgroup (T=4: 27 us against 21.5 us)
+        const int cq0 = kDecUpShare * wave, cq1 = wave + 1 < kDecUpWaves ? cq0 + kDecUpShare : kDecUpTotal;
+        const int q0 = p0 + (int)((uint32_t)((p1 - p0) * cq0) / kDecUpTotal);
+        const int q1 = p0 + (int)((uint32_t)((p1 - p0) * cq1) / kDecUpTotal);
         const int nstep = (q1 - q0 + kPairBatch - 1) / kPairBatch;
         const int u0 = n_u > 0 ? q0 / F : 0, f0 = q0 - u0 * F;
         // pair q0 + i is (u, f): f0 + i carried into the following experts
