@@ -7,20 +7,19 @@
 // One workgroup per compute unit (all resident), 8 waves:
 //  - phase 1 (waves 0-4): the (distinct selected expert u, f) pairs, n_u * F
 //    of them, are split evenly over the workgroups (wave 4, which also
-//    polls, takes a smaller share of its workgroup's).  A wave streams the gate row f
-//    and the up row F + f of expert u (each byte read once, two steps of
-//    rows in flight), dots them with every token that chose u and stores
-//    W * silu(gate . x) * (up . x) as bf16 into the workspace row of the
-//    (expert, token)'s representative slot, with device-scope stores (W is
-//    the summed routing weight of the token's slots on u);
+//    polls, takes a smaller share of its workgroup's).  A wave streams the
+//    gate row f and the up row F + f of expert u (each byte read once, two
+//    steps of rows in flight), dots them with every token that chose u and
+//    stores W * silu(gate . x) * (up . x) as bf16 into the workspace row of
+//    the (expert, token)'s representative slot, with device-scope stores (W
+//    is the summed routing weight of the token's slots on u);
 //  - hand-off: once all five waves' stores have completed, wave 4 stores
 //    the workgroup's flag (a 64-bit word made from the call's stamp) and
 //    polls the flags of the whole grid (bounded by a clock limit), then
 //    copies all of h into LDS with device-scope loads and raises an LDS
-//    flag.  The stamp comes from a
-//    generation word that workgroup 0 advances once every flag is seen, so
-//    consecutive calls (also replays of a captured graph) never match an old
-//    flag;
+//    flag.  The stamp comes from a generation word that workgroup 0
+//    advances once every flag is seen, so consecutive calls (also replays of
+//    a captured graph) never match an old flag;
 //  - phase 2: the H output rows are split evenly over the grid, and a
 //    workgroup's (row, expert) tasks over waves 0-3 and 5-7.  Waves 5-7
 //    request their down rows at kernel start and hold them in registers;
@@ -196,7 +195,6 @@ struct DecRouting {
 struct DecExperts {
     int n_u;      // distinct experts, in order of first appearance
     int u_s;      // this lane's slot: its distinct expert (-1 dropped)
-    int first;    // the first slot with this lane's expert
     int ue;       // lane u < n_u: expert id of u (-1 otherwise)
 };
 __device__ __forceinline__ DecExperts dec_experts(const int e, int P) {
@@ -210,7 +208,6 @@ __device__ __forceinline__ DecExperts dec_experts(const int e, int P) {
     uint32_t fm = (uint32_t)__ballot(e >= 0 && first == ls);   // first slots (lanes 0-31)
     x.n_u = __popc(fm);
     x.u_s = e >= 0 ? __popc(fm & ((1u << first) - 1u)) : -1;
-    x.first = first;
     x.ue = -1;
     for (int u = 0; fm; ++u) {   // u-th set bit of fm: the first slot of expert u
         const int eq = __builtin_amdgcn_readlane(e, __builtin_ctz(fm));

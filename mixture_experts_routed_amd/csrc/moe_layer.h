@@ -412,13 +412,14 @@ __device__ __forceinline__ uint64_t layer_stamp(uint64_t g, LayerSync sy) {
 // `ldsi`: 56 KB of idle LDS; `gen`: layer_gen's value.  Returns the call's
 // stamp (layer_stamp).
 __device__ __forceinline__ uint64_t layer_plan(int* ldsi, const int32_t* __restrict__ idx, int P,
-                                           int E, int tile_m, int32_t* __restrict__ counts,
-                                           int32_t* __restrict__ offsets,
-                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                           int32_t* __restrict__ tiles,
-                                           int32_t* __restrict__ ntiles,
-                                           int32_t* __restrict__ tile_off, uint64_t gen,
-                                           LayerSync sy) {
+                                               int E, int tile_m, int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ perm,
+                                               int32_t* __restrict__ inv,
+                                               int32_t* __restrict__ tiles,
+                                               int32_t* __restrict__ ntiles,
+                                               int32_t* __restrict__ tile_off, uint64_t gen,
+                                               LayerSync sy) {
     constexpr int NW = 8;   // waves of a 512-thread workgroup
     const int G = gridDim.x, b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
