@@ -377,9 +377,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // Phase-2 tasks (row r of [c0, c1), expert u), u fastest, in contiguous
     // ranges.  Waves 5, 6, 7 fetch their rows at kernel start and hold them
     // in registers; waves 0-3 fetch theirs after their gate/up work; wave 4
-    // polls the flags.  When every wave needs at most one step, the tasks are
-    // spread over all seven (the down products are then short); otherwise
-    // waves 5-7 take two steps each first and waves 0-3 split the rest.
+    // polls the flags.  When every wave needs at most one step, the tasks go
+    // out in whole steps of DB rows, waves 5-7 first, then waves 0-3 (a
+    // step's rows past the end would still be loaded and multiplied);
+    // otherwise waves 5-7 take two steps each first and waves 0-3 split the
+    // rest.
     // (32-bit quotients: b * H < 2^21 and b * N1 < 2^26 at the decode limits)
     // (worked out by each wave where it first needs them: the gate/up
     // waves after their first weight requests)
@@ -392,9 +394,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         int tb = 0;
         if (ntask_wg <= kDecP2Waves * DB) {
             if (wave != kDecPollWave) {
-                const int q = wave < kDecPollWave ? wave : wave - 1;   // 0..6
-                ta = ntask_wg * q / kDecP2Waves;
-                tb = ntask_wg * (q + 1) / kDecP2Waves;
+                const int q = wave >= kDecUpWaves ? wave - kDecUpWaves : wave + kDecDownWaves;   // 0..6
+                ta = min(q * DB, ntask_wg);
+                tb = min((q + 1) * DB, ntask_wg);
             }
         } else if (wave >= kDecUpWaves) {
             const int q = wave - kDecUpWaves;
@@ -441,10 +443,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         // shares 3, 3, 3, 3, 2 (of 14): wave 4 shares a SIMD with wave 0, so
         // it issues only in wave 0's idle slots and sends its first requests
         // behind those of the other seven waves; with an even share it ended
-        // phase 1 last in every workgroup (T=4: 27 us against 21.5 us)
+        // phase 1 last in every workgroup (T=4: 27 us against 21.5 us).
+        // The shares are whole batches of kPairBatch pairs, so that only the
+        // workgroup's last batch can be partial: a partial batch still issues
+        // its loads past the end (through empty resources, to keep the waits
+        // exact), and at T=1 cutting pairs instead of batches left a partial
+        // batch in four waves of every workgroup (27 pair loads for 21 pairs)
         const int cq0 = kDecUpShare * wave, cq1 = wave + 1 < kDecUpWaves ? cq0 + kDecUpShare : kDecUpTotal;
-        const int q0 = p0 + (int)((uint32_t)((p1 - p0) * cq0) / kDecUpTotal);
-        const int q1 = p0 + (int)((uint32_t)((p1 - p0) * cq1) / kDecUpTotal);
+        const int nbt = (p1 - p0 + kPairBatch - 1) / kPairBatch;   // the workgroup's batches
+        const int q0 = p0 + (int)((uint32_t)(nbt * cq0) / kDecUpTotal) * kPairBatch;
+        const int q1 = min(p0 + (int)((uint32_t)(nbt * cq1) / kDecUpTotal) * kPairBatch, p1);
         const int nstep = (q1 - q0 + kPairBatch - 1) / kPairBatch;
         const int u0 = n_u > 0 ? q0 / F : 0, f0 = q0 - u0 * F;
         // pair q0 + i is (u, f): f0 + i carried into the following experts
