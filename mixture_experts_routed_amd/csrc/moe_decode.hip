@@ -642,14 +642,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             for (int i = 0; i < DB; ++i) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    // scalar: the h row of u's representative for token t
-                    const int r = max(__builtin_amdgcn_readlane(rep_of[t], u), 0);
-                    const u32x4* hs = h_lds + r * (F / 8);
+                    // scalar: the h row of u's representative for token t;
+                    // with 2-4 tokens an expert is usually routed for only
+                    // some of them, and the others' values would be dropped
+                    // (a uniform branch: no h read, no dot products)
+                    const int rraw = __builtin_amdgcn_readlane(rep_of[t], u);
                     float part = 0.0f;
+                    if (NT == 1 || rraw >= 0) {
+                        const u32x4* hs = h_lds + max(rraw, 0) * (F / 8);
 #pragma unroll
-                    for (int j = 0; j < NCF; ++j) {
-                        const u32x4 hv = hs[hch[j]];
-                        part = dot8_bf16(buf[i][j], make_uint4(hv.x, hv.y, hv.z, hv.w), part);
+                        for (int j = 0; j < NCF; ++j) {
+                            const u32x4 hv = hs[hch[j]];
+                            part = dot8_bf16(buf[i][j], make_uint4(hv.x, hv.y, hv.z, hv.w), part);
+                        }
                     }
                     v[i * NT + t] = part;
                 }
