@@ -9,10 +9,12 @@
 //    of them, are split evenly over the workgroups (wave 4, which also
 //    polls, takes a smaller share of its workgroup's).  A wave streams the
 //    gate row f and the up row F + f of expert u (each byte read once, two
-//    steps of rows in flight), dots them with every token that chose u and
-//    stores W * silu(gate . x) * (up . x) as bf16 into the workspace row of
-//    the (expert, token)'s representative slot, with device-scope stores (W
-//    is the summed routing weight of the token's slots on u);
+//    steps of rows in flight), dots them with every token's row (branch-free:
+//    this phase is bound by the weight stream) and, for each token that
+//    chose u, stores W * silu(gate . x) * (up . x) as bf16 into the
+//    workspace row of the (expert, token)'s representative slot, with
+//    device-scope stores (W is the summed routing weight of the token's
+//    slots on u);
 //  - hand-off: once all five waves' stores have completed, wave 4 stores
 //    the workgroup's flag (a 64-bit word made from the call's stamp) and
 //    polls the flags of the whole grid (bounded by a clock limit), then
@@ -25,8 +27,9 @@
 //    request their down rows at kernel start and hold them in registers;
 //    waves 0-3 request theirs after their gate/up work.  A step dots a
 //    batch of down rows with the h rows of the expert's representatives
-//    (from LDS) and sums all of them across the wave at once (register-swap
-//    and DPP moves); y[row][representative] goes to LDS;
+//    (from LDS; tokens that did not choose the expert are skipped) and sums
+//    all of them across the wave at once (register-swap and DPP moves);
+//    y[row][representative] goes to LDS;
 //  - out[t][c] = sum of y over token t's representatives in slot order
 //    (+ residual), written once.
 // So the layer is one launch: no partial sums, no combine kernel, no float
