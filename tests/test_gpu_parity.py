@@ -217,6 +217,25 @@ def test_decode_shapes(shape):
     check_tol(run_bf16("moe_experts_decode", to_gpu(p)), ref, BF16_TOL, str(shape))
 
 
+@pytest.mark.parametrize("shape", [(1, 1792, 896, 64, 8), (1, 1920, 896, 64, 8), (1, 1280, 512, 64, 8),
+                                   (1, 1280, 896, 64, 3), (2, 1280, 896, 64, 8), (3, 1536, 896, 64, 6),
+                                   (4, 1536, 896, 64, 6)])
+def test_decode_work_split_boundaries(shape):
+    """Work splits of the one-launch decode on a grid of one workgroup per
+    CU (256 on MI355X): with H = 1792 and 8 distinct experts each workgroup
+    has exactly seven full down steps of 8 rows; with H = 1920 its output
+    rows alternate between 7 and 8, so one grid mixes the one-step split
+    and the split into two-step prefetches plus the rest; F = 512 gives
+    16-row steps; k = 3 leaves a partial last gate/up batch in most
+    workgroups; T = 2-4 take the multi-token kernel, whose down products
+    skip the tokens not routed to the task's expert (tokens past T too)."""
+    T, H, F, E, k = shape
+    _say(f"decode split {shape}")
+    p = bf16_problem(T, H, F, E, k, seed=7 * T + H, std=1 / np.sqrt(H))
+    ref = bf16_ref(p, batched=False)
+    check_tol(run_bf16("moe_experts_decode", to_gpu(p)), ref, BF16_TOL, str(shape))
+
+
 @pytest.mark.parametrize("T", [1, 3])
 def test_decode_dropped_slots_with_stale_workspace(T):
     """Dropped slots (-1 and E) on the gather-GEMV path with a workspace whose
